@@ -1,0 +1,194 @@
+"""fp64 CPU oracle for the causal sparse-attention prefill.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  It shares no code
+with the HIP library and never calls it.
+
+``oracle.c`` holds the definitions (pooled keys, block and token selection,
+attention over the union with a sink); this module builds it with gcc,
+loads it with ctypes and wraps it for numpy arrays.  ``brute.py`` is a
+second, exact pure-Python version for tiny inputs used to pin this one.
+
+Every function takes the exact input values as float32 numpy arrays in the
+layouts q [Bt,Hq,N,d], k/v [Bt,Hkv,N,d], idx_q/idx_k [Bt,N,dI].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_f32p = np.ctypeslib.ndpointer(np.float32, flags="C_CONTIGUOUS")
+_f64p = np.ctypeslib.ndpointer(np.float64, flags="C_CONTIGUOUS")
+_i32p = np.ctypeslib.ndpointer(np.int32, flags="C_CONTIGUOUS")
+_i64p = np.ctypeslib.ndpointer(np.int64, flags="C_CONTIGUOUS")
+_i64 = ctypes.c_int64
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so (gcc, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared",
+                               "-fno-fast-math", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    lib.orc_block_pool.argtypes = [_f32p, _i64, _i64, _i64, _i64, _f64p]
+    lib.orc_block_pool.restype = None
+    lib.orc_block_scores.argtypes = [_f32p, _f64p, _i64, _i64, _i64, _i64, _i64,
+                                     _i64p, _i64, _f64p]
+    lib.orc_block_scores.restype = None
+    lib.orc_block_select.argtypes = [_f32p, _f64p, _i64, _i64, _i64, _i64, _i64, _i64,
+                                     _i64p, _i64, _i32p, _f64p, _f64p]
+    lib.orc_block_select.restype = None
+    lib.orc_token_scores.argtypes = [_f32p, _f32p, _i64, _i64, _i64p, _i64, _f64p]
+    lib.orc_token_scores.restype = None
+    lib.orc_token_select.argtypes = [_f32p, _f32p, _i64, _i64, _i64, _i64p, _i64,
+                                     _i32p, _f64p, _f64p]
+    lib.orc_token_select.restype = None
+    lib.orc_attend.argtypes = [_f32p, _f32p, _f32p, _i64, _i64, _i64, _i64,
+                               ctypes.c_double, _i64, _i64,
+                               ctypes.c_void_p, _i64, ctypes.c_void_p, _i64,
+                               ctypes.c_void_p, _i64p, _i64, _f64p, _f64p, _i64p]
+    lib.orc_attend.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _f32(a):
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def _rows(rows, total):
+    if rows is None:
+        return np.arange(total, dtype=np.int64)
+    return np.ascontiguousarray(rows, dtype=np.int64)
+
+
+def block_pool(k, B):
+    """Mean-pooled block keys, [Bt, Hkv, N/B, d] fp64."""
+    k = _f32(k)
+    Bt, Hkv, N, d = k.shape
+    if B <= 0 or N % B:
+        raise ValueError("block size must divide N")
+    kbar = np.empty((Bt, Hkv, N // B, d), dtype=np.float64)
+    _load().orc_block_pool(k, Bt * Hkv, N, d, B, kbar)
+    return kbar
+
+
+def block_scores(q, kbar, B, rows):
+    """Gate scores [len(rows), n]; -inf for blocks that are not candidates."""
+    q = _f32(q)
+    Bt, Hq, N, d = q.shape
+    Hkv, n = kbar.shape[1], kbar.shape[2]
+    rows = _rows(rows, Bt * Hq * N)
+    out = np.empty((len(rows), n), dtype=np.float64)
+    _load().orc_block_scores(q, np.ascontiguousarray(kbar), Hq, Hkv, N, d, B,
+                             rows, len(rows), out)
+    return out
+
+
+def block_select(q, kbar, B, top_k, rows=None):
+    """Selected blocks per row [len(rows), top_k] (ascending, -1 padded) and the
+    scores of the last kept / first dropped candidate (NaN when absent)."""
+    q = _f32(q)
+    Bt, Hq, N, d = q.shape
+    Hkv = kbar.shape[1]
+    rows = _rows(rows, Bt * Hq * N)
+    sel = np.empty((len(rows), top_k), dtype=np.int32)
+    s_last = np.empty(len(rows), dtype=np.float64)
+    s_next = np.empty(len(rows), dtype=np.float64)
+    _load().orc_block_select(q, np.ascontiguousarray(kbar), Hq, Hkv, N, d, B, top_k,
+                             rows, len(rows), sel, s_last, s_next)
+    return sel, s_last, s_next
+
+
+def token_scores(idx_q, idx_k, rows):
+    iq, ik = _f32(idx_q), _f32(idx_k)
+    Bt, N, dI = iq.shape
+    rows = _rows(rows, Bt * N)
+    out = np.empty((len(rows), N), dtype=np.float64)
+    _load().orc_token_scores(iq, ik, N, dI, rows, len(rows), out)
+    return out
+
+
+def token_select(idx_q, idx_k, top_t, rows=None):
+    """Selected tokens per token row r = b*N + i: [len(rows), top_t]."""
+    iq, ik = _f32(idx_q), _f32(idx_k)
+    Bt, N, dI = iq.shape
+    rows = _rows(rows, Bt * N)
+    tsel = np.empty((len(rows), top_t), dtype=np.int32)
+    s_last = np.empty(len(rows), dtype=np.float64)
+    s_next = np.empty(len(rows), dtype=np.float64)
+    _load().orc_token_select(iq, ik, N, dI, top_t, rows, len(rows), tsel, s_last, s_next)
+    return tsel, s_last, s_next
+
+
+def attend(q, k, v, *, scale=None, window=0, block_size=0, sel=None, tsel=None,
+           sink=None, rows=None):
+    """Attention of the listed rows under a given selection.
+    sel [len(rows), w] block ids and tsel [len(rows), w'] token ids are per
+    listed row.  Returns out [len(rows), d] fp64, lse fp64, |A(i)| int64."""
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    Bt, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    rows = _rows(rows, Bt * Hq * N)
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    out = np.empty((len(rows), d), dtype=np.float64)
+    lse = np.empty(len(rows), dtype=np.float64)
+    cnt = np.empty(len(rows), dtype=np.int64)
+    sel_a = None if sel is None else np.ascontiguousarray(sel, dtype=np.int32)
+    tsel_a = None if tsel is None else np.ascontiguousarray(tsel, dtype=np.int32)
+    sink_a = None if sink is None else _f32(sink)
+    for a in (sel_a, tsel_a):
+        if a is not None and a.shape[0] != len(rows):
+            raise ValueError("selections are per listed row")
+    rc = _load().orc_attend(
+        q, k, v, Hq, Hkv, N, d, scale, int(window), int(block_size),
+        None if sel_a is None else sel_a.ctypes.data, 0 if sel_a is None else sel_a.shape[1],
+        None if tsel_a is None else tsel_a.ctypes.data, 0 if tsel_a is None else tsel_a.shape[1],
+        None if sink_a is None else sink_a.ctypes.data,
+        rows, len(rows), out, lse, cnt)
+    if rc != 0:
+        raise ValueError("selection id out of range")
+    return out, lse, cnt
+
+
+def forward(q, k, v, *, block_size=0, top_k=0, window=0, idx_q=None, idx_k=None,
+            token_top_k=0, sink=None, scale=None, rows=None):
+    """The whole path for the listed rows: pool, gate, token select, attend.
+    Returns a dict with out, lse, count, sel, s_last, s_next, tsel, t_last,
+    t_next (selection entries are None when that gate is off)."""
+    Bt, Hq, N, d = np.shape(q)
+    rows = _rows(rows, Bt * Hq * N)
+    res = dict(sel=None, s_last=None, s_next=None, tsel=None, t_last=None, t_next=None)
+    if top_k > 0:
+        kbar = block_pool(k, block_size)
+        res["sel"], res["s_last"], res["s_next"] = block_select(q, kbar, block_size, top_k, rows)
+    if token_top_k > 0:
+        trow = (rows // (Hq * N)) * N + rows % N
+        uniq, inv = np.unique(trow, return_inverse=True)
+        ts, tl, tn = token_select(idx_q, idx_k, token_top_k, uniq)
+        res["tsel"], res["t_last"], res["t_next"] = ts[inv], tl[inv], tn[inv]
+    out, lse, cnt = attend(q, k, v, scale=scale, window=window, block_size=block_size,
+                           sel=res["sel"], tsel=res["tsel"], sink=sink, rows=rows)
+    res.update(out=out, lse=lse, count=cnt)
+    return res

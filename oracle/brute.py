@@ -1,0 +1,94 @@
+"""Exact brute-force version of the method for tiny inputs (N <= ~32).
+
+TEST INFRASTRUCTURE: a second, independent statement of the definitions,
+used only to pin the C oracle.  It shares nothing with it: gate scores are
+exact rationals (``fractions.Fraction``), the block selection is found by
+enumerating every admissible subset of past blocks, and the attended set is
+built pair by pair from the three clauses of the mask predicate.
+
+Sources: the MoBA summary page (discuss.pytorch.kr), sections "블록 분할과
+top-k 게이팅" and "인과성 보존"; the Bit-Axon "SWA + MoE" page, section
+"슬라이딩 윈도우 마스크"; the Naive-N0.5-Flash page, section "SWA와 DSA를
+결합한 어텐션".
+"""
+from __future__ import annotations
+
+import itertools
+import math
+from fractions import Fraction
+
+import numpy as np
+
+
+def _frac(x) -> Fraction:
+    return Fraction(float(x))
+
+
+def best_subset(scores: dict[int, Fraction], m: int) -> tuple[int, ...]:
+    """Among all m-subsets of the candidate ids, the one with the largest exact
+    score sum; among equal sums the lexicographically smallest sorted tuple
+    (so a tie is resolved toward lower ids)."""
+    best, best_sum = None, None
+    for sub in itertools.combinations(sorted(scores), m):
+        s = sum((scores[c] for c in sub), Fraction(0))
+        if best is None or s > best_sum or (s == best_sum and sub < best):
+            best, best_sum = sub, s
+    return best if best is not None else ()
+
+
+def forward(q, k, v, *, block_size=0, top_k=0, window=0, idx_q=None, idx_k=None,
+            token_top_k=0, sink=None, scale=None):
+    """Returns (out [Bt,Hq,N,d], lse [Bt,Hq,N], sel dict, tsel dict, count)."""
+    q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
+    Bt, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    out = np.zeros((Bt, Hq, N, d))
+    lse = np.zeros((Bt, Hq, N))
+    count = np.zeros((Bt, Hq, N), dtype=np.int64)
+    sels, tsels = {}, {}
+    for b in range(Bt):
+        tok = {}
+        if token_top_k:
+            for i in range(N):
+                sc = {j: sum((_frac(idx_q[b, i, e]) * _frac(idx_k[b, j, e])
+                              for e in range(idx_q.shape[2])), Fraction(0))
+                      for j in range(i)}
+                tok[i] = set(best_subset(sc, min(token_top_k, i)))
+                tsels[(b, i)] = tok[i]
+        for h in range(Hq):
+            g = h // G
+            pooled = {}
+            if top_k:
+                for c in range(N // block_size):
+                    pooled[c] = [sum((_frac(k[b, g, j, e])
+                                      for j in range(c * block_size, (c + 1) * block_size)),
+                                     Fraction(0)) / block_size for e in range(d)]
+            for i in range(N):
+                chosen = set()
+                if top_k:
+                    own = i // block_size
+                    sc = {c: sum((_frac(q[b, h, i, e]) * pooled[c][e] for e in range(d)),
+                                 Fraction(0)) for c in range(own)}
+                    chosen = set(best_subset(sc, min(top_k - 1, own))) | {own}
+                    sels[(b, h, i)] = chosen
+                keys = []
+                for j in range(N):
+                    causal = j <= i
+                    in_window = window > 0 and i - j < window
+                    in_block = bool(top_k) and (j // block_size) in chosen
+                    in_tokens = bool(token_top_k) and j in tok[i]
+                    if causal and (in_window or in_block or in_tokens):
+                        keys.append(j)
+                logits = [scale * sum(q[b, h, i, e] * k[b, g, j, e] for e in range(d))
+                          for j in keys]
+                z = None if sink is None else float(sink[h])
+                M = max(logits + ([z] if z is not None else []), default=-math.inf)
+                w = [math.exp(x - M) for x in logits]
+                L = sum(w) + (math.exp(z - M) if z is not None else 0.0)
+                for e in range(d):
+                    out[b, h, i, e] = sum(wj * v[b, g, j, e] for wj, j in zip(w, keys)) / L
+                lse[b, h, i] = M + math.log(L)
+                count[b, h, i] = len(keys)
+    return out, lse, sels, tsels, count

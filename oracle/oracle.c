@@ -1,0 +1,288 @@
+/*
+ * oracle.c -- plain, slow fp64 CPU definition of the causal sparse-attention
+ * prefill: block gating by mean-pooled keys, unioned with a causal sliding
+ * window and an optional per-query token selection, under GQA, with an
+ * optional per-head sink logit.
+ *
+ * TEST INFRASTRUCTURE.  Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg load this library.  It shares no code, header, table or
+ * helper with the HIP library and does not include anything from it.
+ *
+ * Inputs are the exact values the device sees (bf16 or fp32, passed here as
+ * fp32, which holds bf16 exactly) and every sum is taken in fp64, one term at
+ * a time, in index order.  Loops are the definitions written out; OpenMP only
+ * splits independent rows across threads.
+ *
+ * Layouts (row-major, contiguous):
+ *   q   [Bt, Hq,  N, d]     k, v [Bt, Hkv, N, d]
+ *   idx_q, idx_k [Bt, N, dI]  (indexer; one head shared by all query heads)
+ *   "row" r = (b*Hq + h)*N + i names query i of head h in batch b.
+ *   Query head h reads kv head h / (Hq/Hkv) (consecutive grouping).
+ *
+ * Sources (pages as titled):
+ *   [MoBA]  "MoBA: 어텐션에 전문가 혼합을 적용해 긴 문맥을 효율적으로 처리하는
+ *           블록 어텐션 (feat. MoonshotAI)", discuss.pytorch.kr summary page.
+ *   [SWA]   Bit-Axon docs, "SWA + MoE: 어텐션과 희소 전문가".
+ *   [Naive] "Naive-N0.5-Flash -- 100만 토큰 문맥을 지원하는 오픈 가중치 MoE 모델",
+ *           section "SWA와 DSA를 결합한 어텐션".
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+typedef struct {
+    double s;
+    int64_t idx;
+} cand_t;
+
+/* Descending score, then ascending index: the lower index wins a tie. */
+static int cand_cmp(const void* pa, const void* pb) {
+    const cand_t* a = (const cand_t*)pa;
+    const cand_t* b = (const cand_t*)pb;
+    if (a->s > b->s) return -1;
+    if (a->s < b->s) return 1;
+    if (a->idx < b->idx) return -1;
+    if (a->idx > b->idx) return 1;
+    return 0;
+}
+
+static int int32_cmp(const void* pa, const void* pb) {
+    int32_t a = *(const int32_t*)pa, b = *(const int32_t*)pb;
+    return (a > b) - (a < b);
+}
+
+/*
+ * Mean-pooled block keys [MoBA, "블록 분할과 top-k 게이팅": the score uses
+ * MeanPool(K[I_i]) over the B keys of block i].
+ *   kbar[(b*Hkv + g)*n + c][e] = (1/B) * sum_{j=cB}^{cB+B-1} k[b][g][j][e]
+ */
+void orc_block_pool(const float* k, int64_t n_bh, int64_t N, int64_t d, int64_t B,
+                    double* kbar) {
+    const int64_t n = N / B;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < n_bh * n; ++t) {
+        const int64_t bh = t / n, c = t % n;
+        double* dst = kbar + t * d;
+        for (int64_t e = 0; e < d; ++e) {
+            double acc = 0.0;
+            for (int64_t j = c * B; j < (c + 1) * B; ++j)
+                acc += (double)k[(bh * N + j) * d + e];
+            dst[e] = acc / (double)B;
+        }
+    }
+}
+
+/* Unscaled gate score s_c = <q_i, kbar_c> [MoBA, gate score equation]. */
+static double gate_score(const float* qrow, const double* kb, int64_t d) {
+    double acc = 0.0;
+    for (int64_t e = 0; e < d; ++e) acc += (double)qrow[e] * kb[e];
+    return acc;
+}
+
+/*
+ * Gate scores of listed rows against every block: scores[r][c] for c < b(i),
+ * -INFINITY for the own block and later ones (they are never candidates;
+ * the own block is forced separately) [MoBA, "인과성 보존": future blocks get
+ * s = -inf and g = 0].
+ */
+void orc_block_scores(const float* q, const double* kbar, int64_t Hq, int64_t Hkv,
+                      int64_t N, int64_t d, int64_t B, const int64_t* rows, int64_t nrows,
+                      double* scores) {
+    const int64_t n = N / B, G = Hq / Hkv;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t t = 0; t < nrows; ++t) {
+        const int64_t r = rows[t];
+        const int64_t i = r % N, bh = r / N, b = bh / Hq, h = bh % Hq, g = h / G;
+        const int64_t own = i / B;
+        const float* qrow = q + r * d;
+        for (int64_t c = 0; c < n; ++c)
+            scores[t * n + c] = (c < own)
+                ? gate_score(qrow, kbar + ((b * Hkv + g) * n + c) * d, d) : -INFINITY;
+    }
+}
+
+/*
+ * Block selection [MoBA, "블록 분할과 top-k 게이팅" (g_i = 1 iff s_i is among
+ * the top k) and "인과성 보존" (future blocks excluded; the own block always
+ * attended, like a shared expert)].  The own block takes one of the k slots
+ * (the sparsity 1 - kB/N printed with the scaling results holds only then).
+ * Candidates c < b are ranked by (-s_c, c); the first m = min(k-1, b) are
+ * kept.  sel row = ascending block ids of {b} and the kept ones, then -1.
+ * s_last[t] = score of the m-th kept candidate (NaN if m == 0);
+ * s_next[t] = score of the best candidate not kept (NaN if none).
+ */
+void orc_block_select(const float* q, const double* kbar, int64_t Hq, int64_t Hkv,
+                      int64_t N, int64_t d, int64_t B, int64_t top_k,
+                      const int64_t* rows, int64_t nrows,
+                      int32_t* sel, double* s_last, double* s_next) {
+    const int64_t n = N / B, G = Hq / Hkv;
+#pragma omp parallel
+    {
+        cand_t* cand = (cand_t*)malloc(sizeof(cand_t) * (size_t)(n > 0 ? n : 1));
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t t = 0; t < nrows; ++t) {
+            const int64_t r = rows[t];
+            const int64_t i = r % N, bh = r / N, b = bh / Hq, h = bh % Hq, g = h / G;
+            const int64_t own = i / B;
+            const float* qrow = q + r * d;
+            for (int64_t c = 0; c < own; ++c) {
+                cand[c].s = gate_score(qrow, kbar + ((b * Hkv + g) * n + c) * d, d);
+                cand[c].idx = c;
+            }
+            qsort(cand, (size_t)own, sizeof(cand_t), cand_cmp);
+            const int64_t m = (top_k - 1 < own) ? top_k - 1 : own;
+            int32_t* out = sel + t * top_k;
+            for (int64_t x = 0; x < top_k; ++x) out[x] = -1;
+            for (int64_t x = 0; x < m; ++x) out[x] = (int32_t)cand[x].idx;
+            out[m] = (int32_t)own;
+            qsort(out, (size_t)(m + 1), sizeof(int32_t), int32_cmp);
+            s_last[t] = m > 0 ? cand[m - 1].s : NAN;
+            s_next[t] = m < own ? cand[m].s : NAN;
+        }
+        free(cand);
+    }
+}
+
+/*
+ * Token selection by a single-head indexer [Naive, "SWA와 DSA를 결합한 어텐션":
+ * a light indexer scores the history and attention runs on the top 2,048
+ * tokens].  Reading taken: score = <idx_q_i, idx_k_j> (unscaled), candidates
+ * j < i, keep the first min(Kt, i) by (-score, j).  Token rows are
+ * r = b*N + i; tsel row = ascending token ids, then -1.
+ */
+void orc_token_scores(const float* iq, const float* ik, int64_t N, int64_t dI,
+                      const int64_t* rows, int64_t nrows, double* scores) {
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t t = 0; t < nrows; ++t) {
+        const int64_t r = rows[t], i = r % N, b = r / N;
+        for (int64_t j = 0; j < N; ++j) {
+            if (j >= i) { scores[t * N + j] = -INFINITY; continue; }
+            double acc = 0.0;
+            for (int64_t e = 0; e < dI; ++e)
+                acc += (double)iq[r * dI + e] * (double)ik[(b * N + j) * dI + e];
+            scores[t * N + j] = acc;
+        }
+    }
+}
+
+void orc_token_select(const float* iq, const float* ik, int64_t N, int64_t dI, int64_t Kt,
+                      const int64_t* rows, int64_t nrows,
+                      int32_t* tsel, double* s_last, double* s_next) {
+#pragma omp parallel
+    {
+        cand_t* cand = (cand_t*)malloc(sizeof(cand_t) * (size_t)(N > 0 ? N : 1));
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t t = 0; t < nrows; ++t) {
+            const int64_t r = rows[t], i = r % N, b = r / N;
+            for (int64_t j = 0; j < i; ++j) {
+                double acc = 0.0;
+                for (int64_t e = 0; e < dI; ++e)
+                    acc += (double)iq[r * dI + e] * (double)ik[(b * N + j) * dI + e];
+                cand[j].s = acc;
+                cand[j].idx = j;
+            }
+            qsort(cand, (size_t)i, sizeof(cand_t), cand_cmp);
+            const int64_t m = Kt < i ? Kt : i;
+            int32_t* out = tsel + t * Kt;
+            for (int64_t x = 0; x < Kt; ++x) out[x] = -1;
+            for (int64_t x = 0; x < m; ++x) out[x] = (int32_t)cand[x].idx;
+            qsort(out, (size_t)m, sizeof(int32_t), int32_cmp);
+            s_last[t] = m > 0 ? cand[m - 1].s : NAN;
+            s_next[t] = m < i ? cand[m].s : NAN;
+        }
+        free(cand);
+    }
+}
+
+/*
+ * Attention of listed rows under a given selection.
+ *
+ * Attended set [SWA, "슬라이딩 윈도우 마스크": j <= i and i - j < w;
+ * MoBA, "표준 어텐션에서 블록 어텐션으로": softmax over K[I] only]:
+ *   A(i) = { j <= i : (w > 0 and i - j < w)  or  j/B in sel(i)
+ *                      or  j in tsel(i) }
+ * one softmax over the union.  Logits x_j = scale * <q_i, k_j>
+ * [SWA, "어텐션 공식": QK^T / sqrt(d_k) plus the additive mask].  A sink
+ * [Naive: sink bias in SWA and DSA] is one more logit z = sink[h], not
+ * scaled, with a zero value vector:
+ *   M = max(max_j x_j, z),  L = sum_j e^(x_j - M) + e^(z - M)
+ *   out = sum_j e^(x_j - M) v_j / L,   lse = M + ln L.
+ * sel  [nrows, sel_w]  block ids per listed row, -1 ignored (NULL: none)
+ * tsel [nrows, tsel_w] token ids per listed row, -1 ignored (NULL: none)
+ * count[t] = |A(i)|.  Returns 0, or -1 if an id is out of range.
+ */
+int orc_attend(const float* q, const float* k, const float* v,
+               int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+               double scale, int64_t window, int64_t B,
+               const int32_t* sel, int64_t sel_w,
+               const int32_t* tsel, int64_t tsel_w,
+               const float* sink,
+               const int64_t* rows, int64_t nrows,
+               double* out, double* lse, int64_t* count) {
+    const int64_t G = Hq / Hkv;
+    int bad = 0;
+#pragma omp parallel
+    {
+        unsigned char* mark = (unsigned char*)malloc((size_t)(N > 0 ? N : 1));
+        double* x = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+#pragma omp for schedule(dynamic, 8)
+        for (int64_t t = 0; t < nrows; ++t) {
+            const int64_t r = rows[t];
+            const int64_t i = r % N, bh = r / N, b = bh / Hq, h = bh % Hq, g = h / G;
+            memset(mark, 0, (size_t)(i + 1));
+            if (window > 0)
+                for (int64_t j = (i - window + 1 > 0 ? i - window + 1 : 0); j <= i; ++j)
+                    mark[j] = 1;
+            if (sel)
+                for (int64_t s = 0; s < sel_w; ++s) {
+                    const int64_t c = sel[t * sel_w + s];
+                    if (c < 0) continue;
+                    if (B <= 0 || c >= N / B) { bad = 1; continue; }
+                    for (int64_t j = c * B; j < (c + 1) * B && j <= i; ++j) mark[j] = 1;
+                }
+            if (tsel)
+                for (int64_t s = 0; s < tsel_w; ++s) {
+                    const int64_t j = tsel[t * tsel_w + s];
+                    if (j < 0) continue;
+                    if (j >= N) { bad = 1; continue; }
+                    if (j <= i) mark[j] = 1;
+                }
+            const float* qrow = q + r * d;
+            const float* kb = k + (b * Hkv + g) * N * d;
+            const float* vb = v + (b * Hkv + g) * N * d;
+            double M = -INFINITY;
+            int64_t cnt = 0;
+            for (int64_t j = 0; j <= i; ++j) {
+                if (!mark[j]) continue;
+                double acc = 0.0;
+                for (int64_t e = 0; e < d; ++e) acc += (double)qrow[e] * (double)kb[j * d + e];
+                x[j] = scale * acc;
+                if (x[j] > M) M = x[j];
+                ++cnt;
+            }
+            const double z = sink ? (double)sink[h] : -INFINITY;
+            if (z > M) M = z;
+            double L = 0.0;
+            double* o = out + t * d;
+            for (int64_t e = 0; e < d; ++e) o[e] = 0.0;
+            for (int64_t j = 0; j <= i; ++j) {
+                if (!mark[j]) continue;
+                const double p = exp(x[j] - M);
+                L += p;
+                for (int64_t e = 0; e < d; ++e) o[e] += p * (double)vb[j * d + e];
+            }
+            if (sink) L += exp(z - M);
+            if (L > 0.0) {
+                for (int64_t e = 0; e < d; ++e) o[e] /= L;
+                lse[t] = M + log(L);
+            } else {
+                lse[t] = -INFINITY;
+            }
+            count[t] = cnt;
+        }
+        free(mark);
+        free(x);
+    }
+    return bad ? -1 : 0;
+}

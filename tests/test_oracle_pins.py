@@ -1,0 +1,338 @@
+"""Pins of the fp64 oracle against things other than itself: textbook
+attention (torch SDPA in fp64), closed forms, invariants, the sparsity values
+printed on the MoBA page, and an exact brute-force enumeration.  CPU only."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import brute
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def rnd(shape, seed, scale=1.0):
+    return (scale * np.random.default_rng(seed).standard_normal(shape)).astype(np.float32)
+
+
+def sdpa(q, k, v, mask=None, causal=False, scale=None):
+    """torch SDPA in fp64 on the CPU; returns (out, lse) with lse from
+    torch.logsumexp of the masked, scaled logits."""
+    qt, kt, vt = (torch.from_numpy(np.asarray(a, dtype=np.float64)) for a in (q, k, v))
+    d = qt.shape[-1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    N = qt.shape[-2]
+    if causal:
+        mask = np.tril(np.ones((N, N), dtype=bool))
+    m = torch.from_numpy(mask)
+    out = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=m, scale=scale)
+    logits = torch.matmul(qt, kt.transpose(-1, -2)) * scale
+    logits = logits.masked_fill(~m, -math.inf)
+    lse = torch.logsumexp(logits, dim=-1)
+    return out.numpy(), lse.numpy()
+
+
+def run(q, k, v, **kw):
+    Bt, Hq, N, d = q.shape
+    r = oracle.forward(q, k, v, **kw)
+    return r, r["out"].reshape(Bt, Hq, N, d), r["lse"].reshape(Bt, Hq, N)
+
+
+# P1: with k = n blocks kept, block gating is full causal attention (MoBA page,
+# "세밀한 블록 분할과 유연한 하이브리드": MoBA is a drop-in replacement of
+# full attention), for any window.
+@pytest.mark.parametrize("window", [0, 1, 7, 1000])
+def test_p1_all_blocks_is_dense_causal(window):
+    q, k, v = rnd((1, 2, 64, 16), 1), rnd((1, 2, 64, 16), 2), rnd((1, 2, 64, 16), 3)
+    _, out, lse = run(q, k, v, block_size=8, top_k=8, window=window)
+    ro, rl = sdpa(q, k, v, causal=True)
+    np.testing.assert_allclose(out, ro, atol=1e-12)
+    np.testing.assert_allclose(lse, rl, atol=1e-12)
+
+
+# P2: the window alone (Bit-Axon "SWA + MoE", sliding-window mask): w >= N is
+# causal; 1 <= w < N is SDPA with the mask of that page's three-line code.
+@pytest.mark.parametrize("window", [1, 2, 5, 16, 63, 64, 500])
+def test_p2_window_matches_sdpa_mask(window):
+    N = 64
+    q, k, v = rnd((2, 3, N, 8), 4), rnd((2, 3, N, 8), 5), rnd((2, 3, N, 8), 6)
+    _, out, lse = run(q, k, v, window=window)
+    q_pos, k_pos = np.arange(N), np.arange(N)
+    causal_mask = k_pos[None, :] <= q_pos[:, None]
+    window_mask = q_pos[:, None] - k_pos[None, :] < window
+    ro, rl = sdpa(q, k, v, mask=causal_mask & window_mask)
+    np.testing.assert_allclose(out, ro, atol=1e-12)
+    np.testing.assert_allclose(lse, rl, atol=1e-12)
+    if window >= N:
+        ro2, rl2 = sdpa(q, k, v, causal=True)
+        np.testing.assert_allclose(out, ro2, atol=1e-12)
+
+
+# P3: w = 1 attends to the query's own key only.
+def test_p3_window_one_is_identity():
+    q, k, v = rnd((1, 2, 40, 8), 7), rnd((1, 2, 40, 8), 8), rnd((1, 2, 40, 8), 9)
+    r, out, lse = run(q, k, v, window=1)
+    np.testing.assert_array_equal(out, v.astype(np.float64))
+    x = (q.astype(np.float64) * k.astype(np.float64)).sum(-1) / math.sqrt(8)
+    np.testing.assert_allclose(lse, x, atol=1e-13)
+    assert (r["count"] == 1).all()
+
+
+# P4: top_k = 1 keeps only the own block under a causal mask (MoBA page,
+# "인과성 보존"): per-block causal attention.  With B = 1 that is out = v.
+def test_p4_topk_one_is_blockwise_causal():
+    B, N = 8, 48
+    q, k, v = rnd((1, 2, N, 8), 10), rnd((1, 2, N, 8), 11), rnd((1, 2, N, 8), 12)
+    r, out, lse = run(q, k, v, block_size=B, top_k=1)
+    for c in range(N // B):
+        s = slice(c * B, (c + 1) * B)
+        ro, rl = sdpa(q[:, :, s], k[:, :, s], v[:, :, s], causal=True)
+        np.testing.assert_allclose(out[:, :, s], ro, atol=1e-12)
+        np.testing.assert_allclose(lse[:, :, s], rl, atol=1e-12)
+    _, out1, _ = run(q, k, v, block_size=1, top_k=1)
+    np.testing.assert_array_equal(out1, v.astype(np.float64))
+
+
+# P5a: all keys equal -> all gate scores tie -> the lowest past blocks win.
+def test_p5_ties_go_to_lower_block():
+    B, N, top_k = 4, 40, 4
+    q = rnd((1, 1, N, 8), 13)
+    k = np.broadcast_to(rnd((1, 1, 1, 8), 14), (1, 1, N, 8)).copy()
+    v = rnd((1, 1, N, 8), 15)
+    r, _, _ = run(q, k, v, block_size=B, top_k=top_k)
+    for i in range(N):
+        b = i // B
+        m = min(top_k - 1, b)
+        want = list(range(m)) + [b] + [-1] * (top_k - 1 - m)
+        assert r["sel"][i].tolist() == want, i
+
+
+# P5b: block offsets growing along a direction u with <q, u> > 0 make the
+# most recent blocks score highest: block gating becomes block-level SWA
+# (MoBA page: sliding-window attention is MoBA whose gate keeps the latest
+# blocks).
+def test_p5_monotone_offsets_give_recent_blocks():
+    B, N, top_k, d = 4, 64, 3, 8
+    rng = np.random.default_rng(16)
+    u = np.zeros(d, np.float32); u[0] = 1.0
+    k = (0.01 * rng.standard_normal((1, 1, N, d))).astype(np.float32)
+    for c in range(N // B):
+        k[0, 0, c * B:(c + 1) * B] += c * u
+    q = (0.01 * rng.standard_normal((1, 1, N, d))).astype(np.float32)
+    q[..., 0] = 1.0
+    v = rnd((1, 1, N, d), 17)
+    r, _, _ = run(q, k, v, block_size=B, top_k=top_k)
+    for i in range(N):
+        b = i // B
+        want = list(range(max(0, b - top_k + 1), b + 1))
+        want += [-1] * (top_k - len(want))
+        assert r["sel"][i].tolist() == want, i
+
+
+# P6: the sparsity values printed on the MoBA page (and BORA's 16 of 32
+# blocks) fix that the own block takes one of the k slots: the last query of
+# a sequence attends exactly k*B keys.
+def test_p6_printed_sparsity():
+    cases = json.load(open(os.path.join(HERE, "golden", "moba_sparsity.json")))["cases"]
+    for c in cases:
+        N, B, top_k = c["N"], c["B"], c["top_k"]
+        d = 2
+        rng = np.random.default_rng(N + B)
+        q = rng.standard_normal((1, 1, N, d)).astype(np.float32)
+        k = rng.standard_normal((1, 1, N, d)).astype(np.float32)
+        r = oracle.forward(q, k, k, block_size=B, top_k=top_k, rows=np.array([N - 1]))
+        attended = int(r["count"][0])
+        assert attended == top_k * B
+        assert round(100.0 * (1.0 - attended / N), 2) == c["percent"], c["cite"]
+
+
+# P7: exact brute force (rational gate scores, subset enumeration, pairwise
+# mask clauses) on tiny inputs, over every feature combination; inputs drawn
+# from a small integer set so that exact ties occur.
+BRUTE_CASES = [
+    dict(block_size=2, top_k=3),
+    dict(block_size=4, top_k=2, window=3),
+    dict(block_size=2, top_k=4, window=5, sink=True),
+    dict(window=4, token_top_k=3, sink=True),
+    dict(block_size=4, top_k=2, window=2, token_top_k=2),
+    dict(block_size=1, top_k=5),
+]
+
+
+@pytest.mark.parametrize("case", range(len(BRUTE_CASES)))
+@pytest.mark.parametrize("ties", [False, True])
+def test_p7_brute_force(case, ties):
+    kw = dict(BRUTE_CASES[case])
+    use_sink = kw.pop("sink", False)
+    Bt, Hq, Hkv, N, d, dI = 1, 2, 1, 16, 4, 3
+    rng = np.random.default_rng(100 + case + 50 * ties)
+    draw = (lambda s: rng.integers(-1, 2, size=s).astype(np.float32)) if ties else \
+           (lambda s: rng.standard_normal(s).astype(np.float32))
+    q, k, v = draw((Bt, Hq, N, d)), draw((Bt, Hkv, N, d)), draw((Bt, Hkv, N, d))
+    iq = ik = None
+    if kw.get("token_top_k"):
+        iq, ik = draw((Bt, N, dI)), draw((Bt, N, dI))
+    sink = rng.standard_normal(Hq).astype(np.float32) if use_sink else None
+    r, out, lse = run(q, k, v, idx_q=iq, idx_k=ik, sink=sink, **kw)
+    bo, bl, bsel, btsel, bcnt = brute.forward(q, k, v, idx_q=iq, idx_k=ik, sink=sink, **kw)
+    np.testing.assert_allclose(out, bo, atol=1e-12)
+    np.testing.assert_allclose(lse, bl, atol=1e-12)
+    np.testing.assert_array_equal(r["count"].reshape(Bt, Hq, N), bcnt)
+    for t, (b, h, i) in enumerate((b, h, i) for b in range(Bt) for h in range(Hq) for i in range(N)):
+        if kw.get("top_k"):
+            got = {c for c in r["sel"][t].tolist() if c >= 0}
+            assert got == bsel[(b, h, i)], (b, h, i)
+        if kw.get("token_top_k"):
+            got = {j for j in r["tsel"][t].tolist() if j >= 0}
+            assert got == btsel[(b, i)], (b, i)
+
+
+# P8: GQA equals MHA with every kv head repeated for its query group, with
+# per-head block selection.
+def test_p8_gqa_is_repeated_mha():
+    Bt, Hq, Hkv, N, d = 2, 6, 2, 32, 8
+    q, k, v = rnd((Bt, Hq, N, d), 20), rnd((Bt, Hkv, N, d), 21), rnd((Bt, Hkv, N, d), 22)
+    kw = dict(block_size=4, top_k=3, window=5)
+    r1, o1, l1 = run(q, k, v, **kw)
+    kr, vr = np.repeat(k, Hq // Hkv, axis=1), np.repeat(v, Hq // Hkv, axis=1)
+    r2, o2, l2 = run(q, kr, vr, **kw)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+    np.testing.assert_array_equal(r1["sel"], r2["sel"])
+
+
+# P9: a sink logit z with a zero value rescales the sink-free result:
+# out_s = out * e^lse / (e^lse + e^z), lse_s = logaddexp(lse, z); z -> -inf
+# gives the sink-free result back.
+def test_p9_sink_closed_form():
+    Bt, Hq, N, d = 1, 3, 48, 8
+    q, k, v = rnd((Bt, Hq, N, d), 23), rnd((Bt, Hq, N, d), 24), rnd((Bt, Hq, N, d), 25)
+    z = np.array([0.5, -2.0, 3.0], np.float32)
+    kw = dict(block_size=8, top_k=2, window=6)
+    _, o, l = run(q, k, v, **kw)
+    _, os_, ls = run(q, k, v, sink=z, **kw)
+    zz = z.astype(np.float64)[None, :, None]
+    np.testing.assert_allclose(ls, np.logaddexp(l, zz), atol=1e-12)
+    np.testing.assert_allclose(os_, o * (np.exp(l) / (np.exp(l) + np.exp(zz)))[..., None], atol=1e-12)
+    _, o3, l3 = run(q, k, v, sink=np.full(Hq, -1e30, np.float32), **kw)
+    np.testing.assert_allclose(o3, o, atol=1e-14)
+    np.testing.assert_allclose(l3, l, atol=1e-14)
+
+
+# P10: token selection (Naive-N0.5-Flash page, SWA combined with DSA):
+# keeping at least i earlier tokens is dense causal; equal indexer keys keep
+# the lowest token ids.
+def test_p10_token_selection_cases():
+    Bt, Hq, N, d, dI = 1, 2, 40, 8, 4
+    q, k, v = rnd((Bt, Hq, N, d), 26), rnd((Bt, Hq, N, d), 27), rnd((Bt, Hq, N, d), 28)
+    iq, ik = rnd((Bt, N, dI), 29), rnd((Bt, N, dI), 30)
+    _, o, l = run(q, k, v, window=2, idx_q=iq, idx_k=ik, token_top_k=N - 1)
+    ro, rl = sdpa(q, k, v, causal=True)
+    np.testing.assert_allclose(o, ro, atol=1e-12)
+    np.testing.assert_allclose(l, rl, atol=1e-12)
+    ik_eq = np.broadcast_to(ik[:, :1], ik.shape).copy()
+    r, _, _ = run(q, k, v, window=1, idx_q=iq, idx_k=ik_eq, token_top_k=5)
+    for t in range(Hq * N):
+        i = t % N
+        m = min(5, i)
+        assert r["tsel"][t].tolist() == list(range(m)) + [-1] * (5 - m)
+
+
+# P11: union idempotence.  top_k = 1 with w >= B: the own block's causal part
+# is inside the window, so the union is the window alone; w = 1 lies inside
+# the own block, so the union is block gating alone; w >= N is causal.
+def test_p11_union_idempotence():
+    Bt, Hq, N, d = 1, 2, 64, 8
+    q, k, v = rnd((Bt, Hq, N, d), 31), rnd((Bt, Hq, N, d), 32), rnd((Bt, Hq, N, d), 33)
+    _, o1, l1 = run(q, k, v, block_size=8, top_k=1, window=8)
+    _, o2, l2 = run(q, k, v, window=8)
+    np.testing.assert_array_equal(o1, o2); np.testing.assert_array_equal(l1, l2)
+    _, o3, l3 = run(q, k, v, block_size=8, top_k=3, window=1)
+    _, o4, l4 = run(q, k, v, block_size=8, top_k=3)
+    np.testing.assert_array_equal(o3, o4); np.testing.assert_array_equal(l3, l4)
+    _, o5, l5 = run(q, k, v, block_size=8, top_k=3, window=N)
+    ro, rl = sdpa(q, k, v, causal=True)
+    np.testing.assert_allclose(o5, ro, atol=1e-12); np.testing.assert_allclose(l5, rl, atol=1e-12)
+
+
+# P12: softmax over a disjoint union equals the online-softmax merge of the
+# parts (MoBA page, implementation step 5: partial results are combined with
+# online softmax): window part and far-block part merged by their lse.
+def test_p12_merge_of_disjoint_parts():
+    Bt, Hq, N, d, B, w = 1, 2, 64, 8, 8, 6
+    q, k, v = rnd((Bt, Hq, N, d), 34), rnd((Bt, Hq, N, d), 35), rnd((Bt, Hq, N, d), 36)
+    rows = np.array([r for r in range(Bt * Hq * N) if (r % N) // B >= 3], dtype=np.int64)
+    far = np.full((len(rows), 2), -1, np.int32)
+    for t, r in enumerate(rows):
+        b = (r % N) // B
+        far[t] = [0, b - 2]          # both end before the window starts
+    ow, lw, cw = oracle.attend(q, k, v, window=w, rows=rows)
+    of, lf, cf = oracle.attend(q, k, v, block_size=B, sel=far, rows=rows)
+    ou, lu, cu = oracle.attend(q, k, v, window=w, block_size=B, sel=far, rows=rows)
+    assert (cu == cw + cf).all()
+    lm = np.logaddexp(lw, lf)
+    om = ow * np.exp(lw - lm)[:, None] + of * np.exp(lf - lm)[:, None]
+    np.testing.assert_allclose(lu, lm, atol=1e-12)
+    np.testing.assert_allclose(ou, om, atol=1e-12)
+
+
+# P13: adding a constant to every logit of a row leaves out unchanged and
+# shifts lse by that constant (done through a key component that is 1 for
+# every key, which also shifts every gate score equally).
+def test_p13_shift_invariance():
+    Bt, Hq, N, d = 1, 2, 48, 8
+    q, k, v = rnd((Bt, Hq, N, d), 37), rnd((Bt, Hq, N, d), 38), rnd((Bt, Hq, N, d), 39)
+    k[..., 0] = 1.0
+    q[..., 0] = 0.0
+    kw = dict(block_size=8, top_k=3, window=5)
+    r0, o0, l0 = run(q, k, v, **kw)
+    q2 = q.copy(); q2[..., 0] = 2.0
+    r1, o1, l1 = run(q2, k, v, **kw)
+    np.testing.assert_array_equal(r0["sel"], r1["sel"])
+    np.testing.assert_allclose(o1, o0, atol=1e-12)
+    np.testing.assert_allclose(l1, l0 + 2.0 / math.sqrt(d), atol=1e-12)
+
+
+# P14: permuting batches, or kv heads together with their query groups,
+# permutes the outputs the same way.
+def test_p14_permutation_equivariance():
+    Bt, Hq, Hkv, N, d = 2, 4, 2, 32, 8
+    q, k, v = rnd((Bt, Hq, N, d), 40), rnd((Bt, Hkv, N, d), 41), rnd((Bt, Hkv, N, d), 42)
+    kw = dict(block_size=4, top_k=3, window=3)
+    _, o, l = run(q, k, v, **kw)
+    pb, pg = [1, 0], [1, 0]
+    pq = [2, 3, 0, 1]
+    _, o2, l2 = run(q[pb][:, pq], k[pb][:, pg], v[pb][:, pg], **kw)
+    np.testing.assert_array_equal(o2, o[pb][:, pq])
+    np.testing.assert_array_equal(l2, l[pb][:, pq])
+
+
+# The pooled keys are block means (checked with numpy's mean, a different
+# summation routine than the oracle's loop).
+def test_pool_is_block_mean():
+    k = rnd((2, 3, 64, 5), 43)
+    kb = oracle.block_pool(k, 16)
+    np.testing.assert_allclose(kb, k.astype(np.float64).reshape(2, 3, 4, 16, 5).mean(3), atol=1e-14)
+
+
+def test_gaps_reported():
+    q, k = rnd((1, 1, 64, 8), 44), rnd((1, 1, 64, 8), 45)
+    kbar = oracle.block_pool(k, 8)
+    sel, s_last, s_next = oracle.block_select(q, kbar, 8, 3)
+    sc = oracle.block_scores(q, kbar, 8, np.arange(64))
+    for i in range(64):
+        b = i // 8
+        cand = sorted(sc[i, :b], reverse=True)
+        m = min(2, b)
+        if m:
+            assert s_last[i] == cand[m - 1]
+        else:
+            assert np.isnan(s_last[i])
+        if m < b:
+            assert s_next[i] == cand[m]
+        else:
+            assert np.isnan(s_next[i])
