@@ -1,0 +1,229 @@
+"""Benchmark of the causal sparse-attention prefill on one MI355X.
+
+Headline workload: the Bit-Axon SWA shape (batch 1, 32 heads, head dim 80,
+N = 16384, window 4096, causal, bf16) -- the shape the metric's 40 %-of-peak
+target is stated on.  A step is one sparse_attn_fwd call over inputs already
+resident in HBM.  Also reported (same JSON line, "workloads"): the other
+synthetic workloads, each a full forward (pool, gate, compaction, far-block
+and near attention) timed the same way.
+
+value      = tokens/s of the headline workload (batch * seq_len / step time)
+roofline   = attended FLOPs of the dominant kernel per launch / its mean
+             launch duration (HIP events on the launch stream, over the
+             timed steps) against the bf16 dense MFMA peak (2.5 PFLOP/s)
+cpu_baseline = the fp64 oracle on a bounded sample of rows of the same
+             workload, on the host cores, scaled to tokens/s
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ["sliding_window_long_amd/csrc/sa_attn.hip",
+                  "sliding_window_long_amd/csrc/sa_device.hpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_rows_bitaxon_swa_n16384_traffic.json")
+
+
+# ---------------------------------------------------------------------------
+# attended pairs (FLOPs = 4 * d * pairs): exact from the workload and, where
+# the union depends on the selection, from the device's selection
+# ---------------------------------------------------------------------------
+def window_pairs_per_head(N, w):
+    i = np.arange(N, dtype=np.int64)
+    return int(np.minimum(i + 1, w).sum())
+
+
+def attended_pairs(wl, bsel=None):
+    Bt, Hq, N = wl.batch, wl.n_q_heads, wl.seq_len
+    i = np.arange(N, dtype=np.int64)
+    if not wl.top_k:
+        return window_pairs_per_head(N, wl.window) * Bt * Hq
+    B = wl.block_size
+    if wl.window == 0:
+        b = i // B
+        per = (i % B + 1) + B * np.minimum(wl.top_k - 1, b)
+        return int(per.sum()) * Bt * Hq
+    # window U kept blocks: window interval plus the parts of kept blocks
+    # before the window start
+    sel = bsel.reshape(Bt * Hq, N, wl.top_k).astype(np.int64)
+    ws = np.maximum(i - wl.window + 1, 0)[None, :, None]
+    cb = sel * B
+    ce = np.minimum(cb + B - 1, i[None, :, None])
+    extra = np.where(sel >= 0, np.maximum(0, np.minimum(ce, ws - 1) - cb + 1), 0)
+    win = (i - ws[0, :, 0] + 1)[None, :]
+    return int(win.sum() * Bt * Hq + extra.sum())
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(launch_bytes_alg):
+    """HBM bytes per launch of the dominant kernel from committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE counters (scaled by the copy-kernel factor), or
+    None when absent or taken on a different kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+def device_inputs(wl, seed, dev):
+    inp = W.make_inputs(wl, seed)
+    t = inp.tensors()
+    return inp, {k: (None if v is None else v.to(dev)) for k, v in t.items()}
+
+
+def time_workload(wl, seed, dev, steps, warmup, want_sel=False):
+    import torch
+    import sliding_window_long_amd as sa
+    inp, g = device_inputs(wl, seed, dev)
+    ws = sa.Workspace()
+    kw = dict(block_size=wl.block_size, top_k=wl.top_k, window=wl.window, idx_q=g["idx_q"],
+              idx_k=g["idx_k"], token_top_k=wl.token_top_k, sink=g["sink"], workspace=ws)
+    out = torch.empty_like(g["q"])
+    lse = torch.empty(g["q"].shape[:3], dtype=torch.float32, device=dev)
+    bsel = None
+    if want_sel and wl.top_k:
+        _, _, bsel_t, _ = sa.forward(g["q"], g["k"], g["v"], return_selection=True, **kw)
+        torch.cuda.synchronize()
+        bsel = bsel_t.cpu().numpy()
+    for _ in range(warmup):
+        sa.forward(g["q"], g["k"], g["v"], out=out, lse=lse, **kw)
+    torch.cuda.synchronize()
+    sa.sparse_attn_set_timing(True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        sa.forward(g["q"], g["k"], g["v"], out=out, lse=lse, **kw)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    sa.sparse_attn_set_timing(False)
+    stages = {}
+    for name, ms in sa.sparse_attn_stage_times(1024):
+        stages.setdefault(name, []).append(ms)
+    stage_ms = {k: float(np.mean(v)) for k, v in stages.items()}
+    return inp, (t1 - t0) * 1e3 / steps, stage_ms, bsel
+
+
+def cpu_baseline(inp, budget_s=15.0):
+    """The oracle as it stands, on sampled rows of the workload."""
+    import oracle
+    wl = inp.wl
+    rng = np.random.default_rng(0)
+    total = wl.batch * wl.n_q_heads * wl.seq_len
+    kw = dict(window=wl.window, block_size=wl.block_size)
+    probe = np.sort(rng.choice(total, 256, replace=False))
+    t0 = time.perf_counter()
+    oracle.attend(inp.q, inp.k, inp.v, rows=probe, **kw)
+    dt = time.perf_counter() - t0
+    n = int(min(total, max(256, 256 * budget_s / max(dt, 1e-3))))
+    rows = np.sort(rng.choice(total, n, replace=False))
+    t0 = time.perf_counter()
+    oracle.attend(inp.q, inp.k, inp.v, rows=rows, **kw)
+    dt = time.perf_counter() - t0
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": (n / wl.n_q_heads) / dt, "unit": "tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{n} uniformly sampled (head, query) rows of {wl.name} "
+                      f"({dt:.1f} s), tokens/s = rows / n_q_heads / seconds"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-extra", action="store_true", help="only the headline workload")
+    ap.add_argument("--extra-steps", type=int, default=5)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sliding_window_long_amd as sa
+    sa.load_library()
+    dev = torch.device("cuda:0")
+
+    wl = W.BITAXON_SWA
+    print(f"[bench] headline {wl.name}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
+    inp, ms, stage_ms, _ = time_workload(wl, 3, dev, args.steps, args.warmup)
+    pairs = attended_pairs(wl)
+    flops = 4.0 * wl.head_dim * pairs
+    tokens = wl.batch * wl.seq_len
+    kern = "attn_rows"
+    kms = stage_ms[kern]
+    achieved = flops / (kms * 1e-3) / 1e12
+    alg_bytes = 2 * (2 * wl.batch * wl.n_q_heads * wl.seq_len * wl.head_dim) \
+        + 2 * (2 * wl.batch * wl.n_kv_heads * wl.seq_len * wl.head_dim) \
+        + 4 * wl.batch * wl.n_q_heads * wl.seq_len
+    result = {
+        "metric": "prefill tokens/sec and attended-FLOP TFLOP/s (% of bf16 MFMA peak), 1 GPU",
+        "value": tokens / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 q/k/v, resident in HBM)",
+        "config": {"workload": wl.name, "batch": wl.batch, "n_q_heads": wl.n_q_heads,
+                   "n_kv_heads": wl.n_kv_heads, "seq_len": wl.seq_len,
+                   "head_dim": wl.head_dim, "window": wl.window, "causal": True},
+        "attended_tflops": flops / (ms * 1e-3) / 1e12,
+        "pct_of_bf16_peak": 100.0 * flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+        "attended_flops_per_step": flops,
+        "roofline": {"bound": "mfma", "kernel": "attn_rows_kernel<80,1>",
+                     "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": load_traffic(alg_bytes),
+                     "algorithmic_bytes": alg_bytes, "kernel_ms": kms},
+        "stage_ms": stage_ms,
+    }
+    if not args.no_extra:
+        extra = {}
+        for idx in (1, 2, 4):
+            ewl = W.WORKLOADS[idx]
+            print(f"[bench] workload {ewl.name}", file=sys.stderr, flush=True)
+            _, ems, est, bsel = time_workload(ewl, idx, dev, args.extra_steps, 2, want_sel=True)
+            ep = attended_pairs(ewl, bsel)
+            ef = 4.0 * ewl.head_dim * ep
+            extra[ewl.name] = {"ms_per_step": ems,
+                               "tokens_per_s": ewl.batch * ewl.seq_len / (ems * 1e-3),
+                               "attended_tflops": ef / (ems * 1e-3) / 1e12,
+                               "pct_of_bf16_peak": 100 * ef / (ems * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                               "stage_ms": est}
+        result["workloads"] = extra
+    if not args.no_cpu:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

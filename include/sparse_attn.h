@@ -1,0 +1,137 @@
+/*
+ * sparse_attn.h -- C ABI of the MI355X (gfx950) causal sparse-attention
+ * prefill library.
+ *
+ * The operation (one call computes all of it):
+ *
+ *   For query i of head h (block b = i / B, kv head g = h / (Hq/Hkv)):
+ *   1. Block gate, when top_k > 0 [MoBA summary page, "블록 분할과 top-k
+ *      게이팅" and "인과성 보존"]: each earlier block c < b is scored by
+ *      s_c = <q_i, mean of the B keys of block c> (unscaled); the own block b
+ *      is always kept and takes one of the top_k slots; the min(top_k-1, b)
+ *      best earlier blocks are kept, a tie going to the lower block id.
+ *   2. Token gate, when token_top_k > 0 [Naive-N0.5-Flash page, "SWA와 DSA를
+ *      결합한 어텐션"]: each earlier token j < i is scored by
+ *      <idx_q_i, idx_k_j> (one indexer head shared by all query heads); the
+ *      min(token_top_k, i) best are kept, a tie going to the lower token id.
+ *   3. One softmax over the union A(i) = { j <= i : (window > 0 and
+ *      i - j < window) or block(j) kept or token j kept } [Bit-Axon
+ *      "SWA + MoE" page, "어텐션 공식" and "슬라이딩 윈도우 마스크"], logits
+ *      softmax_scale * <q_i, k_j>, plus -- when sink != NULL -- one extra
+ *      logit sink[h] (not scaled) whose value vector is zero.
+ *      out_i = sum_j p_j v_j,  lse_i = natural log of the softmax
+ *      normaliser (sink included).
+ *
+ * Layouts (row-major, contiguous, device memory):
+ *   q, out  [batch, n_q_heads,  seq_len, head_dim]   dtype cfg->dtype
+ *   k, v    [batch, n_kv_heads, seq_len, head_dim]   dtype cfg->dtype
+ *   lse     [batch, n_q_heads,  seq_len]              fp32
+ *   idx_q, idx_k [batch, seq_len, index_dim]          dtype cfg->dtype
+ *   sink    [n_q_heads]                               fp32
+ *   block_sel_out [batch, n_q_heads, seq_len, top_k]  int32: kept block ids
+ *           ascending (the own block is the last valid one), then -1.
+ *   token_sel_out [batch, seq_len, token_top_k]       int32: kept token ids
+ *           ascending, then -1.
+ *
+ * Ownership: the caller owns and allocates every buffer, the workspace
+ * included (size from sparse_attn_workspace_bytes).  The library allocates
+ * no device memory, keeps no per-call state, never synchronises, and
+ * enqueues all work on cfg->stream (a hipStream_t; NULL = the default
+ * stream).  Calls are reentrant for distinct workspaces.
+ *
+ * Errors: every entry point returns SA_OK (0) or a negative SA_E_* code.
+ * All argument checks happen before anything is enqueued, so every code but
+ * SA_E_HIP is returned without touching the GPU.  On error, out, lse and
+ * the selection outputs are unspecified.
+ */
+#ifndef SPARSE_ATTN_H
+#define SPARSE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPARSE_ATTN_ABI_VERSION 1
+
+typedef enum {
+    SA_BF16 = 0, /* bfloat16 inputs and out; fp32 accumulation */
+    SA_F32 = 1   /* float32 inputs and out; each operand split into two
+                    bf16 terms on the matrix cores (about 16 mantissa bits) */
+} sa_dtype;
+
+enum {
+    SA_OK = 0,
+    SA_E_INVALID_ARG = -1,      /* NULL pointer, bad struct_size, negative size */
+    SA_E_SHAPE = -2,            /* seq_len % block_size, Hq % Hkv, top_k > n, ... */
+    SA_E_UNSUPPORTED_HEAD_DIM = -3, /* head_dim not in {64, 80, 128}, or index_dim != 64 */
+    SA_E_NO_SELF = -4,          /* window == 0 and top_k == 0: no key is guaranteed */
+    SA_E_ALIGNMENT = -5,        /* a tensor pointer is not 16-byte aligned */
+    SA_E_WORKSPACE_TOO_SMALL = -6,
+    SA_E_HIP = -7,              /* a kernel launch failed (hipGetLastError) */
+    SA_E_UNSUPPORTED = -8       /* a combination outside the documented limits */
+};
+
+typedef struct {
+    uint32_t struct_size;   /* = sizeof(sparse_attn_cfg) */
+    int32_t batch;
+    int32_t n_q_heads;      /* Hq, a multiple of n_kv_heads (GQA: h -> h / (Hq/Hkv)) */
+    int32_t n_kv_heads;     /* Hkv; Hq/Hkv <= 16 */
+    int32_t seq_len;        /* N >= 1 */
+    int32_t head_dim;       /* d in {64, 80, 128} */
+    int32_t dtype;          /* sa_dtype */
+    int32_t block_size;     /* B: a multiple of 64 dividing N; ignored if top_k == 0 */
+    int32_t top_k;          /* blocks kept per query, own block included; 0 = no
+                               block gate; 1 <= top_k <= min(33, N/B) */
+    int32_t window;         /* w >= 0: attend iff 0 <= i-j < w; 0 = no window */
+    int32_t token_top_k;    /* 0 = no token gate; else tokens kept per query */
+    int32_t index_dim;      /* indexer head dim (64) when token_top_k > 0 */
+    const void* idx_q;      /* indexer queries, or NULL when token_top_k == 0 */
+    const void* idx_k;      /* indexer keys, or NULL when token_top_k == 0 */
+    const float* sink;      /* per-head sink logits, or NULL */
+    float softmax_scale;    /* logit scale; 0 -> 1/sqrt(head_dim) */
+    void* workspace;        /* device scratch, >= sparse_attn_workspace_bytes */
+    size_t workspace_bytes;
+    int32_t* block_sel_out; /* optional copy-out of the block selection, or NULL */
+    int32_t* token_sel_out; /* optional copy-out of the token selection, or NULL */
+    void* stream;           /* hipStream_t, NULL = default stream */
+} sparse_attn_cfg;
+
+/* Bytes of device workspace sparse_attn_fwd needs for this configuration
+ * (workspace fields of cfg are ignored).  Host only; touches no GPU. */
+int sparse_attn_workspace_bytes(const sparse_attn_cfg* cfg, size_t* bytes);
+
+/* The whole prefill forward: enqueues every stage on cfg->stream and returns
+ * without waiting.  q, k, v, out, lse are device pointers (16-byte aligned). */
+int sparse_attn_fwd(const void* q, const void* k, const void* v,
+                    const sparse_attn_cfg* cfg, void* out, float* lse);
+
+/* The block mean-pool stage alone [MoBA summary page, implementation figure:
+ * partition into blocks, mean pooling]: kbar[b, g, c, :] = mean of the
+ * block_size keys of block c, fp32, [batch, n_kv_heads, seq_len/block_size,
+ * head_dim].  Uses no workspace.  Same checks as sparse_attn_fwd. */
+int sparse_attn_block_pool(const void* k, const sparse_attn_cfg* cfg, float* kbar);
+
+/* Static description of an error code. */
+const char* sparse_attn_strerror(int status);
+
+/* Optional per-stage timing for benchmarks.  sparse_attn_set_timing(1)
+ * starts a new record (creating the HIP events on first use); from then on
+ * every sparse_attn_fwd / sparse_attn_block_pool call records an event pair
+ * on cfg->stream around each kernel it enqueues, up to 1024 records.
+ * sparse_attn_set_timing(0) stops recording.  sparse_attn_stage_times waits
+ * for the recorded events and writes up to `capacity` stage names (static
+ * strings) and durations in milliseconds, in enqueue order; *n_stages
+ * receives the number recorded.  The record is process-wide: time one caller
+ * at a time. */
+int sparse_attn_set_timing(int enable);
+int sparse_attn_stage_times(int32_t* n_stages, const char** names, float* ms,
+                            int32_t capacity);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_ATTN_H */

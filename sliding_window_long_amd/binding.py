@@ -1,0 +1,243 @@
+"""ctypes binding of libsparse_attn.so.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of the library.  torch provides device memory (outputs and
+workspace) and the current HIP stream.  There is no fallback: if the shared
+library is missing, importing any entry point raises.
+
+The names mirror the C ABI of ``include/sparse_attn.h``; ``forward`` is the
+convenience wrapper that allocates outputs and workspace and calls
+``sparse_attn_fwd`` on torch's current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsparse_attn.so")
+
+SA_BF16, SA_F32 = 0, 1
+SA_OK = 0
+ERROR_CODES = {
+    -1: "SA_E_INVALID_ARG", -2: "SA_E_SHAPE", -3: "SA_E_UNSUPPORTED_HEAD_DIM",
+    -4: "SA_E_NO_SELF", -5: "SA_E_ALIGNMENT", -6: "SA_E_WORKSPACE_TOO_SMALL",
+    -7: "SA_E_HIP", -8: "SA_E_UNSUPPORTED",
+}
+# Every symbol the C header declares.
+EXPORTS = ("sparse_attn_workspace_bytes", "sparse_attn_fwd", "sparse_attn_block_pool",
+           "sparse_attn_strerror", "sparse_attn_set_timing", "sparse_attn_stage_times")
+
+
+class SparseAttnCfg(ctypes.Structure):
+    """Mirror of ``sparse_attn_cfg``."""
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32), ("seq_len", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("block_size", ctypes.c_int32), ("top_k", ctypes.c_int32),
+        ("window", ctypes.c_int32), ("token_top_k", ctypes.c_int32),
+        ("index_dim", ctypes.c_int32),
+        ("idx_q", ctypes.c_void_p), ("idx_k", ctypes.c_void_p),
+        ("sink", ctypes.c_void_p), ("softmax_scale", ctypes.c_float),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("block_sel_out", ctypes.c_void_p), ("token_sel_out", ctypes.c_void_p),
+        ("stream", ctypes.c_void_p),
+    ]
+
+
+class SparseAttnError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {ERROR_CODES.get(code, code)} ({sparse_attn_strerror(code)})")
+
+
+_lib = None
+
+
+def load_library():
+    """Load libsparse_attn.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m sliding_window_long_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    lib.sparse_attn_workspace_bytes.argtypes = [P(SparseAttnCfg), P(ctypes.c_size_t)]
+    lib.sparse_attn_workspace_bytes.restype = ctypes.c_int
+    lib.sparse_attn_fwd.argtypes = [ctypes.c_void_p] * 3 + [P(SparseAttnCfg), ctypes.c_void_p,
+                                                            ctypes.c_void_p]
+    lib.sparse_attn_fwd.restype = ctypes.c_int
+    lib.sparse_attn_block_pool.argtypes = [ctypes.c_void_p, P(SparseAttnCfg), ctypes.c_void_p]
+    lib.sparse_attn_block_pool.restype = ctypes.c_int
+    lib.sparse_attn_strerror.argtypes = [ctypes.c_int]
+    lib.sparse_attn_strerror.restype = ctypes.c_char_p
+    lib.sparse_attn_set_timing.argtypes = [ctypes.c_int]
+    lib.sparse_attn_set_timing.restype = ctypes.c_int
+    lib.sparse_attn_stage_times.argtypes = [P(ctypes.c_int32), P(ctypes.c_char_p),
+                                            P(ctypes.c_float), ctypes.c_int32]
+    lib.sparse_attn_stage_times.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+@dataclass
+class Params:
+    """Shape and method parameters of one call (see the C header)."""
+    batch: int
+    n_q_heads: int
+    n_kv_heads: int
+    seq_len: int
+    head_dim: int
+    dtype: int = SA_BF16
+    block_size: int = 0
+    top_k: int = 0
+    window: int = 0
+    token_top_k: int = 0
+    index_dim: int = 0
+    softmax_scale: float = 0.0
+
+    def cfg(self) -> SparseAttnCfg:
+        c = SparseAttnCfg()
+        c.struct_size = ctypes.sizeof(SparseAttnCfg)
+        for f in ("batch", "n_q_heads", "n_kv_heads", "seq_len", "head_dim", "dtype",
+                  "block_size", "top_k", "window", "token_top_k", "index_dim"):
+            setattr(c, f, int(getattr(self, f)))
+        c.softmax_scale = float(self.softmax_scale)
+        return c
+
+
+def sparse_attn_strerror(code: int) -> str:
+    return load_library().sparse_attn_strerror(int(code)).decode()
+
+
+def _check(rc: int, where: str):
+    if rc != SA_OK:
+        raise SparseAttnError(rc, where)
+
+
+def sparse_attn_workspace_bytes(cfg: SparseAttnCfg) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().sparse_attn_workspace_bytes(ctypes.byref(cfg), ctypes.byref(n)),
+           "sparse_attn_workspace_bytes")
+    return n.value
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def sparse_attn_fwd(q, k, v, cfg: SparseAttnCfg, out, lse) -> None:
+    _check(load_library().sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), ctypes.byref(cfg),
+                                          _ptr(out), _ptr(lse)), "sparse_attn_fwd")
+
+
+def sparse_attn_block_pool(k, cfg: SparseAttnCfg, kbar) -> None:
+    _check(load_library().sparse_attn_block_pool(_ptr(k), ctypes.byref(cfg), _ptr(kbar)),
+           "sparse_attn_block_pool")
+
+
+def sparse_attn_set_timing(enable: bool) -> None:
+    _check(load_library().sparse_attn_set_timing(1 if enable else 0), "sparse_attn_set_timing")
+
+
+def sparse_attn_stage_times(capacity: int = 16) -> list[tuple[str, float]]:
+    n = ctypes.c_int32(0)
+    names = (ctypes.c_char_p * capacity)()
+    ms = (ctypes.c_float * capacity)()
+    _check(load_library().sparse_attn_stage_times(ctypes.byref(n), names, ms, capacity),
+           "sparse_attn_stage_times")
+    return [(names[i].decode(), float(ms[i])) for i in range(min(n.value, capacity))]
+
+
+# ---------------------------------------------------------------------------
+# torch-facing convenience wrapper
+# ---------------------------------------------------------------------------
+def params_for(q, k, *, block_size=0, top_k=0, window=0, token_top_k=0, index_dim=0,
+               scale=None) -> Params:
+    import torch
+    Bt, Hq, N, d = q.shape
+    dt = {torch.bfloat16: SA_BF16, torch.float32: SA_F32}.get(q.dtype)
+    if dt is None:
+        raise TypeError(f"q dtype {q.dtype} not supported (bfloat16 or float32)")
+    return Params(Bt, Hq, k.shape[1], N, d, dt, block_size, top_k, window, token_top_k,
+                  index_dim, 0.0 if scale is None else float(scale))
+
+
+class Workspace:
+    """A reusable device workspace (grown on demand, never shrunk)."""
+
+    def __init__(self):
+        self.buf = None
+
+    def get(self, nbytes: int, device):
+        import torch
+        if nbytes == 0:
+            return None
+        if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
+            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        return self.buf
+
+
+_default_ws = Workspace()
+
+
+def forward(q, k, v, *, block_size=0, top_k=0, window=0, idx_q=None, idx_k=None,
+            token_top_k=0, sink=None, scale=None, return_selection=False,
+            workspace: Workspace | None = None, out=None, lse=None):
+    """Causal sparse-attention prefill on q's device and torch's current
+    stream.  Returns (out, lse) or, with return_selection,
+    (out, lse, block_sel, token_sel)."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous device tensor")
+        if t.dtype != q.dtype:
+            raise TypeError("q, k, v must share one dtype")
+    index_dim = idx_q.shape[-1] if idx_q is not None else 0
+    p = params_for(q, k, block_size=block_size, top_k=top_k, window=window,
+                   token_top_k=token_top_k, index_dim=index_dim, scale=scale)
+    cfg = p.cfg()
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    bsel = tsel = None
+    if return_selection and top_k > 0:
+        bsel = torch.empty(q.shape[:3] + (top_k,), dtype=torch.int32, device=dev)
+        cfg.block_sel_out = bsel.data_ptr()
+    if return_selection and token_top_k > 0:
+        tsel = torch.empty((q.shape[0], q.shape[2], token_top_k), dtype=torch.int32, device=dev)
+        cfg.token_sel_out = tsel.data_ptr()
+    if idx_q is not None:
+        cfg.idx_q, cfg.idx_k = idx_q.data_ptr(), idx_k.data_ptr()
+    if sink is not None:
+        if sink.dtype != torch.float32 or not sink.is_cuda:
+            raise TypeError("sink must be a float32 device tensor")
+        cfg.sink = sink.data_ptr()
+    nbytes = sparse_attn_workspace_bytes(cfg)
+    ws = (workspace or _default_ws).get(nbytes, dev)
+    cfg.workspace = None if ws is None else ws.data_ptr()
+    cfg.workspace_bytes = nbytes
+    cfg.stream = torch.cuda.current_stream(dev).cuda_stream
+    sparse_attn_fwd(q, k, v, cfg, out, lse)
+    if return_selection:
+        return out, lse, bsel, tsel
+    return out, lse
+
+
+def block_pool(k, block_size: int):
+    """Mean-pooled keys [Bt, Hkv, N/B, d] in fp32 (the pooling stage alone)."""
+    import torch
+    Bt, Hkv, N, d = k.shape
+    p = params_for(k, k, block_size=block_size, top_k=1)
+    cfg = p.cfg()
+    cfg.stream = torch.cuda.current_stream(k.device).cuda_stream
+    kbar = torch.empty((Bt, Hkv, N // max(block_size, 1), d), dtype=torch.float32, device=k.device)
+    sparse_attn_block_pool(k, cfg, kbar)
+    return kbar

@@ -1,0 +1,312 @@
+// sa_api.hip -- C ABI: argument checks, workspace plan, launch sequence.
+//
+// Stage order of one forward call (all on cfg->stream, no host sync):
+//   [fp32 only] split q, k, v into hi/lo bf16 planes
+//   [block gate] mean-pool -> gate (scores + top-k) -> compaction of far
+//                blocks -> far-block attention partials
+//   query-centric attention over window / own block / near kept blocks,
+//   merging the far partials and the sink -> out, lse
+#include "sparse_attn.h"
+#include "sa_internal.hpp"
+
+#include <math.h>
+#include <string.h>
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kRowsPerChunk = 128;     // entries per far-block workgroup
+constexpr int kMaxStages = 1024;   // stage records kept per timing session
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Plan {
+    int Bt, Hq, Hkv, N, D, G;
+    bool f32;
+    bool gate;
+    int B, n, top_k, span, kslots, idx_bits, lists;
+    bool far;
+    long long max_entries;
+    int max_chunks;
+    float scale;
+    // workspace regions (byte offsets)
+    size_t o_split, o_kb3, o_sel, o_count, o_cursor, o_listoff, o_nchunks, o_chunk_list,
+        o_chunk_start, o_entries, o_part_o, o_part_lse, total;
+};
+
+bool misaligned(const void* p, size_t a) { return p && (reinterpret_cast<uintptr_t>(p) % a) != 0; }
+
+int make_plan(const sparse_attn_cfg* c, Plan* p) {
+    if (!c || c->struct_size != sizeof(sparse_attn_cfg)) return SA_E_INVALID_ARG;
+    if (c->batch < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 || c->seq_len < 1)
+        return SA_E_INVALID_ARG;
+    if (c->dtype != SA_BF16 && c->dtype != SA_F32) return SA_E_INVALID_ARG;
+    if (c->window < 0 || c->top_k < 0 || c->token_top_k < 0 || c->block_size < 0)
+        return SA_E_INVALID_ARG;
+    if (!(c->softmax_scale >= 0.f) || isinf(c->softmax_scale)) return SA_E_INVALID_ARG;
+    if (c->head_dim != 64 && c->head_dim != 80 && c->head_dim != 128)
+        return SA_E_UNSUPPORTED_HEAD_DIM;
+    if (c->n_q_heads % c->n_kv_heads) return SA_E_SHAPE;
+    if (c->n_q_heads / c->n_kv_heads > 16) return SA_E_UNSUPPORTED;
+    if (c->window == 0 && c->top_k == 0) return SA_E_NO_SELF;
+    if (c->token_top_k > 0) return SA_E_UNSUPPORTED;   // token gate: not built yet
+
+    Plan& P = *p;
+    memset(&P, 0, sizeof(P));
+    P.Bt = c->batch; P.Hq = c->n_q_heads; P.Hkv = c->n_kv_heads; P.N = c->seq_len;
+    P.D = c->head_dim; P.G = P.Hq / P.Hkv;
+    P.f32 = c->dtype == SA_F32;
+    P.scale = c->softmax_scale > 0.f ? c->softmax_scale : 1.0f / sqrtf((float)P.D);
+    const long long rows = (long long)P.Bt * P.Hq * P.N;
+    const size_t esz = P.f32 ? 4 : 2;
+    if (rows * P.D * (long long)esz > (1LL << 40)) return SA_E_UNSUPPORTED;
+
+    P.gate = c->top_k > 0;
+    if (P.gate) {
+        P.B = c->block_size;
+        if (P.B < 64 || P.B % 64 || P.N % P.B) return SA_E_SHAPE;
+        P.n = P.N / P.B;
+        P.top_k = c->top_k;
+        if (P.top_k > P.n) return SA_E_SHAPE;
+        if (P.top_k > 33 || P.n > 4096) return SA_E_UNSUPPORTED;
+        P.idx_bits = 1;
+        while ((1 << P.idx_bits) < P.n) ++P.idx_bits;
+        // Blocks within `span` below the own block overlap the window span of
+        // some row of the block and are attended by the query-centric pass.
+        long long span = 0;
+        if (c->window > 0) span = ((long long)c->window - 1 + P.B - 1) / P.B;
+        if (span > P.n) span = P.n;
+        if (span > 32 && c->window < P.N) return SA_E_UNSUPPORTED;
+        P.span = (int)span;
+        P.kslots = P.top_k > 1 ? P.top_k - 1 : 1;
+        P.lists = P.Bt * P.Hkv * P.n;
+        long long per_head = 0;   // far entries per head, upper bound
+        for (int b = 0; b < P.n; ++b) {
+            long long fc = b - P.span;
+            if (fc < 0) fc = 0;
+            per_head += (fc < P.top_k - 1 ? fc : P.top_k - 1) * (long long)P.B;
+        }
+        P.max_entries = per_head * P.Bt * P.Hq;
+        P.far = P.max_entries > 0;
+        if ((long long)P.N * P.G * P.kslots >= (1LL << 31) || P.max_entries >= (1LL << 31))
+            return SA_E_UNSUPPORTED;
+        long long mc = (P.max_entries + kRowsPerChunk - 1) / kRowsPerChunk + P.lists;
+        mc = (mc + 7) / 8 * 8;
+        P.max_chunks = (int)mc;
+    }
+
+    size_t off = 0;
+    auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
+    const size_t nq = (size_t)rows * P.D, nkv = (size_t)P.Bt * P.Hkv * P.N * P.D;
+    P.o_split = take(P.f32 ? 2 * (nq + 2 * nkv) * 2 : 0);
+    if (P.gate) {
+        P.o_kb3 = take((size_t)3 * P.lists * P.D * 2);
+        P.o_sel = take((size_t)rows * P.top_k * 4);
+        if (P.far) {
+            P.o_count = take((size_t)P.lists * 4);
+            P.o_cursor = take((size_t)P.lists * 4);
+            P.o_listoff = take((size_t)(P.lists + 1) * 4);
+            P.o_nchunks = take(4);
+            P.o_chunk_list = take((size_t)P.max_chunks * 4);
+            P.o_chunk_start = take((size_t)P.max_chunks * 4);
+            P.o_entries = take((size_t)P.max_entries * 4);
+            P.o_part_o = take((size_t)rows * P.kslots * P.D * 2);
+            P.o_part_lse = take((size_t)rows * P.kslots * 4);
+        }
+    }
+    P.total = off;
+    return SA_OK;
+}
+
+// ----------------------------------------------------------------------------
+// Stage timing (benchmark aid).
+// ----------------------------------------------------------------------------
+struct Timing {
+    bool on = false;
+    bool created = false;
+    int n = 0;
+    const char* names[kMaxStages];
+    hipEvent_t ev[kMaxStages][2];
+};
+Timing g_timing;
+
+struct StageScope {
+    int idx = -1;
+    hipStream_t s;
+    StageScope(const char* name, hipStream_t st) : s(st) {
+        if (!g_timing.on || g_timing.n >= kMaxStages) return;
+        idx = g_timing.n++;
+        g_timing.names[idx] = name;
+        hipEventRecord(g_timing.ev[idx][0], s);
+    }
+    ~StageScope() {
+        if (idx >= 0) hipEventRecord(g_timing.ev[idx][1], s);
+    }
+};
+
+}  // namespace
+
+extern "C" {
+
+const char* sparse_attn_strerror(int status) {
+    switch (status) {
+        case SA_OK: return "success";
+        case SA_E_INVALID_ARG: return "invalid argument (null pointer, struct_size, negative size or scale)";
+        case SA_E_SHAPE: return "shape mismatch (block_size must be a multiple of 64 dividing seq_len; n_q_heads a multiple of n_kv_heads; top_k <= seq_len/block_size)";
+        case SA_E_UNSUPPORTED_HEAD_DIM: return "unsupported head_dim (64, 80 or 128) or index_dim (64)";
+        case SA_E_NO_SELF: return "window == 0 and top_k == 0: a query would have no guaranteed key";
+        case SA_E_ALIGNMENT: return "tensor pointer not aligned (16 bytes for q/k/v/out/idx/workspace, 4 for lse/sink/selections)";
+        case SA_E_WORKSPACE_TOO_SMALL: return "workspace smaller than sparse_attn_workspace_bytes";
+        case SA_E_HIP: return "HIP kernel launch failed";
+        case SA_E_UNSUPPORTED: return "configuration outside the supported limits";
+        default: return "unknown status";
+    }
+}
+
+int sparse_attn_workspace_bytes(const sparse_attn_cfg* cfg, size_t* bytes) {
+    if (!bytes) return SA_E_INVALID_ARG;
+    Plan P;
+    const int rc = make_plan(cfg, &P);
+    if (rc != SA_OK) return rc;
+    *bytes = P.total;
+    return SA_OK;
+}
+
+int sparse_attn_set_timing(int enable) {
+    if (enable && !g_timing.created) {
+        for (int i = 0; i < kMaxStages; ++i)
+            for (int j = 0; j < 2; ++j)
+                if (hipEventCreate(&g_timing.ev[i][j]) != hipSuccess) return SA_E_HIP;
+        g_timing.created = true;
+    }
+    g_timing.on = enable != 0;
+    if (g_timing.on) g_timing.n = 0;
+    return SA_OK;
+}
+
+int sparse_attn_stage_times(int32_t* n_stages, const char** names, float* ms, int32_t capacity) {
+    if (!n_stages) return SA_E_INVALID_ARG;
+    *n_stages = g_timing.created ? g_timing.n : 0;
+    for (int i = 0; i < *n_stages && i < capacity; ++i) {
+        if (hipEventSynchronize(g_timing.ev[i][1]) != hipSuccess) return SA_E_HIP;
+        float t = 0.f;
+        if (hipEventElapsedTime(&t, g_timing.ev[i][0], g_timing.ev[i][1]) != hipSuccess)
+            return SA_E_HIP;
+        if (names) names[i] = g_timing.names[i];
+        if (ms) ms[i] = t;
+    }
+    return SA_OK;
+}
+
+int sparse_attn_block_pool(const void* k, const sparse_attn_cfg* cfg, float* kbar) {
+    Plan P;
+    int rc = make_plan(cfg, &P);
+    if (rc != SA_OK) return rc;
+    if (!P.gate) return SA_E_INVALID_ARG;
+    if (!k || !kbar) return SA_E_INVALID_ARG;
+    if (misaligned(k, 16) || misaligned(kbar, 16)) return SA_E_ALIGNMENT;
+    hipStream_t s = (hipStream_t)cfg->stream;
+    sa::PoolArgs pa{k, P.N, P.B, P.n, kbar, nullptr, 0};
+    StageScope t("block_pool", s);
+    return sa::launch_pool(pa, P.D, P.f32, P.lists, s) == hipSuccess ? SA_OK : SA_E_HIP;
+}
+
+int sparse_attn_fwd(const void* q, const void* k, const void* v, const sparse_attn_cfg* cfg,
+                    void* out, float* lse) {
+    Plan P;
+    int rc = make_plan(cfg, &P);
+    if (rc != SA_OK) return rc;
+    if (!q || !k || !v || !out || !lse) return SA_E_INVALID_ARG;
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(out, 16) ||
+        misaligned(cfg->workspace, 16) || misaligned(lse, 4) || misaligned(cfg->sink, 4) ||
+        misaligned(cfg->block_sel_out, 4) || misaligned(cfg->token_sel_out, 4))
+        return SA_E_ALIGNMENT;
+    if (P.total > 0 && (!cfg->workspace || cfg->workspace_bytes < P.total))
+        return SA_E_WORKSPACE_TOO_SMALL;
+
+    hipStream_t s = (hipStream_t)cfg->stream;
+    char* ws = (char*)cfg->workspace;
+    auto ok = [](hipError_t e) { return e == hipSuccess; };
+
+    // Operand planes: bf16 inputs are used in place; fp32 inputs are split.
+    const uint16_t* qp[2] = {(const uint16_t*)q, nullptr};
+    const uint16_t* kp[2] = {(const uint16_t*)k, nullptr};
+    const uint16_t* vp[2] = {(const uint16_t*)v, nullptr};
+    const int split = P.f32 ? 2 : 1;
+    if (P.f32) {
+        const size_t nq = (size_t)P.Bt * P.Hq * P.N * P.D, nkv = (size_t)P.Bt * P.Hkv * P.N * P.D;
+        uint16_t* base = (uint16_t*)(ws + P.o_split);
+        uint16_t* qh = base; uint16_t* ql = qh + nq;
+        uint16_t* kh = ql + nq; uint16_t* kl = kh + nkv;
+        uint16_t* vh = kl + nkv; uint16_t* vl = vh + nkv;
+        StageScope t("split_f32", s);
+        if (!ok(sa::launch_split_f32((const float*)q, qh, ql, nq, s)) ||
+            !ok(sa::launch_split_f32((const float*)k, kh, kl, nkv, s)) ||
+            !ok(sa::launch_split_f32((const float*)v, vh, vl, nkv, s)))
+            return SA_E_HIP;
+        qp[0] = qh; qp[1] = ql; kp[0] = kh; kp[1] = kl; vp[0] = vh; vp[1] = vl;
+    }
+
+    int32_t* sel = nullptr;
+    uint16_t* part_o = nullptr;
+    float* part_lse = nullptr;
+    if (P.gate) {
+        sel = cfg->block_sel_out ? cfg->block_sel_out : (int32_t*)(ws + P.o_sel);
+        uint16_t* kb3 = (uint16_t*)(ws + P.o_kb3);
+        const size_t plane = (size_t)P.lists * P.D;
+        {
+            sa::PoolArgs pa{k, P.N, P.B, P.n, nullptr, kb3, plane};
+            StageScope t("block_pool", s);
+            if (!ok(sa::launch_pool(pa, P.D, P.f32, P.lists, s))) return SA_E_HIP;
+        }
+        {
+            sa::GateArgs ga{{qp[0], qp[1]}, kb3, plane, sel, P.Bt, P.Hq, P.Hkv, P.N, P.B, P.n,
+                            P.top_k, P.idx_bits};
+            StageScope t("block_gate", s);
+            if (!ok(sa::launch_gate(ga, P.D, split, s))) return SA_E_HIP;
+        }
+        if (P.far) {
+            part_o = (uint16_t*)(ws + P.o_part_o);
+            part_lse = (float*)(ws + P.o_part_lse);
+            sa::CompactArgs ca{};
+            ca.sel = sel; ca.Bt = P.Bt; ca.Hq = P.Hq; ca.Hkv = P.Hkv; ca.N = P.N; ca.B = P.B;
+            ca.n = P.n; ca.top_k = P.top_k; ca.span = P.span; ca.kslots = P.kslots;
+            ca.count = (int32_t*)(ws + P.o_count);
+            ca.cursor = (int32_t*)(ws + P.o_cursor);
+            ca.list_off = (int32_t*)(ws + P.o_listoff);
+            ca.entries = (int32_t*)(ws + P.o_entries);
+            ca.chunk_list = (int32_t*)(ws + P.o_chunk_list);
+            ca.chunk_start = (int32_t*)(ws + P.o_chunk_start);
+            ca.n_chunks = (int32_t*)(ws + P.o_nchunks);
+            ca.max_chunks = P.max_chunks;
+            ca.rows_per_chunk = kRowsPerChunk;
+            {
+                StageScope t("compact", s);
+                if (!ok(sa::launch_compact(ca, s))) return SA_E_HIP;
+            }
+            sa::BlocksArgs ba{};
+            for (int i = 0; i < 2; ++i) { ba.q[i] = qp[i]; ba.k[i] = kp[i]; ba.v[i] = vp[i]; }
+            ba.Bt = P.Bt; ba.Hq = P.Hq; ba.Hkv = P.Hkv; ba.N = P.N; ba.B = P.B; ba.n = P.n;
+            ba.scale = P.scale;
+            ba.chunk_list = ca.chunk_list; ba.chunk_start = ca.chunk_start;
+            ba.list_off = ca.list_off; ba.entries = ca.entries; ba.n_chunks = ca.n_chunks;
+            ba.part_o = part_o; ba.part_lse = part_lse; ba.kslots = P.kslots;
+            StageScope t("attn_far_blocks", s);
+            if (!ok(sa::launch_blocks(ba, P.D, split, P.max_chunks, s))) return SA_E_HIP;
+        }
+    }
+
+    sa::RowsArgs ra{};
+    for (int i = 0; i < 2; ++i) { ra.q[i] = qp[i]; ra.k[i] = kp[i]; ra.v[i] = vp[i]; }
+    ra.out = out; ra.lse = lse;
+    ra.Bt = P.Bt; ra.Hq = P.Hq; ra.Hkv = P.Hkv; ra.N = P.N;
+    ra.scale = P.scale; ra.window = cfg->window;
+    ra.gate = P.gate ? 1 : 0; ra.B = P.B; ra.top_k = P.top_k; ra.span = P.span;
+    ra.sel = sel; ra.part_o = part_o; ra.part_lse = part_lse; ra.kslots = P.kslots;
+    ra.sink = cfg->sink; ra.out_f32 = P.f32 ? 1 : 0;
+    StageScope t("attn_rows", s);
+    if (!ok(sa::launch_rows(ra, P.D, split, s))) return SA_E_HIP;
+    return SA_OK;
+}
+
+}  // extern "C"

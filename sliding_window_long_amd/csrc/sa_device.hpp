@@ -1,0 +1,52 @@
+// sa_device.hpp -- device-side building blocks shared by the HIP kernels of
+// the sparse-attention prefill (gfx950 / CDNA4 only).
+//
+// Matrix-core convention used throughout (v_mfma_f32_32x32x16_bf16,
+// wave64): for D = A(32x16) * B(16x32) + C, lane l supplies row (l % 32) of
+// A and column (l % 32) of B, each as 8 consecutive contraction elements
+// starting at 8 * (l / 32); it receives D[8*(v/4) + 4*(l/32) + v%4][l % 32]
+// in accumulator register v (v = 0..15).
+//
+// Attention is computed transposed, S^T = K * Q^T, so that a lane owns one
+// query column: row statistics of the softmax stay in the lane (plus its
+// partner lane l ^ 32), and the probabilities it holds are already laid out
+// as the B operand of O^T = V^T * P^T.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Value of lane (l ^ 32).
+__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
+
+// fp32 -> bf16 with round-to-nearest-even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ bf16x8 to_bf16x8(const float* p) {
+    bf16x8 r;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) r[t] = (__bf16)p[t];
+    return r;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
+
+}  // namespace sa

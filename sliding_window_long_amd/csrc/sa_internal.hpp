@@ -1,0 +1,97 @@
+// sa_internal.hpp -- launch descriptors shared by the host planner and the
+// kernels (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sa {
+
+// Query-centric attention over the "near" key range of a row tile: the
+// sliding window, the own block and the kept blocks that overlap the window
+// span, then the merge of the far-block partials and of the sink.
+struct RowsArgs {
+    const uint16_t* q[2];   // bf16 planes of q (plane 1 only for split fp32)
+    const uint16_t* k[2];
+    const uint16_t* v[2];
+    void* out;              // bf16 or fp32 (out_f32)
+    float* lse;
+    int Bt, Hq, Hkv, N;
+    float scale;            // softmax scale of the logits
+    int window;             // 0 = off
+    int gate;               // block gating on
+    int B;                  // block size (gate)
+    int top_k;
+    int span;               // blocks below the own block handled here
+    const int32_t* sel;     // [Bt,Hq,N,top_k] kept blocks, ascending, -1 padded
+    const uint16_t* part_o; // fp16 [Bt*Hq*N, kslots, D] far-block partials
+    const float* part_lse;  // [Bt*Hq*N, kslots]
+    int kslots;
+    const float* sink;      // [Hq] or nullptr
+    int out_f32;
+};
+
+// KV-centric attention of one far block against a chunk of gathered rows,
+// writing one normalised partial (o, lse) per entry.
+struct BlocksArgs {
+    const uint16_t* q[2];
+    const uint16_t* k[2];
+    const uint16_t* v[2];
+    int Bt, Hq, Hkv, N, B, n;
+    float scale;
+    const int32_t* chunk_list;   // [grid] list id of each chunk
+    const int32_t* chunk_start;  // [grid] first entry of each chunk
+    const int32_t* list_off;     // [lists+1] entry offsets of the lists
+    const int32_t* entries;      // (i*G + h_local)*kslots + slot
+    const int32_t* n_chunks;     // device count of valid chunks
+    uint16_t* part_o;
+    float* part_lse;
+    int kslots;
+};
+
+// Block mean-pool: kbar (fp32, optional) and the hi/mid/lo bf16 planes of it
+// (optional), both [Bt*Hkv*n, D].
+struct PoolArgs {
+    const void* k;          // bf16 or fp32 keys [Bt, Hkv, N, D]
+    int N, B, n;
+    float* kbar;
+    uint16_t* kb3;          // 3 planes of `plane` elements each
+    size_t plane;
+};
+
+// Block gate: scores against the pooled keys and top-(k-1) earlier blocks.
+struct GateArgs {
+    const uint16_t* q[2];   // bf16 planes of q
+    const uint16_t* kb3;
+    size_t plane;
+    int32_t* sel;           // [Bt, Hq, N, top_k]
+    int Bt, Hq, Hkv, N, B, n, top_k, idx_bits;
+};
+
+// Inversion of the block selection into per-(batch, kv head, block) lists of
+// the rows that keep that block as a far block.
+struct CompactArgs {
+    const int32_t* sel;
+    int Bt, Hq, Hkv, N, B, n, top_k, span, kslots;
+    int32_t* count;         // [lists] zeroed before the count pass
+    int32_t* cursor;        // [lists]
+    int32_t* list_off;      // [lists + 1]
+    int32_t* entries;
+    int32_t* chunk_list;    // [max_chunks]
+    int32_t* chunk_start;   // [max_chunks]
+    int32_t* n_chunks;      // [1]
+    int max_chunks;
+    int rows_per_chunk;
+};
+
+hipError_t launch_pool(const PoolArgs& a, int head_dim, bool f32_in, int lists, hipStream_t s);
+hipError_t launch_gate(const GateArgs& a, int head_dim, int qsplit, hipStream_t s);
+hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
+hipError_t launch_fill_i32(int32_t* p, int32_t value, size_t n, hipStream_t s);
+
+hipError_t launch_rows(const RowsArgs& a, int head_dim, int split, hipStream_t s);
+hipError_t launch_blocks(const BlocksArgs& a, int head_dim, int split, int grid, hipStream_t s);
+hipError_t launch_split_f32(const float* x, uint16_t* hi, uint16_t* lo, size_t n, hipStream_t s);
+
+}  // namespace sa

@@ -1,0 +1,124 @@
+"""CPU tests of the C-ABI library: it loads, exports every symbol the header
+declares, and rejects bad arguments with the documented codes before any
+GPU work.  No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sliding_window_long_amd as sa
+from sliding_window_long_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparse_attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from sliding_window_long_amd.build import build_library
+        build_library()
+    return sa.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sparse_attn_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(sa.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_struct_layout_matches(lib):
+    # The library rejects any struct_size other than its own sizeof.
+    cfg = sa.Params(1, 4, 4, 256, 64, window=16).cfg()
+    assert sa.sparse_attn_workspace_bytes(cfg) == 0
+    cfg.struct_size = ctypes.sizeof(binding.SparseAttnCfg) - 8
+    with pytest.raises(sa.SparseAttnError) as e:
+        sa.sparse_attn_workspace_bytes(cfg)
+    assert e.value.code == -1
+
+
+def code_of(params, **cfg_fields):
+    cfg = params.cfg()
+    for k_, v_ in cfg_fields.items():
+        setattr(cfg, k_, v_)
+    n = ctypes.c_size_t()
+    return sa.load_library().sparse_attn_workspace_bytes(ctypes.byref(cfg), ctypes.byref(n))
+
+
+@pytest.mark.parametrize("params,code", [
+    (sa.Params(0, 4, 4, 256, 64, window=8), -1),                      # batch < 1
+    (sa.Params(1, 4, 4, 256, 64, window=-1, top_k=1, block_size=64), -1),
+    (sa.Params(1, 4, 4, 256, 64, dtype=7, window=8), -1),
+    (sa.Params(1, 4, 4, 256, 96, window=8), -3),                      # head dim
+    (sa.Params(1, 6, 4, 256, 64, window=8), -2),                      # Hq % Hkv
+    (sa.Params(1, 4, 4, 256, 64), -4),                                # no window, no gate
+    (sa.Params(1, 4, 4, 250, 64, block_size=64, top_k=2), -2),        # N % B
+    (sa.Params(1, 4, 4, 256, 64, block_size=32, top_k=2), -2),        # B % 64
+    (sa.Params(1, 4, 4, 256, 64, block_size=64, top_k=5), -2),        # top_k > n
+    (sa.Params(1, 34, 1, 256, 64, window=8), -8),                     # group > 16
+    (sa.Params(1, 4, 4, 64 * 40, 64, block_size=64, top_k=34), -8),   # top_k > 33
+    (sa.Params(1, 4, 4, 256, 64, window=8, softmax_scale=-1.0), -1),
+])
+def test_invalid_configs(lib, params, code):
+    assert code_of(params) == code
+
+
+def test_valid_configs(lib):
+    for p in (sa.Params(1, 1, 1, 512, 64, dtype=sa.SA_F32, block_size=64, top_k=3),
+              sa.Params(2, 8, 4, 4096, 128, block_size=128, top_k=16, window=512),
+              sa.Params(1, 32, 32, 16384, 80, window=4096),
+              sa.Params(1, 32, 8, 131072, 128, block_size=512, top_k=8),
+              sa.Params(1, 3, 3, 77, 80, window=1)):
+        assert code_of(p) == 0
+
+
+def test_workspace_sizes_scale(lib):
+    # window only: no workspace; block gating with far blocks: partials
+    # [rows, top_k-1, d] fp16 dominate.
+    assert sa.sparse_attn_workspace_bytes(sa.Params(1, 32, 32, 16384, 80, window=4096).cfg()) == 0
+    p = sa.Params(1, 32, 8, 131072, 128, block_size=512, top_k=8)
+    rows = 32 * 131072
+    assert sa.sparse_attn_workspace_bytes(p.cfg()) >= rows * 7 * 128 * 2
+
+
+def fwd_code(params, q=0x1000, k=0x2000, v=0x3000, out=0x4000, lse=0x5000, **cfg_fields):
+    """Call sparse_attn_fwd with fake device addresses; only checks that
+    reject the call before any launch are exercised."""
+    cfg = params.cfg()
+    for k_, v_ in cfg_fields.items():
+        setattr(cfg, k_, v_)
+    return sa.load_library().sparse_attn_fwd(
+        ctypes.c_void_p(q), ctypes.c_void_p(k), ctypes.c_void_p(v), ctypes.byref(cfg),
+        ctypes.c_void_p(out), ctypes.c_void_p(lse))
+
+
+def test_fwd_rejects_before_launch(lib):
+    p = sa.Params(1, 4, 4, 256, 64, window=8)
+    assert fwd_code(p, q=0) == -1                       # null q
+    assert fwd_code(p, lse=0) == -1
+    assert fwd_code(p, q=0x1008) == -5                  # misaligned q
+    assert fwd_code(p, out=0x4004) == -5
+    assert fwd_code(p, lse=0x5002) == -5
+    g = sa.Params(1, 4, 4, 256, 64, block_size=64, top_k=2)
+    need = sa.sparse_attn_workspace_bytes(g.cfg())
+    assert need > 0
+    assert fwd_code(g, workspace=0x10000, workspace_bytes=need - 1) == -6
+    assert fwd_code(g, workspace=0, workspace_bytes=0) == -6
+
+
+def test_strerror_covers_codes(lib):
+    for c in range(-8, 1):
+        assert sa.sparse_attn_strerror(c) != "unknown status"
+    assert sa.sparse_attn_strerror(-99) == "unknown status"
+
+
+def test_stage_times_without_timing(lib):
+    assert isinstance(sa.sparse_attn_stage_times(), list)

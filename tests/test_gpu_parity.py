@@ -1,0 +1,160 @@
+"""Parity of the HIP path with the fp64 oracle, through the C ABI.
+
+Small shapes compare every row; the full-size workloads compare sampled rows
+(first/last rows of every head, rows at block and window edges, random rows)
+in the launch configuration the benchmark times.  Tolerances and the
+selection rule are in parity.py."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from parity import check
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import sliding_window_long_amd as sa
+    sa.load_library()
+    return torch.device("cuda:0")
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_device(inp, dev):
+    import torch
+    import sliding_window_long_amd as sa
+    wl = inp.wl
+    t = inp.tensors()
+    g = {k_: (None if v_ is None else v_.to(dev)) for k_, v_ in t.items()}
+    out, lse, bsel, tsel = sa.forward(
+        g["q"], g["k"], g["v"], block_size=wl.block_size, top_k=wl.top_k, window=wl.window,
+        idx_q=g["idx_q"], idx_k=g["idx_k"], token_top_k=wl.token_top_k, sink=g["sink"],
+        return_selection=True)
+    torch.cuda.synchronize()
+    return (out.float().cpu().numpy(), lse.cpu().numpy(),
+            None if bsel is None else bsel.cpu().numpy(),
+            None if tsel is None else tsel.cpu().numpy())
+
+
+def run_and_check(inp, dev, rows=None, label=""):
+    wl = inp.wl
+    log(f"[gpu] {label} {wl}")
+    out, lse, bsel, tsel = run_device(inp, dev)
+    if rows is None:
+        rows = np.arange(wl.batch * wl.n_q_heads * wl.seq_len)
+    rep = check(inp, out, lse, rows, bsel, tsel)
+    log(f"[gpu] {label} {rep}")
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    assert rep.ok(), str(rep)
+    return rep
+
+
+# --- window only (the Bit-Axon SWA shape family) ---------------------------
+@pytest.mark.parametrize("d", [64, 80, 128])
+@pytest.mark.parametrize("N,window", [(1, 4), (63, 1), (300, 17), (300, 64), (513, 1000)])
+def test_window_small(dev, d, N, window):
+    wl = W.Workload(f"swa_small", 2, 4, 2, N, d, "bf16", window=window)
+    run_and_check(W.make_inputs(wl, 7 + d + N), dev, label="window_small")
+
+
+def test_window_one_is_v(dev):
+    wl = W.Workload("swa_w1", 1, 2, 2, 200, 80, "bf16", window=1)
+    inp = W.make_inputs(wl, 3)
+    out, lse, _, _ = run_device(inp, dev)
+    np.testing.assert_array_equal(out, inp.v)
+
+
+def test_bitaxon_reduced_all_rows(dev):
+    wl = W.BITAXON_SWA.replace(n_q_heads=4, n_kv_heads=4, seq_len=2048 + 37, window=512)
+    run_and_check(W.make_inputs(wl, 103), dev, label="bitaxon_reduced")
+
+
+def test_bitaxon_full_sampled(dev):
+    wl = W.BITAXON_SWA
+    run_and_check(W.make_inputs(wl, 103), dev, W.sample_rows(wl, 3000, 1), label="bitaxon_full")
+
+
+# --- block gating -----------------------------------------------------------
+def test_tiny_moba_fp32_all_rows(dev):
+    run_and_check(W.make_inputs(W.TINY_MOBA, 101), dev, label="tiny_moba")
+
+
+def test_bora_hybrid_all_rows(dev):
+    run_and_check(W.make_inputs(W.BORA_HYBRID, 102), dev, label="bora_hybrid")
+
+
+def test_long_moba_reduced_sampled(dev):
+    wl = W.LONG_MOBA.replace(seq_len=W.LONG_MOBA.seq_len // 8)
+    run_and_check(W.make_inputs(wl, 104), dev, W.sample_rows(wl, 4096, 2), label="long_moba_n/8")
+
+
+def test_long_moba_full_sampled(dev):
+    wl = W.LONG_MOBA
+    run_and_check(W.make_inputs(wl, 104), dev, W.sample_rows(wl, 2048, 3), label="long_moba_full")
+
+
+@pytest.mark.parametrize("kw", [
+    dict(block_size=64, top_k=8),                 # k = n: dense causal
+    dict(block_size=64, top_k=1),                 # own block only
+    dict(block_size=64, top_k=3, window=1),       # window inside own block
+    dict(block_size=64, top_k=3, window=100000),  # window covers everything
+    dict(block_size=128, top_k=2, window=200),    # near block partly in window
+    dict(block_size=64, top_k=5, window=70),
+])
+@pytest.mark.parametrize("d", [64, 128])
+def test_gate_edges(dev, kw, d):
+    wl = W.Workload("gate_edge", 2, 4, 2, 512, d, "bf16", block_offsets=True, **kw)
+    run_and_check(W.make_inputs(wl, 11 + d), dev, label=f"gate_edge {kw}")
+
+
+def test_gate_wide_group(dev):
+    wl = W.Workload("gqa16", 1, 16, 1, 1024, 80, "bf16", block_size=128, top_k=4, window=64,
+                    block_offsets=True)
+    run_and_check(W.make_inputs(wl, 12), dev, label="gqa16")
+
+
+def test_fp32_window_and_gate(dev):
+    wl = W.Workload("f32_mix", 1, 2, 1, 384, 128, "f32", block_size=64, top_k=3, window=40,
+                    block_offsets=True)
+    run_and_check(W.make_inputs(wl, 13), dev, label="f32_mix")
+
+
+def test_block_pool_stage(dev):
+    import torch
+    import sliding_window_long_amd as sa
+    for wl, seed in ((W.BORA_HYBRID, 1), (W.TINY_MOBA, 2)):
+        inp = W.make_inputs(wl, seed)
+        kd = inp.tensors()["k"].to(dev)
+        got = sa.block_pool(kd, wl.block_size).cpu().numpy()
+        torch.cuda.synchronize()
+        ref = oracle.block_pool(inp.k, wl.block_size)
+        np.testing.assert_allclose(got, ref, atol=2e-6, rtol=1e-5)
+
+
+def test_deterministic(dev):
+    inp = W.make_inputs(W.BORA_HYBRID, 5)
+    a = run_device(inp, dev)
+    b = run_device(inp, dev)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+
+
+# --- token top-k (Naive SWA + DSA shape) -------------------------------------
+def test_token_topk_not_built(dev):
+    import sliding_window_long_amd as sa
+    wl = W.SWA_TOKEN_TOPK.replace(seq_len=512, n_q_heads=4, n_kv_heads=1, token_top_k=64)
+    p = sa.Params(wl.batch, wl.n_q_heads, wl.n_kv_heads, wl.seq_len, wl.head_dim,
+                  window=wl.window, token_top_k=wl.token_top_k, index_dim=wl.index_dim)
+    with pytest.raises(sa.SparseAttnError):
+        sa.sparse_attn_workspace_bytes(p.cfg())
