@@ -158,6 +158,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-extra", action="store_true", help="only the headline workload")
     ap.add_argument("--extra-steps", type=int, default=5)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one plain 1 GiB device copy, the known-traffic kernel "
+                         "that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path "
@@ -168,6 +171,13 @@ def main():
     import sliding_window_long_amd as sa
     sa.load_library()
     dev = torch.device("cuda:0")
+
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     wl = W.BITAXON_SWA
     print(f"[bench] headline {wl.name}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
