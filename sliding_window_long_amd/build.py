@@ -24,30 +24,35 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # No packed-fp32 VALU instructions (v_pk_{add,mul,fma}_f32).
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # The kernels never produce or consume NaN (masking uses -inf, and every
+    # comparison is written NaN-free), so min/max need no quieting.
+    "-fno-honor-nans", "-mno-amdgpu-ieee",
     "-I", INCLUDE, "-I", CSRC,
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, build_dir: str = BUILD_DIR, defines=()) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
     return obj
 
 
-def build_library(jobs: int = 4) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build_library(jobs: int = 4, out: str = LIB_PATH, defines=(), build_dir: str = BUILD_DIR) -> str:
+    """Compile and link; `defines` (NAME=VALUE strings) select build-time
+    kernel variants, `out` and `build_dir` place a variant elsewhere."""
+    os.makedirs(build_dir, exist_ok=True)
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB_PATH + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, build_dir, defines), SOURCES))
+    tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

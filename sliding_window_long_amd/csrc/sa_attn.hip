@@ -18,12 +18,23 @@
 // combined with the online-softmax rule.  The window of the Bit-Axon SWA page
 // ("슬라이딩 윈도우 마스크") joins the causal own-block pass.
 //
-// Every tile does S^T = K Q^T (bf16 MFMA 32x32x16, fp32 accumulation),
-// an online softmax in base 2 on the VALU, and O^T += V^T P^T.
+// Every tile does S^T = K Q^T (bf16 MFMA 32x32x16, fp32 accumulation), an
+// online softmax in base 2 on the VALU, and O^T += V^T P^T.  K and V tiles sit
+// row-major in LDS; the V^T operand comes from the transposing LDS reads of
+// gfx950 (ds_read_b64_tr_b16).  The key loop is
+// skewed by one tile: iteration t issues S_t = K_t Q^T, then O += V_{t-1}
+// P_{t-1}, then the softmax of S_t, so the VALU softmax of one tile runs while
+// the matrix core is still busy with the previous tile's P V.  V is staged
+// one tile behind K, which keeps both double-buffered.
 #include "sa_device.hpp"
 #include "sa_internal.hpp"
 
 #include <math.h>
+
+// Instruction-group schedule of one key-loop step (see kv_step).
+#ifndef SA_SCHED
+#define SA_SCHED 0
+#endif
 
 namespace sa {
 
@@ -37,184 +48,233 @@ struct Tile {
     static constexpr int DK = D / 16;              // contraction steps of K Q^T
     static constexpr int DM = (D + 31) / 32;       // 32-row blocks of O^T
     static constexpr int DPAD = DM * 32;
-    static constexpr int KS = D + 8;               // K tile row stride (elements)
-    static constexpr int VS = KT + 8;              // V^T tile row stride (elements)
+    // Row strides (elements) of the K and V tiles in LDS, both row-major
+    // [key][dim].  K rows are read 16 bytes per lane by 32 consecutive keys:
+    // D + 8 puts those reads on distinct banks.  V rows are read by the
+    // transposing LDS loads, 4 keys x 32 bytes per 16-lane group: a stride of
+    // 8 (mod 32) dwords keeps the 4 rows on distinct banks.
+    static constexpr int KS = D + 8;
+    static constexpr int VS = D == 64 ? 80 : D == 80 ? 80 : 144;
     static constexpr int KELEMS = KT * KS;
-    static constexpr int VELEMS = DPAD * VS;
-    static constexpr int KCHUNKS = KT * D / 8;     // 16-byte pieces of a K tile
-    static constexpr int KPT = (KCHUNKS + NTHREADS - 1) / NTHREADS;
-    static constexpr int VTASKS = (KT / 4) * (D / 8);  // 4 keys x 8 dims each
-    static constexpr int VPT = (VTASKS + NTHREADS - 1) / NTHREADS;
+    static constexpr int VELEMS = KT * VS;
+    static constexpr int CHUNKS = KT * D / 8;      // 16-byte pieces of a tile
+    static constexpr int CPT = (CHUNKS + NTHREADS - 1) / NTHREADS;
 };
 
+// Registers holding one K or V tile between its global load and LDS store.
 template <int D, int SPLIT>
 struct Stage {
-    uint4 k[SPLIT][Tile<D>::KPT];
-    uint4 v[SPLIT][Tile<D>::VPT][4];
+    uint4 x[SPLIT][Tile<D>::CPT];
 };
 
-__device__ __forceinline__ uint32_t word_of(const uint4& u, int i) {
-    return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
-}
-
-// Global -> registers for the 64-key tile starting at kt0 (keys >= kend read
-// as zero; they are always masked by causality).
+// Global -> registers for the 64-key tile starting at kt0 (K or V).
+// Branch-free: keys at or past kend read key kend-1 instead (finite data that
+// causality always masks), and threads past the last chunk repeat it (they
+// later write the same bytes to the same LDS address).
 template <int D, int SPLIT>
-__device__ __forceinline__ void stage_load(Stage<D, SPLIT>& st, const uint16_t* const* kp,
-                                           const uint16_t* const* vp, int kt0, int kend, int tid) {
+__device__ __forceinline__ void load_tile(Stage<D, SPLIT>& st, const uint16_t* const* src, int kt0,
+                                          int kend, int tid) {
     using T = Tile<D>;
 #pragma unroll
-    for (int p = 0; p < SPLIT; ++p) {
+    for (int p = 0; p < SPLIT; ++p)
 #pragma unroll
-        for (int c = 0; c < T::KPT; ++c) {
-            const int idx = tid + c * NTHREADS;
-            uint4 val = make_uint4(0, 0, 0, 0);
-            if (idx < T::KCHUNKS) {
-                const int row = idx / (D / 8), col = idx % (D / 8);
-                const int key = kt0 + row;
-                if (key < kend) val = *(const uint4*)(kp[p] + (size_t)key * D + col * 8);
-            }
-            st.k[p][c] = val;
+        for (int c = 0; c < T::CPT; ++c) {
+            const int idx = min(tid + c * NTHREADS, T::CHUNKS - 1);
+            const int row = idx / (D / 8), col = idx % (D / 8);
+            const int key = min(kt0 + row, kend - 1);
+            st.x[p][c] = *(const uint4*)(src[p] + (size_t)key * D + col * 8);
         }
-#pragma unroll
-        for (int c = 0; c < T::VPT; ++c) {
-            const int task = tid + c * NTHREADS;
-            const int kq = task % (KT / 4), dc = task / (KT / 4);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                uint4 val = make_uint4(0, 0, 0, 0);
-                const int key = kt0 + kq * 4 + r;
-                if (task < T::VTASKS && key < kend)
-                    val = *(const uint4*)(vp[p] + (size_t)key * D + dc * 8);
-                st.v[p][c][r] = val;
-            }
-        }
-    }
 }
 
-// Registers -> LDS.  K keeps its row-major layout (padded rows).  V is
-// written transposed (one row per head dimension) with the 16 keys of each
-// contraction step permuted so that lane half h finds the 8 keys it feeds to
-// the matrix core contiguous: positions 8h..8h+7 of a 16-key group hold keys
-// {4h..4h+3, 8+4h..8+4h+3}, the order in which the S^T accumulator hands
-// them out.
-template <int D, int SPLIT>
-__device__ __forceinline__ void stage_store(const Stage<D, SPLIT>& st, uint16_t* ks, uint16_t* vt,
-                                            int tid) {
+// Registers -> LDS, row-major with row stride STRIDE; planes PLANE apart.
+template <int D, int SPLIT, int STRIDE, int PLANE>
+__device__ __forceinline__ void store_tile(const Stage<D, SPLIT>& st, uint16_t* dst, int tid) {
     using T = Tile<D>;
 #pragma unroll
-    for (int p = 0; p < SPLIT; ++p) {
-        uint16_t* kdst = ks + p * T::KELEMS;
-        uint16_t* vdst = vt + p * T::VELEMS;
+    for (int p = 0; p < SPLIT; ++p)
 #pragma unroll
-        for (int c = 0; c < T::KPT; ++c) {
-            const int idx = tid + c * NTHREADS;
-            if (idx < T::KCHUNKS) {
-                const int row = idx / (D / 8), col = idx % (D / 8);
-                *(uint4*)(kdst + row * T::KS + col * 8) = st.k[p][c];
-            }
+        for (int c = 0; c < T::CPT; ++c) {
+            const int idx = min(tid + c * NTHREADS, T::CHUNKS - 1);
+            const int row = idx / (D / 8), col = idx % (D / 8);
+            *(uint4*)(dst + p * PLANE + row * STRIDE + col * 8) = st.x[p][c];
         }
-#pragma unroll
-        for (int c = 0; c < T::VPT; ++c) {
-            const int task = tid + c * NTHREADS;
-            if (task < T::VTASKS) {
-                const int kq = task % (KT / 4), dc = task / (KT / 4);
-                const int q4 = kq & 3;
-                const int pos = (kq >> 2) * 16 + (((q4 & 1) << 3) | ((q4 >> 1) << 2));
-#pragma unroll
-                for (int t = 0; t < 8; ++t) {
-                    const uint32_t w0 = word_of(st.v[p][c][0], t >> 1);
-                    const uint32_t w1 = word_of(st.v[p][c][1], t >> 1);
-                    const uint32_t w2 = word_of(st.v[p][c][2], t >> 1);
-                    const uint32_t w3 = word_of(st.v[p][c][3], t >> 1);
-                    uint2 pk;
-                    if (t & 1) {
-                        pk.x = (w0 >> 16) | (w1 & 0xffff0000u);
-                        pk.y = (w2 >> 16) | (w3 & 0xffff0000u);
-                    } else {
-                        pk.x = (w0 & 0xffffu) | (w1 << 16);
-                        pk.y = (w2 & 0xffffu) | (w3 << 16);
-                    }
-                    *(uint2*)(vdst + (dc * 8 + t) * T::VS + pos) = pk;
-                }
-            }
-        }
-    }
 }
 
-// Per-lane mask state for one query row.
-struct RowMask {
-    int row;        // query position i
-    int window;     // 0 = off
-    bool blk_ok;    // the current tile's block is attended by this row
+// Before the key loop: V buffer 1 is read by the first iteration's P V,
+// whose P is zero; it is zeroed so no stale LDS bits (possibly NaN) meet it.
+template <int D, int SPLIT>
+__device__ __forceinline__ void zero_v_init(uint16_t* vs, int tid) {
+    using T = Tile<D>;
+    uint32_t* b1 = (uint32_t*)(vs + SPLIT * T::VELEMS);
+    for (int x = tid; x < SPLIT * T::VELEMS / 2; x += NTHREADS) b1[x] = 0u;
+}
+
+// Softmax state of one query row in one lane (the lane pair l, l^32 shares
+// the row and keeps the same m).
+struct RowState {
+    float m;      // exponent base, raw dot-product units; lags the running max
+                  // by less than kLazy / c (rescaling is deferred until then)
+    float l;      // this lane's partial sum of exp2((s - m) c)
+    float alpha;  // pending rescale of O from the last softmax
+    bool need;    // alpha != 1 for this row
 };
 
-// One 64-key tile for one wave (32 query rows, one per lane pair).
-//   m: running max of the raw dot products of this row (both lane halves
-//      agree), l: this lane's partial sum of exp2((s - m) * c).
-template <int D, int SPLIT, bool MASKED>
-__device__ __forceinline__ void attend_tile(const uint16_t* ks, const uint16_t* vt,
-                                            const bf16x8 (&qf)[SPLIT][Tile<D>::DK],
-                                            f32x16 (&o)[Tile<D>::DM], float& m, float& l,
-                                            float c, int lane, const RowMask& mk, int kt0) {
+// Rescale the accumulators only when the row max grew by more than 2^8 in
+// the exponent: until then exp2((s - m) c) <= 256, harmless in fp32 and bf16,
+// and the final normalisation uses the same base.
+constexpr float kLazy = 8.f;
+
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
+
+// v_permlane32_swap gives every lane the pair {x of lane l%32, x of lane
+// l%32+32}, lower lane first, so both lanes of a row compute the same value.
+__device__ __forceinline__ float pair_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float tree_max32(const f32x16& x, const f32x16& y) {
+    float t[11];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) t[i] = max3f(x[3 * i], x[3 * i + 1], x[3 * i + 2]);
+    t[5] = max3f(x[15], y[0], y[1]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t[6 + i] = max3f(y[2 + 3 * i], y[3 + 3 * i], y[4 + 3 * i]);
+    t[10] = fmaxf(y[14], y[15]);
+    const float u0 = max3f(t[0], t[1], t[2]), u1 = max3f(t[3], t[4], t[5]);
+    const float u2 = max3f(t[6], t[7], t[8]), u3 = fmaxf(t[9], t[10]);
+    return fmaxf(max3f(u0, u1, u2), u3);
+}
+
+__device__ __forceinline__ float tree_sum32(const float (&p)[2][16]) {
+    float t[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) t[i] = p[0][i] + p[1][i];
+#pragma unroll
+    for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+        for (int i = 0; i < w; ++i) t[i] += t[i + w];
+    return t[0];
+}
+
+// S^T tile (64 keys x 32 queries) of one wave: s[sub] covers keys
+// sub*32 .. sub*32+31; the two halves are interleaved so consecutive
+// matrix-core ops are independent.
+template <int D, int SPLIT>
+__device__ __forceinline__ void qk_tile(const uint16_t* ks, const bf16x8 (&qf)[SPLIT][Tile<D>::DK],
+                                        f32x16 (&s)[2], int lane) {
     using T = Tile<D>;
     const int col = lane & 31, hh = lane >> 5;
-    f32x16 s[2];
+    s[0] = f32x16{};
+    s[1] = f32x16{};
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-        f32x16 acc = {};
+    for (int k_ = 0; k_ < T::DK; ++k_)
 #pragma unroll
-        for (int ks_ = 0; ks_ < T::DK; ++ks_) {
-            const int off = (sub * 32 + col) * T::KS + ks_ * 16 + 8 * hh;
+        for (int sub = 0; sub < 2; ++sub) {
+            const int off = (sub * 32 + col) * T::KS + k_ * 16 + 8 * hh;
             const bf16x8 a = *(const bf16x8*)(ks + off);
-            acc = mfma32(a, qf[0][ks_], acc);
+            s[sub] = mfma32(a, qf[0][k_], s[sub]);
             if constexpr (SPLIT == 2) {
-                const bf16x8 alo = *(const bf16x8*)(ks + T::KELEMS + off);
-                acc = mfma32(a, qf[1][ks_], acc);
-                acc = mfma32(alo, qf[0][ks_], acc);
+                s[sub] = mfma32(a, qf[1][k_], s[sub]);
+                s[sub] = mfma32(*(const bf16x8*)(ks + T::KELEMS + off), qf[0][k_], s[sub]);
             }
         }
-        s[sub] = acc;
-    }
-    if constexpr (MASKED) {
+#if SA_SCHED >= 2
+    // All K fragment reads first, then the matrix-core ops.
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * T::DK * SPLIT, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * T::DK * (SPLIT == 2 ? 3 : 1), 0);
+#endif
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// 4 keys x 1 dim per lane from row-major V (ds_read_b64_tr_b16): within each
+// 16-lane group, lane i receives the i%4-th 16-bit column of the 8 bytes
+// addressed by lanes 4r + i/4, r = 0..3.
+__device__ __forceinline__ v4i16 read_tr(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
+}
+
+// Per-lane offset (elements) into a V tile for the V^T operand of O^T row
+// block mb: lane group G = lane/16 covers dims mb*32 + 16*(G%2) .. +15 and
+// key half h = G/2; source lane 4r + q of the group points at key 4h + r,
+// dims +4q, so lane i of the group receives keys 4h..4h+3 of dim +i.  Dims
+// past D (padding rows of O^T, discarded) read dim 0 instead.
+template <int D>
+__device__ __forceinline__ int v_lane_offset(int lane, int mb) {
+    const int j = lane & 15, r = j >> 2, q = j & 3, G = lane >> 4, h = G >> 1;
+    int dim = mb * 32 + 16 * (G & 1) + 4 * q;
+    if (dim >= D) dim = 0;
+    return (4 * h + r) * Tile<D>::VS + dim;
+}
+
+// O^T += V^T P^T for one tile.  For contraction step kk (keys 16kk..16kk+15)
+// lane half h feeds keys {4h..4h+3, 8+4h..8+4h+3}: two transposing reads.
+template <int D, int SPLIT>
+__device__ __forceinline__ void pv_tile(const uint16_t* vs, const bf16x8 (&pb)[4],
+                                        const bf16x8 (&pl)[4], f32x16 (&o)[Tile<D>::DM],
+                                        const int (&voff)[Tile<D>::DM]) {
+    using T = Tile<D>;
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
+    for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int key = kt0 + sub * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
-                const bool ok = key <= mk.row &&
-                                ((mk.window > 0 && mk.row - key < mk.window) || mk.blk_ok);
-                if (!ok) s[sub][v] = -INFINITY;
+        for (int mb = 0; mb < T::DM; ++mb) {
+            const uint16_t* p0 = vs + voff[mb] + 16 * kk * T::VS;
+            const v4i16 lo = read_tr(p0), hi = read_tr(p0 + 8 * T::VS);
+            const bf16x8 a =
+                __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            o[mb] = mfma32(a, pb[kk], o[mb]);
+            if constexpr (SPLIT == 2) {
+                const v4i16 lo2 = read_tr(p0 + T::VELEMS), hi2 = read_tr(p0 + T::VELEMS + 8 * T::VS);
+                const bf16x8 a2 = __builtin_bit_cast(
+                    bf16x8, __builtin_shufflevector(lo2, hi2, 0, 1, 2, 3, 4, 5, 6, 7));
+                o[mb] = mfma32(a, pl[kk], o[mb]);
+                o[mb] = mfma32(a2, pb[kk], o[mb]);
             }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[sub][v]);
-    mx = fmaxf(mx, xor32(mx));
-    const float m_new = fmaxf(m, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2((m - m_use) * c);
-    const float nb = -m_use * c;
-    float p[2][16];
-    float psum = 0.f;
+        }
+}
+
+// Mask of an S^T tile: key j stays for this lane's row i iff
+// (unsigned)(i - j) < wl: wl = 2^31 keeps every causal key (an attended
+// block), wl = w the window.  rk = i - kt0 - 4*(lane/32), so i - j = rk - (a
+// constant of the accumulator register).
+//
+// Online softmax of the tile: produces the bf16 operand P (and its low part
+// for split fp32 operands) and leaves in st the factor by which O must be
+// rescaled once the previous tile's P V is in.
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int rk, uint32_t wl) {
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            p[sub][v] = fast_exp2(fmaf(s[sub][v], c, nb));
-            psum += p[sub][v];
+            const int cv = sub * 32 + 8 * (v >> 2) + (v & 3);
+            if ((uint32_t)(rk - cv) >= wl) s[sub][v] = -INFINITY;
         }
-    l = l * alpha + psum;
-    m = m_new;
-#pragma unroll
-    for (int mb = 0; mb < T::DM; ++mb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) o[mb][v] *= alpha;
+}
 
-    bf16x8 pb[4];
-    bf16x8 pl[4];
+template <int SPLIT>
+__device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], RowState& st, float c,
+                                             bf16x8 (&pb)[4], bf16x8 (&pl)[4]) {
+    const float mx = pair_max(tree_max32(s[0], s[1]));
+    // NaN-free test: true while m is still -inf and mx is finite; false when
+    // both are -inf (a fully masked tile before the row's first key).
+    st.need = mx > st.m + kLazy / c;
+    st.alpha = st.need ? fast_exp2((st.m - mx) * c) : 1.f;
+    st.m = st.need ? mx : st.m;
+    const float nb = st.m == -INFINITY ? 0.f : -st.m * c;
+    float p[2][16];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) p[sub][v] = fast_exp2(fmaf(s[sub][v], c, nb));
+    st.l = fmaf(st.l, st.alpha, tree_sum32(p));
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
         pb[kk] = to_bf16x8(&p[kk >> 1][8 * (kk & 1)]);
@@ -225,20 +285,57 @@ __device__ __forceinline__ void attend_tile(const uint16_t* ks, const uint16_t* 
             pl[kk] = to_bf16x8(r);
         }
     }
+}
+
+// Rescale O by the factor the last softmax left pending (rare: only when a
+// row max grew past the lazy threshold).
+template <int D>
+__device__ __forceinline__ void apply_rescale(f32x16 (&o)[Tile<D>::DM], RowState& st) {
+    if (__any(st.need)) {
 #pragma unroll
-    for (int mb = 0; mb < T::DM; ++mb) {
+        for (int mb = 0; mb < Tile<D>::DM; ++mb)
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int off = (mb * 32 + col) * T::VS + kk * 16 + 8 * hh;
-            const bf16x8 a = *(const bf16x8*)(vt + off);
-            o[mb] = mfma32(a, pb[kk], o[mb]);
-            if constexpr (SPLIT == 2) {
-                const bf16x8 alo = *(const bf16x8*)(vt + T::VELEMS + off);
-                o[mb] = mfma32(a, pl[kk], o[mb]);
-                o[mb] = mfma32(alo, pb[kk], o[mb]);
-            }
-        }
+            for (int v = 0; v < 16; ++v) o[mb][v] *= st.alpha;
     }
+    st.need = false;
+}
+
+// One step of the skewed key loop: the pending rescale of O, then, as
+// straight-line code the scheduler can interleave, S_t = K_t Q^T,
+// O += V_{t-1} P_{t-1} and the softmax of S_t into P_t.
+template <int D, int SPLIT>
+__device__ __forceinline__ void kv_step(const uint16_t* ks, const uint16_t* vs_prev,
+                                        const bf16x8 (&qf)[SPLIT][Tile<D>::DK],
+                                        f32x16 (&o)[Tile<D>::DM], RowState& st, bf16x8 (&pb)[4],
+                                        bf16x8 (&pl)[4], float c, int lane,
+                                        const int (&voff)[Tile<D>::DM], bool masked, int rk,
+                                        uint32_t wl) {
+    apply_rescale<D>(o, st);
+    f32x16 s[2];
+    qk_tile<D, SPLIT>(ks, qf, s, lane);
+    if (masked) mask_tile(s, rk, wl);   // wave-uniform; edge tiles only
+    pv_tile<D, SPLIT>(vs_prev, pb, pl, o, voff);
+    softmax_tile<SPLIT>(s, st, c, pb, pl);
+#if SA_SCHED == 3
+    // V^T fragment reads first, then P V interleaved with the softmax VALU.
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 * Tile<D>::DM * SPLIT, 0);
+#pragma unroll
+    for (int i = 0; i < 4 * Tile<D>::DM * (SPLIT == 2 ? 3 : 1); ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+    }
+#endif
+#if SA_SCHED == 1
+    // K fragment reads, S^T, then P V interleaved with the softmax VALU.
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * Tile<D>::DK, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * Tile<D>::DK * (SPLIT == 2 ? 3 : 1), 0);
+#pragma unroll
+    for (int i = 0; i < 4 * Tile<D>::DM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, SPLIT, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, SPLIT == 2 ? 3 : 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+    }
+#endif
 }
 
 template <int D, int SPLIT>
@@ -252,16 +349,6 @@ __device__ __forceinline__ void load_q(bf16x8 (&qf)[SPLIT][Tile<D>::DK], const u
             if (ok) u = *(const uint4*)(qp[p] + row_off + ks_ * 16 + 8 * hh);
             qf[p][ks_] = as_bf16x8(u);
         }
-}
-
-template <int D>
-__device__ __forceinline__ void zero_pad_rows(uint16_t* vt, int planes_x_bufs, int tid) {
-    using T = Tile<D>;
-    if constexpr (T::DPAD > D) {
-        const int n = (T::DPAD - D) * T::VS;
-        for (int b = 0; b < planes_x_bufs; ++b)
-            for (int x = tid; x < n; x += NTHREADS) vt[b * T::VELEMS + D * T::VS + x] = 0;
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -320,57 +407,60 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_rows_kernel(RowsArgs a) {
         return max(lo, 0);
     };
     const int t_begin = lower_key(r0) / KT, t_end = r_hi / KT;
-    const int q0 = r0 + wave * 32;
-    const bool wave_rows = q0 < N;
+    const int q0 = r0 + __builtin_amdgcn_readfirstlane(wave) * 32;   // wave-uniform
     const int q1 = min(q0 + 31, N - 1);
-    const int wlo = lower_key(q0);
     const float c = a.scale * kLog2e;
+    const uint32_t wl_window = a.window > 0 ? (uint32_t)a.window : 0u;
 
-    zero_pad_rows<D>(&lds_v[0][0], 2 * SPLIT, tid);
+    zero_v_init<D, SPLIT>(&lds_v[0][0], tid);
 
     f32x16 o[T::DM];
 #pragma unroll
     for (int mb = 0; mb < T::DM; ++mb) o[mb] = f32x16{};
-    float m = -INFINITY, l = 0.f;
+    RowState rs{-INFINITY, 0.f, 1.f, false};
+    bf16x8 pb[4], pl[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) pb[kk] = pl[kk] = as_bf16x8(make_uint4(0, 0, 0, 0));
 
-    Stage<D, SPLIT> st;
-    stage_load<D, SPLIT>(st, kp, vp, t_begin * KT, N, tid);
-    stage_store<D, SPLIT>(st, lds_k[0], lds_v[0], tid);
+    int voff[T::DM];
+#pragma unroll
+    for (int mb = 0; mb < T::DM; ++mb) voff[mb] = v_lane_offset<D>(lane, mb);
+    Stage<D, SPLIT> kst, vst;
+    load_tile<D, SPLIT>(kst, kp, t_begin * KT, N, tid);
+    store_tile<D, SPLIT, T::KS, T::KELEMS>(kst, lds_k[0], tid);
     __syncthreads();
 
-    RowMask mk;
-    mk.row = row;
-    mk.window = a.window;
+    // Every wave walks every tile of the workgroup's range; keys a row does
+    // not attend are masked (a tile outside a wave's rows is fully masked).
     for (int t = t_begin; t <= t_end; ++t) {
-        const int buf = (t - t_begin) & 1;
-        const bool more = t < t_end;
-        if (more) stage_load<D, SPLIT>(st, kp, vp, (t + 1) * KT, N, tid);
+        const int it = t - t_begin;
+        load_tile<D, SPLIT>(kst, kp, min(t + 1, t_end) * KT, N, tid);
+        load_tile<D, SPLIT>(vst, vp, t * KT, N, tid);
         const int kt0 = t * KT;
-        if (wave_rows && kt0 <= q1 && kt0 + KT - 1 >= wlo) {
-            bool full = kt0 + KT - 1 <= q0 &&
-                        ((a.window > 0 && q1 - kt0 < a.window) ||
-                         (a.gate && kt0 / a.B == q0 / a.B && q1 / a.B == q0 / a.B));
-            if (a.gate) {
-                const int dlt = row_blk - kt0 / a.B;
-                mk.blk_ok = dlt == 0 || (dlt >= 1 && dlt <= a.span && dlt <= 32 &&
-                                         ((near_bits >> (dlt - 1)) & 1u));
-            } else {
-                mk.blk_ok = false;
-            }
-            if (full)
-                attend_tile<D, SPLIT, false>(lds_k[buf], lds_v[buf], qf, o, m, l, c, lane, mk, kt0);
-            else
-                attend_tile<D, SPLIT, true>(lds_k[buf], lds_v[buf], qf, o, m, l, c, lane, mk, kt0);
+        const bool full = kt0 + KT - 1 <= q0 &&
+                          ((a.window > 0 && q1 - kt0 < a.window) ||
+                           (a.gate && kt0 / a.B == q0 / a.B && q1 / a.B == q0 / a.B));
+        uint32_t wl = wl_window;
+        if (!full && a.gate) {
+            const int dlt = row_blk - kt0 / a.B;
+            const bool blk_ok = dlt == 0 || (dlt >= 1 && dlt <= a.span && dlt <= 32 &&
+                                             ((near_bits >> (dlt - 1)) & 1u));
+            if (blk_ok) wl = 0x80000000u;
         }
-        if (more) stage_store<D, SPLIT>(st, lds_k[buf ^ 1], lds_v[buf ^ 1], tid);
+        kv_step<D, SPLIT>(lds_k[it & 1], lds_v[(it + 1) & 1], qf, o, rs, pb, pl, c, lane, voff, !full,
+                          row - kt0 - 4 * hh, wl);
+        store_tile<D, SPLIT, T::KS, T::KELEMS>(kst, lds_k[(it + 1) & 1], tid);
+        store_tile<D, SPLIT, T::VS, T::VELEMS>(vst, lds_v[it & 1], tid);
         __syncthreads();
     }
+    apply_rescale<D>(o, rs);
+    pv_tile<D, SPLIT>(lds_v[(t_end - t_begin) & 1], pb, pl, o, voff);
 
     if (!row_ok) return;
 
     // Combine: near part (this kernel), far partials, sink.
-    const float lt = l + xor32(l);
-    const float lse_near = m * a.scale + kLn2 * fast_log2(lt);
+    const float lt = pair_sum(rs.l);
+    const float lse_near = rs.m * a.scale + kLn2 * fast_log2(lt);
     float M = lse_near;
     const size_t pbase = prow * (size_t)a.kslots;
     for (int s_ = 0; s_ < nfar; ++s_) M = fmaxf(M, a.part_lse[pbase + s_]);
@@ -465,32 +555,39 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_blocks_kernel(BlocksArgs a) 
     const uint16_t* vp[2] = {a.v[0] + kvoff, SPLIT == 2 ? a.v[1] + kvoff : nullptr};
     const float c = a.scale * kLog2e;
 
-    zero_pad_rows<D>(&lds_v[0][0], 2 * SPLIT, tid);
+    zero_v_init<D, SPLIT>(&lds_v[0][0], tid);
 
     f32x16 o[T::DM];
 #pragma unroll
     for (int mb = 0; mb < T::DM; ++mb) o[mb] = f32x16{};
-    float m = -INFINITY, l = 0.f;
+    RowState rs{-INFINITY, 0.f, 1.f, false};
+    bf16x8 pb[4], pl[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) pb[kk] = pl[kk] = as_bf16x8(make_uint4(0, 0, 0, 0));
 
     const int ntile = a.B / KT;
     const int k_begin = cblk * a.B;
-    Stage<D, SPLIT> st;
-    stage_load<D, SPLIT>(st, kp, vp, k_begin, N, tid);
-    stage_store<D, SPLIT>(st, lds_k[0], lds_v[0], tid);
+    int voff[T::DM];
+#pragma unroll
+    for (int mb = 0; mb < T::DM; ++mb) voff[mb] = v_lane_offset<D>(lane, mb);
+    Stage<D, SPLIT> kst, vst;
+    load_tile<D, SPLIT>(kst, kp, k_begin, N, tid);
+    store_tile<D, SPLIT, T::KS, T::KELEMS>(kst, lds_k[0], tid);
     __syncthreads();
-    RowMask mk{0, 0, true};
     for (int t = 0; t < ntile; ++t) {
-        const int buf = t & 1;
-        const bool more = t + 1 < ntile;
-        if (more) stage_load<D, SPLIT>(st, kp, vp, k_begin + (t + 1) * KT, N, tid);
-        attend_tile<D, SPLIT, false>(lds_k[buf], lds_v[buf], qf, o, m, l, c, lane, mk,
-                                     k_begin + t * KT);
-        if (more) stage_store<D, SPLIT>(st, lds_k[buf ^ 1], lds_v[buf ^ 1], tid);
+        load_tile<D, SPLIT>(kst, kp, k_begin + min(t + 1, ntile - 1) * KT, N, tid);
+        load_tile<D, SPLIT>(vst, vp, k_begin + t * KT, N, tid);
+        kv_step<D, SPLIT>(lds_k[t & 1], lds_v[(t + 1) & 1], qf, o, rs, pb, pl, c, lane, voff, false, 0,
+                          0u);
+        store_tile<D, SPLIT, T::KS, T::KELEMS>(kst, lds_k[(t + 1) & 1], tid);
+        store_tile<D, SPLIT, T::VS, T::VELEMS>(vst, lds_v[t & 1], tid);
         __syncthreads();
     }
+    apply_rescale<D>(o, rs);
+    pv_tile<D, SPLIT>(lds_v[(ntile - 1) & 1], pb, pl, o, voff);
     if (!ok) return;
 
-    const float lt = l + xor32(l);
+    const float lt = pair_sum(rs.l);
     const float inv = 1.f / lt;
     const size_t pidx = prow * (size_t)a.kslots + slot;
     uint16_t* po = a.part_o + pidx * D;
@@ -506,7 +603,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_blocks_kernel(BlocksArgs a) 
                 *(uint2*)(po + d0) = *(const uint2*)r;
             }
         }
-    if (hh == 0) a.part_lse[pidx] = m * a.scale + kLn2 * fast_log2(lt);
+    if (hh == 0) a.part_lse[pidx] = rs.m * a.scale + kLn2 * fast_log2(lt);
 }
 
 // fp32 -> (hi, lo) bf16 planes: x = hi + lo + O(2^-16 |x|).
