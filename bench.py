@@ -46,9 +46,15 @@ def window_pairs_per_head(N, w):
     return int(np.minimum(i + 1, w).sum())
 
 
-def attended_pairs(wl, bsel=None):
+def attended_pairs(wl, bsel=None, tsel=None):
     Bt, Hq, N = wl.batch, wl.n_q_heads, wl.seq_len
     i = np.arange(N, dtype=np.int64)
+    if wl.token_top_k:
+        # window [i-w+1, i] plus the kept tokens before the window start
+        t = tsel.reshape(Bt, N, wl.token_top_k).astype(np.int64)
+        ws = np.maximum(i - wl.window + 1, 0)[None, :, None]
+        extra = ((t >= 0) & (t < ws)).sum()
+        return int((window_pairs_per_head(N, wl.window) * Bt + extra) * Hq)
     if not wl.top_k:
         return window_pairs_per_head(N, wl.window) * Bt * Hq
     B = wl.block_size
@@ -105,11 +111,13 @@ def time_workload(wl, seed, dev, steps, warmup, want_sel=False):
               idx_k=g["idx_k"], token_top_k=wl.token_top_k, sink=g["sink"], workspace=ws)
     out = torch.empty_like(g["q"])
     lse = torch.empty(g["q"].shape[:3], dtype=torch.float32, device=dev)
-    bsel = None
-    if want_sel and wl.top_k:
-        _, _, bsel_t, _ = sa.forward(g["q"], g["k"], g["v"], return_selection=True, **kw)
+    bsel = tsel = None
+    if want_sel and (wl.top_k or wl.token_top_k):
+        _, _, bsel_t, tsel_t = sa.forward(g["q"], g["k"], g["v"], return_selection=True, **kw)
         torch.cuda.synchronize()
-        bsel = bsel_t.cpu().numpy()
+        bsel = None if bsel_t is None else bsel_t.cpu().numpy()
+        tsel = None if tsel_t is None else tsel_t.cpu().numpy()
+        del bsel_t, tsel_t
     for _ in range(warmup):
         sa.forward(g["q"], g["k"], g["v"], out=out, lse=lse, **kw)
     torch.cuda.synchronize()
@@ -124,7 +132,7 @@ def time_workload(wl, seed, dev, steps, warmup, want_sel=False):
     for name, ms in sa.sparse_attn_stage_times(1024):
         stages.setdefault(name, []).append(ms)
     stage_ms = {k: float(np.mean(v)) for k, v in stages.items()}
-    return inp, (t1 - t0) * 1e3 / steps, stage_ms, bsel
+    return inp, (t1 - t0) * 1e3 / steps, stage_ms, (bsel, tsel)
 
 
 def cpu_baseline(inp, budget_s=15.0):
@@ -217,11 +225,12 @@ def main():
     }
     if not args.no_extra:
         extra = {}
-        for idx in (1, 2, 4):
+        for idx in (1, 2, 4, 5):
             ewl = W.WORKLOADS[idx]
             print(f"[bench] workload {ewl.name}", file=sys.stderr, flush=True)
-            _, ems, est, bsel = time_workload(ewl, idx, dev, args.extra_steps, 2, want_sel=True)
-            ep = attended_pairs(ewl, bsel)
+            _, ems, est, (bsel, tsel) = time_workload(ewl, idx, dev, args.extra_steps, 2,
+                                                      want_sel=True)
+            ep = attended_pairs(ewl, bsel, tsel)
             ef = 4.0 * ewl.head_dim * ep
             extra[ewl.name] = {"ms_per_step": ems,
                                "tokens_per_s": ewl.batch * ewl.seq_len / (ems * 1e-3),

@@ -57,7 +57,10 @@ extern "C" {
 #define SPARSE_ATTN_ABI_VERSION 1
 
 typedef enum {
-    SA_BF16 = 0, /* bfloat16 inputs and out; fp32 accumulation */
+    SA_BF16 = 0, /* bfloat16 inputs and out; fp32 accumulation.  Q K^T runs on
+                    bf16 matrix cores; P V on fp16 ones (V converted once into
+                    the workspace, exact for |v| in [2^-14, 65504]; larger |v|
+                    overflows, smaller ones keep fp16 subnormal precision). */
     SA_F32 = 1   /* float32 inputs and out; each operand split into two
                     bf16 terms on the matrix cores (about 16 mantissa bits) */
 } sa_dtype;

@@ -28,10 +28,13 @@ struct Plan {
     bool far;
     long long max_entries;
     int max_chunks;
+    bool tok;
+    int top_t, nt32;
     float scale;
     // workspace regions (byte offsets)
     size_t o_split, o_kb3, o_sel, o_count, o_cursor, o_listoff, o_nchunks, o_chunk_list,
-        o_chunk_start, o_entries, o_part_o, o_part_lse, total;
+        o_chunk_start, o_entries, o_part_o, o_part_lse, o_tok_split, o_tok_state, o_tok_mask,
+        o_v16, total;
 };
 
 bool misaligned(const void* p, size_t a) { return p && (reinterpret_cast<uintptr_t>(p) % a) != 0; }
@@ -49,7 +52,12 @@ int make_plan(const sparse_attn_cfg* c, Plan* p) {
     if (c->n_q_heads % c->n_kv_heads) return SA_E_SHAPE;
     if (c->n_q_heads / c->n_kv_heads > 16) return SA_E_UNSUPPORTED;
     if (c->window == 0 && c->top_k == 0) return SA_E_NO_SELF;
-    if (c->token_top_k > 0) return SA_E_UNSUPPORTED;   // token gate: not built yet
+    if (c->token_top_k > 0) {
+        if (c->index_dim != 64) return SA_E_UNSUPPORTED_HEAD_DIM;
+        // 16 index bits in the selection key; block and token gates are
+        // separate methods and are not combined in one call.
+        if (c->seq_len > 65536 || c->top_k > 0) return SA_E_UNSUPPORTED;
+    }
 
     Plan& P = *p;
     memset(&P, 0, sizeof(P));
@@ -99,6 +107,7 @@ int make_plan(const sparse_attn_cfg* c, Plan* p) {
     auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
     const size_t nq = (size_t)rows * P.D, nkv = (size_t)P.Bt * P.Hkv * P.N * P.D;
     P.o_split = take(P.f32 ? 2 * (nq + 2 * nkv) * 2 : 0);
+    P.o_v16 = take(P.f32 ? 0 : nkv * 2);   // fp16 copy of V for the P V products
     if (P.gate) {
         P.o_kb3 = take((size_t)3 * P.lists * P.D * 2);
         P.o_sel = take((size_t)rows * P.top_k * 4);
@@ -113,6 +122,15 @@ int make_plan(const sparse_attn_cfg* c, Plan* p) {
             P.o_part_o = take((size_t)rows * P.kslots * P.D * 2);
             P.o_part_lse = take((size_t)rows * P.kslots * 4);
         }
+    }
+    P.tok = c->token_top_k > 0;
+    if (P.tok) {
+        P.top_t = c->token_top_k;
+        P.nt32 = (P.N + 31) / 32;
+        const size_t nidx = (size_t)P.Bt * P.N * 64;
+        P.o_tok_split = take(P.f32 ? 2 * 2 * nidx * 2 : 0);
+        P.o_tok_state = take((size_t)P.Bt * P.N * 16);
+        P.o_tok_mask = take((size_t)P.Bt * P.nt32 * ((P.N + 63) / 64) * 64 * 4);
     }
     P.total = off;
     return SA_OK;
@@ -221,6 +239,10 @@ int sparse_attn_fwd(const void* q, const void* k, const void* v, const sparse_at
         misaligned(cfg->workspace, 16) || misaligned(lse, 4) || misaligned(cfg->sink, 4) ||
         misaligned(cfg->block_sel_out, 4) || misaligned(cfg->token_sel_out, 4))
         return SA_E_ALIGNMENT;
+    if (P.tok) {
+        if (!cfg->idx_q || !cfg->idx_k) return SA_E_INVALID_ARG;
+        if (misaligned(cfg->idx_q, 16) || misaligned(cfg->idx_k, 16)) return SA_E_ALIGNMENT;
+    }
     if (P.total > 0 && (!cfg->workspace || cfg->workspace_bytes < P.total))
         return SA_E_WORKSPACE_TOO_SMALL;
 
@@ -245,6 +267,13 @@ int sparse_attn_fwd(const void* q, const void* k, const void* v, const sparse_at
             !ok(sa::launch_split_f32((const float*)v, vh, vl, nkv, s)))
             return SA_E_HIP;
         qp[0] = qh; qp[1] = ql; kp[0] = kh; kp[1] = kl; vp[0] = vh; vp[1] = vl;
+    } else {
+        uint16_t* v16 = (uint16_t*)(ws + P.o_v16);
+        StageScope t("v_to_f16", s);
+        if (!ok(sa::launch_bf16_to_f16((const uint16_t*)v, v16,
+                                       (size_t)P.Bt * P.Hkv * P.N * P.D, s)))
+            return SA_E_HIP;
+        vp[0] = v16;
     }
 
     int32_t* sel = nullptr;
@@ -296,6 +325,36 @@ int sparse_attn_fwd(const void* q, const void* k, const void* v, const sparse_at
         }
     }
 
+    const uint32_t* tokmask = nullptr;
+    if (P.tok) {
+        sa::TokArgs ta{};
+        ta.iq[0] = (const uint16_t*)cfg->idx_q;
+        ta.ik[0] = (const uint16_t*)cfg->idx_k;
+        if (P.f32) {
+            const size_t nidx = (size_t)P.Bt * P.N * 64;
+            uint16_t* base = (uint16_t*)(ws + P.o_tok_split);
+            StageScope t("split_f32_indexer", s);
+            if (!ok(sa::launch_split_f32((const float*)cfg->idx_q, base, base + nidx, nidx, s)) ||
+                !ok(sa::launch_split_f32((const float*)cfg->idx_k, base + 2 * nidx, base + 3 * nidx,
+                                         nidx, s)))
+                return SA_E_HIP;
+            ta.iq[0] = base; ta.iq[1] = base + nidx;
+            ta.ik[0] = base + 2 * nidx; ta.ik[1] = base + 3 * nidx;
+        }
+        ta.Bt = P.Bt; ta.N = P.N; ta.top_t = P.top_t;
+        ta.state = (int4*)(ws + P.o_tok_state);
+        ta.mask = (uint16_t*)(ws + P.o_tok_mask);
+        {
+            StageScope t("token_select", s);
+            if (!ok(sa::launch_token_select(ta, split, s))) return SA_E_HIP;
+        }
+        if (cfg->token_sel_out) {
+            StageScope t("token_list", s);
+            if (!ok(sa::launch_token_list(ta, cfg->token_sel_out, s))) return SA_E_HIP;
+        }
+        tokmask = (const uint32_t*)ta.mask;
+    }
+
     sa::RowsArgs ra{};
     for (int i = 0; i < 2; ++i) { ra.q[i] = qp[i]; ra.k[i] = kp[i]; ra.v[i] = vp[i]; }
     ra.out = out; ra.lse = lse;
@@ -304,6 +363,7 @@ int sparse_attn_fwd(const void* q, const void* k, const void* v, const sparse_at
     ra.gate = P.gate ? 1 : 0; ra.B = P.B; ra.top_k = P.top_k; ra.span = P.span;
     ra.sel = sel; ra.part_o = part_o; ra.part_lse = part_lse; ra.kslots = P.kslots;
     ra.sink = cfg->sink; ra.out_f32 = P.f32 ? 1 : 0;
+    ra.tokmask = tokmask;
     StageScope t("attn_rows", s);
     if (!ok(sa::launch_rows(ra, P.D, split, s))) return SA_E_HIP;
     return SA_OK;

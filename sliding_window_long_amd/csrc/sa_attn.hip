@@ -217,9 +217,12 @@ __device__ __forceinline__ int v_lane_offset(int lane, int mb) {
 
 // O^T += V^T P^T for one tile.  For contraction step kk (keys 16kk..16kk+15)
 // lane half h feeds keys {4h..4h+3, 8+4h..8+4h+3}: two transposing reads.
+// bf16 inputs: V (converted once) and P are fp16 -- P keeps 11 significant
+// bits, which the few-key rows need to stay within the output tolerance.
+// fp32 inputs: hi/lo bf16 splits of V and P, three products.
 template <int D, int SPLIT>
-__device__ __forceinline__ void pv_tile(const uint16_t* vs, const bf16x8 (&pb)[4],
-                                        const bf16x8 (&pl)[4], f32x16 (&o)[Tile<D>::DM],
+__device__ __forceinline__ void pv_tile(const uint16_t* vs, const uint4 (&pb)[4],
+                                        const uint4 (&pl)[4], f32x16 (&o)[Tile<D>::DM],
                                         const int (&voff)[Tile<D>::DM]) {
     using T = Tile<D>;
 #pragma unroll
@@ -228,15 +231,18 @@ __device__ __forceinline__ void pv_tile(const uint16_t* vs, const bf16x8 (&pb)[4
         for (int mb = 0; mb < T::DM; ++mb) {
             const uint16_t* p0 = vs + voff[mb] + 16 * kk * T::VS;
             const v4i16 lo = read_tr(p0), hi = read_tr(p0 + 8 * T::VS);
-            const bf16x8 a =
-                __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            o[mb] = mfma32(a, pb[kk], o[mb]);
-            if constexpr (SPLIT == 2) {
+            const auto a8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            if constexpr (SPLIT == 1) {
+                o[mb] = mfma32_f16(__builtin_bit_cast(f16x8, a8), __builtin_bit_cast(f16x8, pb[kk]),
+                                   o[mb]);
+            } else {
+                const bf16x8 a = __builtin_bit_cast(bf16x8, a8);
                 const v4i16 lo2 = read_tr(p0 + T::VELEMS), hi2 = read_tr(p0 + T::VELEMS + 8 * T::VS);
                 const bf16x8 a2 = __builtin_bit_cast(
                     bf16x8, __builtin_shufflevector(lo2, hi2, 0, 1, 2, 3, 4, 5, 6, 7));
-                o[mb] = mfma32(a, pl[kk], o[mb]);
-                o[mb] = mfma32(a2, pb[kk], o[mb]);
+                o[mb] = mfma32(a, __builtin_bit_cast(bf16x8, pb[kk]), o[mb]);
+                o[mb] = mfma32(a, __builtin_bit_cast(bf16x8, pl[kk]), o[mb]);
+                o[mb] = mfma32(a2, __builtin_bit_cast(bf16x8, pb[kk]), o[mb]);
             }
         }
 }
@@ -259,9 +265,27 @@ __device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int rk, uint32_t wl) {
         }
 }
 
+// Token-gate mask of an S^T tile: key j stays iff its bit is set in this
+// lane's mask word (bit 16*sub + v for register v of half sub) or, on tiles
+// that meet a window, it passes the same unsigned window test as mask_tile.
+__device__ __forceinline__ void mask_tile_tok(f32x16 (&s)[2], int rk, uint32_t wl, bool window,
+                                              uint32_t word) {
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            bool keep = (word >> (16 * sub + v)) & 1u;
+            if (window) {
+                const int cv = sub * 32 + 8 * (v >> 2) + (v & 3);
+                keep = keep || (uint32_t)(rk - cv) < wl;
+            }
+            if (!keep) s[sub][v] = -INFINITY;
+        }
+}
+
 template <int SPLIT>
 __device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], RowState& st, float c,
-                                             bf16x8 (&pb)[4], bf16x8 (&pl)[4]) {
+                                             uint4 (&pb)[4], uint4 (&pl)[4]) {
     const float mx = pair_max(tree_max32(s[0], s[1]));
     // NaN-free test: true while m is still -inf and mx is finite; false when
     // both are -inf (a fully masked tile before the row's first key).
@@ -277,12 +301,16 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], RowState& st, float
     st.l = fmaf(st.l, st.alpha, tree_sum32(p));
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-        pb[kk] = to_bf16x8(&p[kk >> 1][8 * (kk & 1)]);
-        if constexpr (SPLIT == 2) {
+        const float* pk = &p[kk >> 1][8 * (kk & 1)];
+        if constexpr (SPLIT == 1) {
+            pb[kk] = __builtin_bit_cast(uint4, to_f16x8(pk));
+        } else {
+            const bf16x8 hb = to_bf16x8(pk);
             float r[8];
 #pragma unroll
-            for (int t = 0; t < 8; ++t) r[t] = p[kk >> 1][8 * (kk & 1) + t] - (float)pb[kk][t];
-            pl[kk] = to_bf16x8(r);
+            for (int t = 0; t < 8; ++t) r[t] = pk[t] - (float)hb[t];
+            pb[kk] = __builtin_bit_cast(uint4, hb);
+            pl[kk] = __builtin_bit_cast(uint4, to_bf16x8(r));
         }
     }
 }
@@ -306,14 +334,15 @@ __device__ __forceinline__ void apply_rescale(f32x16 (&o)[Tile<D>::DM], RowState
 template <int D, int SPLIT>
 __device__ __forceinline__ void kv_step(const uint16_t* ks, const uint16_t* vs_prev,
                                         const bf16x8 (&qf)[SPLIT][Tile<D>::DK],
-                                        f32x16 (&o)[Tile<D>::DM], RowState& st, bf16x8 (&pb)[4],
-                                        bf16x8 (&pl)[4], float c, int lane,
+                                        f32x16 (&o)[Tile<D>::DM], RowState& st, uint4 (&pb)[4],
+                                        uint4 (&pl)[4], float c, int lane,
                                         const int (&voff)[Tile<D>::DM], bool masked, int rk,
-                                        uint32_t wl) {
+                                        uint32_t wl, bool tok = false, uint32_t tword = 0) {
     apply_rescale<D>(o, st);
     f32x16 s[2];
     qk_tile<D, SPLIT>(ks, qf, s, lane);
-    if (masked) mask_tile(s, rk, wl);   // wave-uniform; edge tiles only
+    if (tok) mask_tile_tok(s, rk, wl, masked, tword);   // token gate: every tile
+    else if (masked) mask_tile(s, rk, wl);             // wave-uniform; edge tiles only
     pv_tile<D, SPLIT>(vs_prev, pb, pl, o, voff);
     softmax_tile<SPLIT>(s, st, c, pb, pl);
 #if SA_SCHED == 3
@@ -354,7 +383,7 @@ __device__ __forceinline__ void load_q(bf16x8 (&qf)[SPLIT][Tile<D>::DK], const u
 // ---------------------------------------------------------------------------
 // Query-centric kernel.
 // ---------------------------------------------------------------------------
-template <int D, int SPLIT>
+template <int D, int SPLIT, bool TOK>
 __global__ __launch_bounds__(NTHREADS, 2) void attn_rows_kernel(RowsArgs a) {
     using T = Tile<D>;
     __shared__ __align__(16) uint16_t lds_k[2][SPLIT * T::KELEMS];
@@ -401,6 +430,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_rows_kernel(RowsArgs a) {
     // Key range of the workgroup and of this wave.
     const int r_hi = min(r0 + RT - 1, N - 1);
     auto lower_key = [&](int r) {
+        if (TOK) return 0;   // selected tokens can be anywhere before r
         int lo = r;
         if (a.window > 0) lo = min(lo, r - a.window + 1);
         if (a.gate) lo = min(lo, (r / a.B - a.span) * a.B);
@@ -418,9 +448,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_rows_kernel(RowsArgs a) {
 #pragma unroll
     for (int mb = 0; mb < T::DM; ++mb) o[mb] = f32x16{};
     RowState rs{-INFINITY, 0.f, 1.f, false};
-    bf16x8 pb[4], pl[4];
+    uint4 pb[4], pl[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) pb[kk] = pl[kk] = as_bf16x8(make_uint4(0, 0, 0, 0));
+    for (int kk = 0; kk < 4; ++kk) pb[kk] = pl[kk] = make_uint4(0, 0, 0, 0);
 
     int voff[T::DM];
 #pragma unroll
@@ -447,8 +477,22 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_rows_kernel(RowsArgs a) {
                                              ((near_bits >> (dlt - 1)) & 1u));
             if (blk_ok) wl = 0x80000000u;
         }
-        kv_step<D, SPLIT>(lds_k[it & 1], lds_v[(it + 1) & 1], qf, o, rs, pb, pl, c, lane, voff, !full,
-                          row - kt0 - 4 * hh, wl);
+        if constexpr (TOK) {
+            // This lane's keep bits for the tile; key tiles past the wave's
+            // rows hold no kept key.
+            const int nt32 = (N + 31) / 32, nt64 = (N + KT - 1) / KT, rt = q0 / 32;
+            // Only 32-key halves kc <= rt are written; a half past the row
+            // tile (kc = rt + 1 when rt is even) is all future keys: cleared.
+            uint32_t tword =
+                t <= rt / 2 ? a.tokmask[(((size_t)b * nt32 + rt) * nt64 + t) * 64 + lane] : 0u;
+            if (2 * t + 1 > rt) tword &= 0xffffu;
+            const bool near = kt0 + KT - 1 >= q0 - a.window + 1;   // tile meets a window
+            kv_step<D, SPLIT>(lds_k[it & 1], lds_v[(it + 1) & 1], qf, o, rs, pb, pl, c, lane, voff,
+                              near, row - kt0 - 4 * hh, wl_window, true, tword);
+        } else {
+            kv_step<D, SPLIT>(lds_k[it & 1], lds_v[(it + 1) & 1], qf, o, rs, pb, pl, c, lane, voff,
+                              !full, row - kt0 - 4 * hh, wl);
+        }
         store_tile<D, SPLIT, T::KS, T::KELEMS>(kst, lds_k[(it + 1) & 1], tid);
         store_tile<D, SPLIT, T::VS, T::VELEMS>(vst, lds_v[it & 1], tid);
         __syncthreads();
@@ -561,9 +605,9 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_blocks_kernel(BlocksArgs a) 
 #pragma unroll
     for (int mb = 0; mb < T::DM; ++mb) o[mb] = f32x16{};
     RowState rs{-INFINITY, 0.f, 1.f, false};
-    bf16x8 pb[4], pl[4];
+    uint4 pb[4], pl[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) pb[kk] = pl[kk] = as_bf16x8(make_uint4(0, 0, 0, 0));
+    for (int kk = 0; kk < 4; ++kk) pb[kk] = pl[kk] = make_uint4(0, 0, 0, 0);
 
     const int ntile = a.B / KT;
     const int k_begin = cblk * a.B;
@@ -606,6 +650,30 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_blocks_kernel(BlocksArgs a) 
     if (hh == 0) a.part_lse[pidx] = rs.m * a.scale + kLn2 * fast_log2(lt);
 }
 
+// bf16 -> fp16, exact for |x| in the fp16 normal range [2^-14, 65504].
+__global__ void bf16_to_f16_kernel(const uint4* __restrict__ x, uint4* __restrict__ y, size_t n8) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n8) return;
+    const uint4 u = x[i];
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    uint32_t r[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const _Float16 lo = (_Float16)bf16_to_f32(w[t] & 0xffffu);
+        const _Float16 hi = (_Float16)bf16_to_f32(w[t] >> 16);
+        r[t] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+    y[i] = make_uint4(r[0], r[1], r[2], r[3]);
+}
+
+hipError_t launch_bf16_to_f16(const uint16_t* x, uint16_t* y, size_t n, hipStream_t s) {
+    const size_t n8 = n / 8;   // n is a multiple of the head dim, hence of 8
+    if (n8 == 0) return hipSuccess;
+    hipLaunchKernelGGL(bf16_to_f16_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s,
+                       (const uint4*)x, (uint4*)y, n8);
+    return hipGetLastError();
+}
+
 // fp32 -> (hi, lo) bf16 planes: x = hi + lo + O(2^-16 |x|).
 __global__ void split_f32_kernel(const float* __restrict__ x, uint16_t* __restrict__ hi,
                                  uint16_t* __restrict__ lo, size_t n) {
@@ -622,7 +690,10 @@ template <int D, int SPLIT>
 static hipError_t rows_d(const RowsArgs& a, hipStream_t s) {
     const int ntiles = (a.N + RT - 1) / RT;
     const unsigned grid = (unsigned)(ntiles * a.Bt * a.Hq);
-    hipLaunchKernelGGL((attn_rows_kernel<D, SPLIT>), dim3(grid), dim3(NTHREADS), 0, s, a);
+    if (a.tokmask)
+        hipLaunchKernelGGL((attn_rows_kernel<D, SPLIT, true>), dim3(grid), dim3(NTHREADS), 0, s, a);
+    else
+        hipLaunchKernelGGL((attn_rows_kernel<D, SPLIT, false>), dim3(grid), dim3(NTHREADS), 0, s, a);
     return hipGetLastError();
 }
 

@@ -19,6 +19,7 @@
 namespace sa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -27,6 +28,10 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma32_f16(const f16x8& a, const f16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -40,6 +45,14 @@ __device__ __forceinline__ bf16x8 to_bf16x8(const float* p) {
     bf16x8 r;
 #pragma unroll
     for (int t = 0; t < 8; ++t) r[t] = (__bf16)p[t];
+    return r;
+}
+
+// fp32 -> fp16 with round-to-nearest-even (v_cvt_pk_f16_f32).
+__device__ __forceinline__ f16x8 to_f16x8(const float* p) {
+    f16x8 r;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) r[t] = (_Float16)p[t];
     return r;
 }
 

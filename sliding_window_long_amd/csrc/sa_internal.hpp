@@ -14,7 +14,7 @@ namespace sa {
 struct RowsArgs {
     const uint16_t* q[2];   // bf16 planes of q (plane 1 only for split fp32)
     const uint16_t* k[2];
-    const uint16_t* v[2];
+    const uint16_t* v[2];   // fp16 V (bf16 inputs) or bf16 hi/lo planes (fp32)
     void* out;              // bf16 or fp32 (out_f32)
     float* lse;
     int Bt, Hq, Hkv, N;
@@ -30,6 +30,7 @@ struct RowsArgs {
     int kslots;
     const float* sink;      // [Hq] or nullptr
     int out_f32;
+    const uint32_t* tokmask;  // token keep mask words (see sa_token.hip), or nullptr
 };
 
 // KV-centric attention of one far block against a chunk of gathered rows,
@@ -85,6 +86,18 @@ struct CompactArgs {
     int rows_per_chunk;
 };
 
+// Token gate: per-row radix-select state and the keep mask it produces.
+struct TokArgs {
+    const uint16_t* iq[2];  // bf16 planes of the indexer queries [Bt, N, 64]
+    const uint16_t* ik[2];  // bf16 planes of the indexer keys [Bt, N, 64]
+    int Bt, N, top_t;
+    int4* state;            // [Bt*N]
+    uint16_t* mask;         // keep-mask half-words [Bt][N/32][N/64][64 lanes][2]
+};
+
+hipError_t launch_token_select(const TokArgs& a, int split, hipStream_t s);
+hipError_t launch_token_list(const TokArgs& a, int32_t* out, hipStream_t s);
+
 hipError_t launch_pool(const PoolArgs& a, int head_dim, bool f32_in, int lists, hipStream_t s);
 hipError_t launch_gate(const GateArgs& a, int head_dim, int qsplit, hipStream_t s);
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
@@ -92,6 +105,7 @@ hipError_t launch_fill_i32(int32_t* p, int32_t value, size_t n, hipStream_t s);
 
 hipError_t launch_rows(const RowsArgs& a, int head_dim, int split, hipStream_t s);
 hipError_t launch_blocks(const BlocksArgs& a, int head_dim, int split, int grid, hipStream_t s);
+hipError_t launch_bf16_to_f16(const uint16_t* x, uint16_t* y, size_t n, hipStream_t s);
 hipError_t launch_split_f32(const float* x, uint16_t* hi, uint16_t* lo, size_t n, hipStream_t s);
 
 }  // namespace sa

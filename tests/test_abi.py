@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 def test_struct_layout_matches(lib):
     # The library rejects any struct_size other than its own sizeof.
     cfg = sa.Params(1, 4, 4, 256, 64, window=16).cfg()
-    assert sa.sparse_attn_workspace_bytes(cfg) == 0
+    assert sa.sparse_attn_workspace_bytes(cfg) == 4 * 256 * 64 * 2
     cfg.struct_size = ctypes.sizeof(binding.SparseAttnCfg) - 8
     with pytest.raises(sa.SparseAttnError) as e:
         sa.sparse_attn_workspace_bytes(cfg)
@@ -66,6 +66,10 @@ def code_of(params, **cfg_fields):
     (sa.Params(1, 34, 1, 256, 64, window=8), -8),                     # group > 16
     (sa.Params(1, 4, 4, 64 * 40, 64, block_size=64, top_k=34), -8),   # top_k > 33
     (sa.Params(1, 4, 4, 256, 64, window=8, softmax_scale=-1.0), -1),
+    (sa.Params(1, 4, 1, 256, 128, window=8, token_top_k=16, index_dim=32), -3),
+    (sa.Params(1, 4, 1, 65536 + 64, 128, window=8, token_top_k=16, index_dim=64), -8),
+    (sa.Params(1, 4, 1, 256, 128, window=8, block_size=64, top_k=2, token_top_k=16,
+               index_dim=64), -8),
 ])
 def test_invalid_configs(lib, params, code):
     assert code_of(params) == code
@@ -76,14 +80,16 @@ def test_valid_configs(lib):
               sa.Params(2, 8, 4, 4096, 128, block_size=128, top_k=16, window=512),
               sa.Params(1, 32, 32, 16384, 80, window=4096),
               sa.Params(1, 32, 8, 131072, 128, block_size=512, top_k=8),
-              sa.Params(1, 3, 3, 77, 80, window=1)):
+              sa.Params(1, 3, 3, 77, 80, window=1),
+              sa.Params(1, 16, 4, 65536, 128, window=128, token_top_k=2048, index_dim=64)):
         assert code_of(p) == 0
 
 
 def test_workspace_sizes_scale(lib):
-    # window only: no workspace; block gating with far blocks: partials
+    # block gating with far blocks: partials
     # [rows, top_k-1, d] fp16 dominate.
-    assert sa.sparse_attn_workspace_bytes(sa.Params(1, 32, 32, 16384, 80, window=4096).cfg()) == 0
+    # window only: an fp16 copy of V
+    assert sa.sparse_attn_workspace_bytes(sa.Params(1, 32, 32, 16384, 80, window=4096).cfg()) == 32 * 16384 * 80 * 2
     p = sa.Params(1, 32, 8, 131072, 128, block_size=512, top_k=8)
     rows = 32 * 131072
     assert sa.sparse_attn_workspace_bytes(p.cfg()) >= rows * 7 * 128 * 2
@@ -100,6 +106,12 @@ def fwd_code(params, q=0x1000, k=0x2000, v=0x3000, out=0x4000, lse=0x5000, **cfg
         ctypes.c_void_p(out), ctypes.c_void_p(lse))
 
 
+def test_token_workspace(lib):
+    # keep-mask words [N/32][N/64][64] plus per-row select state
+    p = sa.Params(1, 16, 4, 65536, 128, window=128, token_top_k=2048, index_dim=64)
+    assert sa.sparse_attn_workspace_bytes(p.cfg()) >= 2048 * 1024 * 64 * 4 + 65536 * 16
+
+
 def test_fwd_rejects_before_launch(lib):
     p = sa.Params(1, 4, 4, 256, 64, window=8)
     assert fwd_code(p, q=0) == -1                       # null q
@@ -112,6 +124,12 @@ def test_fwd_rejects_before_launch(lib):
     assert need > 0
     assert fwd_code(g, workspace=0x10000, workspace_bytes=need - 1) == -6
     assert fwd_code(g, workspace=0, workspace_bytes=0) == -6
+    t = sa.Params(1, 4, 1, 256, 64, window=8, token_top_k=16, index_dim=64)
+    need = sa.sparse_attn_workspace_bytes(t.cfg())
+    assert fwd_code(t, workspace=0x10000, workspace_bytes=need) == -1          # no indexer inputs
+    assert fwd_code(t) == -1                                # checked before the workspace
+    assert fwd_code(t, workspace=0x10000, workspace_bytes=need, idx_q=0x20008,
+                    idx_k=0x30000) == -5                                         # misaligned idx_q
 
 
 def test_strerror_covers_codes(lib):
