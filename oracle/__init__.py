@@ -42,13 +42,13 @@ def build(force: bool = True) -> str:
     return _LIB
 
 
-def _load():
+def _load(path=None):
     global _lib
-    if _lib is not None:
+    if _lib is not None and path is None:
         return _lib
-    if not os.path.exists(_LIB):
+    if path is None and not os.path.exists(_LIB):
         build()
-    lib = ctypes.CDLL(_LIB)
+    lib = ctypes.CDLL(path or _LIB)
     lib.orc_block_pool.argtypes = [_f32p, _i64, _i64, _i64, _i64, _f64p]
     lib.orc_block_pool.restype = None
     lib.orc_block_scores.argtypes = [_f32p, _f64p, _i64, _i64, _i64, _i64, _i64,
@@ -69,6 +69,26 @@ def _load():
     lib.orc_attend.restype = ctypes.c_int
     _lib = lib
     return lib
+
+
+class use_library:
+    """Context manager running the wrappers on another build of oracle.c
+    (the mutation tests use it to check that the pins catch planted bugs)."""
+
+    def __init__(self, path):
+        self.path = path
+
+    def __enter__(self):
+        global _lib
+        self.saved = _lib
+        _lib = None
+        _load(self.path)
+        return self
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.saved
+        return False
 
 
 def _f32(a):

@@ -336,3 +336,25 @@ def test_gaps_reported():
             assert s_next[i] == cand[m]
         else:
             assert np.isnan(s_next[i])
+
+
+# The score helpers the parity checker uses are plain dot products: compare
+# them with numpy's matmul of the same operands (future candidates -inf).
+def test_score_helpers_are_dot_products():
+    q, k = rnd((1, 2, 64, 8), 46), rnd((1, 1, 64, 8), 47)
+    kbar = oracle.block_pool(k, 8)
+    rows = np.arange(2 * 64)
+    sc = oracle.block_scores(q, kbar, 8, rows)
+    ref = np.einsum("hid,cd->hic", q[0].astype(np.float64), kbar[0, 0]).reshape(128, 8)
+    own = (rows % 64) // 8
+    for t in range(128):
+        np.testing.assert_allclose(sc[t, :own[t]], ref[t, :own[t]], atol=1e-12)
+        assert np.all(np.isneginf(sc[t, own[t]:]))
+    iq, ik = rnd((2, 40, 5), 48), rnd((2, 40, 5), 49)
+    trows = np.arange(80)
+    ts = oracle.token_scores(iq, ik, trows)
+    for r in trows:
+        b, i = divmod(int(r), 40)
+        ref = ik[b].astype(np.float64) @ iq[b, i].astype(np.float64)
+        np.testing.assert_allclose(ts[r, :i], ref[:i], atol=1e-12)
+        assert np.all(np.isneginf(ts[r, i:]))
