@@ -68,6 +68,8 @@ int make_plan(const sparse_attn_cfg* c, Plan* p) {
     const long long rows = (long long)P.Bt * P.Hq * P.N;
     const size_t esz = P.f32 ? 4 : 2;
     if (rows * P.D * (long long)esz > (1LL << 40)) return SA_E_UNSUPPORTED;
+    // One head's K or V (16-bit) must be addressable by a 32-bit byte offset.
+    if ((long long)P.N * P.D * 2 >= (1LL << 31)) return SA_E_UNSUPPORTED;
 
     P.gate = c->top_k > 0;
     if (P.gate) {

@@ -35,6 +35,14 @@
 #ifndef SA_SCHED
 #define SA_SCHED 0
 #endif
+// K fragment reads issued ahead of the S^T matrix-core ops (0 = in order).
+#ifndef SA_QKPF
+#define SA_QKPF 0
+#endif
+// Raise the wave priority while it issues matrix-core ops.
+#ifndef SA_PRIO
+#define SA_PRIO 0
+#endif
 
 namespace sa {
 
@@ -54,7 +62,11 @@ struct Tile {
     // transposing LDS loads, 4 keys x 32 bytes per 16-lane group: a stride of
     // 8 (mod 32) dwords keeps the 4 rows on distinct banks.
     static constexpr int KS = D + 8;
-    static constexpr int VS = D == 64 ? 80 : D == 80 ? 80 : 144;
+    // When O^T has padding rows (D = 80: rows 80..95), V carries a constant
+    // column of ones at dim D so that O^T row D accumulates the row sum of P
+    // on the matrix core; the columns from D on are set once per kernel.
+    static constexpr bool ONES = DPAD > D;
+    static constexpr int VS = D == 64 ? 80 : D == 80 ? 112 : 144;
     static constexpr int KELEMS = KT * KS;
     static constexpr int VELEMS = KT * VS;
     static constexpr int CHUNKS = KT * D / 8;      // 16-byte pieces of a tile
@@ -67,23 +79,56 @@ struct Stage {
     uint4 x[SPLIT][Tile<D>::CPT];
 };
 
-// Global -> registers for the 64-key tile starting at kt0 (K or V).
-// Branch-free: keys at or past kend read key kend-1 instead (finite data that
-// causality always masks), and threads past the last chunk repeat it (they
-// later write the same bytes to the same LDS address).
+// Source of the K or V tiles of one head ([N, D] 16-bit planes) and this
+// thread's byte offsets within a 64-key tile.  Each tile load builds a
+// buffer descriptor in scalar registers whose base is the tile's first key
+// and whose size is what is left of the head, so a tile costs scalar work
+// only; keys at or past N fall outside the descriptor and read as zero
+// (finite data that causality always masks).  Threads past the last chunk
+// repeat it (they later write the same bytes to the same LDS address).
 template <int D, int SPLIT>
-__device__ __forceinline__ void load_tile(Stage<D, SPLIT>& st, const uint16_t* const* src, int kt0,
-                                          int kend, int tid) {
+struct TileSrc {
+    uint64_t base[SPLIT];   // byte addresses, workgroup-uniform
+    int N;
+    int off[Tile<D>::CPT];
+};
+
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t u) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+    return ((uint64_t)hi << 32) | (uint64_t)lo;
+}
+
+template <int D, int SPLIT>
+__device__ __forceinline__ TileSrc<D, SPLIT> tile_src(const uint16_t* const* base, int N, int tid) {
     using T = Tile<D>;
+    TileSrc<D, SPLIT> ts;
 #pragma unroll
-    for (int p = 0; p < SPLIT; ++p)
+    for (int p = 0; p < SPLIT; ++p) ts.base[p] = uniform_u64((uint64_t)base[p]);
+    ts.N = N;
 #pragma unroll
-        for (int c = 0; c < T::CPT; ++c) {
-            const int idx = min(tid + c * NTHREADS, T::CHUNKS - 1);
-            const int row = idx / (D / 8), col = idx % (D / 8);
-            const int key = min(kt0 + row, kend - 1);
-            st.x[p][c] = *(const uint4*)(src[p] + (size_t)key * D + col * 8);
-        }
+    for (int c = 0; c < T::CPT; ++c) {
+        const int idx = min(tid + c * NTHREADS, T::CHUNKS - 1);
+        ts.off[c] = ((idx / (D / 8)) * D + (idx % (D / 8)) * 8) * 2;
+    }
+    return ts;
+}
+
+// Global -> registers for the 64-key tile starting at key kt0 (K or V);
+// requires 0 <= kt0 < N.
+template <int D, int SPLIT>
+__device__ __forceinline__ void load_tile(Stage<D, SPLIT>& st, const TileSrc<D, SPLIT>& ts, int kt0) {
+    using T = Tile<D>;
+    const int k0 = __builtin_amdgcn_readfirstlane(kt0);   // wave-uniform
+    const int bytes = (ts.N - k0) * D * 2;
+#pragma unroll
+    for (int p = 0; p < SPLIT; ++p) {
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(ts.base[p] + (uint64_t)k0 * D * 2), (short)0, bytes, 0x00020000);
+#pragma unroll
+        for (int c = 0; c < T::CPT; ++c)
+            st.x[p][c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, ts.off[c], 0, 0));
+    }
 }
 
 // Registers -> LDS, row-major with row stride STRIDE; planes PLANE apart.
@@ -102,11 +147,25 @@ __device__ __forceinline__ void store_tile(const Stage<D, SPLIT>& st, uint16_t* 
 
 // Before the key loop: V buffer 1 is read by the first iteration's P V,
 // whose P is zero; it is zeroed so no stale LDS bits (possibly NaN) meet it.
+// With the ones column, columns D.. of both buffers get their constant
+// values: 1 at dim D (fp16 for SPLIT 1, bf16 in the high plane for SPLIT 2),
+// 0 elsewhere.  Each 32-bit word is written by exactly one thread.
 template <int D, int SPLIT>
 __device__ __forceinline__ void zero_v_init(uint16_t* vs, int tid) {
     using T = Tile<D>;
-    uint32_t* b1 = (uint32_t*)(vs + SPLIT * T::VELEMS);
-    for (int x = tid; x < SPLIT * T::VELEMS / 2; x += NTHREADS) b1[x] = 0u;
+    if constexpr (T::ONES) {
+        constexpr int RW = T::VS / 2;   // 32-bit words per row
+        constexpr uint32_t one = SPLIT == 1 ? 0x3C00u : 0x3F80u;
+        uint32_t* w32 = (uint32_t*)vs;
+        for (int x = tid; x < 2 * SPLIT * KT * RW; x += NTHREADS) {
+            const int w = x % RW, pl = x / (RW * KT);   // pl = buffer * SPLIT + plane
+            if (pl >= SPLIT || 2 * w >= D)
+                w32[x] = (2 * w == D && pl % SPLIT == 0) ? one : 0u;
+        }
+    } else {
+        uint32_t* b1 = (uint32_t*)(vs + SPLIT * T::VELEMS);
+        for (int x = tid; x < SPLIT * T::VELEMS / 2; x += NTHREADS) b1[x] = 0u;
+    }
 }
 
 // Softmax state of one query row in one lane (the lane pair l, l^32 shares
@@ -173,6 +232,36 @@ __device__ __forceinline__ void qk_tile(const uint16_t* ks, const bf16x8 (&qf)[S
     const int col = lane & 31, hh = lane >> 5;
     s[0] = f32x16{};
     s[1] = f32x16{};
+#if SA_QKPF
+    if constexpr (SPLIT == 1) {
+        // Fragment f = 2*k + sub; the reads run SA_QKPF fragments ahead of
+        // the matrix-core ops that consume them.
+        constexpr int F = 2 * T::DK, PF = SA_QKPF < F ? SA_QKPF : F;
+        const uint16_t* base = ks + col * T::KS + 8 * hh;
+        auto frag = [&](int f) {
+            return *(const bf16x8*)(base + (f & 1) * 32 * T::KS + (f >> 1) * 16);
+        };
+        bf16x8 buf[PF];
+#pragma unroll
+        for (int f = 0; f < PF; ++f) buf[f] = frag(f);
+#pragma unroll
+        for (int f = 0; f < F; ++f) {
+            const bf16x8 a = buf[f % PF];
+            if (f + PF < F) buf[f % PF] = frag(f + PF);
+            s[f & 1] = mfma32(a, qf[0][f >> 1], s[f & 1]);
+        }
+        // Pin that order: PF reads, then each matrix-core op followed by the
+        // read it made room for.
+        __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+#pragma unroll
+        for (int f = 0; f + PF < F; ++f) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
+        return;
+    }
+#endif
 #pragma unroll
     for (int k_ = 0; k_ < T::DK; ++k_)
 #pragma unroll
@@ -206,12 +295,13 @@ __device__ __forceinline__ v4i16 read_tr(const uint16_t* p) {
 // block mb: lane group G = lane/16 covers dims mb*32 + 16*(G%2) .. +15 and
 // key half h = G/2; source lane 4r + q of the group points at key 4h + r,
 // dims +4q, so lane i of the group receives keys 4h..4h+3 of dim +i.  Dims
-// past D (padding rows of O^T, discarded) read dim 0 instead.
+// past D are the padding rows of O^T: they read the constant columns when V
+// carries the ones column, else dim 0 (rows discarded).
 template <int D>
 __device__ __forceinline__ int v_lane_offset(int lane, int mb) {
     const int j = lane & 15, r = j >> 2, q = j & 3, G = lane >> 4, h = G >> 1;
     int dim = mb * 32 + 16 * (G & 1) + 4 * q;
-    if (dim >= D) dim = 0;
+    if (!Tile<D>::ONES && dim >= D) dim = 0;
     return (4 * h + r) * Tile<D>::VS + dim;
 }
 
@@ -283,7 +373,7 @@ __device__ __forceinline__ void mask_tile_tok(f32x16 (&s)[2], int rk, uint32_t w
         }
 }
 
-template <int SPLIT>
+template <int SPLIT, bool ROWSUM>
 __device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], RowState& st, float c,
                                              uint4 (&pb)[4], uint4 (&pl)[4]) {
     const float mx = pair_max(tree_max32(s[0], s[1]));
@@ -298,7 +388,8 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], RowState& st, float
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
         for (int v = 0; v < 16; ++v) p[sub][v] = fast_exp2(fmaf(s[sub][v], c, nb));
-    st.l = fmaf(st.l, st.alpha, tree_sum32(p));
+    // Without the ones column of V the row sum is kept here, in fp32.
+    if constexpr (ROWSUM) st.l = fmaf(st.l, st.alpha, tree_sum32(p));
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
         const float* pk = &p[kk >> 1][8 * (kk & 1)];
@@ -340,11 +431,30 @@ __device__ __forceinline__ void kv_step(const uint16_t* ks, const uint16_t* vs_p
                                         uint32_t wl, bool tok = false, uint32_t tword = 0) {
     apply_rescale<D>(o, st);
     f32x16 s[2];
+#if SA_PRIO
+    __builtin_amdgcn_s_setprio(1);
+#endif
     qk_tile<D, SPLIT>(ks, qf, s, lane);
     if (tok) mask_tile_tok(s, rk, wl, masked, tword);   // token gate: every tile
     else if (masked) mask_tile(s, rk, wl);             // wave-uniform; edge tiles only
     pv_tile<D, SPLIT>(vs_prev, pb, pl, o, voff);
-    softmax_tile<SPLIT>(s, st, c, pb, pl);
+#if SA_PRIO
+    __builtin_amdgcn_s_setprio(0);
+#endif
+    softmax_tile<SPLIT, !Tile<D>::ONES>(s, st, c, pb, pl);
+#if SA_SCHED == 4
+    // P V matrix-core ops spread through the softmax VALU work: the operand
+    // reads of one op, then each op with the next op's reads and a slice of
+    // VALU instructions.
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * SPLIT, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);
+#pragma unroll
+    for (int i = 0; i < 4 * Tile<D>::DM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, SPLIT == 2 ? 3 : 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * SPLIT, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+    }
+#endif
 #if SA_SCHED == 3
     // V^T fragment reads first, then P V interleaved with the softmax VALU.
     __builtin_amdgcn_sched_group_barrier(0x100, 4 * Tile<D>::DM * SPLIT, 0);
@@ -365,6 +475,32 @@ __device__ __forceinline__ void kv_step(const uint16_t* ks, const uint16_t* vs_p
         __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
     }
 #endif
+#if SA_SCHED == 5
+    // Two P V ops first (they cover the latency of the last S^T op), then
+    // the row-max VALU work, then the remaining P V ops each with its
+    // operand reads and a slice of the exponentials.
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * SPLIT, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, SPLIT == 2 ? 3 : 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * SPLIT, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, SPLIT == 2 ? 3 : 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 26, 0);
+#pragma unroll
+    for (int i = 2; i < 4 * Tile<D>::DM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * SPLIT, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, SPLIT == 2 ? 3 : 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+    }
+#endif
+}
+
+// Sum of the row's P over the whole key loop (both lanes of the pair get it):
+// O^T row D (register 8 of the last row block in lanes 0..31, row D + 4 = 0
+// in lanes 32..63) with the ones column, else the fp32 partial sums.
+template <int D>
+__device__ __forceinline__ float row_sum(const f32x16 (&o)[Tile<D>::DM], const RowState& st) {
+    static_assert(!Tile<D>::ONES || D % 32 == 16, "ones row must sit at register 8");
+    if constexpr (Tile<D>::ONES) return pair_sum(o[Tile<D>::DM - 1][8]);
+    else return pair_sum(st.l);
 }
 
 template <int D, int SPLIT>
@@ -456,7 +592,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_rows_kernel(RowsArgs a) {
 #pragma unroll
     for (int mb = 0; mb < T::DM; ++mb) voff[mb] = v_lane_offset<D>(lane, mb);
     Stage<D, SPLIT> kst, vst;
-    load_tile<D, SPLIT>(kst, kp, t_begin * KT, N, tid);
+    const TileSrc<D, SPLIT> ksrc = tile_src<D, SPLIT>(kp, N, tid), vsrc = tile_src<D, SPLIT>(vp, N, tid);
+    load_tile<D, SPLIT>(kst, ksrc, t_begin * KT);
     store_tile<D, SPLIT, T::KS, T::KELEMS>(kst, lds_k[0], tid);
     __syncthreads();
 
@@ -464,8 +601,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_rows_kernel(RowsArgs a) {
     // not attend are masked (a tile outside a wave's rows is fully masked).
     for (int t = t_begin; t <= t_end; ++t) {
         const int it = t - t_begin;
-        load_tile<D, SPLIT>(kst, kp, min(t + 1, t_end) * KT, N, tid);
-        load_tile<D, SPLIT>(vst, vp, t * KT, N, tid);
+        load_tile<D, SPLIT>(kst, ksrc, min(t + 1, t_end) * KT);
+        load_tile<D, SPLIT>(vst, vsrc, t * KT);
         const int kt0 = t * KT;
         const bool full = kt0 + KT - 1 <= q0 &&
                           ((a.window > 0 && q1 - kt0 < a.window) ||
@@ -503,7 +640,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_rows_kernel(RowsArgs a) {
     if (!row_ok) return;
 
     // Combine: near part (this kernel), far partials, sink.
-    const float lt = pair_sum(rs.l);
+    const float lt = row_sum<D>(o, rs);
     const float lse_near = rs.m * a.scale + kLn2 * fast_log2(lt);
     float M = lse_near;
     const size_t pbase = prow * (size_t)a.kslots;
@@ -615,12 +752,13 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_blocks_kernel(BlocksArgs a) 
 #pragma unroll
     for (int mb = 0; mb < T::DM; ++mb) voff[mb] = v_lane_offset<D>(lane, mb);
     Stage<D, SPLIT> kst, vst;
-    load_tile<D, SPLIT>(kst, kp, k_begin, N, tid);
+    const TileSrc<D, SPLIT> ksrc = tile_src<D, SPLIT>(kp, N, tid), vsrc = tile_src<D, SPLIT>(vp, N, tid);
+    load_tile<D, SPLIT>(kst, ksrc, k_begin);
     store_tile<D, SPLIT, T::KS, T::KELEMS>(kst, lds_k[0], tid);
     __syncthreads();
     for (int t = 0; t < ntile; ++t) {
-        load_tile<D, SPLIT>(kst, kp, k_begin + min(t + 1, ntile - 1) * KT, N, tid);
-        load_tile<D, SPLIT>(vst, vp, k_begin + t * KT, N, tid);
+        load_tile<D, SPLIT>(kst, ksrc, k_begin + min(t + 1, ntile - 1) * KT);
+        load_tile<D, SPLIT>(vst, vsrc, k_begin + t * KT);
         kv_step<D, SPLIT>(lds_k[t & 1], lds_v[(t + 1) & 1], qf, o, rs, pb, pl, c, lane, voff, false, 0,
                           0u);
         store_tile<D, SPLIT, T::KS, T::KELEMS>(kst, lds_k[(t + 1) & 1], tid);
@@ -631,7 +769,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_blocks_kernel(BlocksArgs a) 
     pv_tile<D, SPLIT>(lds_v[(ntile - 1) & 1], pb, pl, o, voff);
     if (!ok) return;
 
-    const float lt = pair_sum(rs.l);
+    const float lt = row_sum<D>(o, rs);
     const float inv = 1.f / lt;
     const size_t pidx = prow * (size_t)a.kslots + slot;
     uint16_t* po = a.part_o + pidx * D;
