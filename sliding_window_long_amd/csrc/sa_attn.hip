@@ -31,19 +31,6 @@
 
 #include <math.h>
 
-// Instruction-group schedule of one key-loop step (see kv_step).
-#ifndef SA_SCHED
-#define SA_SCHED 0
-#endif
-// K fragment reads issued ahead of the S^T matrix-core ops (0 = in order).
-#ifndef SA_QKPF
-#define SA_QKPF 0
-#endif
-// Raise the wave priority while it issues matrix-core ops.
-#ifndef SA_PRIO
-#define SA_PRIO 0
-#endif
-
 namespace sa {
 
 constexpr int KT = 64;                 // keys per tile
@@ -62,11 +49,7 @@ struct Tile {
     // transposing LDS loads, 4 keys x 32 bytes per 16-lane group: a stride of
     // 8 (mod 32) dwords keeps the 4 rows on distinct banks.
     static constexpr int KS = D + 8;
-    // When O^T has padding rows (D = 80: rows 80..95), V carries a constant
-    // column of ones at dim D so that O^T row D accumulates the row sum of P
-    // on the matrix core; the columns from D on are set once per kernel.
-    static constexpr bool ONES = DPAD > D;
-    static constexpr int VS = D == 64 ? 80 : D == 80 ? 112 : 144;
+    static constexpr int VS = D == 128 ? 144 : 80;
     static constexpr int KELEMS = KT * KS;
     static constexpr int VELEMS = KT * VS;
     static constexpr int CHUNKS = KT * D / 8;      // 16-byte pieces of a tile
@@ -147,25 +130,11 @@ __device__ __forceinline__ void store_tile(const Stage<D, SPLIT>& st, uint16_t* 
 
 // Before the key loop: V buffer 1 is read by the first iteration's P V,
 // whose P is zero; it is zeroed so no stale LDS bits (possibly NaN) meet it.
-// With the ones column, columns D.. of both buffers get their constant
-// values: 1 at dim D (fp16 for SPLIT 1, bf16 in the high plane for SPLIT 2),
-// 0 elsewhere.  Each 32-bit word is written by exactly one thread.
 template <int D, int SPLIT>
 __device__ __forceinline__ void zero_v_init(uint16_t* vs, int tid) {
     using T = Tile<D>;
-    if constexpr (T::ONES) {
-        constexpr int RW = T::VS / 2;   // 32-bit words per row
-        constexpr uint32_t one = SPLIT == 1 ? 0x3C00u : 0x3F80u;
-        uint32_t* w32 = (uint32_t*)vs;
-        for (int x = tid; x < 2 * SPLIT * KT * RW; x += NTHREADS) {
-            const int w = x % RW, pl = x / (RW * KT);   // pl = buffer * SPLIT + plane
-            if (pl >= SPLIT || 2 * w >= D)
-                w32[x] = (2 * w == D && pl % SPLIT == 0) ? one : 0u;
-        }
-    } else {
-        uint32_t* b1 = (uint32_t*)(vs + SPLIT * T::VELEMS);
-        for (int x = tid; x < SPLIT * T::VELEMS / 2; x += NTHREADS) b1[x] = 0u;
-    }
+    uint32_t* b1 = (uint32_t*)(vs + SPLIT * T::VELEMS);
+    for (int x = tid; x < SPLIT * T::VELEMS / 2; x += NTHREADS) b1[x] = 0u;
 }
 
 // Softmax state of one query row in one lane (the lane pair l, l^32 shares
@@ -232,36 +201,6 @@ __device__ __forceinline__ void qk_tile(const uint16_t* ks, const bf16x8 (&qf)[S
     const int col = lane & 31, hh = lane >> 5;
     s[0] = f32x16{};
     s[1] = f32x16{};
-#if SA_QKPF
-    if constexpr (SPLIT == 1) {
-        // Fragment f = 2*k + sub; the reads run SA_QKPF fragments ahead of
-        // the matrix-core ops that consume them.
-        constexpr int F = 2 * T::DK, PF = SA_QKPF < F ? SA_QKPF : F;
-        const uint16_t* base = ks + col * T::KS + 8 * hh;
-        auto frag = [&](int f) {
-            return *(const bf16x8*)(base + (f & 1) * 32 * T::KS + (f >> 1) * 16);
-        };
-        bf16x8 buf[PF];
-#pragma unroll
-        for (int f = 0; f < PF; ++f) buf[f] = frag(f);
-#pragma unroll
-        for (int f = 0; f < F; ++f) {
-            const bf16x8 a = buf[f % PF];
-            if (f + PF < F) buf[f % PF] = frag(f + PF);
-            s[f & 1] = mfma32(a, qf[0][f >> 1], s[f & 1]);
-        }
-        // Pin that order: PF reads, then each matrix-core op followed by the
-        // read it made room for.
-        __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
-#pragma unroll
-        for (int f = 0; f + PF < F; ++f) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, PF, 0);
-        return;
-    }
-#endif
 #pragma unroll
     for (int k_ = 0; k_ < T::DK; ++k_)
 #pragma unroll
@@ -274,11 +213,6 @@ __device__ __forceinline__ void qk_tile(const uint16_t* ks, const bf16x8 (&qf)[S
                 s[sub] = mfma32(*(const bf16x8*)(ks + T::KELEMS + off), qf[0][k_], s[sub]);
             }
         }
-#if SA_SCHED >= 2
-    // All K fragment reads first, then the matrix-core ops.
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * T::DK * SPLIT, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 2 * T::DK * (SPLIT == 2 ? 3 : 1), 0);
-#endif
 }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -295,13 +229,12 @@ __device__ __forceinline__ v4i16 read_tr(const uint16_t* p) {
 // block mb: lane group G = lane/16 covers dims mb*32 + 16*(G%2) .. +15 and
 // key half h = G/2; source lane 4r + q of the group points at key 4h + r,
 // dims +4q, so lane i of the group receives keys 4h..4h+3 of dim +i.  Dims
-// past D are the padding rows of O^T: they read the constant columns when V
-// carries the ones column, else dim 0 (rows discarded).
+// past D (padding rows of O^T, discarded) read dim 0 instead.
 template <int D>
 __device__ __forceinline__ int v_lane_offset(int lane, int mb) {
     const int j = lane & 15, r = j >> 2, q = j & 3, G = lane >> 4, h = G >> 1;
     int dim = mb * 32 + 16 * (G & 1) + 4 * q;
-    if (!Tile<D>::ONES && dim >= D) dim = 0;
+    if (dim >= D) dim = 0;
     return (4 * h + r) * Tile<D>::VS + dim;
 }
 
@@ -373,10 +306,15 @@ __device__ __forceinline__ void mask_tile_tok(f32x16 (&s)[2], int rk, uint32_t w
         }
 }
 
-template <int SPLIT, bool ROWSUM>
-__device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], RowState& st, float c,
+// Row max of an S^T tile (both lanes of a row get it).
+__device__ __forceinline__ float tile_max(const f32x16 (&s)[2]) {
+    return pair_max(tree_max32(s[0], s[1]));
+}
+
+template <int SPLIT>
+__device__ __forceinline__ void softmax_tile(const f32x16 (&s)[2], RowState& st, float c,
                                              uint4 (&pb)[4], uint4 (&pl)[4]) {
-    const float mx = pair_max(tree_max32(s[0], s[1]));
+    const float mx = tile_max(s);
     // NaN-free test: true while m is still -inf and mx is finite; false when
     // both are -inf (a fully masked tile before the row's first key).
     st.need = mx > st.m + kLazy / c;
@@ -388,8 +326,7 @@ __device__ __forceinline__ void softmax_tile(f32x16 (&s)[2], RowState& st, float
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
         for (int v = 0; v < 16; ++v) p[sub][v] = fast_exp2(fmaf(s[sub][v], c, nb));
-    // Without the ones column of V the row sum is kept here, in fp32.
-    if constexpr (ROWSUM) st.l = fmaf(st.l, st.alpha, tree_sum32(p));
+    st.l = fmaf(st.l, st.alpha, tree_sum32(p));
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
         const float* pk = &p[kk >> 1][8 * (kk & 1)];
@@ -419,88 +356,20 @@ __device__ __forceinline__ void apply_rescale(f32x16 (&o)[Tile<D>::DM], RowState
     st.need = false;
 }
 
-// One step of the skewed key loop: the pending rescale of O, then, as
-// straight-line code the scheduler can interleave, S_t = K_t Q^T,
-// O += V_{t-1} P_{t-1} and the softmax of S_t into P_t.
+// One step of the skewed key loop without masking (the far-block kernel):
+// the pending rescale of O, then S_t = K_t Q^T, O += V_{t-1} P_{t-1} and the
+// softmax of S_t into P_t.
 template <int D, int SPLIT>
 __device__ __forceinline__ void kv_step(const uint16_t* ks, const uint16_t* vs_prev,
                                         const bf16x8 (&qf)[SPLIT][Tile<D>::DK],
                                         f32x16 (&o)[Tile<D>::DM], RowState& st, uint4 (&pb)[4],
                                         uint4 (&pl)[4], float c, int lane,
-                                        const int (&voff)[Tile<D>::DM], bool masked, int rk,
-                                        uint32_t wl, bool tok = false, uint32_t tword = 0) {
+                                        const int (&voff)[Tile<D>::DM]) {
     apply_rescale<D>(o, st);
     f32x16 s[2];
-#if SA_PRIO
-    __builtin_amdgcn_s_setprio(1);
-#endif
     qk_tile<D, SPLIT>(ks, qf, s, lane);
-    if (tok) mask_tile_tok(s, rk, wl, masked, tword);   // token gate: every tile
-    else if (masked) mask_tile(s, rk, wl);             // wave-uniform; edge tiles only
     pv_tile<D, SPLIT>(vs_prev, pb, pl, o, voff);
-#if SA_PRIO
-    __builtin_amdgcn_s_setprio(0);
-#endif
-    softmax_tile<SPLIT, !Tile<D>::ONES>(s, st, c, pb, pl);
-#if SA_SCHED == 4
-    // P V matrix-core ops spread through the softmax VALU work: the operand
-    // reads of one op, then each op with the next op's reads and a slice of
-    // VALU instructions.
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * SPLIT, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);
-#pragma unroll
-    for (int i = 0; i < 4 * Tile<D>::DM; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, SPLIT == 2 ? 3 : 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * SPLIT, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-    }
-#endif
-#if SA_SCHED == 3
-    // V^T fragment reads first, then P V interleaved with the softmax VALU.
-    __builtin_amdgcn_sched_group_barrier(0x100, 4 * Tile<D>::DM * SPLIT, 0);
-#pragma unroll
-    for (int i = 0; i < 4 * Tile<D>::DM * (SPLIT == 2 ? 3 : 1); ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-    }
-#endif
-#if SA_SCHED == 1
-    // K fragment reads, S^T, then P V interleaved with the softmax VALU.
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * Tile<D>::DK, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 2 * Tile<D>::DK * (SPLIT == 2 ? 3 : 1), 0);
-#pragma unroll
-    for (int i = 0; i < 4 * Tile<D>::DM; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, SPLIT, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, SPLIT == 2 ? 3 : 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-    }
-#endif
-#if SA_SCHED == 5
-    // Two P V ops first (they cover the latency of the last S^T op), then
-    // the row-max VALU work, then the remaining P V ops each with its
-    // operand reads and a slice of the exponentials.
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * SPLIT, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, SPLIT == 2 ? 3 : 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * SPLIT, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, SPLIT == 2 ? 3 : 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 26, 0);
-#pragma unroll
-    for (int i = 2; i < 4 * Tile<D>::DM; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * SPLIT, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, SPLIT == 2 ? 3 : 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-    }
-#endif
-}
-
-// Sum of the row's P over the whole key loop (both lanes of the pair get it):
-// O^T row D (register 8 of the last row block in lanes 0..31, row D + 4 = 0
-// in lanes 32..63) with the ones column, else the fp32 partial sums.
-template <int D>
-__device__ __forceinline__ float row_sum(const f32x16 (&o)[Tile<D>::DM], const RowState& st) {
-    static_assert(!Tile<D>::ONES || D % 32 == 16, "ones row must sit at register 8");
-    if constexpr (Tile<D>::ONES) return pair_sum(o[Tile<D>::DM - 1][8]);
-    else return pair_sum(st.l);
+    softmax_tile<SPLIT>(s, st, c, pb, pl);
 }
 
 template <int D, int SPLIT>
@@ -514,6 +383,63 @@ __device__ __forceinline__ void load_q(bf16x8 (&qf)[SPLIT][Tile<D>::DK], const u
             if (ok) u = *(const uint4*)(qp[p] + row_off + ks_ * 16 + 8 * hh);
             qf[p][ks_] = as_bf16x8(u);
         }
+}
+
+// Epilogue of the query-centric kernels: combine the near part (o, row sum
+// lt, exponent base m), the far-block partials of the row and the sink
+// column; write out and lse.
+template <int D>
+__device__ __forceinline__ void finish_rows(const RowsArgs& a, f32x16 (&o)[Tile<D>::DM], float lt,
+                                            float m, size_t prow, int h, int nfar, int hh) {
+    using T = Tile<D>;
+    const float lse_near = m * a.scale + kLn2 * fast_log2(lt);
+    float M = lse_near;
+    const size_t pbase = prow * (size_t)a.kslots;
+    for (int s_ = 0; s_ < nfar; ++s_) M = fmaxf(M, a.part_lse[pbase + s_]);
+    const float z = a.sink ? a.sink[h] : -INFINITY;
+    M = fmaxf(M, z);
+    float total = __expf(lse_near - M);
+    const float wn = total / lt;
+#pragma unroll
+    for (int mb = 0; mb < T::DM; ++mb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[mb][v] *= wn;
+    for (int s_ = 0; s_ < nfar; ++s_) {
+        const float w = __expf(a.part_lse[pbase + s_] - M);
+        total += w;
+        const uint16_t* po = a.part_o + (pbase + s_) * D;
+#pragma unroll
+        for (int mb = 0; mb < T::DM; ++mb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int d0 = mb * 32 + 8 * j + 4 * hh;
+                if (d0 < D) {
+                    const uint2 raw = *(const uint2*)(po + d0);
+                    const _Float16* hv = (const _Float16*)&raw;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[mb][4 * j + e] += w * (float)hv[e];
+                }
+            }
+    }
+    if (a.sink) total += __expf(z - M);
+    const float inv = 1.f / total;
+#pragma unroll
+    for (int mb = 0; mb < T::DM; ++mb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int d0 = mb * 32 + 8 * j + 4 * hh;
+            if (d0 < D) {
+                const float v0 = o[mb][4 * j] * inv, v1 = o[mb][4 * j + 1] * inv;
+                const float v2 = o[mb][4 * j + 2] * inv, v3 = o[mb][4 * j + 3] * inv;
+                if (a.out_f32) {
+                    *(float4*)((float*)a.out + prow * D + d0) = make_float4(v0, v1, v2, v3);
+                } else {
+                    __bf16 r[4] = {(__bf16)v0, (__bf16)v1, (__bf16)v2, (__bf16)v3};
+                    *(uint2*)((uint16_t*)a.out + prow * D + d0) = *(const uint2*)r;
+                }
+            }
+        }
+    if (hh == 0) a.lse[prow] = M + kLn2 * fast_log2(total);
 }
 
 // ---------------------------------------------------------------------------
@@ -597,39 +523,53 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_rows_kernel(RowsArgs a) {
     store_tile<D, SPLIT, T::KS, T::KELEMS>(kst, lds_k[0], tid);
     __syncthreads();
 
-    // Every wave walks every tile of the workgroup's range; keys a row does
-    // not attend are masked (a tile outside a wave's rows is fully masked).
-    for (int t = t_begin; t <= t_end; ++t) {
-        const int it = t - t_begin;
-        load_tile<D, SPLIT>(kst, ksrc, min(t + 1, t_end) * KT);
-        load_tile<D, SPLIT>(vst, vsrc, t * KT);
+    // Mask of key tile t for this wave's rows: keys a row does not attend
+    // become -inf (a tile outside a wave's rows is fully masked).  Tiles
+    // that are entirely inside every row's window, or inside every row's own
+    // block, need no mask (wave-uniform test).
+    auto mask_t = [&](f32x16 (&sv)[2], int t) {
         const int kt0 = t * KT;
-        const bool full = kt0 + KT - 1 <= q0 &&
-                          ((a.window > 0 && q1 - kt0 < a.window) ||
-                           (a.gate && kt0 / a.B == q0 / a.B && q1 / a.B == q0 / a.B));
-        uint32_t wl = wl_window;
-        if (!full && a.gate) {
-            const int dlt = row_blk - kt0 / a.B;
-            const bool blk_ok = dlt == 0 || (dlt >= 1 && dlt <= a.span && dlt <= 32 &&
-                                             ((near_bits >> (dlt - 1)) & 1u));
-            if (blk_ok) wl = 0x80000000u;
-        }
+        const int rk = row - kt0 - 4 * hh;
         if constexpr (TOK) {
             // This lane's keep bits for the tile; key tiles past the wave's
-            // rows hold no kept key.
+            // rows hold no kept key.  Only 32-key halves kc <= rt are
+            // written; a half past the row tile (kc = rt + 1 when rt is
+            // even) is all future keys: cleared.
             const int nt32 = (N + 31) / 32, nt64 = (N + KT - 1) / KT, rt = q0 / 32;
-            // Only 32-key halves kc <= rt are written; a half past the row
-            // tile (kc = rt + 1 when rt is even) is all future keys: cleared.
             uint32_t tword =
                 t <= rt / 2 ? a.tokmask[(((size_t)b * nt32 + rt) * nt64 + t) * 64 + lane] : 0u;
             if (2 * t + 1 > rt) tword &= 0xffffu;
             const bool near = kt0 + KT - 1 >= q0 - a.window + 1;   // tile meets a window
-            kv_step<D, SPLIT>(lds_k[it & 1], lds_v[(it + 1) & 1], qf, o, rs, pb, pl, c, lane, voff,
-                              near, row - kt0 - 4 * hh, wl_window, true, tword);
+            mask_tile_tok(sv, rk, wl_window, near, tword);
         } else {
-            kv_step<D, SPLIT>(lds_k[it & 1], lds_v[(it + 1) & 1], qf, o, rs, pb, pl, c, lane, voff,
-                              !full, row - kt0 - 4 * hh, wl);
+            const bool full = kt0 + KT - 1 <= q0 &&
+                              ((a.window > 0 && q1 - kt0 < a.window) ||
+                               (a.gate && kt0 / a.B == q0 / a.B && q1 / a.B == q0 / a.B));
+            if (!full) {
+                uint32_t wl = wl_window;
+                if (a.gate) {
+                    const int dlt = row_blk - kt0 / a.B;
+                    const bool blk_ok = dlt == 0 || (dlt >= 1 && dlt <= a.span && dlt <= 32 &&
+                                                     ((near_bits >> (dlt - 1)) & 1u));
+                    if (blk_ok) wl = 0x80000000u;
+                }
+                mask_tile(sv, rk, wl);
+            }
         }
+    };
+
+    // One-stage skew: the step of tile t computes S_t, O += V_{t-1}
+    // P_{t-1} and P_t; V is staged one tile behind K.
+    for (int t = t_begin; t <= t_end; ++t) {
+        const int it = t - t_begin;
+        load_tile<D, SPLIT>(kst, ksrc, min(t + 1, t_end) * KT);
+        load_tile<D, SPLIT>(vst, vsrc, t * KT);
+        apply_rescale<D>(o, rs);
+        f32x16 sv[2];
+        qk_tile<D, SPLIT>(lds_k[it & 1], qf, sv, lane);
+        mask_t(sv, t);
+        pv_tile<D, SPLIT>(lds_v[(it + 1) & 1], pb, pl, o, voff);
+        softmax_tile<SPLIT>(sv, rs, c, pb, pl);
         store_tile<D, SPLIT, T::KS, T::KELEMS>(kst, lds_k[(it + 1) & 1], tid);
         store_tile<D, SPLIT, T::VS, T::VELEMS>(vst, lds_v[it & 1], tid);
         __syncthreads();
@@ -639,56 +579,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_rows_kernel(RowsArgs a) {
 
     if (!row_ok) return;
 
-    // Combine: near part (this kernel), far partials, sink.
-    const float lt = row_sum<D>(o, rs);
-    const float lse_near = rs.m * a.scale + kLn2 * fast_log2(lt);
-    float M = lse_near;
-    const size_t pbase = prow * (size_t)a.kslots;
-    for (int s_ = 0; s_ < nfar; ++s_) M = fmaxf(M, a.part_lse[pbase + s_]);
-    const float z = a.sink ? a.sink[h] : -INFINITY;
-    M = fmaxf(M, z);
-    float total = __expf(lse_near - M);
-    const float wn = total / lt;
-#pragma unroll
-    for (int mb = 0; mb < T::DM; ++mb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) o[mb][v] *= wn;
-    for (int s_ = 0; s_ < nfar; ++s_) {
-        const float w = __expf(a.part_lse[pbase + s_] - M);
-        total += w;
-        const uint16_t* po = a.part_o + (pbase + s_) * D;
-#pragma unroll
-        for (int mb = 0; mb < T::DM; ++mb)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int d0 = mb * 32 + 8 * j + 4 * hh;
-                if (d0 < D) {
-                    const uint2 raw = *(const uint2*)(po + d0);
-                    const _Float16* hv = (const _Float16*)&raw;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) o[mb][4 * j + e] += w * (float)hv[e];
-                }
-            }
-    }
-    if (a.sink) total += __expf(z - M);
-    const float inv = 1.f / total;
-#pragma unroll
-    for (int mb = 0; mb < T::DM; ++mb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int d0 = mb * 32 + 8 * j + 4 * hh;
-            if (d0 < D) {
-                const float v0 = o[mb][4 * j] * inv, v1 = o[mb][4 * j + 1] * inv;
-                const float v2 = o[mb][4 * j + 2] * inv, v3 = o[mb][4 * j + 3] * inv;
-                if (a.out_f32) {
-                    *(float4*)((float*)a.out + prow * D + d0) = make_float4(v0, v1, v2, v3);
-                } else {
-                    __bf16 r[4] = {(__bf16)v0, (__bf16)v1, (__bf16)v2, (__bf16)v3};
-                    *(uint2*)((uint16_t*)a.out + prow * D + d0) = *(const uint2*)r;
-                }
-            }
-        }
-    if (hh == 0) a.lse[prow] = M + kLn2 * fast_log2(total);
+    finish_rows<D>(a, o, pair_sum(rs.l), rs.m, prow, h, nfar, hh);
 }
 
 // ---------------------------------------------------------------------------
@@ -759,8 +650,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_blocks_kernel(BlocksArgs a) 
     for (int t = 0; t < ntile; ++t) {
         load_tile<D, SPLIT>(kst, ksrc, k_begin + min(t + 1, ntile - 1) * KT);
         load_tile<D, SPLIT>(vst, vsrc, k_begin + t * KT);
-        kv_step<D, SPLIT>(lds_k[t & 1], lds_v[(t + 1) & 1], qf, o, rs, pb, pl, c, lane, voff, false, 0,
-                          0u);
+        kv_step<D, SPLIT>(lds_k[t & 1], lds_v[(t + 1) & 1], qf, o, rs, pb, pl, c, lane, voff);
         store_tile<D, SPLIT, T::KS, T::KELEMS>(kst, lds_k[(t + 1) & 1], tid);
         store_tile<D, SPLIT, T::VS, T::VELEMS>(vst, lds_v[t & 1], tid);
         __syncthreads();
@@ -769,7 +659,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_blocks_kernel(BlocksArgs a) 
     pv_tile<D, SPLIT>(lds_v[(ntile - 1) & 1], pb, pl, o, voff);
     if (!ok) return;
 
-    const float lt = row_sum<D>(o, rs);
+    const float lt = pair_sum(rs.l);
     const float inv = 1.f / lt;
     const size_t pidx = prow * (size_t)a.kslots + slot;
     uint16_t* po = a.part_o + pidx * D;
