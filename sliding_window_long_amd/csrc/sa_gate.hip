@@ -113,9 +113,24 @@ __device__ __forceinline__ void sort_asc(int (&x)[M]) {
             }
 }
 
+// Candidate blocks are scored 32 at a time.  The three planes of those 32
+// pooled keys go through LDS (double buffered, rows D + 8 elements apart so
+// the 16-byte reads of 32 consecutive rows hit distinct banks); every wave
+// of the workgroup reads them from there as the A operand of
+// S^T = Kbar Q^T.
+template <int D>
+struct GateTile {
+    static constexpr int RS = D + 8;                 // LDS row stride
+    static constexpr int PLANE = 32 * RS;            // one plane of 32 rows
+    static constexpr int CHUNKS = 3 * 32 * D / 8;    // 16-byte pieces per tile
+    static constexpr int CPT = (CHUNKS + 255) / 256;
+};
+
 template <int D, int M, int QSPLIT>
 __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
+    using GT = GateTile<D>;
     constexpr int DK = D / 16;
+    __shared__ __align__(16) uint16_t lds[2][3 * GT::PLANE];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int col = lane & 31, hh = lane >> 5;
     const int BH = a.Bt * a.Hq;
@@ -123,8 +138,7 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
     const int bh = blockIdx.x % BH;
     const int tile = ntiles - 1 - (int)(blockIdx.x / BH);
     const int b = bh / a.Hq, h = bh % a.Hq, g = h / (a.Hq / a.Hkv);
-    const int q0 = tile * 128 + wave * 32;
-    if (q0 >= a.N) return;
+    const int q0 = tile * 128 + __builtin_amdgcn_readfirstlane(wave) * 32;
     const int row = q0 + col;
     const bool row_ok = row < a.N;
     const size_t prow = (size_t)bh * a.N + row;
@@ -140,38 +154,71 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
         }
 
     const int row_blk = (row_ok ? row : a.N - 1) / a.B;
-    const int q1 = min(q0 + 31, a.N - 1);
-    const int ncand_wave = q1 / a.B;              // candidates are blocks < own block
+    const int last = min(tile * 128 + 127, a.N - 1);
+    const int ncand_wg = last / a.B;                           // candidates: blocks < own block
+    const int ncand_wave = q0 < a.N ? min(q0 + 31, a.N - 1) / a.B : 0;
+    const int ntc = (ncand_wg + 31) / 32;
     const uint32_t mask = (1u << a.idx_bits) - 1u;
     const uint16_t* kb = a.kb3 + (size_t)(b * a.Hkv + g) * a.n * D;
+
+    // Staging of candidate tile mt: chunk x = (plane, row, 16-byte column).
+    uint4 st[GT::CPT];
+    auto load = [&](int mt) {
+#pragma unroll
+        for (int c = 0; c < GT::CPT; ++c) {
+            const int x = min(tid + 256 * c, GT::CHUNKS - 1);
+            const int pl = x / (32 * D / 8), r = (x / (D / 8)) % 32, cc = x % (D / 8);
+            const int cblk = min(mt * 32 + r, a.n - 1);
+            st[c] = *(const uint4*)(kb + pl * a.plane + (size_t)cblk * D + cc * 8);
+        }
+    };
+    auto store = [&](uint16_t* dst) {
+#pragma unroll
+        for (int c = 0; c < GT::CPT; ++c) {
+            const int x = min(tid + 256 * c, GT::CHUNKS - 1);
+            const int pl = x / (32 * D / 8), r = (x / (D / 8)) % 32, cc = x % (D / 8);
+            *(uint4*)(dst + pl * GT::PLANE + r * GT::RS + cc * 8) = st[c];
+        }
+    };
 
     uint32_t L[M];
 #pragma unroll
     for (int t = 0; t < M; ++t) L[t] = 0u;
 
-    for (int mt = 0; mt * 32 < ncand_wave; ++mt) {
-        const int cblk_a = mt * 32 + col;         // A-operand row this lane loads
-        f32x16 acc = {};
+    if (ntc > 0) {
+        load(0);
+        store(lds[0]);
+    }
+    __syncthreads();
+    for (int mt = 0; mt < ntc; ++mt) {
+        if (mt + 1 < ntc) load(mt + 1);
+        if (mt * 32 < ncand_wave) {
+            const uint16_t* src = lds[mt & 1] + col * GT::RS + 8 * hh;
+            f32x16 acc = {};
 #pragma unroll
-        for (int ks = 0; ks < DK; ++ks) {
+            for (int ks = 0; ks < DK; ++ks) {
 #pragma unroll
-            for (int p = 0; p < 3; ++p) {
-                uint4 u = make_uint4(0, 0, 0, 0);
-                if (cblk_a < a.n)
-                    u = *(const uint4*)(kb + p * a.plane + (size_t)cblk_a * D + ks * 16 + 8 * hh);
-                const bf16x8 av = as_bf16x8(u);
-                acc = mfma32(av, qf[0][ks], acc);
-                if constexpr (QSPLIT == 2) {
-                    if (p < 2) acc = mfma32(av, qf[1][ks], acc);
+                for (int p = 0; p < 3; ++p) {
+                    const bf16x8 av = *(const bf16x8*)(src + p * GT::PLANE + ks * 16);
+                    acc = mfma32(av, qf[0][ks], acc);
+                    if constexpr (QSPLIT == 2) {
+                        if (p < 2) acc = mfma32(av, qf[1][ks], acc);
+                    }
                 }
             }
-        }
+            // Insert the 16 scores of this lane; a score that does not beat
+            // the lane's current M-th key cannot enter its list, and a wave
+            // in which no lane has such a score skips the insertion.
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int cblk = mt * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
-            // A key of 0 ranks below every real key: inserting it is a no-op.
-            insert_desc<M>(L, cblk < row_blk ? order_key(acc[v], cblk, mask) : 0u);
+            for (int v = 0; v < 16; ++v) {
+                const int cblk = mt * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
+                const uint32_t key = cblk < row_blk ? order_key(acc[v], cblk, mask) : 0u;
+                const bool in = key > L[M - 1];
+                if (__any(in)) insert_desc<M>(L, in ? key : 0u);   // inserting 0 changes nothing
+            }
         }
+        if (mt + 1 < ntc) store(lds[(mt + 1) & 1]);
+        __syncthreads();
     }
     // Merge with the partner lane, which scored the other half of the blocks.
     uint32_t P[M];

@@ -34,6 +34,9 @@ constexpr int TOK_THREADS = 64 * TOK_WAVES;
 constexpr uint32_t kTokAll = 1u;    // row keeps every candidate
 constexpr uint32_t kTokNone = 2u;   // row keeps nothing
 constexpr uint32_t kTokDone = 4u;   // threshold final
+// Per-row 256-bin histograms in LDS, 257 words apart so that rows adding
+// to the same bin hit different banks.
+constexpr int HSTRIDE = 257;
 
 __device__ __forceinline__ uint32_t ord32(float s) {
     const uint32_t u = __float_as_uint(s);
@@ -71,12 +74,13 @@ __device__ __forceinline__ f32x16 index_scores(const TokArgs& a, int bt, int kc,
 // tiles).  pass 0..5: radix histogram step; pass 6: write the keep mask.
 template <int SPLIT>
 __global__ __launch_bounds__(TOK_THREADS) void token_select_kernel(TokArgs a, int pass) {
-    __shared__ uint32_t hist[32 * 256];
+    __shared__ uint32_t hist[32 * HSTRIDE];
     __shared__ int s_skip;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int col = lane & 31, hh = lane >> 5;
     const int nt = (a.N + 31) / 32;
-    const int rt = blockIdx.x % nt, bt = blockIdx.x / nt;
+    // Row tiles with the most candidates first (they run longest).
+    const int rt = nt - 1 - (int)(blockIdx.x % nt), bt = blockIdx.x / nt;
     const int r0 = rt * 32;
     const int row = r0 + col;
     const bool row_ok = row < a.N;
@@ -103,7 +107,7 @@ __global__ __launch_bounds__(TOK_THREADS) void token_select_kernel(TokArgs a, in
         if (tid == 0) s_skip = 1;
         __syncthreads();
         if (!(flags & kTokDone)) s_skip = 0;   // benign race: every writer stores 0
-        for (int x = tid; x < 32 * 256; x += TOK_THREADS) hist[x] = 0;
+        for (int x = tid; x < 32 * HSTRIDE; x += TOK_THREADS) hist[x] = 0;
         __syncthreads();
         if (s_skip) {
             if (pass == 0 && tid < 32 && row_ok) state[row] = stt;
@@ -143,7 +147,7 @@ __global__ __launch_bounds__(TOK_THREADS) void token_select_kernel(TokArgs a, in
                     if (pass == 5) take = take && ((ik ^ preidx) >> 8) == 0;
                     digit = (ik >> shift) & 0xffu;
                 }
-                if (take) atomicAdd(&hist[col * 256 + digit], 1u);
+                if (take) atomicAdd(&hist[col * HSTRIDE + digit], 1u);
             }
         } else {
             // Keep mask: key >= threshold (all / none handled by the flags).
@@ -168,11 +172,11 @@ __global__ __launch_bounds__(TOK_THREADS) void token_select_kernel(TokArgs a, in
             uint32_t k = (uint32_t)stt.z, cum = 0;
             int b = 255;
             for (; b > 0; --b) {
-                const uint32_t h = hist[tid * 256 + b];
+                const uint32_t h = hist[tid * HSTRIDE + b];
                 if (cum + h >= k) break;
                 cum += h;
             }
-            const uint32_t hb = hist[tid * 256 + b];
+            const uint32_t hb = hist[tid * HSTRIDE + b];
             k -= cum;
             uint32_t fl = flags;
             if (pass < 4) {
