@@ -98,7 +98,8 @@ int make_plan(const sparse_attn_cfg* c, Plan* p) {
         }
         P.max_entries = per_head * P.Bt * P.Hq;
         P.far = P.max_entries > 0;
-        if ((long long)P.N * P.G * P.kslots >= (1LL << 31) || P.max_entries >= (1LL << 31))
+        if ((long long)P.N * P.G * P.kslots >= (1LL << 31) || P.max_entries >= (1LL << 31) ||
+            rows * P.kslots >= (1LL << 31))   // partial slots are indexed with 32 bits
             return SA_E_UNSUPPORTED;
         long long mc = (P.max_entries + kRowsPerChunk - 1) / kRowsPerChunk + P.lists;
         mc = (mc + 7) / 8 * 8;

@@ -1,0 +1,372 @@
+// sa_attn_common.hpp -- tile machinery shared by the attention kernels
+// (query-centric in sa_attn.hip, KV-centric in sa_blocks.hip).
+//
+// Every tile does S^T = K Q^T (bf16 MFMA 32x32x16, fp32 accumulation), an
+// online softmax in base 2 on the VALU, and O^T += V^T P^T.  K and V tiles sit
+// row-major in LDS; the V^T operand comes from the transposing LDS reads of
+// gfx950 (ds_read_b64_tr_b16).  The key loop is skewed by one tile:
+// iteration t issues S_t = K_t Q^T, then O += V_{t-1} P_{t-1}, then the
+// softmax of S_t.  V is staged one tile behind K, which keeps both
+// double-buffered.
+#pragma once
+
+#include "sa_device.hpp"
+#include "sa_internal.hpp"
+
+#include <math.h>
+
+namespace sa {
+
+constexpr int KT = 64;                 // keys per tile
+constexpr int NWAVES = 4;              // waves per workgroup
+constexpr int NTHREADS = 64 * NWAVES;
+constexpr int RT = 32 * NWAVES;        // query rows per workgroup
+
+template <int D>
+struct Tile {
+    static constexpr int DK = D / 16;              // contraction steps of K Q^T
+    static constexpr int DM = (D + 31) / 32;       // 32-row blocks of O^T
+    static constexpr int DPAD = DM * 32;
+    // Row strides (elements) of the K and V tiles in LDS, both row-major
+    // [key][dim].  K rows are read 16 bytes per lane by 32 consecutive keys:
+    // D + 8 puts those reads on distinct banks.  V rows are read by the
+    // transposing LDS loads, 4 keys x 32 bytes per 16-lane group: a stride of
+    // 8 (mod 32) dwords keeps the 4 rows on distinct banks.
+    static constexpr int KS = D + 8;
+    static constexpr int VS = D == 128 ? 144 : 80;
+    static constexpr int KELEMS = KT * KS;
+    static constexpr int VELEMS = KT * VS;
+    static constexpr int CHUNKS = KT * D / 8;      // 16-byte pieces of a tile
+    static constexpr int CPT = (CHUNKS + NTHREADS - 1) / NTHREADS;
+};
+
+// Registers holding one K or V tile between its global load and LDS store.
+template <int D, int SPLIT>
+struct Stage {
+    uint4 x[SPLIT][Tile<D>::CPT];
+};
+
+// Source of the K or V tiles of one head ([N, D] 16-bit planes) and this
+// thread's byte offsets within a 64-key tile.  Each tile load builds a
+// buffer descriptor in scalar registers whose base is the tile's first key
+// and whose size is what is left of the head, so a tile costs scalar work
+// only; keys at or past N fall outside the descriptor and read as zero
+// (finite data that causality always masks).  Threads past the last chunk
+// repeat it (they later write the same bytes to the same LDS address).
+template <int D, int SPLIT>
+struct TileSrc {
+    uint64_t base[SPLIT];   // byte addresses, workgroup-uniform
+    int N;
+    int off[Tile<D>::CPT];
+};
+
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t u) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+    return ((uint64_t)hi << 32) | (uint64_t)lo;
+}
+
+template <int D, int SPLIT>
+__device__ __forceinline__ TileSrc<D, SPLIT> tile_src(const uint16_t* const* base, int N, int tid) {
+    using T = Tile<D>;
+    TileSrc<D, SPLIT> ts;
+#pragma unroll
+    for (int p = 0; p < SPLIT; ++p) ts.base[p] = uniform_u64((uint64_t)base[p]);
+    ts.N = N;
+#pragma unroll
+    for (int c = 0; c < T::CPT; ++c) {
+        const int idx = min(tid + c * NTHREADS, T::CHUNKS - 1);
+        ts.off[c] = ((idx / (D / 8)) * D + (idx % (D / 8)) * 8) * 2;
+    }
+    return ts;
+}
+
+// Global -> registers for the 64-key tile starting at key kt0 (K or V);
+// requires 0 <= kt0 < N.
+template <int D, int SPLIT>
+__device__ __forceinline__ void load_tile(Stage<D, SPLIT>& st, const TileSrc<D, SPLIT>& ts, int kt0) {
+    using T = Tile<D>;
+    const int k0 = __builtin_amdgcn_readfirstlane(kt0);   // wave-uniform
+    const int bytes = (ts.N - k0) * D * 2;
+#pragma unroll
+    for (int p = 0; p < SPLIT; ++p) {
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(ts.base[p] + (uint64_t)k0 * D * 2), (short)0, bytes, 0x00020000);
+#pragma unroll
+        for (int c = 0; c < T::CPT; ++c)
+            st.x[p][c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, ts.off[c], 0, 0));
+    }
+}
+
+// Registers -> LDS, row-major with row stride STRIDE; planes PLANE apart.
+template <int D, int SPLIT, int STRIDE, int PLANE>
+__device__ __forceinline__ void store_tile(const Stage<D, SPLIT>& st, uint16_t* dst, int tid) {
+    using T = Tile<D>;
+#pragma unroll
+    for (int p = 0; p < SPLIT; ++p)
+#pragma unroll
+        for (int c = 0; c < T::CPT; ++c) {
+            const int idx = min(tid + c * NTHREADS, T::CHUNKS - 1);
+            const int row = idx / (D / 8), col = idx % (D / 8);
+            *(uint4*)(dst + p * PLANE + row * STRIDE + col * 8) = st.x[p][c];
+        }
+}
+
+// Before the key loop: V buffer 1 is read by the first iteration's P V,
+// whose P is zero; it is zeroed so no stale LDS bits (possibly NaN) meet it.
+template <int D, int SPLIT>
+__device__ __forceinline__ void zero_v_init(uint16_t* vs, int tid) {
+    using T = Tile<D>;
+    uint32_t* b1 = (uint32_t*)(vs + SPLIT * T::VELEMS);
+    for (int x = tid; x < SPLIT * T::VELEMS / 2; x += NTHREADS) b1[x] = 0u;
+}
+
+// Softmax state of one query row in one lane (the lane pair l, l^32 shares
+// the row and keeps the same m).
+struct RowState {
+    float m;      // exponent base, raw dot-product units; lags the running max
+                  // by less than kLazy / c (rescaling is deferred until then)
+    float l;      // this lane's partial sum of exp2((s - m) c)
+    float alpha;  // pending rescale of O from the last softmax
+    bool need;    // alpha != 1 for this row
+};
+
+// Rescale the accumulators only when the row max grew by more than 2^8 in
+// the exponent: until then exp2((s - m) c) <= 256, harmless in fp32 and bf16,
+// and the final normalisation uses the same base.
+constexpr float kLazy = 8.f;
+
+__device__ __forceinline__ float max3f(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
+
+// v_permlane32_swap gives every lane the pair {x of lane l%32, x of lane
+// l%32+32}, lower lane first, so both lanes of a row compute the same value.
+__device__ __forceinline__ float pair_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                    false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float tree_max32(const f32x16& x, const f32x16& y) {
+    float t[11];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) t[i] = max3f(x[3 * i], x[3 * i + 1], x[3 * i + 2]);
+    t[5] = max3f(x[15], y[0], y[1]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t[6 + i] = max3f(y[2 + 3 * i], y[3 + 3 * i], y[4 + 3 * i]);
+    t[10] = fmaxf(y[14], y[15]);
+    const float u0 = max3f(t[0], t[1], t[2]), u1 = max3f(t[3], t[4], t[5]);
+    const float u2 = max3f(t[6], t[7], t[8]), u3 = fmaxf(t[9], t[10]);
+    return fmaxf(max3f(u0, u1, u2), u3);
+}
+
+__device__ __forceinline__ float tree_sum32(const float (&p)[2][16]) {
+    float t[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) t[i] = p[0][i] + p[1][i];
+#pragma unroll
+    for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+        for (int i = 0; i < w; ++i) t[i] += t[i + w];
+    return t[0];
+}
+
+// S^T tile (64 keys x 32 queries) of one wave: s[sub] covers keys
+// sub*32 .. sub*32+31; the two halves are interleaved so consecutive
+// matrix-core ops are independent.
+template <int D, int SPLIT>
+__device__ __forceinline__ void qk_tile(const uint16_t* ks, const bf16x8 (&qf)[SPLIT][Tile<D>::DK],
+                                        f32x16 (&s)[2], int lane) {
+    using T = Tile<D>;
+    const int col = lane & 31, hh = lane >> 5;
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+#pragma unroll
+    for (int k_ = 0; k_ < T::DK; ++k_)
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+            const int off = (sub * 32 + col) * T::KS + k_ * 16 + 8 * hh;
+            const bf16x8 a = *(const bf16x8*)(ks + off);
+            s[sub] = mfma32(a, qf[0][k_], s[sub]);
+            if constexpr (SPLIT == 2) {
+                s[sub] = mfma32(a, qf[1][k_], s[sub]);
+                s[sub] = mfma32(*(const bf16x8*)(ks + T::KELEMS + off), qf[0][k_], s[sub]);
+            }
+        }
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// 4 keys x 1 dim per lane from row-major V (ds_read_b64_tr_b16): within each
+// 16-lane group, lane i receives the i%4-th 16-bit column of the 8 bytes
+// addressed by lanes 4r + i/4, r = 0..3.
+__device__ __forceinline__ v4i16 read_tr(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
+}
+
+// Per-lane offset (elements) into a V tile for the V^T operand of O^T row
+// block mb: lane group G = lane/16 covers dims mb*32 + 16*(G%2) .. +15 and
+// key half h = G/2; source lane 4r + q of the group points at key 4h + r,
+// dims +4q, so lane i of the group receives keys 4h..4h+3 of dim +i.  Dims
+// past D (padding rows of O^T, discarded) read dim 0 instead.
+template <int D>
+__device__ __forceinline__ int v_lane_offset(int lane, int mb) {
+    const int j = lane & 15, r = j >> 2, q = j & 3, G = lane >> 4, h = G >> 1;
+    int dim = mb * 32 + 16 * (G & 1) + 4 * q;
+    if (dim >= D) dim = 0;
+    return (4 * h + r) * Tile<D>::VS + dim;
+}
+
+// O^T += V^T P^T for one tile.  For contraction step kk (keys 16kk..16kk+15)
+// lane half h feeds keys {4h..4h+3, 8+4h..8+4h+3}: two transposing reads.
+// bf16 inputs: V (converted once) and P are fp16 -- P keeps 11 significant
+// bits, which the few-key rows need to stay within the output tolerance.
+// fp32 inputs: hi/lo bf16 splits of V and P, three products.
+template <int D, int SPLIT>
+__device__ __forceinline__ void pv_tile(const uint16_t* vs, const uint4 (&pb)[4],
+                                        const uint4 (&pl)[4], f32x16 (&o)[Tile<D>::DM],
+                                        const int (&voff)[Tile<D>::DM]) {
+    using T = Tile<D>;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int mb = 0; mb < T::DM; ++mb) {
+            const uint16_t* p0 = vs + voff[mb] + 16 * kk * T::VS;
+            const v4i16 lo = read_tr(p0), hi = read_tr(p0 + 8 * T::VS);
+            const auto a8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            if constexpr (SPLIT == 1) {
+                o[mb] = mfma32_f16(__builtin_bit_cast(f16x8, a8), __builtin_bit_cast(f16x8, pb[kk]),
+                                   o[mb]);
+            } else {
+                const bf16x8 a = __builtin_bit_cast(bf16x8, a8);
+                const v4i16 lo2 = read_tr(p0 + T::VELEMS), hi2 = read_tr(p0 + T::VELEMS + 8 * T::VS);
+                const bf16x8 a2 = __builtin_bit_cast(
+                    bf16x8, __builtin_shufflevector(lo2, hi2, 0, 1, 2, 3, 4, 5, 6, 7));
+                o[mb] = mfma32(a, __builtin_bit_cast(bf16x8, pb[kk]), o[mb]);
+                o[mb] = mfma32(a, __builtin_bit_cast(bf16x8, pl[kk]), o[mb]);
+                o[mb] = mfma32(a2, __builtin_bit_cast(bf16x8, pb[kk]), o[mb]);
+            }
+        }
+}
+
+// Mask of an S^T tile: key j stays for this lane's row i iff
+// (unsigned)(i - j) < wl: wl = 2^31 keeps every causal key (an attended
+// block), wl = w the window.  rk = i - kt0 - 4*(lane/32), so i - j = rk - (a
+// constant of the accumulator register).
+//
+// Online softmax of the tile: produces the bf16 operand P (and its low part
+// for split fp32 operands) and leaves in st the factor by which O must be
+// rescaled once the previous tile's P V is in.
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int rk, uint32_t wl) {
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int cv = sub * 32 + 8 * (v >> 2) + (v & 3);
+            if ((uint32_t)(rk - cv) >= wl) s[sub][v] = -INFINITY;
+        }
+}
+
+// Token-gate mask of an S^T tile: key j stays iff its bit is set in this
+// lane's mask word (bit 16*sub + v for register v of half sub) or, on tiles
+// that meet a window, it passes the same unsigned window test as mask_tile.
+__device__ __forceinline__ void mask_tile_tok(f32x16 (&s)[2], int rk, uint32_t wl, bool window,
+                                              uint32_t word) {
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            bool keep = (word >> (16 * sub + v)) & 1u;
+            if (window) {
+                const int cv = sub * 32 + 8 * (v >> 2) + (v & 3);
+                keep = keep || (uint32_t)(rk - cv) < wl;
+            }
+            if (!keep) s[sub][v] = -INFINITY;
+        }
+}
+
+// Row max of an S^T tile (both lanes of a row get it).
+__device__ __forceinline__ float tile_max(const f32x16 (&s)[2]) {
+    return pair_max(tree_max32(s[0], s[1]));
+}
+
+template <int SPLIT>
+__device__ __forceinline__ void softmax_tile(const f32x16 (&s)[2], RowState& st, float c,
+                                             uint4 (&pb)[4], uint4 (&pl)[4]) {
+    const float mx = tile_max(s);
+    // NaN-free test: true while m is still -inf and mx is finite; false when
+    // both are -inf (a fully masked tile before the row's first key).
+    st.need = mx > st.m + kLazy / c;
+    st.alpha = st.need ? fast_exp2((st.m - mx) * c) : 1.f;
+    st.m = st.need ? mx : st.m;
+    const float nb = st.m == -INFINITY ? 0.f : -st.m * c;
+    float p[2][16];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) p[sub][v] = fast_exp2(fmaf(s[sub][v], c, nb));
+    st.l = fmaf(st.l, st.alpha, tree_sum32(p));
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        const float* pk = &p[kk >> 1][8 * (kk & 1)];
+        if constexpr (SPLIT == 1) {
+            pb[kk] = __builtin_bit_cast(uint4, to_f16x8(pk));
+        } else {
+            const bf16x8 hb = to_bf16x8(pk);
+            float r[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) r[t] = pk[t] - (float)hb[t];
+            pb[kk] = __builtin_bit_cast(uint4, hb);
+            pl[kk] = __builtin_bit_cast(uint4, to_bf16x8(r));
+        }
+    }
+}
+
+// Rescale O by the factor the last softmax left pending (rare: only when a
+// row max grew past the lazy threshold).
+template <int D>
+__device__ __forceinline__ void apply_rescale(f32x16 (&o)[Tile<D>::DM], RowState& st) {
+    if (__any(st.need)) {
+#pragma unroll
+        for (int mb = 0; mb < Tile<D>::DM; ++mb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) o[mb][v] *= st.alpha;
+    }
+    st.need = false;
+}
+
+// One step of the skewed key loop without masking (the far-block kernel):
+// the pending rescale of O, then S_t = K_t Q^T, O += V_{t-1} P_{t-1} and the
+// softmax of S_t into P_t.
+template <int D, int SPLIT>
+__device__ __forceinline__ void kv_step(const uint16_t* ks, const uint16_t* vs_prev,
+                                        const bf16x8 (&qf)[SPLIT][Tile<D>::DK],
+                                        f32x16 (&o)[Tile<D>::DM], RowState& st, uint4 (&pb)[4],
+                                        uint4 (&pl)[4], float c, int lane,
+                                        const int (&voff)[Tile<D>::DM]) {
+    apply_rescale<D>(o, st);
+    f32x16 s[2];
+    qk_tile<D, SPLIT>(ks, qf, s, lane);
+    pv_tile<D, SPLIT>(vs_prev, pb, pl, o, voff);
+    softmax_tile<SPLIT>(s, st, c, pb, pl);
+}
+
+template <int D, int SPLIT>
+__device__ __forceinline__ void load_q(bf16x8 (&qf)[SPLIT][Tile<D>::DK], const uint16_t* const* qp,
+                                       size_t row_off, bool ok, int hh) {
+#pragma unroll
+    for (int p = 0; p < SPLIT; ++p)
+#pragma unroll
+        for (int ks_ = 0; ks_ < Tile<D>::DK; ++ks_) {
+            uint4 u = make_uint4(0, 0, 0, 0);
+            if (ok) u = *(const uint4*)(qp[p] + row_off + ks_ * 16 + 8 * hh);
+            qf[p][ks_] = as_bf16x8(u);
+        }
+}
+
+}  // namespace sa
