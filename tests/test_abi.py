@@ -70,6 +70,7 @@ def code_of(params, **cfg_fields):
     (sa.Params(1, 4, 1, 65536 + 64, 128, window=8, token_top_k=16, index_dim=64), -8),
     (sa.Params(1, 4, 1, 256, 128, window=8, block_size=64, top_k=2, token_top_k=16,
                index_dim=64), -8),
+    (sa.Params(1, 1, 1, 1 << 23, 128, window=8), -8),                # one head's K past 2 GiB
 ])
 def test_invalid_configs(lib, params, code):
     assert code_of(params) == code
