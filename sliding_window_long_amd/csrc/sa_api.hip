@@ -29,11 +29,12 @@ struct Plan {
     long long max_entries;
     int max_chunks;
     bool tok;
-    int top_t, nt32;
+    int top_t, nt32, tok_units, tok_nkp;
     float scale;
     // workspace regions (byte offsets)
     size_t o_split, o_kb3, o_sel, o_count, o_cursor, o_listoff, o_nchunks, o_chunk_list,
         o_chunk_start, o_entries, o_part_o, o_part_lse, o_tok_split, o_tok_state, o_tok_mask,
+        o_tok_qn, o_tok_win, o_tok_kpart, o_tok_scr, o_tok_nslow,
         o_v16, total;
 };
 
@@ -134,6 +135,16 @@ int make_plan(const sparse_attn_cfg* c, Plan* p) {
         P.o_tok_split = take(P.f32 ? 2 * 2 * nidx * 2 : 0);
         P.o_tok_state = take((size_t)P.Bt * P.N * 16);
         P.o_tok_mask = take((size_t)P.Bt * P.nt32 * ((P.N + 63) / 64) * 64 * 4);
+        P.tok_units = sa::tok_units(P.N);
+        P.tok_nkp = (P.N + 255) / 256;
+        P.o_tok_qn = take((size_t)P.Bt * P.N * 4);
+        P.o_tok_win = take((size_t)P.Bt * P.N * 8);
+        P.o_tok_kpart = take((size_t)P.Bt * P.tok_nkp * 4);
+        // Per-unit bin counts, later reused for the threshold-bin candidates.
+        const size_t counts = (size_t)P.Bt * P.tok_units * 64 * 256 * 4;
+        const size_t cands = (size_t)P.Bt * P.N * sa::kTokCap * 8;
+        P.o_tok_scr = take(counts > cands ? counts : cands);
+        P.o_tok_nslow = take(4);
     }
     P.total = off;
     return SA_OK;
@@ -347,6 +358,13 @@ int sparse_attn_fwd(const void* q, const void* k, const void* v, const sparse_at
         ta.Bt = P.Bt; ta.N = P.N; ta.top_t = P.top_t;
         ta.state = (int4*)(ws + P.o_tok_state);
         ta.mask = (uint16_t*)(ws + P.o_tok_mask);
+        ta.qn = (float*)(ws + P.o_tok_qn);
+        ta.win = (float2*)(ws + P.o_tok_win);
+        ta.kpart = (float*)(ws + P.o_tok_kpart);
+        ta.part = (uint32_t*)(ws + P.o_tok_scr);
+        ta.hits = (uint2*)(ws + P.o_tok_scr);
+        ta.nslow = (int*)(ws + P.o_tok_nslow);
+        ta.units = P.tok_units; ta.nkp = P.tok_nkp;
         {
             StageScope t("token_select", s);
             if (!ok(sa::launch_token_select(ta, split, s))) return SA_E_HIP;

@@ -86,14 +86,45 @@ struct CompactArgs {
     int rows_per_chunk;
 };
 
-// Token gate: per-row radix-select state and the keep mask it produces.
+// Token gate: per-row selection state and the keep mask it produces.
 struct TokArgs {
     const uint16_t* iq[2];  // bf16 planes of the indexer queries [Bt, N, 64]
     const uint16_t* ik[2];  // bf16 planes of the indexer keys [Bt, N, 64]
     int Bt, N, top_t;
     int4* state;            // [Bt*N]
     uint16_t* mask;         // keep-mask half-words [Bt][N/32][N/64][64 lanes][2]
+    float* qn;              // [Bt*N] indexer query norms
+    float2* win;            // [Bt*N] bin map (scale, offset) of the exact pass
+    float* kpart;           // [Bt][nkp] largest indexer key norm per 256 keys
+    uint32_t* part;         // [Bt][units][64][256] per-unit bin counts (two rows per word);
+                            // the sampled pass uses [Bt][NB][64][256] of it first
+    uint2* hits;            // [Bt*N][kTokCap] threshold-bin candidates (aliases part)
+    int* nslow;             // rows left to the radix fallback
+    int units, nkp;
 };
+
+// Work units of the binned token passes: 128 query rows (4 waves x 32) by
+// a chunk of at most 256 key tiles of 32 keys.  Row block b reads key tiles
+// [0, tok_tiles(N, b)), up to the diagonal tile of its last row (every mask
+// half a row tile owns is written); key chunk c is present for the blocks
+// [64c, NB).
+constexpr int kTokRows = 128;
+constexpr int kTokChunk = 256;
+constexpr int kTokCap = 512;   // threshold-bin candidates a row may collect
+
+__host__ __device__ inline int tok_blocks(int N) { return (N + kTokRows - 1) / kTokRows; }
+__host__ __device__ inline int tok_tiles(int N, int b) {
+    const int last = (N < (b + 1) * kTokRows ? N : (b + 1) * kTokRows) - 1;   // last row
+    return last / 32 + 1;
+}
+__host__ __device__ inline int tok_chunks(int N, int b) {
+    return (tok_tiles(N, b) + kTokChunk - 1) / kTokChunk;
+}
+// Units before chunk c (chunk-major, blocks descending inside a chunk).
+__host__ __device__ inline int tok_unit_base(int N, int c) {
+    return c * tok_blocks(N) - 64 * c * (c - 1) / 2;
+}
+inline int tok_units(int N) { return tok_unit_base(N, tok_chunks(N, tok_blocks(N) - 1)); }
 
 hipError_t launch_token_select(const TokArgs& a, int split, hipStream_t s);
 hipError_t launch_token_list(const TokArgs& a, int32_t* out, hipStream_t s);

@@ -155,8 +155,8 @@ def test_deterministic(dev):
 
 # --- token top-k (Naive SWA + DSA shape) -------------------------------------
 @pytest.mark.parametrize("N,top_t,window,sink", [
-    (64, 8, 1, False), (300, 16, 8, True), (1024, 100, 128, True), (1000, 1, 4, False),
-    (256, 300, 2, True)])
+    (1, 4, 1, False), (33, 5, 2, True), (64, 8, 1, False), (300, 16, 8, True),
+    (1024, 100, 128, True), (1000, 1, 4, False), (256, 300, 2, True), (8400, 700, 16, False)])
 @pytest.mark.parametrize("d", [64, 128])
 def test_token_small_all_rows(dev, N, top_t, window, sink, d):
     wl = W.Workload("tok_small", 1, 4, 1, N, d, "bf16", window=window, token_top_k=top_t,
@@ -164,17 +164,20 @@ def test_token_small_all_rows(dev, N, top_t, window, sink, d):
     run_and_check(W.make_inputs(wl, 21 + N + d), dev, label=f"tok_small N={N} k={top_t}")
 
 
-def test_token_ties_go_to_lower_index(dev):
-    # Equal indexer keys: every candidate ties, the lowest token ids must win
-    # (exercises the index-byte passes of the radix select).
-    wl = W.Workload("tok_ties", 1, 2, 1, 512, 64, "bf16", window=2, token_top_k=37, index_dim=64)
+@pytest.mark.parametrize("N", [512, 1500])
+def test_token_ties_go_to_lower_index(dev, N):
+    # Equal indexer keys: every candidate of a row ties, the lowest token ids
+    # must win.  Rows with up to 512 candidates are settled by the binned
+    # path's candidate select (index bytes), longer rows by the radix
+    # fallback; row tile 16 mixes both.
+    wl = W.Workload("tok_ties", 1, 2, 1, N, 64, "bf16", window=2, token_top_k=37, index_dim=64)
     inp = W.make_inputs(wl, 5)
     inp.idx_k[:] = inp.idx_k[:, :1]
     out, lse, _, tsel = run_device(inp, dev)
     for i in range(wl.seq_len):
         m = min(37, i)
         assert tsel[0, i].tolist() == list(range(m)) + [-1] * (37 - m), i
-    rep = check(inp, out, lse, np.arange(2 * 512), None, tsel)
+    rep = check(inp, out, lse, np.arange(2 * N), None, tsel)
     log(f"[gpu] tok_ties {rep}")
     assert rep.ok(), str(rep)
 
