@@ -32,9 +32,16 @@ FLAGS = [
 ]
 
 
+# Per-source additions.  The token passes read every matrix-core result with
+# vector ops: the VGPR form of the MFMA ops saves a copy out of the
+# accumulation registers per element.
+EXTRA = {"sa_token.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str, build_dir: str = BUILD_DIR, defines=()) -> str:
     obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), *[f"-D{d}" for d in defines], "-c",
+           os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")

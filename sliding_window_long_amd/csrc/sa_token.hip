@@ -46,8 +46,6 @@
 // of the sub-th 32-key half of the S^T tile.  The two halves are written as
 // separate 16-bit halves of the word; halves past the row tile are not
 // written.
-#include <type_traits>
-
 #include "sa_device.hpp"
 #include "sa_internal.hpp"
 
@@ -75,6 +73,9 @@ __device__ __forceinline__ uint32_t ord32(float s) {
 __device__ __forceinline__ size_t mask_half(int bt, int nt32, int nt64, int rt, int kc, int lane) {
     return ((((size_t)bt * nt32 + rt) * nt64 + (kc >> 1)) * 64 + lane) * 2 + (kc & 1);
 }
+
+// Wave index within the block, as a scalar (wave-uniform) value.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 __device__ __forceinline__ void wave_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -305,7 +306,7 @@ __global__ __launch_bounds__(TOK_THREADS) void tok_hist_kernel(TokArgs a) {
     __shared__ uint32_t hist[BINS * 64];
     __shared__ __attribute__((aligned(16))) TokLds<SPLIT> lds;
     __shared__ float red[TOK_WAVES];
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
     const int col = lane & 31, hh = lane >> 5;
     const int bt = blockIdx.y, u = blockIdx.x;
     int b, t0, t1, step;
@@ -413,7 +414,7 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
 // k' - 6 sd - 16 (or +B).  win = map of [L, U) onto [1, kTokBins - 1).
 __global__ __launch_bounds__(TOK_THREADS) void tok_window_kernel(TokArgs a) {
     __shared__ float red[TOK_WAVES];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = wave_id(), lane = threadIdx.x & 63;
     const int bt = blockIdx.y, wr = blockIdx.x * TOK_WAVES + wave;
     const float kmax = tok_kmax(a, bt, red, threadIdx.x);
     const int nb = tok_blocks(a.N), b = wr >> 6, w = wr & 63;
@@ -460,7 +461,7 @@ __global__ __launch_bounds__(TOK_THREADS) void tok_window_kernel(TokArgs a) {
 // 128b + 64 + w): sum the unit counts, find b*.  state = {b*, 0 (collect
 // counter), rank left inside b*, flags}.
 __global__ __launch_bounds__(TOK_THREADS) void tok_bin_kernel(TokArgs a) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = wave_id(), lane = threadIdx.x & 63;
     const int bt = blockIdx.y, wr = blockIdx.x * TOK_WAVES + wave;
     const int nb = tok_blocks(a.N), b = wr >> 6, w = wr & 63;
     if (b >= nb) return;
@@ -502,14 +503,14 @@ __global__ __launch_bounds__(TOK_THREADS) void tok_bin_kernel(TokArgs a) {
 // Mask pass: the keep mask of every binned row: keys in bins above b* kept,
 // candidates of b* collected (48-bit key) for the resolve step.  Rows left
 // to the radix fallback are not written.
-constexpr int kTokStage = 4096;   // candidates one mask unit can hold in LDS
+constexpr int kTokStage = 2048;   // candidates one mask unit can hold in LDS
 template <int SPLIT>
 __global__ __launch_bounds__(TOK_THREADS) void tok_mask_kernel(TokArgs a) {
     __shared__ __attribute__((aligned(16))) TokLds<SPLIT> lds;
     // Candidates of this unit: 48-bit key, local row in bits 48..54.
     __shared__ uint2 stage[kTokStage];
     __shared__ int s_cnt;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
     const int col = lane & 31, hh = lane >> 5;
     const int bt = blockIdx.y, u = blockIdx.x;
     int b, c;
@@ -537,47 +538,38 @@ __global__ __launch_bounds__(TOK_THREADS) void tok_mask_kernel(TokArgs a) {
     const uint32_t lr = (uint32_t)(32 * wave + col);
     if (tid == 0) s_cnt = 0;   // ordered before any add by the stream's first barrier
 
+    // Register v of a tile holds key 32 t + cv(v) + 4 hh; on the diagonal
+    // tile only keys before the row count.
+    uint32_t diag_bits = 0;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) diag_bits |= (8 * (v >> 2) + (v & 3) + 4 * hh < col ? 1u : 0u) << v;
+
     // Keep bits of one tile; candidates of bin b* go to the LDS stage (the
     // wave-level test keeps that rare path out of the common one).
-    auto tile = [&](int t, const f32x16& acc, auto diag_tag) {
-        constexpr bool DIAG = decltype(diag_tag)::value;
+    tok_stream<SPLIT>(a, bt, t0, t1 - t0, 1, lds, tid, [&](int t, const uint16_t* kl) {
+        if (t > rt) return;
+        const f32x16 acc = index_scores_lds<SPLIT>(kl, qf, lane);
+        const uint32_t cm = t < rt ? 0xffffu : diag_bits;
         uint32_t bits = 0;
-        bool any_in = false;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            const int cv = 8 * (v >> 2) + (v & 3) + 4 * hh;
             const float x = fmaf(acc[v], map.x, map.y);
-            bool keep = x >= keep_x, in = x >= in_x;
-            if (DIAG) {
-                keep = keep && cv < col;
-                in = in && cv < col;
-            }
+            const bool keep = x >= keep_x;
             bits |= (keep ? 1u : 0u) << v;
-            any_in = any_in || (in && !keep);
-        }
-        if (write) a.mask[mask_half(bt, nt32, nt64, rt, t, lane)] = (uint16_t)bits;
-        if (__any(any_in)) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int cv = 8 * (v >> 2) + (v & 3) + 4 * hh;
-                const float x = fmaf(acc[v], map.x, map.y);
-                if ((!DIAG || cv < col) && x >= in_x && !(x >= keep_x)) {
-                    const int pos = atomicAdd(&s_cnt, 1);
-                    const uint32_t o = ord32(acc[v]);
-                    if (pos < kTokStage) {
-                        stage[pos] = make_uint2((o << 16) | (0xffffu - (uint32_t)(t * 32 + cv)),
-                                                (o >> 16) | (lr << 16));
-                    } else {   // no room: the radix fallback takes the row
-                        atomicOr(&a.state[gr].w, (int)kTokSlow);
-                        atomicAdd(a.nslow, 1);
-                    }
+            if (x >= in_x && !keep) {   // rare: a candidate of b*
+                if (!((cm >> v) & 1u)) continue;
+                const int pos = atomicAdd(&s_cnt, 1);
+                const uint32_t o = ord32(acc[v]);
+                const uint32_t j = (uint32_t)(t * 32 + 8 * (v >> 2) + (v & 3) + 4 * hh);
+                if (pos < kTokStage) {
+                    stage[pos] = make_uint2((o << 16) | (0xffffu - j), (o >> 16) | (lr << 16));
+                } else {   // no room: the radix fallback takes the row
+                    atomicOr(&a.state[gr].w, (int)kTokSlow);
+                    atomicAdd(a.nslow, 1);
                 }
             }
         }
-    };
-    tok_stream<SPLIT>(a, bt, t0, t1 - t0, 1, lds, tid, [&](int t, const uint16_t* kl) {
-        if (t < rt) tile(t, index_scores_lds<SPLIT>(kl, qf, lane), std::false_type{});
-        else if (t == rt) tile(t, index_scores_lds<SPLIT>(kl, qf, lane), std::true_type{});
+        if (write) a.mask[mask_half(bt, nt32, nt64, rt, t, lane)] = (uint16_t)(bits & cm);
     });
     // Publish the staged candidates to their rows' lists (the stream ends
     // with a barrier).
@@ -595,7 +587,7 @@ __global__ __launch_bounds__(TOK_THREADS) void tok_mask_kernel(TokArgs a) {
 // their mask bits.
 __global__ __launch_bounds__(TOK_THREADS) void tok_resolve_kernel(TokArgs a) {
     __shared__ uint32_t hs[TOK_WAVES][256];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = wave_id(), lane = threadIdx.x & 63;
     const long long gi = (long long)blockIdx.x * TOK_WAVES + wave;
     if (gi >= (long long)a.Bt * a.N) return;
     const int4 st = a.state[gi];
@@ -665,7 +657,7 @@ __global__ __launch_bounds__(TOK_THREADS) void token_select_kernel(TokArgs a, in
     if (*a.nslow == 0) return;
     __shared__ uint32_t hist[32 * HSTRIDE];
     __shared__ int s_skip;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
     const int col = lane & 31, hh = lane >> 5;
     const int nt = (a.N + 31) / 32;
     // Row tiles with the most candidates first (they run longest).
