@@ -78,52 +78,130 @@ __device__ __forceinline__ void finish_rows(const RowsArgs& a, f32x16 (&o)[Tile<
 // ---------------------------------------------------------------------------
 // Query-centric kernel.
 // ---------------------------------------------------------------------------
-template <int D, int SPLIT, bool TOK>
-__global__ __launch_bounds__(NTHREADS, 2) void attn_rows_kernel(RowsArgs a) {
+
+// S^T tiles of NG 32-row groups of one wave: every K fragment read from LDS
+// feeds the matrix-core ops of all groups.
+template <int D, int SPLIT, int NG>
+__device__ __forceinline__ void qk_tiles(const uint16_t* ks, const bf16x8 (&qf)[NG][SPLIT][Tile<D>::DK],
+                                         f32x16 (&s)[NG][2], int lane) {
     using T = Tile<D>;
+    const int col = lane & 31, hh = lane >> 5;
+#pragma unroll
+    for (int g = 0; g < NG; ++g) s[g][0] = s[g][1] = f32x16{};
+#pragma unroll
+    for (int k_ = 0; k_ < T::DK; ++k_)
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+            const int off = (sub * 32 + col) * T::KS + k_ * 16 + 8 * hh;
+            const bf16x8 a = *(const bf16x8*)(ks + off);
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                s[g][sub] = mfma32(a, qf[g][0][k_], s[g][sub]);
+                if constexpr (SPLIT == 2) {
+                    s[g][sub] = mfma32(a, qf[g][1][k_], s[g][sub]);
+                    s[g][sub] = mfma32(*(const bf16x8*)(ks + T::KELEMS + off), qf[g][0][k_], s[g][sub]);
+                }
+            }
+        }
+}
+
+// O^T += V^T P^T for NG row groups; every V^T fragment feeds all groups.
+template <int D, int SPLIT, int NG>
+__device__ __forceinline__ void pv_tiles(const uint16_t* vs, const uint4 (&pb)[NG][4],
+                                         const uint4 (&pl)[NG][4], f32x16 (&o)[NG][Tile<D>::DM],
+                                         const int (&voff)[Tile<D>::DM]) {
+    using T = Tile<D>;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int mb = 0; mb < T::DM; ++mb) {
+            const uint16_t* p0 = vs + voff[mb] + 16 * kk * T::VS;
+            const v4i16 lo = read_tr(p0), hi = read_tr(p0 + 8 * T::VS);
+            const auto a8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            if constexpr (SPLIT == 1) {
+#pragma unroll
+                for (int g = 0; g < NG; ++g)
+                    o[g][mb] = mfma32_f16(__builtin_bit_cast(f16x8, a8),
+                                          __builtin_bit_cast(f16x8, pb[g][kk]), o[g][mb]);
+            } else {
+                const bf16x8 av = __builtin_bit_cast(bf16x8, a8);
+                const v4i16 lo2 = read_tr(p0 + T::VELEMS), hi2 = read_tr(p0 + T::VELEMS + 8 * T::VS);
+                const bf16x8 a2 = __builtin_bit_cast(
+                    bf16x8, __builtin_shufflevector(lo2, hi2, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+                for (int g = 0; g < NG; ++g) {
+                    o[g][mb] = mfma32(av, __builtin_bit_cast(bf16x8, pb[g][kk]), o[g][mb]);
+                    o[g][mb] = mfma32(av, __builtin_bit_cast(bf16x8, pl[g][kk]), o[g][mb]);
+                    o[g][mb] = mfma32(a2, __builtin_bit_cast(bf16x8, pb[g][kk]), o[g][mb]);
+                }
+            }
+        }
+}
+
+// A workgroup owns NG * 128 consecutive query rows of one head: wave w holds
+// the 32-row groups w*NG .. w*NG + NG - 1, one row per lane pair in each.
+template <int D, int SPLIT, bool TOK, int NG>
+__global__ __launch_bounds__(NTHREADS, NG == 1 ? 2 : 1) void attn_rows_kernel(RowsArgs a) {
+    using T = Tile<D>;
+    constexpr int RTW = RT * NG;   // query rows per workgroup
     __shared__ __align__(16) uint16_t lds_k[2][SPLIT * T::KELEMS];
     __shared__ __align__(16) uint16_t lds_v[2][SPLIT * T::VELEMS];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int col = lane & 31, hh = lane >> 5;
     const int BH = a.Bt * a.Hq;
-    const int ntiles = (a.N + RT - 1) / RT;
+    const int ntiles = (a.N + RTW - 1) / RTW;
     const int bh = blockIdx.x % BH;
     const int tile = ntiles - 1 - (int)(blockIdx.x / BH);   // longest rows first
-    const int b = bh / a.Hq, h = bh % a.Hq, G = a.Hq / a.Hkv, g = h / G;
+    const int b = bh / a.Hq, h = bh % a.Hq, G = a.Hq / a.Hkv, g_kv = h / G;
     const int N = a.N;
-    const int r0 = tile * RT;
+    const int r0 = tile * RTW;
 
-    const size_t kvoff = (size_t)(b * a.Hkv + g) * N * D;
+    const size_t kvoff = (size_t)(b * a.Hkv + g_kv) * N * D;
     const uint16_t* kp[2] = {a.k[0] + kvoff, SPLIT == 2 ? a.k[1] + kvoff : nullptr};
     const uint16_t* vp[2] = {a.v[0] + kvoff, SPLIT == 2 ? a.v[1] + kvoff : nullptr};
 
-    const int row = r0 + wave * 32 + col;
-    const bool row_ok = row < N;
-    const size_t prow = (size_t)bh * N + row;   // flat row id
-    bf16x8 qf[SPLIT][T::DK];
-    load_q<D, SPLIT>(qf, a.q, prow * D, row_ok, hh);
+    const int wu = __builtin_amdgcn_readfirstlane(wave);   // wave-uniform
+    int row[NG], q0[NG], q1[NG];
+    bool row_ok[NG];
+    size_t prow[NG];   // flat row ids
+    bf16x8 qf[NG][SPLIT][T::DK];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        q0[g] = r0 + (wu * NG + g) * 32;
+        q1[g] = min(q0[g] + 31, N - 1);
+        row[g] = q0[g] + col;
+        row_ok[g] = row[g] < N;
+        prow[g] = (size_t)bh * N + row[g];
+        load_q<D, SPLIT>(qf[g], a.q, prow[g] * D, row_ok[g], hh);
+    }
 
-    // Block-gate state of this row: its block, the kept near blocks as a
+    // Block-gate state of each row: its block, the kept near blocks as a
     // bit mask over (own block - 1 - bit), and the count of far blocks.
-    int row_blk = 0, nfar = 0;
-    uint32_t near_bits = 0;
-    if (a.gate) {
-        row_blk = (row_ok ? row : N - 1) / a.B;
-        if (row_ok) {
-            const int32_t* sr = a.sel + prow * a.top_k;
-            for (int x = 0; x < a.top_k; ++x) {
-                const int cblk = sr[x];
-                if (cblk < 0) break;
-                const int dlt = row_blk - cblk;
-                if (dlt > a.span) ++nfar;
-                else if (dlt >= 1 && dlt <= 32) near_bits |= 1u << (dlt - 1);
+    int row_blk[NG], nfar[NG];
+    uint32_t near_bits[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        row_blk[g] = 0;
+        nfar[g] = 0;
+        near_bits[g] = 0;
+        if (a.gate) {
+            row_blk[g] = (row_ok[g] ? row[g] : N - 1) / a.B;
+            if (row_ok[g]) {
+                const int32_t* sr = a.sel + prow[g] * a.top_k;
+                for (int x = 0; x < a.top_k; ++x) {
+                    const int cblk = sr[x];
+                    if (cblk < 0) break;
+                    const int dlt = row_blk[g] - cblk;
+                    if (dlt > a.span) ++nfar[g];
+                    else if (dlt >= 1 && dlt <= 32) near_bits[g] |= 1u << (dlt - 1);
+                }
             }
         }
     }
 
-    // Key range of the workgroup and of this wave.
-    const int r_hi = min(r0 + RT - 1, N - 1);
+    // Key range of the workgroup.
+    const int r_hi = min(r0 + RTW - 1, N - 1);
     auto lower_key = [&](int r) {
         if (TOK) return 0;   // selected tokens can be anywhere before r
         int lo = r;
@@ -132,20 +210,22 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_rows_kernel(RowsArgs a) {
         return max(lo, 0);
     };
     const int t_begin = lower_key(r0) / KT, t_end = r_hi / KT;
-    const int q0 = r0 + __builtin_amdgcn_readfirstlane(wave) * 32;   // wave-uniform
-    const int q1 = min(q0 + 31, N - 1);
     const float c = a.scale * kLog2e;
     const uint32_t wl_window = a.window > 0 ? (uint32_t)a.window : 0u;
 
     zero_v_init<D, SPLIT>(&lds_v[0][0], tid);
 
-    f32x16 o[T::DM];
+    f32x16 o[NG][T::DM];
+    RowState rs[NG];
+    uint4 pb[NG][4], pl[NG][4];
 #pragma unroll
-    for (int mb = 0; mb < T::DM; ++mb) o[mb] = f32x16{};
-    RowState rs{-INFINITY, 0.f, 1.f, false};
-    uint4 pb[4], pl[4];
+    for (int g = 0; g < NG; ++g) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) pb[kk] = pl[kk] = make_uint4(0, 0, 0, 0);
+        for (int mb = 0; mb < T::DM; ++mb) o[g][mb] = f32x16{};
+        rs[g] = RowState{-INFINITY, 0.f, 1.f, false};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) pb[g][kk] = pl[g][kk] = make_uint4(0, 0, 0, 0);
+    }
 
     int voff[T::DM];
 #pragma unroll
@@ -156,34 +236,36 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_rows_kernel(RowsArgs a) {
     store_tile<D, SPLIT, T::KS, T::KELEMS>(kst, lds_k[0], tid);
     __syncthreads();
 
-    // Mask of key tile t for this wave's rows: keys a row does not attend
-    // become -inf (a tile outside a wave's rows is fully masked).  Tiles
-    // that are entirely inside every row's window, or inside every row's own
+    // Mask of key tile t for the rows of group g: keys a row does not attend
+    // become -inf (a tile past a group's rows is fully masked).  Tiles that
+    // are entirely inside every row's window, or inside every row's own
     // block, need no mask (wave-uniform test).
-    auto mask_t = [&](f32x16 (&sv)[2], int t) {
+    auto mask_t = [&](f32x16 (&sv)[2], int t, int g) {
         const int kt0 = t * KT;
-        const int rk = row - kt0 - 4 * hh;
+        const int rk = row[g] - kt0 - 4 * hh;
         if constexpr (TOK) {
-            // This lane's keep bits for the tile; key tiles past the wave's
-            // rows hold no kept key.  Only 32-key halves kc <= rt are
-            // written; a half past the row tile (kc = rt + 1 when rt is
-            // even) is all future keys: cleared.
-            const int nt32 = (N + 31) / 32, nt64 = (N + KT - 1) / KT, rt = q0 / 32;
-            uint32_t tword =
-                t <= rt / 2 ? a.tokmask[(((size_t)b * nt32 + rt) * nt64 + t) * 64 + lane] : 0u;
+            // This lane's keep bits for the tile; key tiles past the group's
+            // rows hold no kept key, and a group past the last row has no
+            // mask.  Only 32-key halves kc <= rt are written; a half past the
+            // row tile (kc = rt + 1 when rt is even) is all future keys:
+            // cleared.
+            const int nt32 = (N + 31) / 32, nt64 = (N + KT - 1) / KT, rt = q0[g] / 32;
+            uint32_t tword = t <= rt / 2 && q0[g] < N
+                                 ? a.tokmask[(((size_t)b * nt32 + rt) * nt64 + t) * 64 + lane]
+                                 : 0u;
             if (2 * t + 1 > rt) tword &= 0xffffu;
-            const bool near = kt0 + KT - 1 >= q0 - a.window + 1;   // tile meets a window
+            const bool near = kt0 + KT - 1 >= q0[g] - a.window + 1;   // tile meets a window
             mask_tile_tok(sv, rk, wl_window, near, tword);
         } else {
-            const bool full = kt0 + KT - 1 <= q0 &&
-                              ((a.window > 0 && q1 - kt0 < a.window) ||
-                               (a.gate && kt0 / a.B == q0 / a.B && q1 / a.B == q0 / a.B));
+            const bool full = kt0 + KT - 1 <= q0[g] &&
+                              ((a.window > 0 && q1[g] - kt0 < a.window) ||
+                               (a.gate && kt0 / a.B == q0[g] / a.B && q1[g] / a.B == q0[g] / a.B));
             if (!full) {
                 uint32_t wl = wl_window;
                 if (a.gate) {
-                    const int dlt = row_blk - kt0 / a.B;
+                    const int dlt = row_blk[g] - kt0 / a.B;
                     const bool blk_ok = dlt == 0 || (dlt >= 1 && dlt <= a.span && dlt <= 32 &&
-                                                     ((near_bits >> (dlt - 1)) & 1u));
+                                                     ((near_bits[g] >> (dlt - 1)) & 1u));
                     if (blk_ok) wl = 0x80000000u;
                 }
                 mask_tile(sv, rk, wl);
@@ -191,28 +273,32 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_rows_kernel(RowsArgs a) {
         }
     };
 
-    // One-stage skew: the step of tile t computes S_t, O += V_{t-1}
-    // P_{t-1} and P_t; V is staged one tile behind K.
+    // One-stage skew: the step of tile t computes S_t, O += V_{t-1} P_{t-1}
+    // and P_t; V is staged one tile behind K.
     for (int t = t_begin; t <= t_end; ++t) {
         const int it = t - t_begin;
         load_tile<D, SPLIT>(kst, ksrc, min(t + 1, t_end) * KT);
         load_tile<D, SPLIT>(vst, vsrc, t * KT);
-        apply_rescale<D>(o, rs);
-        f32x16 sv[2];
-        qk_tile<D, SPLIT>(lds_k[it & 1], qf, sv, lane);
-        mask_t(sv, t);
-        pv_tile<D, SPLIT>(lds_v[(it + 1) & 1], pb, pl, o, voff);
-        softmax_tile<SPLIT>(sv, rs, c, pb, pl);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) apply_rescale<D>(o[g], rs[g]);
+        f32x16 sv[NG][2];
+        qk_tiles<D, SPLIT, NG>(lds_k[it & 1], qf, sv, lane);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) mask_t(sv[g], t, g);
+        pv_tiles<D, SPLIT, NG>(lds_v[(it + 1) & 1], pb, pl, o, voff);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) softmax_tile<SPLIT>(sv[g], rs[g], c, pb[g], pl[g]);
         store_tile<D, SPLIT, T::KS, T::KELEMS>(kst, lds_k[(it + 1) & 1], tid);
         store_tile<D, SPLIT, T::VS, T::VELEMS>(vst, lds_v[it & 1], tid);
         __syncthreads();
     }
-    apply_rescale<D>(o, rs);
-    pv_tile<D, SPLIT>(lds_v[(t_end - t_begin) & 1], pb, pl, o, voff);
+#pragma unroll
+    for (int g = 0; g < NG; ++g) apply_rescale<D>(o[g], rs[g]);
+    pv_tiles<D, SPLIT, NG>(lds_v[(t_end - t_begin) & 1], pb, pl, o, voff);
 
-    if (!row_ok) return;
-
-    finish_rows<D>(a, o, pair_sum(rs.l), rs.m, prow, h, nfar, hh);
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+        if (row_ok[g]) finish_rows<D>(a, o[g], pair_sum(rs[g].l), rs[g].m, prow[g], h, nfar[g], hh);
 }
 
 
@@ -254,12 +340,16 @@ __global__ void split_f32_kernel(const float* __restrict__ x, uint16_t* __restri
 
 template <int D, int SPLIT>
 static hipError_t rows_d(const RowsArgs& a, hipStream_t s) {
-    const int ntiles = (a.N + RT - 1) / RT;
+    // One 32-row group per wave.  Two (every K/V fragment read from LDS
+    // feeding 64 rows) leave room for one wave per SIMD and measured slower
+    // on every shape (d = 80 window: 1.20 vs 0.94 ms).
+    constexpr int NG = 1;
+    const int ntiles = (a.N + RT * NG - 1) / (RT * NG);
     const unsigned grid = (unsigned)(ntiles * a.Bt * a.Hq);
     if (a.tokmask)
-        hipLaunchKernelGGL((attn_rows_kernel<D, SPLIT, true>), dim3(grid), dim3(NTHREADS), 0, s, a);
+        hipLaunchKernelGGL((attn_rows_kernel<D, SPLIT, true, NG>), dim3(grid), dim3(NTHREADS), 0, s, a);
     else
-        hipLaunchKernelGGL((attn_rows_kernel<D, SPLIT, false>), dim3(grid), dim3(NTHREADS), 0, s, a);
+        hipLaunchKernelGGL((attn_rows_kernel<D, SPLIT, false, NG>), dim3(grid), dim3(NTHREADS), 0, s, a);
     return hipGetLastError();
 }
 
