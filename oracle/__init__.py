@@ -10,7 +10,9 @@ loads it with ctypes and wraps it for numpy arrays.  ``brute.py`` is a
 second, exact pure-Python version for tiny inputs used to pin this one.
 
 Every function takes the exact input values as float32 numpy arrays in the
-layouts q [Bt,Hq,N,d], k/v [Bt,Hkv,N,d], idx_q/idx_k [Bt,N,dI].
+layouts q [Bt,Hq,N,d], k/v [Bt,Hkv,N,d], idx_q/idx_k [Bt,N,dI].  For a
+decode/append step q and idx_q hold only the Nq newest positions of a
+history of Nk keys (query row rq at position rq + Nk - Nq).
 """
 from __future__ import annotations
 
@@ -67,6 +69,14 @@ def _load(path=None):
                                ctypes.c_void_p, _i64, ctypes.c_void_p, _i64,
                                ctypes.c_void_p, _i64p, _i64, _f64p, _f64p, _i64p]
     lib.orc_attend.restype = ctypes.c_int
+    lib.orc_token_select_at.argtypes = [_f32p, _f32p, _i64, _i64, _i64, _i64, _i64, _i64p, _i64,
+                                        _i32p, _f64p, _f64p]
+    lib.orc_token_select_at.restype = None
+    lib.orc_attend_at.argtypes = [_f32p, _f32p, _f32p, _i64, _i64, _i64, _i64, _i64, _i64,
+                                  ctypes.c_double, _i64, _i64,
+                                  ctypes.c_void_p, _i64, ctypes.c_void_p, _i64,
+                                  ctypes.c_void_p, _i64p, _i64, _f64p, _f64p, _i64p]
+    lib.orc_attend_at.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -148,15 +158,28 @@ def token_scores(idx_q, idx_k, rows):
     return out
 
 
+def _offset(nq, nk):
+    """Position of query row 0: the queries continue a history of nk keys
+    (nk - nq; 0 for a prefill)."""
+    if nk < nq:
+        raise ValueError("fewer keys than queries")
+    return nk - nq
+
+
 def token_select(idx_q, idx_k, top_t, rows=None):
-    """Selected tokens per token row r = b*N + i: [len(rows), top_t]."""
+    """Selected tokens per token row r = b*Nq + rq: [len(rows), top_t].
+    idx_q [Bt, Nq, dI], idx_k [Bt, Nk, dI]; row rq sits at position
+    rq + Nk - Nq (a prefill when Nq = Nk)."""
     iq, ik = _f32(idx_q), _f32(idx_k)
-    Bt, N, dI = iq.shape
-    rows = _rows(rows, Bt * N)
+    Bt, Nq, dI = iq.shape
+    Nk = ik.shape[1]
+    off = _offset(Nq, Nk)
+    rows = _rows(rows, Bt * Nq)
     tsel = np.empty((len(rows), top_t), dtype=np.int32)
     s_last = np.empty(len(rows), dtype=np.float64)
     s_next = np.empty(len(rows), dtype=np.float64)
-    _load().orc_token_select(iq, ik, N, dI, top_t, rows, len(rows), tsel, s_last, s_next)
+    _load().orc_token_select_at(iq, ik, Nq, Nk, dI, top_t, off, rows, len(rows), tsel, s_last,
+                                s_next)
     return tsel, s_last, s_next
 
 
@@ -166,11 +189,12 @@ def attend(q, k, v, *, scale=None, window=0, block_size=0, sel=None, tsel=None,
     sel [len(rows), w] block ids and tsel [len(rows), w'] token ids are per
     listed row.  Returns out [len(rows), d] fp64, lse fp64, |A(i)| int64."""
     q, k, v = _f32(q), _f32(k), _f32(v)
-    Bt, Hq, N, d = q.shape
-    Hkv = k.shape[1]
+    Bt, Hq, Nq, d = q.shape
+    Hkv, N = k.shape[1], k.shape[2]
+    off = _offset(Nq, N)
     if Hq % Hkv:
         raise ValueError("Hq must be a multiple of Hkv")
-    rows = _rows(rows, Bt * Hq * N)
+    rows = _rows(rows, Bt * Hq * Nq)
     scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
     out = np.empty((len(rows), d), dtype=np.float64)
     lse = np.empty(len(rows), dtype=np.float64)
@@ -181,8 +205,8 @@ def attend(q, k, v, *, scale=None, window=0, block_size=0, sel=None, tsel=None,
     for a in (sel_a, tsel_a):
         if a is not None and a.shape[0] != len(rows):
             raise ValueError("selections are per listed row")
-    rc = _load().orc_attend(
-        q, k, v, Hq, Hkv, N, d, scale, int(window), int(block_size),
+    rc = _load().orc_attend_at(
+        q, k, v, Hq, Hkv, Nq, N, d, off, scale, int(window), int(block_size),
         None if sel_a is None else sel_a.ctypes.data, 0 if sel_a is None else sel_a.shape[1],
         None if tsel_a is None else tsel_a.ctypes.data, 0 if tsel_a is None else tsel_a.shape[1],
         None if sink_a is None else sink_a.ctypes.data,
@@ -196,10 +220,17 @@ def forward(q, k, v, *, block_size=0, top_k=0, window=0, idx_q=None, idx_k=None,
             token_top_k=0, sink=None, scale=None, rows=None):
     """The whole path for the listed rows: pool, gate, token select, attend.
     Returns a dict with out, lse, count, sel, s_last, s_next, tsel, t_last,
-    t_next (selection entries are None when that gate is off)."""
+    t_next (selection entries are None when that gate is off).
+
+    q [Bt, Hq, Nq, d] may be shorter than k, v [Bt, Hkv, Nk, d] (and idx_q
+    than idx_k): the queries then continue the cached history, row rq at
+    position rq + Nk - Nq.  Block gating is a prefill method here (the MoBA
+    summary switches to full attention for generation) and needs Nq = Nk."""
     Bt, Hq, N, d = np.shape(q)
     rows = _rows(rows, Bt * Hq * N)
     res = dict(sel=None, s_last=None, s_next=None, tsel=None, t_last=None, t_next=None)
+    if top_k > 0 and np.shape(k)[2] != N:
+        raise ValueError("block gating needs as many queries as keys")
     if top_k > 0:
         kbar = block_pool(k, block_size)
         res["sel"], res["s_last"], res["s_next"] = block_select(q, kbar, block_size, top_k, rows)

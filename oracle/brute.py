@@ -38,25 +38,32 @@ def best_subset(scores: dict[int, Fraction], m: int) -> tuple[int, ...]:
 
 def forward(q, k, v, *, block_size=0, top_k=0, window=0, idx_q=None, idx_k=None,
             token_top_k=0, sink=None, scale=None):
-    """Returns (out [Bt,Hq,N,d], lse [Bt,Hq,N], sel dict, tsel dict, count)."""
+    """Returns (out [Bt,Hq,Nq,d], lse [Bt,Hq,Nq], sel dict, tsel dict, count).
+
+    q may hold fewer rows (Nq) than k, v (Nk): query row iq is then the token
+    at position iq + Nk - Nq of the history (the causal offset of the
+    Bit-Axon page).  Block gating needs Nq = Nk."""
     q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
-    Bt, Hq, N, d = q.shape
-    Hkv = k.shape[1]
+    Bt, Hq, Nq, d = q.shape
+    Hkv, N = k.shape[1], k.shape[2]
+    off = N - Nq
+    assert off >= 0 and (not top_k or off == 0)
     G = Hq // Hkv
     scale = 1.0 / math.sqrt(d) if scale is None else scale
-    out = np.zeros((Bt, Hq, N, d))
-    lse = np.zeros((Bt, Hq, N))
-    count = np.zeros((Bt, Hq, N), dtype=np.int64)
+    out = np.zeros((Bt, Hq, Nq, d))
+    lse = np.zeros((Bt, Hq, Nq))
+    count = np.zeros((Bt, Hq, Nq), dtype=np.int64)
     sels, tsels = {}, {}
     for b in range(Bt):
         tok = {}
         if token_top_k:
-            for i in range(N):
-                sc = {j: sum((_frac(idx_q[b, i, e]) * _frac(idx_k[b, j, e])
+            for iq in range(Nq):
+                i = iq + off
+                sc = {j: sum((_frac(idx_q[b, iq, e]) * _frac(idx_k[b, j, e])
                               for e in range(idx_q.shape[2])), Fraction(0))
                       for j in range(i)}
                 tok[i] = set(best_subset(sc, min(token_top_k, i)))
-                tsels[(b, i)] = tok[i]
+                tsels[(b, iq)] = tok[i]
         for h in range(Hq):
             g = h // G
             pooled = {}
@@ -65,14 +72,15 @@ def forward(q, k, v, *, block_size=0, top_k=0, window=0, idx_q=None, idx_k=None,
                     pooled[c] = [sum((_frac(k[b, g, j, e])
                                       for j in range(c * block_size, (c + 1) * block_size)),
                                      Fraction(0)) / block_size for e in range(d)]
-            for i in range(N):
+            for iq in range(Nq):
+                i = iq + off
                 chosen = set()
                 if top_k:
                     own = i // block_size
-                    sc = {c: sum((_frac(q[b, h, i, e]) * pooled[c][e] for e in range(d)),
+                    sc = {c: sum((_frac(q[b, h, iq, e]) * pooled[c][e] for e in range(d)),
                                  Fraction(0)) for c in range(own)}
                     chosen = set(best_subset(sc, min(top_k - 1, own))) | {own}
-                    sels[(b, h, i)] = chosen
+                    sels[(b, h, iq)] = chosen
                 keys = []
                 for j in range(N):
                     causal = j <= i
@@ -81,14 +89,14 @@ def forward(q, k, v, *, block_size=0, top_k=0, window=0, idx_q=None, idx_k=None,
                     in_tokens = bool(token_top_k) and j in tok[i]
                     if causal and (in_window or in_block or in_tokens):
                         keys.append(j)
-                logits = [scale * sum(q[b, h, i, e] * k[b, g, j, e] for e in range(d))
+                logits = [scale * sum(q[b, h, iq, e] * k[b, g, j, e] for e in range(d))
                           for j in keys]
                 z = None if sink is None else float(sink[h])
                 M = max(logits + ([z] if z is not None else []), default=-math.inf)
                 w = [math.exp(x - M) for x in logits]
                 L = sum(w) + (math.exp(z - M) if z is not None else 0.0)
                 for e in range(d):
-                    out[b, h, i, e] = sum(wj * v[b, g, j, e] for wj, j in zip(w, keys)) / L
-                lse[b, h, i] = M + math.log(L)
-                count[b, h, i] = len(keys)
+                    out[b, h, iq, e] = sum(wj * v[b, g, j, e] for wj, j in zip(w, keys)) / L
+                lse[b, h, iq] = M + math.log(L)
+                count[b, h, iq] = len(keys)
     return out, lse, sels, tsels, count

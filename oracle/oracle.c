@@ -150,6 +150,11 @@ void orc_block_select(const float* q, const double* kbar, int64_t Hq, int64_t Hk
  * tokens].  Reading taken: score = <idx_q_i, idx_k_j> (unscaled), candidates
  * j < i, keep the first min(Kt, i) by (-score, j).  Token rows are
  * r = b*N + i; tsel row = ascending token ids, then -1.
+ *
+ * The _at form scores Nq queries that continue a history of Nk tokens
+ * [Bit-Axon SWA + MoE page, "슬라이딩 윈도우 마스크": the causal offset
+ * kv_len - seq_len places query row rq at position rq + off]: row
+ * r = b*Nq + rq sits at i = rq + off, keys come from [Bt, Nk, dI].
  */
 void orc_token_scores(const float* iq, const float* ik, int64_t N, int64_t dI,
                       const int64_t* rows, int64_t nrows, double* scores) {
@@ -166,19 +171,19 @@ void orc_token_scores(const float* iq, const float* ik, int64_t N, int64_t dI,
     }
 }
 
-void orc_token_select(const float* iq, const float* ik, int64_t N, int64_t dI, int64_t Kt,
-                      const int64_t* rows, int64_t nrows,
-                      int32_t* tsel, double* s_last, double* s_next) {
+void orc_token_select_at(const float* iq, const float* ik, int64_t Nq, int64_t Nk, int64_t dI,
+                         int64_t Kt, int64_t off, const int64_t* rows, int64_t nrows,
+                         int32_t* tsel, double* s_last, double* s_next) {
 #pragma omp parallel
     {
-        cand_t* cand = (cand_t*)malloc(sizeof(cand_t) * (size_t)(N > 0 ? N : 1));
+        cand_t* cand = (cand_t*)malloc(sizeof(cand_t) * (size_t)(Nk > 0 ? Nk : 1));
 #pragma omp for schedule(dynamic, 4)
         for (int64_t t = 0; t < nrows; ++t) {
-            const int64_t r = rows[t], i = r % N, b = r / N;
+            const int64_t r = rows[t], i = r % Nq + off, b = r / Nq;
             for (int64_t j = 0; j < i; ++j) {
                 double acc = 0.0;
                 for (int64_t e = 0; e < dI; ++e)
-                    acc += (double)iq[r * dI + e] * (double)ik[(b * N + j) * dI + e];
+                    acc += (double)iq[r * dI + e] * (double)ik[(b * Nk + j) * dI + e];
                 cand[j].s = acc;
                 cand[j].idx = j;
             }
@@ -193,6 +198,12 @@ void orc_token_select(const float* iq, const float* ik, int64_t N, int64_t dI, i
         }
         free(cand);
     }
+}
+
+void orc_token_select(const float* iq, const float* ik, int64_t N, int64_t dI, int64_t Kt,
+                      const int64_t* rows, int64_t nrows,
+                      int32_t* tsel, double* s_last, double* s_next) {
+    orc_token_select_at(iq, ik, N, N, dI, Kt, 0, rows, nrows, tsel, s_last, s_next);
 }
 
 /*
@@ -211,15 +222,20 @@ void orc_token_select(const float* iq, const float* ik, int64_t N, int64_t dI, i
  * sel  [nrows, sel_w]  block ids per listed row, -1 ignored (NULL: none)
  * tsel [nrows, tsel_w] token ids per listed row, -1 ignored (NULL: none)
  * count[t] = |A(i)|.  Returns 0, or -1 if an id is out of range.
+ *
+ * Queries q [Bt, Hq, Nq, d] against keys k, v [Bt, Hkv, N, d]: row
+ * r = (b*Hq + h)*Nq + rq sits at position i = rq + off [Bit-Axon page,
+ * "슬라이딩 윈도우 마스크": the causal offset kv_len - seq_len during
+ * decoding]; orc_attend is the case Nq = N, off = 0.
  */
-int orc_attend(const float* q, const float* k, const float* v,
-               int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
-               double scale, int64_t window, int64_t B,
-               const int32_t* sel, int64_t sel_w,
-               const int32_t* tsel, int64_t tsel_w,
-               const float* sink,
-               const int64_t* rows, int64_t nrows,
-               double* out, double* lse, int64_t* count) {
+int orc_attend_at(const float* q, const float* k, const float* v,
+                  int64_t Hq, int64_t Hkv, int64_t Nq, int64_t N, int64_t d, int64_t off,
+                  double scale, int64_t window, int64_t B,
+                  const int32_t* sel, int64_t sel_w,
+                  const int32_t* tsel, int64_t tsel_w,
+                  const float* sink,
+                  const int64_t* rows, int64_t nrows,
+                  double* out, double* lse, int64_t* count) {
     const int64_t G = Hq / Hkv;
     int bad = 0;
 #pragma omp parallel
@@ -229,7 +245,7 @@ int orc_attend(const float* q, const float* k, const float* v,
 #pragma omp for schedule(dynamic, 8)
         for (int64_t t = 0; t < nrows; ++t) {
             const int64_t r = rows[t];
-            const int64_t i = r % N, bh = r / N, b = bh / Hq, h = bh % Hq, g = h / G;
+            const int64_t i = r % Nq + off, bh = r / Nq, b = bh / Hq, h = bh % Hq, g = h / G;
             memset(mark, 0, (size_t)(i + 1));
             if (window > 0)
                 for (int64_t j = (i - window + 1 > 0 ? i - window + 1 : 0); j <= i; ++j)
@@ -285,4 +301,16 @@ int orc_attend(const float* q, const float* k, const float* v,
         free(x);
     }
     return bad ? -1 : 0;
+}
+
+int orc_attend(const float* q, const float* k, const float* v,
+               int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+               double scale, int64_t window, int64_t B,
+               const int32_t* sel, int64_t sel_w,
+               const int32_t* tsel, int64_t tsel_w,
+               const float* sink,
+               const int64_t* rows, int64_t nrows,
+               double* out, double* lse, int64_t* count) {
+    return orc_attend_at(q, k, v, Hq, Hkv, N, N, d, 0, scale, window, B, sel, sel_w, tsel, tsel_w,
+                         sink, rows, nrows, out, lse, count);
 }

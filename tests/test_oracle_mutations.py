@@ -31,6 +31,9 @@ MUTATIONS = [
     ("token selection keeps one too few", [("const int64_t m = Kt < i ? Kt : i;", "const int64_t m = Kt - 1 < i ? Kt - 1 : i;")]),
     ("lse without the max", [("lse[t] = M + log(L);", "lse[t] = log(L);")]),
     ("pool divides by B - 1", [("dst[e] = acc / (double)B;", "dst[e] = acc / (double)(B - 1);")]),
+    ("decode attention ignores the offset", [("const int64_t i = r % Nq + off, bh = r / Nq,",
+                                              "const int64_t i = r % Nq, bh = r / Nq,")]),
+    ("decode token select ignores the offset", [("i = r % Nq + off, b = r / Nq;", "i = r % Nq, b = r / Nq;")]),
 ]
 
 PIN_CALLS = [
@@ -48,6 +51,11 @@ PIN_CALLS = [
     lambda: pins.test_p9_sink_closed_form(),
     lambda: pins.test_p10_token_selection_cases(),
     lambda: pins.test_pool_is_block_mean(),
+] + [
+    (lambda c=c, n=n: pins.test_p15_decode_is_last_prefill_rows(c, n))
+    for c in range(len(pins.DECODE_CASES)) for n in (1, 5)
+] + [
+    (lambda c=c: pins.test_p16_decode_brute_force(c, False)) for c in range(len(pins.DECODE_CASES))
 ]
 
 

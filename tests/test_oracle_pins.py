@@ -311,6 +311,78 @@ def test_p14_permutation_equivariance():
     np.testing.assert_array_equal(l2, l[pb][:, pq])
 
 
+# P15: a decode/append step -- Nq new queries continuing a history of Nk
+# keys, query row rq at position rq + Nk - Nq (the causal offset of the
+# Bit-Axon page, "슬라이딩 윈도우 마스크") -- gives exactly the last Nq rows
+# of the prefill over the whole sequence (window, token gate, sink, GQA,
+# full attention as a window past the sequence).
+DECODE_CASES = [
+    dict(window=7),
+    dict(window=1000),
+    dict(window=5, token_top_k=6, sink=True),
+    dict(window=1, token_top_k=40),
+]
+
+
+@pytest.mark.parametrize("case", range(len(DECODE_CASES)))
+@pytest.mark.parametrize("nq", [1, 5, 64])
+def test_p15_decode_is_last_prefill_rows(case, nq):
+    kw = dict(DECODE_CASES[case])
+    use_sink = kw.pop("sink", False)
+    Bt, Hq, Hkv, Nk, d, dI = 2, 4, 2, 64, 8, 6
+    q, k, v = rnd((Bt, Hq, Nk, d), 60 + case), rnd((Bt, Hkv, Nk, d), 61), rnd((Bt, Hkv, Nk, d), 62)
+    iq = ik = None
+    if kw.get("token_top_k"):
+        iq, ik = rnd((Bt, Nk, dI), 63), rnd((Bt, Nk, dI), 64)
+    sink = rnd(Hq, 65) if use_sink else None
+    full = oracle.forward(q, k, v, idx_q=iq, idx_k=ik, sink=sink, **kw)
+    off = Nk - nq
+    dec = oracle.forward(np.ascontiguousarray(q[:, :, off:]), k, v,
+                         idx_q=None if iq is None else np.ascontiguousarray(iq[:, off:]),
+                         idx_k=ik, sink=sink, **kw)
+    last = np.array([(bh * Nk + off + r) for bh in range(Bt * Hq) for r in range(nq)])
+    np.testing.assert_array_equal(dec["out"], full["out"][last])
+    np.testing.assert_array_equal(dec["lse"], full["lse"][last])
+    np.testing.assert_array_equal(dec["count"], full["count"][last])
+    if kw.get("token_top_k"):
+        np.testing.assert_array_equal(dec["tsel"], full["tsel"][last])
+
+
+# P16: the decode step against the exact brute force, which places the
+# queries by its own reading of the offset.
+@pytest.mark.parametrize("case", range(len(DECODE_CASES)))
+@pytest.mark.parametrize("ties", [False, True])
+def test_p16_decode_brute_force(case, ties):
+    kw = dict(DECODE_CASES[case])
+    use_sink = kw.pop("sink", False)
+    Bt, Hq, Hkv, Nq, Nk, d, dI = 1, 2, 1, 3, 16, 4, 3
+    kw["window"] = min(kw["window"], 20)
+    kw["token_top_k"] = min(kw.get("token_top_k", 0), 9)
+    rng = np.random.default_rng(200 + case + 50 * ties)
+    draw = (lambda s: rng.integers(-1, 2, size=s).astype(np.float32)) if ties else \
+           (lambda s: rng.standard_normal(s).astype(np.float32))
+    q, k, v = draw((Bt, Hq, Nq, d)), draw((Bt, Hkv, Nk, d)), draw((Bt, Hkv, Nk, d))
+    iq = ik = None
+    if kw["token_top_k"]:
+        iq, ik = draw((Bt, Nq, dI)), draw((Bt, Nk, dI))
+    sink = rng.standard_normal(Hq).astype(np.float32) if use_sink else None
+    r = oracle.forward(q, k, v, idx_q=iq, idx_k=ik, sink=sink, **kw)
+    bo, bl, _, btsel, bcnt = brute.forward(q, k, v, idx_q=iq, idx_k=ik, sink=sink, **kw)
+    np.testing.assert_allclose(r["out"].reshape(bo.shape), bo, atol=1e-12)
+    np.testing.assert_allclose(r["lse"].reshape(bl.shape), bl, atol=1e-12)
+    np.testing.assert_array_equal(r["count"].reshape(bcnt.shape), bcnt)
+    if kw["token_top_k"]:
+        for t, (b, h, iqr) in enumerate((b, h, i) for b in range(Bt) for h in range(Hq)
+                                        for i in range(Nq)):
+            assert {j for j in r["tsel"][t].tolist() if j >= 0} == btsel[(b, iqr)]
+
+
+def test_decode_rejects_block_gating():
+    q, k = rnd((1, 1, 4, 8), 70), rnd((1, 1, 16, 8), 71)
+    with pytest.raises(ValueError):
+        oracle.forward(q, k, k, block_size=4, top_k=2)
+
+
 # The pooled keys are block means (checked with numpy's mean, a different
 # summation routine than the oracle's loop).
 def test_pool_is_block_mean():
