@@ -22,11 +22,22 @@
  *      out_i = sum_j p_j v_j,  lse_i = natural log of the softmax
  *      normaliser (sink included).
  *
- * Layouts (row-major, contiguous, device memory):
+ * Decode/append step (kv_len > seq_len) [Bit-Axon "SWA + MoE" page,
+ * "슬라이딩 윈도우 마스크": the causal offset kv_len - seq_len during
+ * autoregressive decoding with a KV cache]: the seq_len queries are the
+ * newest positions of a history of kv_len keys; query row r is position
+ * i = kv_len - seq_len + r and the three steps above apply to it over keys
+ * 0 .. kv_len-1 (the token gate scans the whole cached history).  Block
+ * gating is not offered here: the MoBA summary page runs generation with
+ * full attention (window >= kv_len).  Limits: seq_len <= 64.
+ *
+ * Layouts (row-major, contiguous, device memory; kv_len = seq_len unless a
+ * decode step):
  *   q, out  [batch, n_q_heads,  seq_len, head_dim]   dtype cfg->dtype
- *   k, v    [batch, n_kv_heads, seq_len, head_dim]   dtype cfg->dtype
+ *   k, v    [batch, n_kv_heads, kv_len,  head_dim]   dtype cfg->dtype
  *   lse     [batch, n_q_heads,  seq_len]              fp32
- *   idx_q, idx_k [batch, seq_len, index_dim]          dtype cfg->dtype
+ *   idx_q   [batch, seq_len, index_dim], idx_k [batch, kv_len, index_dim]
+ *                                                     dtype cfg->dtype
  *   sink    [n_q_heads]                               fp32
  *   block_sel_out [batch, n_q_heads, seq_len, top_k]  int32: kept block ids
  *           ascending (the own block is the last valid one), then -1.
@@ -54,7 +65,7 @@
 extern "C" {
 #endif
 
-#define SPARSE_ATTN_ABI_VERSION 1
+#define SPARSE_ATTN_ABI_VERSION 2
 
 typedef enum {
     SA_BF16 = 0, /* bfloat16 inputs and out; fp32 accumulation.  Q K^T runs on
@@ -100,14 +111,18 @@ typedef struct {
     int32_t* block_sel_out; /* optional copy-out of the block selection, or NULL */
     int32_t* token_sel_out; /* optional copy-out of the token selection, or NULL */
     void* stream;           /* hipStream_t, NULL = default stream */
+    int32_t kv_len;         /* keys of the history: 0 or seq_len for a prefill;
+                               > seq_len for a decode/append step (seq_len <= 64,
+                               top_k == 0; kv_len <= 65536 with a token gate) */
 } sparse_attn_cfg;
 
 /* Bytes of device workspace sparse_attn_fwd needs for this configuration
  * (workspace fields of cfg are ignored).  Host only; touches no GPU. */
 int sparse_attn_workspace_bytes(const sparse_attn_cfg* cfg, size_t* bytes);
 
-/* The whole prefill forward: enqueues every stage on cfg->stream and returns
- * without waiting.  q, k, v, out, lse are device pointers (16-byte aligned). */
+/* The whole forward (a prefill, or a decode/append step when kv_len >
+ * seq_len): enqueues every stage on cfg->stream and returns without
+ * waiting.  q, k, v, out, lse are device pointers (16-byte aligned). */
 int sparse_attn_fwd(const void* q, const void* k, const void* v,
                     const sparse_attn_cfg* cfg, void* out, float* lse);
 

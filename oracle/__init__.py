@@ -69,6 +69,8 @@ def _load(path=None):
                                ctypes.c_void_p, _i64, ctypes.c_void_p, _i64,
                                ctypes.c_void_p, _i64p, _i64, _f64p, _f64p, _i64p]
     lib.orc_attend.restype = ctypes.c_int
+    lib.orc_token_scores_at.argtypes = [_f32p, _f32p, _i64, _i64, _i64, _i64, _i64p, _i64, _f64p]
+    lib.orc_token_scores_at.restype = None
     lib.orc_token_select_at.argtypes = [_f32p, _f32p, _i64, _i64, _i64, _i64, _i64, _i64p, _i64,
                                         _i32p, _f64p, _f64p]
     lib.orc_token_select_at.restype = None
@@ -108,7 +110,10 @@ def _f32(a):
 def _rows(rows, total):
     if rows is None:
         return np.arange(total, dtype=np.int64)
-    return np.ascontiguousarray(rows, dtype=np.int64)
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    if len(rows) and (rows.min() < 0 or rows.max() >= total):
+        raise IndexError("row id out of range")
+    return rows
 
 
 def block_pool(k, B):
@@ -150,11 +155,14 @@ def block_select(q, kbar, B, top_k, rows=None):
 
 
 def token_scores(idx_q, idx_k, rows):
+    """Indexer scores [len(rows), Nk] of token rows r = b*Nq + rq; -inf for
+    keys that are not candidates (j >= position)."""
     iq, ik = _f32(idx_q), _f32(idx_k)
-    Bt, N, dI = iq.shape
-    rows = _rows(rows, Bt * N)
-    out = np.empty((len(rows), N), dtype=np.float64)
-    _load().orc_token_scores(iq, ik, N, dI, rows, len(rows), out)
+    Bt, Nq, dI = iq.shape
+    Nk = ik.shape[1]
+    rows = _rows(rows, Bt * Nq)
+    out = np.empty((len(rows), Nk), dtype=np.float64)
+    _load().orc_token_scores_at(iq, ik, Nq, Nk, dI, _offset(Nq, Nk), rows, len(rows), out)
     return out
 
 

@@ -156,19 +156,24 @@ void orc_block_select(const float* q, const double* kbar, int64_t Hq, int64_t Hk
  * kv_len - seq_len places query row rq at position rq + off]: row
  * r = b*Nq + rq sits at i = rq + off, keys come from [Bt, Nk, dI].
  */
-void orc_token_scores(const float* iq, const float* ik, int64_t N, int64_t dI,
-                      const int64_t* rows, int64_t nrows, double* scores) {
+void orc_token_scores_at(const float* iq, const float* ik, int64_t Nq, int64_t Nk, int64_t dI,
+                         int64_t off, const int64_t* rows, int64_t nrows, double* scores) {
 #pragma omp parallel for schedule(dynamic, 4)
     for (int64_t t = 0; t < nrows; ++t) {
-        const int64_t r = rows[t], i = r % N, b = r / N;
-        for (int64_t j = 0; j < N; ++j) {
-            if (j >= i) { scores[t * N + j] = -INFINITY; continue; }
+        const int64_t r = rows[t], i = r % Nq + off, b = r / Nq;
+        for (int64_t j = 0; j < Nk; ++j) {
+            if (j >= i) { scores[t * Nk + j] = -INFINITY; continue; }
             double acc = 0.0;
             for (int64_t e = 0; e < dI; ++e)
-                acc += (double)iq[r * dI + e] * (double)ik[(b * N + j) * dI + e];
-            scores[t * N + j] = acc;
+                acc += (double)iq[r * dI + e] * (double)ik[(b * Nk + j) * dI + e];
+            scores[t * Nk + j] = acc;
         }
     }
+}
+
+void orc_token_scores(const float* iq, const float* ik, int64_t N, int64_t dI,
+                      const int64_t* rows, int64_t nrows, double* scores) {
+    orc_token_scores_at(iq, ik, N, N, dI, 0, rows, nrows, scores);
 }
 
 void orc_token_select_at(const float* iq, const float* ik, int64_t Nq, int64_t Nk, int64_t dI,

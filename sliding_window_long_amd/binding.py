@@ -45,6 +45,7 @@ class SparseAttnCfg(ctypes.Structure):
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("block_sel_out", ctypes.c_void_p), ("token_sel_out", ctypes.c_void_p),
         ("stream", ctypes.c_void_p),
+        ("kv_len", ctypes.c_int32),
     ]
 
 
@@ -100,12 +101,13 @@ class Params:
     token_top_k: int = 0
     index_dim: int = 0
     softmax_scale: float = 0.0
+    kv_len: int = 0           # > seq_len: decode/append step over a cached history
 
     def cfg(self) -> SparseAttnCfg:
         c = SparseAttnCfg()
         c.struct_size = ctypes.sizeof(SparseAttnCfg)
         for f in ("batch", "n_q_heads", "n_kv_heads", "seq_len", "head_dim", "dtype",
-                  "block_size", "top_k", "window", "token_top_k", "index_dim"):
+                  "block_size", "top_k", "window", "token_top_k", "index_dim", "kv_len"):
             setattr(c, f, int(getattr(self, f)))
         c.softmax_scale = float(self.softmax_scale)
         return c
@@ -164,8 +166,9 @@ def params_for(q, k, *, block_size=0, top_k=0, window=0, token_top_k=0, index_di
     dt = {torch.bfloat16: SA_BF16, torch.float32: SA_F32}.get(q.dtype)
     if dt is None:
         raise TypeError(f"q dtype {q.dtype} not supported (bfloat16 or float32)")
+    Nk = k.shape[2]
     return Params(Bt, Hq, k.shape[1], N, d, dt, block_size, top_k, window, token_top_k,
-                  index_dim, 0.0 if scale is None else float(scale))
+                  index_dim, 0.0 if scale is None else float(scale), Nk if Nk != N else 0)
 
 
 class Workspace:
@@ -191,7 +194,9 @@ def forward(q, k, v, *, block_size=0, top_k=0, window=0, idx_q=None, idx_k=None,
             workspace: Workspace | None = None, out=None, lse=None):
     """Causal sparse-attention prefill on q's device and torch's current
     stream.  Returns (out, lse) or, with return_selection,
-    (out, lse, block_sel, token_sel)."""
+    (out, lse, block_sel, token_sel).  When k, v (and idx_k) hold more
+    positions than q (and idx_q), the call is a decode/append step: the
+    queries are the newest positions of that history."""
     import torch
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not t.is_cuda or not t.is_contiguous():

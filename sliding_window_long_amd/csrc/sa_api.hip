@@ -30,11 +30,14 @@ struct Plan {
     int max_chunks;
     bool tok;
     int top_t, nt32, tok_units, tok_nkp;
+    bool dec;               // decode/append step: Nk > N
+    int Nk, dec_cmax;
     float scale;
     // workspace regions (byte offsets)
     size_t o_split, o_kb3, o_sel, o_count, o_cursor, o_listoff, o_nchunks, o_chunk_list,
         o_chunk_start, o_entries, o_part_o, o_part_lse, o_tok_split, o_tok_state, o_tok_mask,
-        o_tok_qn, o_tok_win, o_tok_kpart, o_tok_scr, o_tok_nslow,
+        o_tok_qn, o_tok_win, o_tok_kpart, o_tok_scr, o_tok_nslow, o_dec_scores, o_dec_list,
+        o_dec_nfar, o_dec_part,
         o_v16, total;
 };
 
@@ -53,15 +56,23 @@ int make_plan(const sparse_attn_cfg* c, Plan* p) {
     if (c->n_q_heads % c->n_kv_heads) return SA_E_SHAPE;
     if (c->n_q_heads / c->n_kv_heads > 16) return SA_E_UNSUPPORTED;
     if (c->window == 0 && c->top_k == 0) return SA_E_NO_SELF;
+    // Keys of the history: a decode/append step has more keys than queries.
+    if (c->kv_len < 0) return SA_E_INVALID_ARG;
+    const int Nk = c->kv_len > 0 ? c->kv_len : c->seq_len;
+    if (Nk < c->seq_len) return SA_E_INVALID_ARG;
+    const bool dec = Nk > c->seq_len;
+    if (dec && (c->top_k > 0 || c->seq_len > sa::kDecMaxQ)) return SA_E_UNSUPPORTED;
     if (c->token_top_k > 0) {
         if (c->index_dim != 64) return SA_E_UNSUPPORTED_HEAD_DIM;
         // 16 index bits in the selection key; block and token gates are
         // separate methods and are not combined in one call.
-        if (c->seq_len > 65536 || c->top_k > 0) return SA_E_UNSUPPORTED;
+        if (Nk > 65536 || c->top_k > 0) return SA_E_UNSUPPORTED;
     }
 
     Plan& P = *p;
     memset(&P, 0, sizeof(P));
+    P.Nk = Nk;
+    P.dec = dec;
     P.Bt = c->batch; P.Hq = c->n_q_heads; P.Hkv = c->n_kv_heads; P.N = c->seq_len;
     P.D = c->head_dim; P.G = P.Hq / P.Hkv;
     P.f32 = c->dtype == SA_F32;
@@ -70,7 +81,26 @@ int make_plan(const sparse_attn_cfg* c, Plan* p) {
     const size_t esz = P.f32 ? 4 : 2;
     if (rows * P.D * (long long)esz > (1LL << 40)) return SA_E_UNSUPPORTED;
     // One head's K or V (16-bit) must be addressable by a 32-bit byte offset.
-    if ((long long)P.N * P.D * 2 >= (1LL << 31)) return SA_E_UNSUPPORTED;
+    if ((long long)P.Nk * P.D * 2 >= (1LL << 31)) return SA_E_UNSUPPORTED;
+
+    if (P.dec) {
+        // Decode/append step: its own small workspace (indexer scores, kept
+        // lists, chunk partials).
+        size_t off = 0;
+        auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
+        P.tok = c->token_top_k > 0;
+        P.top_t = P.tok ? c->token_top_k : 0;
+        if (P.tok) {
+            P.o_dec_scores = take((size_t)P.Bt * P.N * P.Nk * 4);
+            P.o_dec_list = take((size_t)P.Bt * P.N * P.top_t * 4);
+            P.o_dec_nfar = take((size_t)P.Bt * P.N * 4);
+        }
+        const long long span = (c->window < P.Nk ? c->window : P.Nk) + (long long)P.top_t;
+        P.dec_cmax = (int)((span + 255) / 256);
+        P.o_dec_part = take((size_t)P.Bt * P.Hq * P.N * P.dec_cmax * (P.D + 2) * 4);
+        P.total = off;
+        return SA_OK;
+    }
 
     P.gate = c->top_k > 0;
     if (P.gate) {
@@ -263,6 +293,25 @@ int sparse_attn_fwd(const void* q, const void* k, const void* v, const sparse_at
     hipStream_t s = (hipStream_t)cfg->stream;
     char* ws = (char*)cfg->workspace;
     auto ok = [](hipError_t e) { return e == hipSuccess; };
+
+    if (P.dec) {
+        sa::DecArgs da{};
+        da.q = q; da.k = k; da.v = v; da.iq = cfg->idx_q; da.ik = cfg->idx_k;
+        da.f32 = P.f32 ? 1 : 0;
+        da.Bt = P.Bt; da.Hq = P.Hq; da.Hkv = P.Hkv; da.Nq = P.N; da.Nk = P.Nk; da.D = P.D;
+        da.top_t = P.top_t; da.window = cfg->window; da.scale = P.scale; da.sink = cfg->sink;
+        da.part = (float*)(ws + P.o_dec_part); da.cmax = P.dec_cmax;
+        da.out = out; da.lse = lse;
+        if (P.tok) {
+            da.scores = (float*)(ws + P.o_dec_scores);
+            da.list = cfg->token_sel_out ? cfg->token_sel_out : (int32_t*)(ws + P.o_dec_list);
+            da.nfar = (int32_t*)(ws + P.o_dec_nfar);
+            StageScope t("decode_token_select", s);
+            if (!ok(sa::launch_decode_select(da, s))) return SA_E_HIP;
+        }
+        StageScope t("decode_attn", s);
+        return ok(sa::launch_decode_attn(da, s)) ? SA_OK : SA_E_HIP;
+    }
 
     // Operand planes: bf16 inputs are used in place; fp32 inputs are split.
     const uint16_t* qp[2] = {(const uint16_t*)q, nullptr};

@@ -1,0 +1,332 @@
+// sa_decode.hip -- decode/append step: a few new queries continuing a cached
+// history.
+//
+// [Bit-Axon SWA + MoE page, "슬라이딩 윈도우 마스크"]: while decoding, the KV
+// cache is longer than the queries; the causal offset kv_len - seq_len
+// places query row r at position p = r + off, which attends j <= p with
+// p - j < w.  [Naive-N0.5-Flash page, "SWA와 DSA를 결합한 어텐션"]: the
+// indexer scans the whole cached history and the top tokens join the window
+// (same reading as the prefill: candidates j < p, keep min(top_t, p), a tie
+// to the lower j).  [MoBA summary page, the long-context experiments]:
+// generation runs full attention, i.e. a window of kv_len or more.
+//
+// Decode reads the cache once and does little arithmetic per byte, so the
+// kernels are vector-ALU kernels in fp32:
+//   dec_scores  : indexer scores of every (query, key), fp32, to workspace.
+//   dec_select  : per query, exact radix select of the kept tokens on the
+//                 48-bit key ord(score) << 16 | (0xFFFF - j), then the kept
+//                 ids as an ascending list and the count below the window.
+//   dec_attn    : per (batch, kv head, query, chunk of 256 attended keys --
+//                 the window [lo, p] first, then the kept tokens before lo):
+//                 logits, chunk max and sum, and the chunk's P V, for every
+//                 q head of the kv group from one load of each key and value.
+//   dec_combine : merges the chunk partials and the sink column; out, lse.
+#include "sa_device.hpp"
+#include "sa_internal.hpp"
+
+namespace sa {
+
+constexpr int DEC_THREADS = 256;
+constexpr int DEC_CHUNK = 256;   // attended keys per dec_attn workgroup
+
+__device__ __forceinline__ float dec_load(const void* p, size_t i, int f32) {
+    return f32 ? ((const float*)p)[i] : bf16_to_f32(((const uint16_t*)p)[i]);
+}
+
+__device__ __forceinline__ uint32_t dec_ord32(float s) {
+    const uint32_t u = __float_as_uint(s);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Indexer scores [Bt, Nq, Nk]: one key per thread against every query.
+__global__ __launch_bounds__(DEC_THREADS) void dec_scores_kernel(DecArgs a) {
+    __shared__ float qs[kDecMaxQ * 64];
+    const int bt = blockIdx.y, tid = threadIdx.x, j = blockIdx.x * DEC_THREADS + tid;
+    for (int x = tid; x < a.Nq * 64; x += DEC_THREADS)
+        qs[x] = dec_load(a.iq, (size_t)bt * a.Nq * 64 + x, a.f32);
+    __syncthreads();
+    if (j >= a.Nk) return;
+    float kj[64];
+#pragma unroll
+    for (int e = 0; e < 64; ++e) kj[e] = dec_load(a.ik, ((size_t)bt * a.Nk + j) * 64 + e, a.f32);
+    for (int r = 0; r < a.Nq; ++r) {
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < 64; ++e) s = fmaf(qs[r * 64 + e], kj[e], s);
+        a.scores[((size_t)bt * a.Nq + r) * a.Nk + j] = s;
+    }
+}
+
+// Block-wide exclusive prefix sum of one value per thread (256 threads);
+// *total receives the sum.
+__device__ __forceinline__ int dec_scan(int x, int* sh, int tid, int* total) {
+    sh[tid] = x;
+    __syncthreads();
+    for (int d = 1; d < DEC_THREADS; d <<= 1) {
+        const int y = tid >= d ? sh[tid - d] : 0;
+        __syncthreads();
+        sh[tid] += y;
+        __syncthreads();
+    }
+    const int incl = sh[tid];
+    *total = sh[DEC_THREADS - 1];
+    __syncthreads();
+    return incl - x;
+}
+
+// Highest bin b of a 256-bin histogram whose count from the top reaches k
+// (one wave, 4 bins per lane): out = {b, count above b, count of b}.  The
+// histogram holds at least k entries.
+__device__ __forceinline__ void dec_find(const uint32_t* hist, uint32_t k, int lane, uint32_t* out) {
+    uint32_t cnt[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cnt[i] = hist[4 * lane + i];
+    const uint32_t tot = cnt[0] + cnt[1] + cnt[2] + cnt[3];
+    uint32_t incl = tot;   // count of bins >= 4 lane
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t o = __shfl_down(incl, d);
+        if (lane + d < 64) incl += o;
+    }
+    const uint32_t excl = incl - tot;
+    if (excl < k && incl >= k) {
+        uint32_t cum = excl;
+        for (int i = 3; i >= 0; --i) {
+            if (cum + cnt[i] >= k) {
+                out[0] = (uint32_t)(4 * lane + i);
+                out[1] = cum;
+                out[2] = cnt[i];
+                break;
+            }
+            cum += cnt[i];
+        }
+    }
+}
+
+// Kept tokens of one query: min(top_t, p) best of j < p, ascending, -1
+// padded; nfar = how many of them lie before the window start lo.
+__global__ __launch_bounds__(DEC_THREADS) void dec_select_kernel(DecArgs a) {
+    __shared__ uint32_t hist[256];
+    __shared__ int sh[DEC_THREADS];
+    __shared__ uint32_t s_b[3];
+    const int r = blockIdx.x, bt = blockIdx.y, tid = threadIdx.x;
+    const int p = a.Nk - a.Nq + r;
+    const int k = min(a.top_t, p);
+    const int lo = a.window > 0 ? max(0, p - a.window + 1) : p;
+    const float* sc = a.scores + ((size_t)bt * a.Nq + r) * a.Nk;
+    int32_t* list = a.list + ((size_t)bt * a.Nq + r) * a.top_t;
+    auto key_of = [&](int j) {
+        return ((uint64_t)dec_ord32(sc[j]) << 16) | (uint64_t)(0xffff - j);
+    };
+
+    // Threshold T: the k-th largest key (every key >= T is kept).
+    uint64_t prefix = 0, pmask = 0;
+    if (k > 0 && k < p) {
+        uint32_t rem = (uint32_t)k;
+        for (int d = 5; d >= 0; --d) {
+            const int shift = 8 * d;
+            hist[tid] = 0;
+            __syncthreads();
+            for (int j = tid; j < p; j += DEC_THREADS) {
+                const uint64_t key = key_of(j);
+                if ((key & pmask) == prefix) atomicAdd(&hist[(uint32_t)(key >> shift) & 255u], 1u);
+            }
+            __syncthreads();
+            if (tid < 64) dec_find(hist, rem, tid, s_b);
+            __syncthreads();
+            const uint32_t b = s_b[0], above = s_b[1], in_bin = s_b[2];
+            prefix |= (uint64_t)b << shift;
+            pmask |= (uint64_t)0xff << shift;
+            rem -= above;
+            __syncthreads();
+            if (in_bin == rem) break;   // every key of this bin is kept
+        }
+    }
+    // Compaction in key order: thread t owns ids [t*ch, t*ch + ch).
+    const int ch = (p + DEC_THREADS - 1) / DEC_THREADS;
+    const int j0 = min(p, tid * ch), j1 = min(p, j0 + ch);
+    auto kept = [&](int j) { return k >= p || (k > 0 && key_of(j) >= prefix); };
+    int n = 0, nlo = 0;
+    for (int j = j0; j < j1; ++j)
+        if (kept(j)) {
+            ++n;
+            nlo += j < lo;
+        }
+    int total = 0, total_lo = 0;
+    int pos = dec_scan(n, sh, tid, &total);
+    dec_scan(nlo, sh, tid, &total_lo);
+    for (int j = j0; j < j1; ++j)
+        if (kept(j) && pos < a.top_t) list[pos++] = j;
+    for (int x = total + tid; x < a.top_t; x += DEC_THREADS) list[x] = -1;
+    if (tid == 0) a.nfar[(size_t)bt * a.Nq + r] = total_lo;
+}
+
+// Attended keys of query r: the window [lo, p] (nw keys) then the nt kept
+// tokens before lo.
+__device__ __forceinline__ void dec_span(const DecArgs& a, int bt, int r, int& p, int& lo, int& nw,
+                                         int& nt) {
+    p = a.Nk - a.Nq + r;
+    lo = a.window > 0 ? max(0, p - a.window + 1) : p;
+    nw = a.window > 0 ? p - lo + 1 : 0;
+    nt = a.list ? a.nfar[(size_t)bt * a.Nq + r] : 0;
+}
+
+// One chunk of 256 attended keys of query r for all G q heads of kv head g.
+// Partial per (row, chunk): o[D] = sum_j e^(x_j - m) v_j, then m, l
+// (x in base-2 units: logit * log2(e)).
+template <int D>
+__global__ __launch_bounds__(DEC_THREADS) void dec_attn_kernel(DecArgs a) {
+    constexpr int PARTS = DEC_THREADS / D;   // key groups of the P V step
+    __shared__ float qs[16 * D];
+    __shared__ float ps[16 * DEC_CHUNK];
+    __shared__ int js[DEC_CHUNK];
+    __shared__ float red[16][2];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int c = blockIdx.x, bt = blockIdx.z;
+    const int g = blockIdx.y / a.Nq, r = blockIdx.y % a.Nq;
+    const int G = a.Hq / a.Hkv;
+    int p, lo, nw, nt;
+    dec_span(a, bt, r, p, lo, nw, nt);
+    const int L = nw + nt, key0 = c * DEC_CHUNK;
+    if (key0 >= L) return;   // whole block: nothing past the attended keys
+    const int nk = min(DEC_CHUNK, L - key0);
+
+    for (int x = tid; x < G * D; x += DEC_THREADS) {
+        const int hl = x / D, e = x % D;
+        qs[x] = dec_load(a.q, (((size_t)bt * a.Hq + g * G + hl) * a.Nq + r) * D + e, a.f32);
+    }
+    if (tid < nk) {
+        const int idx = key0 + tid;
+        js[tid] = idx < nw ? lo + idx : a.list[((size_t)bt * a.Nq + r) * a.top_t + (idx - nw)];
+    }
+    __syncthreads();
+
+    const size_t kvb = ((size_t)bt * a.Hkv + g) * a.Nk;
+    const float c2 = a.scale * kLog2e;
+    if (tid < nk) {
+        float kr[D];
+        const size_t kro = (kvb + js[tid]) * D;
+#pragma unroll
+        for (int e = 0; e < D; ++e) kr[e] = dec_load(a.k, kro + e, a.f32);
+        for (int hl = 0; hl < G; ++hl) {
+            float s = 0.f;
+#pragma unroll
+            for (int e = 0; e < D; ++e) s = fmaf(qs[hl * D + e], kr[e], s);
+            ps[hl * DEC_CHUNK + tid] = s * c2;
+        }
+    }
+    __syncthreads();
+    // Per head: max and sum over the chunk (wave w takes heads w, w+4, ...).
+    for (int hl = wave; hl < G; hl += 4) {
+        float* row = ps + hl * DEC_CHUNK;
+        float m = -INFINITY;
+        for (int t = lane; t < nk; t += 64) m = fmaxf(m, row[t]);
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d));
+        float l = 0.f;
+        for (int t = lane; t < nk; t += 64) {
+            const float e = fast_exp2(row[t] - m);
+            row[t] = e;
+            l += e;
+        }
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) l += __shfl_xor(l, d);
+        if (lane == 0) {
+            red[hl][0] = m;
+            red[hl][1] = l;
+        }
+    }
+    __syncthreads();
+    // P V: thread (part, e) sums its share of the chunk's keys for dim e.
+    const int part = tid / D, e = tid % D;
+    float o[16];
+#pragma unroll
+    for (int hl = 0; hl < 16; ++hl) o[hl] = 0.f;
+    if (part < PARTS) {
+        for (int t = part; t < nk; t += PARTS) {
+            const float vv = dec_load(a.v, (kvb + js[t]) * D + e, a.f32);
+#pragma unroll
+            for (int hl = 0; hl < 16; ++hl)
+                if (hl < G) o[hl] = fmaf(ps[hl * DEC_CHUNK + t], vv, o[hl]);
+        }
+    }
+    __syncthreads();   // ps is reused for the part sums below
+    float* acc = ps;   // [PARTS][16][D] <= 16 * DEC_CHUNK floats
+    if (part < PARTS)
+#pragma unroll
+        for (int hl = 0; hl < 16; ++hl)
+            if (hl < G) acc[(part * 16 + hl) * D + e] = o[hl];
+    __syncthreads();
+    for (int x = tid; x < G * D; x += DEC_THREADS) {
+        const int hl = x / D, ee = x % D;
+        float s = 0.f;
+        for (int q_ = 0; q_ < PARTS; ++q_) s += acc[(q_ * 16 + hl) * D + ee];
+        const size_t row = ((size_t)bt * a.Hq + g * G + hl) * a.Nq + r;
+        float* dst = a.part + (row * a.cmax + c) * (D + 2);
+        dst[ee] = s;
+        if (ee == 0) {
+            dst[D] = red[hl][0];
+            dst[D + 1] = red[hl][1];
+        }
+    }
+}
+
+// One wave per (batch, head, query): merge the chunks and the sink.
+template <int D>
+__global__ __launch_bounds__(DEC_THREADS) void dec_combine_kernel(DecArgs a) {
+    const int lane = threadIdx.x & 63;
+    const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= (size_t)a.Bt * a.Hq * a.Nq) return;
+    const int r = (int)(row % a.Nq), bt = (int)(row / ((size_t)a.Hq * a.Nq));
+    const int h = (int)((row / a.Nq) % a.Hq);
+    int p, lo, nw, nt;
+    dec_span(a, bt, r, p, lo, nw, nt);
+    const int nc = (nw + nt + DEC_CHUNK - 1) / DEC_CHUNK;
+    const float* src = a.part + row * a.cmax * (D + 2);
+    const float z = a.sink ? a.sink[h] * kLog2e : -INFINITY;   // base-2 units
+    float M = z;
+    for (int c = 0; c < nc; ++c) M = fmaxf(M, src[c * (D + 2) + D]);
+    float Ltot = a.sink ? fast_exp2(z - M) : 0.f;
+    for (int c = 0; c < nc; ++c) Ltot += src[c * (D + 2) + D + 1] * fast_exp2(src[c * (D + 2) + D] - M);
+    const float inv = Ltot > 0.f ? 1.f / Ltot : 0.f;
+    for (int e = lane; e < D; e += 64) {
+        float o = 0.f;
+        for (int c = 0; c < nc; ++c) o += src[c * (D + 2) + e] * fast_exp2(src[c * (D + 2) + D] - M);
+        o *= inv;
+        if (a.f32) ((float*)a.out)[row * D + e] = o;
+        else ((__bf16*)a.out)[row * D + e] = (__bf16)o;
+    }
+    if (lane == 0) a.lse[row] = Ltot > 0.f ? (M + fast_log2(Ltot)) * kLn2 : -INFINITY;
+}
+
+template <int D>
+static hipError_t dec_d(const DecArgs& a, hipStream_t s) {
+    const dim3 ag((unsigned)a.cmax, (unsigned)(a.Hkv * a.Nq), (unsigned)a.Bt);
+    hipLaunchKernelGGL(dec_attn_kernel<D>, ag, dim3(DEC_THREADS), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t rows = (size_t)a.Bt * a.Hq * a.Nq;
+    hipLaunchKernelGGL(dec_combine_kernel<D>, dim3((unsigned)((rows + 3) / 4)), dim3(DEC_THREADS), 0,
+                       s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_select(const DecArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL(dec_scores_kernel, dim3((unsigned)((a.Nk + DEC_THREADS - 1) / DEC_THREADS),
+                                               (unsigned)a.Bt),
+                       dim3(DEC_THREADS), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(dec_select_kernel, dim3((unsigned)a.Nq, (unsigned)a.Bt), dim3(DEC_THREADS), 0, s,
+                       a);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_attn(const DecArgs& a, hipStream_t s) {
+    if (a.D == 64) return dec_d<64>(a, s);
+    if (a.D == 80) return dec_d<80>(a, s);
+    if (a.D == 128) return dec_d<128>(a, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace sa

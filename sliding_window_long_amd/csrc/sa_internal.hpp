@@ -126,6 +126,31 @@ __host__ __device__ inline int tok_unit_base(int N, int c) {
 }
 inline int tok_units(int N) { return tok_unit_base(N, tok_chunks(N, tok_blocks(N) - 1)); }
 
+// Decode/append step: Nq (<= kDecMaxQ) queries at positions Nk - Nq + r of
+// a history of Nk keys.
+constexpr int kDecMaxQ = 64;
+struct DecArgs {
+    const void* q;          // [Bt, Hq, Nq, D], bf16 or fp32
+    const void* k;          // [Bt, Hkv, Nk, D]
+    const void* v;
+    const void* iq;         // [Bt, Nq, 64] indexer queries, or nullptr
+    const void* ik;         // [Bt, Nk, 64] indexer keys, or nullptr
+    int f32;                // inputs (and out) are fp32
+    int Bt, Hq, Hkv, Nq, Nk, D, top_t, window;
+    float scale;
+    const float* sink;      // [Hq] or nullptr
+    float* scores;          // [Bt, Nq, Nk] indexer scores
+    int32_t* list;          // [Bt, Nq, top_t] kept tokens, ascending, -1 padded; nullptr: no gate
+    int32_t* nfar;          // [Bt, Nq] kept tokens before the window
+    float* part;            // [Bt*Hq*Nq, cmax, D + 2] chunk partials (o, m, l)
+    int cmax;               // chunks of 256 attended keys per query, upper bound
+    void* out;              // [Bt, Hq, Nq, D], the input dtype
+    float* lse;             // [Bt, Hq, Nq]
+};
+
+hipError_t launch_decode_select(const DecArgs& a, hipStream_t s);
+hipError_t launch_decode_attn(const DecArgs& a, hipStream_t s);
+
 hipError_t launch_token_select(const TokArgs& a, int split, hipStream_t s);
 hipError_t launch_token_list(const TokArgs& a, int32_t* out, hipStream_t s);
 

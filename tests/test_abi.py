@@ -71,6 +71,13 @@ def code_of(params, **cfg_fields):
     (sa.Params(1, 4, 1, 256, 128, window=8, block_size=64, top_k=2, token_top_k=16,
                index_dim=64), -8),
     (sa.Params(1, 1, 1, 1 << 23, 128, window=8), -8),                # one head's K past 2 GiB
+    (sa.Params(1, 4, 4, 256, 64, window=8, kv_len=255), -1),          # fewer keys than queries
+    (sa.Params(1, 4, 4, 256, 64, window=8, kv_len=-1), -1),
+    (sa.Params(1, 4, 4, 4, 64, block_size=64, top_k=2, kv_len=256), -8),  # decode with block gate
+    (sa.Params(1, 4, 4, 65, 64, window=8, kv_len=256), -8),           # decode past 64 queries
+    (sa.Params(1, 4, 1, 1, 128, window=8, token_top_k=16, index_dim=64,
+               kv_len=65536 + 1), -8),                               # 16-bit token ids
+    (sa.Params(1, 4, 4, 1, 64, kv_len=256), -4),                      # decode, no window
 ])
 def test_invalid_configs(lib, params, code):
     assert code_of(params) == code
@@ -82,8 +89,21 @@ def test_valid_configs(lib):
               sa.Params(1, 32, 32, 16384, 80, window=4096),
               sa.Params(1, 32, 8, 131072, 128, block_size=512, top_k=8),
               sa.Params(1, 3, 3, 77, 80, window=1),
-              sa.Params(1, 16, 4, 65536, 128, window=128, token_top_k=2048, index_dim=64)):
+              sa.Params(1, 16, 4, 65536, 128, window=128, token_top_k=2048, index_dim=64),
+              sa.Params(1, 32, 32, 1, 80, window=4096, kv_len=16384),
+              sa.Params(4, 16, 4, 64, 128, window=128, token_top_k=2048, index_dim=64,
+                        kv_len=65536),
+              sa.Params(1, 8, 8, 16, 64, window=4, kv_len=16)):     # kv_len = seq_len: prefill
         assert code_of(p) == 0
+
+
+def test_decode_workspace(lib):
+    # chunk partials [rows, ceil((min(w, kv_len) + top_t) / 256), d + 2] fp32,
+    # plus indexer scores [Bt, Nq, kv_len] and the kept lists
+    p = sa.Params(1, 32, 32, 1, 80, window=4096, kv_len=16384)
+    assert sa.sparse_attn_workspace_bytes(p.cfg()) == 32 * 16 * 82 * 4
+    p = sa.Params(2, 16, 4, 3, 128, window=128, token_top_k=2048, index_dim=64, kv_len=65536)
+    assert sa.sparse_attn_workspace_bytes(p.cfg()) >= 2 * 3 * 65536 * 4 + 2 * 16 * 3 * 9 * 130 * 4
 
 
 def test_workspace_sizes_scale(lib):

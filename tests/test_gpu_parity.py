@@ -52,7 +52,7 @@ def run_and_check(inp, dev, rows=None, label=""):
     log(f"[gpu] {label} {wl}")
     out, lse, bsel, tsel = run_device(inp, dev)
     if rows is None:
-        rows = np.arange(wl.batch * wl.n_q_heads * wl.seq_len)
+        rows = np.arange(inp.q.shape[0] * inp.q.shape[1] * inp.q.shape[2])   # every query row
     rep = check(inp, out, lse, rows, bsel, tsel)
     log(f"[gpu] {label} {rep}")
     assert np.isfinite(out).all() and np.isfinite(lse).all()
@@ -196,3 +196,62 @@ def test_swa_token_reduced_sampled(dev):
 def test_swa_token_full_sampled(dev):
     wl = W.SWA_TOKEN_TOPK
     run_and_check(W.make_inputs(wl, 105), dev, W.sample_rows(wl, 160, 5), label="swa_token_full")
+
+
+# --- decode/append step (queries continuing a cached history) ---------------
+def decode_inputs(wl, nq, seed):
+    """The last nq positions of a seeded full-length input as the queries;
+    k, v, idx_k keep the whole history."""
+    inp = W.make_inputs(wl, seed)
+    off = wl.seq_len - nq
+    iq = None if inp.idx_q is None else np.ascontiguousarray(inp.idx_q[:, off:])
+    return W.Inputs(wl, np.ascontiguousarray(inp.q[:, :, off:]), inp.k, inp.v, inp.sink, iq,
+                    inp.idx_k)
+
+
+@pytest.mark.parametrize("d", [64, 80, 128])
+@pytest.mark.parametrize("Nk,nq,window", [(300, 1, 17), (300, 7, 1), (1000, 64, 300),
+                                          (1000, 3, 5000), (513, 64, 64)])
+def test_decode_window(dev, d, Nk, nq, window):
+    wl = W.Workload("dec_swa", 2, 4, 2, Nk, d, "bf16", window=window)
+    run_and_check(decode_inputs(wl, nq, 11 + d + Nk + nq), dev, label=f"decode_window nq={nq}")
+
+
+def test_decode_fp32_sink(dev):
+    wl = W.Workload("dec_f32", 1, 6, 3, 700, 64, "f32", window=200, sink=True)
+    run_and_check(decode_inputs(wl, 9, 4), dev, label="decode_f32")
+
+
+@pytest.mark.parametrize("Nk,nq,top_t,window", [(3000, 1, 100, 16), (3000, 5, 100, 1),
+                                                (3000, 64, 700, 64), (200, 8, 300, 4),
+                                                (2100, 3, 2048, 128)])
+def test_decode_token(dev, Nk, nq, top_t, window):
+    wl = W.Workload("dec_tok", 1, 4, 1, Nk, 128, "bf16", window=window, token_top_k=top_t,
+                    index_dim=64, sink=True)
+    run_and_check(decode_inputs(wl, nq, 31 + nq + top_t), dev, label=f"decode_token nq={nq}")
+
+
+def test_decode_token_ties(dev):
+    # Equal indexer keys: the lowest token ids win in the decode step too.
+    wl = W.Workload("dec_ties", 1, 2, 1, 1500, 64, "bf16", window=2, token_top_k=37, index_dim=64)
+    inp = decode_inputs(wl, 4, 5)
+    inp.idx_k[:] = inp.idx_k[:, :1]
+    out, lse, _, tsel = run_device(inp, dev)
+    for r in range(4):
+        assert tsel[0, r].tolist() == list(range(37)), r
+    rep = check(inp, out, lse, np.arange(2 * 4), None, tsel)
+    log(f"[gpu] decode_ties {rep}")
+    assert rep.ok(), str(rep)
+
+
+def test_decode_bitaxon_full_size(dev):
+    # One new token (and a 16-token append) after a 16384-token cache, 32
+    # heads, d = 80, window 4096.
+    for nq in (1, 16):
+        run_and_check(decode_inputs(W.BITAXON_SWA, nq, 105), dev, label=f"decode_bitaxon nq={nq}")
+
+
+def test_decode_token_full_size(dev):
+    # Four new tokens after a 65536-token cache: window 128 plus the top 2048
+    # of the whole history, sink, GQA 16/4.
+    run_and_check(decode_inputs(W.SWA_TOKEN_TOPK, 4, 105), dev, label="decode_token_full")

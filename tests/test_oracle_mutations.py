@@ -33,7 +33,9 @@ MUTATIONS = [
     ("pool divides by B - 1", [("dst[e] = acc / (double)B;", "dst[e] = acc / (double)(B - 1);")]),
     ("decode attention ignores the offset", [("const int64_t i = r % Nq + off, bh = r / Nq,",
                                               "const int64_t i = r % Nq, bh = r / Nq,")]),
-    ("decode token select ignores the offset", [("i = r % Nq + off, b = r / Nq;", "i = r % Nq, b = r / Nq;")]),
+    ("decode token select ignores the offset", [
+        ("i = r % Nq + off, b = r / Nq;\n            for (int64_t j = 0; j < i; ++j) {",
+         "i = r % Nq, b = r / Nq;\n            for (int64_t j = 0; j < i; ++j) {")]),
 ]
 
 PIN_CALLS = [

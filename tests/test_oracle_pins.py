@@ -430,3 +430,10 @@ def test_score_helpers_are_dot_products():
         ref = ik[b].astype(np.float64) @ iq[b, i].astype(np.float64)
         np.testing.assert_allclose(ts[r, :i], ref[:i], atol=1e-12)
         assert np.all(np.isneginf(ts[r, i:]))
+    # decode form: 7 queries at positions 33..39 of a 40-token history
+    ts = oracle.token_scores(iq[:, 33:], ik, np.arange(14))
+    for r in range(14):
+        b, i = divmod(r, 7)
+        ref = ik[b].astype(np.float64) @ iq[b, 33 + i].astype(np.float64)
+        np.testing.assert_allclose(ts[r, :33 + i], ref[:33 + i], atol=1e-12)
+        assert np.all(np.isneginf(ts[r, 33 + i:]))
