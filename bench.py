@@ -5,7 +5,9 @@ N = 16384, window 4096, causal, bf16) -- the shape the metric's 40 %-of-peak
 target is stated on.  A step is one sparse_attn_fwd call over inputs already
 resident in HBM.  Also reported (same JSON line, "workloads"): the other
 synthetic workloads, each a full forward (pool, gate, compaction, far-block
-and near attention) timed the same way.
+and near attention) timed the same way, and two decode/append steps (new
+tokens after a resident KV cache) reported as step time and algorithmic HBM
+bytes per step against the 8 TB/s peak.
 
 value      = tokens/s of the headline workload (batch * seq_len / step time)
 roofline   = attended FLOPs of the dominant kernel per launch / its mean
@@ -136,6 +138,59 @@ def time_workload(wl, seed, dev, steps, warmup, want_sel=False):
     return inp, (t1 - t0) * 1e3 / steps, stage_ms, (bsel, tsel)
 
 
+# Decode/append steps: nq new tokens per sequence after a cache of
+# wl.seq_len tokens (the queries are the cache's last nq positions).
+DECODE = [(W.BITAXON_SWA.replace(name="bitaxon_swa_decode_kv16384", batch=4), 1),
+          (W.SWA_TOKEN_TOPK.replace(name="swa_tokentopk_decode_kv65536"), 4)]
+
+
+def time_decode(wl, nq, seed, dev, steps, warmup):
+    """Time one decode step; returns (ms, stage_ms, algorithmic HBM bytes)."""
+    import torch
+    import sliding_window_long_amd as sa
+    inp = W.make_inputs(wl, seed)
+    off = wl.seq_len - nq
+    t = inp.tensors()
+    g = {k: (None if v is None else v.to(dev)) for k, v in t.items()}
+    q = g["q"][:, :, off:].contiguous()
+    iq = None if g["idx_q"] is None else g["idx_q"][:, off:].contiguous()
+    ws = sa.Workspace()
+    kw = dict(window=wl.window, idx_q=iq, idx_k=g["idx_k"], token_top_k=wl.token_top_k,
+              sink=g["sink"], workspace=ws)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    _, _, _, tsel = sa.forward(q, g["k"], g["v"], return_selection=True, **kw)
+    torch.cuda.synchronize()
+    # Keys each query reads: the window plus the kept tokens before it.
+    keys = 0
+    tsel = None if tsel is None else tsel.cpu().numpy()
+    for b in range(wl.batch):
+        for r in range(nq):
+            p = off + r
+            lo = max(0, p - wl.window + 1)
+            keys += p - lo + 1
+            if tsel is not None:
+                keys += int(((tsel[b, r] >= 0) & (tsel[b, r] < lo)).sum())
+    kv_bytes = keys * wl.n_kv_heads * wl.head_dim * 2 * 2
+    qo_bytes = wl.batch * wl.n_q_heads * nq * (wl.head_dim * 2 * 2 + 4)
+    idx_bytes = wl.batch * (wl.seq_len + nq) * wl.index_dim * 2 if wl.token_top_k else 0
+    for _ in range(warmup):
+        sa.forward(q, g["k"], g["v"], out=out, lse=lse, **kw)
+    torch.cuda.synchronize()
+    sa.sparse_attn_set_timing(True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        sa.forward(q, g["k"], g["v"], out=out, lse=lse, **kw)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    sa.sparse_attn_set_timing(False)
+    stages = {}
+    for name, ms in sa.sparse_attn_stage_times(1024):
+        stages.setdefault(name, []).append(ms)
+    return (t1 - t0) * 1e3 / steps, {k: float(np.mean(v)) for k, v in stages.items()}, \
+        kv_bytes + qo_bytes + idx_bytes
+
+
 def cpu_baseline(inp, budget_s=15.0):
     """The oracle as it stands, on sampled rows of the workload."""
     import oracle
@@ -238,6 +293,15 @@ def main():
                                "attended_tflops": ef / (ems * 1e-3) / 1e12,
                                "pct_of_bf16_peak": 100 * ef / (ems * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                                "stage_ms": est}
+        for dwl, nq in DECODE:
+            print(f"[bench] decode {dwl.name}", file=sys.stderr, flush=True)
+            dms, dst, dbytes = time_decode(dwl, nq, 7, dev, 50, 5)
+            extra[dwl.name] = {"new_tokens_per_seq": nq, "ms_per_step": dms,
+                               "tokens_per_s": dwl.batch * nq / (dms * 1e-3),
+                               "algorithmic_bytes": dbytes,
+                               "hbm_gbs": dbytes / (dms * 1e-3) / 1e9,
+                               "hbm_frac": dbytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                               "stage_ms": dst}
         result["workloads"] = extra
     if not args.no_cpu:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

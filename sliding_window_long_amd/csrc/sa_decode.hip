@@ -27,10 +27,29 @@
 namespace sa {
 
 constexpr int DEC_THREADS = 256;
-constexpr int DEC_CHUNK = 256;   // attended keys per dec_attn workgroup
+constexpr int SEL_THREADS = 1024;   // one workgroup per query scans its history
+constexpr int DEC_CHUNK = 256;      // attended keys per dec_attn workgroup
 
 __device__ __forceinline__ float dec_load(const void* p, size_t i, int f32) {
     return f32 ? ((const float*)p)[i] : bf16_to_f32(((const uint16_t*)p)[i]);
+}
+
+// Eight consecutive elements starting at element i (a multiple of 8) as fp32.
+template <bool F32>
+__device__ __forceinline__ void dec_load8(const void* p, size_t i, float (&x)[8]) {
+    if constexpr (F32) {
+        const float4 a = *(const float4*)((const float*)p + i), b = *(const float4*)((const float*)p + i + 4);
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    } else {
+        const uint4 u = *(const uint4*)((const uint16_t*)p + i);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            x[2 * t] = bf16_to_f32(w[t] & 0xffffu);
+            x[2 * t + 1] = bf16_to_f32(w[t] >> 16);
+        }
+    }
 }
 
 __device__ __forceinline__ uint32_t dec_ord32(float s) {
@@ -39,6 +58,7 @@ __device__ __forceinline__ uint32_t dec_ord32(float s) {
 }
 
 // Indexer scores [Bt, Nq, Nk]: one key per thread against every query.
+template <bool F32>
 __global__ __launch_bounds__(DEC_THREADS) void dec_scores_kernel(DecArgs a) {
     __shared__ float qs[kDecMaxQ * 64];
     const int bt = blockIdx.y, tid = threadIdx.x, j = blockIdx.x * DEC_THREADS + tid;
@@ -48,7 +68,12 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_scores_kernel(DecArgs a) {
     if (j >= a.Nk) return;
     float kj[64];
 #pragma unroll
-    for (int e = 0; e < 64; ++e) kj[e] = dec_load(a.ik, ((size_t)bt * a.Nk + j) * 64 + e, a.f32);
+    for (int e8 = 0; e8 < 8; ++e8) {
+        float x8[8];
+        dec_load8<F32>(a.ik, ((size_t)bt * a.Nk + j) * 64 + e8 * 8, x8);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) kj[e8 * 8 + t] = x8[t];
+    }
     for (int r = 0; r < a.Nq; ++r) {
         float s = 0.f;
 #pragma unroll
@@ -57,19 +82,19 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_scores_kernel(DecArgs a) {
     }
 }
 
-// Block-wide exclusive prefix sum of one value per thread (256 threads);
+// Block-wide exclusive prefix sum of one value per thread (SEL_THREADS);
 // *total receives the sum.
 __device__ __forceinline__ int dec_scan(int x, int* sh, int tid, int* total) {
     sh[tid] = x;
     __syncthreads();
-    for (int d = 1; d < DEC_THREADS; d <<= 1) {
+    for (int d = 1; d < SEL_THREADS; d <<= 1) {
         const int y = tid >= d ? sh[tid - d] : 0;
         __syncthreads();
         sh[tid] += y;
         __syncthreads();
     }
     const int incl = sh[tid];
-    *total = sh[DEC_THREADS - 1];
+    *total = sh[SEL_THREADS - 1];
     __syncthreads();
     return incl - x;
 }
@@ -105,9 +130,9 @@ __device__ __forceinline__ void dec_find(const uint32_t* hist, uint32_t k, int l
 
 // Kept tokens of one query: min(top_t, p) best of j < p, ascending, -1
 // padded; nfar = how many of them lie before the window start lo.
-__global__ __launch_bounds__(DEC_THREADS) void dec_select_kernel(DecArgs a) {
+__global__ __launch_bounds__(SEL_THREADS) void dec_select_kernel(DecArgs a) {
     __shared__ uint32_t hist[256];
-    __shared__ int sh[DEC_THREADS];
+    __shared__ int sh[SEL_THREADS];
     __shared__ uint32_t s_b[3];
     const int r = blockIdx.x, bt = blockIdx.y, tid = threadIdx.x;
     const int p = a.Nk - a.Nq + r;
@@ -125,9 +150,9 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_select_kernel(DecArgs a) {
         uint32_t rem = (uint32_t)k;
         for (int d = 5; d >= 0; --d) {
             const int shift = 8 * d;
-            hist[tid] = 0;
+            if (tid < 256) hist[tid] = 0;
             __syncthreads();
-            for (int j = tid; j < p; j += DEC_THREADS) {
+            for (int j = tid; j < p; j += SEL_THREADS) {
                 const uint64_t key = key_of(j);
                 if ((key & pmask) == prefix) atomicAdd(&hist[(uint32_t)(key >> shift) & 255u], 1u);
             }
@@ -143,7 +168,7 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_select_kernel(DecArgs a) {
         }
     }
     // Compaction in key order: thread t owns ids [t*ch, t*ch + ch).
-    const int ch = (p + DEC_THREADS - 1) / DEC_THREADS;
+    const int ch = (p + SEL_THREADS - 1) / SEL_THREADS;
     const int j0 = min(p, tid * ch), j1 = min(p, j0 + ch);
     auto kept = [&](int j) { return k >= p || (k > 0 && key_of(j) >= prefix); };
     int n = 0, nlo = 0;
@@ -157,7 +182,7 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_select_kernel(DecArgs a) {
     dec_scan(nlo, sh, tid, &total_lo);
     for (int j = j0; j < j1; ++j)
         if (kept(j) && pos < a.top_t) list[pos++] = j;
-    for (int x = total + tid; x < a.top_t; x += DEC_THREADS) list[x] = -1;
+    for (int x = total + tid; x < a.top_t; x += SEL_THREADS) list[x] = -1;
     if (tid == 0) a.nfar[(size_t)bt * a.Nq + r] = total_lo;
 }
 
@@ -174,11 +199,12 @@ __device__ __forceinline__ void dec_span(const DecArgs& a, int bt, int r, int& p
 // One chunk of 256 attended keys of query r for all G q heads of kv head g.
 // Partial per (row, chunk): o[D] = sum_j e^(x_j - m) v_j, then m, l
 // (x in base-2 units: logit * log2(e)).
-template <int D>
+template <int D, bool F32>
 __global__ __launch_bounds__(DEC_THREADS) void dec_attn_kernel(DecArgs a) {
-    constexpr int PARTS = DEC_THREADS / D;   // key groups of the P V step
+    constexpr int DG = D / 8;   // 8-dim groups of a row
     __shared__ float qs[16 * D];
     __shared__ float ps[16 * DEC_CHUNK];
+    __shared__ float acc[DEC_THREADS * 8];
     __shared__ int js[DEC_CHUNK];
     __shared__ float red[16][2];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -201,19 +227,28 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_attn_kernel(DecArgs a) {
     }
     __syncthreads();
 
+    // Logits: one key per thread, 16-byte loads of its row, every head of
+    // the group against it.
     const size_t kvb = ((size_t)bt * a.Hkv + g) * a.Nk;
     const float c2 = a.scale * kLog2e;
     if (tid < nk) {
-        float kr[D];
+        float sacc[16];
+#pragma unroll
+        for (int hl = 0; hl < 16; ++hl) sacc[hl] = 0.f;
         const size_t kro = (kvb + js[tid]) * D;
 #pragma unroll
-        for (int e = 0; e < D; ++e) kr[e] = dec_load(a.k, kro + e, a.f32);
-        for (int hl = 0; hl < G; ++hl) {
-            float s = 0.f;
+        for (int d8 = 0; d8 < DG; ++d8) {
+            float kx[8];
+            dec_load8<F32>(a.k, kro + d8 * 8, kx);
 #pragma unroll
-            for (int e = 0; e < D; ++e) s = fmaf(qs[hl * D + e], kr[e], s);
-            ps[hl * DEC_CHUNK + tid] = s * c2;
+            for (int hl = 0; hl < 16; ++hl)
+                if (hl < G)
+#pragma unroll
+                    for (int t = 0; t < 8; ++t) sacc[hl] = fmaf(qs[hl * D + d8 * 8 + t], kx[t], sacc[hl]);
         }
+#pragma unroll
+        for (int hl = 0; hl < 16; ++hl)
+            if (hl < G) ps[hl * DEC_CHUNK + tid] = sacc[hl] * c2;
     }
     __syncthreads();
     // Per head: max and sum over the chunk (wave w takes heads w, w+4, ...).
@@ -237,36 +272,32 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_attn_kernel(DecArgs a) {
         }
     }
     __syncthreads();
-    // P V: thread (part, e) sums its share of the chunk's keys for dim e.
-    const int part = tid / D, e = tid % D;
-    float o[16];
+    // P V: thread (part, head, 8-dim group) sums its share of the keys.
+    const int pairs = G * DG, parts = DEC_THREADS / pairs;
+    const int part = tid / pairs, pr = tid % pairs, hl = pr / DG, dg = pr % DG;
+    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (part < parts) {
+        for (int t = part; t < nk; t += parts) {
+            float vx[8];
+            dec_load8<F32>(a.v, (kvb + js[t]) * D + dg * 8, vx);
+            const float pw = ps[hl * DEC_CHUNK + t];
 #pragma unroll
-    for (int hl = 0; hl < 16; ++hl) o[hl] = 0.f;
-    if (part < PARTS) {
-        for (int t = part; t < nk; t += PARTS) {
-            const float vv = dec_load(a.v, (kvb + js[t]) * D + e, a.f32);
-#pragma unroll
-            for (int hl = 0; hl < 16; ++hl)
-                if (hl < G) o[hl] = fmaf(ps[hl * DEC_CHUNK + t], vv, o[hl]);
+            for (int u = 0; u < 8; ++u) o[u] = fmaf(pw, vx[u], o[u]);
         }
-    }
-    __syncthreads();   // ps is reused for the part sums below
-    float* acc = ps;   // [PARTS][16][D] <= 16 * DEC_CHUNK floats
-    if (part < PARTS)
 #pragma unroll
-        for (int hl = 0; hl < 16; ++hl)
-            if (hl < G) acc[(part * 16 + hl) * D + e] = o[hl];
+        for (int u = 0; u < 8; ++u) acc[(part * pairs + pr) * 8 + u] = o[u];
+    }
     __syncthreads();
     for (int x = tid; x < G * D; x += DEC_THREADS) {
-        const int hl = x / D, ee = x % D;
-        float s = 0.f;
-        for (int q_ = 0; q_ < PARTS; ++q_) s += acc[(q_ * 16 + hl) * D + ee];
-        const size_t row = ((size_t)bt * a.Hq + g * G + hl) * a.Nq + r;
+        const int h2 = x / D, ee = x % D, pr2 = h2 * DG + ee / 8;
+        float sum = 0.f;
+        for (int q_ = 0; q_ < parts; ++q_) sum += acc[(q_ * pairs + pr2) * 8 + (ee & 7)];
+        const size_t row = ((size_t)bt * a.Hq + g * G + h2) * a.Nq + r;
         float* dst = a.part + (row * a.cmax + c) * (D + 2);
-        dst[ee] = s;
+        dst[ee] = sum;
         if (ee == 0) {
-            dst[D] = red[hl][0];
-            dst[D + 1] = red[hl][1];
+            dst[D] = red[h2][0];
+            dst[D + 1] = red[h2][1];
         }
     }
 }
@@ -302,7 +333,10 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_combine_kernel(DecArgs a) {
 template <int D>
 static hipError_t dec_d(const DecArgs& a, hipStream_t s) {
     const dim3 ag((unsigned)a.cmax, (unsigned)(a.Hkv * a.Nq), (unsigned)a.Bt);
-    hipLaunchKernelGGL(dec_attn_kernel<D>, ag, dim3(DEC_THREADS), 0, s, a);
+    if (a.f32)
+        hipLaunchKernelGGL((dec_attn_kernel<D, true>), ag, dim3(DEC_THREADS), 0, s, a);
+    else
+        hipLaunchKernelGGL((dec_attn_kernel<D, false>), ag, dim3(DEC_THREADS), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t rows = (size_t)a.Bt * a.Hq * a.Nq;
@@ -312,12 +346,14 @@ static hipError_t dec_d(const DecArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_decode_select(const DecArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL(dec_scores_kernel, dim3((unsigned)((a.Nk + DEC_THREADS - 1) / DEC_THREADS),
-                                               (unsigned)a.Bt),
-                       dim3(DEC_THREADS), 0, s, a);
+    const dim3 sg((unsigned)((a.Nk + DEC_THREADS - 1) / DEC_THREADS), (unsigned)a.Bt);
+    if (a.f32)
+        hipLaunchKernelGGL(dec_scores_kernel<true>, sg, dim3(DEC_THREADS), 0, s, a);
+    else
+        hipLaunchKernelGGL(dec_scores_kernel<false>, sg, dim3(DEC_THREADS), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(dec_select_kernel, dim3((unsigned)a.Nq, (unsigned)a.Bt), dim3(DEC_THREADS), 0, s,
+    hipLaunchKernelGGL(dec_select_kernel, dim3((unsigned)a.Nq, (unsigned)a.Bt), dim3(SEL_THREADS), 0, s,
                        a);
     return hipGetLastError();
 }
