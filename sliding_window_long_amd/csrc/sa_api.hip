@@ -96,7 +96,8 @@ int make_plan(const sparse_attn_cfg* c, Plan* p) {
             P.o_dec_nfar = take((size_t)P.Bt * P.N * 4);
         }
         const long long span = (c->window < P.Nk ? c->window : P.Nk) + (long long)P.top_t;
-        P.dec_cmax = (int)((span + 255) / 256);
+        const int chunk = sa::dec_chunk(P.f32);
+        P.dec_cmax = (int)((span + chunk - 1) / chunk);
         P.o_dec_part = take((size_t)P.Bt * P.Hq * P.N * P.dec_cmax * (P.D + 2) * 4);
         P.total = off;
         return SA_OK;

@@ -16,10 +16,11 @@
 //   dec_select  : per query, exact radix select of the kept tokens on the
 //                 48-bit key ord(score) << 16 | (0xFFFF - j), then the kept
 //                 ids as an ascending list and the count below the window.
-//   dec_attn    : per (batch, kv head, query, chunk of 256 attended keys --
-//                 the window [lo, p] first, then the kept tokens before lo):
-//                 logits, chunk max and sum, and the chunk's P V, for every
-//                 q head of the kv group from one load of each key and value.
+//   dec_attn    : per (batch, kv head, query, chunk of 128 attended keys (64
+//                 for fp32) -- the window [lo, p] first, then the kept tokens
+//                 before lo): the chunk's K and V rows staged in LDS, logits,
+//                 chunk max and sum, and the chunk's P V, for every q head of
+//                 the kv group from one load of each key and value.
 //   dec_combine : merges the chunk partials and the sink column; out, lse.
 #include "sa_device.hpp"
 #include "sa_internal.hpp"
@@ -28,7 +29,6 @@ namespace sa {
 
 constexpr int DEC_THREADS = 256;
 constexpr int SEL_THREADS = 1024;   // one workgroup per query scans its history
-constexpr int DEC_CHUNK = 256;      // attended keys per dec_attn workgroup
 
 __device__ __forceinline__ float dec_load(const void* p, size_t i, int f32) {
     return f32 ? ((const float*)p)[i] : bf16_to_f32(((const uint16_t*)p)[i]);
@@ -129,8 +129,12 @@ __device__ __forceinline__ void dec_find(const uint32_t* hist, uint32_t k, int l
 }
 
 // Kept tokens of one query: min(top_t, p) best of j < p, ascending, -1
-// padded; nfar = how many of them lie before the window start lo.
+// padded; nfar = how many of them lie before the window start lo.  Thread t
+// owns ids [t*ch, t*ch + ch) (ch <= 64 since p <= 65535) and keeps their
+// ordered scores in registers for every pass.  The 48-bit key is handled as
+// its ordered-score half (32 bits) and its index half (16 bits).
 __global__ __launch_bounds__(SEL_THREADS) void dec_select_kernel(DecArgs a) {
+    constexpr int PT = 65536 / SEL_THREADS;
     __shared__ uint32_t hist[256];
     __shared__ int sh[SEL_THREADS];
     __shared__ uint32_t s_b[3];
@@ -140,48 +144,60 @@ __global__ __launch_bounds__(SEL_THREADS) void dec_select_kernel(DecArgs a) {
     const int lo = a.window > 0 ? max(0, p - a.window + 1) : p;
     const float* sc = a.scores + ((size_t)bt * a.Nq + r) * a.Nk;
     int32_t* list = a.list + ((size_t)bt * a.Nq + r) * a.top_t;
-    auto key_of = [&](int j) {
-        return ((uint64_t)dec_ord32(sc[j]) << 16) | (uint64_t)(0xffff - j);
-    };
+    const int ch = (p + SEL_THREADS - 1) / SEL_THREADS;
+    const int j0 = min(p, tid * ch), n_own = min(p, j0 + ch) - j0;
+    uint32_t ov[PT];   // ordered scores of the owned ids
+#pragma unroll
+    for (int u = 0; u < PT; ++u) ov[u] = u < n_own ? dec_ord32(sc[j0 + u]) : 0u;
 
-    // Threshold T: the k-th largest key (every key >= T is kept).
-    uint64_t prefix = 0, pmask = 0;
+    // Threshold: score half T_hi and index half T_lo of the k-th largest key.
+    uint32_t pre_hi = 0, msk_hi = 0, pre_lo = 0, msk_lo = 0;
     if (k > 0 && k < p) {
         uint32_t rem = (uint32_t)k;
         for (int d = 5; d >= 0; --d) {
-            const int shift = 8 * d;
             if (tid < 256) hist[tid] = 0;
             __syncthreads();
-            for (int j = tid; j < p; j += SEL_THREADS) {
-                const uint64_t key = key_of(j);
-                if ((key & pmask) == prefix) atomicAdd(&hist[(uint32_t)(key >> shift) & 255u], 1u);
+#pragma unroll
+            for (int u = 0; u < PT; ++u) {
+                const uint32_t ix = 0xffffu - (uint32_t)(j0 + u);
+                const bool match = u < n_own && (ov[u] & msk_hi) == pre_hi && (ix & msk_lo) == pre_lo;
+                const uint32_t digit = d >= 2 ? (ov[u] >> (8 * d - 16)) & 255u : (ix >> (8 * d)) & 255u;
+                if (match) atomicAdd(&hist[digit], 1u);
             }
             __syncthreads();
             if (tid < 64) dec_find(hist, rem, tid, s_b);
             __syncthreads();
             const uint32_t b = s_b[0], above = s_b[1], in_bin = s_b[2];
-            prefix |= (uint64_t)b << shift;
-            pmask |= (uint64_t)0xff << shift;
+            if (d >= 2) {
+                pre_hi |= b << (8 * d - 16);
+                msk_hi |= 255u << (8 * d - 16);
+            } else {
+                pre_lo |= b << (8 * d);
+                msk_lo |= 255u << (8 * d);
+            }
             rem -= above;
             __syncthreads();
             if (in_bin == rem) break;   // every key of this bin is kept
         }
     }
-    // Compaction in key order: thread t owns ids [t*ch, t*ch + ch).
-    const int ch = (p + SEL_THREADS - 1) / SEL_THREADS;
-    const int j0 = min(p, tid * ch), j1 = min(p, j0 + ch);
-    auto kept = [&](int j) { return k >= p || (k > 0 && key_of(j) >= prefix); };
+    // Kept <=> key >= (pre_hi, pre_lo) (unresolved low bits are zero).
     int n = 0, nlo = 0;
-    for (int j = j0; j < j1; ++j)
-        if (kept(j)) {
+    uint64_t keep = 0;   // bit u: owned id j0 + u is kept
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+        const uint32_t ix = 0xffffu - (uint32_t)(j0 + u);
+        const bool kp = u < n_own && (k >= p || ov[u] > pre_hi || (ov[u] == pre_hi && ix >= pre_lo));
+        if (kp) {
+            keep |= 1ull << u;
             ++n;
-            nlo += j < lo;
+            nlo += j0 + u < lo;
         }
+    }
     int total = 0, total_lo = 0;
     int pos = dec_scan(n, sh, tid, &total);
     dec_scan(nlo, sh, tid, &total_lo);
-    for (int j = j0; j < j1; ++j)
-        if (kept(j) && pos < a.top_t) list[pos++] = j;
+    for (int u = 0; u < n_own; ++u)
+        if (((keep >> u) & 1ull) && pos < a.top_t) list[pos++] = j0 + u;
     for (int x = total + tid; x < a.top_t; x += SEL_THREADS) list[x] = -1;
     if (tid == 0) a.nfar[(size_t)bt * a.Nq + r] = total_lo;
 }
@@ -196,16 +212,46 @@ __device__ __forceinline__ void dec_span(const DecArgs& a, int bt, int r, int& p
     nt = a.list ? a.nfar[(size_t)bt * a.Nq + r] : 0;
 }
 
-// One chunk of 256 attended keys of query r for all G q heads of kv head g.
-// Partial per (row, chunk): o[D] = sum_j e^(x_j - m) v_j, then m, l
-// (x in base-2 units: logit * log2(e)).
+// Eight consecutive elements of a row staged in LDS, from byte offset b.
+template <bool F32>
+__device__ __forceinline__ void lds_load8(const uint8_t* row, int b, float (&x)[8]) {
+    if constexpr (F32) {
+        const float4 u = *(const float4*)(row + b), v = *(const float4*)(row + b + 16);
+        x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
+        x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
+    } else {
+        const uint4 u = *(const uint4*)(row + b);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            x[2 * t] = bf16_to_f32(w[t] & 0xffffu);
+            x[2 * t + 1] = bf16_to_f32(w[t] >> 16);
+        }
+    }
+}
+
+// Attended-key tile c (CH keys: the window [lo, lo + nw) first, then the
+// listed tokens) of query r for all G q heads of kv head g.  The tile's K
+// and V rows are staged in LDS together (coalesced 16-byte loads, all issued
+// before the first store); then logits (one key per thread), per-head max
+// and sum, and P V.  Partial per (row, tile): o[D] = sum_j e^(x_j - m) v_j,
+// then m, l (x in base-2 units: logit * log2 e).
 template <int D, bool F32>
 __global__ __launch_bounds__(DEC_THREADS) void dec_attn_kernel(DecArgs a) {
-    constexpr int DG = D / 8;   // 8-dim groups of a row
+    constexpr int CH = dec_chunk(F32);
+    constexpr int ESZ = F32 ? 4 : 2;
+    constexpr int RB = D * ESZ;         // bytes of a K or V row
+    constexpr int ROWB = RB + 16;       // LDS row stride (keeps per-key reads off one bank)
+    constexpr int PIECES = RB / 16;     // 16-byte pieces of a row
+    constexpr int PER = CH * PIECES / DEC_THREADS;   // pieces per thread
+    constexpr int DG = D / 8;           // 8-dim groups of a row
+    static_assert(CH * PIECES % DEC_THREADS == 0, "tile pieces must split evenly");
+    static_assert(CH * ROWB >= DEC_THREADS * 8 * 4, "part sums must fit the K tile");
+    __shared__ __align__(16) uint8_t kt[CH * ROWB];   // K rows; at the end the P V part sums
+    __shared__ __align__(16) uint8_t vt[CH * ROWB];
     __shared__ float qs[16 * D];
-    __shared__ float ps[16 * DEC_CHUNK];
-    __shared__ float acc[DEC_THREADS * 8];
-    __shared__ int js[DEC_CHUNK];
+    __shared__ float ps[16 * CH];
+    __shared__ int js[CH];
     __shared__ float red[16][2];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c = blockIdx.x, bt = blockIdx.z;
@@ -213,55 +259,72 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_attn_kernel(DecArgs a) {
     const int G = a.Hq / a.Hkv;
     int p, lo, nw, nt;
     dec_span(a, bt, r, p, lo, nw, nt);
-    const int L = nw + nt, key0 = c * DEC_CHUNK;
+    const int L = nw + nt, key0 = c * CH;
     if (key0 >= L) return;   // whole block: nothing past the attended keys
-    const int nk = min(DEC_CHUNK, L - key0);
+    const int nk = min(CH, L - key0);
 
     for (int x = tid; x < G * D; x += DEC_THREADS) {
         const int hl = x / D, e = x % D;
         qs[x] = dec_load(a.q, (((size_t)bt * a.Hq + g * G + hl) * a.Nq + r) * D + e, a.f32);
     }
-    if (tid < nk) {
-        const int idx = key0 + tid;
+    if (tid < CH) {
+        const int idx = key0 + min(tid, nk - 1);   // rows past nk repeat the last key
         js[tid] = idx < nw ? lo + idx : a.list[((size_t)bt * a.Nq + r) * a.top_t + (idx - nw)];
     }
     __syncthreads();
 
-    // Logits: one key per thread, 16-byte loads of its row, every head of
-    // the group against it.
+    // Stage K and V rows: piece x = row * PIECES + col.
     const size_t kvb = ((size_t)bt * a.Hkv + g) * a.Nk;
+    const uint8_t* kg = (const uint8_t*)a.k;
+    const uint8_t* vg = (const uint8_t*)a.v;
+    uint4 kr[PER], vr[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int x = tid + i * DEC_THREADS, row = x / PIECES, col = x % PIECES;
+        const size_t off = (kvb + js[row]) * RB + col * 16;
+        kr[i] = *(const uint4*)(kg + off);
+        vr[i] = *(const uint4*)(vg + off);
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int x = tid + i * DEC_THREADS, row = x / PIECES, col = x % PIECES;
+        *(uint4*)(kt + row * ROWB + col * 16) = kr[i];
+        *(uint4*)(vt + row * ROWB + col * 16) = vr[i];
+    }
+    __syncthreads();
+
+    // Logits: one key per thread, every head of the group against it.
     const float c2 = a.scale * kLog2e;
     if (tid < nk) {
         float sacc[16];
 #pragma unroll
         for (int hl = 0; hl < 16; ++hl) sacc[hl] = 0.f;
-        const size_t kro = (kvb + js[tid]) * D;
 #pragma unroll
         for (int d8 = 0; d8 < DG; ++d8) {
             float kx[8];
-            dec_load8<F32>(a.k, kro + d8 * 8, kx);
+            lds_load8<F32>(kt + tid * ROWB, d8 * 8 * ESZ, kx);
 #pragma unroll
             for (int hl = 0; hl < 16; ++hl)
                 if (hl < G)
 #pragma unroll
-                    for (int t = 0; t < 8; ++t) sacc[hl] = fmaf(qs[hl * D + d8 * 8 + t], kx[t], sacc[hl]);
+                    for (int u = 0; u < 8; ++u) sacc[hl] = fmaf(qs[hl * D + d8 * 8 + u], kx[u], sacc[hl]);
         }
 #pragma unroll
         for (int hl = 0; hl < 16; ++hl)
-            if (hl < G) ps[hl * DEC_CHUNK + tid] = sacc[hl] * c2;
+            if (hl < G) ps[hl * CH + tid] = sacc[hl] * c2;
     }
     __syncthreads();
-    // Per head: max and sum over the chunk (wave w takes heads w, w+4, ...).
+    // Per head: max and sum over the tile (wave w takes heads w, w+4, ...).
     for (int hl = wave; hl < G; hl += 4) {
-        float* row = ps + hl * DEC_CHUNK;
+        float* prow = ps + hl * CH;
         float m = -INFINITY;
-        for (int t = lane; t < nk; t += 64) m = fmaxf(m, row[t]);
+        for (int u = lane; u < nk; u += 64) m = fmaxf(m, prow[u]);
 #pragma unroll
         for (int d = 32; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d));
         float l = 0.f;
-        for (int t = lane; t < nk; t += 64) {
-            const float e = fast_exp2(row[t] - m);
-            row[t] = e;
+        for (int u = lane; u < nk; u += 64) {
+            const float e = fast_exp2(prow[u] - m);
+            prow[u] = e;
             l += e;
         }
 #pragma unroll
@@ -277,16 +340,18 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_attn_kernel(DecArgs a) {
     const int part = tid / pairs, pr = tid % pairs, hl = pr / DG, dg = pr % DG;
     float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (part < parts) {
-        for (int t = part; t < nk; t += parts) {
+        for (int k = part; k < nk; k += parts) {
             float vx[8];
-            dec_load8<F32>(a.v, (kvb + js[t]) * D + dg * 8, vx);
-            const float pw = ps[hl * DEC_CHUNK + t];
+            lds_load8<F32>(vt + k * ROWB, dg * 8 * ESZ, vx);
+            const float pw = ps[hl * CH + k];
 #pragma unroll
             for (int u = 0; u < 8; ++u) o[u] = fmaf(pw, vx[u], o[u]);
         }
+    }
+    float* acc = (float*)kt;   // the K tile is no longer read
+    if (part < parts)
 #pragma unroll
         for (int u = 0; u < 8; ++u) acc[(part * pairs + pr) * 8 + u] = o[u];
-    }
     __syncthreads();
     for (int x = tid; x < G * D; x += DEC_THREADS) {
         const int h2 = x / D, ee = x % D, pr2 = h2 * DG + ee / 8;
@@ -302,32 +367,61 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_attn_kernel(DecArgs a) {
     }
 }
 
-// One wave per (batch, head, query): merge the chunks and the sink.
+// One workgroup per (batch, head, query): merge the tile partials and the
+// sink.  Thread (slice s, dim e) sums partials s, s + S, ...
 template <int D>
 __global__ __launch_bounds__(DEC_THREADS) void dec_combine_kernel(DecArgs a) {
-    const int lane = threadIdx.x & 63;
-    const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= (size_t)a.Bt * a.Hq * a.Nq) return;
+    constexpr int S = DEC_THREADS / D;   // partial slices
+    __shared__ float sm[DEC_THREADS], sl[DEC_THREADS];
+    __shared__ float so[S * D];
+    const int tid = threadIdx.x;
+    const size_t row = blockIdx.x;
     const int r = (int)(row % a.Nq), bt = (int)(row / ((size_t)a.Hq * a.Nq));
     const int h = (int)((row / a.Nq) % a.Hq);
     int p, lo, nw, nt;
     dec_span(a, bt, r, p, lo, nw, nt);
-    const int nc = (nw + nt + DEC_CHUNK - 1) / DEC_CHUNK;
+    const int chunk = dec_chunk(a.f32 != 0);
+    const int nc = (nw + nt + chunk - 1) / chunk;
     const float* src = a.part + row * a.cmax * (D + 2);
-    const float z = a.sink ? a.sink[h] * kLog2e : -INFINITY;   // base-2 units
-    float M = z;
-    for (int c = 0; c < nc; ++c) M = fmaxf(M, src[c * (D + 2) + D]);
-    float Ltot = a.sink ? fast_exp2(z - M) : 0.f;
-    for (int c = 0; c < nc; ++c) Ltot += src[c * (D + 2) + D + 1] * fast_exp2(src[c * (D + 2) + D] - M);
-    const float inv = Ltot > 0.f ? 1.f / Ltot : 0.f;
-    for (int e = lane; e < D; e += 64) {
-        float o = 0.f;
-        for (int c = 0; c < nc; ++c) o += src[c * (D + 2) + e] * fast_exp2(src[c * (D + 2) + D] - M);
-        o *= inv;
-        if (a.f32) ((float*)a.out)[row * D + e] = o;
-        else ((__bf16*)a.out)[row * D + e] = (__bf16)o;
+    // Largest exponent base over the partials and the sink (base-2 units).
+    float m = -INFINITY;
+    for (int cc = tid; cc < nc; cc += DEC_THREADS) m = fmaxf(m, src[cc * (D + 2) + D]);
+    sm[tid] = m;
+    __syncthreads();
+    for (int d = DEC_THREADS / 2; d >= 1; d >>= 1) {
+        if (tid < d) sm[tid] = fmaxf(sm[tid], sm[tid + d]);
+        __syncthreads();
     }
-    if (lane == 0) a.lse[row] = Ltot > 0.f ? (M + fast_log2(Ltot)) * kLn2 : -INFINITY;
+    const float z = a.sink ? a.sink[h] * kLog2e : -INFINITY;
+    const float M = fmaxf(sm[0], z);
+    float l = 0.f;
+    for (int cc = tid; cc < nc; cc += DEC_THREADS)
+        l += src[cc * (D + 2) + D + 1] * fast_exp2(src[cc * (D + 2) + D] - M);
+    sl[tid] = l;
+    __syncthreads();
+    for (int d = DEC_THREADS / 2; d >= 1; d >>= 1) {
+        if (tid < d) sl[tid] += sl[tid + d];
+        __syncthreads();
+    }
+    const float Ltot = sl[0] + (a.sink ? fast_exp2(z - M) : 0.f);
+    const int s = tid / D, e = tid % D;
+    if (s < S) {
+        float o = 0.f;
+#pragma unroll 4
+        for (int cc = s; cc < nc; cc += S)
+            o += src[cc * (D + 2) + e] * fast_exp2(src[cc * (D + 2) + D] - M);
+        so[s * D + e] = o;
+    }
+    __syncthreads();
+    const float inv = Ltot > 0.f ? 1.f / Ltot : 0.f;
+    if (tid < D) {
+        float o = 0.f;
+        for (int s2 = 0; s2 < S; ++s2) o += so[s2 * D + tid];
+        o *= inv;
+        if (a.f32) ((float*)a.out)[row * D + tid] = o;
+        else ((__bf16*)a.out)[row * D + tid] = (__bf16)o;
+    }
+    if (tid == 0) a.lse[row] = Ltot > 0.f ? (M + fast_log2(Ltot)) * kLn2 : -INFINITY;
 }
 
 template <int D>
@@ -340,8 +434,7 @@ static hipError_t dec_d(const DecArgs& a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t rows = (size_t)a.Bt * a.Hq * a.Nq;
-    hipLaunchKernelGGL(dec_combine_kernel<D>, dim3((unsigned)((rows + 3) / 4)), dim3(DEC_THREADS), 0,
-                       s, a);
+    hipLaunchKernelGGL(dec_combine_kernel<D>, dim3((unsigned)rows), dim3(DEC_THREADS), 0, s, a);
     return hipGetLastError();
 }
 

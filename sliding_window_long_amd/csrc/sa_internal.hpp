@@ -129,6 +129,9 @@ inline int tok_units(int N) { return tok_unit_base(N, tok_chunks(N, tok_blocks(N
 // Decode/append step: Nq (<= kDecMaxQ) queries at positions Nk - Nq + r of
 // a history of Nk keys.
 constexpr int kDecMaxQ = 64;
+// Attended keys per decode attention workgroup (its K and V rows are staged
+// in LDS together: 128 rows of 16-bit elements or 64 rows of fp32).
+__host__ __device__ constexpr int dec_chunk(bool f32) { return f32 ? 64 : 128; }
 struct DecArgs {
     const void* q;          // [Bt, Hq, Nq, D], bf16 or fp32
     const void* k;          // [Bt, Hkv, Nk, D]
@@ -142,8 +145,8 @@ struct DecArgs {
     float* scores;          // [Bt, Nq, Nk] indexer scores
     int32_t* list;          // [Bt, Nq, top_t] kept tokens, ascending, -1 padded; nullptr: no gate
     int32_t* nfar;          // [Bt, Nq] kept tokens before the window
-    float* part;            // [Bt*Hq*Nq, cmax, D + 2] chunk partials (o, m, l)
-    int cmax;               // chunks of 256 attended keys per query, upper bound
+    float* part;            // [Bt*Hq*Nq, cmax, D + 2] partials (o, m, l) of each key tile
+    int cmax;               // tiles of dec_chunk(f32) attended keys per query, upper bound
     void* out;              // [Bt, Hq, Nq, D], the input dtype
     float* lse;             // [Bt, Hq, Nq]
 };
