@@ -36,7 +36,8 @@ PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ["sliding_window_long_amd/csrc/sa_attn.hip",
                   "sliding_window_long_amd/csrc/sa_attn_common.hpp",
-                  "sliding_window_long_amd/csrc/sa_device.hpp"]
+                  "sliding_window_long_amd/csrc/sa_device.hpp",
+                  "sliding_window_long_amd/build.py"]   # its compile flags shape the code too
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_rows_bitaxon_swa_n16384_traffic.json")
 
 

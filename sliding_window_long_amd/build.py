@@ -26,8 +26,11 @@ FLAGS = [
     # No packed-fp32 VALU instructions (v_pk_{add,mul,fma}_f32).
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # The kernels never produce or consume NaN (masking uses -inf, and every
-    # comparison is written NaN-free), so min/max need no quieting.
-    "-fno-honor-nans", "-mno-amdgpu-ieee",
+    # comparison is written NaN-free), so min/max need no quieting.  The
+    # hardware IEEE mode stays at its default: switching it off differs from
+    # the device library's functions, which then are not inlined (every
+    # kernel would call out for its work-item and group ids).
+    "-fno-honor-nans",
     "-I", INCLUDE, "-I", CSRC,
 ]
 

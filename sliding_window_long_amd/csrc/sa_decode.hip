@@ -13,9 +13,11 @@
 // Decode reads the cache once and does little arithmetic per byte, so the
 // kernels are vector-ALU kernels in fp32:
 //   dec_scores  : indexer scores of every (query, key), fp32, to workspace.
-//   dec_select  : per query, exact radix select of the kept tokens on the
-//                 48-bit key ord(score) << 16 | (0xFFFF - j), then the kept
-//                 ids as an ascending list and the count below the window.
+//   dec_select  : per query, exact top-k on the 48-bit key
+//                 ord(score) << 16 | (0xFFFF - j): 4096 linear score bins
+//                 locate the threshold bin, whose few members are resolved
+//                 exactly; then the kept ids as an ascending list and the
+//                 count below the window.
 //   dec_attn    : per (batch, kv head, query, chunk of 128 attended keys (64
 //                 for fp32) -- the window [lo, p] first, then the kept tokens
 //                 before lo): the chunk's K and V rows staged in LDS, logits,
@@ -82,21 +84,43 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_scores_kernel(DecArgs a) {
     }
 }
 
-// Block-wide exclusive prefix sum of one value per thread (SEL_THREADS);
-// *total receives the sum.
-__device__ __forceinline__ int dec_scan(int x, int* sh, int tid, int* total) {
-    sh[tid] = x;
-    __syncthreads();
-    for (int d = 1; d < SEL_THREADS; d <<= 1) {
-        const int y = tid >= d ? sh[tid - d] : 0;
-        __syncthreads();
-        sh[tid] += y;
-        __syncthreads();
+// Block-wide exclusive prefix sum of one value per thread (SEL_THREADS
+// threads, 16 waves): wave scans by shuffles, then the wave totals through
+// LDS (wsum, 16 entries).  *total receives the sum.
+__device__ __forceinline__ int dec_scan(int x, int* wsum, int tid, int* total) {
+    const int lane = tid & 63, w = tid >> 6;
+    int incl = x;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(incl, d);
+        if (lane >= d) incl += y;
     }
-    const int incl = sh[tid];
-    *total = sh[SEL_THREADS - 1];
+    if (lane == 63) wsum[w] = incl;
     __syncthreads();
-    return incl - x;
+    int off = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < SEL_THREADS / 64; ++i) {
+        const int v = wsum[i];
+        off += i < w ? v : 0;
+        tot += v;
+    }
+    *total = tot;
+    __syncthreads();
+    return off + incl - x;
+}
+
+// Histogram increment from every active lane; lanes that all hit the same
+// bin (ties, narrow ranges) are merged into one atomic.
+__device__ __forceinline__ void dec_hist_add(uint32_t* h, uint32_t bin, bool on) {
+    const uint64_t act = __ballot(on);
+    if (act == 0) return;
+    const uint32_t first = (uint32_t)__builtin_amdgcn_readfirstlane(on ? bin : 0xffffffffu);
+    const uint64_t same = __ballot(on && bin == first);
+    if (same == act) {
+        if ((__lane_id() == (uint32_t)__builtin_ctzll(act))) atomicAdd(&h[first], (uint32_t)__popcll(act));
+    } else if (on) {
+        atomicAdd(&h[bin], 1u);
+    }
 }
 
 // Highest bin b of a 256-bin histogram whose count from the top reaches k
@@ -128,76 +152,211 @@ __device__ __forceinline__ void dec_find(const uint32_t* hist, uint32_t k, int l
     }
 }
 
+constexpr int kSelBins = 4096;          // linear score bins
+constexpr int kSelRank = 256;           // threshold-bin size resolved by rank counting
+constexpr uint16_t kSelKept = 0xffff;   // bin mark of a kept member of b*
+
+// Linear bin of score s over [mn, mn + kSelBins / inv]; inv == 0 puts every
+// score in bin 0.  Non-decreasing in s, so bins order the keys.
+__device__ __forceinline__ uint32_t dec_bin(float s, float mn, float inv) {
+    if (!(inv > 0.f)) return 0u;
+    const float t = (s - mn) * inv;
+    return t < (float)(kSelBins - 1) ? (uint32_t)t : (uint32_t)(kSelBins - 1);
+}
+
+// 48-bit key of token j with score s: ord(score) << 16 | (0xFFFF - j).
+__device__ __forceinline__ uint64_t dec_key(float s, int j) {
+    return (uint64_t)dec_ord32(s) << 16 | (uint64_t)(0xffffu - (uint32_t)j);
+}
+
 // Kept tokens of one query: min(top_t, p) best of j < p, ascending, -1
-// padded; nfar = how many of them lie before the window start lo.  Thread t
-// owns ids [t*ch, t*ch + ch) (ch <= 64 since p <= 65535) and keeps their
-// ordered scores in registers for every pass.  The 48-bit key is handled as
-// its ordered-score half (32 bits) and its index half (16 bits).
+// padded; nfar = how many of them lie before the window start lo.  Keys are
+// unique (the index breaks score ties toward the lower j).  Thread t handles
+// ids u * SEL_THREADS + t (coalesced; u < 64 since p <= 65535).
+//   1. the row's score range (scores held in registers for steps 1-2);
+//   2. 4096 linear bins over that range: each id's bin is kept in LDS
+//      (16 bits) and counted in an LDS histogram;
+//   3. the bin b* holding the k-th best key and the count above it; the
+//      rem = k - above best members of b* are marked kept (bin 0xFFFF):
+//      by rank counting over the members gathered in LDS when b* holds at
+//      most 256 keys, else by a byte-wise radix select over its members'
+//      48-bit keys (6 passes, scores reloaded);
+//   4. kept = bin above b* (marks included), written in ascending id order
+//      from wave ballots and one block scan.
 __global__ __launch_bounds__(SEL_THREADS) void dec_select_kernel(DecArgs a) {
     constexpr int PT = 65536 / SEL_THREADS;
-    __shared__ uint32_t hist[256];
+    constexpr int NW = SEL_THREADS / 64;
+    __shared__ uint16_t binv[PT * SEL_THREADS];
+    __shared__ uint32_t hist[kSelBins];
     __shared__ int sh[SEL_THREADS];
+    __shared__ int wsum[NW];
+    __shared__ float s_mm[2 * NW];
     __shared__ uint32_t s_b[3];
+    __shared__ uint32_t s_n;
+    __shared__ uint64_t cand[kSelRank];
     const int r = blockIdx.x, bt = blockIdx.y, tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
     const int p = a.Nk - a.Nq + r;
     const int k = min(a.top_t, p);
     const int lo = a.window > 0 ? max(0, p - a.window + 1) : p;
     const float* sc = a.scores + ((size_t)bt * a.Nq + r) * a.Nk;
     int32_t* list = a.list + ((size_t)bt * a.Nq + r) * a.top_t;
-    const int ch = (p + SEL_THREADS - 1) / SEL_THREADS;
-    const int j0 = min(p, tid * ch), n_own = min(p, j0 + ch) - j0;
-    uint32_t ov[PT];   // ordered scores of the owned ids
-#pragma unroll
-    for (int u = 0; u < PT; ++u) ov[u] = u < n_own ? dec_ord32(sc[j0 + u]) : 0u;
+    const bool sel = k > 0 && k < p;   // otherwise every id (k >= p) or none is kept
+    uint32_t bstar = 0;
 
-    // Threshold: score half T_hi and index half T_lo of the k-th largest key.
-    uint32_t pre_hi = 0, msk_hi = 0, pre_lo = 0, msk_lo = 0;
-    if (k > 0 && k < p) {
-        uint32_t rem = (uint32_t)k;
-        for (int d = 5; d >= 0; --d) {
-            if (tid < 256) hist[tid] = 0;
-            __syncthreads();
+    if (sel) {
+        // 1. range (slots past p re-read id p - 1, which leaves it unchanged)
+        float sv[PT];
 #pragma unroll
-            for (int u = 0; u < PT; ++u) {
-                const uint32_t ix = 0xffffu - (uint32_t)(j0 + u);
-                const bool match = u < n_own && (ov[u] & msk_hi) == pre_hi && (ix & msk_lo) == pre_lo;
-                const uint32_t digit = d >= 2 ? (ov[u] >> (8 * d - 16)) & 255u : (ix >> (8 * d)) & 255u;
-                if (match) atomicAdd(&hist[digit], 1u);
-            }
-            __syncthreads();
-            if (tid < 64) dec_find(hist, rem, tid, s_b);
-            __syncthreads();
-            const uint32_t b = s_b[0], above = s_b[1], in_bin = s_b[2];
-            if (d >= 2) {
-                pre_hi |= b << (8 * d - 16);
-                msk_hi |= 255u << (8 * d - 16);
-            } else {
-                pre_lo |= b << (8 * d);
-                msk_lo |= 255u << (8 * d);
-            }
-            rem -= above;
-            __syncthreads();
-            if (in_bin == rem) break;   // every key of this bin is kept
+        for (int u = 0; u < PT; ++u) sv[u] = sc[min(u * SEL_THREADS + tid, p - 1)];
+        float lo_s = sv[0], hi_s = sv[0];
+#pragma unroll
+        for (int u = 1; u < PT; ++u) {
+            lo_s = fminf(lo_s, sv[u]);
+            hi_s = fmaxf(hi_s, sv[u]);
         }
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) {
+            lo_s = fminf(lo_s, __shfl_xor(lo_s, d));
+            hi_s = fmaxf(hi_s, __shfl_xor(hi_s, d));
+        }
+        if (lane == 0) {
+            s_mm[w] = lo_s;
+            s_mm[NW + w] = hi_s;
+        }
+        for (int x = tid; x < kSelBins; x += SEL_THREADS) hist[x] = 0;
+        __syncthreads();
+        lo_s = s_mm[0];
+        hi_s = s_mm[NW];
+#pragma unroll
+        for (int i = 1; i < NW; ++i) {
+            lo_s = fminf(lo_s, s_mm[i]);
+            hi_s = fmaxf(hi_s, s_mm[NW + i]);
+        }
+        const float mn = lo_s;
+        float inv = (float)kSelBins / (hi_s - lo_s);
+        if (!(inv > 0.f && inv <= 3.0e38f)) inv = 0.f;
+
+        // 2. bins
+#pragma unroll
+        for (int u = 0; u < PT; ++u) {
+            const uint32_t b = dec_bin(sv[u], mn, inv);
+            const bool valid = tid < p - u * SEL_THREADS;
+            if (valid) binv[u * SEL_THREADS + tid] = (uint16_t)b;
+            dec_hist_add(hist, b, valid);
+        }
+        __syncthreads();
+
+        // 3. threshold bin: thread t holds bins 4095 - 4t - i, highest first
+        uint32_t cnt[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cnt[i] = hist[kSelBins - 1 - 4 * tid - i];
+        const int tot = (int)(cnt[0] + cnt[1] + cnt[2] + cnt[3]);
+        int total = 0;
+        const int excl = dec_scan(tot, wsum, tid, &total);
+        if (excl < k && excl + tot >= k) {
+            uint32_t cum = (uint32_t)excl;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (cum < (uint32_t)k && cum + cnt[i] >= (uint32_t)k) {
+                    s_b[0] = (uint32_t)(kSelBins - 1 - 4 * tid - i);
+                    s_b[1] = cum;
+                    s_b[2] = cnt[i];
+                }
+                cum += cnt[i];
+            }
+        }
+        if (tid == 0) s_n = 0;
+        __syncthreads();
+        bstar = s_b[0];
+        const uint32_t in_bin = s_b[2];
+        uint32_t rem = (uint32_t)k - s_b[1];   // 1 <= rem <= in_bin
+
+        if (in_bin <= (uint32_t)kSelRank) {
+            // gather b*; a member is kept when fewer than rem members beat it
+            for (int u = 0; u < PT; ++u) {
+                const int j = u * SEL_THREADS + tid;
+                if (j < p && binv[j] == bstar) cand[atomicAdd(&s_n, 1u)] = dec_key(sc[j], j);
+            }
+            __syncthreads();
+            if (tid < (int)in_bin) {
+                const uint64_t me = cand[tid];
+                uint32_t above = 0;
+                for (uint32_t x = 0; x < in_bin; ++x) above += cand[x] > me;
+                if (above < rem) binv[0xffff - (int)(me & 0xffffu)] = kSelKept;
+            }
+        } else {
+            // radix select of the rem-th best member key, then mark
+            uint32_t pre_hi = 0, msk_hi = 0, pre_lo = 0, msk_lo = 0;
+            for (int d = 5; d >= 0; --d) {
+                if (tid < 256) hist[tid] = 0;
+                __syncthreads();
+                for (int u = 0; u < PT; ++u) {
+                    const int j = u * SEL_THREADS + tid;
+                    const bool in = j < p && binv[j] == bstar;
+                    uint32_t ov = 0, ix = 0;
+                    if (in) {
+                        ov = dec_ord32(sc[j]);
+                        ix = 0xffffu - (uint32_t)j;
+                    }
+                    const bool match = in && (ov & msk_hi) == pre_hi && (ix & msk_lo) == pre_lo;
+                    const uint32_t digit = d >= 2 ? (ov >> (8 * d - 16)) & 255u : (ix >> (8 * d)) & 255u;
+                    dec_hist_add(hist, digit, match);
+                }
+                __syncthreads();
+                if (tid < 64) dec_find(hist, rem, tid, s_b);
+                __syncthreads();
+                const uint32_t b = s_b[0];
+                if (d >= 2) {
+                    pre_hi |= b << (8 * d - 16);
+                    msk_hi |= 255u << (8 * d - 16);
+                } else {
+                    pre_lo |= b << (8 * d);
+                    msk_lo |= 255u << (8 * d);
+                }
+                rem -= s_b[1];
+                __syncthreads();
+            }
+            const uint64_t thr = (uint64_t)pre_hi << 16 | pre_lo;
+            for (int u = 0; u < PT; ++u) {
+                const int j = u * SEL_THREADS + tid;
+                if (j < p && binv[j] == bstar && dec_key(sc[j], j) >= thr) binv[j] = kSelKept;
+            }
+        }
+        __syncthreads();
     }
-    // Kept <=> key >= (pre_hi, pre_lo) (unresolved low bits are zero).
-    int n = 0, nlo = 0;
-    uint64_t keep = 0;   // bit u: owned id j0 + u is kept
+
+    // 4. kept ids in ascending order; lane u of each wave keeps the wave's
+    // ballot for slot u
+    uint32_t mlo = 0, mhi = 0;
+    int nlo = 0;
 #pragma unroll
     for (int u = 0; u < PT; ++u) {
-        const uint32_t ix = 0xffffu - (uint32_t)(j0 + u);
-        const bool kp = u < n_own && (k >= p || ov[u] > pre_hi || (ov[u] == pre_hi && ix >= pre_lo));
-        if (kp) {
-            keep |= 1ull << u;
-            ++n;
-            nlo += j0 + u < lo;
-        }
+        const int j = u * SEL_THREADS + tid;
+        bool kp = j < p && k > 0;
+        if (sel) kp = kp && binv[min(j, p - 1)] > bstar;
+        const uint64_t m = __ballot(kp);
+        mlo = lane == u ? (uint32_t)m : mlo;
+        mhi = lane == u ? (uint32_t)(m >> 32) : mhi;
+        nlo += kp && j < lo;
     }
+    sh[lane * NW + w] = __popc(mlo) + __popc(mhi);   // entry (u, w) at u * NW + w
+    __syncthreads();
     int total = 0, total_lo = 0;
-    int pos = dec_scan(n, sh, tid, &total);
-    dec_scan(nlo, sh, tid, &total_lo);
-    for (int u = 0; u < n_own; ++u)
-        if (((keep >> u) & 1ull) && pos < a.top_t) list[pos++] = j0 + u;
+    const int ex = dec_scan(sh[tid], wsum, tid, &total);
+    sh[tid] = ex;
+    dec_scan(nlo, wsum, tid, &total_lo);   // its barriers also publish sh
+    const int base = sh[lane * NW + w];
+    const uint32_t below_lo = lane >= 32 ? 0xffffffffu : (1u << lane) - 1u;
+    const uint32_t below_hi = lane < 32 ? 0u : (lane == 63 ? 0x7fffffffu : (1u << (lane - 32)) - 1u);
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+        const uint32_t ml = (uint32_t)__builtin_amdgcn_readlane((int)mlo, u);
+        const uint32_t mh = (uint32_t)__builtin_amdgcn_readlane((int)mhi, u);
+        const bool kp = ((lane < 32 ? ml >> lane : mh >> (lane - 32)) & 1u) != 0;
+        const int pos = __builtin_amdgcn_readlane(base, u) + __popc(ml & below_lo) + __popc(mh & below_hi);
+        if (kp && pos < a.top_t) list[pos] = u * SEL_THREADS + tid;
+    }
     for (int x = total + tid; x < a.top_t; x += SEL_THREADS) list[x] = -1;
     if (tid == 0) a.nfar[(size_t)bt * a.Nq + r] = total_lo;
 }

@@ -244,6 +244,19 @@ def test_decode_token_ties(dev):
     assert rep.ok(), str(rep)
 
 
+def test_decode_token_crowded_bins(dev):
+    # Seven distinct indexer keys repeated over a 20000-token history, and
+    # one key of 32x the norm: the outlier stretches the score range and the
+    # repeats tie, so the threshold falls in a bin of ~2900 keys (the radix
+    # resolution of the decode select; ties go to the lower token id).
+    wl = W.Workload("dec_crowd", 1, 2, 1, 20000, 64, "bf16", window=8, token_top_k=1000, index_dim=64)
+    inp = decode_inputs(wl, 6, 17)
+    base = inp.idx_k[:, :7].copy()
+    inp.idx_k[:] = base[:, np.arange(wl.seq_len) % 7]
+    inp.idx_k[:, 123] = 32 * base[:, 0]   # exact in bf16
+    run_and_check(inp, dev, label="decode_token_crowded")
+
+
 def test_decode_bitaxon_full_size(dev):
     # One new token (and a 16-token append) after a 16384-token cache, 32
     # heads, d = 80, window 4096.
