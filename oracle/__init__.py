@@ -53,11 +53,13 @@ def _load(path=None):
     lib = ctypes.CDLL(path or _LIB)
     lib.orc_block_pool.argtypes = [_f32p, _i64, _i64, _i64, _i64, _f64p]
     lib.orc_block_pool.restype = None
-    lib.orc_block_scores.argtypes = [_f32p, _f64p, _i64, _i64, _i64, _i64, _i64,
-                                     _i64p, _i64, _f64p]
+    lib.orc_block_minmax.argtypes = [_f32p, _i64, _i64, _i64, _i64, _f64p]
+    lib.orc_block_minmax.restype = None
+    lib.orc_block_scores.argtypes = [_f32p, _f64p, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+                                     _i64, _i64p, _i64, _f64p]
     lib.orc_block_scores.restype = None
     lib.orc_block_select.argtypes = [_f32p, _f64p, _i64, _i64, _i64, _i64, _i64, _i64,
-                                     _i64p, _i64, _i32p, _f64p, _f64p]
+                                     _i64, _i64, _i64, _i64p, _i64, _i32p, _f64p, _f64p]
     lib.orc_block_select.restype = None
     lib.orc_token_scores.argtypes = [_f32p, _f32p, _i64, _i64, _i64p, _i64, _f64p]
     lib.orc_token_scores.restype = None
@@ -116,41 +118,70 @@ def _rows(rows, total):
     return rows
 
 
-def block_pool(k, B):
-    """Mean-pooled block keys, [Bt, Hkv, N/B, d] fp64."""
+_REPR = {"mean": 0, "minmax": 1}
+
+
+def _repr(gate_repr):
+    if gate_repr not in _REPR:
+        raise ValueError("gate_repr is 'mean' or 'minmax'")
+    return _REPR[gate_repr]
+
+
+def block_pool(k, B, gate_repr="mean"):
+    """Pooled block keys, fp64: mean keys [Bt, Hkv, N/B, d], or for
+    gate_repr="minmax" the per-dimension (min, max) [Bt, Hkv, N/B, 2, d]."""
     k = _f32(k)
     Bt, Hkv, N, d = k.shape
     if B <= 0 or N % B:
         raise ValueError("block size must divide N")
+    if _repr(gate_repr) == 1:
+        kmm = np.empty((Bt, Hkv, N // B, 2, d), dtype=np.float64)
+        _load().orc_block_minmax(k, Bt * Hkv, N, d, B, kmm)
+        return kmm
     kbar = np.empty((Bt, Hkv, N // B, d), dtype=np.float64)
     _load().orc_block_pool(k, Bt * Hkv, N, d, B, kbar)
     return kbar
 
 
-def block_scores(q, kbar, B, rows):
-    """Gate scores [len(rows), n]; -inf for blocks that are not candidates."""
+def _gate_args(kb, gate_repr, d):
+    rep = _repr(gate_repr)
+    want = (2, d) if rep else (d,)
+    if tuple(kb.shape[3:]) != want:
+        raise ValueError("pooled keys do not match gate_repr")
+    return rep
+
+
+def block_scores(q, kb, B, rows, gate_repr="mean", shared=False, first=False):
+    """Gate scores [len(rows), n]; -inf for blocks that are not candidates
+    (later blocks, the own block, and block 0 when it is forced)."""
     q = _f32(q)
     Bt, Hq, N, d = q.shape
-    Hkv, n = kbar.shape[1], kbar.shape[2]
+    Hkv, n = kb.shape[1], kb.shape[2]
+    rep = _gate_args(kb, gate_repr, d)
     rows = _rows(rows, Bt * Hq * N)
     out = np.empty((len(rows), n), dtype=np.float64)
-    _load().orc_block_scores(q, np.ascontiguousarray(kbar), Hq, Hkv, N, d, B,
-                             rows, len(rows), out)
+    _load().orc_block_scores(q, np.ascontiguousarray(kb), Hq, Hkv, N, d, B, rep, int(shared),
+                             int(first), rows, len(rows), out)
     return out
 
 
-def block_select(q, kbar, B, top_k, rows=None):
+def block_select(q, kb, B, top_k, rows=None, gate_repr="mean", shared=False, first=False):
     """Selected blocks per row [len(rows), top_k] (ascending, -1 padded) and the
-    scores of the last kept / first dropped candidate (NaN when absent)."""
+    scores of the last kept / first dropped candidate (NaN when absent).
+    shared: one selection per kv group (scores summed over its heads);
+    first: block 0 always kept, taking a slot (needs top_k >= 2)."""
     q = _f32(q)
     Bt, Hq, N, d = q.shape
-    Hkv = kbar.shape[1]
+    Hkv = kb.shape[1]
+    rep = _gate_args(kb, gate_repr, d)
+    if first and top_k < 2:
+        raise ValueError("keeping the first block needs top_k >= 2")
     rows = _rows(rows, Bt * Hq * N)
     sel = np.empty((len(rows), top_k), dtype=np.int32)
     s_last = np.empty(len(rows), dtype=np.float64)
     s_next = np.empty(len(rows), dtype=np.float64)
-    _load().orc_block_select(q, np.ascontiguousarray(kbar), Hq, Hkv, N, d, B, top_k,
-                             rows, len(rows), sel, s_last, s_next)
+    _load().orc_block_select(q, np.ascontiguousarray(kb), Hq, Hkv, N, d, B, top_k, rep,
+                             int(shared), int(first), rows, len(rows), sel, s_last, s_next)
     return sel, s_last, s_next
 
 
@@ -225,7 +256,8 @@ def attend(q, k, v, *, scale=None, window=0, block_size=0, sel=None, tsel=None,
 
 
 def forward(q, k, v, *, block_size=0, top_k=0, window=0, idx_q=None, idx_k=None,
-            token_top_k=0, sink=None, scale=None, rows=None):
+            token_top_k=0, sink=None, scale=None, rows=None, gate_repr="mean",
+            gate_shared=False, gate_first=False):
     """The whole path for the listed rows: pool, gate, token select, attend.
     Returns a dict with out, lse, count, sel, s_last, s_next, tsel, t_last,
     t_next (selection entries are None when that gate is off).
@@ -233,15 +265,18 @@ def forward(q, k, v, *, block_size=0, top_k=0, window=0, idx_q=None, idx_k=None,
     q [Bt, Hq, Nq, d] may be shorter than k, v [Bt, Hkv, Nk, d] (and idx_q
     than idx_k): the queries then continue the cached history, row rq at
     position rq + Nk - Nq.  Block gating is a prefill method here (the MoBA
-    summary switches to full attention for generation) and needs Nq = Nk."""
+    summary switches to full attention for generation) and needs Nq = Nk.
+    gate_repr / gate_shared / gate_first pick the block gate's variant
+    (see block_pool and block_select)."""
     Bt, Hq, N, d = np.shape(q)
     rows = _rows(rows, Bt * Hq * N)
     res = dict(sel=None, s_last=None, s_next=None, tsel=None, t_last=None, t_next=None)
     if top_k > 0 and np.shape(k)[2] != N:
         raise ValueError("block gating needs as many queries as keys")
     if top_k > 0:
-        kbar = block_pool(k, block_size)
-        res["sel"], res["s_last"], res["s_next"] = block_select(q, kbar, block_size, top_k, rows)
+        kb = block_pool(k, block_size, gate_repr)
+        res["sel"], res["s_last"], res["s_next"] = block_select(
+            q, kb, block_size, top_k, rows, gate_repr, gate_shared, gate_first)
     if token_top_k > 0:
         trow = (rows // (Hq * N)) * N + rows % N
         uniq, inv = np.unique(trow, return_inverse=True)

@@ -7,9 +7,19 @@ enumerating every admissible subset of past blocks, and the attended set is
 built pair by pair from the three clauses of the mask predicate.
 
 Sources: the MoBA summary page (discuss.pytorch.kr), sections "블록 분할과
-top-k 게이팅" and "인과성 보존"; the Bit-Axon "SWA + MoE" page, section
+top-k 게이팅" and "인과성 보존", and its remark casting attention sinks and
+Quest as MoBA with other gates; the Bit-Axon "SWA + MoE" page, section
 "슬라이딩 윈도우 마스크"; the Naive-N0.5-Flash page, section "SWA와 DSA를
 결합한 어텐션".
+
+Gate variants, stated here independently of the C oracle:
+* min/max blocks: a block is the box spanned by its keys' per-dimension
+  minima and maxima; its score is the largest <q, x> over the box's 2^d
+  corners (enumerated);
+* shared: the score of a block for query position i of kv group g is the
+  sum over the group's heads of that head's score; all of them keep the
+  same blocks;
+* first: block 0 is kept like the own block and takes one of the k slots.
 """
 from __future__ import annotations
 
@@ -36,8 +46,20 @@ def best_subset(scores: dict[int, Fraction], m: int) -> tuple[int, ...]:
     return best if best is not None else ()
 
 
+def _box_score(qv, lo, hi) -> Fraction:
+    """max <q, x> over the corners x of the box [lo, hi] (exact)."""
+    best = None
+    for corner in itertools.product((0, 1), repeat=len(qv)):
+        s = sum(((hi[e] if bit else lo[e]) * qv[e] for e, bit in enumerate(corner)),
+                Fraction(0))
+        if best is None or s > best:
+            best = s
+    return best
+
+
 def forward(q, k, v, *, block_size=0, top_k=0, window=0, idx_q=None, idx_k=None,
-            token_top_k=0, sink=None, scale=None):
+            token_top_k=0, sink=None, scale=None, gate_repr="mean", gate_shared=False,
+            gate_first=False):
     """Returns (out [Bt,Hq,Nq,d], lse [Bt,Hq,Nq], sel dict, tsel dict, count).
 
     q may hold fewer rows (Nq) than k, v (Nk): query row iq is then the token
@@ -64,22 +86,32 @@ def forward(q, k, v, *, block_size=0, top_k=0, window=0, idx_q=None, idx_k=None,
                       for j in range(i)}
                 tok[i] = set(best_subset(sc, min(token_top_k, i)))
                 tsels[(b, iq)] = tok[i]
+        def head_score(h, iq, c):
+            """Exact gate score of query iq of head h against block c."""
+            g = h // G
+            rows = range(c * block_size, (c + 1) * block_size)
+            qv = [_frac(q[b, h, iq, e]) for e in range(d)]
+            if gate_repr == "minmax":
+                lo = [min(_frac(k[b, g, j, e]) for j in rows) for e in range(d)]
+                hi = [max(_frac(k[b, g, j, e]) for j in rows) for e in range(d)]
+                return _box_score(qv, lo, hi)
+            mean = [sum((_frac(k[b, g, j, e]) for j in rows), Fraction(0)) / block_size
+                    for e in range(d)]
+            return sum((qv[e] * mean[e] for e in range(d)), Fraction(0))
+
         for h in range(Hq):
             g = h // G
-            pooled = {}
-            if top_k:
-                for c in range(N // block_size):
-                    pooled[c] = [sum((_frac(k[b, g, j, e])
-                                      for j in range(c * block_size, (c + 1) * block_size)),
-                                     Fraction(0)) / block_size for e in range(d)]
             for iq in range(Nq):
                 i = iq + off
                 chosen = set()
                 if top_k:
                     own = i // block_size
-                    sc = {c: sum((_frac(q[b, h, iq, e]) * pooled[c][e] for e in range(d)),
-                                 Fraction(0)) for c in range(own)}
-                    chosen = set(best_subset(sc, min(top_k - 1, own))) | {own}
+                    forced = {own} | ({0} if gate_first and own > 0 else set())
+                    heads = range(g * G, (g + 1) * G) if gate_shared else (h,)
+                    sc = {c: sum((head_score(hh, iq, c) for hh in heads), Fraction(0))
+                          for c in range(own) if c not in forced}
+                    m = min(top_k - len(forced), len(sc))
+                    chosen = set(best_subset(sc, m)) | forced
                     sels[(b, h, iq)] = chosen
                 keys = []
                 for j in range(N):

@@ -1,8 +1,9 @@
 /*
  * oracle.c -- plain, slow fp64 CPU definition of the causal sparse-attention
- * prefill: block gating by mean-pooled keys, unioned with a causal sliding
- * window and an optional per-query token selection, under GQA, with an
- * optional per-head sink logit.
+ * prefill: block gating by mean-pooled (or min/max-pooled) keys, per query
+ * head or per kv group, optionally always keeping the first block, unioned
+ * with a causal sliding window and an optional per-query token selection,
+ * under GQA, with an optional per-head sink logit.
  *
  * TEST INFRASTRUCTURE.  Only the tests, the smoke check and the benchmark's
  * CPU-baseline leg load this library.  It shares no code, header, table or
@@ -73,32 +74,97 @@ void orc_block_pool(const float* k, int64_t n_bh, int64_t N, int64_t d, int64_t 
     }
 }
 
-/* Unscaled gate score s_c = <q_i, kbar_c> [MoBA, gate score equation]. */
-static double gate_score(const float* qrow, const double* kb, int64_t d) {
+/*
+ * Min/max-pooled block keys [MoBA, the related-work remark: Quest is MoBA
+ * with smaller blocks and a block representation by min/max pooling]:
+ *   kmm[((b*Hkv + g)*n + c)*2 + 0][e] = min_{j in block c} k[b][g][j][e]
+ *   kmm[((b*Hkv + g)*n + c)*2 + 1][e] = max_{j in block c} k[b][g][j][e]
+ */
+void orc_block_minmax(const float* k, int64_t n_bh, int64_t N, int64_t d, int64_t B,
+                      double* kmm) {
+    const int64_t n = N / B;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < n_bh * n; ++t) {
+        const int64_t bh = t / n, c = t % n;
+        double* lo = kmm + t * 2 * d;
+        double* hi = lo + d;
+        for (int64_t e = 0; e < d; ++e) {
+            double mn = INFINITY, mx = -INFINITY;
+            for (int64_t j = c * B; j < (c + 1) * B; ++j) {
+                const double x = (double)k[(bh * N + j) * d + e];
+                if (x < mn) mn = x;
+                if (x > mx) mx = x;
+            }
+            lo[e] = mn;
+            hi[e] = mx;
+        }
+    }
+}
+
+/*
+ * Unscaled gate score of one query against one block representation.
+ *   rep 0, kb = mean key:         s = <q, kb>  [MoBA, gate score equation]
+ *   rep 1, kb = (min row, max row): s = sum_e max(q_e * min_e, q_e * max_e),
+ *     the largest <q, x> over all x in the block's per-dimension box
+ *     [min, max], which every key of the block lies in.  Reading: the pages
+ *     name the min/max representation but no score; this upper bound of
+ *     the block's best key score is the plainest score it supports.
+ */
+static double gate_score(const float* qrow, const double* kb, int64_t d, int rep) {
     double acc = 0.0;
-    for (int64_t e = 0; e < d; ++e) acc += (double)qrow[e] * kb[e];
+    if (rep == 0) {
+        for (int64_t e = 0; e < d; ++e) acc += (double)qrow[e] * kb[e];
+    } else {
+        for (int64_t e = 0; e < d; ++e) {
+            const double a = (double)qrow[e] * kb[e], b = (double)qrow[e] * kb[d + e];
+            acc += a > b ? a : b;
+        }
+    }
     return acc;
 }
 
 /*
- * Gate scores of listed rows against every block: scores[r][c] for c < b(i),
- * -INFINITY for the own block and later ones (they are never candidates;
- * the own block is forced separately) [MoBA, "인과성 보존": future blocks get
- * s = -inf and g = 0].
+ * Gate score of query i of head h (batch b) against block c.  Per query
+ * head, or -- shared != 0 -- one score per kv group, the sum of the scores
+ * of the group's G heads for the same position, so that every head of the
+ * group makes the same selection.  Reading: the pages give GQA layers with
+ * a block selection (BORA page, NSA layers: 8 heads over 4 kv heads, top
+ * 16 blocks) but no rule for sharing it; summing the heads' scores is the
+ * plainest one.
  */
-void orc_block_scores(const float* q, const double* kbar, int64_t Hq, int64_t Hkv,
-                      int64_t N, int64_t d, int64_t B, const int64_t* rows, int64_t nrows,
-                      double* scores) {
-    const int64_t n = N / B, G = Hq / Hkv;
+static double row_score(const float* q, const double* kb, int64_t Hq, int64_t Hkv, int64_t N,
+                        int64_t d, int64_t n, int rep, int shared, int64_t b, int64_t h,
+                        int64_t i, int64_t c) {
+    const int64_t G = Hq / Hkv, g = h / G;
+    const double* kbc = kb + ((b * Hkv + g) * n + c) * d * (rep ? 2 : 1);
+    if (!shared) return gate_score(q + ((b * Hq + h) * N + i) * d, kbc, d, rep);
+    double acc = 0.0;
+    for (int64_t hh = g * G; hh < (g + 1) * G; ++hh)
+        acc += gate_score(q + ((b * Hq + hh) * N + i) * d, kbc, d, rep);
+    return acc;
+}
+
+/*
+ * Gate scores of listed rows against every block: scores[r][c] for the
+ * candidates c (first <= c < b(i), first = 1 when block 0 is always kept
+ * and b(i) > 0, else 0), -INFINITY for the rest (forced blocks are never
+ * candidates, later blocks never seen) [MoBA, "인과성 보존": future blocks
+ * get s = -inf and g = 0].
+ */
+void orc_block_scores(const float* q, const double* kb, int64_t Hq, int64_t Hkv,
+                      int64_t N, int64_t d, int64_t B, int64_t rep, int64_t shared,
+                      int64_t first, const int64_t* rows, int64_t nrows, double* scores) {
+    const int64_t n = N / B;
 #pragma omp parallel for schedule(dynamic, 16)
     for (int64_t t = 0; t < nrows; ++t) {
         const int64_t r = rows[t];
-        const int64_t i = r % N, bh = r / N, b = bh / Hq, h = bh % Hq, g = h / G;
+        const int64_t i = r % N, bh = r / N, b = bh / Hq, h = bh % Hq;
         const int64_t own = i / B;
-        const float* qrow = q + r * d;
+        const int64_t c0 = (first && own > 0) ? 1 : 0;
         for (int64_t c = 0; c < n; ++c)
-            scores[t * n + c] = (c < own)
-                ? gate_score(qrow, kbar + ((b * Hkv + g) * n + c) * d, d) : -INFINITY;
+            scores[t * n + c] = (c >= c0 && c < own)
+                ? row_score(q, kb, Hq, Hkv, N, d, n, (int)rep, (int)shared, b, h, i, c)
+                : -INFINITY;
     }
 }
 
@@ -107,38 +173,49 @@ void orc_block_scores(const float* q, const double* kbar, int64_t Hq, int64_t Hk
  * the top k) and "인과성 보존" (future blocks excluded; the own block always
  * attended, like a shared expert)].  The own block takes one of the k slots
  * (the sparsity 1 - kB/N printed with the scaling results holds only then).
- * Candidates c < b are ranked by (-s_c, c); the first m = min(k-1, b) are
- * kept.  sel row = ascending block ids of {b} and the kept ones, then -1.
+ * first != 0: block 0 is always kept as well [MoBA, the remark that an
+ * attention sink is MoBA whose gate always picks the first block along
+ * with the recent one]; reading: like the own block it takes a slot, so
+ * top_k >= 2.  Candidates first..b-1 (see orc_block_scores) are ranked by
+ * (-s_c, c); the first m = min(k - forced, candidates) are kept.  sel row =
+ * ascending block ids of the forced and the kept ones, then -1.
  * s_last[t] = score of the m-th kept candidate (NaN if m == 0);
  * s_next[t] = score of the best candidate not kept (NaN if none).
  */
-void orc_block_select(const float* q, const double* kbar, int64_t Hq, int64_t Hkv,
-                      int64_t N, int64_t d, int64_t B, int64_t top_k,
-                      const int64_t* rows, int64_t nrows,
+void orc_block_select(const float* q, const double* kb, int64_t Hq, int64_t Hkv,
+                      int64_t N, int64_t d, int64_t B, int64_t top_k, int64_t rep,
+                      int64_t shared, int64_t first, const int64_t* rows, int64_t nrows,
                       int32_t* sel, double* s_last, double* s_next) {
-    const int64_t n = N / B, G = Hq / Hkv;
+    const int64_t n = N / B;
 #pragma omp parallel
     {
         cand_t* cand = (cand_t*)malloc(sizeof(cand_t) * (size_t)(n > 0 ? n : 1));
 #pragma omp for schedule(dynamic, 16)
         for (int64_t t = 0; t < nrows; ++t) {
             const int64_t r = rows[t];
-            const int64_t i = r % N, bh = r / N, b = bh / Hq, h = bh % Hq, g = h / G;
+            const int64_t i = r % N, bh = r / N, b = bh / Hq, h = bh % Hq;
             const int64_t own = i / B;
-            const float* qrow = q + r * d;
-            for (int64_t c = 0; c < own; ++c) {
-                cand[c].s = gate_score(qrow, kbar + ((b * Hkv + g) * n + c) * d, d);
-                cand[c].idx = c;
+            /* block 0 forced (top_k >= 2 is the caller's contract; the
+             * guard only keeps the row's writes in bounds) */
+            const int64_t c0 = (first && own > 0 && top_k >= 2) ? 1 : 0;
+            const int64_t nc = own - c0;
+            for (int64_t c = c0; c < own; ++c) {
+                cand[c - c0].s = row_score(q, kb, Hq, Hkv, N, d, n, (int)rep, (int)shared,
+                                           b, h, i, c);
+                cand[c - c0].idx = c;
             }
-            qsort(cand, (size_t)own, sizeof(cand_t), cand_cmp);
-            const int64_t m = (top_k - 1 < own) ? top_k - 1 : own;
+            qsort(cand, (size_t)nc, sizeof(cand_t), cand_cmp);
+            int64_t m = top_k - 1 - c0;
+            if (m > nc) m = nc;
+            if (m < 0) m = 0;
             int32_t* out = sel + t * top_k;
             for (int64_t x = 0; x < top_k; ++x) out[x] = -1;
             for (int64_t x = 0; x < m; ++x) out[x] = (int32_t)cand[x].idx;
             out[m] = (int32_t)own;
-            qsort(out, (size_t)(m + 1), sizeof(int32_t), int32_cmp);
+            if (c0) out[m + 1] = 0;
+            qsort(out, (size_t)(m + 1 + c0), sizeof(int32_t), int32_cmp);
             s_last[t] = m > 0 ? cand[m - 1].s : NAN;
-            s_next[t] = m < own ? cand[m].s : NAN;
+            s_next[t] = m < nc ? cand[m].s : NAN;
         }
         free(cand);
     }

@@ -78,9 +78,10 @@ def check(inp, dev_out, dev_lse, rows, dev_bsel=None, dev_tsel=None, *, kbar=Non
     Bt, Hq, N, d = inp.q.shape
     rows = np.asarray(rows, dtype=np.int64)
     rep = Report(rows=len(rows))
+    gv = dict(gate_repr=wl.gate_repr, gate_shared=wl.gate_shared, gate_first=wl.gate_first)
     res = oracle.forward(inp.q, inp.k, inp.v, block_size=wl.block_size, top_k=wl.top_k,
                          window=wl.window, idx_q=inp.idx_q, idx_k=inp.idx_k,
-                         token_top_k=wl.token_top_k, sink=inp.sink, rows=rows)
+                         token_top_k=wl.token_top_k, sink=inp.sink, rows=rows, **gv)
     ref_out, ref_lse = res["out"].copy(), res["lse"].copy()
     redo = np.zeros(len(rows), dtype=bool)
     use_bsel = res["sel"]
@@ -96,13 +97,17 @@ def check(inp, dev_out, dev_lse, rows, dev_bsel=None, dev_tsel=None, *, kbar=Non
         nd = np.flatnonzero(~dec & ~same)
         rep.non_decisive += int((~dec).sum())
         if len(nd):
-            kb = kbar if kbar is not None else oracle.block_pool(inp.k, wl.block_size)
-            sc = oracle.block_scores(inp.q, kb, wl.block_size, rows[nd])
+            kb = kbar if kbar is not None else oracle.block_pool(inp.k, wl.block_size,
+                                                                 wl.gate_repr)
+            sc = oracle.block_scores(inp.q, kb, wl.block_size, rows[nd], wl.gate_repr,
+                                     wl.gate_shared, wl.gate_first)
             for t, r in enumerate(nd):
                 own = (rows[r] % N) // wl.block_size
-                chosen = {int(c) for c in gsel[r] if c >= 0 and c != own}
-                if own not in set(gsel[r].tolist()) or len(chosen) != len(
-                        [c for c in res["sel"][r] if c >= 0]) - 1 or not _valid_tolerant(
+                forced = {own} | ({0} if wl.gate_first and own > 0 else set())
+                got = set(gsel[r].tolist())
+                chosen = {int(c) for c in got if c >= 0 and c not in forced}
+                if not forced <= got or len(chosen) != len(
+                        [c for c in res["sel"][r] if c >= 0]) - len(forced) or not _valid_tolerant(
                         chosen, sc[t], res["s_last"][r], res["s_next"][r]):
                     rep.invalid += 1
         redo |= ~same

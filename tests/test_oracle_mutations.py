@@ -11,14 +11,29 @@ import test_oracle_pins as pins
 MUTATIONS = [
     ("window admits w+1 keys", [("(i - window + 1 > 0 ? i - window + 1 : 0)", "(i - window > 0 ? i - window : 0)")]),
     ("tie goes to the higher index", [("if (a->idx < b->idx) return -1;", "if (a->idx < b->idx) return 1;")]),
-    ("own block not counted in k", [("const int64_t m = (top_k - 1 < own) ? top_k - 1 : own;",
-                                     "const int64_t m = (top_k < own) ? top_k : own;")]),
+    ("own block not counted in k", [("int64_t m = top_k - 1 - c0;", "int64_t m = top_k - c0;")]),
     ("own block competes instead of being forced", [
-        ("for (int64_t c = 0; c < own; ++c) {\n                cand[c].s",
-         "for (int64_t c = 0; c <= own; ++c) {\n                cand[c].s"),
-        ("qsort(cand, (size_t)own, sizeof(cand_t), cand_cmp);\n            const int64_t m = (top_k - 1 < own) ? top_k - 1 : own;",
-         "qsort(cand, (size_t)(own + 1), sizeof(cand_t), cand_cmp);\n            const int64_t m = (top_k < own + 1) ? top_k : own + 1;"),
-        ("out[m] = (int32_t)own;\n            qsort(out, (size_t)(m + 1)", "qsort(out, (size_t)m")]),
+        ("const int64_t nc = own - c0;", "const int64_t nc = own + 1 - c0;"),
+        ("for (int64_t c = c0; c < own; ++c) {\n                cand[c - c0].s",
+         "for (int64_t c = c0; c <= own; ++c) {\n                cand[c - c0].s"),
+        ("int64_t m = top_k - 1 - c0;", "int64_t m = top_k - c0;"),
+        ("out[m] = (int32_t)own;\n            if (c0) out[m + 1] = 0;\n            qsort(out, (size_t)(m + 1 + c0)",
+         "if (c0) out[m] = 0;\n            qsort(out, (size_t)(m + c0)")]),
+    ("min/max score keeps only the max corner", [("acc += a > b ? a : b;", "acc += b;")]),
+    ("min/max pool swaps min and max", [("lo[e] = mn;\n            hi[e] = mx;",
+                                         "lo[e] = mx;\n            hi[e] = mn;")]),
+    ("min/max score from the mean formula", [("if (rep == 0) {\n        for (int64_t e = 0; e < d; ++e) acc",
+                                              "if (1) {\n        for (int64_t e = 0; e < d; ++e) acc")]),
+    ("shared score from the own head only", [("for (int64_t hh = g * G; hh < (g + 1) * G; ++hh)",
+                                              "for (int64_t hh = h; hh < h + 1; ++hh)")]),
+    ("gate reads the wrong kv group", [("const int64_t G = Hq / Hkv, g = h / G;\n    const double* kbc",
+                                        "const int64_t G = Hq / Hkv, g = h % Hkv;\n    const double* kbc")]),
+    ("first block not counted in k", [("int64_t m = top_k - 1 - c0;", "int64_t m = top_k - 1;")]),
+    ("first block forced as block 1", [("if (c0) out[m + 1] = 0;", "if (c0) out[m + 1] = 1;")]),
+    ("first block also competes", [("const int64_t c0 = (first && own > 0) ? 1 : 0;\n        for (int64_t c = 0; c < n; ++c)",
+                                    "const int64_t c0 = 0;\n        for (int64_t c = 0; c < n; ++c)"),
+                                   ("const int64_t c0 = (first && own > 0 && top_k >= 2) ? 1 : 0;",
+                                    "const int64_t c0 = 0;\n            if (first && own > 0) sel[t * top_k] = 0;")]),
     ("sink logit scaled", [("const double z = sink ? (double)sink[h] : -INFINITY;",
                             "const double z = sink ? scale * (double)sink[h] : -INFINITY;")]),
     ("softmax scale dropped", [("x[j] = scale * acc;", "x[j] = acc;")]),
@@ -53,6 +68,18 @@ PIN_CALLS = [
     lambda: pins.test_p9_sink_closed_form(),
     lambda: pins.test_p10_token_selection_cases(),
     lambda: pins.test_pool_is_block_mean(),
+    lambda: pins.test_p17_minmax_block_of_one_is_dot_product(),
+    lambda: pins.test_p18_minmax_bounds_and_box_corners(),
+    lambda: pins.test_p20_shared_is_summed_query(),
+] + [
+    (lambda g=g: pins.test_p19_shared_with_one_head_per_group(g)) for g in ("mean", "minmax")
+] + [
+    (lambda g=g: pins.test_p21_first_block_top2_is_sink_pattern(g)) for g in ("mean", "minmax")
+] + [
+    (lambda g=g: pins.test_p22_first_block_is_gate_on_shifted_history(g)) for g in ("mean", "minmax")
+] + [
+    (lambda c=c, t=t: pins.test_p23_variants_brute_force(c, t))
+    for c in range(len(pins.VARIANT_CASES)) for t in (False, True)
 ] + [
     (lambda c=c, n=n: pins.test_p15_decode_is_last_prefill_rows(c, n))
     for c in range(len(pins.DECODE_CASES)) for n in (1, 5)

@@ -377,6 +377,172 @@ def test_p16_decode_brute_force(case, ties):
             assert {j for j in r["tsel"][t].tolist() if j >= 0} == btsel[(b, iqr)]
 
 
+# ---------------------------------------------------------------------------
+# Gate variants (MoBA summary page: the related-work remark casting attention
+# sinks, Quest and LongHeads as MoBA with other gates; BORA page: block
+# selection in GQA layers).
+# ---------------------------------------------------------------------------
+
+# P17: min/max blocks of one key are that key: the min/max score is then the
+# plain dot product q . k_c, and the selection is the mean gate's (B = 1).
+def test_p17_minmax_block_of_one_is_dot_product():
+    Bt, Hq, Hkv, N, d = 1, 4, 2, 24, 8
+    q, k = rnd((Bt, Hq, N, d), 300), rnd((Bt, Hkv, N, d), 301)
+    kmm = oracle.block_pool(k, 1, "minmax")
+    np.testing.assert_array_equal(kmm[:, :, :, 0], k.astype(np.float64))
+    np.testing.assert_array_equal(kmm[:, :, :, 1], k.astype(np.float64))
+    rows = np.arange(Bt * Hq * N)
+    sc = oracle.block_scores(q, kmm, 1, rows, "minmax")
+    kv = np.repeat(k.astype(np.float64), Hq // Hkv, axis=1)          # [Bt, Hq, N, d]
+    dots = np.einsum("bhid,bhjd->bhij", q.astype(np.float64), kv).reshape(-1, N)
+    i = rows % N
+    for t in range(len(rows)):
+        np.testing.assert_allclose(sc[t, :i[t]], dots[t, :i[t]], rtol=1e-13, atol=1e-13)
+        assert np.isneginf(sc[t, i[t]:]).all()
+    s_mm, _, _ = oracle.block_select(q, kmm, 1, 5, None, "minmax")
+    s_mean, _, _ = oracle.block_select(q, oracle.block_pool(k, 1), 1, 5)
+    np.testing.assert_array_equal(s_mm, s_mean)
+
+
+# P18: the min/max score bounds every key of the block from above, is the
+# maximum over the corners of the block's box (enumerated), is at least the
+# mean key's score, and equals the key score when the block's keys agree.
+def test_p18_minmax_bounds_and_box_corners():
+    Bt, Hq, Hkv, N, d, B = 1, 2, 1, 32, 5, 4
+    q, k = rnd((Bt, Hq, N, d), 302), rnd((Bt, Hkv, N, d), 303)
+    k[:, :, 8:12] = k[:, :, 8:9]                # block 2: four equal keys
+    kmm = oracle.block_pool(k, B, "minmax")
+    kbar = oracle.block_pool(k, B)
+    rows = np.arange(Bt * Hq * N)
+    sc = oracle.block_scores(q, kmm, B, rows, "minmax")
+    sm = oracle.block_scores(q, kbar, B, rows)
+    q64, k64 = q.astype(np.float64), k.astype(np.float64)
+    blocks = k64.reshape(Bt, Hkv, N // B, B, d)
+    lo, hi = kmm[:, :, :, 0][:, :, :, None], kmm[:, :, :, 1][:, :, :, None]
+    assert ((lo <= blocks) & (blocks <= hi)).all()             # the box holds every key
+    assert ((blocks == lo).any(axis=3) & (blocks == hi).any(axis=3)).all()   # and is tight
+    corners = np.array(list(__import__("itertools").product((0, 1), repeat=d)))
+    for t, r in enumerate(rows):
+        h, i = r // N, r % N
+        for c in range(i // B):
+            keys = k64[0, 0, c * B:(c + 1) * B]
+            qv = q64[0, h, i]
+            assert sc[t, c] >= (keys @ qv).max() - 1e-12
+            assert sc[t, c] >= sm[t, c] - 1e-12
+            box = np.where(corners == 1, kmm[0, 0, c, 1], kmm[0, 0, c, 0])  # [2^d, d]
+            np.testing.assert_allclose(sc[t, c], (box @ qv).max(), rtol=1e-13, atol=1e-13)
+            if c == 2:
+                np.testing.assert_allclose(sc[t, c], keys[0] @ qv, rtol=1e-13, atol=1e-13)
+
+
+# P19: with one query head per kv head, sharing the selection across the
+# group changes nothing.
+@pytest.mark.parametrize("gate_repr", ["mean", "minmax"])
+def test_p19_shared_with_one_head_per_group(gate_repr):
+    q, k = rnd((2, 3, 48, 8), 304), rnd((2, 3, 48, 8), 305)
+    kb = oracle.block_pool(k, 4, gate_repr)
+    a, _, _ = oracle.block_select(q, kb, 4, 4, None, gate_repr, False)
+    b, _, _ = oracle.block_select(q, kb, 4, 4, None, gate_repr, True)
+    np.testing.assert_array_equal(a, b)
+
+
+# P20: for mean blocks, the group's shared selection is the per-head
+# selection of the group's summed query (sum_h <q_h, kbar> = <sum_h q_h,
+# kbar>); inputs on a coarse grid so the fp32 sums are exact.  Every head of
+# a group keeps the same blocks.
+def test_p20_shared_is_summed_query():
+    Bt, Hq, Hkv, N, d, B = 2, 8, 2, 64, 8, 4
+    rng = np.random.default_rng(306)
+    q = (rng.integers(-8, 9, size=(Bt, Hq, N, d)) / 4).astype(np.float32)
+    k = rnd((Bt, Hkv, N, d), 307)
+    G = Hq // Hkv
+    qs = q.reshape(Bt, Hkv, G, N, d).sum(axis=2, dtype=np.float32)
+    q2 = np.repeat(qs, G, axis=1)                                     # [Bt, Hq, N, d]
+    kb = oracle.block_pool(k, B)
+    shared, _, _ = oracle.block_select(q, kb, B, 5, None, "mean", True)
+    per_head, _, _ = oracle.block_select(q2, kb, B, 5)
+    np.testing.assert_array_equal(shared, per_head)
+    sel = shared.reshape(Bt, Hkv, G, N, 5)
+    assert (sel == sel[:, :, :1]).all()
+
+
+# P21: always keeping the first block with top_k = 2 is the static
+# attention-sink pattern the MoBA page describes: every query attends to
+# block 0 and to its own block (causally), nothing else.
+@pytest.mark.parametrize("gate_repr", ["mean", "minmax"])
+def test_p21_first_block_top2_is_sink_pattern(gate_repr):
+    B, N = 4, 40
+    q, k, v = rnd((1, 2, N, 8), 308), rnd((1, 2, N, 8), 309), rnd((1, 2, N, 8), 310)
+    r, out, lse = run(q, k, v, block_size=B, top_k=2, gate_repr=gate_repr, gate_first=True)
+    pos = np.arange(N)
+    mask = (pos[None, :] <= pos[:, None]) & ((pos[None, :] < B) |
+                                              (pos[None, :] // B == pos[:, None] // B))
+    ro, rl = sdpa(q, k, v, mask=mask)
+    np.testing.assert_allclose(out, ro, atol=1e-12)
+    np.testing.assert_allclose(lse, rl, atol=1e-12)
+
+
+# P22: for queries past block 0, keeping block 0 leaves the ordinary gate,
+# with one slot less, on the history without block 0 (the other blocks'
+# pooled keys and scores do not depend on it; block ids shift by one).
+@pytest.mark.parametrize("gate_repr", ["mean", "minmax"])
+def test_p22_first_block_is_gate_on_shifted_history(gate_repr):
+    Bt, Hq, Hkv, N, d, B, K = 1, 4, 2, 64, 8, 4, 5
+    q, k = rnd((Bt, Hq, N, d), 311), rnd((Bt, Hkv, N, d), 312)
+    rows = np.array([(h * N + i) for h in range(Hq) for i in range(B, N)])
+    first, _, _ = oracle.block_select(q, oracle.block_pool(k, B, gate_repr), B, K, rows,
+                                      gate_repr, False, True)
+    qs, ks = np.ascontiguousarray(q[:, :, B:]), np.ascontiguousarray(k[:, :, B:])
+    rows_s = np.array([(h * (N - B) + i - B) for h in range(Hq) for i in range(B, N)])
+    plain, _, _ = oracle.block_select(qs, oracle.block_pool(ks, B, gate_repr), B, K - 1,
+                                      rows_s, gate_repr)
+    for a, b in zip(first, plain):
+        got = sorted(c for c in a.tolist() if c >= 0)
+        want = [0] + sorted(c + 1 for c in b.tolist() if c >= 0)
+        assert got == want
+
+
+# P23: exact brute force (rational scores, box corners, subset enumeration)
+# over the gate variants and their combinations, with and without ties.
+VARIANT_CASES = [
+    dict(block_size=2, top_k=3, gate_repr="minmax"),
+    dict(block_size=4, top_k=2, window=3, gate_shared=True),
+    dict(block_size=2, top_k=3, gate_first=True, sink=True),
+    dict(block_size=2, top_k=4, window=2, gate_repr="minmax", gate_shared=True, gate_first=True),
+    dict(block_size=1, top_k=3, gate_repr="minmax", gate_shared=True),
+]
+
+
+@pytest.mark.parametrize("case", range(len(VARIANT_CASES)))
+@pytest.mark.parametrize("ties", [False, True])
+def test_p23_variants_brute_force(case, ties):
+    kw = dict(VARIANT_CASES[case])
+    use_sink = kw.pop("sink", False)
+    Bt, Hq, Hkv, N, d = 1, 4, 2, 12, 3
+    rng = np.random.default_rng(400 + case + 50 * ties)
+    draw = (lambda s: rng.integers(-1, 2, size=s).astype(np.float32)) if ties else \
+           (lambda s: rng.standard_normal(s).astype(np.float32))
+    q, k, v = draw((Bt, Hq, N, d)), draw((Bt, Hkv, N, d)), draw((Bt, Hkv, N, d))
+    sink = rng.standard_normal(Hq).astype(np.float32) if use_sink else None
+    r, out, lse = run(q, k, v, sink=sink, **kw)
+    bo, bl, bsel, _, bcnt = brute.forward(q, k, v, sink=sink, **kw)
+    np.testing.assert_allclose(out, bo, atol=1e-12)
+    np.testing.assert_allclose(lse, bl, atol=1e-12)
+    np.testing.assert_array_equal(r["count"].reshape(Bt, Hq, N), bcnt)
+    for t, (h, i) in enumerate((h, i) for h in range(Hq) for i in range(N)):
+        assert {c for c in r["sel"][t].tolist() if c >= 0} == bsel[(0, h, i)], (h, i)
+
+
+def test_gate_variant_arguments_checked():
+    q, k = rnd((1, 2, 16, 4), 313), rnd((1, 2, 16, 4), 314)
+    with pytest.raises(ValueError):
+        oracle.block_pool(k, 4, "max")
+    with pytest.raises(ValueError):   # pooled keys of the other representation
+        oracle.block_select(q, oracle.block_pool(k, 4), 4, 2, None, "minmax")
+    with pytest.raises(ValueError):   # the forced first block needs a slot of its own
+        oracle.block_select(q, oracle.block_pool(k, 4), 4, 1, None, "mean", False, True)
+
+
 def test_decode_rejects_block_gating():
     q, k = rnd((1, 1, 4, 8), 70), rnd((1, 1, 16, 8), 71)
     with pytest.raises(ValueError):

@@ -46,6 +46,9 @@ class Workload:
     index_dim: int = 0         # indexer head dim
     sink: bool = False         # per-head sink logit
     block_offsets: bool = False
+    gate_repr: str = "mean"    # block summary for the gate: "mean" or "minmax"
+    gate_shared: bool = False  # one block selection per kv group
+    gate_first: bool = False   # block 0 always kept (takes one of the top_k slots)
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
