@@ -10,6 +10,20 @@
  *      s_c = <q_i, mean of the B keys of block c> (unscaled); the own block b
  *      is always kept and takes one of the top_k slots; the min(top_k-1, b)
  *      best earlier blocks are kept, a tie going to the lower block id.
+ *      Gate variants [same page, the remark that attention sinks, Quest
+ *      and LongHeads are MoBA with other gates; BORA page, NSA layers with
+ *      a block selection under GQA]:
+ *      - gate_repr = SA_GATE_MINMAX: block c is summarised by the
+ *        per-dimension min and max of its keys and scored by
+ *        sum_e max(q_e * min_e, q_e * max_e), the largest <q_i, x> over the
+ *        box those bounds span (Quest's block representation);
+ *      - gate_shared = 1: one selection per (batch, kv group, position),
+ *        scored by the sum of the group's heads' scores; every query head
+ *        of the group keeps the same blocks;
+ *      - gate_first = 1: block 0 is always kept as well (an attention sink
+ *        as a gate rule) and, like the own block, takes one of the top_k
+ *        slots (top_k >= 2); candidates are then blocks 1 .. b-1.
+ *      top_k = 1 keeps the own block only (LongHeads' top-1 gate).
  *   2. Token gate, when token_top_k > 0 [Naive-N0.5-Flash page, "SWA와 DSA를
  *      결합한 어텐션"]: each earlier token j < i is scored by
  *      <idx_q_i, idx_k_j> (one indexer head shared by all query heads); the
@@ -65,7 +79,7 @@
 extern "C" {
 #endif
 
-#define SPARSE_ATTN_ABI_VERSION 2
+#define SPARSE_ATTN_ABI_VERSION 3
 
 typedef enum {
     SA_BF16 = 0, /* bfloat16 inputs and out; fp32 accumulation.  Q K^T runs on
@@ -75,6 +89,11 @@ typedef enum {
     SA_F32 = 1   /* float32 inputs and out; each operand split into two
                     bf16 terms on the matrix cores (about 16 mantissa bits) */
 } sa_dtype;
+
+typedef enum {
+    SA_GATE_MEAN = 0,   /* block summary: mean of its keys */
+    SA_GATE_MINMAX = 1  /* block summary: per-dimension min and max of its keys */
+} sa_gate_repr;
 
 enum {
     SA_OK = 0,
@@ -114,6 +133,9 @@ typedef struct {
     int32_t kv_len;         /* keys of the history: 0 or seq_len for a prefill;
                                > seq_len for a decode/append step (seq_len <= 64,
                                top_k == 0; kv_len <= 65536 with a token gate) */
+    int32_t gate_repr;      /* sa_gate_repr; SA_GATE_MEAN unless top_k > 0 */
+    int32_t gate_shared;    /* 0 or 1: one block selection per kv group; 0 unless top_k > 0 */
+    int32_t gate_first;     /* 0 or 1: block 0 always kept (top_k >= 2); 0 unless top_k > 0 */
 } sparse_attn_cfg;
 
 /* Bytes of device workspace sparse_attn_fwd needs for this configuration
@@ -126,10 +148,13 @@ int sparse_attn_workspace_bytes(const sparse_attn_cfg* cfg, size_t* bytes);
 int sparse_attn_fwd(const void* q, const void* k, const void* v,
                     const sparse_attn_cfg* cfg, void* out, float* lse);
 
-/* The block mean-pool stage alone [MoBA summary page, implementation figure:
+/* The block pooling stage alone [MoBA summary page, implementation figure:
  * partition into blocks, mean pooling]: kbar[b, g, c, :] = mean of the
  * block_size keys of block c, fp32, [batch, n_kv_heads, seq_len/block_size,
- * head_dim].  Uses no workspace.  Same checks as sparse_attn_fwd. */
+ * head_dim].  With gate_repr = SA_GATE_MINMAX: kbar[b, g, c, 0, :] = the
+ * per-dimension min and kbar[b, g, c, 1, :] the max over those keys, fp32,
+ * [batch, n_kv_heads, seq_len/block_size, 2, head_dim].  Uses no workspace.
+ * Same checks as sparse_attn_fwd. */
 int sparse_attn_block_pool(const void* k, const sparse_attn_cfg* cfg, float* kbar);
 
 /* Static description of an error code. */

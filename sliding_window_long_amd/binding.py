@@ -19,6 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsparse_attn.so")
 
 SA_BF16, SA_F32 = 0, 1
+SA_GATE_MEAN, SA_GATE_MINMAX = 0, 1
 SA_OK = 0
 ERROR_CODES = {
     -1: "SA_E_INVALID_ARG", -2: "SA_E_SHAPE", -3: "SA_E_UNSUPPORTED_HEAD_DIM",
@@ -46,6 +47,8 @@ class SparseAttnCfg(ctypes.Structure):
         ("block_sel_out", ctypes.c_void_p), ("token_sel_out", ctypes.c_void_p),
         ("stream", ctypes.c_void_p),
         ("kv_len", ctypes.c_int32),
+        ("gate_repr", ctypes.c_int32), ("gate_shared", ctypes.c_int32),
+        ("gate_first", ctypes.c_int32),
     ]
 
 
@@ -102,12 +105,16 @@ class Params:
     index_dim: int = 0
     softmax_scale: float = 0.0
     kv_len: int = 0           # > seq_len: decode/append step over a cached history
+    gate_repr: int = SA_GATE_MEAN   # block summary: SA_GATE_MEAN or SA_GATE_MINMAX
+    gate_shared: int = 0      # 1: one block selection per kv group
+    gate_first: int = 0       # 1: block 0 always kept (takes a slot)
 
     def cfg(self) -> SparseAttnCfg:
         c = SparseAttnCfg()
         c.struct_size = ctypes.sizeof(SparseAttnCfg)
         for f in ("batch", "n_q_heads", "n_kv_heads", "seq_len", "head_dim", "dtype",
-                  "block_size", "top_k", "window", "token_top_k", "index_dim", "kv_len"):
+                  "block_size", "top_k", "window", "token_top_k", "index_dim", "kv_len",
+                  "gate_repr", "gate_shared", "gate_first"):
             setattr(c, f, int(getattr(self, f)))
         c.softmax_scale = float(self.softmax_scale)
         return c
@@ -159,16 +166,22 @@ def sparse_attn_stage_times(capacity: int = 16) -> list[tuple[str, float]]:
 # ---------------------------------------------------------------------------
 # torch-facing convenience wrapper
 # ---------------------------------------------------------------------------
+GATE_REPR = {"mean": SA_GATE_MEAN, "minmax": SA_GATE_MINMAX}
+
+
 def params_for(q, k, *, block_size=0, top_k=0, window=0, token_top_k=0, index_dim=0,
-               scale=None) -> Params:
+               scale=None, gate_repr="mean", gate_shared=False, gate_first=False) -> Params:
     import torch
     Bt, Hq, N, d = q.shape
     dt = {torch.bfloat16: SA_BF16, torch.float32: SA_F32}.get(q.dtype)
     if dt is None:
         raise TypeError(f"q dtype {q.dtype} not supported (bfloat16 or float32)")
+    if gate_repr not in GATE_REPR:
+        raise ValueError("gate_repr is 'mean' or 'minmax'")
     Nk = k.shape[2]
     return Params(Bt, Hq, k.shape[1], N, d, dt, block_size, top_k, window, token_top_k,
-                  index_dim, 0.0 if scale is None else float(scale), Nk if Nk != N else 0)
+                  index_dim, 0.0 if scale is None else float(scale), Nk if Nk != N else 0,
+                  GATE_REPR[gate_repr], int(bool(gate_shared)), int(bool(gate_first)))
 
 
 class Workspace:
@@ -191,12 +204,15 @@ _default_ws = Workspace()
 
 def forward(q, k, v, *, block_size=0, top_k=0, window=0, idx_q=None, idx_k=None,
             token_top_k=0, sink=None, scale=None, return_selection=False,
-            workspace: Workspace | None = None, out=None, lse=None):
+            workspace: Workspace | None = None, out=None, lse=None, gate_repr="mean",
+            gate_shared=False, gate_first=False):
     """Causal sparse-attention prefill on q's device and torch's current
     stream.  Returns (out, lse) or, with return_selection,
     (out, lse, block_sel, token_sel).  When k, v (and idx_k) hold more
     positions than q (and idx_q), the call is a decode/append step: the
-    queries are the newest positions of that history."""
+    queries are the newest positions of that history.  gate_repr ("mean" or
+    "minmax"), gate_shared and gate_first select the block gate's variant
+    (see the C header)."""
     import torch
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not t.is_cuda or not t.is_contiguous():
@@ -205,7 +221,8 @@ def forward(q, k, v, *, block_size=0, top_k=0, window=0, idx_q=None, idx_k=None,
             raise TypeError("q, k, v must share one dtype")
     index_dim = idx_q.shape[-1] if idx_q is not None else 0
     p = params_for(q, k, block_size=block_size, top_k=top_k, window=window,
-                   token_top_k=token_top_k, index_dim=index_dim, scale=scale)
+                   token_top_k=token_top_k, index_dim=index_dim, scale=scale,
+                   gate_repr=gate_repr, gate_shared=gate_shared, gate_first=gate_first)
     cfg = p.cfg()
     dev = q.device
     if out is None:
@@ -236,13 +253,15 @@ def forward(q, k, v, *, block_size=0, top_k=0, window=0, idx_q=None, idx_k=None,
     return out, lse
 
 
-def block_pool(k, block_size: int):
-    """Mean-pooled keys [Bt, Hkv, N/B, d] in fp32 (the pooling stage alone)."""
+def block_pool(k, block_size: int, gate_repr: str = "mean"):
+    """The pooling stage alone, fp32: mean keys [Bt, Hkv, N/B, d], or for
+    gate_repr="minmax" the per-dimension (min, max) [Bt, Hkv, N/B, 2, d]."""
     import torch
     Bt, Hkv, N, d = k.shape
-    p = params_for(k, k, block_size=block_size, top_k=1)
+    p = params_for(k, k, block_size=block_size, top_k=1, gate_repr=gate_repr)
     cfg = p.cfg()
     cfg.stream = torch.cuda.current_stream(k.device).cuda_stream
-    kbar = torch.empty((Bt, Hkv, N // max(block_size, 1), d), dtype=torch.float32, device=k.device)
+    shape = (Bt, Hkv, N // max(block_size, 1)) + ((2, d) if gate_repr == "minmax" else (d,))
+    kbar = torch.empty(shape, dtype=torch.float32, device=k.device)
     sparse_attn_block_pool(k, cfg, kbar)
     return kbar

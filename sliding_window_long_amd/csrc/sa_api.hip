@@ -2,7 +2,8 @@
 //
 // Stage order of one forward call (all on cfg->stream, no host sync):
 //   [fp32 only] split q, k, v into hi/lo bf16 planes
-//   [block gate] mean-pool -> gate (scores + top-k) -> compaction of far
+//   [block gate] pool (mean or min/max) -> [shared per kv group] group-summed
+//                queries -> gate (scores + top-k) -> compaction of far
 //                blocks -> far-block attention partials
 //   query-centric attention over window / own block / near kept blocks,
 //   merging the far partials and the sink -> out, lse
@@ -25,6 +26,8 @@ struct Plan {
     bool f32;
     bool gate;
     int B, n, top_k, span, kslots, idx_bits, lists;
+    bool gate_mm, gate_shared, gate_first;   // gate variants
+    int gate_planes;
     bool far;
     long long max_entries;
     int max_chunks;
@@ -37,7 +40,7 @@ struct Plan {
     size_t o_split, o_kb3, o_sel, o_count, o_cursor, o_listoff, o_nchunks, o_chunk_list,
         o_chunk_start, o_entries, o_part_o, o_part_lse, o_tok_split, o_tok_state, o_tok_mask,
         o_tok_qn, o_tok_win, o_tok_kpart, o_tok_scr, o_tok_nslow, o_dec_scores, o_dec_list,
-        o_dec_nfar, o_dec_part,
+        o_dec_nfar, o_dec_part, o_qsum,
         o_v16, total;
 };
 
@@ -56,6 +59,14 @@ int make_plan(const sparse_attn_cfg* c, Plan* p) {
     if (c->n_q_heads % c->n_kv_heads) return SA_E_SHAPE;
     if (c->n_q_heads / c->n_kv_heads > 16) return SA_E_UNSUPPORTED;
     if (c->window == 0 && c->top_k == 0) return SA_E_NO_SELF;
+    // Gate variants: only with block gating; the forced first block needs a
+    // slot of its own besides the own block.
+    if (c->gate_repr != SA_GATE_MEAN && c->gate_repr != SA_GATE_MINMAX) return SA_E_INVALID_ARG;
+    if ((c->gate_shared != 0 && c->gate_shared != 1) || (c->gate_first != 0 && c->gate_first != 1))
+        return SA_E_INVALID_ARG;
+    if (c->top_k == 0 && (c->gate_repr != SA_GATE_MEAN || c->gate_shared || c->gate_first))
+        return SA_E_INVALID_ARG;
+    if (c->gate_first && c->top_k < 2) return SA_E_INVALID_ARG;
     // Keys of the history: a decode/append step has more keys than queries.
     if (c->kv_len < 0) return SA_E_INVALID_ARG;
     const int Nk = c->kv_len > 0 ? c->kv_len : c->seq_len;
@@ -113,6 +124,10 @@ int make_plan(const sparse_attn_cfg* c, Plan* p) {
         if (P.top_k > 33 || P.n > 4096) return SA_E_UNSUPPORTED;
         P.idx_bits = 1;
         while ((1 << P.idx_bits) < P.n) ++P.idx_bits;
+        P.gate_mm = c->gate_repr == SA_GATE_MINMAX;
+        P.gate_shared = c->gate_shared != 0;
+        P.gate_first = c->gate_first != 0;
+        P.gate_planes = sa::gate_planes(P.gate_mm, P.f32);
         // Blocks within `span` below the own block overlap the window span of
         // some row of the block and are attended by the query-centric pass.
         long long span = 0;
@@ -144,7 +159,9 @@ int make_plan(const sparse_attn_cfg* c, Plan* p) {
     P.o_split = take(P.f32 ? 2 * (nq + 2 * nkv) * 2 : 0);
     P.o_v16 = take(P.f32 ? 0 : nkv * 2);   // fp16 copy of V for the P V products
     if (P.gate) {
-        P.o_kb3 = take((size_t)3 * P.lists * P.D * 2);
+        P.o_kb3 = take((size_t)P.gate_planes * P.lists * P.D * 2);
+        P.o_qsum = take(P.gate_shared ? (size_t)(P.gate_mm ? 4 : 2) * P.Bt * P.Hkv * P.N * P.D * 2
+                                      : 0);
         P.o_sel = take((size_t)rows * P.top_k * 4);
         if (P.far) {
             P.o_count = take((size_t)P.lists * 4);
@@ -269,7 +286,7 @@ int sparse_attn_block_pool(const void* k, const sparse_attn_cfg* cfg, float* kba
     if (!k || !kbar) return SA_E_INVALID_ARG;
     if (misaligned(k, 16) || misaligned(kbar, 16)) return SA_E_ALIGNMENT;
     hipStream_t s = (hipStream_t)cfg->stream;
-    sa::PoolArgs pa{k, P.N, P.B, P.n, kbar, nullptr, 0};
+    sa::PoolArgs pa{k, P.N, P.B, P.n, kbar, nullptr, 0, P.gate_mm ? 1 : 0};
     StageScope t("block_pool", s);
     return sa::launch_pool(pa, P.D, P.f32, P.lists, s) == hipSuccess ? SA_OK : SA_E_HIP;
 }
@@ -348,15 +365,32 @@ int sparse_attn_fwd(const void* q, const void* k, const void* v, const sparse_at
         uint16_t* kb3 = (uint16_t*)(ws + P.o_kb3);
         const size_t plane = (size_t)P.lists * P.D;
         {
-            sa::PoolArgs pa{k, P.N, P.B, P.n, nullptr, kb3, plane};
+            sa::PoolArgs pa{k, P.N, P.B, P.n, nullptr, kb3, plane, P.gate_mm ? 1 : 0};
             StageScope t("block_pool", s);
             if (!ok(sa::launch_pool(pa, P.D, P.f32, P.lists, s))) return SA_E_HIP;
         }
+        sa::GateArgs ga{{qp[0], qp[1], nullptr, nullptr}, kb3, plane, sel, P.Bt, P.Hq, P.Hkv,
+                        P.N, P.B, P.n, P.top_k, P.idx_bits, 1, P.gate_first ? 1 : 0};
+        int gate_split = split;
+        if (P.gate_shared) {
+            // One gate row per (batch, kv group, position) on the group's
+            // summed query (bf16 hi + lo; for min/max the summed positive
+            // and negative parts), its selection written to every head of
+            // the group.
+            const size_t plane_q = (size_t)P.Bt * P.Hkv * P.N * P.D;
+            uint16_t* qs = (uint16_t*)(ws + P.o_qsum);
+            sa::GroupSumArgs gs{q, {qs, qs + plane_q, qs + 2 * plane_q, qs + 3 * plane_q},
+                                P.Bt, P.Hq, P.Hkv, P.N, P.D, P.gate_mm ? 1 : 0};
+            StageScope t("group_sum", s);
+            if (!ok(sa::launch_group_sum(gs, P.f32, s))) return SA_E_HIP;
+            for (int x = 0; x < 4; ++x) ga.q[x] = gs.out[x];
+            ga.Hq = P.Hkv; ga.rep = P.G;
+            gate_split = P.gate_mm ? 4 : 2;
+        }
         {
-            sa::GateArgs ga{{qp[0], qp[1]}, kb3, plane, sel, P.Bt, P.Hq, P.Hkv, P.N, P.B, P.n,
-                            P.top_k, P.idx_bits};
             StageScope t("block_gate", s);
-            if (!ok(sa::launch_gate(ga, P.D, split, s))) return SA_E_HIP;
+            if (!ok(sa::launch_gate(ga, P.D, gate_split, P.gate_planes, P.gate_mm, s)))
+                return SA_E_HIP;
         }
         if (P.far) {
             part_o = (uint16_t*)(ws + P.o_part_o);

@@ -24,54 +24,97 @@
 namespace sa {
 
 // ---------------------------------------------------------------------------
-// Mean pool: one workgroup per (batch, kv head, block).
+// Pool: one workgroup per (batch, kv head, block).  MM = false: the mean of
+// the block's keys; MM = true: their per-dimension min and max [MoBA summary
+// page, the remark on Quest's min/max-pooled block representation].
 // ---------------------------------------------------------------------------
-template <int D, bool F32IN>
+__device__ __forceinline__ void split3(float x, uint16_t* dst, size_t plane, size_t o) {
+    const __bf16 hi = (__bf16)x;
+    const float r1 = x - (float)hi;
+    const __bf16 mid = (__bf16)r1;
+    const __bf16 lo = (__bf16)(r1 - (float)mid);
+    dst[o] = __builtin_bit_cast(uint16_t, hi);
+    dst[plane + o] = __builtin_bit_cast(uint16_t, mid);
+    dst[2 * plane + o] = __builtin_bit_cast(uint16_t, lo);
+}
+
+template <int D, bool F32IN, bool MM>
 __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
     constexpr int OCT = D / 8;            // 8-element column groups
     constexpr int NG = 256 / OCT;         // row groups
-    __shared__ float red[NG * D];
+    constexpr int NR = MM ? 2 : 1;        // reductions: sum, or min and max
+    __shared__ float red[NR][NG * D];
     const int tid = threadIdx.x;
     const int list = blockIdx.x;          // (b*Hkv + g)*n + c
     const int bg = list / a.n, cblk = list % a.n;
     const int co = tid % OCT, rg = tid / OCT;
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    float acc[NR][8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        acc[0][t] = MM ? INFINITY : 0.f;
+        acc[NR - 1][t] = MM ? -INFINITY : acc[0][t];
+    }
     if (rg < NG) {
         const size_t base = ((size_t)bg * a.N + (size_t)cblk * a.B) * D + co * 8;
         for (int j = rg; j < a.B; j += NG) {
+            float x[8];
             if constexpr (F32IN) {
                 const float4* p = (const float4*)((const float*)a.k + base + (size_t)j * D);
                 const float4 x0 = p[0], x1 = p[1];
-                acc[0] += x0.x; acc[1] += x0.y; acc[2] += x0.z; acc[3] += x0.w;
-                acc[4] += x1.x; acc[5] += x1.y; acc[6] += x1.z; acc[7] += x1.w;
+                x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
+                x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
             } else {
                 const uint4 u = *(const uint4*)((const uint16_t*)a.k + base + (size_t)j * D);
                 const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
                 for (int t = 0; t < 4; ++t) {
-                    acc[2 * t] += bf16_to_f32(w[t] & 0xffffu);
-                    acc[2 * t + 1] += bf16_to_f32(w[t] >> 16);
+                    x[2 * t] = bf16_to_f32(w[t] & 0xffffu);
+                    x[2 * t + 1] = bf16_to_f32(w[t] >> 16);
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                if constexpr (MM) {
+                    acc[0][t] = fminf(acc[0][t], x[t]);
+                    acc[NR - 1][t] = fmaxf(acc[NR - 1][t], x[t]);
+                } else {
+                    acc[0][t] += x[t];
                 }
             }
         }
 #pragma unroll
-        for (int t = 0; t < 8; ++t) red[rg * D + co * 8 + t] = acc[t];
+        for (int r = 0; r < NR; ++r)
+#pragma unroll
+            for (int t = 0; t < 8; ++t) red[r][rg * D + co * 8 + t] = acc[r][t];
     }
     __syncthreads();
     if (tid < D) {
-        float s = 0.f;
-        for (int r = 0; r < NG; ++r) s += red[r * D + tid];
-        const float mean = s / (float)a.B;
         const size_t o = (size_t)list * D + tid;
-        if (a.kbar) a.kbar[o] = mean;
-        if (a.kb3) {
-            const __bf16 hi = (__bf16)mean;
-            const float r1 = mean - (float)hi;
-            const __bf16 mid = (__bf16)r1;
-            const __bf16 lo = (__bf16)(r1 - (float)mid);
-            a.kb3[o] = __builtin_bit_cast(uint16_t, hi);
-            a.kb3[a.plane + o] = __builtin_bit_cast(uint16_t, mid);
-            a.kb3[2 * a.plane + o] = __builtin_bit_cast(uint16_t, lo);
+        if constexpr (MM) {
+            float mn = INFINITY, mx = -INFINITY;
+            for (int r = 0; r < NG; ++r) {
+                mn = fminf(mn, red[0][r * D + tid]);
+                mx = fmaxf(mx, red[NR - 1][r * D + tid]);
+            }
+            if (a.kbar) {
+                a.kbar[((size_t)list * 2) * D + tid] = mn;
+                a.kbar[((size_t)list * 2 + 1) * D + tid] = mx;
+            }
+            if (a.kb3) {
+                if constexpr (F32IN) {   // max terms in planes 0-2, min terms in 3-5
+                    split3(mx, a.kb3, a.plane, o);
+                    split3(mn, a.kb3 + 3 * a.plane, a.plane, o);
+                } else {                 // bf16 keys: both bounds are bf16 values
+                    a.kb3[o] = __builtin_bit_cast(uint16_t, (__bf16)mx);
+                    a.kb3[a.plane + o] = __builtin_bit_cast(uint16_t, (__bf16)mn);
+                }
+            }
+        } else {
+            float sum = 0.f;
+            for (int r = 0; r < NG; ++r) sum += red[0][r * D + tid];
+            const float mean = sum / (float)a.B;
+            if (a.kbar) a.kbar[o] = mean;
+            if (a.kb3) split3(mean, a.kb3, a.plane, o);
         }
     }
 }
@@ -113,24 +156,41 @@ __device__ __forceinline__ void sort_asc(int (&x)[M]) {
             }
 }
 
-// Candidate blocks are scored 32 at a time.  The three planes of those 32
+// Candidate blocks are scored 32 at a time.  The NP planes of those 32
 // pooled keys go through LDS (double buffered, rows D + 8 elements apart so
 // the 16-byte reads of 32 consecutive rows hit distinct banks); every wave
 // of the workgroup reads them from there as the A operand of
 // S^T = Kbar Q^T.
-template <int D>
+template <int D, int NP>
 struct GateTile {
     static constexpr int RS = D + 8;                 // LDS row stride
     static constexpr int PLANE = 32 * RS;            // one plane of 32 rows
-    static constexpr int CHUNKS = 3 * 32 * D / 8;    // 16-byte pieces per tile
+    static constexpr int CHUNKS = NP * 32 * D / 8;   // 16-byte pieces per tile
     static constexpr int CPT = (CHUNKS + 255) / 256;
 };
 
-template <int D, int M, int QSPLIT>
+// Positive and negative parts of eight bf16 values, selected by the signs of
+// `sgn` (the hi term of the same values): pos + neg = x, exactly.
+__device__ __forceinline__ void sign_split(const bf16x8& x, const bf16x8& sgn, bf16x8& pos,
+                                           bf16x8& neg) {
+    const uint4 u = __builtin_bit_cast(uint4, x), g = __builtin_bit_cast(uint4, sgn);
+    const uint32_t m0 = ((g.x >> 15) & 0x00010001u) * 0xffffu, m1 = ((g.y >> 15) & 0x00010001u) * 0xffffu;
+    const uint32_t m2 = ((g.z >> 15) & 0x00010001u) * 0xffffu, m3 = ((g.w >> 15) & 0x00010001u) * 0xffffu;
+    neg = as_bf16x8(make_uint4(u.x & m0, u.y & m1, u.z & m2, u.w & m3));
+    pos = as_bf16x8(make_uint4(u.x & ~m0, u.y & ~m1, u.z & ~m2, u.w & ~m3));
+}
+
+// MM = false: NP = 3 planes of the mean.  MM = true: the min/max summary,
+// NP / 2 planes of the max then of the min; the score
+// sum_e max(q_e min_e, q_e max_e) is <q+, max> + <q-, min> with q+ and q-
+// the positive and negative parts of q, two exact products on the matrix
+// cores.  QSPLIT: bf16 terms of q (1 or 2); 4 = the parts come split
+// already (q+ hi, lo, q- hi, lo: group sums of a shared min/max gate).
+template <int D, int M, int QSPLIT, int NP, bool MM>
 __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
-    using GT = GateTile<D>;
+    using GT = GateTile<D, NP>;
     constexpr int DK = D / 16;
-    __shared__ __align__(16) uint16_t lds[2][3 * GT::PLANE];
+    __shared__ __align__(16) uint16_t lds[2][NP * GT::PLANE];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int col = lane & 31, hh = lane >> 5;
     const int BH = a.Bt * a.Hq;
@@ -159,6 +219,9 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
     const int ncand_wave = q0 < a.N ? min(q0 + 31, a.N - 1) / a.B : 0;
     const int ntc = (ncand_wg + 31) / 32;
     const uint32_t mask = (1u << a.idx_bits) - 1u;
+    // Block 0 forced (first block always kept, rows past block 0): not a
+    // candidate, and one slot fewer for the candidates.
+    const int c0 = (a.first && row_blk > 0) ? 1 : 0;
     const uint16_t* kb = a.kb3 + (size_t)(b * a.Hkv + g) * a.n * D;
 
     // Staging of candidate tile mt: chunk x = (plane, row, 16-byte column).
@@ -197,12 +260,38 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
             f32x16 acc = {};
 #pragma unroll
             for (int ks = 0; ks < DK; ++ks) {
+                if constexpr (!MM) {
 #pragma unroll
-                for (int p = 0; p < 3; ++p) {
-                    const bf16x8 av = *(const bf16x8*)(src + p * GT::PLANE + ks * 16);
-                    acc = mfma32(av, qf[0][ks], acc);
-                    if constexpr (QSPLIT == 2) {
-                        if (p < 2) acc = mfma32(av, qf[1][ks], acc);
+                    for (int p = 0; p < 3; ++p) {
+                        const bf16x8 av = *(const bf16x8*)(src + p * GT::PLANE + ks * 16);
+                        acc = mfma32(av, qf[0][ks], acc);
+                        if constexpr (QSPLIT >= 2) {
+                            if (p < 2) acc = mfma32(av, qf[1][ks], acc);
+                        }
+                    }
+                } else {
+                    constexpr int NH = NP / 2;
+                    constexpr int QT = QSPLIT == 4 ? 2 : QSPLIT;   // terms per part
+                    bf16x8 qp[QT], qn[QT];
+                    if constexpr (QSPLIT == 4) {
+                        qp[0] = qf[0][ks]; qp[1] = qf[1][ks];
+                        qn[0] = qf[2][ks]; qn[1] = qf[3][ks];
+                    } else {
+#pragma unroll
+                        for (int x = 0; x < QT; ++x) sign_split(qf[x][ks], qf[0][ks], qp[x], qn[x]);
+                    }
+#pragma unroll
+                    for (int p = 0; p < NH; ++p) {
+                        const bf16x8 amax = *(const bf16x8*)(src + p * GT::PLANE + ks * 16);
+                        const bf16x8 amin = *(const bf16x8*)(src + (NH + p) * GT::PLANE + ks * 16);
+                        acc = mfma32(amax, qp[0], acc);
+                        acc = mfma32(amin, qn[0], acc);
+                        if constexpr (QT == 2) {
+                            if (p < 2) {
+                                acc = mfma32(amax, qp[1], acc);
+                                acc = mfma32(amin, qn[1], acc);
+                            }
+                        }
                     }
                 }
             }
@@ -212,7 +301,7 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int cblk = mt * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
-                const uint32_t key = cblk < row_blk ? order_key(acc[v], cblk, mask) : 0u;
+                const uint32_t key = cblk < row_blk && cblk >= c0 ? order_key(acc[v], cblk, mask) : 0u;
                 const bool in = key > L[M - 1];
                 if (__any(in)) insert_desc<M>(L, in ? key : 0u);   // inserting 0 changes nothing
             }
@@ -228,28 +317,37 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
     for (int t = 0; t < M; ++t) insert_desc<M>(L, P[t]);
 
     if (!row_ok || hh != 0) return;
-    const int m = min(a.top_k - 1, row_blk);
+    const int m = max(0, min(a.top_k - 1 - c0, row_blk - c0));
     int ids[M];
 #pragma unroll
     for (int t = 0; t < M; ++t) ids[t] = t < m ? (int)(mask - (L[t] & mask)) : 0x7fffffff;
     sort_asc<M>(ids);
-    int32_t* out = a.sel + prow * a.top_k;
-    for (int t = 0; t < a.top_k; ++t) {
-        int val = -1;
-        if (t < m) {
+    // Ascending: block 0 when forced, the m kept candidates, the own block.
+    for (int r = 0; r < a.rep; ++r) {
+        int32_t* out = a.sel + (((size_t)b * a.Hq + h) * a.rep + r) * a.N * a.top_k +
+                       (size_t)row * a.top_k;
+        for (int t = 0; t < a.top_k; ++t) {
+            int val = -1;
+            if (t < c0) {
+                val = 0;
+            } else if (t < c0 + m) {
 #pragma unroll
-            for (int u = 0; u < M; ++u)
-                if (u == t) val = ids[u];
-        } else if (t == m) {
-            val = row_blk;
+                for (int u = 0; u < M; ++u)
+                    if (u == t - c0) val = ids[u];
+            } else if (t == c0 + m) {
+                val = row_blk;
+            }
+            out[t] = val;
         }
-        out[t] = val;
     }
 }
 
 template <int D, bool F32IN>
 static hipError_t pool_d(const PoolArgs& a, int lists, hipStream_t s) {
-    hipLaunchKernelGGL((pool_kernel<D, F32IN>), dim3(lists), dim3(256), 0, s, a);
+    if (a.minmax)
+        hipLaunchKernelGGL((pool_kernel<D, F32IN, true>), dim3(lists), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((pool_kernel<D, F32IN, false>), dim3(lists), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
@@ -267,35 +365,128 @@ hipError_t launch_pool(const PoolArgs& a, int head_dim, bool f32_in, int lists, 
     return hipErrorInvalidValue;
 }
 
-template <int D, int M, int QS>
+template <int D, int M, int QS, int NP, bool MM>
 static hipError_t gate_dm(const GateArgs& a, hipStream_t s) {
     const int ntiles = (a.N + 127) / 128;
-    hipLaunchKernelGGL((gate_kernel<D, M, QS>), dim3(ntiles * a.Bt * a.Hq), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((gate_kernel<D, M, QS, NP, MM>), dim3(ntiles * a.Bt * a.Hq), dim3(256), 0, s,
+                       a);
     return hipGetLastError();
 }
 
-template <int D, int QS>
+template <int D, int QS, int NP, bool MM>
 static hipError_t gate_d(const GateArgs& a, hipStream_t s) {
     const int need = a.top_k - 1;
-    if (need <= 2) return gate_dm<D, 2, QS>(a, s);
-    if (need <= 4) return gate_dm<D, 4, QS>(a, s);
-    if (need <= 8) return gate_dm<D, 8, QS>(a, s);
-    if (need <= 16) return gate_dm<D, 16, QS>(a, s);
-    if (need <= 32) return gate_dm<D, 32, QS>(a, s);
+    if (need <= 2) return gate_dm<D, 2, QS, NP, MM>(a, s);
+    if (need <= 4) return gate_dm<D, 4, QS, NP, MM>(a, s);
+    if (need <= 8) return gate_dm<D, 8, QS, NP, MM>(a, s);
+    if (need <= 16) return gate_dm<D, 16, QS, NP, MM>(a, s);
+    if (need <= 32) return gate_dm<D, 32, QS, NP, MM>(a, s);
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_gate(const GateArgs& a, int head_dim, int qsplit, hipStream_t s) {
-    if (qsplit == 1) {
-        if (head_dim == 64) return gate_d<64, 1>(a, s);
-        if (head_dim == 80) return gate_d<80, 1>(a, s);
-        if (head_dim == 128) return gate_d<128, 1>(a, s);
-    } else {
-        if (head_dim == 64) return gate_d<64, 2>(a, s);
-        if (head_dim == 80) return gate_d<80, 2>(a, s);
-        if (head_dim == 128) return gate_d<128, 2>(a, s);
+template <int QS, int NP, bool MM>
+static hipError_t gate_v(const GateArgs& a, int head_dim, hipStream_t s) {
+    if (head_dim == 64) return gate_d<64, QS, NP, MM>(a, s);
+    if (head_dim == 80) return gate_d<80, QS, NP, MM>(a, s);
+    if (head_dim == 128) return gate_d<128, QS, NP, MM>(a, s);
+    return hipErrorInvalidValue;
+}
+
+// planes: the gate_planes() of the summary; qsplit: bf16 terms of q (1 or
+// 2), or 4 for the pre-split parts of a shared min/max gate.  fp32 min/max
+// planes come with fp32 (split) queries only.
+hipError_t launch_gate(const GateArgs& a, int head_dim, int qsplit, int planes, bool minmax,
+                       hipStream_t s) {
+    if (!minmax && planes == 3) {
+        if (qsplit == 1) return gate_v<1, 3, false>(a, head_dim, s);
+        if (qsplit == 2) return gate_v<2, 3, false>(a, head_dim, s);
+    }
+    if (minmax && planes == 2) {
+        if (qsplit == 1) return gate_v<1, 2, true>(a, head_dim, s);
+        if (qsplit == 2) return gate_v<2, 2, true>(a, head_dim, s);
+        if (qsplit == 4) return gate_v<4, 2, true>(a, head_dim, s);
+    }
+    if (minmax && planes == 6) {
+        if (qsplit == 2) return gate_v<2, 6, true>(a, head_dim, s);
+        if (qsplit == 4) return gate_v<4, 6, true>(a, head_dim, s);
     }
     return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// Group sums of the queries (selection shared per kv group): one thread per
+// 8 consecutive elements of one (batch, kv group, position) row.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void store_split8(const float (&s)[8], uint16_t* hi, uint16_t* lo,
+                                             size_t o) {
+    uint32_t hw[4], lw[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const __bf16 h0 = (__bf16)s[2 * t], h1 = (__bf16)s[2 * t + 1];
+        const __bf16 l0 = (__bf16)(s[2 * t] - (float)h0), l1 = (__bf16)(s[2 * t + 1] - (float)h1);
+        hw[t] = (uint32_t)__builtin_bit_cast(uint16_t, h0) |
+                ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+        lw[t] = (uint32_t)__builtin_bit_cast(uint16_t, l0) |
+                ((uint32_t)__builtin_bit_cast(uint16_t, l1) << 16);
+    }
+    *(uint4*)(hi + o) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    *(uint4*)(lo + o) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+}
+
+template <bool F32IN, bool MM>
+__global__ __launch_bounds__(256) void group_sum_kernel(GroupSumArgs a) {
+    const size_t oct = (size_t)a.D / 8;
+    const size_t total = (size_t)a.Bt * a.Hkv * a.N * oct;
+    const size_t x = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (x >= total) return;
+    const size_t row = x / oct, e0 = (x % oct) * 8;      // row = (b*Hkv + g)*N + i
+    const int i = (int)(row % a.N), bg = (int)(row / a.N);
+    const int b = bg / a.Hkv, g = bg % a.Hkv, G = a.Hq / a.Hkv;
+    float sp[8] = {0, 0, 0, 0, 0, 0, 0, 0}, sn[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int h = g * G; h < (g + 1) * G; ++h) {
+        const size_t src = (((size_t)b * a.Hq + h) * a.N + i) * a.D + e0;
+        float v[8];
+        if constexpr (F32IN) {
+            const float4 p0 = *(const float4*)((const float*)a.q + src);
+            const float4 p1 = *(const float4*)((const float*)a.q + src + 4);
+            v[0] = p0.x; v[1] = p0.y; v[2] = p0.z; v[3] = p0.w;
+            v[4] = p1.x; v[5] = p1.y; v[6] = p1.z; v[7] = p1.w;
+        } else {
+            const uint4 u = *(const uint4*)((const uint16_t*)a.q + src);
+            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                v[2 * t] = bf16_to_f32(w[t] & 0xffffu);
+                v[2 * t + 1] = bf16_to_f32(w[t] >> 16);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            if constexpr (MM) {
+                sp[t] += fmaxf(v[t], 0.f);
+                sn[t] += fminf(v[t], 0.f);
+            } else {
+                sp[t] += v[t];
+            }
+        }
+    }
+    const size_t o = row * a.D + e0;
+    store_split8(sp, a.out[0], a.out[1], o);
+    if constexpr (MM) store_split8(sn, a.out[2], a.out[3], o);
+}
+
+hipError_t launch_group_sum(const GroupSumArgs& a, bool f32_in, hipStream_t s) {
+    const size_t total = (size_t)a.Bt * a.Hkv * a.N * (a.D / 8);
+    if (total == 0) return hipSuccess;
+    const unsigned grid = (unsigned)((total + 255) / 256);
+    if (f32_in) {
+        if (a.minmax) hipLaunchKernelGGL((group_sum_kernel<true, true>), dim3(grid), dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((group_sum_kernel<true, false>), dim3(grid), dim3(256), 0, s, a);
+    } else {
+        if (a.minmax) hipLaunchKernelGGL((group_sum_kernel<false, true>), dim3(grid), dim3(256), 0, s, a);
+        else hipLaunchKernelGGL((group_sum_kernel<false, false>), dim3(grid), dim3(256), 0, s, a);
+    }
+    return hipGetLastError();
 }
 
 }  // namespace sa

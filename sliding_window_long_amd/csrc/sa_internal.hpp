@@ -56,18 +56,46 @@ struct BlocksArgs {
 struct PoolArgs {
     const void* k;          // bf16 or fp32 keys [Bt, Hkv, N, D]
     int N, B, n;
-    float* kbar;
-    uint16_t* kb3;          // 3 planes of `plane` elements each
+    float* kbar;            // fp32 summary: [lists, D] (mean) or [lists, 2, D] (min, max)
+    uint16_t* kb3;          // bf16 planes of `plane` elements each (gate_planes of them)
     size_t plane;
+    int minmax;             // 0: mean; 1: per-dimension min and max
 };
 
+// bf16 planes of the pooled keys the gate reads: the mean split into three
+// terms; min/max as the max terms then the min terms, one term each for
+// bf16 keys (exact) and three for fp32 keys.
+inline int gate_planes(bool minmax, bool f32) { return minmax ? (f32 ? 6 : 2) : 3; }
+
 // Block gate: scores against the pooled keys and top-(k-1) earlier blocks.
+// Rows are (batch, head, position) over Hq heads of q; each row's selection
+// is written to `rep` consecutive heads of sel (rep > 1 when one selection
+// per kv group is shared: q then holds the group sums and Hq = Hkv).
+// q planes: hi (and lo) of q; for a shared min/max gate the four planes
+// hi, lo of the summed positive parts and hi, lo of the summed negative
+// parts.
 struct GateArgs {
-    const uint16_t* q[2];   // bf16 planes of q
+    const uint16_t* q[4];   // bf16 planes of q
     const uint16_t* kb3;
     size_t plane;
-    int32_t* sel;           // [Bt, Hq, N, top_k]
+    int32_t* sel;           // [Bt, Hq * rep, N, top_k]
     int Bt, Hq, Hkv, N, B, n, top_k, idx_bits;
+    int rep;                // heads of sel per gate row
+    int first;              // 1: block 0 always kept (takes a slot)
+};
+
+// Group sums of the queries for a selection shared per kv group (fp32, head
+// order), each split into bf16 hi and lo planes [Bt, Hkv, N, D]:
+//   mean gate:    out[0], out[1] = sum_h q_h
+//   min/max gate: out[0], out[1] = sum_h max(q_h, 0);
+//                 out[2], out[3] = sum_h min(q_h, 0)
+// (the min/max score is <q+, max> + <q-, min>, linear in q+ and q-, so the
+// group's summed score needs the two parts summed apart).
+struct GroupSumArgs {
+    const void* q;          // bf16 or fp32 [Bt, Hq, N, D]
+    uint16_t* out[4];
+    int Bt, Hq, Hkv, N, D;
+    int minmax;
 };
 
 // Inversion of the block selection into per-(batch, kv head, block) lists of
@@ -158,7 +186,9 @@ hipError_t launch_token_select(const TokArgs& a, int split, hipStream_t s);
 hipError_t launch_token_list(const TokArgs& a, int32_t* out, hipStream_t s);
 
 hipError_t launch_pool(const PoolArgs& a, int head_dim, bool f32_in, int lists, hipStream_t s);
-hipError_t launch_gate(const GateArgs& a, int head_dim, int qsplit, hipStream_t s);
+hipError_t launch_gate(const GateArgs& a, int head_dim, int qsplit, int planes, bool minmax,
+                       hipStream_t s);
+hipError_t launch_group_sum(const GroupSumArgs& a, bool f32_in, hipStream_t s);
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t value, size_t n, hipStream_t s);
 

@@ -78,6 +78,13 @@ def code_of(params, **cfg_fields):
     (sa.Params(1, 4, 1, 1, 128, window=8, token_top_k=16, index_dim=64,
                kv_len=65536 + 1), -8),                               # 16-bit token ids
     (sa.Params(1, 4, 4, 1, 64, kv_len=256), -4),                      # decode, no window
+    (sa.Params(1, 4, 4, 256, 64, block_size=64, top_k=2, gate_repr=2), -1),   # unknown summary
+    (sa.Params(1, 4, 4, 256, 64, block_size=64, top_k=2, gate_shared=2), -1),
+    (sa.Params(1, 4, 4, 256, 64, block_size=64, top_k=2, gate_first=-1), -1),
+    (sa.Params(1, 4, 4, 256, 64, window=8, gate_repr=1), -1),         # variant without a gate
+    (sa.Params(1, 4, 4, 256, 64, window=8, gate_shared=1), -1),
+    (sa.Params(1, 4, 4, 256, 64, window=8, gate_first=1), -1),
+    (sa.Params(1, 4, 4, 256, 64, block_size=64, top_k=1, gate_first=1), -1),  # no slot for block 0
 ])
 def test_invalid_configs(lib, params, code):
     assert code_of(params) == code
@@ -93,8 +100,30 @@ def test_valid_configs(lib):
               sa.Params(1, 32, 32, 1, 80, window=4096, kv_len=16384),
               sa.Params(4, 16, 4, 64, 128, window=128, token_top_k=2048, index_dim=64,
                         kv_len=65536),
-              sa.Params(1, 8, 8, 16, 64, window=4, kv_len=16)):     # kv_len = seq_len: prefill
+              sa.Params(1, 8, 8, 16, 64, window=4, kv_len=16),      # kv_len = seq_len: prefill
+              sa.Params(1, 32, 8, 131072, 128, block_size=512, top_k=8, gate_repr=1),
+              sa.Params(2, 8, 4, 4096, 128, block_size=128, top_k=16, window=512,
+                        gate_shared=1, gate_first=1),
+              sa.Params(1, 1, 1, 512, 64, dtype=sa.SA_F32, block_size=64, top_k=2,
+                        gate_repr=1, gate_first=1)):
         assert code_of(p) == 0
+
+
+def test_gate_variant_workspace(lib):
+    # min/max summaries: 2 bf16 planes per block for bf16 keys (3 for the
+    # mean), 6 for fp32 keys; a shared selection adds the group-summed
+    # queries as two bf16 planes [Bt, Hkv, N, d] (four for min/max: the
+    # positive and the negative parts)
+    base = dict(block_size=128, top_k=4, window=128)
+    ws = lambda **kw: sa.sparse_attn_workspace_bytes(sa.Params(2, 8, 4, 4096, 128, **base, **kw).cfg())
+    lists = 2 * 4 * 32
+    assert ws() - ws(gate_repr=1) == lists * 128 * 2
+    assert ws(gate_shared=1) - ws() == 2 * 2 * 4 * 4096 * 128 * 2
+    assert ws(gate_shared=1, gate_repr=1) - ws(gate_repr=1) == 4 * 2 * 4 * 4096 * 128 * 2
+    assert ws(gate_first=1) == ws()
+    f32 = lambda **kw: sa.sparse_attn_workspace_bytes(
+        sa.Params(1, 2, 2, 512, 64, dtype=sa.SA_F32, block_size=64, top_k=3, **kw).cfg())
+    assert f32(gate_repr=1) - f32() == 3 * 2 * 8 * 64 * 2
 
 
 def test_decode_workspace(lib):

@@ -40,7 +40,8 @@ def run_device(inp, dev):
     out, lse, bsel, tsel = sa.forward(
         g["q"], g["k"], g["v"], block_size=wl.block_size, top_k=wl.top_k, window=wl.window,
         idx_q=g["idx_q"], idx_k=g["idx_k"], token_top_k=wl.token_top_k, sink=g["sink"],
-        return_selection=True)
+        return_selection=True, gate_repr=wl.gate_repr, gate_shared=wl.gate_shared,
+        gate_first=wl.gate_first)
     torch.cuda.synchronize()
     return (out.float().cpu().numpy(), lse.cpu().numpy(),
             None if bsel is None else bsel.cpu().numpy(),
@@ -151,6 +152,96 @@ def test_deterministic(dev):
     b = run_device(inp, dev)
     for x, y in zip(a, b):
         np.testing.assert_array_equal(x, y)
+
+
+# --- gate variants: min/max summary, selection shared per kv group, first
+# block always kept ------------------------------------------------------------
+VARIANTS = [
+    dict(gate_repr="minmax"),
+    dict(gate_shared=True),
+    dict(gate_first=True),
+    dict(gate_repr="minmax", gate_shared=True),
+    dict(gate_repr="minmax", gate_shared=True, gate_first=True),
+]
+VARIANT_IDS = ["minmax", "shared", "first", "minmax_shared", "all"]
+
+
+@pytest.mark.parametrize("var", VARIANTS, ids=VARIANT_IDS)
+@pytest.mark.parametrize("d", [64, 80, 128])
+def test_gate_variants_small(dev, var, d):
+    wl = W.Workload("gate_var", 2, 8, 2, 1024 + 64, d, "bf16", block_size=64, top_k=5,
+                    window=100, block_offsets=True, **var)
+    run_and_check(W.make_inputs(wl, 31 + d), dev, label=f"gate_var {var}")
+
+
+@pytest.mark.parametrize("var", VARIANTS, ids=VARIANT_IDS)
+def test_gate_variants_fp32(dev, var):
+    wl = W.Workload("gate_var_f32", 1, 4, 2, 384, 64, "f32", block_size=64, top_k=3, window=40,
+                    block_offsets=True, **var)
+    run_and_check(W.make_inputs(wl, 41), dev, label=f"gate_var_f32 {var}")
+
+
+@pytest.mark.parametrize("kw", [
+    dict(top_k=2, gate_first=True),                            # block 0 and own: sink pattern
+    dict(top_k=8, gate_first=True),                            # k = n: dense causal
+    dict(top_k=3, gate_first=True, window=100000),
+    dict(top_k=8, gate_repr="minmax"),
+    dict(top_k=2, gate_repr="minmax", gate_shared=True, window=1),
+])
+def test_gate_variant_edges(dev, kw):
+    wl = W.Workload("gate_var_edge", 1, 4, 2, 512, 128, "bf16", block_size=64,
+                    block_offsets=True, **kw)
+    run_and_check(W.make_inputs(wl, 51), dev, label=f"gate_var_edge {kw}")
+
+
+def test_first_block_top2_selects_block0_and_own(dev):
+    wl = W.Workload("first_top2", 1, 4, 2, 640, 64, "bf16", block_size=64, top_k=2,
+                    gate_first=True, block_offsets=True)
+    out, lse, bsel, _ = run_device(W.make_inputs(wl, 52), dev)
+    own = np.arange(wl.seq_len) // wl.block_size
+    want = np.stack([np.where(own > 0, 0, own), np.where(own > 0, own, -1)], axis=1)
+    for h in range(wl.n_q_heads):
+        np.testing.assert_array_equal(bsel[0, h], want)
+
+
+def test_shared_selection_same_for_the_group(dev):
+    for repr_ in ("mean", "minmax"):
+        wl = W.Workload("shared_grp", 2, 12, 3, 1024, 80, "bf16", block_size=64, top_k=6,
+                        window=64, gate_repr=repr_, gate_shared=True, block_offsets=True)
+        _, _, bsel, _ = run_device(W.make_inputs(wl, 53), dev)
+        g = bsel.reshape(2, 3, 4, 1024, 6)
+        assert (g == g[:, :, :1]).all(), repr_
+
+
+def test_block_pool_minmax_stage(dev):
+    import torch
+    import sliding_window_long_amd as sa
+    for wl, seed in ((W.BORA_HYBRID, 1), (W.TINY_MOBA, 2)):
+        inp = W.make_inputs(wl, seed)
+        kd = inp.tensors()["k"].to(dev)
+        got = sa.block_pool(kd, wl.block_size, "minmax").cpu().numpy()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(got, oracle.block_pool(inp.k, wl.block_size, "minmax"))
+
+
+def test_bora_hybrid_shared_first_all_rows(dev):
+    # The BORA shape (GQA 8/4) with one selection per kv group, block 0 kept.
+    wl = W.BORA_HYBRID.replace(name="bora_hybrid_shared_first", gate_shared=True,
+                               gate_first=True)
+    run_and_check(W.make_inputs(wl, 102), dev, label="bora_shared_first")
+
+
+def test_long_moba_minmax_reduced_sampled(dev):
+    wl = W.LONG_MOBA.replace(name="long_moba_minmax", seq_len=W.LONG_MOBA.seq_len // 8,
+                             gate_repr="minmax")
+    run_and_check(W.make_inputs(wl, 104), dev, W.sample_rows(wl, 4096, 2),
+                  label="long_moba_minmax_n/8")
+
+
+def test_long_moba_minmax_full_sampled(dev):
+    wl = W.LONG_MOBA.replace(name="long_moba_minmax", gate_repr="minmax")
+    run_and_check(W.make_inputs(wl, 104), dev, W.sample_rows(wl, 2048, 3),
+                  label="long_moba_minmax_full")
 
 
 # --- token top-k (Naive SWA + DSA shape) -------------------------------------
