@@ -5,7 +5,9 @@ N = 16384, window 4096, causal, bf16) -- the shape the metric's 40 %-of-peak
 target is stated on.  A step is one sparse_attn_fwd call over inputs already
 resident in HBM.  Also reported (same JSON line, "workloads"): the other
 synthetic workloads, each a full forward (pool, gate, compaction, far-block
-and near attention) timed the same way, and two decode/append steps (new
+and near attention) timed the same way, the block-gate variants (min/max
+block summary, selection shared per kv group, first block kept) on the
+block-gated shapes, and two decode/append steps (new
 tokens after a resident KV cache) reported as step time and algorithmic HBM
 bytes per step against the 8 TB/s peak.
 
@@ -112,7 +114,8 @@ def time_workload(wl, seed, dev, steps, warmup, want_sel=False):
     inp, g = device_inputs(wl, seed, dev)
     ws = sa.Workspace()
     kw = dict(block_size=wl.block_size, top_k=wl.top_k, window=wl.window, idx_q=g["idx_q"],
-              idx_k=g["idx_k"], token_top_k=wl.token_top_k, sink=g["sink"], workspace=ws)
+              idx_k=g["idx_k"], token_top_k=wl.token_top_k, sink=g["sink"], workspace=ws,
+              gate_repr=wl.gate_repr, gate_shared=wl.gate_shared, gate_first=wl.gate_first)
     out = torch.empty_like(g["q"])
     lse = torch.empty(g["q"].shape[:3], dtype=torch.float32, device=dev)
     bsel = tsel = None
@@ -137,6 +140,14 @@ def time_workload(wl, seed, dev, steps, warmup, want_sel=False):
         stages.setdefault(name, []).append(ms)
     stage_ms = {k: float(np.mean(v)) for k, v in stages.items()}
     return inp, (t1 - t0) * 1e3 / steps, stage_ms, (bsel, tsel)
+
+
+# Block-gate variants on the block-gated workloads: the min/max block
+# summary, one selection per kv group, and block 0 always kept.
+GATE_VARIANTS = [W.LONG_MOBA.replace(name="long_moba_minmax_n131072", gate_repr="minmax"),
+                 W.LONG_MOBA.replace(name="long_moba_shared_n131072", gate_shared=True),
+                 W.BORA_HYBRID.replace(name="bora_hybrid_shared_first_n4096", gate_shared=True,
+                                       gate_first=True)]
 
 
 # Decode/append steps: nq new tokens per sequence after a cache of
@@ -282,8 +293,8 @@ def main():
     }
     if not args.no_extra:
         extra = {}
-        for idx in (1, 2, 4, 5):
-            ewl = W.WORKLOADS[idx]
+        for idx, ewl in [(i, W.WORKLOADS[i]) for i in (1, 2, 4, 5)] + \
+                [(2 if v.seq_len == W.BORA_HYBRID.seq_len else 4, v) for v in GATE_VARIANTS]:
             print(f"[bench] workload {ewl.name}", file=sys.stderr, flush=True)
             _, ems, est, (bsel, tsel) = time_workload(ewl, idx, dev, args.extra_steps, 2,
                                                       want_sel=True)
