@@ -79,7 +79,8 @@ def _load(path=None):
     lib.orc_attend_at.argtypes = [_f32p, _f32p, _f32p, _i64, _i64, _i64, _i64, _i64, _i64,
                                   ctypes.c_double, _i64, _i64,
                                   ctypes.c_void_p, _i64, ctypes.c_void_p, _i64,
-                                  ctypes.c_void_p, _i64p, _i64, _f64p, _f64p, _i64p]
+                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, _i64,
+                                  _i64p, _i64, _f64p, _f64p, _i64p]
     lib.orc_attend_at.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -149,6 +150,20 @@ def _gate_args(kb, gate_repr, d):
     if tuple(kb.shape[3:]) != want:
         raise ValueError("pooled keys do not match gate_repr")
     return rep
+
+
+def compress(x, C):
+    """Compressed keys or values: the mean of each complete group of C
+    consecutive tokens, [Bt, Hkv, N // C, d] fp64 (the NSA branch's 8:1
+    compression under the mean reading; the same pooling as block_pool)."""
+    x = _f32(x)
+    Bt, Hkv, N, d = x.shape
+    if C <= 0:
+        raise ValueError("group size must be positive")
+    xc = np.empty((Bt, Hkv, N // C, d), dtype=np.float64)
+    if N // C:
+        _load().orc_block_pool(x, Bt * Hkv, N, d, C, xc)
+    return xc
 
 
 def block_scores(q, kb, B, rows, gate_repr="mean", shared=False, first=False):
@@ -223,10 +238,13 @@ def token_select(idx_q, idx_k, top_t, rows=None):
 
 
 def attend(q, k, v, *, scale=None, window=0, block_size=0, sel=None, tsel=None,
-           sink=None, rows=None):
+           sink=None, rows=None, cmp_block=0):
     """Attention of the listed rows under a given selection.
     sel [len(rows), w] block ids and tsel [len(rows), w'] token ids are per
-    listed row.  Returns out [len(rows), d] fp64, lse fp64, |A(i)| int64."""
+    listed row.  cmp_block > 0 adds the compressed columns (groups of
+    cmp_block tokens, see compress) to the same softmax.  Returns out
+    [len(rows), d] fp64, lse fp64, |A(i)| int64 (compressed columns
+    included)."""
     q, k, v = _f32(q), _f32(k), _f32(v)
     Bt, Hq, Nq, d = q.shape
     Hkv, N = k.shape[1], k.shape[2]
@@ -244,12 +262,16 @@ def attend(q, k, v, *, scale=None, window=0, block_size=0, sel=None, tsel=None,
     for a in (sel_a, tsel_a):
         if a is not None and a.shape[0] != len(rows):
             raise ValueError("selections are per listed row")
+    kc = vc = None
+    if cmp_block:
+        kc, vc = compress(k, cmp_block), compress(v, cmp_block)
     rc = _load().orc_attend_at(
         q, k, v, Hq, Hkv, Nq, N, d, off, scale, int(window), int(block_size),
         None if sel_a is None else sel_a.ctypes.data, 0 if sel_a is None else sel_a.shape[1],
         None if tsel_a is None else tsel_a.ctypes.data, 0 if tsel_a is None else tsel_a.shape[1],
         None if sink_a is None else sink_a.ctypes.data,
-        rows, len(rows), out, lse, cnt)
+        None if kc is None else kc.ctypes.data, None if vc is None else vc.ctypes.data,
+        int(cmp_block), rows, len(rows), out, lse, cnt)
     if rc != 0:
         raise ValueError("selection id out of range")
     return out, lse, cnt
@@ -257,7 +279,7 @@ def attend(q, k, v, *, scale=None, window=0, block_size=0, sel=None, tsel=None,
 
 def forward(q, k, v, *, block_size=0, top_k=0, window=0, idx_q=None, idx_k=None,
             token_top_k=0, sink=None, scale=None, rows=None, gate_repr="mean",
-            gate_shared=False, gate_first=False):
+            gate_shared=False, gate_first=False, cmp_block=0):
     """The whole path for the listed rows: pool, gate, token select, attend.
     Returns a dict with out, lse, count, sel, s_last, s_next, tsel, t_last,
     t_next (selection entries are None when that gate is off).
@@ -267,7 +289,8 @@ def forward(q, k, v, *, block_size=0, top_k=0, window=0, idx_q=None, idx_k=None,
     position rq + Nk - Nq.  Block gating is a prefill method here (the MoBA
     summary switches to full attention for generation) and needs Nq = Nk.
     gate_repr / gate_shared / gate_first pick the block gate's variant
-    (see block_pool and block_select)."""
+    (see block_pool and block_select); cmp_block > 0 adds the compressed
+    branch (see attend)."""
     Bt, Hq, N, d = np.shape(q)
     rows = _rows(rows, Bt * Hq * N)
     res = dict(sel=None, s_last=None, s_next=None, tsel=None, t_last=None, t_next=None)
@@ -283,6 +306,7 @@ def forward(q, k, v, *, block_size=0, top_k=0, window=0, idx_q=None, idx_k=None,
         ts, tl, tn = token_select(idx_q, idx_k, token_top_k, uniq)
         res["tsel"], res["t_last"], res["t_next"] = ts[inv], tl[inv], tn[inv]
     out, lse, cnt = attend(q, k, v, scale=scale, window=window, block_size=block_size,
-                           sel=res["sel"], tsel=res["tsel"], sink=sink, rows=rows)
+                           sel=res["sel"], tsel=res["tsel"], sink=sink, rows=rows,
+                           cmp_block=cmp_block)
     res.update(out=out, lse=lse, count=cnt)
     return res

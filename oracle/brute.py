@@ -20,6 +20,11 @@ Gate variants, stated here independently of the C oracle:
   sum over the group's heads of that head's score; all of them keep the
   same blocks;
 * first: block 0 is kept like the own block and takes one of the k slots.
+
+Compressed branch (BORA model card, NSA: 8 tokens -> 1 compressed key and
+value): with cmp_block = C, every complete group c of C tokens whose last
+token is at or before i adds one column to the softmax: the exact mean of
+its keys as the key and the mean of its values as the value.
 """
 from __future__ import annotations
 
@@ -59,7 +64,7 @@ def _box_score(qv, lo, hi) -> Fraction:
 
 def forward(q, k, v, *, block_size=0, top_k=0, window=0, idx_q=None, idx_k=None,
             token_top_k=0, sink=None, scale=None, gate_repr="mean", gate_shared=False,
-            gate_first=False):
+            gate_first=False, cmp_block=0):
     """Returns (out [Bt,Hq,Nq,d], lse [Bt,Hq,Nq], sel dict, tsel dict, count).
 
     q may hold fewer rows (Nq) than k, v (Nk): query row iq is then the token
@@ -123,12 +128,24 @@ def forward(q, k, v, *, block_size=0, top_k=0, window=0, idx_q=None, idx_k=None,
                         keys.append(j)
                 logits = [scale * sum(q[b, h, iq, e] * k[b, g, j, e] for e in range(d))
                           for j in keys]
+                vals = [[v[b, g, j, e] for e in range(d)] for j in keys]
+                if cmp_block:
+                    for c in range(N // cmp_block):
+                        grp = range(c * cmp_block, (c + 1) * cmp_block)
+                        if grp[-1] > i:
+                            continue
+                        kc = [float(sum((_frac(k[b, g, j, e]) for j in grp), Fraction(0)) / cmp_block)
+                              for e in range(d)]
+                        vc = [float(sum((_frac(v[b, g, j, e]) for j in grp), Fraction(0)) / cmp_block)
+                              for e in range(d)]
+                        logits.append(scale * sum(q[b, h, iq, e] * kc[e] for e in range(d)))
+                        vals.append(vc)
                 z = None if sink is None else float(sink[h])
                 M = max(logits + ([z] if z is not None else []), default=-math.inf)
                 w = [math.exp(x - M) for x in logits]
                 L = sum(w) + (math.exp(z - M) if z is not None else 0.0)
                 for e in range(d):
-                    out[b, h, iq, e] = sum(wj * v[b, g, j, e] for wj, j in zip(w, keys)) / L
+                    out[b, h, iq, e] = sum(wj * vj[e] for wj, vj in zip(w, vals)) / L
                 lse[b, h, iq] = M + math.log(L)
-                count[b, h, iq] = len(keys)
+                count[b, h, iq] = len(logits)
     return out, lse, sels, tsels, count

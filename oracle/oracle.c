@@ -303,7 +303,19 @@ void orc_token_select(const float* iq, const float* ik, int64_t N, int64_t dI, i
  *   out = sum_j e^(x_j - M) v_j / L,   lse = M + ln L.
  * sel  [nrows, sel_w]  block ids per listed row, -1 ignored (NULL: none)
  * tsel [nrows, tsel_w] token ids per listed row, -1 ignored (NULL: none)
- * count[t] = |A(i)|.  Returns 0, or -1 if an id is out of range.
+ * count[t] = |A(i)| (compressed columns included).  Returns 0, or -1 if an
+ * id is out of range.
+ *
+ * Compressed columns (C > 0) [BORA model card, NSA: 8 tokens become one
+ * compressed key/value (8:1), next to the top-k block selection and the
+ * sliding window]: kc, vc [Bt, Hkv, N/C, d] hold the compressed keys and
+ * values (orc_block_pool with block C: the mean of each complete group of
+ * C tokens).  Reading: the pages give neither the compression function nor
+ * how the branches combine; the mean is the parameter-free compression
+ * (the same pooling the block gate uses), query i sees group c once all its
+ * tokens are at or before i ((c+1)C - 1 <= i), and each visible group is
+ * one more column x_c = scale * <q_i, kc_c> with value vc_c in the same
+ * softmax as A(i) (the union reading of the other branches).
  *
  * Queries q [Bt, Hq, Nq, d] against keys k, v [Bt, Hkv, N, d]: row
  * r = (b*Hq + h)*Nq + rq sits at position i = rq + off [Bit-Axon page,
@@ -316,14 +328,17 @@ int orc_attend_at(const float* q, const float* k, const float* v,
                   const int32_t* sel, int64_t sel_w,
                   const int32_t* tsel, int64_t tsel_w,
                   const float* sink,
+                  const double* kc, const double* vc, int64_t C,
                   const int64_t* rows, int64_t nrows,
                   double* out, double* lse, int64_t* count) {
     const int64_t G = Hq / Hkv;
+    const int64_t Nc = C > 0 ? N / C : 0;
     int bad = 0;
 #pragma omp parallel
     {
         unsigned char* mark = (unsigned char*)malloc((size_t)(N > 0 ? N : 1));
         double* x = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+        double* xc = (double*)malloc(sizeof(double) * (size_t)(Nc > 0 ? Nc : 1));
 #pragma omp for schedule(dynamic, 8)
         for (int64_t t = 0; t < nrows; ++t) {
             const int64_t r = rows[t];
@@ -359,6 +374,17 @@ int orc_attend_at(const float* q, const float* k, const float* v,
                 if (x[j] > M) M = x[j];
                 ++cnt;
             }
+            /* compressed groups c with (c+1)C - 1 <= i */
+            const int64_t nvis = C > 0 ? (i + 1) / C : 0;
+            const double* kcb = kc ? kc + (b * Hkv + g) * Nc * d : NULL;
+            const double* vcb = vc ? vc + (b * Hkv + g) * Nc * d : NULL;
+            for (int64_t c = 0; c < nvis; ++c) {
+                double acc = 0.0;
+                for (int64_t e = 0; e < d; ++e) acc += (double)qrow[e] * kcb[c * d + e];
+                xc[c] = scale * acc;
+                if (xc[c] > M) M = xc[c];
+                ++cnt;
+            }
             const double z = sink ? (double)sink[h] : -INFINITY;
             if (z > M) M = z;
             double L = 0.0;
@@ -369,6 +395,11 @@ int orc_attend_at(const float* q, const float* k, const float* v,
                 const double p = exp(x[j] - M);
                 L += p;
                 for (int64_t e = 0; e < d; ++e) o[e] += p * (double)vb[j * d + e];
+            }
+            for (int64_t c = 0; c < nvis; ++c) {
+                const double p = exp(xc[c] - M);
+                L += p;
+                for (int64_t e = 0; e < d; ++e) o[e] += p * vcb[c * d + e];
             }
             if (sink) L += exp(z - M);
             if (L > 0.0) {
@@ -381,6 +412,7 @@ int orc_attend_at(const float* q, const float* k, const float* v,
         }
         free(mark);
         free(x);
+        free(xc);
     }
     return bad ? -1 : 0;
 }
@@ -394,5 +426,5 @@ int orc_attend(const float* q, const float* k, const float* v,
                const int64_t* rows, int64_t nrows,
                double* out, double* lse, int64_t* count) {
     return orc_attend_at(q, k, v, Hq, Hkv, N, N, d, 0, scale, window, B, sel, sel_w, tsel, tsel_w,
-                         sink, rows, nrows, out, lse, count);
+                         sink, NULL, NULL, 0, rows, nrows, out, lse, count);
 }

@@ -78,7 +78,8 @@ def check(inp, dev_out, dev_lse, rows, dev_bsel=None, dev_tsel=None, *, kbar=Non
     Bt, Hq, N, d = inp.q.shape
     rows = np.asarray(rows, dtype=np.int64)
     rep = Report(rows=len(rows))
-    gv = dict(gate_repr=wl.gate_repr, gate_shared=wl.gate_shared, gate_first=wl.gate_first)
+    gv = dict(gate_repr=wl.gate_repr, gate_shared=wl.gate_shared, gate_first=wl.gate_first,
+              cmp_block=wl.cmp_block)
     res = oracle.forward(inp.q, inp.k, inp.v, block_size=wl.block_size, top_k=wl.top_k,
                          window=wl.window, idx_q=inp.idx_q, idx_k=inp.idx_k,
                          token_top_k=wl.token_top_k, sink=inp.sink, rows=rows, **gv)
@@ -138,7 +139,8 @@ def check(inp, dev_out, dev_lse, rows, dev_bsel=None, dev_tsel=None, *, kbar=Non
         o2, l2, c2 = oracle.attend(
             inp.q, inp.k, inp.v, window=wl.window, block_size=wl.block_size,
             sel=None if use_bsel is None else use_bsel[idx],
-            tsel=None if use_tsel is None else use_tsel[idx], sink=inp.sink, rows=rows[idx])
+            tsel=None if use_tsel is None else use_tsel[idx], sink=inp.sink, rows=rows[idx],
+            cmp_block=wl.cmp_block)
         ref_out[idx], ref_lse[idx] = o2, l2
         res["count"][idx] = c2
         rep.notes.append(f"{len(idx)} rows re-evaluated under the device selection")

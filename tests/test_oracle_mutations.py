@@ -34,6 +34,12 @@ MUTATIONS = [
                                     "const int64_t c0 = 0;\n        for (int64_t c = 0; c < n; ++c)"),
                                    ("const int64_t c0 = (first && own > 0 && top_k >= 2) ? 1 : 0;",
                                     "const int64_t c0 = 0;\n            if (first && own > 0) sel[t * top_k] = 0;")]),
+    ("compressed group seen one token early", [("const int64_t nvis = C > 0 ? (i + 1) / C : 0;",
+                                                "const int64_t nvis = C > 0 ? (i + 2) / C : 0;")]),
+    ("compressed value is its key", [("o[e] += p * vcb[c * d + e];", "o[e] += p * kcb[c * d + e];")]),
+    ("compressed logit unscaled", [("xc[c] = scale * acc;", "xc[c] = acc;")]),
+    ("compressed columns not counted", [("if (xc[c] > M) M = xc[c];\n                ++cnt;",
+                                         "if (xc[c] > M) M = xc[c];")]),
     ("sink logit scaled", [("const double z = sink ? (double)sink[h] : -INFINITY;",
                             "const double z = sink ? scale * (double)sink[h] : -INFINITY;")]),
     ("softmax scale dropped", [("x[j] = scale * acc;", "x[j] = acc;")]),
@@ -80,6 +86,13 @@ PIN_CALLS = [
 ] + [
     (lambda c=c, t=t: pins.test_p23_variants_brute_force(c, t))
     for c in range(len(pins.VARIANT_CASES)) for t in (False, True)
+] + [
+    lambda: pins.test_p24_groups_of_one_double_the_causal_keys(),
+    lambda: pins.test_p25_compressed_columns_are_group_mean_attention(),
+    lambda: pins.test_p26_union_merges_by_lse(),
+] + [
+    (lambda c=c, t=t: pins.test_p27_compressed_brute_force(c, t))
+    for c in range(len(pins.CMP_CASES)) for t in (False, True)
 ] + [
     (lambda c=c, n=n: pins.test_p15_decode_is_last_prefill_rows(c, n))
     for c in range(len(pins.DECODE_CASES)) for n in (1, 5)

@@ -533,6 +533,104 @@ def test_p23_variants_brute_force(case, ties):
         assert {c for c in r["sel"][t].tolist() if c >= 0} == bsel[(0, h, i)], (h, i)
 
 
+# ---------------------------------------------------------------------------
+# Compressed branch (BORA model card, NSA: 8 tokens -> one compressed key and
+# value, next to block selection and the sliding window).
+# ---------------------------------------------------------------------------
+
+# P24: groups of one token are the tokens themselves: every causal key then
+# appears once more as a compressed column, so window keys count twice --
+# SDPA with an additive log 2 on the window and 0 on the other causal keys.
+def test_p24_groups_of_one_double_the_causal_keys():
+    N, w = 48, 5
+    q, k, v = rnd((1, 3, N, 8), 320), rnd((1, 3, N, 8), 321), rnd((1, 3, N, 8), 322)
+    r, out, lse = run(q, k, v, window=w, cmp_block=1)
+    pos = np.arange(N)
+    causal = pos[None, :] <= pos[:, None]
+    bias = np.where(causal, np.where(pos[:, None] - pos[None, :] < w, math.log(2.0), 0.0), -np.inf)
+    qt, kt, vt = (torch.from_numpy(a.astype(np.float64)) for a in (q, k, v))
+    bt = torch.from_numpy(bias)
+    ro = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=bt,
+                                                          scale=1 / math.sqrt(8))
+    logits = torch.matmul(qt, kt.transpose(-1, -2)) / math.sqrt(8) + bt
+    np.testing.assert_allclose(out, ro.numpy(), atol=1e-12)
+    np.testing.assert_allclose(lse, torch.logsumexp(logits, -1).numpy(), atol=1e-12)
+    assert (r["count"].reshape(3, N) == np.minimum(pos + 1, w) + pos + 1).all()
+
+
+# P25: the compressed columns alone are SDPA over the group means (torch
+# reductions) with the group-causal mask (c+1)C - 1 <= i; group size 8 as
+# on the BORA card, N not a multiple of it (the last partial group is never
+# seen).
+def test_p25_compressed_columns_are_group_mean_attention():
+    N, C = 70, 8
+    q, k, v = rnd((2, 4, N, 8), 323), rnd((2, 2, N, 8), 324), rnd((2, 2, N, 8), 325)
+    kc = torch.from_numpy(k[:, :, :N // C * C].astype(np.float64)).reshape(2, 2, N // C, C, 8).mean(3)
+    vc = torch.from_numpy(v[:, :, :N // C * C].astype(np.float64)).reshape(2, 2, N // C, C, 8).mean(3)
+    np.testing.assert_allclose(oracle.compress(k, C), kc.numpy(), atol=1e-15)
+    kcr, vcr = kc.repeat_interleave(2, dim=1), vc.repeat_interleave(2, dim=1)   # GQA 4/2
+    pos, grp = np.arange(N), np.arange(N // C)
+    mask = (grp[None, :] + 1) * C - 1 <= pos[:, None]
+    rows = np.array([(b * 4 + h) * N + i for b in range(2) for h in range(4) for i in range(C - 1, N)])
+    o, l, cnt = oracle.attend(q, k, v, cmp_block=C, rows=rows)
+    qt = torch.from_numpy(q.astype(np.float64))
+    ro = torch.nn.functional.scaled_dot_product_attention(qt, kcr, vcr, attn_mask=torch.from_numpy(mask))
+    i = rows % N
+    np.testing.assert_allclose(o, ro.numpy().reshape(-1, N, 8)[np.arange(len(rows)) // (N - C + 1), i],
+                               atol=1e-12)
+    np.testing.assert_array_equal(cnt, (i + 1) // C)
+
+
+# P26: one softmax over the union: merging the window-only and the
+# compressed-only results by their lse gives the joint result (the rule the
+# GPU uses to combine the two kernels' outputs).
+def test_p26_union_merges_by_lse():
+    N, C, w = 64, 8, 6
+    q, k, v = rnd((1, 2, N, 16), 326), rnd((1, 2, N, 16), 327), rnd((1, 2, N, 16), 328)
+    sink = rnd((2,), 329)
+    rows = np.arange(2 * N)
+    o, l, _ = oracle.attend(q, k, v, window=w, cmp_block=C, sink=sink, rows=rows)
+    ow, lw, _ = oracle.attend(q, k, v, window=w, sink=sink, rows=rows)
+    oc, lc, _ = oracle.attend(q, k, v, cmp_block=C, rows=rows)
+    lm = np.logaddexp(lw, lc)
+    np.testing.assert_allclose(l, lm, atol=1e-12)
+    wc = np.where(np.isneginf(lc), 0.0, np.exp(lc - lm))
+    np.testing.assert_allclose(o, ow * np.exp(lw - lm)[:, None] + np.nan_to_num(oc) * wc[:, None],
+                               atol=1e-12)
+
+
+# P27: exact brute force with the compressed branch, alone with a window and
+# together with block gating and its variants, with and without ties.
+CMP_CASES = [
+    dict(window=3, cmp_block=4),
+    dict(window=1, cmp_block=5, sink=True),
+    dict(block_size=4, top_k=2, cmp_block=2),
+    dict(block_size=2, top_k=3, window=2, cmp_block=3, gate_first=True, gate_repr="minmax"),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CMP_CASES)))
+@pytest.mark.parametrize("ties", [False, True])
+def test_p27_compressed_brute_force(case, ties):
+    kw = dict(CMP_CASES[case])
+    use_sink = kw.pop("sink", False)
+    Bt, Hq, Hkv, N, d = 1, 4, 2, 13, 3
+    rng = np.random.default_rng(500 + case + 50 * ties)
+    draw = (lambda s: rng.integers(-1, 2, size=s).astype(np.float32)) if ties else \
+           (lambda s: rng.standard_normal(s).astype(np.float32))
+    q, k, v = draw((Bt, Hq, N, d)), draw((Bt, Hkv, N, d)), draw((Bt, Hkv, N, d))
+    if "block_size" in kw:   # block gating needs whole blocks
+        N2 = N // kw["block_size"] * kw["block_size"]
+        q, k, v = (np.ascontiguousarray(a[:, :, :N2]) for a in (q, k, v))
+        N = N2
+    sink = rng.standard_normal(Hq).astype(np.float32) if use_sink else None
+    r, out, lse = run(q, k, v, sink=sink, **kw)
+    bo, bl, bsel, _, bcnt = brute.forward(q, k, v, sink=sink, **kw)
+    np.testing.assert_allclose(out, bo, atol=1e-12)
+    np.testing.assert_allclose(lse, bl, atol=1e-12)
+    np.testing.assert_array_equal(r["count"].reshape(Bt, Hq, N), bcnt)
+
+
 def test_gate_variant_arguments_checked():
     q, k = rnd((1, 2, 16, 4), 313), rnd((1, 2, 16, 4), 314)
     with pytest.raises(ValueError):

@@ -49,6 +49,7 @@ class Workload:
     gate_repr: str = "mean"    # block summary for the gate: "mean" or "minmax"
     gate_shared: bool = False  # one block selection per kv group
     gate_first: bool = False   # block 0 always kept (takes one of the top_k slots)
+    cmp_block: int = 0         # compressed branch: tokens per compressed key/value; 0 = off
 
     def replace(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
