@@ -32,7 +32,12 @@
  *      i - j < window) or block(j) kept or token j kept } [Bit-Axon
  *      "SWA + MoE" page, "어텐션 공식" and "슬라이딩 윈도우 마스크"], logits
  *      softmax_scale * <q_i, k_j>, plus -- when sink != NULL -- one extra
- *      logit sink[h] (not scaled) whose value vector is zero.
+ *      logit sink[h] (not scaled) whose value vector is zero, plus -- when
+ *      cmp_block = C > 0 -- the compressed columns [BORA model card, NSA:
+ *      8 tokens become one compressed key and value]: every complete group
+ *      c of C tokens with (c+1)C - 1 <= i adds the logit
+ *      softmax_scale * <q_i, mean of the group's keys> with the mean of its
+ *      values as the value.
  *      out_i = sum_j p_j v_j,  lse_i = natural log of the softmax
  *      normaliser (sink included).
  *
@@ -79,7 +84,7 @@
 extern "C" {
 #endif
 
-#define SPARSE_ATTN_ABI_VERSION 3
+#define SPARSE_ATTN_ABI_VERSION 4
 
 typedef enum {
     SA_BF16 = 0, /* bfloat16 inputs and out; fp32 accumulation.  Q K^T runs on
@@ -136,6 +141,8 @@ typedef struct {
     int32_t gate_repr;      /* sa_gate_repr; SA_GATE_MEAN unless top_k > 0 */
     int32_t gate_shared;    /* 0 or 1: one block selection per kv group; 0 unless top_k > 0 */
     int32_t gate_first;     /* 0 or 1: block 0 always kept (top_k >= 2); 0 unless top_k > 0 */
+    int32_t cmp_block;      /* tokens per compressed key/value (the BORA card's 8); 0 = no
+                               compressed branch.  Prefill only, not with token_top_k */
 } sparse_attn_cfg;
 
 /* Bytes of device workspace sparse_attn_fwd needs for this configuration

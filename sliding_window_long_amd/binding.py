@@ -48,7 +48,7 @@ class SparseAttnCfg(ctypes.Structure):
         ("stream", ctypes.c_void_p),
         ("kv_len", ctypes.c_int32),
         ("gate_repr", ctypes.c_int32), ("gate_shared", ctypes.c_int32),
-        ("gate_first", ctypes.c_int32),
+        ("gate_first", ctypes.c_int32), ("cmp_block", ctypes.c_int32),
     ]
 
 
@@ -108,13 +108,14 @@ class Params:
     gate_repr: int = SA_GATE_MEAN   # block summary: SA_GATE_MEAN or SA_GATE_MINMAX
     gate_shared: int = 0      # 1: one block selection per kv group
     gate_first: int = 0       # 1: block 0 always kept (takes a slot)
+    cmp_block: int = 0        # tokens per compressed key/value; 0 = no compressed branch
 
     def cfg(self) -> SparseAttnCfg:
         c = SparseAttnCfg()
         c.struct_size = ctypes.sizeof(SparseAttnCfg)
         for f in ("batch", "n_q_heads", "n_kv_heads", "seq_len", "head_dim", "dtype",
                   "block_size", "top_k", "window", "token_top_k", "index_dim", "kv_len",
-                  "gate_repr", "gate_shared", "gate_first"):
+                  "gate_repr", "gate_shared", "gate_first", "cmp_block"):
             setattr(c, f, int(getattr(self, f)))
         c.softmax_scale = float(self.softmax_scale)
         return c
@@ -170,7 +171,8 @@ GATE_REPR = {"mean": SA_GATE_MEAN, "minmax": SA_GATE_MINMAX}
 
 
 def params_for(q, k, *, block_size=0, top_k=0, window=0, token_top_k=0, index_dim=0,
-               scale=None, gate_repr="mean", gate_shared=False, gate_first=False) -> Params:
+               scale=None, gate_repr="mean", gate_shared=False, gate_first=False,
+               cmp_block=0) -> Params:
     import torch
     Bt, Hq, N, d = q.shape
     dt = {torch.bfloat16: SA_BF16, torch.float32: SA_F32}.get(q.dtype)
@@ -181,7 +183,8 @@ def params_for(q, k, *, block_size=0, top_k=0, window=0, token_top_k=0, index_di
     Nk = k.shape[2]
     return Params(Bt, Hq, k.shape[1], N, d, dt, block_size, top_k, window, token_top_k,
                   index_dim, 0.0 if scale is None else float(scale), Nk if Nk != N else 0,
-                  GATE_REPR[gate_repr], int(bool(gate_shared)), int(bool(gate_first)))
+                  GATE_REPR[gate_repr], int(bool(gate_shared)), int(bool(gate_first)),
+                  int(cmp_block))
 
 
 class Workspace:
@@ -205,14 +208,14 @@ _default_ws = Workspace()
 def forward(q, k, v, *, block_size=0, top_k=0, window=0, idx_q=None, idx_k=None,
             token_top_k=0, sink=None, scale=None, return_selection=False,
             workspace: Workspace | None = None, out=None, lse=None, gate_repr="mean",
-            gate_shared=False, gate_first=False):
+            gate_shared=False, gate_first=False, cmp_block=0):
     """Causal sparse-attention prefill on q's device and torch's current
     stream.  Returns (out, lse) or, with return_selection,
     (out, lse, block_sel, token_sel).  When k, v (and idx_k) hold more
     positions than q (and idx_q), the call is a decode/append step: the
     queries are the newest positions of that history.  gate_repr ("mean" or
-    "minmax"), gate_shared and gate_first select the block gate's variant
-    (see the C header)."""
+    "minmax"), gate_shared and gate_first select the block gate's variant;
+    cmp_block > 0 adds the compressed branch (see the C header)."""
     import torch
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not t.is_cuda or not t.is_contiguous():
@@ -222,7 +225,8 @@ def forward(q, k, v, *, block_size=0, top_k=0, window=0, idx_q=None, idx_k=None,
     index_dim = idx_q.shape[-1] if idx_q is not None else 0
     p = params_for(q, k, block_size=block_size, top_k=top_k, window=window,
                    token_top_k=token_top_k, index_dim=index_dim, scale=scale,
-                   gate_repr=gate_repr, gate_shared=gate_shared, gate_first=gate_first)
+                   gate_repr=gate_repr, gate_shared=gate_shared, gate_first=gate_first,
+                   cmp_block=cmp_block)
     cfg = p.cfg()
     dev = q.device
     if out is None:

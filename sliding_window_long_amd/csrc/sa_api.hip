@@ -7,6 +7,9 @@
 //                blocks -> far-block attention partials
 //   query-centric attention over window / own block / near kept blocks,
 //   merging the far partials and the sink -> out, lse
+//   [compressed branch] group means of K, V -> attention over the visible
+//                compressed columns, merged by lse into out, lse (the
+//                query-centric pass then leaves an fp32 out in the workspace)
 #include "sparse_attn.h"
 #include "sa_internal.hpp"
 
@@ -28,6 +31,8 @@ struct Plan {
     int B, n, top_k, span, kslots, idx_bits, lists;
     bool gate_mm, gate_shared, gate_first;   // gate variants
     int gate_planes;
+    bool cmp;               // compressed branch
+    int C, Nc;
     bool far;
     long long max_entries;
     int max_chunks;
@@ -40,7 +45,7 @@ struct Plan {
     size_t o_split, o_kb3, o_sel, o_count, o_cursor, o_listoff, o_nchunks, o_chunk_list,
         o_chunk_start, o_entries, o_part_o, o_part_lse, o_tok_split, o_tok_state, o_tok_mask,
         o_tok_qn, o_tok_win, o_tok_kpart, o_tok_scr, o_tok_nslow, o_dec_scores, o_dec_list,
-        o_dec_nfar, o_dec_part, o_qsum,
+        o_dec_nfar, o_dec_part, o_qsum, o_cmp_k, o_cmp_v, o_cmp_out,
         o_v16, total;
 };
 
@@ -67,12 +72,17 @@ int make_plan(const sparse_attn_cfg* c, Plan* p) {
     if (c->top_k == 0 && (c->gate_repr != SA_GATE_MEAN || c->gate_shared || c->gate_first))
         return SA_E_INVALID_ARG;
     if (c->gate_first && c->top_k < 2) return SA_E_INVALID_ARG;
+    if (c->cmp_block < 0) return SA_E_INVALID_ARG;
     // Keys of the history: a decode/append step has more keys than queries.
     if (c->kv_len < 0) return SA_E_INVALID_ARG;
     const int Nk = c->kv_len > 0 ? c->kv_len : c->seq_len;
     if (Nk < c->seq_len) return SA_E_INVALID_ARG;
     const bool dec = Nk > c->seq_len;
-    if (dec && (c->top_k > 0 || c->seq_len > sa::kDecMaxQ)) return SA_E_UNSUPPORTED;
+    if (dec && (c->top_k > 0 || c->seq_len > sa::kDecMaxQ || c->cmp_block > 0))
+        return SA_E_UNSUPPORTED;
+    // The compressed branch joins window / block gating (the NSA layout), not
+    // the token gate.
+    if (c->cmp_block > 0 && c->token_top_k > 0) return SA_E_UNSUPPORTED;
     if (c->token_top_k > 0) {
         if (c->index_dim != 64) return SA_E_UNSUPPORTED_HEAD_DIM;
         // 16 index bits in the selection key; block and token gates are
@@ -174,6 +184,16 @@ int make_plan(const sparse_attn_cfg* c, Plan* p) {
             P.o_part_o = take((size_t)rows * P.kslots * P.D * 2);
             P.o_part_lse = take((size_t)rows * P.kslots * 4);
         }
+    }
+    P.cmp = c->cmp_block > 0;
+    if (P.cmp) {
+        P.C = c->cmp_block;
+        P.Nc = P.N / P.C;
+        const size_t ncmp = (size_t)P.Bt * P.Hkv * P.Nc * P.D;
+        const int planes = P.f32 ? 2 : 1;
+        P.o_cmp_k = take(planes * ncmp * 2);
+        P.o_cmp_v = take(planes * ncmp * 2);
+        P.o_cmp_out = take((size_t)rows * P.D * 4);
     }
     P.tok = c->token_top_k > 0;
     if (P.tok) {
@@ -469,8 +489,33 @@ int sparse_attn_fwd(const void* q, const void* k, const void* v, const sparse_at
     ra.sel = sel; ra.part_o = part_o; ra.part_lse = part_lse; ra.kslots = P.kslots;
     ra.sink = cfg->sink; ra.out_f32 = P.f32 ? 1 : 0;
     ra.tokmask = tokmask;
-    StageScope t("attn_rows", s);
-    if (!ok(sa::launch_rows(ra, P.D, split, s))) return SA_E_HIP;
+    float* out_r = P.cmp ? (float*)(ws + P.o_cmp_out) : nullptr;
+    if (P.cmp) {   // the compressed pass merges into the final out
+        ra.out = out_r;
+        ra.out_f32 = 1;
+    }
+    {
+        StageScope t("attn_rows", s);
+        if (!ok(sa::launch_rows(ra, P.D, split, s))) return SA_E_HIP;
+    }
+    if (P.cmp) {
+        const size_t ncmp = (size_t)P.Bt * P.Hkv * P.Nc * P.D;
+        uint16_t* kc = (uint16_t*)(ws + P.o_cmp_k);
+        uint16_t* vc = (uint16_t*)(ws + P.o_cmp_v);
+        sa::CmpPoolArgs cp{k, v, {kc, P.f32 ? kc + ncmp : nullptr}, {vc, P.f32 ? vc + ncmp : nullptr},
+                           P.Bt * P.Hkv, P.N, P.C, P.Nc, P.D};
+        {
+            StageScope t("cmp_pool", s);
+            if (!ok(sa::launch_cmp_pool(cp, P.f32, s))) return SA_E_HIP;
+        }
+        sa::CmpArgs ca{};
+        for (int i = 0; i < 2; ++i) { ca.q[i] = qp[i]; ca.kc[i] = cp.kc[i]; ca.vc[i] = cp.vc[i]; }
+        ca.out_r = out_r; ca.out = out; ca.lse = lse;
+        ca.Bt = P.Bt; ca.Hq = P.Hq; ca.Hkv = P.Hkv; ca.N = P.N; ca.C = P.C; ca.Nc = P.Nc;
+        ca.scale = P.scale; ca.out_f32 = P.f32 ? 1 : 0;
+        StageScope t("attn_compressed", s);
+        if (!ok(sa::launch_cmp(ca, P.D, split, s))) return SA_E_HIP;
+    }
     return SA_OK;
 }
 

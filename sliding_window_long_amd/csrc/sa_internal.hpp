@@ -98,6 +98,33 @@ struct GroupSumArgs {
     int minmax;
 };
 
+// Compressed branch: group means of K and V ([lists = Bt*Hkv, Nc, D]; bf16 K
+// and fp16 V planes for bf16 inputs, bf16 hi/lo planes of both for fp32).
+struct CmpPoolArgs {
+    const void* k;
+    const void* v;
+    uint16_t* kc[2];
+    uint16_t* vc[2];
+    int lists, N, C, Nc, D;
+};
+
+// Attention over the compressed columns, merged with the other branches'
+// normalised fp32 result out_r and its lse (updated in place).
+struct CmpArgs {
+    const uint16_t* q[2];
+    const uint16_t* kc[2];
+    const uint16_t* vc[2];
+    const float* out_r;     // [Bt*Hq*N, D] fp32
+    void* out;              // final out, bf16 or fp32 (out_f32)
+    float* lse;             // in: lse_r; out: the merged lse
+    int Bt, Hq, Hkv, N, C, Nc;
+    float scale;
+    int out_f32;
+};
+
+hipError_t launch_cmp_pool(const CmpPoolArgs& a, bool f32_in, hipStream_t s);
+hipError_t launch_cmp(const CmpArgs& a, int head_dim, int split, hipStream_t s);
+
 // Inversion of the block selection into per-(batch, kv head, block) lists of
 // the rows that keep that block as a far block.
 struct CompactArgs {

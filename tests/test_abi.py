@@ -85,6 +85,9 @@ def code_of(params, **cfg_fields):
     (sa.Params(1, 4, 4, 256, 64, window=8, gate_shared=1), -1),
     (sa.Params(1, 4, 4, 256, 64, window=8, gate_first=1), -1),
     (sa.Params(1, 4, 4, 256, 64, block_size=64, top_k=1, gate_first=1), -1),  # no slot for block 0
+    (sa.Params(1, 4, 4, 256, 64, window=8, cmp_block=-8), -1),
+    (sa.Params(1, 4, 4, 1, 64, window=8, kv_len=256, cmp_block=8), -8),       # decode + compressed
+    (sa.Params(1, 4, 1, 256, 128, window=8, token_top_k=16, index_dim=64, cmp_block=8), -8),
 ])
 def test_invalid_configs(lib, params, code):
     assert code_of(params) == code
@@ -107,6 +110,17 @@ def test_valid_configs(lib):
               sa.Params(1, 1, 1, 512, 64, dtype=sa.SA_F32, block_size=64, top_k=2,
                         gate_repr=1, gate_first=1)):
         assert code_of(p) == 0
+
+
+def test_compressed_workspace(lib):
+    # compressed K and V [Bt, Hkv, N/C, d] (one 16-bit plane each, two for
+    # fp32) plus the other branches' fp32 out [Bt, Hq, N, d]
+    base = dict(block_size=128, top_k=16, window=512)
+    ws = lambda **kw: sa.sparse_attn_workspace_bytes(sa.Params(2, 8, 4, 4096, 128, **base, **kw).cfg())
+    ncmp = 2 * 4 * 512 * 128
+    delta = ws(cmp_block=8) - ws()
+    assert 2 * ncmp * 2 + 2 * 8 * 4096 * 128 * 4 <= delta <= 2 * ncmp * 2 + 2 * 8 * 4096 * 128 * 4 + 768
+    assert code_of(sa.Params(1, 2, 2, 100, 64, window=4, cmp_block=1000)) == 0   # no complete group
 
 
 def test_gate_variant_workspace(lib):

@@ -41,7 +41,7 @@ def run_device(inp, dev):
         g["q"], g["k"], g["v"], block_size=wl.block_size, top_k=wl.top_k, window=wl.window,
         idx_q=g["idx_q"], idx_k=g["idx_k"], token_top_k=wl.token_top_k, sink=g["sink"],
         return_selection=True, gate_repr=wl.gate_repr, gate_shared=wl.gate_shared,
-        gate_first=wl.gate_first)
+        gate_first=wl.gate_first, cmp_block=wl.cmp_block)
     torch.cuda.synchronize()
     return (out.float().cpu().numpy(), lse.cpu().numpy(),
             None if bsel is None else bsel.cpu().numpy(),
@@ -242,6 +242,36 @@ def test_long_moba_minmax_full_sampled(dev):
     wl = W.LONG_MOBA.replace(name="long_moba_minmax", gate_repr="minmax")
     run_and_check(W.make_inputs(wl, 104), dev, W.sample_rows(wl, 2048, 3),
                   label="long_moba_minmax_full")
+
+
+# --- compressed branch (NSA: 8 tokens -> one compressed key and value) --------
+@pytest.mark.parametrize("d", [64, 80, 128])
+@pytest.mark.parametrize("N,C,window", [(1, 8, 4), (7, 8, 3), (300, 8, 17), (1000, 8, 64),
+                                        (513, 1, 1), (700, 64, 100), (200, 300, 8)])
+def test_compressed_window(dev, d, N, C, window):
+    wl = W.Workload("cmp_swa", 2, 4, 2, N, d, "bf16", window=window, cmp_block=C, sink=True)
+    run_and_check(W.make_inputs(wl, 61 + d + N + C), dev, label=f"cmp_window N={N} C={C}")
+
+
+@pytest.mark.parametrize("var", [dict(), dict(gate_shared=True, gate_first=True),
+                                 dict(gate_repr="minmax")], ids=["mean", "shared_first", "minmax"])
+def test_compressed_with_block_gate(dev, var):
+    wl = W.Workload("cmp_gate", 2, 8, 4, 1024, 128, "bf16", block_size=128, top_k=4, window=128,
+                    cmp_block=8, block_offsets=True, **var)
+    run_and_check(W.make_inputs(wl, 62), dev, label=f"cmp_gate {var}")
+
+
+def test_compressed_fp32(dev):
+    wl = W.Workload("cmp_f32", 1, 2, 1, 384, 64, "f32", block_size=64, top_k=3, window=40,
+                    cmp_block=8, sink=True, block_offsets=True)
+    run_and_check(W.make_inputs(wl, 63), dev, label="cmp_f32")
+
+
+def test_bora_nsa_all_rows(dev):
+    # The BORA NSA layout: GQA 8/4, 8:1 compression, top 16 of 32 blocks,
+    # window 512, one selection per kv group.
+    wl = W.BORA_HYBRID.replace(name="bora_nsa_n4096", cmp_block=8, gate_shared=True)
+    run_and_check(W.make_inputs(wl, 102), dev, label="bora_nsa")
 
 
 # --- token top-k (Naive SWA + DSA shape) -------------------------------------
