@@ -53,6 +53,17 @@ def window_pairs_per_head(N, w):
 
 
 def attended_pairs(wl, bsel=None, tsel=None):
+    """(query, key) pairs one call attends: the union of window, blocks and
+    tokens, plus the compressed columns (complete groups of cmp_block tokens
+    at or before the query)."""
+    pairs = _union_pairs(wl, bsel, tsel)
+    if wl.cmp_block:
+        i = np.arange(wl.seq_len, dtype=np.int64)
+        pairs += int(((i + 1) // wl.cmp_block).sum()) * wl.batch * wl.n_q_heads
+    return pairs
+
+
+def _union_pairs(wl, bsel=None, tsel=None):
     Bt, Hq, N = wl.batch, wl.n_q_heads, wl.seq_len
     i = np.arange(N, dtype=np.int64)
     if wl.token_top_k:
@@ -115,7 +126,8 @@ def time_workload(wl, seed, dev, steps, warmup, want_sel=False):
     ws = sa.Workspace()
     kw = dict(block_size=wl.block_size, top_k=wl.top_k, window=wl.window, idx_q=g["idx_q"],
               idx_k=g["idx_k"], token_top_k=wl.token_top_k, sink=g["sink"], workspace=ws,
-              gate_repr=wl.gate_repr, gate_shared=wl.gate_shared, gate_first=wl.gate_first)
+              gate_repr=wl.gate_repr, gate_shared=wl.gate_shared, gate_first=wl.gate_first,
+              cmp_block=wl.cmp_block)
     out = torch.empty_like(g["q"])
     lse = torch.empty(g["q"].shape[:3], dtype=torch.float32, device=dev)
     bsel = tsel = None
@@ -147,7 +159,9 @@ def time_workload(wl, seed, dev, steps, warmup, want_sel=False):
 GATE_VARIANTS = [W.LONG_MOBA.replace(name="long_moba_minmax_n131072", gate_repr="minmax"),
                  W.LONG_MOBA.replace(name="long_moba_shared_n131072", gate_shared=True),
                  W.BORA_HYBRID.replace(name="bora_hybrid_shared_first_n4096", gate_shared=True,
-                                       gate_first=True)]
+                                       gate_first=True),
+                 # the BORA NSA layout: 8:1 compressed branch, one selection per kv group
+                 W.BORA_HYBRID.replace(name="bora_nsa_n4096", cmp_block=8, gate_shared=True)]
 
 
 # Decode/append steps: nq new tokens per sequence after a cache of
