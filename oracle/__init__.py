@@ -82,6 +82,10 @@ def _load(path=None):
                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, _i64,
                                   _i64p, _i64, _f64p, _f64p, _i64p]
     lib.orc_attend_at.restype = ctypes.c_int
+    lib.orc_attend_bwd.argtypes = [_f32p, _f32p, _f32p, _f32p, _i64, _i64, _i64, _i64, _i64,
+                                   ctypes.c_double, _i64, _i64, ctypes.c_void_p, _i64,
+                                   ctypes.c_void_p, _f64p, _f64p, _f64p, _f64p]
+    lib.orc_attend_bwd.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -310,3 +314,49 @@ def forward(q, k, v, *, block_size=0, top_k=0, window=0, idx_q=None, idx_k=None,
                            cmp_block=cmp_block)
     res.update(out=out, lse=lse, count=cnt)
     return res
+
+
+def attend_bwd(q, k, v, dout, *, scale=None, window=0, block_size=0, sel=None, sink=None):
+    """Gradients of sum(dout * out) for a fixed selection: window and kept
+    blocks (sel [Bt*Hq*N, w] per row, or None), sink.  Returns dq
+    [Bt,Hq,N,d], dk, dv [Bt,Hkv,N,d] and dsink [Hq] (None without a sink),
+    all fp64."""
+    q, k, v, dout = _f32(q), _f32(k), _f32(v), _f32(dout)
+    Bt, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape[2] != N or dout.shape != q.shape:
+        raise ValueError("the backward is a prefill: q, k, v, dout over the same positions")
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    sel_a = None if sel is None else np.ascontiguousarray(sel, dtype=np.int32)
+    if sel_a is not None and sel_a.shape[0] != Bt * Hq * N:
+        raise ValueError("sel holds one row per query row")
+    sink_a = None if sink is None else _f32(sink)
+    dq = np.empty((Bt, Hq, N, d), dtype=np.float64)
+    dk = np.empty((Bt, Hkv, N, d), dtype=np.float64)
+    dv = np.empty((Bt, Hkv, N, d), dtype=np.float64)
+    dsink = np.empty(Hq, dtype=np.float64)
+    rc = _load().orc_attend_bwd(
+        q, k, v, dout, Bt, Hq, Hkv, N, d, scale, int(window), int(block_size),
+        None if sel_a is None else sel_a.ctypes.data, 0 if sel_a is None else sel_a.shape[1],
+        None if sink_a is None else sink_a.ctypes.data, dq, dk, dv, dsink)
+    if rc != 0:
+        raise ValueError("selection id out of range")
+    return dq, dk, dv, (dsink if sink is not None else None)
+
+
+def backward(q, k, v, dout, *, block_size=0, top_k=0, window=0, sink=None, scale=None,
+             gate_repr="mean", gate_shared=False, gate_first=False):
+    """Gradients of sum(dout * out) of the prefill with block gating and a
+    window (the selection the forward makes, held fixed).  Returns (dq, dk,
+    dv, dsink, sel)."""
+    Bt, Hq, N, d = np.shape(q)
+    sel = None
+    if top_k > 0:
+        kb = block_pool(k, block_size, gate_repr)
+        sel, _, _ = block_select(q, kb, block_size, top_k, None, gate_repr, gate_shared,
+                                 gate_first)
+    dq, dk, dv, dsink = attend_bwd(q, k, v, dout, scale=scale, window=window,
+                                   block_size=block_size, sel=sel, sink=sink)
+    return dq, dk, dv, dsink, sel

@@ -428,3 +428,108 @@ int orc_attend(const float* q, const float* k, const float* v,
     return orc_attend_at(q, k, v, Hq, Hkv, N, N, d, 0, scale, window, B, sel, sel_w, tsel, tsel_w,
                          sink, NULL, NULL, 0, rows, nrows, out, lse, count);
 }
+
+/*
+ * Backward of the attention for a fixed selection (the gates' top-k choices
+ * are not differentiated; MoBA trains through the attention of the chosen
+ * blocks).  For every row i of A(i) (window and blocks, as orc_attend; no
+ * token or compressed columns) with P_ij = e^(x_ij - lse_i), the sink
+ * column P_i0 = e^(z_h - lse_i), loss gradient dO_i:
+ *   D_i   = sum_e dO_ie out_ie
+ *   dS_ij = P_ij (<dO_i, v_j> - D_i)
+ *   dq_i  = scale sum_j dS_ij k_j,   dk_j += scale dS_ij q_i,
+ *   dv_j += P_ij dO_i,               dsink_h += -P_i0 D_i
+ * (the softmax Jacobian; the sink's value vector is zero).  All rows of q
+ * [Bt, Hq, N, d]; sel is [Bt*Hq*N, sel_w] or NULL; dk, dv [Bt, Hkv, N, d]
+ * sum over the kv group's heads.  Returns 0, or -1 if an id is out of range.
+ */
+int orc_attend_bwd(const float* q, const float* k, const float* v, const float* dout,
+                   int64_t Bt, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                   double scale, int64_t window, int64_t B,
+                   const int32_t* sel, int64_t sel_w, const float* sink,
+                   double* dq, double* dk, double* dv, double* dsink) {
+    const int64_t G = Hq / Hkv;
+    int bad = 0;
+    for (int64_t h = 0; h < Hq; ++h) dsink[h] = 0.0;
+    memset(dk, 0, sizeof(double) * (size_t)(Bt * Hkv * N * d));
+    memset(dv, 0, sizeof(double) * (size_t)(Bt * Hkv * N * d));
+    /* one (batch, kv group) per thread: its dk, dv rows have one writer */
+#pragma omp parallel
+    {
+        unsigned char* mark = (unsigned char*)malloc((size_t)(N > 0 ? N : 1));
+        double* x = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+        double* o = (double*)malloc(sizeof(double) * (size_t)(d > 0 ? d : 1));
+        double* ds_h = (double*)calloc((size_t)Hq, sizeof(double));
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t bg = 0; bg < Bt * Hkv; ++bg) {
+            const int64_t b = bg / Hkv, g = bg % Hkv;
+            const float* kb = k + bg * N * d;
+            const float* vb = v + bg * N * d;
+            double* dkb = dk + bg * N * d;
+            double* dvb = dv + bg * N * d;
+            for (int64_t h = g * G; h < (g + 1) * G; ++h)
+                for (int64_t i = 0; i < N; ++i) {
+                    const int64_t r = (b * Hq + h) * N + i;
+                    memset(mark, 0, (size_t)(i + 1));
+                    if (window > 0)
+                        for (int64_t j = (i - window + 1 > 0 ? i - window + 1 : 0); j <= i; ++j)
+                            mark[j] = 1;
+                    if (sel)
+                        for (int64_t s = 0; s < sel_w; ++s) {
+                            const int64_t c = sel[r * sel_w + s];
+                            if (c < 0) continue;
+                            if (B <= 0 || c >= N / B) { bad = 1; continue; }
+                            for (int64_t j = c * B; j < (c + 1) * B && j <= i; ++j) mark[j] = 1;
+                        }
+                    const float* qrow = q + r * d;
+                    const float* dorow = dout + r * d;
+                    /* forward of the row: logits, lse, out */
+                    double M = -INFINITY;
+                    for (int64_t j = 0; j <= i; ++j) {
+                        if (!mark[j]) continue;
+                        double acc = 0.0;
+                        for (int64_t e = 0; e < d; ++e) acc += (double)qrow[e] * (double)kb[j * d + e];
+                        x[j] = scale * acc;
+                        if (x[j] > M) M = x[j];
+                    }
+                    const double z = sink ? (double)sink[h] : -INFINITY;
+                    if (z > M) M = z;
+                    double L = 0.0;
+                    for (int64_t e = 0; e < d; ++e) o[e] = 0.0;
+                    for (int64_t j = 0; j <= i; ++j) {
+                        if (!mark[j]) continue;
+                        const double p = exp(x[j] - M);
+                        L += p;
+                        for (int64_t e = 0; e < d; ++e) o[e] += p * (double)vb[j * d + e];
+                    }
+                    if (sink) L += exp(z - M);
+                    const double lse = M + log(L);
+                    double Di = 0.0;
+                    for (int64_t e = 0; e < d; ++e) Di += (double)dorow[e] * (o[e] / L);
+                    /* gradients */
+                    double* dqr = dq + r * d;
+                    for (int64_t e = 0; e < d; ++e) dqr[e] = 0.0;
+                    for (int64_t j = 0; j <= i; ++j) {
+                        if (!mark[j]) continue;
+                        const double p = exp(x[j] - lse);
+                        double dp = 0.0;
+                        for (int64_t e = 0; e < d; ++e) dp += (double)dorow[e] * (double)vb[j * d + e];
+                        const double dsij = p * (dp - Di);
+                        for (int64_t e = 0; e < d; ++e) {
+                            dqr[e] += scale * dsij * (double)kb[j * d + e];
+                            dkb[j * d + e] += scale * dsij * (double)qrow[e];
+                            dvb[j * d + e] += p * (double)dorow[e];
+                        }
+                    }
+                    if (sink) ds_h[h] += -exp(z - lse) * Di;
+                }
+        }
+#pragma omp critical
+        for (int64_t h = 0; h < Hq; ++h) dsink[h] += ds_h[h];
+        free(mark);
+        free(x);
+        free(o);
+        free(ds_h);
+    }
+    return bad ? -1 : 0;
+}

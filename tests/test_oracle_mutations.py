@@ -40,6 +40,13 @@ MUTATIONS = [
     ("compressed logit unscaled", [("xc[c] = scale * acc;", "xc[c] = acc;")]),
     ("compressed columns not counted", [("if (xc[c] > M) M = xc[c];\n                ++cnt;",
                                          "if (xc[c] > M) M = xc[c];")]),
+    ("backward drops the D term", [("const double dsij = p * (dp - Di);", "const double dsij = p * dp;")]),
+    ("backward dq without the scale", [("dqr[e] += scale * dsij * (double)kb[j * d + e];",
+                                        "dqr[e] += dsij * (double)kb[j * d + e];")]),
+    ("backward dv from unnormalised weights", [("dvb[j * d + e] += p * (double)dorow[e];",
+                                                "dvb[j * d + e] += exp(x[j] - M) * (double)dorow[e];")]),
+    ("backward sink gradient sign", [("if (sink) ds_h[h] += -exp(z - lse) * Di;",
+                                      "if (sink) ds_h[h] += exp(z - lse) * Di;")]),
     ("sink logit scaled", [("const double z = sink ? (double)sink[h] : -INFINITY;",
                             "const double z = sink ? scale * (double)sink[h] : -INFINITY;")]),
     ("softmax scale dropped", [("x[j] = scale * acc;", "x[j] = acc;")]),
@@ -93,6 +100,11 @@ PIN_CALLS = [
 ] + [
     (lambda c=c, t=t: pins.test_p27_compressed_brute_force(c, t))
     for c in range(len(pins.CMP_CASES)) for t in (False, True)
+] + [
+    (lambda c=c: pins.test_p28_backward_is_autograd(c)) for c in range(len(pins.BWD_CASES))
+] + [
+    lambda: pins.test_p29_backward_matches_finite_differences(),
+    lambda: pins.test_p30_key_gradients_sum_to_sink_term(True),
 ] + [
     (lambda c=c, n=n: pins.test_p15_decode_is_last_prefill_rows(c, n))
     for c in range(len(pins.DECODE_CASES)) for n in (1, 5)

@@ -631,6 +631,125 @@ def test_p27_compressed_brute_force(case, ties):
     np.testing.assert_array_equal(r["count"].reshape(Bt, Hq, N), bcnt)
 
 
+# ---------------------------------------------------------------------------
+# Backward for a fixed selection (MoBA trains through the attention of the
+# chosen blocks; the top-k choice itself has no gradient).
+# ---------------------------------------------------------------------------
+def torch_dense_grads(q, k, v, dout, sel, B, window, sink):
+    """Autograd (fp64, CPU) of sum(dout * out) for the dense attention with
+    the boolean mask of window | kept blocks and the sink as an extra column
+    of zero value."""
+    Bt, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    pos = np.arange(N)
+    causal = pos[None, :] <= pos[:, None]
+    mask = np.zeros((Bt, Hq, N, N), dtype=bool)
+    if window:
+        mask |= (causal & (pos[:, None] - pos[None, :] < window))[None, None]
+    if sel is not None:
+        s3 = sel.reshape(Bt, Hq, N, -1)
+        blk = pos // B
+        for b in range(Bt):
+            for h in range(Hq):
+                for i in range(N):
+                    kept = set(int(c) for c in s3[b, h, i] if c >= 0)
+                    mask[b, h, i] |= np.isin(blk, list(kept)) & (pos <= i)
+    qt, kt, vt = (torch.tensor(a.astype(np.float64), requires_grad=True) for a in (q, k, v))
+    zt = torch.tensor(sink.astype(np.float64), requires_grad=True) if sink is not None else None
+    G = Hq // Hkv
+    kr, vr = kt.repeat_interleave(G, dim=1), vt.repeat_interleave(G, dim=1)
+    logits = torch.matmul(qt, kr.transpose(-1, -2)) / math.sqrt(d)
+    logits = logits.masked_fill(~torch.from_numpy(mask), -math.inf)
+    if zt is not None:
+        col = zt.view(1, Hq, 1, 1).expand(Bt, Hq, N, 1)
+        p = torch.softmax(torch.cat([logits, col], dim=-1), dim=-1)[..., :N]
+    else:
+        p = torch.softmax(logits, dim=-1)
+    out = torch.matmul(p, vr)
+    (out * torch.from_numpy(dout.astype(np.float64))).sum().backward()
+    return (qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy(),
+            None if zt is None else zt.grad.numpy())
+
+
+BWD_CASES = [
+    dict(window=5),
+    dict(block_size=4, top_k=3, sink=True),
+    dict(block_size=4, top_k=2, window=3, sink=True),
+    dict(block_size=2, top_k=4, window=2, gate_repr="minmax", gate_first=True),
+]
+
+
+# P28: the backward equals autograd of the dense masked attention (window |
+# kept blocks, sink column), GQA 4/2.
+@pytest.mark.parametrize("case", range(len(BWD_CASES)))
+def test_p28_backward_is_autograd(case):
+    kw = dict(BWD_CASES[case])
+    use_sink = kw.pop("sink", False)
+    Bt, Hq, Hkv, N, d = 2, 4, 2, 24, 8
+    q, k, v = rnd((Bt, Hq, N, d), 330 + case), rnd((Bt, Hkv, N, d), 340 + case), rnd((Bt, Hkv, N, d), 350)
+    dout = rnd((Bt, Hq, N, d), 360 + case)
+    sink = rnd((Hq,), 370) if use_sink else None
+    dq, dk, dv, dsink, sel = oracle.backward(q, k, v, dout, sink=sink, **kw)
+    tq, tk, tv, tz = torch_dense_grads(q, k, v, dout, sel, kw.get("block_size", 0),
+                                       kw.get("window", 0), sink)
+    for a, b_ in ((dq, tq), (dk, tk), (dv, tv)):
+        np.testing.assert_allclose(a, b_, atol=1e-12)
+    if use_sink:
+        np.testing.assert_allclose(dsink, tz, atol=1e-12)
+
+
+# P29: central finite differences of the oracle's own forward (selection
+# held fixed) agree with its backward on sampled coordinates.
+def test_p29_backward_matches_finite_differences():
+    Bt, Hq, Hkv, N, d, B = 1, 2, 1, 12, 3, 3
+    q, k, v = rnd((Bt, Hq, N, d), 380), rnd((Bt, Hkv, N, d), 381), rnd((Bt, Hkv, N, d), 382)
+    dout, sink = rnd((Bt, Hq, N, d), 383), rnd((Hq,), 384)
+    dq, dk, dv, dsink, sel = oracle.backward(q, k, v, dout, block_size=B, top_k=2, window=2,
+                                             sink=sink)
+
+    def loss(q_, k_, v_, z_):
+        o, _, _ = oracle.attend(q_, k_, v_, window=2, block_size=B, sel=sel, sink=z_)
+        return float((o.reshape(dout.shape) * dout.astype(np.float64)).sum())
+
+    rng = np.random.default_rng(385)
+    for name, arr, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv), ("sink", sink, dsink)):
+        for _ in range(6):
+            idx = tuple(rng.integers(0, s_) for s_ in arr.shape)
+            a_p, a_m = arr.copy(), arr.copy()
+            a_p[idx] += np.float32(1e-3)
+            a_m[idx] -= np.float32(1e-3)
+            args_p = dict(q=q, k=k, v=v, z=sink); args_m = dict(args_p)
+            key = {"q": "q", "k": "k", "v": "v", "sink": "z"}[name]
+            args_p[key], args_m[key] = a_p, a_m
+            fd = (loss(args_p["q"], args_p["k"], args_p["v"], args_p["z"]) -
+                  loss(args_m["q"], args_m["k"], args_m["v"], args_m["z"])) / \
+                 (float(a_p[idx]) - float(a_m[idx]))
+            assert abs(fd - grad[idx]) <= 1e-5 * max(1.0, abs(grad[idx])), (name, idx, fd, grad[idx])
+
+
+# P30: shifting all logits of a row leaves its output unchanged, so the
+# score gradients of a row sum to minus that of its sink column: summed over
+# the keys of a kv group, dk = scale * sum_i q_i P_i,sink D_i (zero without a
+# sink).
+@pytest.mark.parametrize("use_sink", [False, True])
+def test_p30_key_gradients_sum_to_sink_term(use_sink):
+    Bt, Hq, Hkv, N, d = 2, 4, 2, 32, 8
+    q, k, v = rnd((Bt, Hq, N, d), 390), rnd((Bt, Hkv, N, d), 391), rnd((Bt, Hkv, N, d), 392)
+    dout = rnd((Bt, Hq, N, d), 393)
+    sink = rnd((Hq,), 394) if use_sink else None
+    dq, dk, dv, dsink, sel = oracle.backward(q, k, v, dout, block_size=4, top_k=3, window=4,
+                                             sink=sink)
+    want = np.zeros((Bt, Hkv, d))
+    if use_sink:
+        o, lse, _ = oracle.attend(q, k, v, window=4, block_size=4, sel=sel, sink=sink)
+        o, lse = o.reshape(Bt, Hq, N, d), lse.reshape(Bt, Hq, N)
+        D = (o * dout).sum(-1)
+        p0 = np.exp(sink[None, :, None] - lse)
+        w = (p0 * D)[..., None] * q.astype(np.float64) / math.sqrt(d)   # [Bt, Hq, N, d]
+        want = w.reshape(Bt, Hkv, Hq // Hkv, N, d).sum(axis=(2, 3))
+    np.testing.assert_allclose(dk.sum(axis=2), want, atol=1e-12)
+
+
 def test_gate_variant_arguments_checked():
     q, k = rnd((1, 2, 16, 4), 313), rnd((1, 2, 16, 4), 314)
     with pytest.raises(ValueError):
