@@ -9,7 +9,10 @@ import oracle
 import test_oracle_pins as pins
 
 MUTATIONS = [
-    ("window admits w+1 keys", [("(i - window + 1 > 0 ? i - window + 1 : 0)", "(i - window > 0 ? i - window : 0)")]),
+    ("window admits w+1 keys", [("\n            if (window > 0)\n                for (int64_t j = (i - window + 1 > 0 ? i - window + 1 : 0)",
+                                 "\n            if (window > 0)\n                for (int64_t j = (i - window > 0 ? i - window : 0)")]),
+    ("backward window admits w+1 keys", [("                    if (window > 0)\n                        for (int64_t j = (i - window + 1 > 0 ? i - window + 1 : 0)",
+                                          "                    if (window > 0)\n                        for (int64_t j = (i - window > 0 ? i - window : 0)")]),
     ("tie goes to the higher index", [("if (a->idx < b->idx) return -1;", "if (a->idx < b->idx) return 1;")]),
     ("own block not counted in k", [("int64_t m = top_k - 1 - c0;", "int64_t m = top_k - c0;")]),
     ("own block competes instead of being forced", [
@@ -47,9 +50,11 @@ MUTATIONS = [
                                                 "dvb[j * d + e] += exp(x[j] - M) * (double)dorow[e];")]),
     ("backward sink gradient sign", [("if (sink) ds_h[h] += -exp(z - lse) * Di;",
                                       "if (sink) ds_h[h] += exp(z - lse) * Di;")]),
-    ("sink logit scaled", [("const double z = sink ? (double)sink[h] : -INFINITY;",
-                            "const double z = sink ? scale * (double)sink[h] : -INFINITY;")]),
-    ("softmax scale dropped", [("x[j] = scale * acc;", "x[j] = acc;")]),
+    ("sink logit scaled", [("\n            const double z = sink ? (double)sink[h] : -INFINITY;",
+                            "\n            const double z = sink ? scale * (double)sink[h] : -INFINITY;")]),
+    ("softmax scale dropped", [("\n                x[j] = scale * acc;", "\n                x[j] = acc;")]),
+    ("backward softmax scale dropped", [("                        x[j] = scale * acc;",
+                                         "                        x[j] = acc;")]),
     ("wrong GQA head mapping", [("b = bh / Hq, h = bh % Hq, g = h / G;\n            memset",
                                  "b = bh / Hq, h = bh % Hq, g = h % Hkv;\n            memset")]),
     ("token candidates include j = i", [
