@@ -7,7 +7,8 @@ resident in HBM.  Also reported (same JSON line, "workloads"): the other
 synthetic workloads, each a full forward (pool, gate, compaction, far-block
 and near attention) timed the same way, the block-gate variants (min/max
 block summary, selection shared per kv group, first block kept) on the
-block-gated shapes, and two decode/append steps (new
+block-gated shapes, backward calls (gradients for the forward's selection) on
+the BORA, Bit-Axon SWA and long MoBA shapes, and two decode/append steps (new
 tokens after a resident KV cache) reported as step time and algorithmic HBM
 bytes per step against the 8 TB/s peak.
 
@@ -162,6 +163,40 @@ GATE_VARIANTS = [W.LONG_MOBA.replace(name="long_moba_minmax_n131072", gate_repr=
                                        gate_first=True),
                  # the BORA NSA layout: 8:1 compressed branch, one selection per kv group
                  W.BORA_HYBRID.replace(name="bora_nsa_n4096", cmp_block=8, gate_shared=True)]
+
+
+# Backward calls (gradients for the forward's selection) on the window and
+# block-gated shapes.
+BACKWARD = [W.BORA_HYBRID, W.BITAXON_SWA, W.LONG_MOBA]
+
+
+def time_backward(wl, seed, dev, steps, warmup):
+    """Time sparse_attn_bwd after one forward; returns (ms, stage_ms,
+    attended pairs)."""
+    import torch
+    import sliding_window_long_amd as sa
+    inp, g = device_inputs(wl, seed, dev)
+    kw = dict(block_size=wl.block_size, top_k=wl.top_k, window=wl.window, sink=g["sink"],
+              gate_repr=wl.gate_repr, gate_shared=wl.gate_shared, gate_first=wl.gate_first)
+    out, lse, bsel, _ = sa.forward(g["q"], g["k"], g["v"], return_selection=True, **kw)
+    dout = torch.randn(g["q"].shape, dtype=torch.float32, device=dev,
+                       generator=torch.Generator(device=dev).manual_seed(seed)).to(torch.bfloat16)
+    ws = sa.Workspace()
+    for _ in range(warmup):
+        sa.backward(g["q"], g["k"], g["v"], out, lse, dout, workspace=ws, **kw)
+    torch.cuda.synchronize()
+    sa.sparse_attn_set_timing(True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        sa.backward(g["q"], g["k"], g["v"], out, lse, dout, workspace=ws, **kw)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    sa.sparse_attn_set_timing(False)
+    stages = {}
+    for name, ms in sa.sparse_attn_stage_times(1024):
+        stages.setdefault(name, []).append(ms)
+    pairs = attended_pairs(wl, None if bsel is None else bsel.cpu().numpy())
+    return (t1 - t0) * 1e3 / steps, {k: float(np.mean(v)) for k, v in stages.items()}, pairs
 
 
 # Decode/append steps: nq new tokens per sequence after a cache of
@@ -319,6 +354,15 @@ def main():
                                "attended_tflops": ef / (ems * 1e-3) / 1e12,
                                "pct_of_bf16_peak": 100 * ef / (ems * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                                "stage_ms": est}
+        for bwl in BACKWARD:
+            print(f"[bench] backward {bwl.name}", file=sys.stderr, flush=True)
+            bms, bst, bpairs = time_backward(bwl, 11, dev, args.extra_steps, 2)
+            bflops = 10.0 * bwl.head_dim * bpairs   # S, dP, dQ, dK, dV: 2d FLOP each per pair
+            extra[bwl.name + "_bwd"] = {"ms_per_step": bms,
+                                        "tokens_per_s": bwl.batch * bwl.seq_len / (bms * 1e-3),
+                                        "attended_tflops": bflops / (bms * 1e-3) / 1e12,
+                                        "pct_of_bf16_peak": 100 * bflops / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                                        "stage_ms": bst}
         for dwl, nq in DECODE:
             print(f"[bench] decode {dwl.name}", file=sys.stderr, flush=True)
             dms, dst, dbytes = time_decode(dwl, nq, 7, dev, 50, 5)

@@ -164,6 +164,28 @@ int sparse_attn_fwd(const void* q, const void* k, const void* v,
  * Same checks as sparse_attn_fwd. */
 int sparse_attn_block_pool(const void* k, const sparse_attn_cfg* cfg, float* kbar);
 
+/* Backward of sparse_attn_fwd for the selection it makes [MoBA summary
+ * page: the model trains through the attention of the selected blocks; the
+ * gates' top-k choices carry no gradient]: with P_ij = e^(x_ij - lse_i) over
+ * the forward's attended set (window, own block, kept blocks, sink column),
+ * D_i = <dout_i, out_i> and dS_ij = P_ij (<dout_i, v_j> - D_i):
+ *   dq_i = scale sum_j dS_ij k_j,  dk_j = scale sum_i dS_ij q_i (summed over
+ *   the kv group's heads),  dv_j = sum_i P_ij dout_i,
+ *   dsink[h] = -sum_i e^(sink[h] - lse_i) D_i.
+ * Same cfg as the forward call (the selection is recomputed, bit-identical;
+ * block_sel_out, if set, receives it again).  q, k, v, out (the forward's
+ * output), dout, dq [batch, n_q_heads, seq_len, head_dim], dk, dv [batch,
+ * n_kv_heads, seq_len, head_dim]: bf16, device, 16-byte aligned; lse the
+ * forward's fp32 lse; dsink [n_q_heads] fp32 or NULL (needs cfg->sink).
+ * Supported: bf16 prefills with a window and/or block gating (any gate
+ * variant); a token gate, the compressed branch, fp32 or a decode step
+ * return SA_E_UNSUPPORTED.  Workspace from sparse_attn_bwd_workspace_bytes;
+ * enqueued on cfg->stream, no host sync, nothing allocated. */
+int sparse_attn_bwd_workspace_bytes(const sparse_attn_cfg* cfg, size_t* bytes);
+int sparse_attn_bwd(const void* q, const void* k, const void* v, const void* out,
+                    const float* lse, const void* dout, const sparse_attn_cfg* cfg,
+                    void* dq, void* dk, void* dv, float* dsink);
+
 /* Static description of an error code. */
 const char* sparse_attn_strerror(int status);
 

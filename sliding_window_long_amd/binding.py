@@ -28,7 +28,8 @@ ERROR_CODES = {
 }
 # Every symbol the C header declares.
 EXPORTS = ("sparse_attn_workspace_bytes", "sparse_attn_fwd", "sparse_attn_block_pool",
-           "sparse_attn_strerror", "sparse_attn_set_timing", "sparse_attn_stage_times")
+           "sparse_attn_strerror", "sparse_attn_set_timing", "sparse_attn_stage_times",
+           "sparse_attn_bwd_workspace_bytes", "sparse_attn_bwd")
 
 
 class SparseAttnCfg(ctypes.Structure):
@@ -85,6 +86,10 @@ def load_library():
     lib.sparse_attn_stage_times.argtypes = [P(ctypes.c_int32), P(ctypes.c_char_p),
                                             P(ctypes.c_float), ctypes.c_int32]
     lib.sparse_attn_stage_times.restype = ctypes.c_int
+    lib.sparse_attn_bwd_workspace_bytes.argtypes = [P(SparseAttnCfg), P(ctypes.c_size_t)]
+    lib.sparse_attn_bwd_workspace_bytes.restype = ctypes.c_int
+    lib.sparse_attn_bwd.argtypes = [ctypes.c_void_p] * 6 + [P(SparseAttnCfg)] + [ctypes.c_void_p] * 4
+    lib.sparse_attn_bwd.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -134,6 +139,13 @@ def sparse_attn_workspace_bytes(cfg: SparseAttnCfg) -> int:
     n = ctypes.c_size_t(0)
     _check(load_library().sparse_attn_workspace_bytes(ctypes.byref(cfg), ctypes.byref(n)),
            "sparse_attn_workspace_bytes")
+    return n.value
+
+
+def sparse_attn_bwd_workspace_bytes(cfg: SparseAttnCfg) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load_library().sparse_attn_bwd_workspace_bytes(ctypes.byref(cfg), ctypes.byref(n)),
+           "sparse_attn_bwd_workspace_bytes")
     return n.value
 
 
@@ -269,3 +281,37 @@ def block_pool(k, block_size: int, gate_repr: str = "mean"):
     kbar = torch.empty(shape, dtype=torch.float32, device=k.device)
     sparse_attn_block_pool(k, cfg, kbar)
     return kbar
+
+
+def backward(q, k, v, out, lse, dout, *, block_size=0, top_k=0, window=0, sink=None, scale=None,
+             gate_repr="mean", gate_shared=False, gate_first=False,
+             workspace: Workspace | None = None):
+    """Gradients of the prefill for the selection the forward makes (same
+    arguments as forward; out and lse are its results, dout the gradient of
+    out).  bf16 tensors on one device; returns (dq, dk, dv, dsink), dsink
+    None without a sink."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be a contiguous bfloat16 device tensor")
+    if lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 device tensor")
+    p = params_for(q, k, block_size=block_size, top_k=top_k, window=window, scale=scale,
+                   gate_repr=gate_repr, gate_shared=gate_shared, gate_first=gate_first)
+    cfg = p.cfg()
+    dev = q.device
+    if sink is not None:
+        if sink.dtype != torch.float32 or not sink.is_cuda:
+            raise TypeError("sink must be a float32 device tensor")
+        cfg.sink = sink.data_ptr()
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dsink = None if sink is None else torch.empty_like(sink)
+    nbytes = sparse_attn_bwd_workspace_bytes(cfg)
+    ws = (workspace or _default_ws).get(nbytes, dev)
+    cfg.workspace = None if ws is None else ws.data_ptr()
+    cfg.workspace_bytes = nbytes
+    cfg.stream = torch.cuda.current_stream(dev).cuda_stream
+    _check(load_library().sparse_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                          _ptr(dout), ctypes.byref(cfg), _ptr(dq), _ptr(dk),
+                                          _ptr(dv), _ptr(dsink)), "sparse_attn_bwd")
+    return dq, dk, dv, dsink

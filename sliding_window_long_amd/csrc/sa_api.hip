@@ -45,13 +45,16 @@ struct Plan {
     size_t o_split, o_kb3, o_sel, o_count, o_cursor, o_listoff, o_nchunks, o_chunk_list,
         o_chunk_start, o_entries, o_part_o, o_part_lse, o_tok_split, o_tok_state, o_tok_mask,
         o_tok_qn, o_tok_win, o_tok_kpart, o_tok_scr, o_tok_nslow, o_dec_scores, o_dec_list,
-        o_dec_nfar, o_dec_part, o_qsum, o_cmp_k, o_cmp_v, o_cmp_out,
+        o_dec_nfar, o_dec_part, o_qsum, o_cmp_k, o_cmp_v, o_cmp_out, o_k16, o_q16, o_do16,
+        o_delta,
         o_v16, total;
 };
 
 bool misaligned(const void* p, size_t a) { return p && (reinterpret_cast<uintptr_t>(p) % a) != 0; }
 
-int make_plan(const sparse_attn_cfg* c, Plan* p) {
+// bwd: plan of the backward call (the forward's selection and far-row lists,
+// no far partials; fp16 copies of q, k, dO and the row deltas).
+int make_plan(const sparse_attn_cfg* c, Plan* p, bool bwd = false) {
     if (!c || c->struct_size != sizeof(sparse_attn_cfg)) return SA_E_INVALID_ARG;
     if (c->batch < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 || c->seq_len < 1)
         return SA_E_INVALID_ARG;
@@ -83,6 +86,9 @@ int make_plan(const sparse_attn_cfg* c, Plan* p) {
     // The compressed branch joins window / block gating (the NSA layout), not
     // the token gate.
     if (c->cmp_block > 0 && c->token_top_k > 0) return SA_E_UNSUPPORTED;
+    // The backward covers window and block gating on bf16 prefills.
+    if (bwd && (dec || c->dtype != SA_BF16 || c->token_top_k > 0 || c->cmp_block > 0))
+        return SA_E_UNSUPPORTED;
     if (c->token_top_k > 0) {
         if (c->index_dim != 64) return SA_E_UNSUPPORTED_HEAD_DIM;
         // 16 index bits in the selection key; block and token gates are
@@ -166,8 +172,15 @@ int make_plan(const sparse_attn_cfg* c, Plan* p) {
     size_t off = 0;
     auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
     const size_t nq = (size_t)rows * P.D, nkv = (size_t)P.Bt * P.Hkv * P.N * P.D;
-    P.o_split = take(P.f32 ? 2 * (nq + 2 * nkv) * 2 : 0);
-    P.o_v16 = take(P.f32 ? 0 : nkv * 2);   // fp16 copy of V for the P V products
+    if (bwd) {
+        P.o_k16 = take(nkv * 2);
+        P.o_q16 = take(nq * 2);
+        P.o_do16 = take(nq * 2);
+        P.o_delta = take((size_t)rows * 4);
+    } else {
+        P.o_split = take(P.f32 ? 2 * (nq + 2 * nkv) * 2 : 0);
+        P.o_v16 = take(P.f32 ? 0 : nkv * 2);   // fp16 copy of V for the P V products
+    }
     if (P.gate) {
         P.o_kb3 = take((size_t)P.gate_planes * P.lists * P.D * 2);
         P.o_qsum = take(P.gate_shared ? (size_t)(P.gate_mm ? 4 : 2) * P.Bt * P.Hkv * P.N * P.D * 2
@@ -181,8 +194,10 @@ int make_plan(const sparse_attn_cfg* c, Plan* p) {
             P.o_chunk_list = take((size_t)P.max_chunks * 4);
             P.o_chunk_start = take((size_t)P.max_chunks * 4);
             P.o_entries = take((size_t)P.max_entries * 4);
-            P.o_part_o = take((size_t)rows * P.kslots * P.D * 2);
-            P.o_part_lse = take((size_t)rows * P.kslots * 4);
+            if (!bwd) {
+                P.o_part_o = take((size_t)rows * P.kslots * P.D * 2);
+                P.o_part_lse = take((size_t)rows * P.kslots * 4);
+            }
         }
     }
     P.cmp = c->cmp_block > 0;
@@ -243,6 +258,59 @@ struct StageScope {
         if (idx >= 0) hipEventRecord(g_timing.ev[idx][1], s);
     }
 };
+
+
+// Block selection (pool, group sums for a shared gate, gate) into sel.
+int select_blocks(const Plan& P, const void* q, const void* k, const uint16_t* const* qp, int split,
+                  char* ws, int32_t* sel, hipStream_t s) {
+    auto ok = [](hipError_t e) { return e == hipSuccess; };
+    uint16_t* kb3 = (uint16_t*)(ws + P.o_kb3);
+    const size_t plane = (size_t)P.lists * P.D;
+    {
+        sa::PoolArgs pa{k, P.N, P.B, P.n, nullptr, kb3, plane, P.gate_mm ? 1 : 0};
+        StageScope t("block_pool", s);
+        if (!ok(sa::launch_pool(pa, P.D, P.f32, P.lists, s))) return SA_E_HIP;
+    }
+    sa::GateArgs ga{{qp[0], qp[1], nullptr, nullptr}, kb3, plane, sel, P.Bt, P.Hq, P.Hkv,
+                    P.N, P.B, P.n, P.top_k, P.idx_bits, 1, P.gate_first ? 1 : 0};
+    int gate_split = split;
+    if (P.gate_shared) {
+        // One gate row per (batch, kv group, position) on the group's summed
+        // query (bf16 hi + lo; for min/max the summed positive and negative
+        // parts), its selection written to every head of the group.
+        const size_t plane_q = (size_t)P.Bt * P.Hkv * P.N * P.D;
+        uint16_t* qs = (uint16_t*)(ws + P.o_qsum);
+        sa::GroupSumArgs gs{q, {qs, qs + plane_q, qs + 2 * plane_q, qs + 3 * plane_q},
+                            P.Bt, P.Hq, P.Hkv, P.N, P.D, P.gate_mm ? 1 : 0};
+        StageScope t("group_sum", s);
+        if (!ok(sa::launch_group_sum(gs, P.f32, s))) return SA_E_HIP;
+        for (int x = 0; x < 4; ++x) ga.q[x] = gs.out[x];
+        ga.Hq = P.Hkv; ga.rep = P.G;
+        gate_split = P.gate_mm ? 4 : 2;
+    }
+    StageScope t("block_gate", s);
+    return ok(sa::launch_gate(ga, P.D, gate_split, P.gate_planes, P.gate_mm, s)) ? SA_OK : SA_E_HIP;
+}
+
+// Per-(batch, kv head, block) lists of the rows that keep that block as a
+// far block, and their chunking.
+int compact_far(const Plan& P, const int32_t* sel, char* ws, hipStream_t s, sa::CompactArgs* out) {
+    sa::CompactArgs& ca = *out;
+    ca = sa::CompactArgs{};
+    ca.sel = sel; ca.Bt = P.Bt; ca.Hq = P.Hq; ca.Hkv = P.Hkv; ca.N = P.N; ca.B = P.B;
+    ca.n = P.n; ca.top_k = P.top_k; ca.span = P.span; ca.kslots = P.kslots;
+    ca.count = (int32_t*)(ws + P.o_count);
+    ca.cursor = (int32_t*)(ws + P.o_cursor);
+    ca.list_off = (int32_t*)(ws + P.o_listoff);
+    ca.entries = (int32_t*)(ws + P.o_entries);
+    ca.chunk_list = (int32_t*)(ws + P.o_chunk_list);
+    ca.chunk_start = (int32_t*)(ws + P.o_chunk_start);
+    ca.n_chunks = (int32_t*)(ws + P.o_nchunks);
+    ca.max_chunks = P.max_chunks;
+    ca.rows_per_chunk = kRowsPerChunk;
+    StageScope t("compact", s);
+    return sa::launch_compact(ca, s) == hipSuccess ? SA_OK : SA_E_HIP;
+}
 
 }  // namespace
 
@@ -382,55 +450,14 @@ int sparse_attn_fwd(const void* q, const void* k, const void* v, const sparse_at
     float* part_lse = nullptr;
     if (P.gate) {
         sel = cfg->block_sel_out ? cfg->block_sel_out : (int32_t*)(ws + P.o_sel);
-        uint16_t* kb3 = (uint16_t*)(ws + P.o_kb3);
-        const size_t plane = (size_t)P.lists * P.D;
-        {
-            sa::PoolArgs pa{k, P.N, P.B, P.n, nullptr, kb3, plane, P.gate_mm ? 1 : 0};
-            StageScope t("block_pool", s);
-            if (!ok(sa::launch_pool(pa, P.D, P.f32, P.lists, s))) return SA_E_HIP;
-        }
-        sa::GateArgs ga{{qp[0], qp[1], nullptr, nullptr}, kb3, plane, sel, P.Bt, P.Hq, P.Hkv,
-                        P.N, P.B, P.n, P.top_k, P.idx_bits, 1, P.gate_first ? 1 : 0};
-        int gate_split = split;
-        if (P.gate_shared) {
-            // One gate row per (batch, kv group, position) on the group's
-            // summed query (bf16 hi + lo; for min/max the summed positive
-            // and negative parts), its selection written to every head of
-            // the group.
-            const size_t plane_q = (size_t)P.Bt * P.Hkv * P.N * P.D;
-            uint16_t* qs = (uint16_t*)(ws + P.o_qsum);
-            sa::GroupSumArgs gs{q, {qs, qs + plane_q, qs + 2 * plane_q, qs + 3 * plane_q},
-                                P.Bt, P.Hq, P.Hkv, P.N, P.D, P.gate_mm ? 1 : 0};
-            StageScope t("group_sum", s);
-            if (!ok(sa::launch_group_sum(gs, P.f32, s))) return SA_E_HIP;
-            for (int x = 0; x < 4; ++x) ga.q[x] = gs.out[x];
-            ga.Hq = P.Hkv; ga.rep = P.G;
-            gate_split = P.gate_mm ? 4 : 2;
-        }
-        {
-            StageScope t("block_gate", s);
-            if (!ok(sa::launch_gate(ga, P.D, gate_split, P.gate_planes, P.gate_mm, s)))
-                return SA_E_HIP;
-        }
+        const int rc_gate = select_blocks(P, q, k, qp, split, ws, sel, s);
+        if (rc_gate != SA_OK) return rc_gate;
         if (P.far) {
             part_o = (uint16_t*)(ws + P.o_part_o);
             part_lse = (float*)(ws + P.o_part_lse);
             sa::CompactArgs ca{};
-            ca.sel = sel; ca.Bt = P.Bt; ca.Hq = P.Hq; ca.Hkv = P.Hkv; ca.N = P.N; ca.B = P.B;
-            ca.n = P.n; ca.top_k = P.top_k; ca.span = P.span; ca.kslots = P.kslots;
-            ca.count = (int32_t*)(ws + P.o_count);
-            ca.cursor = (int32_t*)(ws + P.o_cursor);
-            ca.list_off = (int32_t*)(ws + P.o_listoff);
-            ca.entries = (int32_t*)(ws + P.o_entries);
-            ca.chunk_list = (int32_t*)(ws + P.o_chunk_list);
-            ca.chunk_start = (int32_t*)(ws + P.o_chunk_start);
-            ca.n_chunks = (int32_t*)(ws + P.o_nchunks);
-            ca.max_chunks = P.max_chunks;
-            ca.rows_per_chunk = kRowsPerChunk;
-            {
-                StageScope t("compact", s);
-                if (!ok(sa::launch_compact(ca, s))) return SA_E_HIP;
-            }
+            const int rc_comp = compact_far(P, sel, ws, s, &ca);
+            if (rc_comp != SA_OK) return rc_comp;
             sa::BlocksArgs ba{};
             for (int i = 0; i < 2; ++i) { ba.q[i] = qp[i]; ba.k[i] = kp[i]; ba.v[i] = vp[i]; }
             ba.Bt = P.Bt; ba.Hq = P.Hq; ba.Hkv = P.Hkv; ba.N = P.N; ba.B = P.B; ba.n = P.n;
@@ -517,6 +544,79 @@ int sparse_attn_fwd(const void* q, const void* k, const void* v, const sparse_at
         if (!ok(sa::launch_cmp(ca, P.D, split, s))) return SA_E_HIP;
     }
     return SA_OK;
+}
+
+int sparse_attn_bwd_workspace_bytes(const sparse_attn_cfg* cfg, size_t* bytes) {
+    if (!bytes) return SA_E_INVALID_ARG;
+    Plan P;
+    const int rc = make_plan(cfg, &P, true);
+    if (rc != SA_OK) return rc;
+    *bytes = P.total;
+    return SA_OK;
+}
+
+int sparse_attn_bwd(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                    const void* dout, const sparse_attn_cfg* cfg, void* dq, void* dk, void* dv,
+                    float* dsink) {
+    Plan P;
+    int rc = make_plan(cfg, &P, true);
+    if (rc != SA_OK) return rc;
+    if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv) return SA_E_INVALID_ARG;
+    if (dsink && !cfg->sink) return SA_E_INVALID_ARG;
+    if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(out, 16) ||
+        misaligned(dout, 16) || misaligned(dq, 16) || misaligned(dk, 16) || misaligned(dv, 16) ||
+        misaligned(cfg->workspace, 16) || misaligned(lse, 4) || misaligned(dsink, 4) ||
+        misaligned(cfg->sink, 4) || misaligned(cfg->block_sel_out, 4))
+        return SA_E_ALIGNMENT;
+    if ((long long)P.Bt * P.Hq * P.N >= (1LL << 31)) return SA_E_UNSUPPORTED;   // 32-bit row ids
+    if (P.total > 0 && (!cfg->workspace || cfg->workspace_bytes < P.total))
+        return SA_E_WORKSPACE_TOO_SMALL;
+    hipStream_t s = (hipStream_t)cfg->stream;
+    char* ws = (char*)cfg->workspace;
+    auto ok = [](hipError_t e) { return e == hipSuccess; };
+
+    // The forward's selection and far-row lists (deterministic kernels).
+    int32_t* sel = nullptr;
+    sa::CompactArgs ca{};
+    if (P.gate) {
+        sel = cfg->block_sel_out ? cfg->block_sel_out : (int32_t*)(ws + P.o_sel);
+        const uint16_t* qp[2] = {(const uint16_t*)q, nullptr};
+        rc = select_blocks(P, q, k, qp, 1, ws, sel, s);
+        if (rc != SA_OK) return rc;
+        if (P.far) {
+            rc = compact_far(P, sel, ws, s, &ca);
+            if (rc != SA_OK) return rc;
+        }
+    }
+    const size_t nq = (size_t)P.Bt * P.Hq * P.N * P.D, nkv = (size_t)P.Bt * P.Hkv * P.N * P.D;
+    uint16_t* k16 = (uint16_t*)(ws + P.o_k16);
+    uint16_t* q16 = (uint16_t*)(ws + P.o_q16);
+    uint16_t* do16 = (uint16_t*)(ws + P.o_do16);
+    {
+        StageScope t("bwd_to_f16", s);
+        if (!ok(sa::launch_bf16_to_f16((const uint16_t*)k, k16, nkv, s)) ||
+            !ok(sa::launch_bf16_to_f16((const uint16_t*)q, q16, nq, s)) ||
+            !ok(sa::launch_bf16_to_f16((const uint16_t*)dout, do16, nq, s)))
+            return SA_E_HIP;
+    }
+    sa::BwdArgs ba{};
+    ba.q = (const uint16_t*)q; ba.k = (const uint16_t*)k; ba.v = (const uint16_t*)v;
+    ba.out = (const uint16_t*)out; ba.dout = (const uint16_t*)dout;
+    ba.q16 = q16; ba.k16 = k16; ba.do16 = do16;
+    ba.lse = lse; ba.delta = (float*)(ws + P.o_delta);
+    ba.sink = cfg->sink; ba.dsink = dsink;
+    ba.dq = (uint16_t*)dq; ba.dk = (uint16_t*)dk; ba.dv = (uint16_t*)dv;
+    ba.sel = sel; ba.top_k = P.top_k; ba.B = P.B; ba.n = P.n; ba.span = P.span;
+    ba.kslots = P.kslots;
+    ba.list_off = P.far ? ca.list_off : nullptr; ba.entries = P.far ? ca.entries : nullptr;
+    ba.Bt = P.Bt; ba.Hq = P.Hq; ba.Hkv = P.Hkv; ba.N = P.N; ba.D = P.D; ba.window = cfg->window;
+    ba.scale = P.scale;
+    {
+        StageScope t("bwd_delta", s);
+        if (!ok(sa::launch_bwd_delta(ba, s))) return SA_E_HIP;
+    }
+    StageScope t("bwd_attn", s);
+    return ok(sa::launch_bwd(ba, P.D, s)) ? SA_OK : SA_E_HIP;
 }
 
 }  // extern "C"

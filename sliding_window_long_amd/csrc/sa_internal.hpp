@@ -122,6 +122,35 @@ struct CmpArgs {
     int out_f32;
 };
 
+// Backward (bf16): inputs, fp16 copies for the P V-style products, the
+// forward's lse, the selection and far-row lists, and the gradients.
+struct BwdArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const uint16_t* out;    // forward output
+    const uint16_t* dout;   // gradient of the output
+    const uint16_t* q16;    // fp16 copies [same layouts]
+    const uint16_t* k16;
+    const uint16_t* do16;
+    const float* lse;       // forward lse [Bt*Hq*N]
+    float* delta;           // D_i [Bt*Hq*N]
+    const float* sink;      // [Hq] or nullptr
+    float* dsink;           // [Hq] or nullptr
+    uint16_t* dq;
+    uint16_t* dk;
+    uint16_t* dv;
+    const int32_t* sel;     // [Bt*Hq*N, top_k] or nullptr (no block gate)
+    const int32_t* list_off;  // far-row lists of the compaction, or nullptr
+    const int32_t* entries;
+    int top_k, B, n, span, kslots;
+    int Bt, Hq, Hkv, N, D, window;
+    float scale;
+};
+
+hipError_t launch_bwd_delta(const BwdArgs& a, hipStream_t s);
+hipError_t launch_bwd(const BwdArgs& a, int head_dim, hipStream_t s);
+
 hipError_t launch_cmp_pool(const CmpPoolArgs& a, bool f32_in, hipStream_t s);
 hipError_t launch_cmp(const CmpArgs& a, int head_dim, int split, hipStream_t s);
 

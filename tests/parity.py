@@ -154,3 +154,38 @@ def check(inp, dev_out, dev_lse, rows, dev_bsel=None, dev_tsel=None, *, kbar=Non
     rep.ref_out_absmax = float(np.abs(ref_out).max()) if err.size else 0.0
     rep.attended_pairs = int(res["count"].sum())
     return rep
+
+
+# Gradients (bf16 outputs; fp16 P and dS operands; D_i from the bf16 forward
+# output): per tensor, max |g - g*| <= 2e-2 S_max and mean |g - g*| <=
+# 1e-2 S_mean, S = the tensor's own max |g*| (mean |g*|), floored at 1e-2 of
+# the largest of dq, dk, dv: where the softmax Jacobian cancels (a row with
+# one key has dq = dk = 0 exactly) the error is judged against the call's
+# gradient scale, not against zero.
+GRAD_MAX, GRAD_MEAN = 2e-2, 1e-2
+
+
+def check_grads(inp, dout, dev_sel, dev_grads, *, sink=None):
+    """Compare device (dq, dk, dv, dsink) with the oracle's backward under the
+    device's own block selection.  Returns {name: (max_rel, mean_rel)}."""
+    wl = inp.wl
+    sel = None if dev_sel is None else dev_sel.reshape(-1, wl.top_k)
+    ref = oracle.attend_bwd(inp.q, inp.k, inp.v, dout, window=wl.window,
+                            block_size=wl.block_size, sel=sel, sink=sink)
+    joint_max = max(float(np.abs(r).max()) for r in ref[:3])
+    joint_mean = max(float(np.abs(r).mean()) for r in ref[:3])
+    res = {}
+    for name, g, r in zip(("dq", "dk", "dv", "dsink"), dev_grads, ref):
+        if r is None:
+            continue
+        g = np.asarray(g, dtype=np.float64)
+        err = np.abs(g - r)
+        floor_max = 1e-2 * joint_max if name != "dsink" else 1e-30
+        floor_mean = 1e-2 * joint_mean if name != "dsink" else 1e-30
+        res[name] = (float(err.max() / max(np.abs(r).max(), floor_max)),
+                     float(err.mean() / max(np.abs(r).mean(), floor_mean)))
+    return res
+
+
+def grads_ok(res) -> bool:
+    return all(m <= GRAD_MAX and a <= GRAD_MEAN for m, a in res.values())

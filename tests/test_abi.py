@@ -204,3 +204,32 @@ def test_strerror_covers_codes(lib):
 
 def test_stage_times_without_timing(lib):
     assert isinstance(sa.sparse_attn_stage_times(), list)
+
+
+def test_backward_configs(lib):
+    ws = lambda p: sa.load_library().sparse_attn_bwd_workspace_bytes(
+        ctypes.byref(p.cfg()), ctypes.byref(ctypes.c_size_t()))
+    assert ws(sa.Params(2, 8, 4, 4096, 128, block_size=128, top_k=16, window=512)) == 0
+    assert ws(sa.Params(1, 32, 32, 16384, 80, window=4096)) == 0
+    assert ws(sa.Params(1, 2, 2, 512, 64, dtype=sa.SA_F32, window=8)) == -8           # fp32
+    assert ws(sa.Params(1, 4, 1, 256, 128, window=8, token_top_k=16, index_dim=64)) == -8
+    assert ws(sa.Params(1, 4, 4, 256, 64, window=8, cmp_block=8)) == -8
+    assert ws(sa.Params(1, 4, 4, 1, 64, window=8, kv_len=256)) == -8                 # decode
+    # fp16 copies of q, k and dO plus the row deltas; no far partials
+    p = sa.Params(1, 4, 2, 512, 64, window=16)
+    n = ctypes.c_size_t()
+    sa.load_library().sparse_attn_bwd_workspace_bytes(ctypes.byref(p.cfg()), ctypes.byref(n))
+    assert n.value == (2 * 512 * 64 * 2) + 2 * (4 * 512 * 64 * 2) + 4 * 512 * 4
+
+
+def test_backward_rejects_before_launch(lib):
+    p = sa.Params(1, 4, 4, 256, 64, window=8)
+    f = lambda **kw: sa.load_library().sparse_attn_bwd(
+        *[ctypes.c_void_p(kw.get(n_, 0x1000 * (i + 1))) for i, n_ in
+          enumerate(("q", "k", "v", "out", "lse", "dout"))],
+        ctypes.byref(p.cfg()), *[ctypes.c_void_p(kw.get(n_, 0x8000 * (i + 1))) for i, n_ in
+                                 enumerate(("dq", "dk", "dv"))], ctypes.c_void_p(kw.get("dsink", 0)))
+    assert f(q=0) == -1                        # null pointer
+    assert f(dsink=0x9000) == -1               # a sink gradient without a sink
+    assert f(q=0x1008) == -5                   # misaligned
+    assert f() == -6                           # no workspace

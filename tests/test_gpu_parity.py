@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 import workloads as W
-from parity import check
+from parity import check, check_grads, grads_ok
 
 pytestmark = pytest.mark.gpu
 
@@ -272,6 +272,86 @@ def test_bora_nsa_all_rows(dev):
     # window 512, one selection per kv group.
     wl = W.BORA_HYBRID.replace(name="bora_nsa_n4096", cmp_block=8, gate_shared=True)
     run_and_check(W.make_inputs(wl, 102), dev, label="bora_nsa")
+
+
+# --- backward (window and block gating, bf16) -------------------------------
+def run_backward(inp, dev, seed):
+    import torch
+    import sliding_window_long_amd as sa
+    wl = inp.wl
+    t = inp.tensors()
+    g = {k_: (None if v_ is None else v_.to(dev)) for k_, v_ in t.items()}
+    kw = dict(block_size=wl.block_size, top_k=wl.top_k, window=wl.window, sink=g["sink"],
+              gate_repr=wl.gate_repr, gate_shared=wl.gate_shared, gate_first=wl.gate_first)
+    out, lse, bsel, _ = sa.forward(g["q"], g["k"], g["v"], return_selection=True, **kw)
+    dout = W._round(np.random.default_rng(seed).standard_normal(inp.q.shape, dtype=np.float32),
+                    "bf16")
+    dq, dk, dv, ds = sa.backward(g["q"], g["k"], g["v"], out, lse,
+                                 torch.from_numpy(dout).to(torch.bfloat16).to(dev), **kw)
+    torch.cuda.synchronize()
+    grads = tuple(None if x is None else x.float().cpu().numpy() for x in (dq, dk, dv, ds))
+    return dout, (None if bsel is None else bsel.cpu().numpy()), grads
+
+
+def bwd_and_check(inp, dev, seed, label):
+    log(f"[gpu] {label} {inp.wl}")
+    dout, bsel, grads = run_backward(inp, dev, seed)
+    for x in grads:
+        assert x is None or np.isfinite(x).all()
+    res = check_grads(inp, dout, bsel, grads, sink=inp.sink)
+    log(f"[gpu] {label} " + " ".join(f"{k}: max {m:.2e} mean {a:.2e}" for k, (m, a) in res.items()))
+    assert grads_ok(res), str(res)
+    return grads
+
+
+BWD_SHAPES = [
+    dict(window=64),
+    dict(window=1),
+    dict(block_size=64, top_k=3),                       # own + far blocks, no window
+    dict(block_size=64, top_k=4, window=100),           # near and far blocks
+    dict(block_size=128, top_k=3, window=200, sink=True),
+    dict(block_size=64, top_k=8),                       # k = n: dense causal
+    dict(block_size=64, top_k=3, window=70, gate_shared=True, gate_first=True),
+    dict(block_size=64, top_k=4, gate_repr="minmax", sink=True),
+]
+
+
+@pytest.mark.parametrize("case", range(len(BWD_SHAPES)))
+@pytest.mark.parametrize("d", [64, 80, 128])
+def test_backward_small(dev, case, d):
+    kw = dict(BWD_SHAPES[case])
+    wl = W.Workload("bwd_small", 2, 4, 2, 512, d, "bf16", block_offsets="block_size" in kw, **kw)
+    bwd_and_check(W.make_inputs(wl, 71 + case + d), dev, 81 + case, label=f"bwd {kw}")
+
+
+def test_backward_ragged(dev):
+    wl = W.Workload("bwd_ragged", 1, 3, 1, 300, 80, "bf16", window=37, sink=True)
+    bwd_and_check(W.make_inputs(wl, 72), dev, 82, label="bwd_ragged")
+
+
+def test_backward_bora_all_rows(dev):
+    bwd_and_check(W.make_inputs(W.BORA_HYBRID, 102), dev, 83, label="bwd_bora")
+
+
+def test_backward_deterministic(dev):
+    # dq and (without far blocks) dk, dv are bitwise reproducible.  With far
+    # blocks, dk and dv sum the far rows in the order of the compaction's
+    # lists, which its atomics fill in no fixed order: two runs may then
+    # differ by fp32 rounding (a bf16 step where it crosses a rounding
+    # boundary), far below the gradients' scale.
+    for kw, far in ((dict(window=50), False), (dict(block_size=64, top_k=3, window=50), True)):
+        wl = W.Workload("bwd_det", 1, 4, 2, 640, 64, "bf16", block_offsets=far, **kw)
+        inp = W.make_inputs(wl, 73)
+        a = run_backward(inp, dev, 84)[2]
+        b = run_backward(inp, dev, 84)[2]
+        np.testing.assert_array_equal(a[0], b[0])
+        for x, y in zip(a[1:3], b[1:3]):
+            if far:
+                log(f"[gpu] bwd_det far: max |run1 - run2| = {np.abs(x - y).max():.3e}, "
+                    f"max |g| = {np.abs(x).max():.3e}")
+                assert np.abs(x - y).max() <= 1e-3 * np.abs(x).max()
+            else:
+                np.testing.assert_array_equal(x, y)
 
 
 # --- token top-k (Naive SWA + DSA shape) -------------------------------------
