@@ -194,10 +194,8 @@ int make_plan(const sparse_attn_cfg* c, Plan* p, bool bwd = false) {
             P.o_chunk_list = take((size_t)P.max_chunks * 4);
             P.o_chunk_start = take((size_t)P.max_chunks * 4);
             P.o_entries = take((size_t)P.max_entries * 4);
-            if (!bwd) {
-                P.o_part_o = take((size_t)rows * P.kslots * P.D * 2);
-                P.o_part_lse = take((size_t)rows * P.kslots * 4);
-            }
+            P.o_part_o = take((size_t)rows * P.kslots * P.D * 2);   // backward: dq partials
+            if (!bwd) P.o_part_lse = take((size_t)rows * P.kslots * 4);
         }
     }
     P.cmp = c->cmp_block > 0;
@@ -609,6 +607,9 @@ int sparse_attn_bwd(const void* q, const void* k, const void* v, const void* out
     ba.sel = sel; ba.top_k = P.top_k; ba.B = P.B; ba.n = P.n; ba.span = P.span;
     ba.kslots = P.kslots;
     ba.list_off = P.far ? ca.list_off : nullptr; ba.entries = P.far ? ca.entries : nullptr;
+    ba.chunk_list = ca.chunk_list; ba.chunk_start = ca.chunk_start; ba.n_chunks = ca.n_chunks;
+    ba.max_chunks = P.far ? P.max_chunks : 0;
+    ba.part_dq = P.far ? (uint16_t*)(ws + P.o_part_o) : nullptr;
     ba.Bt = P.Bt; ba.Hq = P.Hq; ba.Hkv = P.Hkv; ba.N = P.N; ba.D = P.D; ba.window = cfg->window;
     ba.scale = P.scale;
     {

@@ -9,11 +9,13 @@
 //   dv_j = sum_i P_ij dO_i,        dsink_h = -sum_i e^(sink_h - lse_i) D_i.
 //
 // bwd_delta  : D_i per row, and the sink gradient.
+// bwd_far_dq : far blocks' share of dQ, key-block-centric over the forward's
+//              compaction lists (gathered rows), as fp16 partials per slot.
 // bwd_dq     : query-centric (lane = query row): per 64-key tile S^T = K Q^T
 //              and dP^T = V dO^T on the matrix cores, P^T from the saved lse,
-//              dS^T, and dQ^T += K^T dS^T (K in fp16, P V-style product).
-//              The key tiles visited are the window span and the blocks any
-//              row of the workgroup kept.
+//              dS^T, and dQ^T += K^T dS^T (K in fp16, P V-style product) over
+//              the near key range (window, own and near blocks); adds the far
+//              partials.
 // bwd_dkv    : key-centric (lane = key): per 64-row tile S = Q K^T and
 //              dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS; rows are
 //              the contiguous span that can reach the keys through the window,
@@ -113,8 +115,7 @@ struct DqSmem {
     static constexpr int V = K + T::KELEMS;              // V tile, K layout (bf16)
     static constexpr int K16 = V + T::KELEMS;            // K tile, V layout (fp16)
     static constexpr int ELEMS = K16 + T::VELEMS;
-    static constexpr int BITS = 4096 / 32;               // kept-block bitmap words
-    static constexpr int BYTES = ELEMS * 2 + BITS * 4;
+    static constexpr int BYTES = ELEMS * 2;
 };
 
 template <int D>
@@ -125,7 +126,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dq_kernel(BwdArgs a) {
     uint16_t* const lk = (uint16_t*)smem + S::K;
     uint16_t* const lv = (uint16_t*)smem + S::V;
     uint16_t* const lk16 = (uint16_t*)smem + S::K16;
-    uint32_t* const bits = (uint32_t*)((uint16_t*)smem + S::ELEMS);
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int col = lane & 31, hh = lane >> 5;
@@ -147,20 +147,18 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dq_kernel(BwdArgs a) {
     const float lse2 = ok ? a.lse[prow] * kLog2e : 0.f;
     const float dr = ok ? a.delta[prow] : 0.f;
 
-    // Blocks any row of the workgroup kept (own, near, far).
+    // Kept blocks: own and near ones (within span below the own block) are
+    // attended here; far ones come as partials from bwd_far_dq.  nfar = the
+    // row's far blocks (slots 0 .. nfar-1 of its partials).
     const int32_t* sr = a.sel ? a.sel + prow * a.top_k : nullptr;
-    if (a.sel) {
-        for (int x = tid; x < S::BITS; x += NTHREADS) bits[x] = 0u;
-        __syncthreads();
-        if (ok && hh == 0)
-            for (int x = 0; x < a.top_k; ++x) {
-                const int cb = sr[x];
-                if (cb < 0) break;
-                atomicOr(&bits[cb >> 5], 1u << (cb & 31));
-            }
-    }
-    __syncthreads();
-    const int win_lo = a.window > 0 ? max(0, r0 - a.window + 1) : N;   // first window key
+    const int row_blk = a.sel ? min(row, N - 1) / a.B : 0;
+    int nfar = 0;
+    if (a.sel && ok)
+        for (int x = 0; x < a.top_k; ++x) {
+            const int cb = sr[x];
+            if (cb < 0) break;
+            nfar += row_blk - cb > a.span;
+        }
     const uint32_t wl_window = a.window > 0 ? (uint32_t)a.window : 0u;
     int cur = 0;   // this row's cursor into its ascending kept-block list
 
@@ -177,12 +175,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dq_kernel(BwdArgs a) {
     const TileSrc<D, 1> ksrc = tile_src<D, 1>(kp, N, tid), vsrc = tile_src<D, 1>(vp, N, tid);
     const TileSrc<D, 1> k16src = tile_src<D, 1>(k16p, N, tid);
 
-    const int t_end = r_hi / KT;
-    for (int t = 0; t <= t_end; ++t) {
+    // Near key range of the workgroup: the window span and the blocks within
+    // span below the rows' own blocks.
+    int lo = r0;
+    if (a.window > 0) lo = min(lo, r0 - a.window + 1);
+    if (a.sel) lo = min(lo, (r0 / a.B - a.span) * a.B);
+    const int t_begin = max(lo, 0) / KT, t_end = r_hi / KT;
+    for (int t = t_begin; t <= t_end; ++t) {
         const int kt0 = t * KT;
-        const bool in_win = kt0 + KT - 1 >= win_lo;
-        const bool kept = a.sel && a.B > 0 && ((bits[(kt0 / a.B) >> 5] >> ((kt0 / a.B) & 31)) & 1u);
-        if (!in_win && !kept) continue;   // workgroup-uniform
         Stage<D, 1> st;
         load_tile<D, 1>(st, ksrc, kt0);
         store_tile<D, 1, T::KS, T::KELEMS>(st, lk, tid);
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dq_kernel(BwdArgs a) {
         if (a.sel && ok) {
             const int blk = kt0 / a.B;
             while (cur < a.top_k && sr[cur] >= 0 && sr[cur] < blk) ++cur;
-            if (cur < a.top_k && sr[cur] == blk) wl = 0x80000000u;
+            if (cur < a.top_k && sr[cur] == blk && row_blk - blk <= a.span) wl = 0x80000000u;
         }
         f32x16 s[2], dp[2];
         qk_tile<D, 1>(lk, qf, s, lane);
@@ -209,7 +209,122 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dq_kernel(BwdArgs a) {
         pv_tile<D, 1>(lk16, db, dl, o, voff);
         __syncthreads();
     }
-    if (ok) write_rows_bf16<D>(a.dq + prow * D, o, a.scale, hh);
+    if (!ok) return;
+    // dq = scale * near part + the far blocks' partials (already scaled).
+#pragma unroll
+    for (int mb = 0; mb < T::DM; ++mb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[mb][v] *= a.scale;
+    for (int s_ = 0; s_ < nfar; ++s_) {
+        const uint16_t* po = a.part_dq + (prow * (size_t)a.kslots + s_) * D;
+#pragma unroll
+        for (int mb = 0; mb < T::DM; ++mb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int d0 = mb * 32 + 8 * j + 4 * hh;
+                if (d0 < D) {
+                    const uint2 raw = *(const uint2*)(po + d0);
+                    const _Float16* hv = (const _Float16*)&raw;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[mb][4 * j + e] += (float)hv[e];
+                }
+            }
+    }
+    write_rows_bf16<D>(a.dq + prow * D, o, 1.f, hh);
+}
+
+// ---------------------------------------------------------------------------
+// Far blocks' share of dQ: a workgroup owns one chunk (<= 128 entries) of
+// the list of rows that kept one block as a far block (the forward's
+// compaction), gathers those rows and walks the block's keys; every key of a
+// far block is attended.  Writes scale * sum_j dS_ij k_j per (row, slot),
+// fp16.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(NTHREADS, 1) void bwd_far_dq_kernel(BwdArgs a) {
+    using T = Tile<D>;
+    using S = DqSmem<D>;
+    __shared__ __align__(16) uint8_t smem[S::BYTES];
+    uint16_t* const lk = (uint16_t*)smem + S::K;
+    uint16_t* const lv = (uint16_t*)smem + S::V;
+    uint16_t* const lk16 = (uint16_t*)smem + S::K16;
+
+    // Chunks of one list are contiguous: give each XCD a contiguous range.
+    const int grid = gridDim.x;
+    const int per_xcd = grid / 8;
+    const int chunk = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (chunk >= *a.n_chunks) return;
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int col = lane & 31, hh = lane >> 5;
+    const int N = a.N, G = a.Hq / a.Hkv;
+    const int list = a.chunk_list[chunk];
+    const int e0 = a.chunk_start[chunk];
+    const int e_end = min(e0 + RT, a.list_off[list + 1]);
+    const int cblk = list % a.n, bg = list / a.n;
+    const int b = bg / a.Hkv, g = bg % a.Hkv;
+    const int e = e0 + wave * 32 + col;
+    const bool ok = e < e_end;
+    int slot = 0;
+    size_t prow = 0;
+    if (ok) {   // entry = (i*G + head in group)*kslots + slot
+        const int ent = a.entries[e];
+        slot = ent % a.kslots;
+        const int t2 = ent / a.kslots;
+        prow = (size_t)(b * a.Hq + g * G + t2 % G) * N + t2 / G;
+    }
+    bf16x8 qf[1][T::DK], df[1][T::DK];
+    load_q<D, 1>(qf, &a.q, prow * D, ok, hh);
+    load_q<D, 1>(df, &a.dout, prow * D, ok, hh);
+    const float c = a.scale * kLog2e;
+    const float lse2 = ok ? a.lse[prow] * kLog2e : INFINITY;
+    const float dr = ok ? a.delta[prow] : 0.f;
+
+    f32x16 o[T::DM];
+#pragma unroll
+    for (int mb = 0; mb < T::DM; ++mb) o[mb] = f32x16{};
+    int voff[T::DM];
+#pragma unroll
+    for (int mb = 0; mb < T::DM; ++mb) voff[mb] = v_lane_offset<D>(lane, mb);
+    const size_t kvoff = (size_t)bg * N * D;
+    const uint16_t* kp[1] = {a.k + kvoff};
+    const uint16_t* vp[1] = {a.v + kvoff};
+    const uint16_t* k16p[1] = {a.k16 + kvoff};
+    const TileSrc<D, 1> ksrc = tile_src<D, 1>(kp, N, tid), vsrc = tile_src<D, 1>(vp, N, tid);
+    const TileSrc<D, 1> k16src = tile_src<D, 1>(k16p, N, tid);
+    const uint4 zero4[4] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0),
+                            make_uint4(0, 0, 0, 0)};
+    for (int t = 0; t < a.B / KT; ++t) {
+        const int kt0 = cblk * a.B + t * KT;
+        Stage<D, 1> st;
+        load_tile<D, 1>(st, ksrc, kt0);
+        store_tile<D, 1, T::KS, T::KELEMS>(st, lk, tid);
+        load_tile<D, 1>(st, vsrc, kt0);
+        store_tile<D, 1, T::KS, T::KELEMS>(st, lv, tid);
+        load_tile<D, 1>(st, k16src, kt0);
+        store_tile<D, 1, T::VS, T::VELEMS>(st, lk16, tid);
+        __syncthreads();
+        f32x16 s[2], dp[2];
+        qk_tile<D, 1>(lk, qf, s, lane);
+        qk_tile<D, 1>(lv, df, dp, lane);
+        uint4 pb[4], db[4];
+        p_ds(s, dp, c, lse2, dr, pb, db);
+        pv_tile<D, 1>(lk16, db, zero4, o, voff);
+        __syncthreads();
+    }
+    if (!ok) return;
+    _Float16* dst = (_Float16*)a.part_dq + (prow * (size_t)a.kslots + slot) * D;
+#pragma unroll
+    for (int mb = 0; mb < T::DM; ++mb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int d0 = mb * 32 + 8 * j + 4 * hh;
+            if (d0 < D) {
+                _Float16 r[4] = {(_Float16)(o[mb][4 * j] * a.scale), (_Float16)(o[mb][4 * j + 1] * a.scale),
+                                 (_Float16)(o[mb][4 * j + 2] * a.scale), (_Float16)(o[mb][4 * j + 3] * a.scale)};
+                *(uint2*)(dst + d0) = *(const uint2*)r;
+            }
+        }
 }
 
 // ---------------------------------------------------------------------------
@@ -418,6 +533,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkv_kernel(BwdArgs a) {
 template <int D>
 static hipError_t bwd_d(const BwdArgs& a, hipStream_t s) {
     const int nt = (a.N + RT - 1) / RT;
+    if (a.list_off && a.max_chunks > 0) {
+        hipLaunchKernelGGL((bwd_far_dq_kernel<D>), dim3(a.max_chunks), dim3(NTHREADS), 0, s, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3(nt * a.Bt * a.Hq), dim3(NTHREADS), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

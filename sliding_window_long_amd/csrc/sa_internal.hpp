@@ -143,6 +143,11 @@ struct BwdArgs {
     const int32_t* sel;     // [Bt*Hq*N, top_k] or nullptr (no block gate)
     const int32_t* list_off;  // far-row lists of the compaction, or nullptr
     const int32_t* entries;
+    const int32_t* chunk_list;  // their chunking (<= 128 entries per chunk)
+    const int32_t* chunk_start;
+    const int32_t* n_chunks;
+    int max_chunks;
+    uint16_t* part_dq;      // fp16 [Bt*Hq*N, kslots, D] far-block dq partials
     int top_k, B, n, span, kslots;
     int Bt, Hq, Hkv, N, D, window;
     float scale;
