@@ -39,8 +39,7 @@ PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ["sliding_window_long_amd/csrc/sa_attn.hip",
                   "sliding_window_long_amd/csrc/sa_attn_common.hpp",
-                  "sliding_window_long_amd/csrc/sa_device.hpp",
-                  "sliding_window_long_amd/build.py"]   # its compile flags shape the code too
+                  "sliding_window_long_amd/csrc/sa_device.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_rows_bitaxon_swa_n16384_traffic.json")
 
 
@@ -92,10 +91,16 @@ def _union_pairs(wl, bsel=None, tsel=None):
 
 
 def kernel_source_hash():
+    """Hash of what shapes the dominant kernel's code: its sources and the
+    compile flags of its file."""
+    from sliding_window_long_amd import build as B
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
+    flags = B.FLAGS + B.EXTRA.get("sa_attn.hip", [])
+    flags = [f for i, f in enumerate(flags) if f != "-I" and (i == 0 or flags[i - 1] != "-I")]
+    h.update(" ".join(flags).encode())   # include paths differ between machines
     return h.hexdigest()[:16]
 
 
@@ -129,7 +134,8 @@ def time_workload(wl, seed, dev, steps, warmup, want_sel=False):
               idx_k=g["idx_k"], token_top_k=wl.token_top_k, sink=g["sink"], workspace=ws,
               gate_repr=wl.gate_repr, gate_shared=wl.gate_shared, gate_first=wl.gate_first,
               cmp_block=wl.cmp_block)
-    out = torch.empty_like(g["q"])
+    out = torch.empty(g["q"].shape, device=dev,   # bf16 out for FP8 inputs
+                      dtype=torch.bfloat16 if wl.dtype == "fp8" else g["q"].dtype)
     lse = torch.empty(g["q"].shape[:3], dtype=torch.float32, device=dev)
     bsel = tsel = None
     if want_sel and (wl.top_k or wl.token_top_k):
@@ -162,7 +168,9 @@ GATE_VARIANTS = [W.LONG_MOBA.replace(name="long_moba_minmax_n131072", gate_repr=
                  W.BORA_HYBRID.replace(name="bora_hybrid_shared_first_n4096", gate_shared=True,
                                        gate_first=True),
                  # the BORA NSA layout: 8:1 compressed branch, one selection per kv group
-                 W.BORA_HYBRID.replace(name="bora_nsa_n4096", cmp_block=8, gate_shared=True)]
+                 W.BORA_HYBRID.replace(name="bora_nsa_n4096", cmp_block=8, gate_shared=True),
+                 # FP8 (E4M3) inputs on the headline shape
+                 W.BITAXON_SWA.replace(name="bitaxon_swa_n16384_fp8", dtype="fp8")]
 
 
 # Backward calls (gradients for the forward's selection) on the window and
@@ -343,7 +351,7 @@ def main():
     if not args.no_extra:
         extra = {}
         for idx, ewl in [(i, W.WORKLOADS[i]) for i in (1, 2, 4, 5)] + \
-                [(2 if v.seq_len == W.BORA_HYBRID.seq_len else 4, v) for v in GATE_VARIANTS]:
+                [({4096: 2, 16384: 3}.get(v.seq_len, 4), v) for v in GATE_VARIANTS]:
             print(f"[bench] workload {ewl.name}", file=sys.stderr, flush=True)
             _, ems, est, (bsel, tsel) = time_workload(ewl, idx, dev, args.extra_steps, 2,
                                                       want_sel=True)

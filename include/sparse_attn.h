@@ -52,7 +52,8 @@
  *
  * Layouts (row-major, contiguous, device memory; kv_len = seq_len unless a
  * decode step):
- *   q, out  [batch, n_q_heads,  seq_len, head_dim]   dtype cfg->dtype
+ *   q, out  [batch, n_q_heads,  seq_len, head_dim]   dtype cfg->dtype (out bf16
+ *                                                     for SA_FP8)
  *   k, v    [batch, n_kv_heads, kv_len,  head_dim]   dtype cfg->dtype
  *   lse     [batch, n_q_heads,  seq_len]              fp32
  *   idx_q   [batch, seq_len, index_dim], idx_k [batch, kv_len, index_dim]
@@ -91,8 +92,15 @@ typedef enum {
                     bf16 matrix cores; P V on fp16 ones (V converted once into
                     the workspace, exact for |v| in [2^-14, 65504]; larger |v|
                     overflows, smaller ones keep fp16 subnormal precision). */
-    SA_F32 = 1   /* float32 inputs and out; each operand split into two
+    SA_F32 = 1,  /* float32 inputs and out; each operand split into two
                     bf16 terms on the matrix cores (about 16 mantissa bits) */
+    SA_FP8 = 2   /* FP8 inputs (OCP E4M3: bias 7, 3 mantissa bits, max 448, no
+                    infinities, 0x7F/0xFF = NaN) for q, k, v, idx_q, idx_k; out
+                    is bf16.  [Naive-N0.5-Flash page: FP8 mixed-precision
+                    inference.]  Every E4M3 value is a bf16 value: the inputs
+                    are decoded exactly into bf16 in the workspace and computed
+                    as SA_BF16.  Not for sparse_attn_block_pool or the backward
+                    (SA_E_UNSUPPORTED). */
 } sa_dtype;
 
 typedef enum {

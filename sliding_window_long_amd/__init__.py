@@ -5,7 +5,7 @@ Importing this package does not load the shared library; the first call of
 an entry point does, and raises if it has not been built.
 """
 from .binding import (  # noqa: F401
-    EXPORTS, SA_BF16, SA_F32, Params, SparseAttnCfg, SparseAttnError, Workspace, backward,
+    EXPORTS, SA_BF16, SA_F32, SA_FP8, Params, SparseAttnCfg, SparseAttnError, Workspace, backward,
     block_pool, forward, load_library, params_for, sparse_attn_block_pool, sparse_attn_fwd,
     sparse_attn_bwd_workspace_bytes,
     sparse_attn_set_timing, sparse_attn_stage_times, sparse_attn_strerror,

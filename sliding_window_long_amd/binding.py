@@ -18,7 +18,7 @@ from dataclasses import dataclass
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsparse_attn.so")
 
-SA_BF16, SA_F32 = 0, 1
+SA_BF16, SA_F32, SA_FP8 = 0, 1, 2
 SA_GATE_MEAN, SA_GATE_MINMAX = 0, 1
 SA_OK = 0
 ERROR_CODES = {
@@ -187,9 +187,10 @@ def params_for(q, k, *, block_size=0, top_k=0, window=0, token_top_k=0, index_di
                cmp_block=0) -> Params:
     import torch
     Bt, Hq, N, d = q.shape
-    dt = {torch.bfloat16: SA_BF16, torch.float32: SA_F32}.get(q.dtype)
+    dt = {torch.bfloat16: SA_BF16, torch.float32: SA_F32,
+          torch.float8_e4m3fn: SA_FP8}.get(q.dtype)
     if dt is None:
-        raise TypeError(f"q dtype {q.dtype} not supported (bfloat16 or float32)")
+        raise TypeError(f"q dtype {q.dtype} not supported (bfloat16, float32 or float8_e4m3fn)")
     if gate_repr not in GATE_REPR:
         raise ValueError("gate_repr is 'mean' or 'minmax'")
     Nk = k.shape[2]
@@ -241,8 +242,9 @@ def forward(q, k, v, *, block_size=0, top_k=0, window=0, idx_q=None, idx_k=None,
                    cmp_block=cmp_block)
     cfg = p.cfg()
     dev = q.device
-    if out is None:
-        out = torch.empty_like(q)
+    if out is None:   # FP8 inputs give a bf16 out
+        out = torch.empty(q.shape, dtype=torch.bfloat16 if q.dtype == torch.float8_e4m3fn else q.dtype,
+                          device=q.device)
     if lse is None:
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
     bsel = tsel = None

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libsparse_attn.so")
 SOURCES = ["sa_api.hip", "sa_attn.hip", "sa_blocks.hip", "sa_gate.hip", "sa_compact.hip",
-           "sa_token.hip", "sa_decode.hip", "sa_cmp.hip", "sa_bwd.hip"]
+           "sa_token.hip", "sa_decode.hip", "sa_cmp.hip", "sa_bwd.hip", "sa_fp8.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -27,6 +27,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct Plan {
     int Bt, Hq, Hkv, N, D, G;
     bool f32;
+    bool fp8;               // FP8 inputs, decoded into bf16 copies first
     bool gate;
     int B, n, top_k, span, kslots, idx_bits, lists;
     bool gate_mm, gate_shared, gate_first;   // gate variants
@@ -46,7 +47,7 @@ struct Plan {
         o_chunk_start, o_entries, o_part_o, o_part_lse, o_tok_split, o_tok_state, o_tok_mask,
         o_tok_qn, o_tok_win, o_tok_kpart, o_tok_scr, o_tok_nslow, o_dec_scores, o_dec_list,
         o_dec_nfar, o_dec_part, o_qsum, o_cmp_k, o_cmp_v, o_cmp_out, o_k16, o_q16, o_do16,
-        o_delta,
+        o_delta, o_f8q, o_f8k, o_f8v, o_f8iq, o_f8ik,
         o_v16, total;
 };
 
@@ -58,7 +59,7 @@ int make_plan(const sparse_attn_cfg* c, Plan* p, bool bwd = false) {
     if (!c || c->struct_size != sizeof(sparse_attn_cfg)) return SA_E_INVALID_ARG;
     if (c->batch < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 || c->seq_len < 1)
         return SA_E_INVALID_ARG;
-    if (c->dtype != SA_BF16 && c->dtype != SA_F32) return SA_E_INVALID_ARG;
+    if (c->dtype != SA_BF16 && c->dtype != SA_F32 && c->dtype != SA_FP8) return SA_E_INVALID_ARG;
     if (c->window < 0 || c->top_k < 0 || c->token_top_k < 0 || c->block_size < 0)
         return SA_E_INVALID_ARG;
     if (!(c->softmax_scale >= 0.f) || isinf(c->softmax_scale)) return SA_E_INVALID_ARG;
@@ -103,9 +104,10 @@ int make_plan(const sparse_attn_cfg* c, Plan* p, bool bwd = false) {
     P.Bt = c->batch; P.Hq = c->n_q_heads; P.Hkv = c->n_kv_heads; P.N = c->seq_len;
     P.D = c->head_dim; P.G = P.Hq / P.Hkv;
     P.f32 = c->dtype == SA_F32;
+    P.fp8 = c->dtype == SA_FP8;
     P.scale = c->softmax_scale > 0.f ? c->softmax_scale : 1.0f / sqrtf((float)P.D);
     const long long rows = (long long)P.Bt * P.Hq * P.N;
-    const size_t esz = P.f32 ? 4 : 2;
+    const size_t esz = P.f32 ? 4 : (P.fp8 ? 1 : 2);
     if (rows * P.D * (long long)esz > (1LL << 40)) return SA_E_UNSUPPORTED;
     // One head's K or V (16-bit) must be addressable by a 32-bit byte offset.
     if ((long long)P.Nk * P.D * 2 >= (1LL << 31)) return SA_E_UNSUPPORTED;
@@ -126,6 +128,15 @@ int make_plan(const sparse_attn_cfg* c, Plan* p, bool bwd = false) {
         const int chunk = sa::dec_chunk(P.f32);
         P.dec_cmax = (int)((span + chunk - 1) / chunk);
         P.o_dec_part = take((size_t)P.Bt * P.Hq * P.N * P.dec_cmax * (P.D + 2) * 4);
+        if (P.fp8) {
+            P.o_f8q = take((size_t)rows * P.D * 2);
+            P.o_f8k = take((size_t)P.Bt * P.Hkv * P.Nk * P.D * 2);
+            P.o_f8v = take((size_t)P.Bt * P.Hkv * P.Nk * P.D * 2);
+            if (P.tok) {
+                P.o_f8iq = take((size_t)P.Bt * P.N * 64 * 2);
+                P.o_f8ik = take((size_t)P.Bt * P.Nk * 64 * 2);
+            }
+        }
         P.total = off;
         return SA_OK;
     }
@@ -226,6 +237,15 @@ int make_plan(const sparse_attn_cfg* c, Plan* p, bool bwd = false) {
         const size_t cands = (size_t)P.Bt * P.N * sa::kTokCap * 8;
         P.o_tok_scr = take(counts > cands ? counts : cands);
         P.o_tok_nslow = take(4);
+    }
+    if (P.fp8) {
+        P.o_f8q = take(nq * 2);
+        P.o_f8k = take(nkv * 2);
+        P.o_f8v = take(nkv * 2);
+        if (P.tok) {
+            P.o_f8iq = take((size_t)P.Bt * P.N * 64 * 2);
+            P.o_f8ik = take((size_t)P.Bt * P.N * 64 * 2);
+        }
     }
     P.total = off;
     return SA_OK;
@@ -369,6 +389,7 @@ int sparse_attn_block_pool(const void* k, const sparse_attn_cfg* cfg, float* kba
     int rc = make_plan(cfg, &P);
     if (rc != SA_OK) return rc;
     if (!P.gate) return SA_E_INVALID_ARG;
+    if (P.fp8) return SA_E_UNSUPPORTED;
     if (!k || !kbar) return SA_E_INVALID_ARG;
     if (misaligned(k, 16) || misaligned(kbar, 16)) return SA_E_ALIGNMENT;
     hipStream_t s = (hipStream_t)cfg->stream;
@@ -397,6 +418,31 @@ int sparse_attn_fwd(const void* q, const void* k, const void* v, const sparse_at
     hipStream_t s = (hipStream_t)cfg->stream;
     char* ws = (char*)cfg->workspace;
     auto ok = [](hipError_t e) { return e == hipSuccess; };
+
+    // FP8 inputs: decode into bf16 copies, then run as bf16.
+    sparse_attn_cfg c8;
+    if (P.fp8) {
+        const size_t nkv = (size_t)P.Bt * P.Hkv * P.Nk * P.D;
+        uint16_t* q8 = (uint16_t*)(ws + P.o_f8q);
+        uint16_t* k8 = (uint16_t*)(ws + P.o_f8k);
+        uint16_t* v8 = (uint16_t*)(ws + P.o_f8v);
+        StageScope t("fp8_to_bf16", s);
+        if (!ok(sa::launch_fp8_to_bf16(q, q8, (size_t)P.Bt * P.Hq * P.N * P.D, s)) ||
+            !ok(sa::launch_fp8_to_bf16(k, k8, nkv, s)) || !ok(sa::launch_fp8_to_bf16(v, v8, nkv, s)))
+            return SA_E_HIP;
+        c8 = *cfg;
+        if (P.tok) {
+            uint16_t* iq8 = (uint16_t*)(ws + P.o_f8iq);
+            uint16_t* ik8 = (uint16_t*)(ws + P.o_f8ik);
+            if (!ok(sa::launch_fp8_to_bf16(cfg->idx_q, iq8, (size_t)P.Bt * P.N * 64, s)) ||
+                !ok(sa::launch_fp8_to_bf16(cfg->idx_k, ik8, (size_t)P.Bt * P.Nk * 64, s)))
+                return SA_E_HIP;
+            c8.idx_q = iq8;
+            c8.idx_k = ik8;
+        }
+        cfg = &c8;
+        q = q8; k = k8; v = v8;
+    }
 
     if (P.dec) {
         sa::DecArgs da{};

@@ -1,0 +1,49 @@
+// sa_fp8.hip -- FP8 inputs: exact decoding of OCP E4M3 values into bf16.
+//
+// [Naive-N0.5-Flash page: the model runs FP8 mixed-precision inference.]
+// E4M3 (bias 7, 3 mantissa bits, no infinities, S.1111.111 = NaN) holds
+// normal values 2^-6 .. 448 and subnormals m * 2^-9; every one of them is a
+// bf16 value (8 exponent bits, 7 mantissa bits), so the decoded tensors
+// carry exactly the inputs' values into the bf16 path.
+#include "sa_device.hpp"
+#include "sa_internal.hpp"
+
+namespace sa {
+
+__device__ __forceinline__ uint32_t e4m3_to_bf16(uint32_t b) {
+    const uint32_t s = (b & 0x80u) << 8;
+    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+    if (e == 15u && m == 7u) return s | 0x7fc0u;                 // NaN
+    if (e != 0u) return s | ((e + 120u) << 7) | (m << 4);         // 2^(e-7) (1 + m/8)
+    if (m == 0u) return s;                                        // signed zero
+    // subnormal m * 2^-9: leading bit p of m, value 2^(p-9) (1 + rest / 2^p)
+    const uint32_t p = m >= 4u ? 2u : (m >= 2u ? 1u : 0u);
+    return s | ((p + 118u) << 7) | (((m - (1u << p)) << (7u - p)) & 0x7fu);
+}
+
+// 16 fp8 values per thread -> 16 bf16 values.
+__global__ __launch_bounds__(256) void fp8_to_bf16_kernel(const uint4* __restrict__ x,
+                                                          uint4* __restrict__ y, size_t n16) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n16) return;
+    const uint4 u = x[i];
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    uint32_t o[8];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        o[2 * t] = e4m3_to_bf16(w[t] & 0xffu) | (e4m3_to_bf16((w[t] >> 8) & 0xffu) << 16);
+        o[2 * t + 1] = e4m3_to_bf16((w[t] >> 16) & 0xffu) | (e4m3_to_bf16(w[t] >> 24) << 16);
+    }
+    y[2 * i] = make_uint4(o[0], o[1], o[2], o[3]);
+    y[2 * i + 1] = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
+hipError_t launch_fp8_to_bf16(const void* x, uint16_t* y, size_t n, hipStream_t s) {
+    const size_t n16 = n / 16;   // every tensor holds a multiple of 16 elements
+    if (n16 == 0) return hipSuccess;
+    hipLaunchKernelGGL(fp8_to_bf16_kernel, dim3((unsigned)((n16 + 255) / 256)), dim3(256), 0, s,
+                       (const uint4*)x, (uint4*)y, n16);
+    return hipGetLastError();
+}
+
+}  // namespace sa

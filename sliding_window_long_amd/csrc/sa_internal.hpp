@@ -156,6 +156,9 @@ struct BwdArgs {
 hipError_t launch_bwd_delta(const BwdArgs& a, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs& a, int head_dim, hipStream_t s);
 
+// FP8 (OCP E4M3) inputs decoded exactly into bf16; n a multiple of 16.
+hipError_t launch_fp8_to_bf16(const void* x, uint16_t* y, size_t n, hipStream_t s);
+
 hipError_t launch_cmp_pool(const CmpPoolArgs& a, bool f32_in, hipStream_t s);
 hipError_t launch_cmp(const CmpArgs& a, int head_dim, int split, hipStream_t s);
 

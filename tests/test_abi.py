@@ -108,7 +108,10 @@ def test_valid_configs(lib):
               sa.Params(2, 8, 4, 4096, 128, block_size=128, top_k=16, window=512,
                         gate_shared=1, gate_first=1),
               sa.Params(1, 1, 1, 512, 64, dtype=sa.SA_F32, block_size=64, top_k=2,
-                        gate_repr=1, gate_first=1)):
+                        gate_repr=1, gate_first=1),
+              sa.Params(1, 32, 32, 16384, 80, dtype=sa.SA_FP8, window=4096),
+              sa.Params(4, 16, 4, 64, 128, dtype=sa.SA_FP8, window=128, token_top_k=2048,
+                        index_dim=64, kv_len=65536)):
         assert code_of(p) == 0
 
 
@@ -233,3 +236,15 @@ def test_backward_rejects_before_launch(lib):
     assert f(dsink=0x9000) == -1               # a sink gradient without a sink
     assert f(q=0x1008) == -5                   # misaligned
     assert f() == -6                           # no workspace
+
+
+def test_fp8_workspace(lib):
+    # bf16 copies of q, k, v (and of the indexer tensors)
+    ws = lambda dt: sa.sparse_attn_workspace_bytes(sa.Params(1, 4, 2, 1024, 64, dtype=dt, window=16).cfg())
+    assert ws(sa.SA_FP8) - ws(sa.SA_BF16) == (4 + 2 + 2) * 1024 * 64 * 2
+    p = sa.Params(1, 4, 2, 1024, 64, dtype=sa.SA_FP8, window=16)
+    assert sa.load_library().sparse_attn_bwd_workspace_bytes(
+        ctypes.byref(p.cfg()), ctypes.byref(ctypes.c_size_t())) == -8     # no fp8 backward
+    p = sa.Params(1, 4, 2, 1024, 64, dtype=sa.SA_FP8, block_size=64, top_k=2)
+    assert sa.load_library().sparse_attn_block_pool(
+        ctypes.c_void_p(0x1000), ctypes.byref(p.cfg()), ctypes.c_void_p(0x2000)) == -8

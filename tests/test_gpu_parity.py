@@ -274,6 +274,32 @@ def test_bora_nsa_all_rows(dev):
     run_and_check(W.make_inputs(wl, 102), dev, label="bora_nsa")
 
 
+# --- FP8 (E4M3) inputs: decoded exactly, computed as bf16, out bf16 ---------
+@pytest.mark.parametrize("kw", [
+    dict(window=100, sink=True),
+    dict(block_size=64, top_k=4, window=70, block_offsets=True),
+    dict(block_size=128, top_k=3, gate_shared=True, gate_repr="minmax", cmp_block=8,
+         block_offsets=True),
+    dict(window=16, token_top_k=40, index_dim=64, sink=True),
+])
+def test_fp8_inputs(dev, kw):
+    wl = W.Workload("fp8", 2, 8, 4, 1024, 128, "fp8", **kw)
+    inp = W.make_inputs(wl, 91)
+    assert np.abs(inp.q).max() <= 448
+    run_and_check(inp, dev, label=f"fp8 {kw}")
+
+
+def test_fp8_decode(dev):
+    wl = W.Workload("fp8_dec", 2, 4, 2, 3000, 128, "fp8", window=64, token_top_k=200,
+                    index_dim=64, sink=True)
+    run_and_check(decode_inputs(wl, 5, 92), dev, label="fp8_decode")
+
+
+def test_fp8_bitaxon_full_sampled(dev):
+    wl = W.BITAXON_SWA.replace(name="bitaxon_swa_n16384_fp8", dtype="fp8")
+    run_and_check(W.make_inputs(wl, 103), dev, W.sample_rows(wl, 3000, 1), label="fp8_bitaxon")
+
+
 # --- backward (window and block gating, bf16) -------------------------------
 def run_backward(inp, dev, seed):
     import torch

@@ -16,8 +16,10 @@ Recipe (the same for every workload):
   every key of that block before rounding, so that the block means differ
   and the gating is not decided by noise;
 * bf16 workloads are rounded to bf16 with round-to-nearest-even
-  (``torch.Tensor.to(torch.bfloat16)``); the fp32 copies handed to the
-  oracle hold exactly the rounded values.
+  (``torch.Tensor.to(torch.bfloat16)``), fp8 workloads to OCP E4M3
+  (``torch.float8_e4m3fn``, round to nearest even; N(0,1) draws stay far
+  below its 448 limit); the fp32 copies handed to the oracle hold exactly
+  the rounded values.
 
 Shapes follow the (batch, heads, seq_len, head_dim) layout of the Bit-Axon
 "SWA + MoE" page (its q/k/v reshape in the algorithm figure).
@@ -38,7 +40,7 @@ class Workload:
     n_kv_heads: int
     seq_len: int
     head_dim: int
-    dtype: str                 # "f32" or "bf16": dtype of q, k, v, out
+    dtype: str                 # "f32", "bf16" or "fp8" (E4M3, out bf16): dtype of q, k, v
     block_size: int = 0        # B; 0 when block gating is off
     top_k: int = 0             # blocks kept per query, own block included
     window: int = 0            # w: attend iff 0 <= i - j < w; 0 = no window
@@ -90,7 +92,8 @@ class Inputs:
 
     def tensors(self):
         import torch
-        dt = torch.bfloat16 if self.wl.dtype == "bf16" else torch.float32
+        dt = {"bf16": torch.bfloat16, "f32": torch.float32,
+              "fp8": torch.float8_e4m3fn}[self.wl.dtype]
         conv = lambda a: None if a is None else torch.from_numpy(a).to(dt)
         return dict(q=conv(self.q), k=conv(self.k), v=conv(self.v),
                     idx_q=conv(self.idx_q), idx_k=conv(self.idx_k),
@@ -102,7 +105,8 @@ def _round(a: np.ndarray, dtype: str) -> np.ndarray:
         return np.ascontiguousarray(a, dtype=np.float32)
     import torch
     t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
-    return t.to(torch.bfloat16).to(torch.float32).numpy()
+    low = torch.float8_e4m3fn if dtype == "fp8" else torch.bfloat16
+    return t.to(low).to(torch.float32).numpy()
 
 
 def make_inputs(wl: Workload, seed: int) -> Inputs:
