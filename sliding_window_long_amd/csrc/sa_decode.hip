@@ -393,7 +393,8 @@ __device__ __forceinline__ void lds_load8(const uint8_t* row, int b, float (&x)[
 // listed tokens) of query r for all G q heads of kv head g.  The tile's K
 // and V rows are staged in LDS together (coalesced 16-byte loads, all issued
 // before the first store); then logits (one key per thread), per-head max
-// and sum, and P V.  Partial per (row, tile): o[D] = sum_j e^(x_j - m) v_j,
+// and sum, and P V.  q and the logits take G * (D + CH) floats of dynamic
+// LDS (G = 1 for multi-head attention), so more workgroups fit on a CU.  Partial per (row, tile): o[D] = sum_j e^(x_j - m) v_j,
 // then m, l (x in base-2 units: logit * log2 e).
 template <int D, bool F32>
 __global__ __launch_bounds__(DEC_THREADS) void dec_attn_kernel(DecArgs a) {
@@ -402,20 +403,21 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_attn_kernel(DecArgs a) {
     constexpr int RB = D * ESZ;         // bytes of a K or V row
     constexpr int ROWB = RB + 16;       // LDS row stride (keeps per-key reads off one bank)
     constexpr int PIECES = RB / 16;     // 16-byte pieces of a row
-    constexpr int PER = CH * PIECES / DEC_THREADS;   // pieces per thread
+    constexpr int NPC = CH * PIECES;    // 16-byte pieces of a tile
+    constexpr int PER = (NPC + DEC_THREADS - 1) / DEC_THREADS;   // pieces per thread
     constexpr int DG = D / 8;           // 8-dim groups of a row
-    static_assert(CH * PIECES % DEC_THREADS == 0, "tile pieces must split evenly");
     static_assert(CH * ROWB >= DEC_THREADS * 8 * 4, "part sums must fit the K tile");
     __shared__ __align__(16) uint8_t kt[CH * ROWB];   // K rows; at the end the P V part sums
     __shared__ __align__(16) uint8_t vt[CH * ROWB];
-    __shared__ float qs[16 * D];
-    __shared__ float ps[16 * CH];
     __shared__ int js[CH];
     __shared__ float red[16][2];
+    extern __shared__ float dyn[];   // q [G][D], logits [G][CH]: sized per launch
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c = blockIdx.x, bt = blockIdx.z;
     const int g = blockIdx.y / a.Nq, r = blockIdx.y % a.Nq;
     const int G = a.Hq / a.Hkv;
+    float* const qs = dyn;
+    float* const ps = dyn + G * D;
     int p, lo, nw, nt;
     dec_span(a, bt, r, p, lo, nw, nt);
     const int L = nw + nt, key0 = c * CH;
@@ -438,15 +440,15 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_attn_kernel(DecArgs a) {
     const uint8_t* vg = (const uint8_t*)a.v;
     uint4 kr[PER], vr[PER];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const int x = tid + i * DEC_THREADS, row = x / PIECES, col = x % PIECES;
+    for (int i = 0; i < PER; ++i) {   // threads past the last piece repeat it
+        const int x = min(tid + i * DEC_THREADS, NPC - 1), row = x / PIECES, col = x % PIECES;
         const size_t off = (kvb + js[row]) * RB + col * 16;
         kr[i] = *(const uint4*)(kg + off);
         vr[i] = *(const uint4*)(vg + off);
     }
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-        const int x = tid + i * DEC_THREADS, row = x / PIECES, col = x % PIECES;
+        const int x = min(tid + i * DEC_THREADS, NPC - 1), row = x / PIECES, col = x % PIECES;
         *(uint4*)(kt + row * ROWB + col * 16) = kr[i];
         *(uint4*)(vt + row * ROWB + col * 16) = vr[i];
     }
@@ -586,10 +588,12 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_combine_kernel(DecArgs a) {
 template <int D>
 static hipError_t dec_d(const DecArgs& a, hipStream_t s) {
     const dim3 ag((unsigned)a.cmax, (unsigned)(a.Hkv * a.Nq), (unsigned)a.Bt);
+    const int G = a.Hq / a.Hkv;
+    const size_t dyn = (size_t)G * (D + dec_chunk(a.f32 != 0)) * sizeof(float);   // q, logits
     if (a.f32)
-        hipLaunchKernelGGL((dec_attn_kernel<D, true>), ag, dim3(DEC_THREADS), 0, s, a);
+        hipLaunchKernelGGL((dec_attn_kernel<D, true>), ag, dim3(DEC_THREADS), dyn, s, a);
     else
-        hipLaunchKernelGGL((dec_attn_kernel<D, false>), ag, dim3(DEC_THREADS), 0, s, a);
+        hipLaunchKernelGGL((dec_attn_kernel<D, false>), ag, dim3(DEC_THREADS), dyn, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t rows = (size_t)a.Bt * a.Hq * a.Nq;

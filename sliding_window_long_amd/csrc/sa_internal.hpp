@@ -223,7 +223,7 @@ inline int tok_units(int N) { return tok_unit_base(N, tok_chunks(N, tok_blocks(N
 constexpr int kDecMaxQ = 64;
 // Attended keys per decode attention workgroup (its K and V rows are staged
 // in LDS together: 128 rows of 16-bit elements or 64 rows of fp32).
-__host__ __device__ constexpr int dec_chunk(bool f32) { return f32 ? 64 : 128; }
+__host__ __device__ constexpr int dec_chunk(bool f32) { return f32 ? 64 : 64; }
 struct DecArgs {
     const void* q;          // [Bt, Hq, Nq, D], bf16 or fp32
     const void* k;          // [Bt, Hkv, Nk, D]

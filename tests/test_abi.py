@@ -144,12 +144,12 @@ def test_gate_variant_workspace(lib):
 
 
 def test_decode_workspace(lib):
-    # partials [rows, ceil((min(w, kv_len) + top_t) / 128), d + 2] fp32 (one
-    # per 128-key tile), plus indexer scores [Bt, Nq, kv_len] and the kept lists
+    # partials [rows, ceil((min(w, kv_len) + top_t) / 64), d + 2] fp32 (one
+    # per 64-key tile), plus indexer scores [Bt, Nq, kv_len] and the kept lists
     p = sa.Params(1, 32, 32, 1, 80, window=4096, kv_len=16384)
-    assert sa.sparse_attn_workspace_bytes(p.cfg()) == 32 * 32 * 82 * 4
+    assert sa.sparse_attn_workspace_bytes(p.cfg()) == 32 * 64 * 82 * 4
     p = sa.Params(2, 16, 4, 3, 128, window=128, token_top_k=2048, index_dim=64, kv_len=65536)
-    assert sa.sparse_attn_workspace_bytes(p.cfg()) >= 2 * 3 * 65536 * 4 + 2 * 16 * 3 * 9 * 130 * 4
+    assert sa.sparse_attn_workspace_bytes(p.cfg()) >= 2 * 3 * 65536 * 4 + 2 * 16 * 3 * 34 * 130 * 4
 
 
 def test_workspace_sizes_scale(lib):
