@@ -79,129 +79,142 @@ __device__ __forceinline__ void finish_rows(const RowsArgs& a, f32x16 (&o)[Tile<
 // Query-centric kernel.
 // ---------------------------------------------------------------------------
 
-// S^T tiles of NG 32-row groups of one wave: every K fragment read from LDS
-// feeds the matrix-core ops of all groups.
-template <int D, int SPLIT, int NG>
-__device__ __forceinline__ void qk_tiles(const uint16_t* ks, const bf16x8 (&qf)[NG][SPLIT][Tile<D>::DK],
-                                         f32x16 (&s)[NG][2], int lane) {
-    using T = Tile<D>;
-    const int col = lane & 31, hh = lane >> 5;
+// Masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedVALU = 0x002, kSchedMFMA = 0x008, kSchedDSRead = 0x100;
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Direct global -> LDS loads of a 64-key tile (buffer_load ... lds, 16 bytes
+// per lane) into an LDS image with row stride S elements: instruction i
+// writes LDS bytes 1024 i .. 1024 i + 1023 of the image, lane l the 16-byte
+// chunk p = 64 i + l = row * (S / 8) + c.  Chunks past the row's D elements
+// (padding, never read) get a copy of the row's last chunk, so every lane
+// loads and no lane masking is needed.  The S / 8 instructions of a plane are
+// dealt round-robin to the waves; where they do not divide evenly, the waves
+// past the last one repeat it (the same bytes to the same LDS address), so
+// every wave issues the same count with no branches.
+template <int D, int S>
+struct TileDma {
+    static constexpr int NI = S / 8;                           // instructions per plane
+    static constexpr int PER = (NI + NWAVES - 1) / NWAVES;     // per wave
+    int voff[PER];   // byte offset of this lane's chunk from the tile's first key
+    __device__ __forceinline__ static int inst(int wave, int j) { return min(wave + NWAVES * j, NI - 1); }
+    __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
-    for (int g = 0; g < NG; ++g) s[g][0] = s[g][1] = f32x16{};
-#pragma unroll
-    for (int k_ = 0; k_ < T::DK; ++k_)
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-            const int off = (sub * 32 + col) * T::KS + k_ * 16 + 8 * hh;
-            const bf16x8 a = *(const bf16x8*)(ks + off);
-#pragma unroll
-            for (int g = 0; g < NG; ++g) {
-                s[g][sub] = mfma32(a, qf[g][0][k_], s[g][sub]);
-                if constexpr (SPLIT == 2) {
-                    s[g][sub] = mfma32(a, qf[g][1][k_], s[g][sub]);
-                    s[g][sub] = mfma32(*(const bf16x8*)(ks + T::KELEMS + off), qf[g][0][k_], s[g][sub]);
-                }
-            }
+        for (int j = 0; j < PER; ++j) {
+            const int p = 64 * inst(wave, j) + lane, row = p / NI, c = min(p % NI, D / 8 - 1);
+            voff[j] = (row * D + c * 8) * 2;
         }
+    }
+};
+
+// Issue the loads of the tile starting at key kt0 (0 <= kt0 < N) of SPLIT
+// [N, D] planes (byte addresses base[]) into lds (planes PLANE elements
+// apart).  Keys at or past N fall outside the buffer descriptor and load
+// zero (finite data that causality always masks).  Completion is awaited
+// with the memory counter (the barrier at the end of a step).
+template <int D, int SPLIT, int PLANE, class TD>
+__device__ __forceinline__ void dma_tile(const TD& td, const uint64_t* base, int N, int kt0,
+                                         uint16_t* lds, int wave) {
+#if defined(__HIP_DEVICE_COMPILE__)   // the host pass rejects the LDS-pointer builtin
+    const int k0 = __builtin_amdgcn_readfirstlane(kt0);
+    const int bytes = (N - k0) * D * 2;
+#pragma unroll
+    for (int p = 0; p < SPLIT; ++p) {
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(base[p] + (uint64_t)k0 * D * 2), (short)0, bytes, 0x00020000);
+#pragma unroll
+        for (int j = 0; j < TD::PER; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                r, (lds_ptr_t)(lds + p * PLANE + TD::inst(wave, j) * 512), 16, td.voff[j], 0, 0, 0);
+    }
+#endif
 }
 
-// O^T += V^T P^T for NG row groups; every V^T fragment feeds all groups.
-template <int D, int SPLIT, int NG>
-__device__ __forceinline__ void pv_tiles(const uint16_t* vs, const uint4 (&pb)[NG][4],
-                                         const uint4 (&pl)[NG][4], f32x16 (&o)[NG][Tile<D>::DM],
-                                         const int (&voff)[Tile<D>::DM]) {
-    using T = Tile<D>;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int mb = 0; mb < T::DM; ++mb) {
-            const uint16_t* p0 = vs + voff[mb] + 16 * kk * T::VS;
-            const v4i16 lo = read_tr(p0), hi = read_tr(p0 + 8 * T::VS);
-            const auto a8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            if constexpr (SPLIT == 1) {
-#pragma unroll
-                for (int g = 0; g < NG; ++g)
-                    o[g][mb] = mfma32_f16(__builtin_bit_cast(f16x8, a8),
-                                          __builtin_bit_cast(f16x8, pb[g][kk]), o[g][mb]);
-            } else {
-                const bf16x8 av = __builtin_bit_cast(bf16x8, a8);
-                const v4i16 lo2 = read_tr(p0 + T::VELEMS), hi2 = read_tr(p0 + T::VELEMS + 8 * T::VS);
-                const bf16x8 a2 = __builtin_bit_cast(
-                    bf16x8, __builtin_shufflevector(lo2, hi2, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-                for (int g = 0; g < NG; ++g) {
-                    o[g][mb] = mfma32(av, __builtin_bit_cast(bf16x8, pb[g][kk]), o[g][mb]);
-                    o[g][mb] = mfma32(av, __builtin_bit_cast(bf16x8, pl[g][kk]), o[g][mb]);
-                    o[g][mb] = mfma32(a2, __builtin_bit_cast(bf16x8, pb[g][kk]), o[g][mb]);
-                }
-            }
-        }
-}
+template <int V>
+struct Par {
+    static constexpr int value = V;
+};
 
-// A workgroup owns NG * 128 consecutive query rows of one head: wave w holds
-// the 32-row groups w*NG .. w*NG + NG - 1, one row per lane pair in each.
-template <int D, int SPLIT, bool TOK, int NG>
-__global__ __launch_bounds__(NTHREADS, NG == 1 ? 2 : 1) void attn_rows_kernel(RowsArgs a) {
+// A workgroup owns 128 consecutive query rows of one head; wave w holds rows
+// 32w .. 32w + 31, one row per lane pair.
+//
+// The key loop runs over 64-key tiles, skewed by one so that the matrix-core
+// products of one tile have independent vector work beside them:
+//   S_{t+1} = K_{t+1} Q^T, then  O += V_t P_t  with  the mask, row max and
+//   exp2((S_{t+1} - m) c) of S_{t+1} (which give P_{t+1}).
+// K_{t+1} and V_t are in LDS when the step of tile t starts; the step loads
+// K_{t+2} and V_{t+1} straight from global memory into the LDS buffers that
+// tiles t and t - 1 used, and its closing barrier waits for them.  Each
+// buffer is its own LDS array and the loop is unrolled by two, so every
+// access names its buffer at compile time (the compiler then knows that the
+// loads in flight never alias the tiles being read).  With no staging
+// registers, head dims up to 80 fit three workgroups per CU (three waves
+// per SIMD): 11 % faster at d 80 than two workgroups with an extra S tile in
+// registers that moved the exp beside the K Q^T products.
+//
+// Head dims that are not a multiple of 32 (80) pad O^T to 96 rows; those
+// rows take constant ones as their V^T operand, so the matrix cores produce
+// the softmax row sums (of the same fp16 P that weights V) and no vector adds
+// are spent on them.
+template <int D, int SPLIT, bool TOK>
+__global__ __launch_bounds__(NTHREADS, D <= 80 && SPLIT == 1 ? 3 : 2) void attn_rows_kernel(RowsArgs a) {
     using T = Tile<D>;
-    constexpr int RTW = RT * NG;   // query rows per workgroup
-    __shared__ __align__(16) uint16_t lds_k[2][SPLIT * T::KELEMS];
-    __shared__ __align__(16) uint16_t lds_v[2][SPLIT * T::VELEMS];
+    constexpr bool ONES = T::DPAD > D;
+    // V row stride: measured fastest for the transposing reads of this
+    // pattern on gfx950 (96 for d 80, 160 for d 128; 11 % and 18 % faster
+    // than 80 and 144).
+    constexpr int VS = D == 80 ? 96 : D == 128 ? 160 : T::VS;
+    constexpr int VELEMS = KT * VS;
+    __shared__ __align__(16) uint16_t lds_k0[SPLIT * T::KELEMS], lds_k1[SPLIT * T::KELEMS];
+    __shared__ __align__(16) uint16_t lds_v0[SPLIT * VELEMS], lds_v1[SPLIT * VELEMS];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int col = lane & 31, hh = lane >> 5;
     const int BH = a.Bt * a.Hq;
-    const int ntiles = (a.N + RTW - 1) / RTW;
+    const int ntiles = (a.N + RT - 1) / RT;
     const int bh = blockIdx.x % BH;
     const int tile = ntiles - 1 - (int)(blockIdx.x / BH);   // longest rows first
     const int b = bh / a.Hq, h = bh % a.Hq, G = a.Hq / a.Hkv, g_kv = h / G;
     const int N = a.N;
-    const int r0 = tile * RTW;
+    const int r0 = tile * RT;
 
     const size_t kvoff = (size_t)(b * a.Hkv + g_kv) * N * D;
-    const uint16_t* kp[2] = {a.k[0] + kvoff, SPLIT == 2 ? a.k[1] + kvoff : nullptr};
-    const uint16_t* vp[2] = {a.v[0] + kvoff, SPLIT == 2 ? a.v[1] + kvoff : nullptr};
-
-    const int wu = __builtin_amdgcn_readfirstlane(wave);   // wave-uniform
-    int row[NG], q0[NG], q1[NG];
-    bool row_ok[NG];
-    size_t prow[NG];   // flat row ids
-    bf16x8 qf[NG][SPLIT][T::DK];
+    uint64_t kb[SPLIT], vb[SPLIT];   // workgroup-uniform byte addresses
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-        q0[g] = r0 + (wu * NG + g) * 32;
-        q1[g] = min(q0[g] + 31, N - 1);
-        row[g] = q0[g] + col;
-        row_ok[g] = row[g] < N;
-        prow[g] = (size_t)bh * N + row[g];
-        load_q<D, SPLIT>(qf[g], a.q, prow[g] * D, row_ok[g], hh);
+    for (int p = 0; p < SPLIT; ++p) {
+        kb[p] = uniform_u64((uint64_t)(a.k[p] + kvoff));
+        vb[p] = uniform_u64((uint64_t)(a.v[p] + kvoff));
     }
 
-    // Block-gate state of each row: its block, the kept near blocks as a
-    // bit mask over (own block - 1 - bit), and the count of far blocks.
-    int row_blk[NG], nfar[NG];
-    uint32_t near_bits[NG];
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-        row_blk[g] = 0;
-        nfar[g] = 0;
-        near_bits[g] = 0;
-        if (a.gate) {
-            row_blk[g] = (row_ok[g] ? row[g] : N - 1) / a.B;
-            if (row_ok[g]) {
-                const int32_t* sr = a.sel + prow[g] * a.top_k;
-                for (int x = 0; x < a.top_k; ++x) {
-                    const int cblk = sr[x];
-                    if (cblk < 0) break;
-                    const int dlt = row_blk[g] - cblk;
-                    if (dlt > a.span) ++nfar[g];
-                    else if (dlt >= 1 && dlt <= 32) near_bits[g] |= 1u << (dlt - 1);
-                }
+    const int wu = __builtin_amdgcn_readfirstlane(wave);   // wave-uniform
+    const int q0 = r0 + wu * 32, q1 = min(q0 + 31, N - 1);
+    const int row = q0 + col;
+    const bool row_ok = row < N;
+    const size_t prow = (size_t)bh * N + row;   // flat row id
+    bf16x8 qf[SPLIT][T::DK];
+    load_q<D, SPLIT>(qf, a.q, prow * D, row_ok, hh);
+
+    // Block-gate state of the row: its block, the kept near blocks as a bit
+    // mask over (own block - 1 - bit), and the count of far blocks.
+    int row_blk = 0, nfar = 0;
+    uint32_t near_bits = 0;
+    if (a.gate) {
+        row_blk = (row_ok ? row : N - 1) / a.B;
+        if (row_ok) {
+            const int32_t* sr = a.sel + prow * a.top_k;
+            for (int x = 0; x < a.top_k; ++x) {
+                const int cblk = sr[x];
+                if (cblk < 0) break;
+                const int dlt = row_blk - cblk;
+                if (dlt > a.span) ++nfar;
+                else if (dlt >= 1 && dlt <= 32) near_bits |= 1u << (dlt - 1);
             }
         }
     }
 
     // Key range of the workgroup.
-    const int r_hi = min(r0 + RTW - 1, N - 1);
+    const int r_hi = min(r0 + RT - 1, N - 1);
     auto lower_key = [&](int r) {
         if (TOK) return 0;   // selected tokens can be anywhere before r
         int lo = r;
@@ -210,62 +223,60 @@ __global__ __launch_bounds__(NTHREADS, NG == 1 ? 2 : 1) void attn_rows_kernel(Ro
         return max(lo, 0);
     };
     const int t_begin = lower_key(r0) / KT, t_end = r_hi / KT;
+    const int n_t = t_end - t_begin + 1;
     const float c = a.scale * kLog2e;
     const uint32_t wl_window = a.window > 0 ? (uint32_t)a.window : 0u;
 
-    zero_v_init<D, SPLIT>(&lds_v[0][0], tid);
-
-    f32x16 o[NG][T::DM];
-    RowState rs[NG];
-    uint4 pb[NG][4], pl[NG][4];
+    f32x16 o[T::DM];
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-#pragma unroll
-        for (int mb = 0; mb < T::DM; ++mb) o[g][mb] = f32x16{};
-        rs[g] = RowState{-INFINITY, 0.f, 1.f, false};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) pb[g][kk] = pl[g][kk] = make_uint4(0, 0, 0, 0);
-    }
+    for (int mb = 0; mb < T::DM; ++mb) o[mb] = f32x16{};
+    RowState rs{-INFINITY, 0.f, 1.f, false};
+    uint4 pb[4], pl[4];
 
     int voff[T::DM];
 #pragma unroll
-    for (int mb = 0; mb < T::DM; ++mb) voff[mb] = v_lane_offset<D>(lane, mb);
-    Stage<D, SPLIT> kst, vst;
-    const TileSrc<D, SPLIT> ksrc = tile_src<D, SPLIT>(kp, N, tid), vsrc = tile_src<D, SPLIT>(vp, N, tid);
-    load_tile<D, SPLIT>(kst, ksrc, t_begin * KT);
-    store_tile<D, SPLIT, T::KS, T::KELEMS>(kst, lds_k[0], tid);
-    __syncthreads();
+    for (int mb = 0; mb < T::DM; ++mb) voff[mb] = v_lane_offset<D, VS, ONES>(lane, mb);
+    const bool pad = ONES && ((lane >> 4) & 1);   // lanes of the padding dims in the last row block
+    TileDma<D, T::KS> kd;
+    TileDma<D, VS> vd;
+    kd.init(wu, lane);
+    vd.init(wu, lane);
+    auto load_k = [&](int t, uint16_t* dst) { dma_tile<D, SPLIT, T::KELEMS>(kd, kb, N, t * KT, dst, wu); };
+    auto load_v = [&](int t, uint16_t* dst) { dma_tile<D, SPLIT, VELEMS>(vd, vb, N, t * KT, dst, wu); };
 
-    // Mask of key tile t for the rows of group g: keys a row does not attend
-    // become -inf (a tile past a group's rows is fully masked).  Tiles that
-    // are entirely inside every row's window, or inside every row's own
-    // block, need no mask (wave-uniform test).
-    auto mask_t = [&](f32x16 (&sv)[2], int t, int g) {
+    // Mask of key tile t: keys the row does not attend become -inf (a tile
+    // past the wave's rows is fully masked).  Tiles that are entirely inside
+    // every row's window, or inside every row's own block, need no mask
+    // (wave-uniform test).
+    // Token gate: this lane's keep bits for key tile t; key tiles past the
+    // wave's rows hold no kept key, and a wave past the last row has no mask.
+    // Only 32-key halves kc <= rt are written; a half past the row tile (kc
+    // = rt + 1 when rt is even) is all future keys: cleared.
+    auto tok_word = [&](int t) -> uint32_t {
+        if constexpr (!TOK) return 0u;
+        const int nt32 = (N + 31) / 32, nt64 = (N + KT - 1) / KT, rt = q0 / 32;
+        uint32_t tword = t <= rt / 2 && q0 < N
+                             ? a.tokmask[(((size_t)b * nt32 + rt) * nt64 + t) * 64 + lane]
+                             : 0u;
+        if (2 * t + 1 > rt) tword &= 0xffffu;
+        return tword;
+    };
+    auto mask_t = [&](f32x16 (&sv)[2], int t, uint32_t tword) {
         const int kt0 = t * KT;
-        const int rk = row[g] - kt0 - 4 * hh;
+        const int rk = row - kt0 - 4 * hh;
         if constexpr (TOK) {
-            // This lane's keep bits for the tile; key tiles past the group's
-            // rows hold no kept key, and a group past the last row has no
-            // mask.  Only 32-key halves kc <= rt are written; a half past the
-            // row tile (kc = rt + 1 when rt is even) is all future keys:
-            // cleared.
-            const int nt32 = (N + 31) / 32, nt64 = (N + KT - 1) / KT, rt = q0[g] / 32;
-            uint32_t tword = t <= rt / 2 && q0[g] < N
-                                 ? a.tokmask[(((size_t)b * nt32 + rt) * nt64 + t) * 64 + lane]
-                                 : 0u;
-            if (2 * t + 1 > rt) tword &= 0xffffu;
-            const bool near = kt0 + KT - 1 >= q0[g] - a.window + 1;   // tile meets a window
+            const bool near = kt0 + KT - 1 >= q0 - a.window + 1;   // tile meets a window
             mask_tile_tok(sv, rk, wl_window, near, tword);
         } else {
-            const bool full = kt0 + KT - 1 <= q0[g] &&
-                              ((a.window > 0 && q1[g] - kt0 < a.window) ||
-                               (a.gate && kt0 / a.B == q0[g] / a.B && q1[g] / a.B == q0[g] / a.B));
+            const bool full = kt0 + KT - 1 <= q0 &&
+                              ((a.window > 0 && q1 - kt0 < a.window) ||
+                               (a.gate && kt0 / a.B == q0 / a.B && q1 / a.B == q0 / a.B));
             if (!full) {
                 uint32_t wl = wl_window;
                 if (a.gate) {
-                    const int dlt = row_blk[g] - kt0 / a.B;
+                    const int dlt = row_blk - kt0 / a.B;
                     const bool blk_ok = dlt == 0 || (dlt >= 1 && dlt <= a.span && dlt <= 32 &&
-                                                     ((near_bits[g] >> (dlt - 1)) & 1u));
+                                                     ((near_bits >> (dlt - 1)) & 1u));
                     if (blk_ok) wl = 0x80000000u;
                 }
                 mask_tile(sv, rk, wl);
@@ -273,32 +284,76 @@ __global__ __launch_bounds__(NTHREADS, NG == 1 ? 2 : 1) void attn_rows_kernel(Ro
         }
     };
 
-    // One-stage skew: the step of tile t computes S_t, O += V_{t-1} P_{t-1}
-    // and P_t; V is staged one tile behind K.
-    for (int t = t_begin; t <= t_end; ++t) {
-        const int it = t - t_begin;
-        load_tile<D, SPLIT>(kst, ksrc, min(t + 1, t_end) * KT);
-        load_tile<D, SPLIT>(vst, vsrc, t * KT);
-#pragma unroll
-        for (int g = 0; g < NG; ++g) apply_rescale<D>(o[g], rs[g]);
-        f32x16 sv[NG][2];
-        qk_tiles<D, SPLIT, NG>(lds_k[it & 1], qf, sv, lane);
-#pragma unroll
-        for (int g = 0; g < NG; ++g) mask_t(sv[g], t, g);
-        pv_tiles<D, SPLIT, NG>(lds_v[(it + 1) & 1], pb, pl, o, voff);
-#pragma unroll
-        for (int g = 0; g < NG; ++g) softmax_tile<SPLIT>(sv[g], rs[g], c, pb[g], pl[g]);
-        store_tile<D, SPLIT, T::KS, T::KELEMS>(kst, lds_k[(it + 1) & 1], tid);
-        store_tile<D, SPLIT, T::VS, T::VELEMS>(vst, lds_v[it & 1], tid);
-        __syncthreads();
-    }
-#pragma unroll
-    for (int g = 0; g < NG; ++g) apply_rescale<D>(o[g], rs[g]);
-    pv_tiles<D, SPLIT, NG>(lds_v[(t_end - t_begin) & 1], pb, pl, o, voff);
+    // Prologue: K_0 and V_0 into LDS; S_0 with its mask and max while K_1
+    // loads.
+    const uint32_t tw0 = tok_word(t_begin);
+    load_k(t_begin, lds_k0);
+    load_v(t_begin, lds_v0);
+    __syncthreads();
+    load_k(min(t_begin + 1, t_end), lds_k1);
+    f32x16 s0[2];
+    qk_tile<D, SPLIT>(lds_k0, qf, s0, lane);
+    mask_t(s0, t_begin, tw0);
+    max_tile(s0, rs, c);
+    exp_tile<SPLIT, !ONES>(s0, rs, c, pb, pl);
+    __syncthreads();
 
+    // Step of relative tile it < n_t - 1 (buffer parity PAR = it & 1):
+    // consumes P_it, produces S_{it+1} and P_{it+1} (in sn and pb, pl).
+    auto step = [&](auto par, int it, f32x16 (&sn)[2]) {
+        constexpr int PAR = decltype(par)::value;
+        uint16_t* const k_next = PAR ? lds_k0 : lds_k1;   // K_{it+1}
+        uint16_t* const k_free = PAR ? lds_k1 : lds_k0;   // K_it: done
+        uint16_t* const v_cur = PAR ? lds_v1 : lds_v0;    // V_it
+        uint16_t* const v_free = PAR ? lds_v0 : lds_v1;   // V_{it-1}: done
+        const int t = t_begin + it;
+        // The mask word first: waiting for it then does not wait for the
+        // tile loads issued after it.
+        const uint32_t tw = tok_word(t + 1);
+        load_k(min(t + 2, t_end), k_free);
+        load_v(t + 1, v_free);
+        apply_rescale<D>(o, rs);
+        qk_tile<D, SPLIT>(k_next, qf, sn, lane);
+        mask_t(sn, t + 1, tw);
+        pv_tile<D, SPLIT, VS, ONES>(v_cur, pb, pl, o, voff, pad);
+        max_tile(sn, rs, c);
+        exp_tile<SPLIT, !ONES>(sn, rs, c, pb, pl);
+        // 12 (d 80) matrix-core ops and 24 transposing reads with about 90
+        // vector ops.
+        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 4, 0);
 #pragma unroll
-    for (int g = 0; g < NG; ++g)
-        if (row_ok[g]) finish_rows<D>(a, o[g], pair_sum(rs[g].l), rs[g].m, prow[g], h, nfar[g], hh);
+        for (int i = 0; i < T::DM * 4 * (SPLIT == 2 ? 3 : 1); ++i) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedVALU, 8, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
+        }
+        __syncthreads();
+    };
+    // Last tile: its P V only.
+    auto last = [&](auto par) {
+        constexpr int PAR = decltype(par)::value;
+        apply_rescale<D>(o, rs);
+        pv_tile<D, SPLIT, VS, ONES>(PAR ? lds_v1 : lds_v0, pb, pl, o, voff, pad);
+    };
+    // Unrolled by two so that the buffer parity is a constant.
+    int it = 0;
+    for (; it + 2 < n_t; it += 2) {
+        step(Par<0>{}, it, s0);
+        step(Par<1>{}, it + 1, s0);
+    }
+    if (it + 1 < n_t) {
+        step(Par<0>{}, it, s0);
+        last(Par<1>{});
+    } else {
+        last(Par<0>{});
+    }
+
+    if (row_ok) {
+        float lt;
+        if constexpr (ONES) lt = o[T::DM - 1][8];   // O^T row D (hh 0) or D + 4 (hh 1)
+        else lt = pair_sum(rs.l);
+        finish_rows<D>(a, o, lt, rs.m, prow, h, nfar, hh);
+    }
 }
 
 
@@ -343,13 +398,12 @@ static hipError_t rows_d(const RowsArgs& a, hipStream_t s) {
     // One 32-row group per wave.  Two (every K/V fragment read from LDS
     // feeding 64 rows) leave room for one wave per SIMD and measured slower
     // on every shape (d = 80 window: 1.20 vs 0.94 ms).
-    constexpr int NG = 1;
-    const int ntiles = (a.N + RT * NG - 1) / (RT * NG);
+    const int ntiles = (a.N + RT - 1) / RT;
     const unsigned grid = (unsigned)(ntiles * a.Bt * a.Hq);
     if (a.tokmask)
-        hipLaunchKernelGGL((attn_rows_kernel<D, SPLIT, true, NG>), dim3(grid), dim3(NTHREADS), 0, s, a);
+        hipLaunchKernelGGL((attn_rows_kernel<D, SPLIT, true>), dim3(grid), dim3(NTHREADS), 0, s, a);
     else
-        hipLaunchKernelGGL((attn_rows_kernel<D, SPLIT, false, NG>), dim3(grid), dim3(NTHREADS), 0, s, a);
+        hipLaunchKernelGGL((attn_rows_kernel<D, SPLIT, false>), dim3(grid), dim3(NTHREADS), 0, s, a);
     return hipGetLastError();
 }
 

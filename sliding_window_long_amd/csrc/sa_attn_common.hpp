@@ -60,6 +60,14 @@ struct TileSrc {
     int off[Tile<D>::CPT];
 };
 
+// Workgroup barrier ordering LDS accesses only: global loads in flight stay
+// in flight (__syncthreads waits for them too).
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ uint64_t uniform_u64(uint64_t u) {
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
@@ -209,17 +217,19 @@ __device__ __forceinline__ v4i16 read_tr(const uint16_t* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
 }
 
-// Per-lane offset (elements) into a V tile for the V^T operand of O^T row
-// block mb: lane group G = lane/16 covers dims mb*32 + 16*(G%2) .. +15 and
-// key half h = G/2; source lane 4r + q of the group points at key 4h + r,
-// dims +4q, so lane i of the group receives keys 4h..4h+3 of dim +i.  Dims
-// past D (padding rows of O^T, discarded) read dim 0 instead.
-template <int D>
+// Per-lane offset (elements) into a V tile of row stride VS for the V^T
+// operand of O^T row block mb: lane group G = lane/16 covers dims mb*32 +
+// 16*(G%2) .. +15 and key half h = G/2; source lane 4r + q of the group
+// points at key 4h + r, dims +4q, so lane i of the group receives keys
+// 4h..4h+3 of dim +i.  Dims past D (padding rows of O^T) read dim 0 and are
+// discarded, or, with PAD_READ, read their own columns (which then must exist
+// in the tile: the row-sum columns of the query-centric kernel).
+template <int D, int VS = Tile<D>::VS, bool PAD_READ = false>
 __device__ __forceinline__ int v_lane_offset(int lane, int mb) {
     const int j = lane & 15, r = j >> 2, q = j & 3, G = lane >> 4, h = G >> 1;
     int dim = mb * 32 + 16 * (G & 1) + 4 * q;
-    if (dim >= D) dim = 0;
-    return (4 * h + r) * Tile<D>::VS + dim;
+    if (!PAD_READ && dim >= D) dim = 0;
+    return (4 * h + r) * VS + dim;
 }
 
 // O^T += V^T P^T for one tile.  For contraction step kk (keys 16kk..16kk+15)
@@ -227,26 +237,45 @@ __device__ __forceinline__ int v_lane_offset(int lane, int mb) {
 // bf16 inputs: V (converted once) and P are fp16 -- P keeps 11 significant
 // bits, which the few-key rows need to stay within the output tolerance.
 // fp32 inputs: hi/lo bf16 splits of V and P, three products.
-template <int D, int SPLIT>
+//
+// ONES (head dims with padding rows in O^T): lanes with pad set (the padding
+// dims of the last row block) take constant ones (zero in the low plane)
+// instead of what they read, so those rows of O^T accumulate the row sums of
+// P.  Their reads must stay inside the tile.
+template <int D, int SPLIT, int VS = Tile<D>::VS, bool ONES = false>
 __device__ __forceinline__ void pv_tile(const uint16_t* vs, const uint4 (&pb)[4],
                                         const uint4 (&pl)[4], f32x16 (&o)[Tile<D>::DM],
-                                        const int (&voff)[Tile<D>::DM]) {
+                                        const int (&voff)[Tile<D>::DM], bool pad = false) {
     using T = Tile<D>;
+    constexpr int VELEMS = KT * VS;
+    constexpr uint32_t one2 = SPLIT == 1 ? 0x3C003C00u : 0x3F803F80u;   // fp16 / bf16 1.0 pairs
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
         for (int mb = 0; mb < T::DM; ++mb) {
-            const uint16_t* p0 = vs + voff[mb] + 16 * kk * T::VS;
-            const v4i16 lo = read_tr(p0), hi = read_tr(p0 + 8 * T::VS);
-            const auto a8 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            const uint16_t* p0 = vs + voff[mb] + 16 * kk * VS;
+            const v4i16 lo = read_tr(p0), hi = read_tr(p0 + 8 * VS);
+            uint4 u = __builtin_bit_cast(uint4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            if (ONES && mb == T::DM - 1) {
+                u.x = pad ? one2 : u.x;
+                u.y = pad ? one2 : u.y;
+                u.z = pad ? one2 : u.z;
+                u.w = pad ? one2 : u.w;
+            }
             if constexpr (SPLIT == 1) {
-                o[mb] = mfma32_f16(__builtin_bit_cast(f16x8, a8), __builtin_bit_cast(f16x8, pb[kk]),
+                o[mb] = mfma32_f16(__builtin_bit_cast(f16x8, u), __builtin_bit_cast(f16x8, pb[kk]),
                                    o[mb]);
             } else {
-                const bf16x8 a = __builtin_bit_cast(bf16x8, a8);
-                const v4i16 lo2 = read_tr(p0 + T::VELEMS), hi2 = read_tr(p0 + T::VELEMS + 8 * T::VS);
-                const bf16x8 a2 = __builtin_bit_cast(
-                    bf16x8, __builtin_shufflevector(lo2, hi2, 0, 1, 2, 3, 4, 5, 6, 7));
+                const bf16x8 a = __builtin_bit_cast(bf16x8, u);
+                const v4i16 lo2 = read_tr(p0 + VELEMS), hi2 = read_tr(p0 + VELEMS + 8 * VS);
+                uint4 u2 = __builtin_bit_cast(uint4, __builtin_shufflevector(lo2, hi2, 0, 1, 2, 3, 4, 5, 6, 7));
+                if (ONES && mb == T::DM - 1) {
+                    u2.x = pad ? 0u : u2.x;
+                    u2.y = pad ? 0u : u2.y;
+                    u2.z = pad ? 0u : u2.z;
+                    u2.w = pad ? 0u : u2.w;
+                }
+                const bf16x8 a2 = __builtin_bit_cast(bf16x8, u2);
                 o[mb] = mfma32(a, __builtin_bit_cast(bf16x8, pb[kk]), o[mb]);
                 o[mb] = mfma32(a, __builtin_bit_cast(bf16x8, pl[kk]), o[mb]);
                 o[mb] = mfma32(a2, __builtin_bit_cast(bf16x8, pb[kk]), o[mb]);
@@ -295,22 +324,30 @@ __device__ __forceinline__ float tile_max(const f32x16 (&s)[2]) {
     return pair_max(tree_max32(s[0], s[1]));
 }
 
-template <int SPLIT>
-__device__ __forceinline__ void softmax_tile(const f32x16 (&s)[2], RowState& st, float c,
-                                             uint4 (&pb)[4], uint4 (&pl)[4]) {
+// Max phase of the online softmax of a tile: the new exponent base and the
+// pending rescale factor.
+__device__ __forceinline__ void max_tile(const f32x16 (&s)[2], RowState& st, float c) {
     const float mx = tile_max(s);
     // NaN-free test: true while m is still -inf and mx is finite; false when
     // both are -inf (a fully masked tile before the row's first key).
     st.need = mx > st.m + kLazy / c;
     st.alpha = st.need ? fast_exp2((st.m - mx) * c) : 1.f;
     st.m = st.need ? mx : st.m;
+}
+
+// Exp phase: P = exp2((s - m) c) as the P V operand(s), and (LSUM) the row
+// sum, rescaled by the pending factor.  Without LSUM the caller gets the row
+// sum elsewhere (from constant-one rows of V^T).
+template <int SPLIT, bool LSUM = true>
+__device__ __forceinline__ void exp_tile(const f32x16 (&s)[2], RowState& st, float c,
+                                         uint4 (&pb)[4], uint4 (&pl)[4]) {
     const float nb = st.m == -INFINITY ? 0.f : -st.m * c;
     float p[2][16];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
         for (int v = 0; v < 16; ++v) p[sub][v] = fast_exp2(fmaf(s[sub][v], c, nb));
-    st.l = fmaf(st.l, st.alpha, tree_sum32(p));
+    if constexpr (LSUM) st.l = fmaf(st.l, st.alpha, tree_sum32(p));
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
         const float* pk = &p[kk >> 1][8 * (kk & 1)];
@@ -325,6 +362,13 @@ __device__ __forceinline__ void softmax_tile(const f32x16 (&s)[2], RowState& st,
             pl[kk] = __builtin_bit_cast(uint4, to_bf16x8(r));
         }
     }
+}
+
+template <int SPLIT>
+__device__ __forceinline__ void softmax_tile(const f32x16 (&s)[2], RowState& st, float c,
+                                             uint4 (&pb)[4], uint4 (&pl)[4]) {
+    max_tile(s, st, c);
+    exp_tile<SPLIT>(s, st, c, pb, pl);
 }
 
 // Rescale O by the factor the last softmax left pending (rare: only when a
