@@ -82,6 +82,14 @@ __device__ __forceinline__ void finish_rows(const RowsArgs& a, f32x16 (&o)[Tile<
 // Masks of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedVALU = 0x002, kSchedMFMA = 0x008, kSchedDSRead = 0x100;
 
+// An empty asm that reads x: its computation stays before this point (the
+// compiler would otherwise sink the softmax of a step past the step's closing
+// barrier, next to its only use in the following step, where nothing runs
+// beside it on the matrix cores).
+__device__ __forceinline__ void pin(const uint4& x) {
+    asm volatile("" ::"v"(x.x), "v"(x.y), "v"(x.z), "v"(x.w));
+}
+
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // Direct global -> LDS loads of a 64-key tile (buffer_load ... lds, 16 bytes
@@ -326,6 +334,11 @@ __global__ __launch_bounds__(NTHREADS, D <= 80 && SPLIT == 1 ? 3 : 2) void attn_
             __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
             __builtin_amdgcn_sched_group_barrier(kSchedVALU, 8, 0);
             __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 2, 0);
+        }
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            pin(pb[kk]);
+            if constexpr (SPLIT == 2) pin(pl[kk]);
         }
         __syncthreads();
     };
