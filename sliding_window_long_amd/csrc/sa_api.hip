@@ -508,6 +508,7 @@ int sparse_attn_fwd(const void* q, const void* k, const void* v, const sparse_at
             ba.scale = P.scale;
             ba.chunk_list = ca.chunk_list; ba.chunk_start = ca.chunk_start;
             ba.list_off = ca.list_off; ba.entries = ca.entries; ba.n_chunks = ca.n_chunks;
+            ba.entries_cap = (int)P.max_entries;
             ba.part_o = part_o; ba.part_lse = part_lse; ba.kslots = P.kslots;
             StageScope t("attn_far_blocks", s);
             if (!ok(sa::launch_blocks(ba, P.D, split, P.max_chunks, s))) return SA_E_HIP;

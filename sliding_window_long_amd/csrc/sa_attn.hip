@@ -79,71 +79,6 @@ __device__ __forceinline__ void finish_rows(const RowsArgs& a, f32x16 (&o)[Tile<
 // Query-centric kernel.
 // ---------------------------------------------------------------------------
 
-// Masks of __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedVALU = 0x002, kSchedMFMA = 0x008, kSchedDSRead = 0x100;
-
-// An empty asm that reads x: its computation stays before this point (the
-// compiler would otherwise sink the softmax of a step past the step's closing
-// barrier, next to its only use in the following step, where nothing runs
-// beside it on the matrix cores).
-__device__ __forceinline__ void pin(const uint4& x) {
-    asm volatile("" ::"v"(x.x), "v"(x.y), "v"(x.z), "v"(x.w));
-}
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// Direct global -> LDS loads of a 64-key tile (buffer_load ... lds, 16 bytes
-// per lane) into an LDS image with row stride S elements: instruction i
-// writes LDS bytes 1024 i .. 1024 i + 1023 of the image, lane l the 16-byte
-// chunk p = 64 i + l = row * (S / 8) + c.  Chunks past the row's D elements
-// (padding, never read) get a copy of the row's last chunk, so every lane
-// loads and no lane masking is needed.  The S / 8 instructions of a plane are
-// dealt round-robin to the waves; where they do not divide evenly, the waves
-// past the last one repeat it (the same bytes to the same LDS address), so
-// every wave issues the same count with no branches.
-template <int D, int S>
-struct TileDma {
-    static constexpr int NI = S / 8;                           // instructions per plane
-    static constexpr int PER = (NI + NWAVES - 1) / NWAVES;     // per wave
-    int voff[PER];   // byte offset of this lane's chunk from the tile's first key
-    __device__ __forceinline__ static int inst(int wave, int j) { return min(wave + NWAVES * j, NI - 1); }
-    __device__ __forceinline__ void init(int wave, int lane) {
-#pragma unroll
-        for (int j = 0; j < PER; ++j) {
-            const int p = 64 * inst(wave, j) + lane, row = p / NI, c = min(p % NI, D / 8 - 1);
-            voff[j] = (row * D + c * 8) * 2;
-        }
-    }
-};
-
-// Issue the loads of the tile starting at key kt0 (0 <= kt0 < N) of SPLIT
-// [N, D] planes (byte addresses base[]) into lds (planes PLANE elements
-// apart).  Keys at or past N fall outside the buffer descriptor and load
-// zero (finite data that causality always masks).  Completion is awaited
-// with the memory counter (the barrier at the end of a step).
-template <int D, int SPLIT, int PLANE, class TD>
-__device__ __forceinline__ void dma_tile(const TD& td, const uint64_t* base, int N, int kt0,
-                                         uint16_t* lds, int wave) {
-#if defined(__HIP_DEVICE_COMPILE__)   // the host pass rejects the LDS-pointer builtin
-    const int k0 = __builtin_amdgcn_readfirstlane(kt0);
-    const int bytes = (N - k0) * D * 2;
-#pragma unroll
-    for (int p = 0; p < SPLIT; ++p) {
-        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(base[p] + (uint64_t)k0 * D * 2), (short)0, bytes, 0x00020000);
-#pragma unroll
-        for (int j = 0; j < TD::PER; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                r, (lds_ptr_t)(lds + p * PLANE + TD::inst(wave, j) * 512), 16, td.voff[j], 0, 0, 0);
-    }
-#endif
-}
-
-template <int V>
-struct Par {
-    static constexpr int value = V;
-};
-
 // A workgroup owns 128 consecutive query rows of one head; wave w holds rows
 // 32w .. 32w + 31, one row per lane pair.
 //
@@ -169,10 +104,7 @@ template <int D, int SPLIT, bool TOK>
 __global__ __launch_bounds__(NTHREADS, D <= 80 && SPLIT == 1 ? 3 : 2) void attn_rows_kernel(RowsArgs a) {
     using T = Tile<D>;
     constexpr bool ONES = T::DPAD > D;
-    // V row stride: measured fastest for the transposing reads of this
-    // pattern on gfx950 (96 for d 80, 160 for d 128; 11 % and 18 % faster
-    // than 80 and 144).
-    constexpr int VS = D == 80 ? 96 : D == 128 ? 160 : T::VS;
+    constexpr int VS = dma_vs<D>();
     constexpr int VELEMS = KT * VS;
     __shared__ __align__(16) uint16_t lds_k0[SPLIT * T::KELEMS], lds_k1[SPLIT * T::KELEMS];
     __shared__ __align__(16) uint16_t lds_v0[SPLIT * VELEMS], lds_v1[SPLIT * VELEMS];

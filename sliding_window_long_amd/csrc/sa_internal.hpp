@@ -46,6 +46,7 @@ struct BlocksArgs {
     const int32_t* list_off;     // [lists+1] entry offsets of the lists
     const int32_t* entries;      // (i*G + h_local)*kslots + slot
     const int32_t* n_chunks;     // device count of valid chunks
+    int entries_cap;             // capacity of entries
     uint16_t* part_o;
     float* part_lse;
     int kslots;
