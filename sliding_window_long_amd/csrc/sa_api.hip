@@ -47,7 +47,7 @@ struct Plan {
         o_chunk_start, o_entries, o_part_o, o_part_lse, o_tok_split, o_tok_state, o_tok_mask,
         o_tok_qn, o_tok_win, o_tok_kpart, o_tok_scr, o_tok_nslow, o_dec_scores, o_dec_list,
         o_dec_nfar, o_dec_part, o_qsum, o_cmp_k, o_cmp_v, o_cmp_out, o_k16, o_q16, o_do16,
-        o_delta, o_f8q, o_f8k, o_f8v, o_f8iq, o_f8ik,
+        o_delta, o_near, o_f8q, o_f8k, o_f8v, o_f8iq, o_f8ik,
         o_v16, total;
 };
 
@@ -188,6 +188,7 @@ int make_plan(const sparse_attn_cfg* c, Plan* p, bool bwd = false) {
         P.o_q16 = take(nq * 2);
         P.o_do16 = take(nq * 2);
         P.o_delta = take((size_t)rows * 4);
+        P.o_near = take(P.gate ? (size_t)rows * 4 : 0);
     } else {
         P.o_split = take(P.f32 ? 2 * (nq + 2 * nkv) * 2 : 0);
         P.o_v16 = take(P.f32 ? 0 : nkv * 2);   // fp16 copy of V for the P V products
@@ -652,8 +653,10 @@ int sparse_attn_bwd(const void* q, const void* k, const void* v, const void* out
     ba.sink = cfg->sink; ba.dsink = dsink;
     ba.dq = (uint16_t*)dq; ba.dk = (uint16_t*)dk; ba.dv = (uint16_t*)dv;
     ba.sel = sel; ba.top_k = P.top_k; ba.B = P.B; ba.n = P.n; ba.span = P.span;
+    ba.near_mask = P.gate ? (uint32_t*)(ws + P.o_near) : nullptr;
     ba.kslots = P.kslots;
     ba.list_off = P.far ? ca.list_off : nullptr; ba.entries = P.far ? ca.entries : nullptr;
+    ba.entries_cap = P.far ? (int)P.max_entries : 0;
     ba.chunk_list = ca.chunk_list; ba.chunk_start = ca.chunk_start; ba.n_chunks = ca.n_chunks;
     ba.max_chunks = P.far ? P.max_chunks : 0;
     ba.part_dq = P.far ? (uint16_t*)(ws + P.o_part_o) : nullptr;

@@ -48,6 +48,18 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
         }
         a.delta[r] = dsum;
         h = (int)((r / a.N) % a.Hq);
+        if (a.near_mask) {   // the row's kept near blocks, as the forward attends them
+            const int rb = (int)(r % a.N) / a.B;
+            const int32_t* sr = a.sel + r * a.top_k;
+            uint32_t nm = 0;
+            for (int x = 0; x < a.top_k; ++x) {
+                const int cb = sr[x];
+                if (cb < 0) break;
+                const int dlt = rb - cb;
+                if (dlt >= 1 && dlt <= a.span && dlt <= 32) nm |= 1u << (dlt - 1);
+            }
+            a.near_mask[r] = nm;
+        }
     }
     if (!a.dsink) return;
     float term = (r < rows && a.sink) ? -__expf(a.sink[h] - a.lse[r]) * dsum : 0.f;
@@ -330,33 +342,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_far_dq_kernel(BwdArgs a) {
 // ---------------------------------------------------------------------------
 // dK, dV: a workgroup owns 128 keys of one (batch, kv head).
 // ---------------------------------------------------------------------------
-template <int D>
-struct DkvSmem {
-    using T = Tile<D>;
-    static constexpr int Q = 0;                          // Q rows, K layout (bf16)
-    static constexpr int DO = Q + T::KELEMS;             // dO rows, K layout (bf16)
-    static constexpr int Q16 = DO + T::KELEMS;           // Q rows, V layout (fp16)
-    static constexpr int DO16 = Q16 + T::VELEMS;         // dO rows, V layout (fp16)
-    static constexpr int ELEMS = DO16 + T::VELEMS;
-    static constexpr int BYTES = ELEMS * 2 + 4 * KT * 4; // + lse2, D, row info, row ids
-};
-
-// Gathered 64-row tile: row x of the tile is global row ids[x] (-1: zeros).
-template <int D>
-__device__ __forceinline__ void gather_tile(const uint16_t* base, const int* ids, uint16_t* dst,
-                                            int stride, int tid) {
-    using T = Tile<D>;
-#pragma unroll
-    for (int cc = 0; cc < T::CPT; ++cc) {
-        const int idx = min(tid + cc * NTHREADS, T::CHUNKS - 1);
-        const int r = idx / (D / 8), c8 = idx % (D / 8);
-        const int id = ids[r];
-        uint4 u = make_uint4(0, 0, 0, 0);
-        if (id >= 0) u = *(const uint4*)(base + (size_t)id * D + c8 * 8);
-        *(uint4*)(dst + r * stride + c8 * 8) = u;
-    }
-}
-
 // Mask of an S tile in the key-centric layout (lane = key j, registers =
 // rows i = rt0 + cv + 4hh): keep iff (unsigned)(i - j) < w, or i >= j and
 // the row's info bit for the key's block is set.  rj = rt0 + 4hh - j.
@@ -373,29 +358,74 @@ __device__ __forceinline__ void mask_rows(f32x16 (&s)[2], int rj, uint32_t w, co
         }
 }
 
+// Lane offsets of a gathered 64-row tile in an LDS image of row stride S
+// (the layout of TileDma): instruction j of this wave writes chunk p = 64 i +
+// lane, i = min(wave + NWAVES j, S/8 - 1), of row p / (S/8); chunks past the
+// row's D elements repeat its last one.  row_c packs (row << 8) | element
+// offset of the chunk.
+template <int D, int S>
+struct GatherDma {
+    static constexpr int NI = S / 8;
+    static constexpr int PER = (NI + NWAVES - 1) / NWAVES;
+    int row_c[PER];
+    __device__ __forceinline__ static int inst(int wave, int j) { return min(wave + NWAVES * j, NI - 1); }
+    __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int p = 64 * inst(wave, j) + lane;
+            row_c[j] = ((p / NI) << 8) | (min(p % NI, D / 8 - 1) * 8);
+        }
+    }
+};
+
+// Issue the gather of one [N, D] plane's rows ids[0..63] into an LDS image
+// (global_load_lds, 16 bytes per lane, per-lane 64-bit addresses).  A row id
+// < 0 loads row 0 instead: such rows carry lse = +inf and D = 0, so their P
+// and dS are zero and the data never counts.
+template <int D, int S>
+__device__ __forceinline__ void gather_dma(const GatherDma<D, S>& gd, const uint16_t* base,
+                                           const int* ids, uint16_t* lds, int wave) {
+#if defined(__HIP_DEVICE_COMPILE__)   // the host pass rejects the LDS-pointer builtin
+#pragma unroll
+    for (int j = 0; j < GatherDma<D, S>::PER; ++j) {
+        const int id = ids[gd.row_c[j] >> 8];
+        const uint16_t* src = base + (size_t)(id >= 0 ? id : 0) * D + (gd.row_c[j] & 0xff);
+        __builtin_amdgcn_global_load_lds((const void*)src,
+                                         (lds_ptr_t)(lds + GatherDma<D, S>::inst(wave, j) * 512), 16, 0, 0);
+    }
+#endif
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: a workgroup owns 128 keys of one (batch, kv head) and walks 64-row
+// tiles: (1) the contiguous rows of every head of the group that can reach
+// the keys through the window, the own block or a near kept block; (2) the
+// rows that kept the keys' block as a far block (the forward's compaction
+// lists).  The tile after the current one is gathered straight into the
+// other LDS buffer while the current one is computed, and wave 0 fetches the
+// per-row data (id, lse, D, kept-block bits) two tiles ahead into a ring of
+// three slots.
+// ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkv_kernel(BwdArgs a) {
     using T = Tile<D>;
-    using S = DkvSmem<D>;
-    __shared__ __align__(16) uint8_t smem[S::BYTES];
-    uint16_t* const lq = (uint16_t*)smem + S::Q;
-    uint16_t* const ldo = (uint16_t*)smem + S::DO;
-    uint16_t* const lq16 = (uint16_t*)smem + S::Q16;
-    uint16_t* const ldo16 = (uint16_t*)smem + S::DO16;
-    float* const l_lse = (float*)((uint16_t*)smem + S::ELEMS);
-    float* const l_d = l_lse + KT;
-    int* const l_info = (int*)(l_d + KT);
-    int* const l_ids = l_info + KT;
+    constexpr int VS = dma_vs<D>();
+    constexpr int VEL = KT * VS;
+    __shared__ __align__(16) uint16_t lq0[T::KELEMS], lq1[T::KELEMS], ldo0[T::KELEMS], ldo1[T::KELEMS];
+    __shared__ __align__(16) uint16_t lq16_0[VEL], lq16_1[VEL], ldo16_0[VEL], ldo16_1[VEL];
+    __shared__ float s_lse[3][KT], s_d[3][KT];
+    __shared__ int s_info[3][KT], s_ids[3][KT];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int col = lane & 31, hh = lane >> 5;
+    const int wu = __builtin_amdgcn_readfirstlane(wave);
     const int N = a.N, G = a.Hq / a.Hkv;
     const int ntiles = (N + RT - 1) / RT;
     const int bg = blockIdx.x / ntiles, ktile = blockIdx.x % ntiles;
     const int b = bg / a.Hkv, g = bg % a.Hkv;
     const int k0 = ktile * RT;
     const int k_hi = min(k0 + RT - 1, N - 1);
-    const int j0 = k0 + __builtin_amdgcn_readfirstlane(wave) * 32;
+    const int j0 = k0 + wu * 32;
     const int key = j0 + col;
     const bool ok = key < N;
     const size_t pkey = (size_t)bg * N + (ok ? key : 0);
@@ -413,18 +443,101 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkv_kernel(BwdArgs a) {
     for (int mb = 0; mb < T::DM; ++mb) dv[mb] = dk[mb] = f32x16{};
     int voff[T::DM];
 #pragma unroll
-    for (int mb = 0; mb < T::DM; ++mb) voff[mb] = v_lane_offset<D>(lane, mb);
+    for (int mb = 0; mb < T::DM; ++mb) voff[mb] = v_lane_offset<D, VS>(lane, mb);
     const uint4 zero4[4] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0),
                             make_uint4(0, 0, 0, 0)};
+    GatherDma<D, T::KS> gk;
+    GatherDma<D, VS> gv;
+    gk.init(wu, lane);
+    gv.init(wu, lane);
 
-    // One 64-row tile staged in LDS (rows by id; lse2, D and the info bits
-    // per row set by the caller) against this wave's 32 keys.
-    auto rows_step = [&](int rt0, bool far, int far_kb) {
+    // The row tiles: n_rt contiguous tiles per head of the group, then the
+    // far lists of the keys' (at most two) blocks.
+    int r_end = a.window > 0 ? min(N - 1, k_hi + a.window - 1) : -1;
+    if (a.sel) r_end = max(r_end, min(N - 1, (k_hi / a.B + a.span + 1) * a.B - 1));
+    const int n_rt = r_end >= k0 ? (r_end - k0) / KT + 1 : 0;
+    const int n1 = G * n_rt;
+    // (Scalars, not arrays: a runtime-indexed array would live in scratch,
+    // whose loads wait for every tile load in flight.)
+    int fa0 = 0, fa1 = 0, fb0 = 0, fb1 = 0;   // entry ranges of blocks blk0, blk0 + 1
+    if (a.sel && a.list_off) {
+        const int list = bg * a.n + blk0;
+        if (blk0 * a.B <= k_hi && blk0 < a.n) {
+            fa0 = a.list_off[list];
+            fa1 = a.list_off[list + 1];
+        }
+        if ((blk0 + 1) * a.B <= k_hi && blk0 + 1 < a.n) {
+            fb0 = a.list_off[list + 1];
+            fb1 = a.list_off[list + 2];
+        }
+    }
+    const int fn0 = (fa1 - fa0 + KT - 1) / KT, fn1 = (fb1 - fb0 + KT - 1) / KT;
+    const int n_tiles = n1 + fn0 + fn1;
+
+    // Per-row data of row r of tile i, fetched by wave 0 (r = lane) in three
+    // parts so that no load is waited for before the step's closing barrier:
+    // the far-list entry one step early (ent_of), the row's loads (fetch,
+    // unconditional at a clamped id) and the values into their slot (put).
+    auto ent_of = [&](int i, int r) __attribute__((always_inline)) -> int {
+        if (i < n1 || i >= n_tiles) return -1;
+        const bool second = i - n1 >= fn0;
+        const int ee = (second ? fb0 + (i - n1 - fn0) * KT : fa0 + (i - n1) * KT) + r;
+        return ee < (second ? fb1 : fa1) ? a.entries[min(ee, a.entries_cap - 1)] : -1;
+    };
+    struct RowData {
+        int id, rr;
+        float lse, d;
+        uint32_t nm;
+    };
+    auto fetch = [&](int i, int r, int ent) __attribute__((always_inline)) -> RowData {
+        RowData rd{-1, 0, 0.f, 0.f, 0u};
+        if (i < n1) {
+            const int hl = i / n_rt, rr = k0 + (i % n_rt) * KT + r;
+            rd.rr = rr;
+            if (rr < N) rd.id = (int)((size_t)(b * a.Hq + g * G + hl) * N + rr);
+        } else if (ent >= 0) {   // entry = (i*G + head in group)*kslots + slot
+            const int t2 = ent / a.kslots;
+            rd.id = (int)((size_t)(b * a.Hq + g * G + t2 % G) * N + t2 / G);
+        }
+        const int idc = max(rd.id, 0);
+        rd.lse = a.lse[idc];
+        rd.d = a.delta[idc];
+        if (a.near_mask && i < n1) rd.nm = a.near_mask[idc];
+        return rd;
+    };
+    auto put = [&](const RowData& rd, int i, int sl) __attribute__((always_inline)) {
+        int info = 0;
+        if (a.near_mask && i < n1 && rd.id >= 0) {
+            // Blocks blk0 and blk0 + 1 kept for this row by the forward: its
+            // own block, or a near block it selected.
+            const int rb = rd.rr / a.B;
+#pragma unroll
+            for (int dl = 0; dl < 2; ++dl) {
+                const int dlt = rb - (blk0 + dl);
+                if (dlt == 0 || (dlt >= 1 && dlt <= 32 && ((rd.nm >> (dlt - 1)) & 1u))) info |= 1 << dl;
+            }
+        }
+        s_ids[sl][lane] = rd.id;
+        s_lse[sl][lane] = rd.id >= 0 ? rd.lse * kLog2e : INFINITY;
+        s_d[sl][lane] = rd.id >= 0 ? rd.d : 0.f;
+        s_info[sl][lane] = info;
+    };
+    auto gather = [&](int sl, uint16_t* q_, uint16_t* do_, uint16_t* q16_, uint16_t* do16_) __attribute__((always_inline)) {
+        gather_dma<D, T::KS>(gk, a.q, s_ids[sl], q_, wu);
+        gather_dma<D, T::KS>(gk, a.dout, s_ids[sl], do_, wu);
+        gather_dma<D, VS>(gv, a.q16, s_ids[sl], q16_, wu);
+        gather_dma<D, VS>(gv, a.do16, s_ids[sl], do16_, wu);
+    };
+
+    // Tile i from its buffers against this wave's 32 keys.
+    auto compute = [&](int i, int sl, const uint16_t* q_, const uint16_t* do_, const uint16_t* q16_,
+                       const uint16_t* do16_) __attribute__((always_inline)) {
         f32x16 s[2], dp[2];
-        qk_tile<D, 1>(lq, kf, s, lane);
-        qk_tile<D, 1>(ldo, vf, dp, lane);
-        if (far) {
+        qk_tile<D, 1>(q_, kf, s, lane);
+        qk_tile<D, 1>(do_, vf, dp, lane);
+        if (i >= n1) {
             // every key of the far block, none of the other block
+            const int far_kb = i - n1 < fn0 ? 0 : 1;
             if (kb != far_kb) {
 #pragma unroll
                 for (int sub = 0; sub < 2; ++sub)
@@ -432,17 +545,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkv_kernel(BwdArgs a) {
                     for (int v = 0; v < 16; ++v) s[sub][v] = -INFINITY;
             }
         } else {
-            mask_rows(s, rt0 + 4 * hh - key, wl, l_info, kb, hh);
+            const int rt0 = k0 + (i % n_rt) * KT;
+            mask_rows(s, rt0 + 4 * hh - key, wl, s_info[sl], kb, hh);
         }
-        // p and ds with per-register rows
         float p[2][16], gds[2][16];
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int rr = sub * 32 + 8 * (v >> 2) + (v & 3) + 4 * hh;
-                p[sub][v] = fast_exp2(fmaf(s[sub][v], c, -l_lse[rr]));
-                gds[sub][v] = p[sub][v] * (dp[sub][v] - l_d[rr]);
+                p[sub][v] = fast_exp2(fmaf(s[sub][v], c, -s_lse[sl][rr]));
+                gds[sub][v] = p[sub][v] * (dp[sub][v] - s_d[sl][rr]);
             }
         uint4 pb[4], db[4];
 #pragma unroll
@@ -450,79 +563,51 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkv_kernel(BwdArgs a) {
             pb[kk] = __builtin_bit_cast(uint4, to_f16x8(&p[kk >> 1][8 * (kk & 1)]));
             db[kk] = __builtin_bit_cast(uint4, to_f16x8(&gds[kk >> 1][8 * (kk & 1)]));
         }
-        pv_tile<D, 1>(ldo16, pb, zero4, dv, voff);
-        pv_tile<D, 1>(lq16, db, zero4, dk, voff);
+        pv_tile<D, 1, VS>(do16_, pb, zero4, dv, voff);
+        pv_tile<D, 1, VS>(q16_, db, zero4, dk, voff);
     };
 
-    // (1) contiguous rows of every head of the group: window, own block and
-    // near kept blocks.
-    int r_end = a.window > 0 ? min(N - 1, k_hi + a.window - 1) : -1;
-    if (a.sel) r_end = max(r_end, min(N - 1, (k_hi / a.B + a.span + 1) * a.B - 1));
-    for (int hl = 0; hl < G; ++hl) {
-        const int h = g * G + hl;
-        const size_t hbase = (size_t)(b * a.Hq + h) * N;
-        for (int rt0 = k0; rt0 <= r_end; rt0 += KT) {
-            if (tid < KT) {
-                const int r = rt0 + tid;
-                const bool rok = r < N;
-                l_ids[tid] = rok ? (int)(hbase + r) : -1;
-                l_lse[tid] = rok ? a.lse[hbase + r] * kLog2e : INFINITY;
-                l_d[tid] = rok ? a.delta[hbase + r] : 0.f;
-                int info = 0;
-                if (rok && a.sel) {
-                    const int rb = r / a.B;
-                    const int32_t* sr = a.sel + (hbase + r) * a.top_k;
-                    for (int x = 0; x < a.top_k; ++x) {
-                        const int cb = sr[x];
-                        if (cb < 0) break;
-                        const int dl = cb - blk0;
-                        if ((dl == 0 || dl == 1) && rb - cb <= a.span) info |= 1 << dl;
-                    }
-                }
-                l_info[tid] = info;
-            }
-            __syncthreads();
-            gather_tile<D>(a.q, l_ids, lq, T::KS, tid);
-            gather_tile<D>(a.dout, l_ids, ldo, T::KS, tid);
-            gather_tile<D>(a.q16, l_ids, lq16, T::VS, tid);
-            gather_tile<D>(a.do16, l_ids, ldo16, T::VS, tid);
-            __syncthreads();
-            rows_step(rt0, false, 0);
-            __syncthreads();
+    if (n_tiles > 0) {
+        int ent2 = -1;   // wave 0: this lane's entry of tile i + 2 (far tiles)
+        if (wu == 0) {
+            put(fetch(0, lane, ent_of(0, lane)), 0, 0);
+            if (n_tiles > 1) put(fetch(1, lane, ent_of(1, lane)), 1, 1);
+            ent2 = ent_of(2, lane);
         }
-    }
+        __syncthreads();
+        gather(0, lq0, ldo0, lq16_0, ldo16_0);
+        __syncthreads();
 
-    // (2) rows that kept a block of these keys as a far block.
-    if (a.sel && a.list_off) {
-        for (int fb = 0; fb < 2; ++fb) {
-            const int cb = blk0 + fb;
-            if (cb * a.B > k_hi || cb >= a.n) break;
-            const int list = bg * a.n + cb;
-            const int e0 = a.list_off[list], e1 = a.list_off[list + 1];
-            for (int e = e0; e < e1; e += KT) {
-                if (tid < KT) {
-                    const int ee = e + tid;
-                    int id = -1;
-                    if (ee < e1) {   // entry = (i*G + head in group)*kslots + slot
-                        const int t2 = a.entries[ee] / a.kslots;
-                        const int hl = t2 % G, i = t2 / G;
-                        id = (int)((size_t)(b * a.Hq + g * G + hl) * N + i);
-                    }
-                    l_ids[tid] = id;
-                    l_lse[tid] = id >= 0 ? a.lse[id] * kLog2e : INFINITY;
-                    l_d[tid] = id >= 0 ? a.delta[id] : 0.f;
-                    l_info[tid] = 0;
-                }
-                __syncthreads();
-                gather_tile<D>(a.q, l_ids, lq, T::KS, tid);
-                gather_tile<D>(a.dout, l_ids, ldo, T::KS, tid);
-                gather_tile<D>(a.q16, l_ids, lq16, T::VS, tid);
-                gather_tile<D>(a.do16, l_ids, ldo16, T::VS, tid);
-                __syncthreads();
-                rows_step(0, true, fb);
-                __syncthreads();
+        // Step of tile i (buffer parity PAR = i & 1, data slot i % 3).
+        auto step = [&](auto par, int i) __attribute__((always_inline)) {
+            constexpr int PAR = decltype(par)::value;
+            const bool ahead = wu == 0 && i + 2 < n_tiles;
+            RowData rd{-1, 0, 0.f, 0.f, 0u};
+            int ent3 = -1;
+            if (ahead) {   // loads first: their data is not needed before the barrier
+                rd = fetch(i + 2, lane, ent2);
+                ent3 = ent_of(i + 3, lane);
             }
+            if (i + 1 < n_tiles) {
+                const int sl1 = (i + 1) % 3;
+                if (PAR) gather(sl1, lq0, ldo0, lq16_0, ldo16_0);
+                else gather(sl1, lq1, ldo1, lq16_1, ldo16_1);
+            }
+            const int sl = i % 3;
+            if (PAR) compute(i, sl, lq1, ldo1, lq16_1, ldo16_1);
+            else compute(i, sl, lq0, ldo0, lq16_0, ldo16_0);
+            if (ahead) {
+                put(rd, i + 2, (i + 2) % 3);
+                ent2 = ent3;
+            }
+            __syncthreads();
+        };
+        int i = 0;
+        for (; i + 1 < n_tiles; i += 2) {
+            step(Par<0>{}, i);
+            step(Par<1>{}, i + 1);
         }
+        if (i < n_tiles) step(Par<0>{}, i);
     }
     if (ok) {
         write_rows_bf16<D>(a.dk + pkey * D, dk, a.scale, hh);

@@ -142,8 +142,11 @@ struct BwdArgs {
     uint16_t* dk;
     uint16_t* dv;
     const int32_t* sel;     // [Bt*Hq*N, top_k] or nullptr (no block gate)
+    uint32_t* near_mask;    // [Bt*Hq*N]: bit dlt-1 = block (own - dlt) kept as a near
+                            // block (1 <= dlt <= min(span, 32)); nullptr without gate
     const int32_t* list_off;  // far-row lists of the compaction, or nullptr
     const int32_t* entries;
+    int entries_cap;            // capacity of entries
     const int32_t* chunk_list;  // their chunking (<= 128 entries per chunk)
     const int32_t* chunk_start;
     const int32_t* n_chunks;
