@@ -118,39 +118,89 @@ __device__ __forceinline__ void write_rows_bf16(uint16_t* dst, const f32x16 (&o)
 }
 
 // ---------------------------------------------------------------------------
+// dQ.  Both dQ kernels walk 64-key tiles of contiguous keys; the K, V and
+// fp16 K tiles go straight from global memory into LDS, double-buffered (one
+// LDS array per buffer, the loop unrolled by two), so the next tile loads
+// while the current one is computed.
+// ---------------------------------------------------------------------------
+template <int D>
+struct DqTiles {
+    using T = Tile<D>;
+    static constexpr int VS = dma_vs<D>();
+    static constexpr int VEL = KT * VS;
+    TileDma<D, T::KS> kd;
+    TileDma<D, VS> vd;
+    uint64_t kb[1], vb[1], k16b[1];
+    int N;
+    __device__ __forceinline__ void init(const BwdArgs& a, size_t kvoff, int wave, int lane) {
+        kd.init(wave, lane);
+        vd.init(wave, lane);
+        kb[0] = uniform_u64((uint64_t)(a.k + kvoff));
+        vb[0] = uniform_u64((uint64_t)(a.v + kvoff));
+        k16b[0] = uniform_u64((uint64_t)(a.k16 + kvoff));
+        N = a.N;
+    }
+    // Issue the loads of the tile at key kt0 (0 <= kt0 < N).
+    __device__ __forceinline__ void load(int kt0, uint16_t* lk, uint16_t* lv, uint16_t* lk16, int wave) const {
+        dma_tile<D, 1, T::KELEMS>(kd, kb, N, kt0, lk, wave);
+        dma_tile<D, 1, T::KELEMS>(kd, vb, N, kt0, lv, wave);
+        dma_tile<D, 1, VEL>(vd, k16b, N, kt0, lk16, wave);
+    }
+};
+
+// dQ^T += K^T dS^T for one tile (lane = query row): S^T = K Q^T and dP^T =
+// V dO^T on the bf16 matrix cores, P^T and dS^T, then the fp16 product.
+template <int D>
+__device__ __forceinline__ void dq_tile(const uint16_t* lk, const uint16_t* lv, const uint16_t* lk16,
+                                        const bf16x8 (&qf)[1][Tile<D>::DK], const bf16x8 (&df)[1][Tile<D>::DK],
+                                        f32x16 (&o)[Tile<D>::DM], const int (&voff)[Tile<D>::DM],
+                                        float c, float lse2, float dr, bool masked, int rk, uint32_t wl,
+                                        int lane) {
+    f32x16 s[2], dp[2];
+    qk_tile<D, 1>(lk, qf, s, lane);
+    qk_tile<D, 1>(lv, df, dp, lane);
+    if (masked) mask_tile(s, rk, wl);
+    uint4 pb[4], db[4];
+    p_ds(s, dp, c, lse2, dr, pb, db);
+    const uint4 zero4[4] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0),
+                            make_uint4(0, 0, 0, 0)};
+    pv_tile<D, 1, DqTiles<D>::VS>(lk16, db, zero4, o, voff);
+}
+
+// ---------------------------------------------------------------------------
 // dQ: a workgroup owns 128 query rows of one (batch, head).
 // ---------------------------------------------------------------------------
 template <int D>
-struct DqSmem {
-    using T = Tile<D>;
-    static constexpr int K = 0;                          // K tile, K layout (bf16)
-    static constexpr int V = K + T::KELEMS;              // V tile, K layout (bf16)
-    static constexpr int K16 = V + T::KELEMS;            // K tile, V layout (fp16)
-    static constexpr int ELEMS = K16 + T::VELEMS;
-    static constexpr int BYTES = ELEMS * 2;
-};
-
-template <int D>
 __global__ __launch_bounds__(NTHREADS, 1) void bwd_dq_kernel(BwdArgs a) {
     using T = Tile<D>;
-    using S = DqSmem<D>;
-    __shared__ __align__(16) uint8_t smem[S::BYTES];
-    uint16_t* const lk = (uint16_t*)smem + S::K;
-    uint16_t* const lv = (uint16_t*)smem + S::V;
-    uint16_t* const lk16 = (uint16_t*)smem + S::K16;
+    using DT = DqTiles<D>;
+    __shared__ __align__(16) uint16_t lk0[T::KELEMS], lk1[T::KELEMS], lv0[T::KELEMS], lv1[T::KELEMS];
+    __shared__ __align__(16) uint16_t lk16_0[DT::VEL], lk16_1[DT::VEL];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int col = lane & 31, hh = lane >> 5;
+    const int wu = __builtin_amdgcn_readfirstlane(wave);
     const int N = a.N;
     const int ntiles = (N + RT - 1) / RT;
     const int bh = blockIdx.x / ntiles, rtile = blockIdx.x % ntiles;
     const int b = bh / a.Hq, h = bh % a.Hq, g = h / (a.Hq / a.Hkv);
     const int r0 = rtile * RT;
     const int r_hi = min(r0 + RT - 1, N - 1);
-    const int q0 = r0 + __builtin_amdgcn_readfirstlane(wave) * 32;
+    const int q0 = r0 + wu * 32;
     const int row = q0 + col;
     const bool ok = row < N;
     const size_t prow = (size_t)bh * N + (ok ? row : 0);
+
+    // Near key range of the workgroup: the window span and the blocks within
+    // span below the rows' own blocks.
+    int lo = r0;
+    if (a.window > 0) lo = min(lo, r0 - a.window + 1);
+    if (a.sel) lo = min(lo, (r0 / a.B - a.span) * a.B);
+    const int t_begin = max(lo, 0) / KT, t_end = r_hi / KT;
+    const int n_t = t_end - t_begin + 1;
+    DT dt;
+    dt.init(a, (size_t)(b * a.Hkv + g) * N * D, wu, lane);
+    dt.load(t_begin * KT, lk0, lv0, lk16_0, wu);
 
     bf16x8 qf[1][T::DK], df[1][T::DK];
     load_q<D, 1>(qf, &a.q, prow * D, ok, hh);
@@ -159,68 +209,57 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dq_kernel(BwdArgs a) {
     const float lse2 = ok ? a.lse[prow] * kLog2e : 0.f;
     const float dr = ok ? a.delta[prow] : 0.f;
 
-    // Kept blocks: own and near ones (within span below the own block) are
+    // Kept blocks: own and near ones (the near mask of the delta pass) are
     // attended here; far ones come as partials from bwd_far_dq.  nfar = the
     // row's far blocks (slots 0 .. nfar-1 of its partials).
-    const int32_t* sr = a.sel ? a.sel + prow * a.top_k : nullptr;
     const int row_blk = a.sel ? min(row, N - 1) / a.B : 0;
+    const uint32_t near_bits = a.near_mask && ok ? a.near_mask[prow] : 0u;
     int nfar = 0;
-    if (a.sel && ok)
+    if (a.sel && ok) {
+        const int32_t* sr = a.sel + prow * a.top_k;
         for (int x = 0; x < a.top_k; ++x) {
             const int cb = sr[x];
             if (cb < 0) break;
             nfar += row_blk - cb > a.span;
         }
+    }
     const uint32_t wl_window = a.window > 0 ? (uint32_t)a.window : 0u;
-    int cur = 0;   // this row's cursor into its ascending kept-block list
 
     f32x16 o[T::DM];
 #pragma unroll
     for (int mb = 0; mb < T::DM; ++mb) o[mb] = f32x16{};
     int voff[T::DM];
 #pragma unroll
-    for (int mb = 0; mb < T::DM; ++mb) voff[mb] = v_lane_offset<D>(lane, mb);
-    const size_t kvoff = (size_t)(b * a.Hkv + g) * N * D;
-    const uint16_t* kp[1] = {a.k + kvoff};
-    const uint16_t* vp[1] = {a.v + kvoff};
-    const uint16_t* k16p[1] = {a.k16 + kvoff};
-    const TileSrc<D, 1> ksrc = tile_src<D, 1>(kp, N, tid), vsrc = tile_src<D, 1>(vp, N, tid);
-    const TileSrc<D, 1> k16src = tile_src<D, 1>(k16p, N, tid);
+    for (int mb = 0; mb < T::DM; ++mb) voff[mb] = v_lane_offset<D, DT::VS>(lane, mb);
+    __syncthreads();
 
-    // Near key range of the workgroup: the window span and the blocks within
-    // span below the rows' own blocks.
-    int lo = r0;
-    if (a.window > 0) lo = min(lo, r0 - a.window + 1);
-    if (a.sel) lo = min(lo, (r0 / a.B - a.span) * a.B);
-    const int t_begin = max(lo, 0) / KT, t_end = r_hi / KT;
-    for (int t = t_begin; t <= t_end; ++t) {
+    // Mask of tile t: window keys, and every causal key of a kept block.
+    auto compute = [&](int t, const uint16_t* lk, const uint16_t* lv, const uint16_t* lk16)
+                       __attribute__((always_inline)) {
         const int kt0 = t * KT;
-        Stage<D, 1> st;
-        load_tile<D, 1>(st, ksrc, kt0);
-        store_tile<D, 1, T::KS, T::KELEMS>(st, lk, tid);
-        load_tile<D, 1>(st, vsrc, kt0);
-        store_tile<D, 1, T::KS, T::KELEMS>(st, lv, tid);
-        load_tile<D, 1>(st, k16src, kt0);
-        store_tile<D, 1, T::VS, T::VELEMS>(st, lk16, tid);
-        __syncthreads();
-        // Mask: window keys, and every causal key of a kept block.
         uint32_t wl = wl_window;
-        if (a.sel && ok) {
-            const int blk = kt0 / a.B;
-            while (cur < a.top_k && sr[cur] >= 0 && sr[cur] < blk) ++cur;
-            if (cur < a.top_k && sr[cur] == blk && row_blk - blk <= a.span) wl = 0x80000000u;
+        if (a.sel) {
+            const int dlt = row_blk - kt0 / a.B;
+            if (dlt == 0 || (dlt >= 1 && dlt <= 32 && ((near_bits >> (dlt - 1)) & 1u))) wl = 0x80000000u;
         }
-        f32x16 s[2], dp[2];
-        qk_tile<D, 1>(lk, qf, s, lane);
-        qk_tile<D, 1>(lv, df, dp, lane);
-        mask_tile(s, row - kt0 - 4 * hh, wl);
-        uint4 pb[4], db[4], dl[4];
-        p_ds(s, dp, c, lse2, dr, pb, db);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) dl[kk] = make_uint4(0, 0, 0, 0);
-        pv_tile<D, 1>(lk16, db, dl, o, voff);
+        dq_tile<D>(lk, lv, lk16, qf, df, o, voff, c, lse2, dr, true, row - kt0 - 4 * hh, wl, lane);
+    };
+    auto step = [&](auto par, int it) __attribute__((always_inline)) {
+        constexpr int PAR = decltype(par)::value;
+        if (it + 1 < n_t) {
+            if (PAR) dt.load((t_begin + it + 1) * KT, lk0, lv0, lk16_0, wu);
+            else dt.load((t_begin + it + 1) * KT, lk1, lv1, lk16_1, wu);
+        }
+        if (PAR) compute(t_begin + it, lk1, lv1, lk16_1);
+        else compute(t_begin + it, lk0, lv0, lk16_0);
         __syncthreads();
+    };
+    int it = 0;
+    for (; it + 1 < n_t; it += 2) {
+        step(Par<0>{}, it);
+        step(Par<1>{}, it + 1);
     }
+    if (it < n_t) step(Par<0>{}, it);
     if (!ok) return;
     // dq = scale * near part + the far blocks' partials (already scaled).
 #pragma unroll
@@ -255,32 +294,38 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dq_kernel(BwdArgs a) {
 template <int D>
 __global__ __launch_bounds__(NTHREADS, 1) void bwd_far_dq_kernel(BwdArgs a) {
     using T = Tile<D>;
-    using S = DqSmem<D>;
-    __shared__ __align__(16) uint8_t smem[S::BYTES];
-    uint16_t* const lk = (uint16_t*)smem + S::K;
-    uint16_t* const lv = (uint16_t*)smem + S::V;
-    uint16_t* const lk16 = (uint16_t*)smem + S::K16;
+    using DT = DqTiles<D>;
+    __shared__ __align__(16) uint16_t lk0[T::KELEMS], lk1[T::KELEMS], lv0[T::KELEMS], lv1[T::KELEMS];
+    __shared__ __align__(16) uint16_t lk16_0[DT::VEL], lk16_1[DT::VEL];
 
-    // Chunks of one list are contiguous: give each XCD a contiguous range.
-    const int grid = gridDim.x;
-    const int per_xcd = grid / 8;
-    const int chunk = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-    if (chunk >= *a.n_chunks) return;
+    // Chunks of one list are contiguous: give each XCD a contiguous eighth
+    // of the valid chunks.
+    const int nch = *a.n_chunks;
+    const int per_xcd = (nch + 7) / 8;
+    const int slot8 = (int)(blockIdx.x / 8);
+    const int chunk = (int)(blockIdx.x % 8) * per_xcd + slot8;
+    if (slot8 >= per_xcd || chunk >= nch) return;
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int col = lane & 31, hh = lane >> 5;
+    const int wu = __builtin_amdgcn_readfirstlane(wave);
     const int N = a.N, G = a.Hq / a.Hkv;
     const int list = a.chunk_list[chunk];
     const int e0 = a.chunk_start[chunk];
+    const int e = e0 + wu * 32 + col;
+    const int ent = a.entries[min(e, a.entries_cap - 1)];   // used only below the list end
     const int e_end = min(e0 + RT, a.list_off[list + 1]);
     const int cblk = list % a.n, bg = list / a.n;
     const int b = bg / a.Hkv, g = bg % a.Hkv;
-    const int e = e0 + wave * 32 + col;
+    const int ntile = a.B / KT;
+    DT dt;
+    dt.init(a, (size_t)bg * N * D, wu, lane);
+    dt.load(cblk * a.B, lk0, lv0, lk16_0, wu);
+
     const bool ok = e < e_end;
     int slot = 0;
     size_t prow = 0;
     if (ok) {   // entry = (i*G + head in group)*kslots + slot
-        const int ent = a.entries[e];
         slot = ent % a.kslots;
         const int t2 = ent / a.kslots;
         prow = (size_t)(b * a.Hq + g * G + t2 % G) * N + t2 / G;
@@ -297,33 +342,25 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_far_dq_kernel(BwdArgs a) {
     for (int mb = 0; mb < T::DM; ++mb) o[mb] = f32x16{};
     int voff[T::DM];
 #pragma unroll
-    for (int mb = 0; mb < T::DM; ++mb) voff[mb] = v_lane_offset<D>(lane, mb);
-    const size_t kvoff = (size_t)bg * N * D;
-    const uint16_t* kp[1] = {a.k + kvoff};
-    const uint16_t* vp[1] = {a.v + kvoff};
-    const uint16_t* k16p[1] = {a.k16 + kvoff};
-    const TileSrc<D, 1> ksrc = tile_src<D, 1>(kp, N, tid), vsrc = tile_src<D, 1>(vp, N, tid);
-    const TileSrc<D, 1> k16src = tile_src<D, 1>(k16p, N, tid);
-    const uint4 zero4[4] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0),
-                            make_uint4(0, 0, 0, 0)};
-    for (int t = 0; t < a.B / KT; ++t) {
-        const int kt0 = cblk * a.B + t * KT;
-        Stage<D, 1> st;
-        load_tile<D, 1>(st, ksrc, kt0);
-        store_tile<D, 1, T::KS, T::KELEMS>(st, lk, tid);
-        load_tile<D, 1>(st, vsrc, kt0);
-        store_tile<D, 1, T::KS, T::KELEMS>(st, lv, tid);
-        load_tile<D, 1>(st, k16src, kt0);
-        store_tile<D, 1, T::VS, T::VELEMS>(st, lk16, tid);
+    for (int mb = 0; mb < T::DM; ++mb) voff[mb] = v_lane_offset<D, DT::VS>(lane, mb);
+    __syncthreads();
+
+    auto step = [&](auto par, int t) __attribute__((always_inline)) {
+        constexpr int PAR = decltype(par)::value;
+        if (t + 1 < ntile) {
+            if (PAR) dt.load(cblk * a.B + (t + 1) * KT, lk0, lv0, lk16_0, wu);
+            else dt.load(cblk * a.B + (t + 1) * KT, lk1, lv1, lk16_1, wu);
+        }
+        if (PAR) dq_tile<D>(lk1, lv1, lk16_1, qf, df, o, voff, c, lse2, dr, false, 0, 0u, lane);
+        else dq_tile<D>(lk0, lv0, lk16_0, qf, df, o, voff, c, lse2, dr, false, 0, 0u, lane);
         __syncthreads();
-        f32x16 s[2], dp[2];
-        qk_tile<D, 1>(lk, qf, s, lane);
-        qk_tile<D, 1>(lv, df, dp, lane);
-        uint4 pb[4], db[4];
-        p_ds(s, dp, c, lse2, dr, pb, db);
-        pv_tile<D, 1>(lk16, db, zero4, o, voff);
-        __syncthreads();
+    };
+    int t = 0;
+    for (; t + 1 < ntile; t += 2) {
+        step(Par<0>{}, t);
+        step(Par<1>{}, t + 1);
     }
+    if (t < ntile) step(Par<0>{}, t);
     if (!ok) return;
     _Float16* dst = (_Float16*)a.part_dq + (prow * (size_t)a.kslots + slot) * D;
 #pragma unroll
@@ -339,9 +376,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_far_dq_kernel(BwdArgs a) {
         }
 }
 
-// ---------------------------------------------------------------------------
-// dK, dV: a workgroup owns 128 keys of one (batch, kv head).
-// ---------------------------------------------------------------------------
 // Mask of an S tile in the key-centric layout (lane = key j, registers =
 // rows i = rt0 + cv + 4hh): keep iff (unsigned)(i - j) < w, or i >= j and
 // the row's info bit for the key's block is set.  rj = rt0 + 4hh - j.
