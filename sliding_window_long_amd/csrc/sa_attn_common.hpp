@@ -1,13 +1,14 @@
 // sa_attn_common.hpp -- tile machinery shared by the attention kernels
-// (query-centric in sa_attn.hip, KV-centric in sa_blocks.hip).
+// (query-centric in sa_attn.hip, KV-centric in sa_blocks.hip, compressed
+// branch in sa_cmp.hip, backward in sa_bwd.hip).
 //
 // Every tile does S^T = K Q^T (bf16 MFMA 32x32x16, fp32 accumulation), an
 // online softmax in base 2 on the VALU, and O^T += V^T P^T.  K and V tiles sit
 // row-major in LDS; the V^T operand comes from the transposing LDS reads of
-// gfx950 (ds_read_b64_tr_b16).  The key loop is skewed by one tile:
-// iteration t issues S_t = K_t Q^T, then O += V_{t-1} P_{t-1}, then the
-// softmax of S_t.  V is staged one tile behind K, which keeps both
-// double-buffered.
+// gfx950 (ds_read_b64_tr_b16).  Key loops are skewed by one tile, so that the
+// P V products of one tile run beside the softmax of the next.  Tiles reach
+// LDS either through registers (load_tile / store_tile) or straight from
+// global memory (TileDma / dma_tile, at the end of this file).
 #pragma once
 
 #include "sa_device.hpp"
@@ -59,14 +60,6 @@ struct TileSrc {
     int N;
     int off[Tile<D>::CPT];
 };
-
-// Workgroup barrier ordering LDS accesses only: global loads in flight stay
-// in flight (__syncthreads waits for them too).
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 __device__ __forceinline__ uint64_t uniform_u64(uint64_t u) {
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
@@ -382,22 +375,6 @@ __device__ __forceinline__ void apply_rescale(f32x16 (&o)[Tile<D>::DM], RowState
             for (int v = 0; v < 16; ++v) o[mb][v] *= st.alpha;
     }
     st.need = false;
-}
-
-// One step of the skewed key loop without masking (the far-block kernel):
-// the pending rescale of O, then S_t = K_t Q^T, O += V_{t-1} P_{t-1} and the
-// softmax of S_t into P_t.
-template <int D, int SPLIT>
-__device__ __forceinline__ void kv_step(const uint16_t* ks, const uint16_t* vs_prev,
-                                        const bf16x8 (&qf)[SPLIT][Tile<D>::DK],
-                                        f32x16 (&o)[Tile<D>::DM], RowState& st, uint4 (&pb)[4],
-                                        uint4 (&pl)[4], float c, int lane,
-                                        const int (&voff)[Tile<D>::DM]) {
-    apply_rescale<D>(o, st);
-    f32x16 s[2];
-    qk_tile<D, SPLIT>(ks, qf, s, lane);
-    pv_tile<D, SPLIT>(vs_prev, pb, pl, o, voff);
-    softmax_tile<SPLIT>(s, st, c, pb, pl);
 }
 
 template <int D, int SPLIT>
