@@ -191,7 +191,8 @@ int make_plan(const sparse_attn_cfg* c, Plan* p, bool bwd = false) {
         P.o_near = take(P.gate ? (size_t)rows * 4 : 0);
     } else {
         P.o_split = take(P.f32 ? 2 * (nq + 2 * nkv) * 2 : 0);
-        P.o_v16 = take(P.f32 ? 0 : nkv * 2);   // fp16 copy of V for the P V products
+        // fp16 copy of V for the P V products (rows padded with ones at d 80)
+        P.o_v16 = take(P.f32 ? 0 : nkv / P.D * sa::v16_row_of(P.D) * 2);
     }
     if (P.gate) {
         P.o_kb3 = take((size_t)P.gate_planes * P.lists * P.D * 2);
@@ -484,8 +485,7 @@ int sparse_attn_fwd(const void* q, const void* k, const void* v, const sparse_at
     } else {
         uint16_t* v16 = (uint16_t*)(ws + P.o_v16);
         StageScope t("v_to_f16", s);
-        if (!ok(sa::launch_bf16_to_f16((const uint16_t*)v, v16,
-                                       (size_t)P.Bt * P.Hkv * P.N * P.D, s)))
+        if (!ok(sa::launch_v_to_f16((const uint16_t*)v, v16, (size_t)P.Bt * P.Hkv * P.N, P.D, s)))
             return SA_E_HIP;
         vp[0] = v16;
     }

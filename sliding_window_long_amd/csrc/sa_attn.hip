@@ -97,8 +97,9 @@ __device__ __forceinline__ void finish_rows(const RowsArgs& a, f32x16 (&o)[Tile<
 // registers that moved the exp beside the K Q^T products.
 //
 // Head dims that are not a multiple of 32 (80) pad O^T to 96 rows; those
-// rows take constant ones as their V^T operand, so the matrix cores produce
-// the softmax row sums (of the same fp16 P that weights V) and no vector adds
+// rows take constant ones as their V^T operand (columns 80..95 of the fp16 V
+// copy hold ones; the fp32 path selects them), so the matrix cores produce
+// the softmax row sums (of the same fp16 P that weights V) and no vector ops
 // are spent on them.
 template <int D, int SPLIT, bool TOK>
 __global__ __launch_bounds__(NTHREADS, D <= 80 && SPLIT == 1 ? 3 : 2) void attn_rows_kernel(RowsArgs a) {
@@ -119,12 +120,16 @@ __global__ __launch_bounds__(NTHREADS, D <= 80 && SPLIT == 1 ? 3 : 2) void attn_
     const int N = a.N;
     const int r0 = tile * RT;
 
+    // V rows: the fp16 copy's stride (bf16 path; ones past D at d 80) or D.
+    constexpr int VSRC = SPLIT == 1 ? v16_row<D>() : D;
+    constexpr bool ONES_SEL = ONES && VSRC == D;   // padding lanes select ones
     const size_t kvoff = (size_t)(b * a.Hkv + g_kv) * N * D;
+    const size_t voff_src = (size_t)(b * a.Hkv + g_kv) * N * VSRC;
     uint64_t kb[SPLIT], vb[SPLIT];   // workgroup-uniform byte addresses
 #pragma unroll
     for (int p = 0; p < SPLIT; ++p) {
         kb[p] = uniform_u64((uint64_t)(a.k[p] + kvoff));
-        vb[p] = uniform_u64((uint64_t)(a.v[p] + kvoff));
+        vb[p] = uniform_u64((uint64_t)(a.v[p] + voff_src));
     }
 
     const int wu = __builtin_amdgcn_readfirstlane(wave);   // wave-uniform
@@ -178,7 +183,7 @@ __global__ __launch_bounds__(NTHREADS, D <= 80 && SPLIT == 1 ? 3 : 2) void attn_
     for (int mb = 0; mb < T::DM; ++mb) voff[mb] = v_lane_offset<D, VS, ONES>(lane, mb);
     const bool pad = ONES && ((lane >> 4) & 1);   // lanes of the padding dims in the last row block
     TileDma<D, T::KS> kd;
-    TileDma<D, VS> vd;
+    TileDma<D, VS, VSRC> vd;
     kd.init(wu, lane);
     vd.init(wu, lane);
     auto load_k = [&](int t, uint16_t* dst) { dma_tile<D, SPLIT, T::KELEMS>(kd, kb, N, t * KT, dst, wu); };
@@ -255,7 +260,7 @@ __global__ __launch_bounds__(NTHREADS, D <= 80 && SPLIT == 1 ? 3 : 2) void attn_
         apply_rescale<D>(o, rs);
         qk_tile<D, SPLIT>(k_next, qf, sn, lane);
         mask_t(sn, t + 1, tw);
-        pv_tile<D, SPLIT, VS, ONES>(v_cur, pb, pl, o, voff, pad);
+        pv_tile<D, SPLIT, VS, ONES_SEL>(v_cur, pb, pl, o, voff, pad);
         max_tile(sn, rs, c);
         exp_tile<SPLIT, !ONES>(sn, rs, c, pb, pl);
         // 12 (d 80) matrix-core ops and 24 transposing reads with about 90
@@ -278,7 +283,7 @@ __global__ __launch_bounds__(NTHREADS, D <= 80 && SPLIT == 1 ? 3 : 2) void attn_
     auto last = [&](auto par) {
         constexpr int PAR = decltype(par)::value;
         apply_rescale<D>(o, rs);
-        pv_tile<D, SPLIT, VS, ONES>(PAR ? lds_v1 : lds_v0, pb, pl, o, voff, pad);
+        pv_tile<D, SPLIT, VS, ONES_SEL>(PAR ? lds_v1 : lds_v0, pb, pl, o, voff, pad);
     };
     // Unrolled by two so that the buffer parity is a constant.
     int it = 0;
@@ -316,6 +321,39 @@ __global__ void bf16_to_f16_kernel(const uint4* __restrict__ x, uint4* __restric
         r[t] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
     }
     y[i] = make_uint4(r[0], r[1], r[2], r[3]);
+}
+
+// bf16 rows of D -> fp16 rows of SR (> D) whose columns D .. SR-1 hold
+// fp16 one; one thread per 8 output elements.
+__global__ void bf16_to_f16_rows_kernel(const uint16_t* __restrict__ x, uint4* __restrict__ y,
+                                        size_t rows, int D, int SR) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int cpr = SR / 8;
+    if (i >= rows * cpr) return;
+    const size_t r = i / cpr;
+    const int c = (int)(i % cpr);
+    uint32_t o[4] = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
+    if (c < D / 8) {
+        const uint4 u = *(const uint4*)(x + r * D + c * 8);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const _Float16 lo = (_Float16)bf16_to_f32(w[t] & 0xffffu);
+            const _Float16 hi = (_Float16)bf16_to_f32(w[t] >> 16);
+            o[t] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+        }
+    }
+    y[i] = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+hipError_t launch_v_to_f16(const uint16_t* v, uint16_t* y, size_t rows, int D, hipStream_t s) {
+    const int SR = v16_row_of(D);
+    if (SR == D) return launch_bf16_to_f16(v, y, rows * D, s);
+    const size_t n8 = rows * (SR / 8);
+    if (n8 == 0) return hipSuccess;
+    hipLaunchKernelGGL(bf16_to_f16_rows_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, v,
+                       (uint4*)y, rows, D, SR);
+    return hipGetLastError();
 }
 
 hipError_t launch_bf16_to_f16(const uint16_t* x, uint16_t* y, size_t n, hipStream_t s) {

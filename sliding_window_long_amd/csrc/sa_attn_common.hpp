@@ -416,23 +416,27 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // dealt round-robin to the waves; where they do not divide evenly, the waves
 // past the last one repeat it (the same bytes to the same LDS address), so
 // every wave issues the same count with no branches.
-template <int D, int S>
+//
+// SRC is the source's row stride (elements, >= D): columns D .. SRC-1 of a
+// source row are copied too (up to the image's row length).
+template <int D, int S, int SRC = D>
 struct TileDma {
     static constexpr int NI = S / 8;                           // instructions per plane
     static constexpr int PER = (NI + NWAVES - 1) / NWAVES;     // per wave
+    static constexpr int ROW = SRC;                            // source row stride
     int voff[PER];   // byte offset of this lane's chunk from the tile's first key
     __device__ __forceinline__ static int inst(int wave, int j) { return min(wave + NWAVES * j, NI - 1); }
     __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
-            const int p = 64 * inst(wave, j) + lane, row = p / NI, c = min(p % NI, D / 8 - 1);
-            voff[j] = (row * D + c * 8) * 2;
+            const int p = 64 * inst(wave, j) + lane, row = p / NI, c = min(p % NI, SRC / 8 - 1);
+            voff[j] = (row * SRC + c * 8) * 2;
         }
     }
 };
 
 // Issue the loads of the tile starting at key kt0 (0 <= kt0 < N) of SPLIT
-// [N, D] planes (byte addresses base[]) into lds (planes PLANE elements
+// [N, TD::ROW] planes (byte addresses base[]) into lds (planes PLANE elements
 // apart).  Keys at or past N fall outside the buffer descriptor and load
 // zero (finite data that causality always masks).  Completion is awaited
 // with the memory counter (the barrier at the end of a step).
@@ -441,11 +445,11 @@ __device__ __forceinline__ void dma_tile(const TD& td, const uint64_t* base, int
                                          uint16_t* lds, int wave) {
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass rejects the LDS-pointer builtin
     const int k0 = __builtin_amdgcn_readfirstlane(kt0);
-    const int bytes = (N - k0) * D * 2;
+    const int bytes = (N - k0) * TD::ROW * 2;
 #pragma unroll
     for (int p = 0; p < SPLIT; ++p) {
         const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(base[p] + (uint64_t)k0 * D * 2), (short)0, bytes, 0x00020000);
+            (void*)(base[p] + (uint64_t)k0 * TD::ROW * 2), (short)0, bytes, 0x00020000);
 #pragma unroll
         for (int j = 0; j < TD::PER; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(

@@ -96,15 +96,18 @@ __global__ __launch_bounds__(NTHREADS, D <= 80 && SPLIT == 1 ? 3 : 2) void attn_
     const int ntile = a.B / KT;
     const int k_begin = cblk * a.B;
 
+    // V rows: the fp16 copy's stride (bf16 path; ones past D at d 80) or D.
+    constexpr int VSRC = SPLIT == 1 ? v16_row<D>() : D;
+    constexpr bool ONES_SEL = ONES && VSRC == D;   // padding lanes select ones
     const size_t kvoff = (size_t)bg * N * D;
     uint64_t kb[SPLIT], vb[SPLIT];   // workgroup-uniform byte addresses
 #pragma unroll
     for (int p = 0; p < SPLIT; ++p) {
         kb[p] = uniform_u64((uint64_t)(a.k[p] + kvoff));
-        vb[p] = uniform_u64((uint64_t)(a.v[p] + kvoff));
+        vb[p] = uniform_u64((uint64_t)(a.v[p] + (size_t)bg * N * VSRC));
     }
     TileDma<D, T::KS> kd;
-    TileDma<D, VS> vd;
+    TileDma<D, VS, VSRC> vd;
     kd.init(wu, lane);
     vd.init(wu, lane);
     auto load_k = [&](int t, uint16_t* dst) { dma_tile<D, SPLIT, T::KELEMS>(kd, kb, N, k_begin + t * KT, dst, wu); };
@@ -155,7 +158,7 @@ __global__ __launch_bounds__(NTHREADS, D <= 80 && SPLIT == 1 ? 3 : 2) void attn_
         load_v(it + 1, v_free);
         apply_rescale<D>(o, rs);
         qk_tile<D, SPLIT>(k_next, qf, s0, lane);
-        pv_tile<D, SPLIT, VS, ONES>(v_cur, pb, pl, o, voff, pad);
+        pv_tile<D, SPLIT, VS, ONES_SEL>(v_cur, pb, pl, o, voff, pad);
         max_tile(s0, rs, c);
         exp_tile<SPLIT, !ONES>(s0, rs, c, pb, pl);
         __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 4, 0);
@@ -175,7 +178,7 @@ __global__ __launch_bounds__(NTHREADS, D <= 80 && SPLIT == 1 ? 3 : 2) void attn_
     auto last = [&](auto par) {
         constexpr int PAR = decltype(par)::value;
         apply_rescale<D>(o, rs);
-        pv_tile<D, SPLIT, VS, ONES>(PAR ? lds_v1 : lds_v0, pb, pl, o, voff, pad);
+        pv_tile<D, SPLIT, VS, ONES_SEL>(PAR ? lds_v1 : lds_v0, pb, pl, o, voff, pad);
     };
     int it = 0;
     for (; it + 2 < ntile; it += 2) {

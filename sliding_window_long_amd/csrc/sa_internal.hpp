@@ -263,6 +263,15 @@ hipError_t launch_fill_i32(int32_t* p, int32_t value, size_t n, hipStream_t s);
 hipError_t launch_rows(const RowsArgs& a, int head_dim, int split, hipStream_t s);
 hipError_t launch_blocks(const BlocksArgs& a, int head_dim, int split, int grid, hipStream_t s);
 hipError_t launch_bf16_to_f16(const uint16_t* x, uint16_t* y, size_t n, hipStream_t s);
+// Row stride of the fp16 V copy that the forward's bf16 path reads: at d 80
+// rows of 96 whose columns 80..95 hold fp16 ones (the padding rows of O^T
+// then read ones and accumulate the row sums); otherwise D.
+__host__ __device__ constexpr int v16_row_of(int D) { return D == 80 ? 96 : D; }
+template <int D>
+__host__ __device__ constexpr int v16_row() { return v16_row_of(D); }
+// The fp16 copy of V ([rows, D] bf16) that the forward's attention kernels
+// read: rows of v16_row(D) elements (at d 80: 96, columns 80..95 fp16 one).
+hipError_t launch_v_to_f16(const uint16_t* v, uint16_t* y, size_t rows, int D, hipStream_t s);
 hipError_t launch_split_f32(const float* x, uint16_t* hi, uint16_t* lo, size_t n, hipStream_t s);
 
 }  // namespace sa
