@@ -155,8 +155,11 @@ def test_decode_workspace(lib):
 def test_workspace_sizes_scale(lib):
     # block gating with far blocks: partials
     # [rows, top_k-1, d] fp16 dominate.
-    # window only: an fp16 copy of V
-    assert sa.sparse_attn_workspace_bytes(sa.Params(1, 32, 32, 16384, 80, window=4096).cfg()) == 32 * 16384 * 80 * 2
+    # window only: an fp16 copy of V, rows padded to 96 at d 80 (ones in the
+    # padding columns feed the row sums), unpadded at d 64 and 128
+    assert sa.sparse_attn_workspace_bytes(sa.Params(1, 32, 32, 16384, 80, window=4096).cfg()) == 32 * 16384 * 96 * 2
+    assert sa.sparse_attn_workspace_bytes(sa.Params(1, 8, 8, 4096, 128, window=512).cfg()) == 8 * 4096 * 128 * 2
+    assert sa.sparse_attn_workspace_bytes(sa.Params(1, 8, 8, 4096, 64, window=512).cfg()) == 8 * 4096 * 64 * 2
     p = sa.Params(1, 32, 8, 131072, 128, block_size=512, top_k=8)
     rows = 32 * 131072
     assert sa.sparse_attn_workspace_bytes(p.cfg()) >= rows * 7 * 128 * 2
