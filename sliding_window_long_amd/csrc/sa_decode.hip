@@ -17,7 +17,9 @@
 //                 ord(score) << 16 | (0xFFFF - j): 4096 linear score bins
 //                 locate the threshold bin, whose few members are resolved
 //                 exactly; then the kept ids as an ascending list and the
-//                 count below the window.
+//                 count below the window.  For a few queries over a long
+//                 history: per-slice selections on eight workgroups per
+//                 query, then their merge.
 //   dec_attn    : per (batch, kv head, query, chunk of 128 attended keys (64
 //                 for fp32) -- the window [lo, p] first, then the kept tokens
 //                 before lo): the chunk's K and V rows staged in LDS, logits,
@@ -169,24 +171,38 @@ __device__ __forceinline__ uint64_t dec_key(float s, int j) {
     return (uint64_t)dec_ord32(s) << 16 | (uint64_t)(0xffffu - (uint32_t)j);
 }
 
+// Selection modes of dec_select_kernel.
+enum SelMode { kSelWhole = 0, kSelPart = 1, kSelMerge = 2 };
+constexpr int kSelParts = kDecSelParts;   // slices of a long history
+constexpr int kSelSlice = 65536 / kSelParts;
+
 // Kept tokens of one query: min(top_t, p) best of j < p, ascending, -1
 // padded; nfar = how many of them lie before the window start lo.  Keys are
-// unique (the index breaks score ties toward the lower j).  Thread t handles
-// ids u * SEL_THREADS + t (coalesced; u < 64 since p <= 65535).
-//   1. the row's score range (scores held in registers for steps 1-2);
-//   2. 4096 linear bins over that range: each id's bin is kept in LDS
-//      (16 bits) and counted in an LDS histogram;
+// unique (the index breaks score ties toward the lower j).
+//
+// The candidates of one selection are n tokens in ascending id order; thread
+// t handles candidates x = u * SEL_THREADS + t (u < PT).  MODE kSelWhole: the
+// whole history, x = j.  A long history is split: kSelPart selects, for each
+// of kSelParts slices of kSelSlice ids (blockIdx.z), the min(top_t, slice
+// length) best of the slice into plist (count in pcnt); kSelMerge then
+// selects from the concatenated slice lists (ids staged in LDS).  The best
+// k of a set are among the best k of any slice that holds them, so the
+// result is the whole history's.
+//   1. the candidates' score range (scores held in registers for 1-2);
+//   2. 4096 linear bins over that range: each candidate's bin is kept in
+//      LDS (16 bits) and counted in an LDS histogram;
 //   3. the bin b* holding the k-th best key and the count above it; the
 //      rem = k - above best members of b* are marked kept (bin 0xFFFF):
 //      by rank counting over the members gathered in LDS when b* holds at
 //      most 256 keys, else by a byte-wise radix select over its members'
 //      48-bit keys (6 passes, scores reloaded);
-//   4. kept = bin above b* (marks included), written in ascending id order
-//      from wave ballots and one block scan.
+//   4. kept = bin above b* (marks included), written in candidate (= id)
+//      order from wave ballots and one block scan.
+template <int PT, int MODE>
 __global__ __launch_bounds__(SEL_THREADS) void dec_select_kernel(DecArgs a) {
-    constexpr int PT = 65536 / SEL_THREADS;
     constexpr int NW = SEL_THREADS / 64;
-    __shared__ uint16_t binv[PT * SEL_THREADS];
+    constexpr int NC = PT * SEL_THREADS;   // candidate capacity
+    __shared__ uint16_t binv[NC];
     __shared__ uint32_t hist[kSelBins];
     __shared__ int sh[SEL_THREADS];
     __shared__ int wsum[NW];
@@ -194,21 +210,51 @@ __global__ __launch_bounds__(SEL_THREADS) void dec_select_kernel(DecArgs a) {
     __shared__ uint32_t s_b[3];
     __shared__ uint32_t s_n;
     __shared__ uint64_t cand[kSelRank];
-    const int r = blockIdx.x, bt = blockIdx.y, tid = threadIdx.x;
+    __shared__ int s_ids[MODE == kSelMerge ? NC : 1];
+    const int r = blockIdx.x, bt = blockIdx.y, part = blockIdx.z, tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
+    const size_t row = (size_t)bt * a.Nq + r;
     const int p = a.Nk - a.Nq + r;
-    const int k = min(a.top_t, p);
     const int lo = a.window > 0 ? max(0, p - a.window + 1) : p;
-    const float* sc = a.scores + ((size_t)bt * a.Nq + r) * a.Nk;
-    int32_t* list = a.list + ((size_t)bt * a.Nq + r) * a.top_t;
-    const bool sel = k > 0 && k < p;   // otherwise every id (k >= p) or none is kept
+    const float* sc = a.scores + row * a.Nk;
+
+    // This selection's candidates [0, n), their ids and how many to keep.
+    int n, j0 = 0, k;
+    if constexpr (MODE == kSelWhole) {
+        n = p;
+        k = min(a.top_t, p);
+    } else if constexpr (MODE == kSelPart) {
+        j0 = part * kSelSlice;
+        n = max(0, min(p - j0, kSelSlice));
+        k = min(a.top_t, n);
+    } else {
+        // concatenate the slice lists (each ascending, slices in order)
+        const int32_t* pc = a.pcnt + row * kSelParts;
+        int off[kSelParts + 1];
+        off[0] = 0;
+#pragma unroll
+        for (int q = 0; q < kSelParts; ++q) off[q + 1] = off[q] + pc[q];
+        n = off[kSelParts];
+#pragma unroll
+        for (int q = 0; q < kSelParts; ++q) {
+            const int32_t* pl = a.plist + (row * kSelParts + q) * a.top_t;
+            for (int x = tid; x < pc[q]; x += SEL_THREADS) s_ids[off[q] + x] = pl[x];
+        }
+        k = min(a.top_t, p);
+        __syncthreads();
+    }
+    auto id_of = [&](int x) -> int {
+        if constexpr (MODE == kSelMerge) return s_ids[x];
+        else return j0 + x;
+    };
+    const bool sel = k > 0 && k < n;   // otherwise every candidate (k >= n) or none is kept
     uint32_t bstar = 0;
 
     if (sel) {
-        // 1. range (slots past p re-read id p - 1, which leaves it unchanged)
+        // 1. range (slots past n re-read candidate n - 1, which leaves it unchanged)
         float sv[PT];
 #pragma unroll
-        for (int u = 0; u < PT; ++u) sv[u] = sc[min(u * SEL_THREADS + tid, p - 1)];
+        for (int u = 0; u < PT; ++u) sv[u] = sc[id_of(min(u * SEL_THREADS + tid, n - 1))];
         float lo_s = sv[0], hi_s = sv[0];
 #pragma unroll
         for (int u = 1; u < PT; ++u) {
@@ -241,7 +287,7 @@ __global__ __launch_bounds__(SEL_THREADS) void dec_select_kernel(DecArgs a) {
 #pragma unroll
         for (int u = 0; u < PT; ++u) {
             const uint32_t b = dec_bin(sv[u], mn, inv);
-            const bool valid = tid < p - u * SEL_THREADS;
+            const bool valid = tid < n - u * SEL_THREADS;
             if (valid) binv[u * SEL_THREADS + tid] = (uint16_t)b;
             dec_hist_add(hist, b, valid);
         }
@@ -273,17 +319,22 @@ __global__ __launch_bounds__(SEL_THREADS) void dec_select_kernel(DecArgs a) {
         uint32_t rem = (uint32_t)k - s_b[1];   // 1 <= rem <= in_bin
 
         if (in_bin <= (uint32_t)kSelRank) {
-            // gather b*; a member is kept when fewer than rem members beat it
+            // gather b* as (48-bit key, candidate) in 64 bits (keys are
+            // unique, so the candidate never decides an order); a member is
+            // kept when fewer than rem members beat it
             for (int u = 0; u < PT; ++u) {
-                const int j = u * SEL_THREADS + tid;
-                if (j < p && binv[j] == bstar) cand[atomicAdd(&s_n, 1u)] = dec_key(sc[j], j);
+                const int x = u * SEL_THREADS + tid;
+                if (x < n && binv[x] == bstar) {
+                    const int j = id_of(x);
+                    cand[atomicAdd(&s_n, 1u)] = dec_key(sc[j], j) << 16 | (uint64_t)x;
+                }
             }
             __syncthreads();
             if (tid < (int)in_bin) {
                 const uint64_t me = cand[tid];
                 uint32_t above = 0;
                 for (uint32_t x = 0; x < in_bin; ++x) above += cand[x] > me;
-                if (above < rem) binv[0xffff - (int)(me & 0xffffu)] = kSelKept;
+                if (above < rem) binv[(int)(me & 0xffffu)] = kSelKept;
             }
         } else {
             // radix select of the rem-th best member key, then mark
@@ -292,10 +343,11 @@ __global__ __launch_bounds__(SEL_THREADS) void dec_select_kernel(DecArgs a) {
                 if (tid < 256) hist[tid] = 0;
                 __syncthreads();
                 for (int u = 0; u < PT; ++u) {
-                    const int j = u * SEL_THREADS + tid;
-                    const bool in = j < p && binv[j] == bstar;
+                    const int x = u * SEL_THREADS + tid;
+                    const bool in = x < n && binv[x] == bstar;
                     uint32_t ov = 0, ix = 0;
                     if (in) {
+                        const int j = id_of(x);
                         ov = dec_ord32(sc[j]);
                         ix = 0xffffu - (uint32_t)j;
                     }
@@ -319,26 +371,29 @@ __global__ __launch_bounds__(SEL_THREADS) void dec_select_kernel(DecArgs a) {
             }
             const uint64_t thr = (uint64_t)pre_hi << 16 | pre_lo;
             for (int u = 0; u < PT; ++u) {
-                const int j = u * SEL_THREADS + tid;
-                if (j < p && binv[j] == bstar && dec_key(sc[j], j) >= thr) binv[j] = kSelKept;
+                const int x = u * SEL_THREADS + tid;
+                if (x < n && binv[x] == bstar) {
+                    const int j = id_of(x);
+                    if (dec_key(sc[j], j) >= thr) binv[x] = kSelKept;
+                }
             }
         }
         __syncthreads();
     }
 
-    // 4. kept ids in ascending order; lane u of each wave keeps the wave's
+    // 4. kept ids in candidate order; lane u of each wave keeps the wave's
     // ballot for slot u
     uint32_t mlo = 0, mhi = 0;
     int nlo = 0;
 #pragma unroll
     for (int u = 0; u < PT; ++u) {
-        const int j = u * SEL_THREADS + tid;
-        bool kp = j < p && k > 0;
-        if (sel) kp = kp && binv[min(j, p - 1)] > bstar;
+        const int x = u * SEL_THREADS + tid;
+        bool kp = x < n && k > 0;
+        if (sel) kp = kp && binv[min(x, n - 1)] > bstar;
         const uint64_t m = __ballot(kp);
         mlo = lane == u ? (uint32_t)m : mlo;
         mhi = lane == u ? (uint32_t)(m >> 32) : mhi;
-        nlo += kp && j < lo;
+        nlo += kp && id_of(min(x, max(n - 1, 0))) < lo;
     }
     sh[lane * NW + w] = __popc(mlo) + __popc(mhi);   // entry (u, w) at u * NW + w
     __syncthreads();
@@ -349,16 +404,22 @@ __global__ __launch_bounds__(SEL_THREADS) void dec_select_kernel(DecArgs a) {
     const int base = sh[lane * NW + w];
     const uint32_t below_lo = lane >= 32 ? 0xffffffffu : (1u << lane) - 1u;
     const uint32_t below_hi = lane < 32 ? 0u : (lane == 63 ? 0x7fffffffu : (1u << (lane - 32)) - 1u);
+    int32_t* const list = MODE == kSelPart ? a.plist + (row * kSelParts + part) * a.top_t
+                                           : a.list + row * a.top_t;
 #pragma unroll
     for (int u = 0; u < PT; ++u) {
         const uint32_t ml = (uint32_t)__builtin_amdgcn_readlane((int)mlo, u);
         const uint32_t mh = (uint32_t)__builtin_amdgcn_readlane((int)mhi, u);
         const bool kp = ((lane < 32 ? ml >> lane : mh >> (lane - 32)) & 1u) != 0;
         const int pos = __builtin_amdgcn_readlane(base, u) + __popc(ml & below_lo) + __popc(mh & below_hi);
-        if (kp && pos < a.top_t) list[pos] = u * SEL_THREADS + tid;
+        if (kp && pos < a.top_t) list[pos] = id_of(u * SEL_THREADS + tid);
     }
-    for (int x = total + tid; x < a.top_t; x += SEL_THREADS) list[x] = -1;
-    if (tid == 0) a.nfar[(size_t)bt * a.Nq + r] = total_lo;
+    if constexpr (MODE == kSelPart) {
+        if (tid == 0) a.pcnt[row * kSelParts + part] = min(total, a.top_t);
+    } else {
+        for (int x = total + tid; x < a.top_t; x += SEL_THREADS) list[x] = -1;
+        if (tid == 0) a.nfar[row] = total_lo;
+    }
 }
 
 // Attended keys of query r: the window [lo, p] (nw keys) then the nt kept
@@ -609,8 +670,19 @@ hipError_t launch_decode_select(const DecArgs& a, hipStream_t s) {
         hipLaunchKernelGGL(dec_scores_kernel<false>, sg, dim3(DEC_THREADS), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(dec_select_kernel, dim3((unsigned)a.Nq, (unsigned)a.Bt), dim3(SEL_THREADS), 0, s,
-                       a);
+    if (!dec_split_select((long long)a.Bt * a.Nq, a.Nk, a.top_t) || !a.plist) {
+        hipLaunchKernelGGL((dec_select_kernel<65536 / SEL_THREADS, kSelWhole>),
+                           dim3((unsigned)a.Nq, (unsigned)a.Bt), dim3(SEL_THREADS), 0, s, a);
+        return hipGetLastError();
+    }
+    // Long histories: the slices' selections spread over kSelParts
+    // workgroups per query, then the merge.
+    hipLaunchKernelGGL((dec_select_kernel<kSelSlice / SEL_THREADS, kSelPart>),
+                       dim3((unsigned)a.Nq, (unsigned)a.Bt, (unsigned)kSelParts), dim3(SEL_THREADS), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((dec_select_kernel<kSelParts * kDecSplitMaxTop / SEL_THREADS, kSelMerge>),
+                       dim3((unsigned)a.Nq, (unsigned)a.Bt), dim3(SEL_THREADS), 0, s, a);
     return hipGetLastError();
 }
 

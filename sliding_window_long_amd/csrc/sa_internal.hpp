@@ -241,12 +241,23 @@ struct DecArgs {
     float* scores;          // [Bt, Nq, Nk] indexer scores
     int32_t* list;          // [Bt, Nq, top_t] kept tokens, ascending, -1 padded; nullptr: no gate
     int32_t* nfar;          // [Bt, Nq] kept tokens before the window
+    int32_t* plist;         // [Bt, Nq, kDecSelParts, top_t] slice selections, or nullptr
+    int32_t* pcnt;          // [Bt, Nq, kDecSelParts] their lengths
     float* part;            // [Bt*Hq*Nq, cmax, D + 2] partials (o, m, l) of each key tile
     int cmax;               // tiles of dec_chunk(f32) attended keys per query, upper bound
     void* out;              // [Bt, Hq, Nq, D], the input dtype
     float* lse;             // [Bt, Hq, Nq]
 };
 
+// The decode token selection takes one workgroup per query.  When few
+// queries (rows = Bt * Nq <= kDecSplitRows) would leave most of the chip
+// idle, a history longer than kDecSplitNk keys is split over kDecSelParts
+// slices (one workgroup each) whose selections are then merged, provided
+// top_t <= kDecSplitMaxTop; the plan then holds plist and pcnt.
+constexpr int kDecSelParts = 8, kDecSplitNk = 16384, kDecSplitMaxTop = 2048, kDecSplitRows = 32;
+inline bool dec_split_select(long long rows, int Nk, int top_t) {
+    return rows <= kDecSplitRows && Nk > kDecSplitNk && top_t > 0 && top_t <= kDecSplitMaxTop;
+}
 hipError_t launch_decode_select(const DecArgs& a, hipStream_t s);
 hipError_t launch_decode_attn(const DecArgs& a, hipStream_t s);
 

@@ -458,9 +458,25 @@ def test_decode_token(dev, Nk, nq, top_t, window):
     run_and_check(decode_inputs(wl, nq, 31 + nq + top_t), dev, label=f"decode_token nq={nq}")
 
 
-def test_decode_token_ties(dev):
+@pytest.mark.parametrize("Nk,nq,top_t,window", [(17000, 3, 2048, 16), (40000, 2, 5, 64),
+                                                (40000, 2, 3000, 8), (65536, 1, 1, 1),
+                                                (20000, 40, 100, 16)])
+def test_decode_token_long_history(dev, Nk, nq, top_t, window):
+    # Histories over 16384 keys: with top_t <= 2048 the selection runs per
+    # slice of 8192 ids and merges (17000: the last slice is shorter than
+    # top_t and keeps all; 65536: every slice full); top_t 3000, and 40
+    # queries (enough workgroups to spread), take the one-workgroup-per-query
+    # selection.
+    wl = W.Workload("dec_long", 1, 2, 1, Nk, 64, "bf16", window=window, token_top_k=top_t,
+                    index_dim=64, sink=True)
+    run_and_check(decode_inputs(wl, nq, 7 + nq + top_t), dev, label=f"decode_long Nk={Nk} k={top_t}")
+
+
+@pytest.mark.parametrize("Nk", [1500, 20000])
+def test_decode_token_ties(dev, Nk):
     # Equal indexer keys: the lowest token ids win in the decode step too.
-    wl = W.Workload("dec_ties", 1, 2, 1, 1500, 64, "bf16", window=2, token_top_k=37, index_dim=64)
+    # (20000 keys: per-slice selections and their merge.)
+    wl = W.Workload("dec_ties", 1, 2, 1, Nk, 64, "bf16", window=2, token_top_k=37, index_dim=64)
     inp = decode_inputs(wl, 4, 5)
     inp.idx_k[:] = inp.idx_k[:, :1]
     out, lse, _, tsel = run_device(inp, dev)
