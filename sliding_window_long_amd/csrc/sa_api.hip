@@ -46,8 +46,8 @@ struct Plan {
     size_t o_split, o_kb3, o_sel, o_count, o_cursor, o_listoff, o_nchunks, o_chunk_list,
         o_chunk_start, o_entries, o_part_o, o_part_lse, o_tok_split, o_tok_state, o_tok_mask,
         o_tok_qn, o_tok_win, o_tok_kpart, o_tok_scr, o_tok_nslow, o_dec_scores, o_dec_list,
-        o_dec_nfar, o_dec_plist, o_dec_pcnt, o_dec_part, o_qsum, o_cmp_k, o_cmp_v, o_cmp_out,
-        o_k16, o_q16, o_do16, o_delta, o_near, o_f8q, o_f8k, o_f8v, o_f8iq, o_f8ik,
+        o_dec_nfar, o_dec_plist, o_dec_pcnt, o_dec_redo, o_dec_part, o_qsum, o_cmp_k, o_cmp_v,
+        o_cmp_out, o_k16, o_q16, o_do16, o_delta, o_near, o_f8q, o_f8k, o_f8v, o_f8iq, o_f8ik,
         o_v16, total;
 };
 
@@ -126,6 +126,7 @@ int make_plan(const sparse_attn_cfg* c, Plan* p, bool bwd = false) {
             if (sa::dec_split_select((long long)P.Bt * P.N, P.Nk, P.top_t)) {
                 P.o_dec_plist = take((size_t)P.Bt * P.N * sa::kDecSelParts * P.top_t * 4);
                 P.o_dec_pcnt = take((size_t)P.Bt * P.N * sa::kDecSelParts * 4);
+                P.o_dec_redo = take((size_t)P.Bt * P.N * 4);
             }
         }
         const long long span = (c->window < P.Nk ? c->window : P.Nk) + (long long)P.top_t;
@@ -465,6 +466,8 @@ int sparse_attn_fwd(const void* q, const void* k, const void* v, const sparse_at
             if (sa::dec_split_select((long long)P.Bt * P.N, P.Nk, P.top_t)) {
                 da.plist = (int32_t*)(ws + P.o_dec_plist);
                 da.pcnt = (int32_t*)(ws + P.o_dec_pcnt);
+                da.redo = (int32_t*)(ws + P.o_dec_redo);
+                da.quota = sa::dec_sel_quota(P.top_t);
             }
             StageScope t("decode_token_select", s);
             if (!ok(sa::launch_decode_select(da, s))) return SA_E_HIP;

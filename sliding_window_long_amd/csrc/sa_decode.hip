@@ -183,11 +183,15 @@ constexpr int kSelSlice = 65536 / kSelParts;
 // The candidates of one selection are n tokens in ascending id order; thread
 // t handles candidates x = u * SEL_THREADS + t (u < PT).  MODE kSelWhole: the
 // whole history, x = j.  A long history is split: kSelPart selects, for each
-// of kSelParts slices of kSelSlice ids (blockIdx.z), the min(top_t, slice
+// of kSelParts slices of kSelSlice ids (blockIdx.z), the min(quota, slice
 // length) best of the slice into plist (count in pcnt); kSelMerge then
-// selects from the concatenated slice lists (ids staged in LDS).  The best
-// k of a set are among the best k of any slice that holds them, so the
-// result is the whole history's.
+// selects from the concatenated slice lists (ids staged in LDS).  A slice
+// whose ids were not all passed on dropped only keys below its lowest
+// passed key; when that key is not among the merged best (or the slice
+// passed on everything, or quota = top_t), nothing dropped can beat the
+// merged k-th key and the result is the whole history's.  Otherwise the
+// merge sets redo for the query, and kSelWhole, launched with redo, selects
+// those queries again (it returns at once for the others).
 //   1. the candidates' score range (scores held in registers for 1-2);
 //   2. 4096 linear bins over that range: each candidate's bin is kept in
 //      LDS (16 bits) and counted in an LDS histogram;
@@ -211,9 +215,14 @@ __global__ __launch_bounds__(SEL_THREADS) void dec_select_kernel(DecArgs a) {
     __shared__ uint32_t s_n;
     __shared__ uint64_t cand[kSelRank];
     __shared__ int s_ids[MODE == kSelMerge ? NC : 1];
+    __shared__ int s_sel[kSelParts];   // merge: merged best per slice
     const int r = blockIdx.x, bt = blockIdx.y, part = blockIdx.z, tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
     const size_t row = (size_t)bt * a.Nq + r;
+    if constexpr (MODE == kSelWhole) {
+        if (a.redo && a.redo[row] == 0) return;   // the merge's result stands
+    }
+    if (tid < kSelParts) s_sel[tid] = 0;
     const int p = a.Nk - a.Nq + r;
     const int lo = a.window > 0 ? max(0, p - a.window + 1) : p;
     const float* sc = a.scores + row * a.Nk;
@@ -226,7 +235,7 @@ __global__ __launch_bounds__(SEL_THREADS) void dec_select_kernel(DecArgs a) {
     } else if constexpr (MODE == kSelPart) {
         j0 = part * kSelSlice;
         n = max(0, min(p - j0, kSelSlice));
-        k = min(a.top_t, n);
+        k = min(a.quota, n);
     } else {
         // concatenate the slice lists (each ascending, slices in order)
         const int32_t* pc = a.pcnt + row * kSelParts;
@@ -406,19 +415,44 @@ __global__ __launch_bounds__(SEL_THREADS) void dec_select_kernel(DecArgs a) {
     const uint32_t below_hi = lane < 32 ? 0u : (lane == 63 ? 0x7fffffffu : (1u << (lane - 32)) - 1u);
     int32_t* const list = MODE == kSelPart ? a.plist + (row * kSelParts + part) * a.top_t
                                            : a.list + row * a.top_t;
+    int scnt[kSelParts] = {};   // merge: this wave's kept ids per slice
 #pragma unroll
     for (int u = 0; u < PT; ++u) {
         const uint32_t ml = (uint32_t)__builtin_amdgcn_readlane((int)mlo, u);
         const uint32_t mh = (uint32_t)__builtin_amdgcn_readlane((int)mhi, u);
         const bool kp = ((lane < 32 ? ml >> lane : mh >> (lane - 32)) & 1u) != 0;
         const int pos = __builtin_amdgcn_readlane(base, u) + __popc(ml & below_lo) + __popc(mh & below_hi);
-        if (kp && pos < a.top_t) list[pos] = id_of(u * SEL_THREADS + tid);
+        const int id = kp ? id_of(u * SEL_THREADS + tid) : 0;
+        if (kp && pos < a.top_t) list[pos] = id;
+        if constexpr (MODE == kSelMerge) {
+#pragma unroll
+            for (int q = 0; q < kSelParts; ++q) scnt[q] += (int)__popcll(__ballot(kp && id / kSelSlice == q));
+        }
     }
     if constexpr (MODE == kSelPart) {
-        if (tid == 0) a.pcnt[row * kSelParts + part] = min(total, a.top_t);
+        if (tid == 0) a.pcnt[row * kSelParts + part] = min(total, a.quota);
     } else {
         for (int x = total + tid; x < a.top_t; x += SEL_THREADS) list[x] = -1;
         if (tid == 0) a.nfar[row] = total_lo;
+    }
+    if constexpr (MODE == kSelMerge) {
+        if (lane == 0) {
+#pragma unroll
+            for (int q = 0; q < kSelParts; ++q) atomicAdd(&s_sel[q], scnt[q]);
+        }
+        __syncthreads();
+        if (tid == 0) {
+            // a slice that held ids back and saw every id it passed on kept
+            // may have dropped a better one than the merged k-th
+            int redo = 0;
+            if (a.quota < a.top_t) {
+                for (int q = 0; q < kSelParts; ++q) {
+                    const int ns = max(0, min(p - q * kSelSlice, kSelSlice));
+                    redo |= ns > a.quota && s_sel[q] >= a.quota;
+                }
+            }
+            a.redo[row] = redo;
+        }
     }
 }
 
@@ -670,18 +704,28 @@ hipError_t launch_decode_select(const DecArgs& a, hipStream_t s) {
         hipLaunchKernelGGL(dec_scores_kernel<false>, sg, dim3(DEC_THREADS), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (!dec_split_select((long long)a.Bt * a.Nq, a.Nk, a.top_t) || !a.plist) {
+    if (!dec_split_select((long long)a.Bt * a.Nq, a.Nk, a.top_t) || !a.plist || !a.redo) {
+        DecArgs b = a;
+        b.redo = nullptr;
         hipLaunchKernelGGL((dec_select_kernel<65536 / SEL_THREADS, kSelWhole>),
-                           dim3((unsigned)a.Nq, (unsigned)a.Bt), dim3(SEL_THREADS), 0, s, a);
+                           dim3((unsigned)a.Nq, (unsigned)a.Bt), dim3(SEL_THREADS), 0, s, b);
         return hipGetLastError();
     }
+    if (a.quota < 1 || a.quota > dec_sel_quota(kDecSplitMaxTop) || a.quota > a.top_t)
+        return hipErrorInvalidValue;
     // Long histories: the slices' selections spread over kSelParts
     // workgroups per query, then the merge.
     hipLaunchKernelGGL((dec_select_kernel<kSelSlice / SEL_THREADS, kSelPart>),
                        dim3((unsigned)a.Nq, (unsigned)a.Bt, (unsigned)kSelParts), dim3(SEL_THREADS), 0, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((dec_select_kernel<kSelParts * kDecSplitMaxTop / SEL_THREADS, kSelMerge>),
+    constexpr int kMergePT = (kSelParts * dec_sel_quota(kDecSplitMaxTop) + SEL_THREADS - 1) / SEL_THREADS;
+    hipLaunchKernelGGL((dec_select_kernel<kMergePT, kSelMerge>), dim3((unsigned)a.Nq, (unsigned)a.Bt),
+                       dim3(SEL_THREADS), 0, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // queries whose merge may be inexact, selected again whole
+    hipLaunchKernelGGL((dec_select_kernel<65536 / SEL_THREADS, kSelWhole>),
                        dim3((unsigned)a.Nq, (unsigned)a.Bt), dim3(SEL_THREADS), 0, s, a);
     return hipGetLastError();
 }

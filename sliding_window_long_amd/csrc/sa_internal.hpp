@@ -243,6 +243,8 @@ struct DecArgs {
     int32_t* nfar;          // [Bt, Nq] kept tokens before the window
     int32_t* plist;         // [Bt, Nq, kDecSelParts, top_t] slice selections, or nullptr
     int32_t* pcnt;          // [Bt, Nq, kDecSelParts] their lengths
+    int quota;              // ids kept per slice (dec_sel_quota(top_t))
+    int32_t* redo;          // [Bt, Nq] set by the merge when its result may be inexact
     float* part;            // [Bt*Hq*Nq, cmax, D + 2] partials (o, m, l) of each key tile
     int cmax;               // tiles of dec_chunk(f32) attended keys per query, upper bound
     void* out;              // [Bt, Hq, Nq, D], the input dtype
@@ -257,6 +259,13 @@ struct DecArgs {
 constexpr int kDecSelParts = 8, kDecSplitNk = 16384, kDecSplitMaxTop = 2048, kDecSplitRows = 32;
 inline bool dec_split_select(long long rows, int Nk, int top_t) {
     return rows <= kDecSplitRows && Nk > kDecSplitNk && top_t > 0 && top_t <= kDecSplitMaxTop;
+}
+// Each slice passes on its best dec_sel_quota(top_t) ids: a quarter of
+// top_t plus 64 (about twice a slice's expected share of the top_t when the
+// best ids spread over the slices).  Where the merge cannot show that no
+// slice held back a winner, the query is selected again whole.
+__host__ __device__ constexpr int dec_sel_quota(int top_t) {
+    return top_t < top_t / 4 + 64 ? top_t : top_t / 4 + 64;
 }
 hipError_t launch_decode_select(const DecArgs& a, hipStream_t s);
 hipError_t launch_decode_attn(const DecArgs& a, hipStream_t s);

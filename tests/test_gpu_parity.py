@@ -463,25 +463,27 @@ def test_decode_token(dev, Nk, nq, top_t, window):
                                                 (20000, 40, 100, 16)])
 def test_decode_token_long_history(dev, Nk, nq, top_t, window):
     # Histories over 16384 keys: with top_t <= 2048 the selection runs per
-    # slice of 8192 ids and merges (17000: the last slice is shorter than
-    # top_t and keeps all; 65536: every slice full); top_t 3000, and 40
-    # queries (enough workgroups to spread), take the one-workgroup-per-query
-    # selection.
+    # slice of 8192 ids and merges (17000: the slices pass on 576, 576 and
+    # 616 ids, fewer than top_t, so the query is selected again whole;
+    # 65536: every slice full); top_t 3000, and 40 queries (enough
+    # workgroups to spread), take the one-workgroup-per-query selection.
     wl = W.Workload("dec_long", 1, 2, 1, Nk, 64, "bf16", window=window, token_top_k=top_t,
                     index_dim=64, sink=True)
     run_and_check(decode_inputs(wl, nq, 7 + nq + top_t), dev, label=f"decode_long Nk={Nk} k={top_t}")
 
 
-@pytest.mark.parametrize("Nk", [1500, 20000])
-def test_decode_token_ties(dev, Nk):
+@pytest.mark.parametrize("Nk,top_t", [(1500, 37), (20000, 37), (20000, 300)])
+def test_decode_token_ties(dev, Nk, top_t):
     # Equal indexer keys: the lowest token ids win in the decode step too.
-    # (20000 keys: per-slice selections and their merge.)
-    wl = W.Workload("dec_ties", 1, 2, 1, Nk, 64, "bf16", window=2, token_top_k=37, index_dim=64)
+    # (20000 keys: per-slice selections and their merge; with top 300 the
+    # first slice passes on only its best 139, all of them kept, so the
+    # query is selected again whole.)
+    wl = W.Workload("dec_ties", 1, 2, 1, Nk, 64, "bf16", window=2, token_top_k=top_t, index_dim=64)
     inp = decode_inputs(wl, 4, 5)
     inp.idx_k[:] = inp.idx_k[:, :1]
     out, lse, _, tsel = run_device(inp, dev)
     for r in range(4):
-        assert tsel[0, r].tolist() == list(range(37)), r
+        assert tsel[0, r].tolist() == list(range(top_t)), r
     rep = check(inp, out, lse, np.arange(2 * 4), None, tsel)
     log(f"[gpu] decode_ties {rep}")
     assert rep.ok(), str(rep)
