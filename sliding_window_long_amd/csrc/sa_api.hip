@@ -124,7 +124,7 @@ int make_plan(const sparse_attn_cfg* c, Plan* p, bool bwd = false) {
             P.o_dec_list = take((size_t)P.Bt * P.N * P.top_t * 4);
             P.o_dec_nfar = take((size_t)P.Bt * P.N * 4);
             if (sa::dec_split_select((long long)P.Bt * P.N, P.Nk, P.top_t)) {
-                P.o_dec_plist = take((size_t)P.Bt * P.N * sa::kDecSelParts * P.top_t * 4);
+                P.o_dec_plist = take((size_t)P.Bt * P.N * sa::kDecSelParts * 2 * P.top_t * 4);
                 P.o_dec_pcnt = take((size_t)P.Bt * P.N * sa::kDecSelParts * 4);
                 P.o_dec_redo = take((size_t)P.Bt * P.N * 4);
             }

@@ -184,8 +184,9 @@ constexpr int kSelSlice = 65536 / kSelParts;
 // t handles candidates x = u * SEL_THREADS + t (u < PT).  MODE kSelWhole: the
 // whole history, x = j.  A long history is split: kSelPart selects, for each
 // of kSelParts slices of kSelSlice ids (blockIdx.z), the min(quota, slice
-// length) best of the slice into plist (count in pcnt); kSelMerge then
-// selects from the concatenated slice lists (ids staged in LDS).  A slice
+// length) best of the slice into plist, ids then their scores (count in
+// pcnt); kSelMerge then selects from the concatenated slice lists (ids and
+// scores staged in LDS).  A slice
 // whose ids were not all passed on dropped only keys below its lowest
 // passed key; when that key is not among the merged best (or the slice
 // passed on everything, or quota = top_t), nothing dropped can beat the
@@ -215,6 +216,7 @@ __global__ __launch_bounds__(SEL_THREADS) void dec_select_kernel(DecArgs a) {
     __shared__ uint32_t s_n;
     __shared__ uint64_t cand[kSelRank];
     __shared__ int s_ids[MODE == kSelMerge ? NC : 1];
+    __shared__ float s_sc[MODE == kSelMerge ? NC : 1];
     __shared__ int s_sel[kSelParts];   // merge: merged best per slice
     const int r = blockIdx.x, bt = blockIdx.y, part = blockIdx.z, tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
@@ -246,8 +248,11 @@ __global__ __launch_bounds__(SEL_THREADS) void dec_select_kernel(DecArgs a) {
         n = off[kSelParts];
 #pragma unroll
         for (int q = 0; q < kSelParts; ++q) {
-            const int32_t* pl = a.plist + (row * kSelParts + q) * a.top_t;
-            for (int x = tid; x < pc[q]; x += SEL_THREADS) s_ids[off[q] + x] = pl[x];
+            const int32_t* pl = a.plist + (row * kSelParts + q) * 2 * a.top_t;
+            for (int x = tid; x < pc[q]; x += SEL_THREADS) {
+                s_ids[off[q] + x] = pl[x];
+                s_sc[off[q] + x] = __int_as_float(pl[a.top_t + x]);
+            }
         }
         k = min(a.top_t, p);
         __syncthreads();
@@ -256,6 +261,10 @@ __global__ __launch_bounds__(SEL_THREADS) void dec_select_kernel(DecArgs a) {
         if constexpr (MODE == kSelMerge) return s_ids[x];
         else return j0 + x;
     };
+    auto score_of = [&](int x) -> float {
+        if constexpr (MODE == kSelMerge) return s_sc[x];
+        else return sc[j0 + x];
+    };
     const bool sel = k > 0 && k < n;   // otherwise every candidate (k >= n) or none is kept
     uint32_t bstar = 0;
 
@@ -263,7 +272,7 @@ __global__ __launch_bounds__(SEL_THREADS) void dec_select_kernel(DecArgs a) {
         // 1. range (slots past n re-read candidate n - 1, which leaves it unchanged)
         float sv[PT];
 #pragma unroll
-        for (int u = 0; u < PT; ++u) sv[u] = sc[id_of(min(u * SEL_THREADS + tid, n - 1))];
+        for (int u = 0; u < PT; ++u) sv[u] = score_of(min(u * SEL_THREADS + tid, n - 1));
         float lo_s = sv[0], hi_s = sv[0];
 #pragma unroll
         for (int u = 1; u < PT; ++u) {
@@ -335,7 +344,7 @@ __global__ __launch_bounds__(SEL_THREADS) void dec_select_kernel(DecArgs a) {
                 const int x = u * SEL_THREADS + tid;
                 if (x < n && binv[x] == bstar) {
                     const int j = id_of(x);
-                    cand[atomicAdd(&s_n, 1u)] = dec_key(sc[j], j) << 16 | (uint64_t)x;
+                    cand[atomicAdd(&s_n, 1u)] = dec_key(score_of(x), j) << 16 | (uint64_t)x;
                 }
             }
             __syncthreads();
@@ -357,7 +366,7 @@ __global__ __launch_bounds__(SEL_THREADS) void dec_select_kernel(DecArgs a) {
                     uint32_t ov = 0, ix = 0;
                     if (in) {
                         const int j = id_of(x);
-                        ov = dec_ord32(sc[j]);
+                        ov = dec_ord32(score_of(x));
                         ix = 0xffffu - (uint32_t)j;
                     }
                     const bool match = in && (ov & msk_hi) == pre_hi && (ix & msk_lo) == pre_lo;
@@ -383,7 +392,7 @@ __global__ __launch_bounds__(SEL_THREADS) void dec_select_kernel(DecArgs a) {
                 const int x = u * SEL_THREADS + tid;
                 if (x < n && binv[x] == bstar) {
                     const int j = id_of(x);
-                    if (dec_key(sc[j], j) >= thr) binv[x] = kSelKept;
+                    if (dec_key(score_of(x), j) >= thr) binv[x] = kSelKept;
                 }
             }
         }
@@ -413,7 +422,7 @@ __global__ __launch_bounds__(SEL_THREADS) void dec_select_kernel(DecArgs a) {
     const int base = sh[lane * NW + w];
     const uint32_t below_lo = lane >= 32 ? 0xffffffffu : (1u << lane) - 1u;
     const uint32_t below_hi = lane < 32 ? 0u : (lane == 63 ? 0x7fffffffu : (1u << (lane - 32)) - 1u);
-    int32_t* const list = MODE == kSelPart ? a.plist + (row * kSelParts + part) * a.top_t
+    int32_t* const list = MODE == kSelPart ? a.plist + (row * kSelParts + part) * 2 * a.top_t
                                            : a.list + row * a.top_t;
     int scnt[kSelParts] = {};   // merge: this wave's kept ids per slice
 #pragma unroll
@@ -423,7 +432,10 @@ __global__ __launch_bounds__(SEL_THREADS) void dec_select_kernel(DecArgs a) {
         const bool kp = ((lane < 32 ? ml >> lane : mh >> (lane - 32)) & 1u) != 0;
         const int pos = __builtin_amdgcn_readlane(base, u) + __popc(ml & below_lo) + __popc(mh & below_hi);
         const int id = kp ? id_of(u * SEL_THREADS + tid) : 0;
-        if (kp && pos < a.top_t) list[pos] = id;
+        if (kp && pos < a.top_t) {
+            list[pos] = id;
+            if constexpr (MODE == kSelPart) list[a.top_t + pos] = __float_as_int(sc[id]);
+        }
         if constexpr (MODE == kSelMerge) {
 #pragma unroll
             for (int q = 0; q < kSelParts; ++q) scnt[q] += (int)__popcll(__ballot(kp && id / kSelSlice == q));

@@ -241,7 +241,8 @@ struct DecArgs {
     float* scores;          // [Bt, Nq, Nk] indexer scores
     int32_t* list;          // [Bt, Nq, top_t] kept tokens, ascending, -1 padded; nullptr: no gate
     int32_t* nfar;          // [Bt, Nq] kept tokens before the window
-    int32_t* plist;         // [Bt, Nq, kDecSelParts, top_t] slice selections, or nullptr
+    int32_t* plist;         // [Bt, Nq, kDecSelParts, 2, top_t] slice selections (ids, then
+                            // their scores' bits), or nullptr
     int32_t* pcnt;          // [Bt, Nq, kDecSelParts] their lengths
     int quota;              // ids kept per slice (dec_sel_quota(top_t))
     int32_t* redo;          // [Bt, Nq] set by the merge when its result may be inexact
