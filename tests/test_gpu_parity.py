@@ -472,6 +472,14 @@ def test_decode_token_long_history(dev, Nk, nq, top_t, window):
     run_and_check(decode_inputs(wl, nq, 7 + nq + top_t), dev, label=f"decode_long Nk={Nk} k={top_t}")
 
 
+def test_decode_token_long_history_batch(dev):
+    # Two sequences: the slice lists, counts and redo flags of each
+    # (sequence, query) are kept apart.
+    wl = W.Workload("dec_long_b2", 2, 2, 1, 20000, 64, "bf16", window=16, token_top_k=300,
+                    index_dim=64, sink=True)
+    run_and_check(decode_inputs(wl, 3, 77), dev, label="decode_long batch 2")
+
+
 @pytest.mark.parametrize("Nk,top_t", [(1500, 37), (20000, 37), (20000, 300)])
 def test_decode_token_ties(dev, Nk, top_t):
     # Equal indexer keys: the lowest token ids win in the decode step too.
