@@ -156,6 +156,33 @@ def check(inp, dev_out, dev_lse, rows, dev_bsel=None, dev_tsel=None, *, kbar=Non
     return rep
 
 
+def check_token_selection(inp, dev_tsel, trows) -> Report:
+    """The token selection alone on token rows r = b*N + i (the selection is
+    shared by every head): exact on decisive rows, a valid tolerant top-m
+    elsewhere (the rule of `check`).  No outputs are compared, so rows cost
+    only the oracle's indexer scores and sort (i x index_dim MACs each)."""
+    wl = inp.wl
+    trows = np.asarray(trows, dtype=np.int64)
+    rep = Report(rows=len(trows))
+    ts, t_last, t_next = oracle.token_select(inp.idx_q, inp.idx_k, wl.token_top_k, trows)
+    gts = dev_tsel.reshape(-1, wl.token_top_k)[trows]
+    gap = _gap_rel(t_last, t_next)
+    same = np.array([set(a[a >= 0]) == set(b[b >= 0]) for a, b in zip(gts, ts)])
+    dec = gap > GAP_REL
+    rep.decisive = int(dec.sum())
+    rep.mismatched = int((dec & ~same).sum())
+    rep.non_decisive = int((~dec).sum())
+    nd = np.flatnonzero(~dec & ~same)
+    if len(nd):
+        sc = oracle.token_scores(inp.idx_q, inp.idx_k, trows[nd])
+        for t, r in enumerate(nd):
+            chosen = {int(j) for j in gts[r] if j >= 0}
+            want = len([j for j in ts[r] if j >= 0])
+            if len(chosen) != want or not _valid_tolerant(chosen, sc[t], t_last[r], t_next[r]):
+                rep.invalid += 1
+    return rep
+
+
 # Gradients (bf16 outputs; fp16 P and dS operands; D_i from the bf16 forward
 # output): per tensor, max |g - g*| <= 2e-2 S_max and mean |g - g*| <=
 # 1e-2 S_mean, S = the tensor's own max |g*| (mean |g*|), floored at 1e-2 of

@@ -421,8 +421,29 @@ def test_swa_token_reduced_sampled(dev):
 
 
 def test_swa_token_full_sampled(dev):
+    # Outputs and lse on sampled rows; the token selection (made per
+    # position, shared by the heads) on 2048 random positions plus every
+    # position of one 128-row tile in each 8192.
+    from parity import check_token_selection
     wl = W.SWA_TOKEN_TOPK
-    run_and_check(W.make_inputs(wl, 105), dev, W.sample_rows(wl, 160, 5), label="swa_token_full")
+    inp = W.make_inputs(wl, 105)
+    log(f"[gpu] swa_token_full {wl}")
+    out, lse, bsel, tsel = run_device(inp, dev)
+    rep = check(inp, out, lse, W.sample_rows(wl, 160, 5), bsel, tsel)
+    log(f"[gpu] swa_token_full outputs {rep}")
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    assert rep.ok(), str(rep)
+    N = wl.seq_len
+    rng = np.random.default_rng(55)
+    pos = set(rng.choice(N, size=2048, replace=False).tolist())
+    for t0 in range(0, N, 8192):
+        start = t0 + 128 * int(rng.integers(0, 64))
+        pos.update(range(start, start + 128))
+    pos = np.array(sorted(pos), dtype=np.int64)
+    srep = check_token_selection(inp, tsel, pos)
+    log(f"[gpu] swa_token_full selection on {len(pos)} positions: {srep}")
+    assert len(pos) >= 2048 + 1024 - 64
+    assert srep.mismatched == 0 and srep.invalid == 0, str(srep)
 
 
 # --- decode/append step (queries continuing a cached history) ---------------
