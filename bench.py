@@ -125,7 +125,41 @@ def device_inputs(wl, seed, dev):
     return inp, {k: (None if v is None else v.to(dev)) for k, v in t.items()}
 
 
+def timed_calls(fn, steps, warmup):
+    """`warmup` untimed calls, then exactly `steps` calls bracketed by
+    torch.cuda.synchronize() on both sides.  Each call is bracketed by HIP
+    events on torch's current stream (the stream the library launches on),
+    and the library records an event pair around each of its kernels on the
+    same stream (two event records per stage: microseconds against calls of
+    tenths of a millisecond and up).  Returns (wall-clock mean ms, median
+    call ms, mean call ms, {stage: median ms})."""
+    import torch
+    import sliding_window_long_amd as sa
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    sa.sparse_attn_set_timing(True)
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    sa.sparse_attn_set_timing(False)
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    stages = {}
+    for name, sms in sa.sparse_attn_stage_times(1024):
+        stages.setdefault(name, []).append(sms)
+    stage_ms = {k: float(np.median(v)) for k, v in stages.items()}
+    return (t1 - t0) * 1e3 / steps, float(np.median(ms)), float(ms.mean()), stage_ms
+
+
 def time_workload(wl, seed, dev, steps, warmup, want_sel=False):
+    """Returns (inputs, timing dict, stage_ms, (bsel, tsel)); timing holds
+    ms (median event time per call), ms_wall_mean and ms_event_mean."""
     import torch
     import sliding_window_long_amd as sa
     inp, g = device_inputs(wl, seed, dev)
@@ -144,21 +178,11 @@ def time_workload(wl, seed, dev, steps, warmup, want_sel=False):
         bsel = None if bsel_t is None else bsel_t.cpu().numpy()
         tsel = None if tsel_t is None else tsel_t.cpu().numpy()
         del bsel_t, tsel_t
-    for _ in range(warmup):
+
+    def call():
         sa.forward(g["q"], g["k"], g["v"], out=out, lse=lse, **kw)
-    torch.cuda.synchronize()
-    sa.sparse_attn_set_timing(True)
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        sa.forward(g["q"], g["k"], g["v"], out=out, lse=lse, **kw)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    sa.sparse_attn_set_timing(False)
-    stages = {}
-    for name, ms in sa.sparse_attn_stage_times(1024):
-        stages.setdefault(name, []).append(ms)
-    stage_ms = {k: float(np.mean(v)) for k, v in stages.items()}
-    return inp, (t1 - t0) * 1e3 / steps, stage_ms, (bsel, tsel)
+    wall, med, mean, stage_ms = timed_calls(call, steps, warmup)
+    return inp, dict(ms=med, ms_wall_mean=wall, ms_event_mean=mean), stage_ms, (bsel, tsel)
 
 
 # Block-gate variants on the block-gated workloads: the min/max block
@@ -179,8 +203,8 @@ BACKWARD = [W.BORA_HYBRID, W.BITAXON_SWA, W.LONG_MOBA]
 
 
 def time_backward(wl, seed, dev, steps, warmup):
-    """Time sparse_attn_bwd after one forward; returns (ms, stage_ms,
-    attended pairs)."""
+    """Time sparse_attn_bwd after one forward; returns (ms (median event
+    time), stage_ms, attended pairs)."""
     import torch
     import sliding_window_long_amd as sa
     inp, g = device_inputs(wl, seed, dev)
@@ -190,21 +214,12 @@ def time_backward(wl, seed, dev, steps, warmup):
     dout = torch.randn(g["q"].shape, dtype=torch.float32, device=dev,
                        generator=torch.Generator(device=dev).manual_seed(seed)).to(torch.bfloat16)
     ws = sa.Workspace()
-    for _ in range(warmup):
+
+    def call():
         sa.backward(g["q"], g["k"], g["v"], out, lse, dout, workspace=ws, **kw)
-    torch.cuda.synchronize()
-    sa.sparse_attn_set_timing(True)
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        sa.backward(g["q"], g["k"], g["v"], out, lse, dout, workspace=ws, **kw)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    sa.sparse_attn_set_timing(False)
-    stages = {}
-    for name, ms in sa.sparse_attn_stage_times(1024):
-        stages.setdefault(name, []).append(ms)
+    _, med, _, stage_ms = timed_calls(call, steps, warmup)
     pairs = attended_pairs(wl, None if bsel is None else bsel.cpu().numpy())
-    return (t1 - t0) * 1e3 / steps, {k: float(np.mean(v)) for k, v in stages.items()}, pairs
+    return med, stage_ms, pairs
 
 
 # Decode/append steps: nq new tokens per sequence after a cache of
@@ -243,21 +258,10 @@ def time_decode(wl, nq, seed, dev, steps, warmup):
     kv_bytes = keys * wl.n_kv_heads * wl.head_dim * 2 * 2
     qo_bytes = wl.batch * wl.n_q_heads * nq * (wl.head_dim * 2 * 2 + 4)
     idx_bytes = wl.batch * (wl.seq_len + nq) * wl.index_dim * 2 if wl.token_top_k else 0
-    for _ in range(warmup):
+    def call():
         sa.forward(q, g["k"], g["v"], out=out, lse=lse, **kw)
-    torch.cuda.synchronize()
-    sa.sparse_attn_set_timing(True)
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        sa.forward(q, g["k"], g["v"], out=out, lse=lse, **kw)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    sa.sparse_attn_set_timing(False)
-    stages = {}
-    for name, ms in sa.sparse_attn_stage_times(1024):
-        stages.setdefault(name, []).append(ms)
-    return (t1 - t0) * 1e3 / steps, {k: float(np.mean(v)) for k, v in stages.items()}, \
-        kv_bytes + qo_bytes + idx_bytes
+    _, med, _, stage_ms = timed_calls(call, steps, warmup)
+    return med, stage_ms, kv_bytes + qo_bytes + idx_bytes
 
 
 def cpu_baseline(inp, budget_s=15.0):
@@ -277,8 +281,17 @@ def cpu_baseline(inp, budget_s=15.0):
     oracle.attend(inp.q, inp.k, inp.v, rows=rows, **kw)
     dt = time.perf_counter() - t0
     cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": (n / wl.n_q_heads) / dt, "unit": "tokens/s", "cores": cores,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model, "host_cpus": os.cpu_count(),
             "sample": f"{n} uniformly sampled (head, query) rows of {wl.name} "
                       f"({dt:.1f} s), tokens/s = rows / n_q_heads / seconds"}
 
@@ -286,11 +299,11 @@ def cpu_baseline(inp, budget_s=15.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-extra", action="store_true", help="only the headline workload")
-    ap.add_argument("--extra-steps", type=int, default=5)
+    ap.add_argument("--extra-steps", type=int, default=10)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB device copy, the known-traffic kernel "
                          "that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
@@ -314,7 +327,8 @@ def main():
 
     wl = W.BITAXON_SWA
     print(f"[bench] headline {wl.name}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)
-    inp, ms, stage_ms, _ = time_workload(wl, 3, dev, args.steps, args.warmup)
+    inp, tm, stage_ms, _ = time_workload(wl, 3, dev, args.steps, args.warmup)
+    ms = tm["ms"]
     pairs = attended_pairs(wl)
     flops = 4.0 * wl.head_dim * pairs
     tokens = wl.batch * wl.seq_len
@@ -330,6 +344,12 @@ def main():
         "unit": "tokens/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms,
+        "ms_wall_mean": tm["ms_wall_mean"],
+        "ms_event_mean": tm["ms_event_mean"],
+        "timing": "value and ms_per_step: median of the per-call HIP event times over the "
+                  "timed steps; ms_wall_mean: wall clock of the timed steps / steps; "
+                  "stage_ms and roofline.kernel_ms: medians of the library's per-stage HIP "
+                  "events in the same calls",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -353,8 +373,9 @@ def main():
         for idx, ewl in [(i, W.WORKLOADS[i]) for i in (1, 2, 4, 5)] + \
                 [({4096: 2, 16384: 3}.get(v.seq_len, 4), v) for v in GATE_VARIANTS]:
             print(f"[bench] workload {ewl.name}", file=sys.stderr, flush=True)
-            _, ems, est, (bsel, tsel) = time_workload(ewl, idx, dev, args.extra_steps, 2,
+            _, etm, est, (bsel, tsel) = time_workload(ewl, idx, dev, args.extra_steps, 2,
                                                       want_sel=True)
+            ems = etm["ms"]
             ep = attended_pairs(ewl, bsel, tsel)
             ef = 4.0 * ewl.head_dim * ep
             extra[ewl.name] = {"ms_per_step": ems,

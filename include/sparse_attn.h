@@ -204,8 +204,9 @@ const char* sparse_attn_strerror(int status);
  * sparse_attn_set_timing(0) stops recording.  sparse_attn_stage_times waits
  * for the recorded events and writes up to `capacity` stage names (static
  * strings) and durations in milliseconds, in enqueue order; *n_stages
- * receives the number recorded.  The record is process-wide: time one caller
- * at a time. */
+ * receives the number recorded.  The record belongs to the calling host
+ * thread (only calls made from that thread are recorded): the one piece of
+ * state the library keeps between calls, and only while timing is on. */
 int sparse_attn_set_timing(int enable);
 int sparse_attn_stage_times(int32_t* n_stages, const char** names, float* ms,
                             int32_t capacity);

@@ -201,7 +201,11 @@ def params_for(q, k, *, block_size=0, top_k=0, window=0, token_top_k=0, index_di
 
 
 class Workspace:
-    """A reusable device workspace (grown on demand, never shrunk)."""
+    """A reusable device workspace (grown on demand, never shrunk), used on
+    torch's current stream of the call.  A buffer reused on a stream other
+    than the one it was allocated on is recorded on that stream, so the
+    caching allocator does not hand its memory out again (when the buffer
+    grows) before the work queued there is done."""
 
     def __init__(self):
         self.buf = None
@@ -212,10 +216,67 @@ class Workspace:
             return None
         if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
             self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        else:
+            self.buf.record_stream(torch.cuda.current_stream(device))
         return self.buf
 
 
-_default_ws = Workspace()
+# Default workspaces, one per (device, stream).
+_default_ws: dict = {}
+
+
+def _workspace_for(workspace, device):
+    import torch
+    if workspace is not None:
+        return workspace
+    key = (str(device), torch.cuda.current_stream(device).cuda_stream)
+    return _default_ws.setdefault(key, Workspace())
+
+
+def _need(cond: bool, msg: str, exc=ValueError):
+    if not cond:
+        raise exc(msg)
+
+
+def _check_fwd_tensors(q, k, v, idx_q, idx_k, sink, out, lse, token_top_k):
+    """Shapes, dtypes, contiguity and device of every tensor the call hands
+    to the library, against q (checked before any launch: a mismatch would
+    make the kernels read or write past an allocation)."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t.dim() == 4, f"{name} must be 4-D [batch, heads, positions, head_dim]")
+        _need(t.dtype == q.dtype, "q, k, v must share one dtype", TypeError)
+        _need(t.is_contiguous(), f"{name} must be contiguous")
+    Bt, Hq, N, d = q.shape
+    _need(tuple(v.shape) == tuple(k.shape), "v must have k's shape")
+    _need(k.shape[0] == Bt and k.shape[3] == d, "k, v must match q's batch and head_dim")
+    Nk = k.shape[2]
+    _need((idx_q is None) == (idx_k is None), "idx_q and idx_k go together")
+    _need(token_top_k == 0 or idx_q is not None, "token_top_k needs idx_q and idx_k")
+    if idx_q is not None:
+        for name, t, n in (("idx_q", idx_q, N), ("idx_k", idx_k, Nk)):
+            _need(t.dim() == 3 and t.shape[0] == Bt and t.shape[1] == n,
+                  f"{name} must be [batch, {n}, index_dim]")
+            _need(t.dtype == q.dtype, f"{name} must have q's dtype", TypeError)
+            _need(t.is_contiguous(), f"{name} must be contiguous")
+        _need(idx_q.shape[2] == idx_k.shape[2], "idx_q and idx_k index dims differ")
+    if sink is not None:
+        _need(sink.dtype == torch.float32, "sink must be float32", TypeError)
+        _need(tuple(sink.shape) == (Hq,) and sink.is_contiguous(),
+              "sink must be a contiguous [n_q_heads] tensor")
+    out_dt = torch.bfloat16 if q.dtype == torch.float8_e4m3fn else q.dtype
+    if out is not None:
+        _need(tuple(out.shape) == tuple(q.shape), "out must have q's shape")
+        _need(out.dtype == out_dt, f"out must be {out_dt}", TypeError)
+        _need(out.is_contiguous(), "out must be contiguous")
+    if lse is not None:
+        _need(tuple(lse.shape) == (Bt, Hq, N), "lse must be [batch, n_q_heads, positions]")
+        _need(lse.dtype == torch.float32, "lse must be float32", TypeError)
+        _need(lse.is_contiguous(), "lse must be contiguous")
+    for name, t in (("q", q), ("k", k), ("v", v), ("idx_q", idx_q), ("idx_k", idx_k),
+                    ("sink", sink), ("out", out), ("lse", lse)):
+        if t is not None:
+            _need(t.is_cuda and t.device == q.device, f"{name} must be on q's device ({q.device})")
 
 
 def forward(q, k, v, *, block_size=0, top_k=0, window=0, idx_q=None, idx_k=None,
@@ -230,11 +291,7 @@ def forward(q, k, v, *, block_size=0, top_k=0, window=0, idx_q=None, idx_k=None,
     "minmax"), gate_shared and gate_first select the block gate's variant;
     cmp_block > 0 adds the compressed branch (see the C header)."""
     import torch
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous device tensor")
-        if t.dtype != q.dtype:
-            raise TypeError("q, k, v must share one dtype")
+    _check_fwd_tensors(q, k, v, idx_q, idx_k, sink, out, lse, token_top_k)
     index_dim = idx_q.shape[-1] if idx_q is not None else 0
     p = params_for(q, k, block_size=block_size, top_k=top_k, window=window,
                    token_top_k=token_top_k, index_dim=index_dim, scale=scale,
@@ -257,11 +314,9 @@ def forward(q, k, v, *, block_size=0, top_k=0, window=0, idx_q=None, idx_k=None,
     if idx_q is not None:
         cfg.idx_q, cfg.idx_k = idx_q.data_ptr(), idx_k.data_ptr()
     if sink is not None:
-        if sink.dtype != torch.float32 or not sink.is_cuda:
-            raise TypeError("sink must be a float32 device tensor")
         cfg.sink = sink.data_ptr()
     nbytes = sparse_attn_workspace_bytes(cfg)
-    ws = (workspace or _default_ws).get(nbytes, dev)
+    ws = _workspace_for(workspace, dev).get(nbytes, dev)
     cfg.workspace = None if ws is None else ws.data_ptr()
     cfg.workspace_bytes = nbytes
     cfg.stream = torch.cuda.current_stream(dev).cuda_stream
@@ -275,6 +330,8 @@ def block_pool(k, block_size: int, gate_repr: str = "mean"):
     """The pooling stage alone, fp32: mean keys [Bt, Hkv, N/B, d], or for
     gate_repr="minmax" the per-dimension (min, max) [Bt, Hkv, N/B, 2, d]."""
     import torch
+    _need(k.dim() == 4 and k.is_contiguous(), "k must be a contiguous 4-D tensor")
+    _need(k.is_cuda, "k must be a device tensor")
     Bt, Hkv, N, d = k.shape
     p = params_for(k, k, block_size=block_size, top_k=1, gate_repr=gate_repr)
     cfg = p.cfg()
@@ -293,23 +350,23 @@ def backward(q, k, v, out, lse, dout, *, block_size=0, top_k=0, window=0, sink=N
     out).  bf16 tensors on one device; returns (dq, dk, dv, dsink), dsink
     None without a sink."""
     import torch
-    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout)):
-        if not t.is_cuda or not t.is_contiguous() or t.dtype != torch.bfloat16:
-            raise ValueError(f"{name} must be a contiguous bfloat16 device tensor")
-    if lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 device tensor")
+    _need(q.dtype == torch.bfloat16, "the backward takes bfloat16 tensors", TypeError)
+    _need(q.dim() == 4 and k.dim() == 4 and k.shape[2] == q.shape[2],
+          "the backward is a prefill: k, v over q's positions")
+    _need(tuple(dout.shape) == tuple(q.shape) and dout.dtype == q.dtype and dout.is_contiguous(),
+          "dout must be a contiguous tensor of q's shape and dtype")
+    _check_fwd_tensors(q, k, v, None, None, sink, out, lse, 0)
+    _need(dout.is_cuda and dout.device == q.device, "dout must be on q's device")
     p = params_for(q, k, block_size=block_size, top_k=top_k, window=window, scale=scale,
                    gate_repr=gate_repr, gate_shared=gate_shared, gate_first=gate_first)
     cfg = p.cfg()
     dev = q.device
     if sink is not None:
-        if sink.dtype != torch.float32 or not sink.is_cuda:
-            raise TypeError("sink must be a float32 device tensor")
         cfg.sink = sink.data_ptr()
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     dsink = None if sink is None else torch.empty_like(sink)
     nbytes = sparse_attn_bwd_workspace_bytes(cfg)
-    ws = (workspace or _default_ws).get(nbytes, dev)
+    ws = _workspace_for(workspace, dev).get(nbytes, dev)
     cfg.workspace = None if ws is None else ws.data_ptr()
     cfg.workspace_bytes = nbytes
     cfg.stream = torch.cuda.current_stream(dev).cuda_stream

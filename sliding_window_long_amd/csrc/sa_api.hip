@@ -268,7 +268,9 @@ struct Timing {
     const char* names[kMaxStages];
     hipEvent_t ev[kMaxStages][2];
 };
-Timing g_timing;
+// One record per host thread: calls made from other threads are neither
+// recorded nor disturbed by it.
+thread_local Timing g_timing;
 
 struct StageScope {
     int idx = -1;

@@ -258,15 +258,20 @@ struct DecArgs {
 // slices (one workgroup each) whose selections are then merged, provided
 // top_t <= kDecSplitMaxTop; the plan then holds plist and pcnt.
 constexpr int kDecSelParts = 8, kDecSplitNk = 16384, kDecSplitMaxTop = 2048, kDecSplitRows = 32;
-inline bool dec_split_select(long long rows, int Nk, int top_t) {
-    return rows <= kDecSplitRows && Nk > kDecSplitNk && top_t > 0 && top_t <= kDecSplitMaxTop;
-}
 // Each slice passes on its best dec_sel_quota(top_t) ids: a quarter of
 // top_t plus 64 (about twice a slice's expected share of the top_t when the
 // best ids spread over the slices).  Where the merge cannot show that no
 // slice held back a winner, the query is selected again whole.
 __host__ __device__ constexpr int dec_sel_quota(int top_t) {
     return top_t < top_t / 4 + 64 ? top_t : top_t / 4 + 64;
+}
+// The split pays only when the non-empty slices can pass on more ids than
+// top_t: otherwise the merge keeps every id it receives, always asks for a
+// whole selection, and the slices and the merge are wasted work.
+inline bool dec_split_select(long long rows, int Nk, int top_t) {
+    const long long slices = ((long long)Nk + 65536 / kDecSelParts - 1) / (65536 / kDecSelParts);
+    return rows <= kDecSplitRows && Nk > kDecSplitNk && top_t > 0 && top_t <= kDecSplitMaxTop &&
+           slices * dec_sel_quota(top_t) > top_t;
 }
 hipError_t launch_decode_select(const DecArgs& a, hipStream_t s);
 hipError_t launch_decode_attn(const DecArgs& a, hipStream_t s);

@@ -484,10 +484,10 @@ def test_decode_token(dev, Nk, nq, top_t, window):
                                                 (20000, 40, 100, 16)])
 def test_decode_token_long_history(dev, Nk, nq, top_t, window):
     # Histories over 16384 keys: with top_t <= 2048 the selection runs per
-    # slice of 8192 ids and merges (17000: the slices pass on 576, 576 and
-    # 616 ids, fewer than top_t, so the query is selected again whole;
-    # 65536: every slice full); top_t 3000, and 40 queries (enough
-    # workgroups to spread), take the one-workgroup-per-query selection.
+    # slice of 8192 ids and merges (65536: every slice full); 17000 keys with
+    # top 2048 (three slices passing on at most 3 x 576 ids, fewer than
+    # top_t), top_t 3000, and 40 queries (enough workgroups to spread), take
+    # the one-workgroup-per-query selection.
     wl = W.Workload("dec_long", 1, 2, 1, Nk, 64, "bf16", window=window, token_top_k=top_t,
                     index_dim=64, sink=True)
     run_and_check(decode_inputs(wl, nq, 7 + nq + top_t), dev, label=f"decode_long Nk={Nk} k={top_t}")
@@ -542,3 +542,25 @@ def test_decode_token_full_size(dev):
     # Four new tokens after a 65536-token cache: window 128 plus the top 2048
     # of the whole history, sink, GQA 16/4.
     run_and_check(decode_inputs(W.SWA_TOKEN_TOPK, 4, 105), dev, label="decode_token_full")
+
+
+# --- binding checks on device tensors: each malformed call raises before any launch
+@pytest.mark.parametrize("which", ["forward", "backward"])
+def test_binding_rejects_on_device(dev, which, monkeypatch):
+    import torch
+    import sliding_window_long_amd as sa
+    from binding_cases import bad_backward_args, bad_forward_args
+    cases = bad_forward_args(dev) if which == "forward" else bad_backward_args(dev)
+    torch.cuda.synchronize()
+
+    def no_library():
+        raise AssertionError("the library was reached")
+    monkeypatch.setattr(sa.binding, "load_library", no_library)
+    for name, a in cases:
+        with pytest.raises((ValueError, TypeError)):
+            if which == "forward":
+                sa.forward(a.pop("q"), a.pop("k"), a.pop("v"), **a)
+            else:
+                sa.backward(a.pop("q"), a.pop("k"), a.pop("v"), a.pop("out"), a.pop("lse"),
+                            a.pop("dout"))
+    torch.cuda.synchronize()
