@@ -117,7 +117,9 @@ enum {
     SA_E_ALIGNMENT = -5,        /* a tensor pointer is not 16-byte aligned */
     SA_E_WORKSPACE_TOO_SMALL = -6,
     SA_E_HIP = -7,              /* a kernel launch failed (hipGetLastError) */
-    SA_E_UNSUPPORTED = -8       /* a combination outside the documented limits */
+    SA_E_UNSUPPORTED = -8,      /* a combination outside the documented limits */
+    SA_E_SCRATCH_LIMIT = -9     /* sparse_attn_fwd_noalloc: the configuration needs
+                                   more workspace than its static scratch holds */
 };
 
 typedef struct {
@@ -162,6 +164,23 @@ int sparse_attn_workspace_bytes(const sparse_attn_cfg* cfg, size_t* bytes);
  * waiting.  q, k, v, out, lse are device pointers (16-byte aligned). */
 int sparse_attn_fwd(const void* q, const void* k, const void* v,
                     const sparse_attn_cfg* cfg, void* out, float* lse);
+
+/* sparse_attn_fwd for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, checks and result as sparse_attn_fwd, except
+ * that cfg->workspace and cfg->workspace_bytes are ignored: the workspace is
+ * a static device array of 128 MiB that the library holds on every device
+ * it runs on until the process ends (its address is looked up once per
+ * device, on the first call with that device current; cfg->stream must
+ * belong to the current device).  A configuration whose
+ * sparse_attn_workspace_bytes exceeds 128 MiB returns SA_E_SCRATCH_LIMIT
+ * before anything is enqueued.  Nothing is allocated.  Every call on one
+ * device shares that device's array and it keeps the last call's contents
+ * (the forward initialises whatever it reads before reading it): calls
+ * that may overlap on one device -- on different streams, or from different
+ * host threads -- race on it and must be serialised by the caller. */
+int sparse_attn_fwd_noalloc(const void* q, const void* k, const void* v,
+                            const sparse_attn_cfg* cfg, void* out, float* lse);
 
 /* The block pooling stage alone [MoBA summary page, implementation figure:
  * partition into blocks, mean pooling]: kbar[b, g, c, :] = mean of the

@@ -24,12 +24,12 @@ SA_OK = 0
 ERROR_CODES = {
     -1: "SA_E_INVALID_ARG", -2: "SA_E_SHAPE", -3: "SA_E_UNSUPPORTED_HEAD_DIM",
     -4: "SA_E_NO_SELF", -5: "SA_E_ALIGNMENT", -6: "SA_E_WORKSPACE_TOO_SMALL",
-    -7: "SA_E_HIP", -8: "SA_E_UNSUPPORTED",
+    -7: "SA_E_HIP", -8: "SA_E_UNSUPPORTED", -9: "SA_E_SCRATCH_LIMIT",
 }
 # Every symbol the C header declares.
 EXPORTS = ("sparse_attn_workspace_bytes", "sparse_attn_fwd", "sparse_attn_block_pool",
            "sparse_attn_strerror", "sparse_attn_set_timing", "sparse_attn_stage_times",
-           "sparse_attn_bwd_workspace_bytes", "sparse_attn_bwd")
+           "sparse_attn_bwd_workspace_bytes", "sparse_attn_bwd", "sparse_attn_fwd_noalloc")
 
 
 class SparseAttnCfg(ctypes.Structure):
@@ -77,6 +77,8 @@ def load_library():
     lib.sparse_attn_fwd.argtypes = [ctypes.c_void_p] * 3 + [P(SparseAttnCfg), ctypes.c_void_p,
                                                             ctypes.c_void_p]
     lib.sparse_attn_fwd.restype = ctypes.c_int
+    lib.sparse_attn_fwd_noalloc.argtypes = lib.sparse_attn_fwd.argtypes
+    lib.sparse_attn_fwd_noalloc.restype = ctypes.c_int
     lib.sparse_attn_block_pool.argtypes = [ctypes.c_void_p, P(SparseAttnCfg), ctypes.c_void_p]
     lib.sparse_attn_block_pool.restype = ctypes.c_int
     lib.sparse_attn_strerror.argtypes = [ctypes.c_int]
@@ -156,6 +158,11 @@ def _ptr(t):
 def sparse_attn_fwd(q, k, v, cfg: SparseAttnCfg, out, lse) -> None:
     _check(load_library().sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), ctypes.byref(cfg),
                                           _ptr(out), _ptr(lse)), "sparse_attn_fwd")
+
+
+def sparse_attn_fwd_noalloc(q, k, v, cfg: SparseAttnCfg, out, lse) -> None:
+    _check(load_library().sparse_attn_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), ctypes.byref(cfg),
+                                                  _ptr(out), _ptr(lse)), "sparse_attn_fwd_noalloc")
 
 
 def sparse_attn_block_pool(k, cfg: SparseAttnCfg, kbar) -> None:
@@ -282,14 +289,16 @@ def _check_fwd_tensors(q, k, v, idx_q, idx_k, sink, out, lse, token_top_k):
 def forward(q, k, v, *, block_size=0, top_k=0, window=0, idx_q=None, idx_k=None,
             token_top_k=0, sink=None, scale=None, return_selection=False,
             workspace: Workspace | None = None, out=None, lse=None, gate_repr="mean",
-            gate_shared=False, gate_first=False, cmp_block=0):
+            gate_shared=False, gate_first=False, cmp_block=0, noalloc=False):
     """Causal sparse-attention prefill on q's device and torch's current
     stream.  Returns (out, lse) or, with return_selection,
     (out, lse, block_sel, token_sel).  When k, v (and idx_k) hold more
     positions than q (and idx_q), the call is a decode/append step: the
     queries are the newest positions of that history.  gate_repr ("mean" or
     "minmax"), gate_shared and gate_first select the block gate's variant;
-    cmp_block > 0 adds the compressed branch (see the C header)."""
+    cmp_block > 0 adds the compressed branch (see the C header).  noalloc:
+    call sparse_attn_fwd_noalloc (the library's static scratch instead of a
+    workspace; out and lse are still allocated here unless given)."""
     import torch
     _check_fwd_tensors(q, k, v, idx_q, idx_k, sink, out, lse, token_top_k)
     index_dim = idx_q.shape[-1] if idx_q is not None else 0
@@ -315,12 +324,15 @@ def forward(q, k, v, *, block_size=0, top_k=0, window=0, idx_q=None, idx_k=None,
         cfg.idx_q, cfg.idx_k = idx_q.data_ptr(), idx_k.data_ptr()
     if sink is not None:
         cfg.sink = sink.data_ptr()
-    nbytes = sparse_attn_workspace_bytes(cfg)
-    ws = _workspace_for(workspace, dev).get(nbytes, dev)
-    cfg.workspace = None if ws is None else ws.data_ptr()
-    cfg.workspace_bytes = nbytes
     cfg.stream = torch.cuda.current_stream(dev).cuda_stream
-    sparse_attn_fwd(q, k, v, cfg, out, lse)
+    if noalloc:
+        sparse_attn_fwd_noalloc(q, k, v, cfg, out, lse)
+    else:
+        nbytes = sparse_attn_workspace_bytes(cfg)
+        ws = _workspace_for(workspace, dev).get(nbytes, dev)
+        cfg.workspace = None if ws is None else ws.data_ptr()
+        cfg.workspace_bytes = nbytes
+        sparse_attn_fwd(q, k, v, cfg, out, lse)
     if return_selection:
         return out, lse, bsel, tsel
     return out, lse

@@ -16,6 +16,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 namespace {
 
 constexpr size_t kAlign = 256;
@@ -339,6 +341,35 @@ int compact_far(const Plan& P, const int32_t* sel, char* ws, hipStream_t s, sa::
     return sa::launch_compact(ca, s) == hipSuccess ? SA_OK : SA_E_HIP;
 }
 
+// ----------------------------------------------------------------------------
+// Allocation-free forward: its workspace is a static device array.
+// ----------------------------------------------------------------------------
+// Largest workspace the allocation-free entry point serves (the headline
+// Bit-Axon SWA shape, 32 heads x 16384 x 80, needs 96 MiB).  Every device
+// the library runs on holds one such array until the process ends.
+constexpr size_t kScratchBytes = (size_t)128 << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+// Device address of the current device's copy of `scratch`, looked up once
+// per device with that device current.  In host code the array's name only
+// stands in for the symbol: kernels get this address, never the name.
+int scratch_address(void** addr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SA_E_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SA_E_HIP;
+        g_scratch_addr[dev] = p;
+    }
+    *addr = g_scratch_addr[dev];
+    return SA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -354,8 +385,26 @@ const char* sparse_attn_strerror(int status) {
         case SA_E_WORKSPACE_TOO_SMALL: return "workspace smaller than sparse_attn_workspace_bytes";
         case SA_E_HIP: return "HIP kernel launch failed";
         case SA_E_UNSUPPORTED: return "configuration outside the supported limits";
+        case SA_E_SCRATCH_LIMIT: return "the configuration needs more workspace than the allocation-free entry point's static scratch (128 MiB)";
         default: return "unknown status";
     }
+}
+
+int sparse_attn_fwd_noalloc(const void* q, const void* k, const void* v,
+                            const sparse_attn_cfg* cfg, void* out, float* lse) {
+    size_t need = 0;
+    int rc = sparse_attn_workspace_bytes(cfg, &need);
+    if (rc != SA_OK) return rc;
+    if (need > kScratchBytes) return SA_E_SCRATCH_LIMIT;
+    sparse_attn_cfg c = *cfg;
+    c.workspace = nullptr;
+    c.workspace_bytes = 0;
+    if (need > 0) {
+        rc = scratch_address(&c.workspace);
+        if (rc != SA_OK) return rc;
+        c.workspace_bytes = kScratchBytes;
+    }
+    return sparse_attn_fwd(q, k, v, &c, out, lse);
 }
 
 int sparse_attn_workspace_bytes(const sparse_attn_cfg* cfg, size_t* bytes) {

@@ -203,7 +203,7 @@ def test_fwd_rejects_before_launch(lib):
 
 
 def test_strerror_covers_codes(lib):
-    for c in range(-8, 1):
+    for c in range(-9, 1):
         assert sa.sparse_attn_strerror(c) != "unknown status"
     assert sa.sparse_attn_strerror(-99) == "unknown status"
 
@@ -251,3 +251,16 @@ def test_fp8_workspace(lib):
     p = sa.Params(1, 4, 2, 1024, 64, dtype=sa.SA_FP8, block_size=64, top_k=2)
     assert sa.load_library().sparse_attn_block_pool(
         ctypes.c_void_p(0x1000), ctypes.byref(p.cfg()), ctypes.c_void_p(0x2000)) == -8
+
+
+def test_noalloc_rejects_before_launch(lib):
+    # Too large for the static scratch: rejected before anything is enqueued.
+    big = sa.Params(1, 32, 8, 131072, 128, block_size=512, top_k=8).cfg()
+    assert sa.sparse_attn_workspace_bytes(big) > 128 << 20
+    rc = lib.sparse_attn_fwd_noalloc(ctypes.c_void_p(0x10000), ctypes.c_void_p(0x20000),
+                                     ctypes.c_void_p(0x30000), ctypes.byref(big),
+                                     ctypes.c_void_p(0x40000), ctypes.c_void_p(0x50000))
+    assert rc == -9
+    # Argument checks as sparse_attn_fwd's.
+    bad = sa.Params(1, 4, 3, 256, 64, window=8).cfg()
+    assert lib.sparse_attn_fwd_noalloc(None, None, None, ctypes.byref(bad), None, None) == -2
