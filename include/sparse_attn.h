@@ -89,9 +89,14 @@ extern "C" {
 
 typedef enum {
     SA_BF16 = 0, /* bfloat16 inputs and out; fp32 accumulation.  Q K^T runs on
-                    bf16 matrix cores; P V on fp16 ones (V converted once into
-                    the workspace, exact for |v| in [2^-14, 65504]; larger |v|
-                    overflows, smaller ones keep fp16 subnormal precision). */
+                    bf16 matrix cores; P V on fp16 ones: V is copied once into
+                    the workspace as fp16(v 2^-s), with one power-of-two
+                    exponent s per (batch, kv head) chosen from its largest
+                    |v| (0 while that lies in [2^-10, 2^15), else the exponent
+                    that brings it into [2^14, 2^15)), and the results are
+                    scaled back by 2^s.  Every finite bf16 V is covered: the
+                    copy is exact wherever |v 2^-s| >= 2^-14 and within
+                    2^-15 of the head's largest |v 2^-s| below that. */
     SA_F32 = 1,  /* float32 inputs and out; each operand split into two
                     bf16 terms on the matrix cores (about 16 mantissa bits) */
     SA_FP8 = 2   /* FP8 inputs (OCP E4M3: bias 7, 3 mantissa bits, max 448, no
@@ -206,7 +211,9 @@ int sparse_attn_block_pool(const void* k, const sparse_attn_cfg* cfg, float* kba
  * forward's fp32 lse; dsink [n_q_heads] fp32 or NULL (needs cfg->sink).
  * Supported: bf16 prefills with a window and/or block gating (any gate
  * variant); a token gate, the compressed branch, fp32 or a decode step
- * return SA_E_UNSUPPORTED.  Workspace from sparse_attn_bwd_workspace_bytes;
+ * return SA_E_UNSUPPORTED.  The gradient products run on fp16 matrix cores
+ * with fp16 copies of q, k and dout and fp16 score gradients dS_ij: their
+ * magnitudes must stay below 65504 (no scaling is applied here).  Workspace from sparse_attn_bwd_workspace_bytes;
  * enqueued on cfg->stream, no host sync, nothing allocated. */
 int sparse_attn_bwd_workspace_bytes(const sparse_attn_cfg* cfg, size_t* bytes);
 int sparse_attn_bwd(const void* q, const void* k, const void* v, const void* out,

@@ -50,7 +50,7 @@ struct Plan {
         o_tok_qn, o_tok_win, o_tok_kpart, o_tok_scr, o_tok_nslow, o_dec_scores, o_dec_list,
         o_dec_nfar, o_dec_plist, o_dec_pcnt, o_dec_redo, o_dec_part, o_qsum, o_cmp_k, o_cmp_v,
         o_cmp_out, o_k16, o_q16, o_do16, o_delta, o_near, o_f8q, o_f8k, o_f8v, o_f8iq, o_f8ik,
-        o_v16, total;
+        o_v16, o_vmax, o_vscale, total;
 };
 
 bool misaligned(const void* p, size_t a) { return p && (reinterpret_cast<uintptr_t>(p) % a) != 0; }
@@ -200,6 +200,9 @@ int make_plan(const sparse_attn_cfg* c, Plan* p, bool bwd = false) {
         P.o_split = take(P.f32 ? 2 * (nq + 2 * nkv) * 2 : 0);
         // fp16 copy of V for the P V products (rows padded with ones at d 80)
         P.o_v16 = take(P.f32 ? 0 : nkv / P.D * sa::v16_row_of(P.D) * 2);
+        // its per-chunk maxima and the per-(batch, kv head) scale exponent
+        P.o_vmax = take(P.f32 ? 0 : (size_t)P.Bt * P.Hkv * sa::f16_chunks(P.N) * 4);
+        P.o_vscale = take(P.f32 ? 0 : (size_t)P.Bt * P.Hkv * 4);
     }
     if (P.gate) {
         P.o_kb3 = take((size_t)P.gate_planes * P.lists * P.D * 2);
@@ -532,6 +535,7 @@ int sparse_attn_fwd(const void* q, const void* k, const void* v, const sparse_at
     const uint16_t* kp[2] = {(const uint16_t*)k, nullptr};
     const uint16_t* vp[2] = {(const uint16_t*)v, nullptr};
     const int split = P.f32 ? 2 : 1;
+    const int32_t* vscale = nullptr;
     if (P.f32) {
         const size_t nq = (size_t)P.Bt * P.Hq * P.N * P.D, nkv = (size_t)P.Bt * P.Hkv * P.N * P.D;
         uint16_t* base = (uint16_t*)(ws + P.o_split);
@@ -545,10 +549,17 @@ int sparse_attn_fwd(const void* q, const void* k, const void* v, const sparse_at
             return SA_E_HIP;
         qp[0] = qh; qp[1] = ql; kp[0] = kh; kp[1] = kl; vp[0] = vh; vp[1] = vl;
     } else {
+        // fp16 copy of V for the P V products, scaled by a power of two per
+        // (batch, kv head) wherever a value would leave the fp16 range.
         uint16_t* v16 = (uint16_t*)(ws + P.o_v16);
+        float* vmax = (float*)(ws + P.o_vmax);
+        int32_t* vsc = (int32_t*)(ws + P.o_vscale);
+        const int heads = P.Bt * P.Hkv, SR = sa::v16_row_of(P.D);
         StageScope t("v_to_f16", s);
-        if (!ok(sa::launch_v_to_f16((const uint16_t*)v, v16, (size_t)P.Bt * P.Hkv * P.N, P.D, s)))
+        if (!ok(sa::launch_f16_copy((const uint16_t*)v, v16, vmax, heads, P.N, P.D, SR, s)) ||
+            !ok(sa::launch_f16_scale((const uint16_t*)v, v16, vmax, vsc, heads, 1, P.N, P.D, SR, s)))
             return SA_E_HIP;
+        vscale = vsc;
         vp[0] = v16;
     }
 
@@ -624,6 +635,7 @@ int sparse_attn_fwd(const void* q, const void* k, const void* v, const sparse_at
     ra.sel = sel; ra.part_o = part_o; ra.part_lse = part_lse; ra.kslots = P.kslots;
     ra.sink = cfg->sink; ra.out_f32 = P.f32 ? 1 : 0;
     ra.tokmask = tokmask;
+    ra.vscale = vscale;
     float* out_r = P.cmp ? (float*)(ws + P.o_cmp_out) : nullptr;
     if (P.cmp) {   // the compressed pass merges into the final out
         ra.out = out_r;
@@ -638,7 +650,7 @@ int sparse_attn_fwd(const void* q, const void* k, const void* v, const sparse_at
         uint16_t* kc = (uint16_t*)(ws + P.o_cmp_k);
         uint16_t* vc = (uint16_t*)(ws + P.o_cmp_v);
         sa::CmpPoolArgs cp{k, v, {kc, P.f32 ? kc + ncmp : nullptr}, {vc, P.f32 ? vc + ncmp : nullptr},
-                           P.Bt * P.Hkv, P.N, P.C, P.Nc, P.D};
+                           P.Bt * P.Hkv, P.N, P.C, P.Nc, P.D, vscale};
         {
             StageScope t("cmp_pool", s);
             if (!ok(sa::launch_cmp_pool(cp, P.f32, s))) return SA_E_HIP;
@@ -648,6 +660,7 @@ int sparse_attn_fwd(const void* q, const void* k, const void* v, const sparse_at
         ca.out_r = out_r; ca.out = out; ca.lse = lse;
         ca.Bt = P.Bt; ca.Hq = P.Hq; ca.Hkv = P.Hkv; ca.N = P.N; ca.C = P.C; ca.Nc = P.Nc;
         ca.scale = P.scale; ca.out_f32 = P.f32 ? 1 : 0;
+        ca.vscale = vscale;
         StageScope t("attn_compressed", s);
         if (!ok(sa::launch_cmp(ca, P.D, split, s))) return SA_E_HIP;
     }

@@ -56,14 +56,16 @@ __device__ __forceinline__ void finish_rows(const RowsArgs& a, f32x16 (&o)[Tile<
     }
     if (a.sink) total += __expf(z - M);
     const float inv = 1.f / total;
+    // V (and the far partials) were taken in units of 2^s.
+    const int vs = a.vscale ? a.vscale[prow / a.N / (a.Hq / a.Hkv)] : 0;
 #pragma unroll
     for (int mb = 0; mb < T::DM; ++mb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int d0 = mb * 32 + 8 * j + 4 * hh;
             if (d0 < D) {
-                const float v0 = o[mb][4 * j] * inv, v1 = o[mb][4 * j + 1] * inv;
-                const float v2 = o[mb][4 * j + 2] * inv, v3 = o[mb][4 * j + 3] * inv;
+                const float v0 = ldexpf(o[mb][4 * j] * inv, vs), v1 = ldexpf(o[mb][4 * j + 1] * inv, vs);
+                const float v2 = ldexpf(o[mb][4 * j + 2] * inv, vs), v3 = ldexpf(o[mb][4 * j + 3] * inv, vs);
                 if (a.out_f32) {
                     *(float4*)((float*)a.out + prow * D + d0) = make_float4(v0, v1, v2, v3);
                 } else {
@@ -323,36 +325,131 @@ __global__ void bf16_to_f16_kernel(const uint4* __restrict__ x, uint4* __restric
     y[i] = make_uint4(r[0], r[1], r[2], r[3]);
 }
 
-// bf16 rows of D -> fp16 rows of SR (> D) whose columns D .. SR-1 hold
-// fp16 one; one thread per 8 output elements.
-__global__ void bf16_to_f16_rows_kernel(const uint16_t* __restrict__ x, uint4* __restrict__ y,
-                                        size_t rows, int D, int SR) {
-    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int cpr = SR / 8;
-    if (i >= rows * cpr) return;
-    const size_t r = i / cpr;
-    const int c = (int)(i % cpr);
-    uint32_t o[4] = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
-    if (c < D / 8) {
-        const uint4 u = *(const uint4*)(x + r * D + c * 8);
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+// Largest |x| of 8 bf16 values (sign bits cleared; NaN-free compares).
+__device__ __forceinline__ float absmax8(const uint4& u, float m) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const _Float16 lo = (_Float16)bf16_to_f32(w[t] & 0xffffu);
-            const _Float16 hi = (_Float16)bf16_to_f32(w[t] >> 16);
-            o[t] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-        }
+    for (int t = 0; t < 4; ++t) {
+        m = fmaxf(m, bf16_to_f32(w[t] & 0x7fffu));
+        m = fmaxf(m, bf16_to_f32((w[t] >> 16) & 0x7fffu));
     }
-    y[i] = make_uint4(o[0], o[1], o[2], o[3]);
+    return m;
 }
 
-hipError_t launch_v_to_f16(const uint16_t* v, uint16_t* y, size_t rows, int D, hipStream_t s) {
-    const int SR = v16_row_of(D);
-    if (SR == D) return launch_bf16_to_f16(v, y, rows * D, s);
-    const size_t n8 = rows * (SR / 8);
-    if (n8 == 0) return hipSuccess;
-    hipLaunchKernelGGL(bf16_to_f16_rows_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, v,
-                       (uint4*)y, rows, D, SR);
+// 8 bf16 values times 2^-e as fp16 (exact for results in the fp16 normal
+// range; ldexp is exact in fp32).
+__device__ __forceinline__ uint4 f16x8_scaled(const uint4& u, int e) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    uint32_t r[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const _Float16 lo = (_Float16)ldexpf(bf16_to_f32(w[t] & 0xffffu), -e);
+        const _Float16 hi = (_Float16)ldexpf(bf16_to_f32(w[t] >> 16), -e);
+        r[t] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+    }
+    return make_uint4(r[0], r[1], r[2], r[3]);
+}
+
+// One workgroup per (chunk of kF16ChunkRows rows, head): the fp16 copy of
+// the chunk (rows of D -> rows of SR, columns D .. SR-1 fp16 one) and the
+// chunk's largest |x|.  Every chunk writes its maximum (no zeroing needed).
+__global__ __launch_bounds__(256) void f16_copy_kernel(const uint16_t* __restrict__ x,
+                                                       uint4* __restrict__ y, float* chunk_max,
+                                                       int rows, int D, int SR) {
+    const int c = blockIdx.x, h = blockIdx.y, nch = gridDim.x;
+    const int r0 = c * kF16ChunkRows, nr = min(kF16ChunkRows, rows - r0);
+    const int cpr = SR / 8, dpr = D / 8;
+    const size_t row0 = (size_t)h * rows + r0;
+    float m = 0.f;
+    const int n = nr * cpr;
+    // Four 16-byte pieces per thread in flight at a time.
+    for (int i0 = threadIdx.x; i0 < n; i0 += 4 * 256) {
+        uint4 u[4];
+        bool data[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int i = i0 + t * 256;
+            const int r = i / cpr, cc = i % cpr;
+            data[t] = i < n && cc < dpr;
+            u[t] = data[t] ? *(const uint4*)(x + (row0 + r) * D + cc * 8) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int i = i0 + t * 256;
+            if (i >= n) break;
+            uint4 o = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
+            if (data[t]) {
+                m = absmax8(u[t], m);
+                o = f16x8_scaled(u[t], 0);
+            }
+            if (y) y[(row0 + i / cpr) * cpr + i % cpr] = o;
+        }
+    }
+    __shared__ float red[4];
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        chunk_max[(size_t)h * nch + c] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// One workgroup per group of hpg heads: the group's largest |x|, its
+// exponent s, and (s != 0 only) the group's copy written again at 2^-s.
+__global__ __launch_bounds__(256) void f16_scale_kernel(const uint16_t* __restrict__ x,
+                                                        uint4* __restrict__ y,
+                                                        const float* __restrict__ chunk_max,
+                                                        int32_t* scale, int hpg, int rows, int D,
+                                                        int SR) {
+    const int grp = blockIdx.x, nch = f16_chunks(rows);
+    const float* cm = chunk_max + (size_t)grp * hpg * nch;
+    float m = 0.f;
+    for (int i = threadIdx.x; i < hpg * nch; i += 256) m = fmaxf(m, cm[i]);
+    __shared__ float red[4];
+    __shared__ int s_sh;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) m = fmaxf(m, __shfl_xor(m, d));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const float mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        int sc = 0;
+        if (mx > 0.f && mx < INFINITY && (mx < 0x1p-10f || mx >= 0x1p15f)) {
+            int e;
+            frexpf(mx, &e);   // mx = f 2^e, f in [0.5, 1): floor(log2 mx) = e - 1
+            sc = e - 1 - 14;
+        }
+        s_sh = sc;
+        scale[grp] = sc;
+    }
+    __syncthreads();
+    const int sc = s_sh;
+    if (sc == 0 || !y) return;
+    const int cpr = SR / 8, dpr = D / 8;
+    const size_t row0 = (size_t)grp * hpg * rows;
+    const size_t n = (size_t)hpg * rows * dpr;
+    for (size_t i = threadIdx.x; i < n; i += 256) {
+        const size_t r = i / dpr;
+        const int cc = (int)(i % dpr);
+        const uint4 u = *(const uint4*)(x + (row0 + r) * D + cc * 8);
+        y[(row0 + r) * cpr + cc] = f16x8_scaled(u, sc);
+    }
+}
+
+hipError_t launch_f16_copy(const uint16_t* x, uint16_t* y, float* chunk_max, int heads, int rows,
+                           int D, int SR, hipStream_t s) {
+    if (heads == 0 || rows == 0) return hipSuccess;
+    hipLaunchKernelGGL(f16_copy_kernel, dim3((unsigned)f16_chunks(rows), (unsigned)heads),
+                       dim3(256), 0, s, x, (uint4*)y, chunk_max, rows, D, SR);
+    return hipGetLastError();
+}
+
+hipError_t launch_f16_scale(const uint16_t* x, uint16_t* y, const float* chunk_max,
+                            int32_t* scale, int groups, int hpg, int rows, int D, int SR,
+                            hipStream_t s) {
+    if (groups == 0 || rows == 0) return hipSuccess;
+    hipLaunchKernelGGL(f16_scale_kernel, dim3((unsigned)groups), dim3(256), 0, s, x, (uint4*)y,
+                       chunk_max, scale, hpg, rows, D, SR);
     return hipGetLastError();
 }
 

@@ -98,6 +98,12 @@ __global__ __launch_bounds__(256) void cmp_pool_kernel(CmpPoolArgs a) {
         *(uint4*)(a.vc[0] + o) = pack_bf16(sv, false);
         *(uint4*)(a.vc[1] + o) = pack_bf16(sv, true);
     } else {                 // bf16 K, fp16 V as in the other kernels' P V
+        // the V copy's power-of-two scale of this (batch, kv head)
+        if (a.vscale) {
+            const int e = a.vscale[bg];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) sv[t] = ldexpf(sv[t], -e);
+        }
         *(uint4*)(a.vc[0] + o) = pack_f16(sv);
     }
 }
@@ -201,6 +207,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_cmp_kernel(CmpArgs a) {
     const float wc = lt > 0.f ? __expf(lse_c - M) : 0.f;
     const float inv = 1.f / (wr + wc);
     const float fc = lt > 0.f ? wc * inv / lt : 0.f, fr = wr * inv;
+    // the compressed values were taken in units of 2^vs
+    const int vs = a.vscale ? a.vscale[prow / a.N / (a.Hq / a.Hkv)] : 0;
 #pragma unroll
     for (int mb = 0; mb < T::DM; ++mb)
 #pragma unroll
@@ -208,8 +216,10 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_cmp_kernel(CmpArgs a) {
             const int d0 = mb * 32 + 8 * j + 4 * hh;
             if (d0 < D) {
                 const float4 r = *(const float4*)(a.out_r + prow * D + d0);
-                const float v0 = fr * r.x + fc * o[mb][4 * j], v1 = fr * r.y + fc * o[mb][4 * j + 1];
-                const float v2 = fr * r.z + fc * o[mb][4 * j + 2], v3 = fr * r.w + fc * o[mb][4 * j + 3];
+                const float v0 = fr * r.x + ldexpf(fc * o[mb][4 * j], vs);
+                const float v1 = fr * r.y + ldexpf(fc * o[mb][4 * j + 1], vs);
+                const float v2 = fr * r.z + ldexpf(fc * o[mb][4 * j + 2], vs);
+                const float v3 = fr * r.w + ldexpf(fc * o[mb][4 * j + 3], vs);
                 if (a.out_f32) {
                     *(float4*)((float*)a.out + prow * D + d0) = make_float4(v0, v1, v2, v3);
                 } else {

@@ -31,6 +31,7 @@ struct RowsArgs {
     const float* sink;      // [Hq] or nullptr
     int out_f32;
     const uint32_t* tokmask;  // token keep mask words (see sa_token.hip), or nullptr
+    const int32_t* vscale;  // [Bt*Hkv] exponent s of the fp16 V copy (v * 2^-s), or nullptr
 };
 
 // KV-centric attention of one far block against a chunk of gathered rows,
@@ -107,6 +108,7 @@ struct CmpPoolArgs {
     uint16_t* kc[2];
     uint16_t* vc[2];
     int lists, N, C, Nc, D;
+    const int32_t* vscale;  // [lists] fp16 V means are stored times 2^-s, or nullptr
 };
 
 // Attention over the compressed columns, merged with the other branches'
@@ -121,6 +123,7 @@ struct CmpArgs {
     int Bt, Hq, Hkv, N, C, Nc;
     float scale;
     int out_f32;
+    const int32_t* vscale;  // [Bt*Hkv] exponent of the compressed V copy, or nullptr
 };
 
 // Backward (bf16): inputs, fp16 copies for the P V-style products, the
@@ -295,9 +298,26 @@ hipError_t launch_bf16_to_f16(const uint16_t* x, uint16_t* y, size_t n, hipStrea
 __host__ __device__ constexpr int v16_row_of(int D) { return D == 80 ? 96 : D; }
 template <int D>
 __host__ __device__ constexpr int v16_row() { return v16_row_of(D); }
-// The fp16 copy of V ([rows, D] bf16) that the forward's attention kernels
-// read: rows of v16_row(D) elements (at d 80: 96, columns 80..95 fp16 one).
-hipError_t launch_v_to_f16(const uint16_t* v, uint16_t* y, size_t rows, int D, hipStream_t s);
+// fp16 copies of bf16 tensors with a power-of-two scale per head group.
+// Rows of D bf16 values, `heads` heads of `rows` rows each; the copy has
+// rows of SR >= D elements whose columns D .. SR-1 hold fp16 one.
+//   launch_f16_copy: y = fp16(x) (no scale) and, per chunk of kF16ChunkRows
+//     rows of a head, the largest |x| into chunk_max
+//     [heads][f16_chunks(rows)] (y may be null: the maxima only);
+//   launch_f16_scale: per group of `hpg` consecutive heads, the largest
+//     |x| m of its chunks and the exponent s (scale[group]): 0 while
+//     2^-10 <= m < 2^15, else s = floor(log2 m) - 14 (so m 2^-s lies in
+//     [2^14, 2^15)); for s != 0 the group's rows of y are written again as
+//     fp16(x 2^-s).  The copy is then exact wherever |x 2^-s| >= 2^-14 and
+//     within 2^-25 <= 2^-15 max|x 2^-s| below: no finite bf16 value
+//     overflows fp16.
+constexpr int kF16ChunkRows = 128;
+__host__ __device__ inline int f16_chunks(int rows) { return (rows + kF16ChunkRows - 1) / kF16ChunkRows; }
+hipError_t launch_f16_copy(const uint16_t* x, uint16_t* y, float* chunk_max, int heads, int rows,
+                           int D, int SR, hipStream_t s);
+hipError_t launch_f16_scale(const uint16_t* x, uint16_t* y, const float* chunk_max,
+                            int32_t* scale, int groups, int hpg, int rows, int D, int SR,
+                            hipStream_t s);
 hipError_t launch_split_f32(const float* x, uint16_t* hi, uint16_t* lo, size_t n, hipStream_t s);
 
 }  // namespace sa

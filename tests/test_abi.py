@@ -35,10 +35,20 @@ def test_exports_every_declared_symbol(lib):
         assert hasattr(lib, n), n
 
 
+def a256(n):
+    return (n + 255) // 256 * 256
+
+
+def v_copy_bytes(heads, N, row):
+    """The fp16 V copy (rows of `row` elements), its per-128-row chunk maxima
+    and the per-head scale exponents, each region 256-byte aligned."""
+    return a256(heads * N * row * 2) + a256(heads * ((N + 127) // 128) * 4) + a256(heads * 4)
+
+
 def test_struct_layout_matches(lib):
     # The library rejects any struct_size other than its own sizeof.
     cfg = sa.Params(1, 4, 4, 256, 64, window=16).cfg()
-    assert sa.sparse_attn_workspace_bytes(cfg) == 4 * 256 * 64 * 2
+    assert sa.sparse_attn_workspace_bytes(cfg) == v_copy_bytes(4, 256, 64)
     cfg.struct_size = ctypes.sizeof(binding.SparseAttnCfg) - 8
     with pytest.raises(sa.SparseAttnError) as e:
         sa.sparse_attn_workspace_bytes(cfg)
@@ -157,9 +167,9 @@ def test_workspace_sizes_scale(lib):
     # [rows, top_k-1, d] fp16 dominate.
     # window only: an fp16 copy of V, rows padded to 96 at d 80 (ones in the
     # padding columns feed the row sums), unpadded at d 64 and 128
-    assert sa.sparse_attn_workspace_bytes(sa.Params(1, 32, 32, 16384, 80, window=4096).cfg()) == 32 * 16384 * 96 * 2
-    assert sa.sparse_attn_workspace_bytes(sa.Params(1, 8, 8, 4096, 128, window=512).cfg()) == 8 * 4096 * 128 * 2
-    assert sa.sparse_attn_workspace_bytes(sa.Params(1, 8, 8, 4096, 64, window=512).cfg()) == 8 * 4096 * 64 * 2
+    assert sa.sparse_attn_workspace_bytes(sa.Params(1, 32, 32, 16384, 80, window=4096).cfg()) == v_copy_bytes(32, 16384, 96)
+    assert sa.sparse_attn_workspace_bytes(sa.Params(1, 8, 8, 4096, 128, window=512).cfg()) == v_copy_bytes(8, 4096, 128)
+    assert sa.sparse_attn_workspace_bytes(sa.Params(1, 8, 8, 4096, 64, window=512).cfg()) == v_copy_bytes(8, 4096, 64)
     p = sa.Params(1, 32, 8, 131072, 128, block_size=512, top_k=8)
     rows = 32 * 131072
     assert sa.sparse_attn_workspace_bytes(p.cfg()) >= rows * 7 * 128 * 2

@@ -564,3 +564,41 @@ def test_binding_rejects_on_device(dev, which, monkeypatch):
                 sa.backward(a.pop("q"), a.pop("k"), a.pop("v"), a.pop("out"), a.pop("lse"),
                             a.pop("dout"))
     torch.cuda.synchronize()
+
+
+# --- value range: bf16 inputs far outside the fp16 range, or tiny ----------
+# out(q, k, c v) = c out(q, k, v): the output bar is applied in units of the
+# largest |v| (max |out - out*| <= 1e-2 max|v|, mean <= 1e-3 max|v|); lse
+# does not depend on v.  q and k scaled: the logits scale (peaked or flat
+# softmax), the bar is as is.
+RANGE_CASES = [
+    ("v_big", dict(window=64), 1.0, 1e5),
+    ("v_tiny", dict(window=64), 1.0, 1e-6),
+    ("v_big_gate", dict(block_size=64, top_k=3, window=70, block_offsets=True), 1.0, 3e5),
+    ("v_tiny_gate_cmp", dict(block_size=64, top_k=3, window=70, block_offsets=True, cmp_block=8),
+     1.0, 2e-6),
+    ("qk_peaked", dict(window=100), 4.0, 1e5),
+    ("qk_tiny", dict(block_size=64, top_k=4, window=16, block_offsets=True), 1e-6, 1.0),
+]
+
+
+@pytest.mark.parametrize("case", range(len(RANGE_CASES)), ids=[c[0] for c in RANGE_CASES])
+@pytest.mark.parametrize("d", [80, 128])
+def test_value_range(dev, case, d):
+    name, kw, qk_scale, v_scale = RANGE_CASES[case]
+    wl = W.Workload("range_" + name, 1, 4, 2, 640, d, "bf16", sink=True, **kw)
+    inp = W.make_inputs(wl, 200 + case)
+    rb = lambda a, c: W._round(a * np.float32(c), "bf16")
+    inp = W.Inputs(wl, rb(inp.q, qk_scale), rb(inp.k, qk_scale), rb(inp.v, v_scale), inp.sink,
+                   inp.idx_q, inp.idx_k)
+    # one row of V with mixed magnitudes: its big entries set the scale
+    inp.v[0, 0, 5, :8] = W._round(np.full(8, 3e4 * v_scale, np.float32), "bf16")
+    log(f"[gpu] range {name} d={d} max|v|={np.abs(inp.v).max():.3e}")
+    out, lse, bsel, tsel = run_device(inp, dev)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    vmax = float(np.abs(inp.v).max())
+    rows = np.arange(wl.batch * wl.n_q_heads * wl.seq_len)
+    unit = W.Inputs(wl, inp.q, inp.k, (inp.v / vmax).astype(np.float32), inp.sink, None, None)
+    rep = check(unit, out / vmax, lse, rows, bsel, tsel)
+    log(f"[gpu] range {name} d={d} (units of max|v|) {rep}")
+    assert rep.ok(), str(rep)
