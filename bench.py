@@ -304,6 +304,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-extra", action="store_true", help="only the headline workload")
     ap.add_argument("--extra-steps", type=int, default=10)
+    ap.add_argument("--workload", default=None,
+                    help="time only this named forward workload (for profiling runs) and "
+                         "print its line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB device copy, the known-traffic kernel "
                          "that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
@@ -324,6 +327,19 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    if args.workload:
+        named = {w.name: (i, w) for i, w in W.WORKLOADS.items()}
+        named.update({v.name: ({4096: 2, 16384: 3}.get(v.seq_len, 4), v) for v in GATE_VARIANTS})
+        if args.workload not in named:
+            print(f"unknown workload {args.workload}; one of {sorted(named)}", file=sys.stderr)
+            sys.exit(2)
+        idx, ewl = named[args.workload]
+        print(f"[bench] workload {ewl.name}: warmup {args.warmup}, steps {args.steps}",
+              file=sys.stderr, flush=True)
+        _, etm, est, _ = time_workload(ewl, idx, dev, args.steps, args.warmup)
+        print(json.dumps({"workload": ewl.name, **etm, "stage_ms": est}))
+        return
 
     wl = W.BITAXON_SWA
     print(f"[bench] headline {wl.name}: warmup {args.warmup}, steps {args.steps}", file=sys.stderr, flush=True)

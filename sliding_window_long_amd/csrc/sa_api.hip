@@ -45,7 +45,7 @@ struct Plan {
     int Nk, dec_cmax;
     float scale;
     // workspace regions (byte offsets)
-    size_t o_split, o_kb3, o_sel, o_count, o_cursor, o_listoff, o_nchunks, o_chunk_list,
+    size_t o_split, o_kb3, o_sel, o_count, o_cursor, o_listoff, o_listch, o_nchunks, o_chunk_list,
         o_chunk_start, o_entries, o_part_o, o_part_lse, o_tok_split, o_tok_state, o_tok_mask,
         o_tok_qn, o_tok_win, o_tok_kpart, o_tok_scr, o_tok_nslow, o_dec_scores, o_dec_list,
         o_dec_nfar, o_dec_plist, o_dec_pcnt, o_dec_redo, o_dec_part, o_qsum, o_cmp_k, o_cmp_v,
@@ -213,6 +213,7 @@ int make_plan(const sparse_attn_cfg* c, Plan* p, bool bwd = false) {
             P.o_count = take((size_t)P.lists * 4);
             P.o_cursor = take((size_t)P.lists * 4);
             P.o_listoff = take((size_t)(P.lists + 1) * 4);
+            P.o_listch = take((size_t)(P.lists + 1) * 4);
             P.o_nchunks = take(4);
             P.o_chunk_list = take((size_t)P.max_chunks * 4);
             P.o_chunk_start = take((size_t)P.max_chunks * 4);
@@ -334,6 +335,7 @@ int compact_far(const Plan& P, const int32_t* sel, char* ws, hipStream_t s, sa::
     ca.count = (int32_t*)(ws + P.o_count);
     ca.cursor = (int32_t*)(ws + P.o_cursor);
     ca.list_off = (int32_t*)(ws + P.o_listoff);
+    ca.list_ch = (int32_t*)(ws + P.o_listch);
     ca.entries = (int32_t*)(ws + P.o_entries);
     ca.chunk_list = (int32_t*)(ws + P.o_chunk_list);
     ca.chunk_start = (int32_t*)(ws + P.o_chunk_start);

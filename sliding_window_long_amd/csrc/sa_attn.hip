@@ -37,22 +37,48 @@ __device__ __forceinline__ void finish_rows(const RowsArgs& a, f32x16 (&o)[Tile<
     for (int mb = 0; mb < T::DM; ++mb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) o[mb][v] *= wn;
-    for (int s_ = 0; s_ < nfar; ++s_) {
-        const float w = __expf(a.part_lse[pbase + s_] - M);
-        total += w;
+    // Far partials two at a time: both slots' loads are issued before either
+    // is accumulated.
+    auto add_part = [&](float w, const uint2 (&raw)[T::DM][4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int mb = 0; mb < T::DM; ++mb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (mb * 32 + 8 * j + 4 * hh < D) {
+                    const _Float16* hv = (const _Float16*)&raw[mb][j];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[mb][4 * j + e] += w * (float)hv[e];
+                }
+            }
+    };
+    auto load_part = [&](int s_, uint2 (&raw)[T::DM][4]) __attribute__((always_inline)) {
         const uint16_t* po = a.part_o + (pbase + s_) * D;
 #pragma unroll
         for (int mb = 0; mb < T::DM; ++mb)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int d0 = mb * 32 + 8 * j + 4 * hh;
-                if (d0 < D) {
-                    const uint2 raw = *(const uint2*)(po + d0);
-                    const _Float16* hv = (const _Float16*)&raw;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) o[mb][4 * j + e] += w * (float)hv[e];
-                }
+                raw[mb][j] = d0 < D ? *(const uint2*)(po + d0) : make_uint2(0, 0);
             }
+    };
+    int s_ = 0;
+    for (; s_ + 1 < nfar; s_ += 2) {
+        uint2 r0[T::DM][4], r1[T::DM][4];
+        const float l0 = a.part_lse[pbase + s_], l1 = a.part_lse[pbase + s_ + 1];
+        load_part(s_, r0);
+        load_part(s_ + 1, r1);
+        const float w0 = __expf(l0 - M), w1 = __expf(l1 - M);
+        total += w0 + w1;
+        add_part(w0, r0);
+        add_part(w1, r1);
+    }
+    if (s_ < nfar) {
+        uint2 r0[T::DM][4];
+        const float l0 = a.part_lse[pbase + s_];
+        load_part(s_, r0);
+        const float w0 = __expf(l0 - M);
+        total += w0;
+        add_part(w0, r0);
     }
     if (a.sink) total += __expf(z - M);
     const float inv = 1.f / total;

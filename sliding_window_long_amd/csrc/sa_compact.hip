@@ -9,8 +9,10 @@
 //
 // count  : per (batch, kv head, block) list, number of (row, head) entries
 //          (LDS histogram per row tile, one global atomic per non-empty bin)
-// scan   : exclusive scan of the counts -> list offsets; cut every list into
-//          chunks of rows_per_chunk entries and write the chunk table
+// scan   : exclusive scan of the counts -> list offsets and each list's first
+//          chunk (lists cut into chunks of rows_per_chunk entries)
+// chunks : the chunk table (list and first entry of every chunk), a thread
+//          per chunk
 // scatter: write every entry (i*G + h_local)*kslots + slot at its list's
 //          running cursor.  Order inside a list depends on atomic order, but
 //          each entry's result depends only on its own row and block, so the
@@ -90,10 +92,7 @@ __global__ __launch_bounds__(1024) void compact_scan_kernel(CompactArgs a, int l
         if (l < lists) {
             a.list_off[l] = off_l;
             a.cursor[l] = off_l;
-            for (int q = 0; q < nch && ch_l + q < a.max_chunks; ++q) {
-                a.chunk_list[ch_l + q] = l;
-                a.chunk_start[ch_l + q] = off_l + q * R;
-            }
+            a.list_ch[l] = ch_l;
         }
         __syncthreads();
         if (tid == 1023) {
@@ -104,8 +103,24 @@ __global__ __launch_bounds__(1024) void compact_scan_kernel(CompactArgs a, int l
     }
     if (tid == 0) {
         a.list_off[lists] = s_carry[0];
+        a.list_ch[lists] = s_carry[1];
         a.n_chunks[0] = min(s_carry[1], a.max_chunks);
     }
+}
+
+// Chunk table: thread per chunk q; its list l (list_ch[l] <= q <
+// list_ch[l + 1], by bisection) and its first entry.
+__global__ __launch_bounds__(256) void compact_chunks_kernel(CompactArgs a, int lists) {
+    const int q = blockIdx.x * 256 + threadIdx.x;
+    if (q >= a.n_chunks[0]) return;
+    int lo = 0, hi = lists;   // list_ch[lo] <= q < list_ch[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (a.list_ch[mid] <= q) lo = mid;
+        else hi = mid;
+    }
+    a.chunk_list[q] = lo;
+    a.chunk_start[q] = a.list_off[lo] + (q - a.list_ch[lo]) * a.rows_per_chunk;
 }
 
 __global__ __launch_bounds__(CT) void compact_scatter_kernel(CompactArgs a) {
@@ -138,6 +153,9 @@ hipError_t launch_compact(const CompactArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(compact_count_kernel, grid, dim3(CT), a.n * sizeof(int32_t), s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(compact_scan_kernel, dim3(1), dim3(1024), 0, s, a, lists);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(compact_chunks_kernel, dim3((unsigned)((a.max_chunks + 255) / 256)), dim3(256),
+                       0, s, a, lists);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(compact_scatter_kernel, grid, dim3(CT), 2 * a.n * sizeof(int32_t), s, a);
     return hipGetLastError();

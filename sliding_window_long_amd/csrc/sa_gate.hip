@@ -316,28 +316,38 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
 #pragma unroll
     for (int t = 0; t < M; ++t) insert_desc<M>(L, P[t]);
 
-    if (!row_ok || hh != 0) return;
+    // Both lanes of a row hold the merged list; each writes half of the row
+    // (16-byte pieces when top_k is a multiple of 4), so a wave's stores
+    // cover its 32 rows' selections contiguously.
+    if (!row_ok) return;
     const int m = max(0, min(a.top_k - 1 - c0, row_blk - c0));
     int ids[M];
 #pragma unroll
     for (int t = 0; t < M; ++t) ids[t] = t < m ? (int)(mask - (L[t] & mask)) : 0x7fffffff;
     sort_asc<M>(ids);
     // Ascending: block 0 when forced, the m kept candidates, the own block.
+    auto val_at = [&](int t) {
+        int val = -1;
+        if (t < c0) {
+            val = 0;
+        } else if (t < c0 + m) {
+#pragma unroll
+            for (int u = 0; u < M; ++u)
+                if (u == t - c0) val = ids[u];
+        } else if (t == c0 + m) {
+            val = row_blk;
+        }
+        return val;
+    };
     for (int r = 0; r < a.rep; ++r) {
         int32_t* out = a.sel + (((size_t)b * a.Hq + h) * a.rep + r) * a.N * a.top_k +
                        (size_t)row * a.top_k;
-        for (int t = 0; t < a.top_k; ++t) {
-            int val = -1;
-            if (t < c0) {
-                val = 0;
-            } else if (t < c0 + m) {
-#pragma unroll
-                for (int u = 0; u < M; ++u)
-                    if (u == t - c0) val = ids[u];
-            } else if (t == c0 + m) {
-                val = row_blk;
-            }
-            out[t] = val;
+        if ((a.top_k & 3) == 0 && ((uintptr_t)a.sel & 15) == 0) {
+            for (int q = hh; q < a.top_k / 4; q += 2)
+                *(int4*)(out + 4 * q) =
+                    make_int4(val_at(4 * q), val_at(4 * q + 1), val_at(4 * q + 2), val_at(4 * q + 3));
+        } else {
+            for (int t = hh; t < a.top_k; t += 2) out[t] = val_at(t);
         }
     }
 }

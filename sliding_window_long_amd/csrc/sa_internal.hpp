@@ -177,6 +177,7 @@ struct CompactArgs {
     int32_t* count;         // [lists] zeroed before the count pass
     int32_t* cursor;        // [lists]
     int32_t* list_off;      // [lists + 1]
+    int32_t* list_ch;       // [lists + 1] first chunk of each list (prefix of chunk counts)
     int32_t* entries;
     int32_t* chunk_list;    // [max_chunks]
     int32_t* chunk_start;   // [max_chunks]
