@@ -125,21 +125,36 @@ def device_inputs(wl, seed, dev):
     return inp, {k: (None if v is None else v.to(dev)) for k, v in t.items()}
 
 
-def timed_calls(fn, steps, warmup):
-    """`warmup` untimed calls, then exactly `steps` calls bracketed by
+def timed_calls(fn, steps, warmup, min_warm_ms=80.0):
+    """`warmup` untimed calls (continued until they have taken at least
+    `min_warm_ms` of wall clock), then exactly `steps` calls bracketed by
     torch.cuda.synchronize() on both sides.  Each call is bracketed by HIP
     events on torch's current stream (the stream the library launches on),
     and the library records an event pair around each of its kernels on the
     same stream (two event records per stage: microseconds against calls of
     tenths of a millisecond and up).  Returns (wall-clock mean ms, median
-    call ms, mean call ms, {stage: median ms})."""
+    call ms, mean call ms, {stage: median ms}).
+
+    The warm-up matters on this chip: after any idle gap the clock controller
+    starts high, pulls the clock down within a few calls and then raises it
+    again over some 30-50 ms of back-to-back work; calls timed inside that
+    transient read up to 30% slow.  Everything the timed loop needs is made
+    before the warm-up so that no idle gap separates the two."""
     import torch
     import sliding_window_long_amd as sa
-    for _ in range(warmup):
-        fn()
-    torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
+    n = warmup
+    if min_warm_ms > 0:
+        torch.cuda.synchronize()
+        tw = time.perf_counter()
+        fn()
+        torch.cuda.synchronize()
+        one = (time.perf_counter() - tw) * 1e3
+        n = max(warmup, int(np.ceil(min_warm_ms / max(one, 1e-3)))) - 1
+    for _ in range(n):
+        fn()
+    torch.cuda.synchronize()
     sa.sparse_attn_set_timing(True)
     t0 = time.perf_counter()
     for a, b in ev:
@@ -299,8 +314,8 @@ def cpu_baseline(inp, budget_s=15.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-extra", action="store_true", help="only the headline workload")
     ap.add_argument("--extra-steps", type=int, default=10)
@@ -362,7 +377,8 @@ def main():
         "ms_per_step": ms,
         "ms_wall_mean": tm["ms_wall_mean"],
         "ms_event_mean": tm["ms_event_mean"],
-        "timing": "value and ms_per_step: median of the per-call HIP event times over the "
+        "timing": "warm-up: max(warmup calls, 80 ms of calls) back to back, so the clock has "
+                  "settled; value and ms_per_step: median of the per-call HIP event times over the "
                   "timed steps; ms_wall_mean: wall clock of the timed steps / steps; "
                   "stage_ms and roofline.kernel_ms: medians of the library's per-stage HIP "
                   "events in the same calls",

@@ -29,7 +29,10 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct Plan {
     int Bt, Hq, Hkv, N, D, G;
     bool f32;
-    bool fp8;               // FP8 inputs, decoded into bf16 copies first
+    bool fp8;               // FP8 inputs, decoded into bf16 copies first (unless qk8)
+    bool qk8;               // FP8 prefill without block gate or compressed branch: the
+                            // attention kernel takes fp8 q, k (K Q^T on the FP8 matrix
+                            // cores) and V goes straight from fp8 to its fp16 copy
     bool gate;
     int B, n, top_k, span, kslots, idx_bits, lists;
     bool gate_mm, gate_shared, gate_first;   // gate variants
@@ -251,10 +254,13 @@ int make_plan(const sparse_attn_cfg* c, Plan* p, bool bwd = false) {
         P.o_tok_scr = take(counts > cands ? counts : cands);
         P.o_tok_nslow = take(4);
     }
+    P.qk8 = P.fp8 && !P.gate && !P.cmp;
     if (P.fp8) {
-        P.o_f8q = take(nq * 2);
-        P.o_f8k = take(nkv * 2);
-        P.o_f8v = take(nkv * 2);
+        if (!P.qk8) {
+            P.o_f8q = take(nq * 2);
+            P.o_f8k = take(nkv * 2);
+            P.o_f8v = take(nkv * 2);
+        }
         if (P.tok) {
             P.o_f8iq = take((size_t)P.Bt * P.N * 64 * 2);
             P.o_f8ik = take((size_t)P.Bt * P.N * 64 * 2);
@@ -482,19 +488,28 @@ int sparse_attn_fwd(const void* q, const void* k, const void* v, const sparse_at
     char* ws = (char*)cfg->workspace;
     auto ok = [](hipError_t e) { return e == hipSuccess; };
 
-    // FP8 inputs: decode into bf16 copies, then run as bf16.
+    // FP8 inputs: decode into bf16 copies, then run as bf16 -- except that
+    // an FP8 prefill without block gate or compressed branch keeps q, k, v in
+    // fp8 (the attention kernel's K Q^T on the FP8 matrix cores, V straight
+    // to its fp16 copy); the indexer tensors are decoded in both cases.
     sparse_attn_cfg c8;
+    const void* q_fp8 = P.qk8 ? q : nullptr;
+    const void* k_fp8 = P.qk8 ? k : nullptr;
     if (P.fp8) {
         const size_t nkv = (size_t)P.Bt * P.Hkv * P.Nk * P.D;
-        uint16_t* q8 = (uint16_t*)(ws + P.o_f8q);
-        uint16_t* k8 = (uint16_t*)(ws + P.o_f8k);
-        uint16_t* v8 = (uint16_t*)(ws + P.o_f8v);
-        StageScope t("fp8_to_bf16", s);
-        if (!ok(sa::launch_fp8_to_bf16(q, q8, (size_t)P.Bt * P.Hq * P.N * P.D, s)) ||
-            !ok(sa::launch_fp8_to_bf16(k, k8, nkv, s)) || !ok(sa::launch_fp8_to_bf16(v, v8, nkv, s)))
-            return SA_E_HIP;
+        if (!P.qk8) {
+            StageScope t("fp8_to_bf16", s);
+            uint16_t* q8 = (uint16_t*)(ws + P.o_f8q);
+            uint16_t* k8 = (uint16_t*)(ws + P.o_f8k);
+            uint16_t* v8 = (uint16_t*)(ws + P.o_f8v);
+            if (!ok(sa::launch_fp8_to_bf16(q, q8, (size_t)P.Bt * P.Hq * P.N * P.D, s)) ||
+                !ok(sa::launch_fp8_to_bf16(k, k8, nkv, s)) || !ok(sa::launch_fp8_to_bf16(v, v8, nkv, s)))
+                return SA_E_HIP;
+            q = q8; k = k8; v = v8;
+        }
         c8 = *cfg;
         if (P.tok) {
+            StageScope t("fp8_to_bf16_indexer", s);
             uint16_t* iq8 = (uint16_t*)(ws + P.o_f8iq);
             uint16_t* ik8 = (uint16_t*)(ws + P.o_f8ik);
             if (!ok(sa::launch_fp8_to_bf16(cfg->idx_q, iq8, (size_t)P.Bt * P.N * 64, s)) ||
@@ -504,7 +519,6 @@ int sparse_attn_fwd(const void* q, const void* k, const void* v, const sparse_at
             c8.idx_k = ik8;
         }
         cfg = &c8;
-        q = q8; k = k8; v = v8;
     }
 
     if (P.dec) {
@@ -558,8 +572,8 @@ int sparse_attn_fwd(const void* q, const void* k, const void* v, const sparse_at
         int32_t* vsc = (int32_t*)(ws + P.o_vscale);
         const int heads = P.Bt * P.Hkv, SR = sa::v16_row_of(P.D);
         StageScope t("v_to_f16", s);
-        if (!ok(sa::launch_f16_copy((const uint16_t*)v, v16, vmax, heads, P.N, P.D, SR, s)) ||
-            !ok(sa::launch_f16_scale((const uint16_t*)v, v16, vmax, vsc, heads, 1, P.N, P.D, SR, s)))
+        if (!ok(sa::launch_f16_copy(v, P.qk8, v16, vmax, heads, P.N, P.D, SR, s)) ||
+            !ok(sa::launch_f16_scale(v, P.qk8, v16, vmax, vsc, heads, 1, P.N, P.D, SR, s)))
             return SA_E_HIP;
         vscale = vsc;
         vp[0] = v16;
@@ -638,6 +652,8 @@ int sparse_attn_fwd(const void* q, const void* k, const void* v, const sparse_at
     ra.sink = cfg->sink; ra.out_f32 = P.f32 ? 1 : 0;
     ra.tokmask = tokmask;
     ra.vscale = vscale;
+    ra.q8 = (const uint8_t*)q_fp8;
+    ra.k8 = (const uint8_t*)k_fp8;
     float* out_r = P.cmp ? (float*)(ws + P.o_cmp_out) : nullptr;
     if (P.cmp) {   // the compressed pass merges into the final out
         ra.out = out_r;

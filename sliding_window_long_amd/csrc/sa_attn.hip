@@ -129,13 +129,19 @@ __device__ __forceinline__ void finish_rows(const RowsArgs& a, f32x16 (&o)[Tile<
 // copy hold ones; the fp32 path selects them), so the matrix cores produce
 // the softmax row sums (of the same fp16 P that weights V) and no vector ops
 // are spent on them.
-template <int D, int SPLIT, bool TOK>
+// FP8 (QK8): q and k arrive as OCP E4M3 and S^T = K Q^T runs on the FP8
+// matrix cores (v_mfma_scale_f32_32x32x64_f8f6f4 at twice the bf16 rate,
+// unit scales; the 16 dims past a multiple of 64 on the 32x32x16 FP8 op);
+// every E4M3 product is exact in the fp32 accumulator, as the bf16 products
+// of the decoded values would be.  K tiles hold fp8 rows of K8S<D>() bytes.
+template <int D, int SPLIT, bool TOK, bool QK8>
 __global__ __launch_bounds__(NTHREADS, D <= 80 && SPLIT == 1 ? 3 : 2) void attn_rows_kernel(RowsArgs a) {
     using T = Tile<D>;
     constexpr bool ONES = T::DPAD > D;
     constexpr int VS = dma_vs<D>();
     constexpr int VELEMS = KT * VS;
-    __shared__ __align__(16) uint16_t lds_k0[SPLIT * T::KELEMS], lds_k1[SPLIT * T::KELEMS];
+    constexpr int KE = QK8 ? KT * K8S<D>() / 2 : SPLIT * T::KELEMS;   // K buffer, 16-bit units
+    __shared__ __align__(16) uint16_t lds_k0[KE], lds_k1[KE];
     __shared__ __align__(16) uint16_t lds_v0[SPLIT * VELEMS], lds_v1[SPLIT * VELEMS];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -156,7 +162,7 @@ __global__ __launch_bounds__(NTHREADS, D <= 80 && SPLIT == 1 ? 3 : 2) void attn_
     uint64_t kb[SPLIT], vb[SPLIT];   // workgroup-uniform byte addresses
 #pragma unroll
     for (int p = 0; p < SPLIT; ++p) {
-        kb[p] = uniform_u64((uint64_t)(a.k[p] + kvoff));
+        kb[p] = uniform_u64(QK8 ? (uint64_t)(a.k8 + kvoff) : (uint64_t)(a.k[p] + kvoff));
         vb[p] = uniform_u64((uint64_t)(a.v[p] + voff_src));
     }
 
@@ -165,8 +171,10 @@ __global__ __launch_bounds__(NTHREADS, D <= 80 && SPLIT == 1 ? 3 : 2) void attn_
     const int row = q0 + col;
     const bool row_ok = row < N;
     const size_t prow = (size_t)bh * N + row;   // flat row id
-    bf16x8 qf[SPLIT][T::DK];
-    load_q<D, SPLIT>(qf, a.q, prow * D, row_ok, hh);
+    bf16x8 qf[SPLIT][QK8 ? 1 : T::DK];
+    Q8Frag<D> q8f;
+    if constexpr (QK8) q8f.load(a.q8 + prow * D, row_ok, hh);
+    else load_q<D, SPLIT>(qf, a.q, prow * D, row_ok, hh);
 
     // Block-gate state of the row: its block, the kept near blocks as a bit
     // mask over (own block - 1 - bit), and the count of far blocks.
@@ -210,11 +218,12 @@ __global__ __launch_bounds__(NTHREADS, D <= 80 && SPLIT == 1 ? 3 : 2) void attn_
 #pragma unroll
     for (int mb = 0; mb < T::DM; ++mb) voff[mb] = v_lane_offset<D, VS, ONES>(lane, mb);
     const bool pad = ONES && ((lane >> 4) & 1);   // lanes of the padding dims in the last row block
-    TileDma<D, T::KS> kd;
+    // fp8 K rows are D bytes: 16-bit units of D / 2 in the DMA's bookkeeping
+    TileDma<D, QK8 ? K8S<D>() / 2 : T::KS, QK8 ? D / 2 : D> kd;
     TileDma<D, VS, VSRC> vd;
     kd.init(wu, lane);
     vd.init(wu, lane);
-    auto load_k = [&](int t, uint16_t* dst) { dma_tile<D, SPLIT, T::KELEMS>(kd, kb, N, t * KT, dst, wu); };
+    auto load_k = [&](int t, uint16_t* dst) { dma_tile<D, SPLIT, KE / SPLIT>(kd, kb, N, t * KT, dst, wu); };
     auto load_v = [&](int t, uint16_t* dst) { dma_tile<D, SPLIT, VELEMS>(vd, vb, N, t * KT, dst, wu); };
 
     // Mask of key tile t: keys the row does not attend become -inf (a tile
@@ -265,7 +274,8 @@ __global__ __launch_bounds__(NTHREADS, D <= 80 && SPLIT == 1 ? 3 : 2) void attn_
     __syncthreads();
     load_k(min(t_begin + 1, t_end), lds_k1);
     f32x16 s0[2];
-    qk_tile<D, SPLIT>(lds_k0, qf, s0, lane);
+    if constexpr (QK8) qk_tile8<D>(lds_k0, q8f, s0, lane);
+    else qk_tile<D, SPLIT>(lds_k0, qf, s0, lane);
     mask_t(s0, t_begin, tw0);
     max_tile(s0, rs, c);
     exp_tile<SPLIT, !ONES>(s0, rs, c, pb, pl);
@@ -286,7 +296,8 @@ __global__ __launch_bounds__(NTHREADS, D <= 80 && SPLIT == 1 ? 3 : 2) void attn_
         load_k(min(t + 2, t_end), k_free);
         load_v(t + 1, v_free);
         apply_rescale<D>(o, rs);
-        qk_tile<D, SPLIT>(k_next, qf, sn, lane);
+        if constexpr (QK8) qk_tile8<D>(k_next, q8f, sn, lane);
+        else qk_tile<D, SPLIT>(k_next, qf, sn, lane);
         mask_t(sn, t + 1, tw);
         pv_tile<D, SPLIT, VS, ONES_SEL>(v_cur, pb, pl, o, voff, pad);
         max_tile(sn, rs, c);
@@ -376,10 +387,47 @@ __device__ __forceinline__ uint4 f16x8_scaled(const uint4& u, int e) {
     return make_uint4(r[0], r[1], r[2], r[3]);
 }
 
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// 8 consecutive source values of row r as fp16 times 2^-e (exact for results
+// in the fp16 normal range), and the running largest |source value| in m
+// (for FP8 sources only when e = 0).
+// bf16 source: widened to fp32 and scaled exactly with ldexp.  FP8 (OCP
+// E4M3) source: the gfx950 conversion to fp16 with scale 2^-e (exact for
+// every E4M3 code at e = 0: checked against the format's definition for all
+// 256 codes).
+template <bool FP8>
+__device__ __forceinline__ uint4 f16x8_from(const void* x, size_t r, int D, int cc, int e,
+                                            float& m) {
+    if constexpr (FP8) {
+        const uint2 b = *(const uint2*)((const unsigned char*)x + r * D + cc * 8);
+        const float sc = ldexpf(1.f, -e);
+        const f16x2 h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)b.x, sc, false);
+        const f16x2 h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)b.x, sc, true);
+        const f16x2 h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)b.y, sc, false);
+        const f16x2 h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)b.y, sc, true);
+        const uint4 u = make_uint4(__builtin_bit_cast(uint32_t, h0), __builtin_bit_cast(uint32_t, h1),
+                                   __builtin_bit_cast(uint32_t, h2), __builtin_bit_cast(uint32_t, h3));
+        // Largest |x| from the converted values (exact at e = 0; every
+        // caller that needs it converts unscaled).
+        const f16x2 hs[4] = {h0, h1, h2, h3};
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            m = fmaxf(m, fmaxf(fabsf((float)hs[t][0]), fabsf((float)hs[t][1])));
+        return u;
+    } else {
+        const uint4 u = *(const uint4*)((const uint16_t*)x + r * D + cc * 8);
+        m = absmax8(u, m);
+        return f16x8_scaled(u, e);
+    }
+}
+
 // One workgroup per (chunk of kF16ChunkRows rows, head): the fp16 copy of
 // the chunk (rows of D -> rows of SR, columns D .. SR-1 fp16 one) and the
 // chunk's largest |x|.  Every chunk writes its maximum (no zeroing needed).
-__global__ __launch_bounds__(256) void f16_copy_kernel(const uint16_t* __restrict__ x,
+// FP8: the source is OCP E4M3, decoded exactly.
+template <bool FP8>
+__global__ __launch_bounds__(256) void f16_copy_kernel(const void* __restrict__ x,
                                                        uint4* __restrict__ y, float* chunk_max,
                                                        int rows, int D, int SR) {
     const int c = blockIdx.x, h = blockIdx.y, nch = gridDim.x;
@@ -388,27 +436,21 @@ __global__ __launch_bounds__(256) void f16_copy_kernel(const uint16_t* __restric
     const size_t row0 = (size_t)h * rows + r0;
     float m = 0.f;
     const int n = nr * cpr;
-    // Four 16-byte pieces per thread in flight at a time.
+    // Four 16-byte output pieces per thread in flight at a time.
     for (int i0 = threadIdx.x; i0 < n; i0 += 4 * 256) {
-        uint4 u[4];
-        bool data[4];
+        uint4 o[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int i = i0 + t * 256;
             const int r = i / cpr, cc = i % cpr;
-            data[t] = i < n && cc < dpr;
-            u[t] = data[t] ? *(const uint4*)(x + (row0 + r) * D + cc * 8) : make_uint4(0, 0, 0, 0);
+            o[t] = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
+            if (i < n && cc < dpr) o[t] = f16x8_from<FP8>(x, row0 + r, D, cc, 0, m);
         }
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int i = i0 + t * 256;
             if (i >= n) break;
-            uint4 o = make_uint4(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
-            if (data[t]) {
-                m = absmax8(u[t], m);
-                o = f16x8_scaled(u[t], 0);
-            }
-            if (y) y[(row0 + i / cpr) * cpr + i % cpr] = o;
+            if (y) y[(row0 + i / cpr) * cpr + i % cpr] = o[t];
         }
     }
     __shared__ float red[4];
@@ -422,7 +464,8 @@ __global__ __launch_bounds__(256) void f16_copy_kernel(const uint16_t* __restric
 
 // One workgroup per group of hpg heads: the group's largest |x|, its
 // exponent s, and (s != 0 only) the group's copy written again at 2^-s.
-__global__ __launch_bounds__(256) void f16_scale_kernel(const uint16_t* __restrict__ x,
+template <bool FP8>
+__global__ __launch_bounds__(256) void f16_scale_kernel(const void* __restrict__ x,
                                                         uint4* __restrict__ y,
                                                         const float* __restrict__ chunk_max,
                                                         int32_t* scale, int hpg, int rows, int D,
@@ -457,25 +500,34 @@ __global__ __launch_bounds__(256) void f16_scale_kernel(const uint16_t* __restri
     for (size_t i = threadIdx.x; i < n; i += 256) {
         const size_t r = i / dpr;
         const int cc = (int)(i % dpr);
-        const uint4 u = *(const uint4*)(x + (row0 + r) * D + cc * 8);
-        y[(row0 + r) * cpr + cc] = f16x8_scaled(u, sc);
+        float unused = 0.f;
+        y[(row0 + r) * cpr + cc] = f16x8_from<FP8>(x, row0 + r, D, cc, sc, unused);
     }
 }
 
-hipError_t launch_f16_copy(const uint16_t* x, uint16_t* y, float* chunk_max, int heads, int rows,
-                           int D, int SR, hipStream_t s) {
+hipError_t launch_f16_copy(const void* x, bool fp8, uint16_t* y, float* chunk_max, int heads,
+                           int rows, int D, int SR, hipStream_t s) {
     if (heads == 0 || rows == 0) return hipSuccess;
-    hipLaunchKernelGGL(f16_copy_kernel, dim3((unsigned)f16_chunks(rows), (unsigned)heads),
-                       dim3(256), 0, s, x, (uint4*)y, chunk_max, rows, D, SR);
+    const dim3 grid((unsigned)f16_chunks(rows), (unsigned)heads);
+    if (fp8)
+        hipLaunchKernelGGL(f16_copy_kernel<true>, grid, dim3(256), 0, s, x, (uint4*)y, chunk_max,
+                           rows, D, SR);
+    else
+        hipLaunchKernelGGL(f16_copy_kernel<false>, grid, dim3(256), 0, s, x, (uint4*)y, chunk_max,
+                           rows, D, SR);
     return hipGetLastError();
 }
 
-hipError_t launch_f16_scale(const uint16_t* x, uint16_t* y, const float* chunk_max,
+hipError_t launch_f16_scale(const void* x, bool fp8, uint16_t* y, const float* chunk_max,
                             int32_t* scale, int groups, int hpg, int rows, int D, int SR,
                             hipStream_t s) {
     if (groups == 0 || rows == 0) return hipSuccess;
-    hipLaunchKernelGGL(f16_scale_kernel, dim3((unsigned)groups), dim3(256), 0, s, x, (uint4*)y,
-                       chunk_max, scale, hpg, rows, D, SR);
+    if (fp8)
+        hipLaunchKernelGGL(f16_scale_kernel<true>, dim3((unsigned)groups), dim3(256), 0, s, x,
+                           (uint4*)y, chunk_max, scale, hpg, rows, D, SR);
+    else
+        hipLaunchKernelGGL(f16_scale_kernel<false>, dim3((unsigned)groups), dim3(256), 0, s, x,
+                           (uint4*)y, chunk_max, scale, hpg, rows, D, SR);
     return hipGetLastError();
 }
 
@@ -506,10 +558,19 @@ static hipError_t rows_d(const RowsArgs& a, hipStream_t s) {
     // on every shape (d = 80 window: 1.20 vs 0.94 ms).
     const int ntiles = (a.N + RT - 1) / RT;
     const unsigned grid = (unsigned)(ntiles * a.Bt * a.Hq);
+    if constexpr (SPLIT == 1) {
+        if (a.q8) {
+            if (a.tokmask)
+                hipLaunchKernelGGL((attn_rows_kernel<D, 1, true, true>), dim3(grid), dim3(NTHREADS), 0, s, a);
+            else
+                hipLaunchKernelGGL((attn_rows_kernel<D, 1, false, true>), dim3(grid), dim3(NTHREADS), 0, s, a);
+            return hipGetLastError();
+        }
+    }
     if (a.tokmask)
-        hipLaunchKernelGGL((attn_rows_kernel<D, SPLIT, true>), dim3(grid), dim3(NTHREADS), 0, s, a);
+        hipLaunchKernelGGL((attn_rows_kernel<D, SPLIT, true, false>), dim3(grid), dim3(NTHREADS), 0, s, a);
     else
-        hipLaunchKernelGGL((attn_rows_kernel<D, SPLIT, false>), dim3(grid), dim3(NTHREADS), 0, s, a);
+        hipLaunchKernelGGL((attn_rows_kernel<D, SPLIT, false, false>), dim3(grid), dim3(NTHREADS), 0, s, a);
     return hipGetLastError();
 }
 

@@ -467,6 +467,73 @@ __host__ __device__ constexpr int dma_vs() {
     return D == 80 ? 96 : D == 128 ? 160 : Tile<D>::VS;
 }
 
+// ---------------------------------------------------------------------------
+// FP8 (OCP E4M3) K Q^T.
+// ---------------------------------------------------------------------------
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// Row stride (bytes) of an fp8 K tile in LDS: 32 lanes read 16 bytes at
+// keys 32 apart; a stride of 20 dwords (80 bytes) or 36 (144) puts those
+// reads on distinct banks (128-byte rows would not).
+template <int D>
+__host__ __device__ constexpr int K8S() { return D == 128 ? 144 : 80; }
+
+// One query row's fp8 fragments as the B operand of S^T = K Q^T: per 64 dims
+// the 32 bytes 32*(lane/32) .. +31 (32x32x64 op), and for D = 80 the 8 bytes
+// of dims 64 + 8*(lane/32) .. +7 (32x32x16 op).  Lane l supplies column l % 32.
+template <int D>
+struct Q8Frag {
+    static constexpr int NB = D / 64;          // 32x32x64 steps
+    static constexpr bool TAIL = D % 64 == 16; // one 32x32x16 step
+    i32x8 b[NB > 0 ? NB : 1];
+    long t;
+    __device__ __forceinline__ void load(const uint8_t* row, bool ok, int hh) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            uint4 lo = make_uint4(0, 0, 0, 0), hi = lo;
+            if (ok) {
+                lo = *(const uint4*)(row + 64 * j + 32 * hh);
+                hi = *(const uint4*)(row + 64 * j + 32 * hh + 16);
+            }
+            b[j] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z,
+                         (int)hi.w};
+        }
+        t = 0;
+        if constexpr (TAIL) {
+            if (ok) t = *(const long*)(row + 64 * NB + 8 * hh);
+        }
+    }
+};
+
+// S^T tile (64 keys x 32 queries) of one wave from an fp8 K tile.
+template <int D>
+__device__ __forceinline__ void qk_tile8(const uint16_t* ks, const Q8Frag<D>& qf, f32x16 (&s)[2],
+                                         int lane) {
+    constexpr int S8 = K8S<D>();
+    const int col = lane & 31, hh = lane >> 5;
+    const uint8_t* kb = (const uint8_t*)ks;
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+#pragma unroll
+    for (int j = 0; j < Q8Frag<D>::NB; ++j)
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+            const uint8_t* p = kb + (sub * 32 + col) * S8 + 64 * j + 32 * hh;
+            const uint4 lo = *(const uint4*)p, hi = *(const uint4*)(p + 16);
+            const i32x8 av = {(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                              (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+            s[sub] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, qf.b[j], s[sub], 0, 0, 0, 127,
+                                                                     0, 127);
+        }
+    if constexpr (Q8Frag<D>::TAIL) {
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+            const long av = *(const long*)(kb + (sub * 32 + col) * S8 + 64 * Q8Frag<D>::NB + 8 * hh);
+            s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_fp8_fp8(av, qf.t, s[sub], 0, 0, 0);
+        }
+    }
+}
+
 template <int V>
 struct Par {
     static constexpr int value = V;

@@ -62,4 +62,18 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
 
+// OCP E4M3 (bias 7, 3 mantissa bits, no infinities, S.1111.111 = NaN) ->
+// bf16 bits, exactly: normal values 2^-6 .. 448 and subnormals m * 2^-9 are
+// all bf16 values.
+__device__ __forceinline__ uint32_t e4m3_to_bf16(uint32_t b) {
+    const uint32_t s = (b & 0x80u) << 8;
+    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+    if (e == 15u && m == 7u) return s | 0x7fc0u;                 // NaN
+    if (e != 0u) return s | ((e + 120u) << 7) | (m << 4);         // 2^(e-7) (1 + m/8)
+    if (m == 0u) return s;                                        // signed zero
+    // subnormal m * 2^-9: leading bit p of m, value 2^(p-9) (1 + rest / 2^p)
+    const uint32_t p = m >= 4u ? 2u : (m >= 2u ? 1u : 0u);
+    return s | ((p + 118u) << 7) | (((m - (1u << p)) << (7u - p)) & 0x7fu);
+}
+
 }  // namespace sa

@@ -32,6 +32,8 @@ struct RowsArgs {
     int out_f32;
     const uint32_t* tokmask;  // token keep mask words (see sa_token.hip), or nullptr
     const int32_t* vscale;  // [Bt*Hkv] exponent s of the fp16 V copy (v * 2^-s), or nullptr
+    const uint8_t* q8;      // FP8 (E4M3) q and k for K Q^T on the FP8 matrix cores, or
+    const uint8_t* k8;      // nullptr (then q[0], k[0] are the bf16 planes)
 };
 
 // KV-centric attention of one far block against a chunk of gathered rows,
@@ -314,9 +316,10 @@ __host__ __device__ constexpr int v16_row() { return v16_row_of(D); }
 //     overflows fp16.
 constexpr int kF16ChunkRows = 128;
 __host__ __device__ inline int f16_chunks(int rows) { return (rows + kF16ChunkRows - 1) / kF16ChunkRows; }
-hipError_t launch_f16_copy(const uint16_t* x, uint16_t* y, float* chunk_max, int heads, int rows,
-                           int D, int SR, hipStream_t s);
-hipError_t launch_f16_scale(const uint16_t* x, uint16_t* y, const float* chunk_max,
+// (fp8: the source holds OCP E4M3 values, decoded exactly.)
+hipError_t launch_f16_copy(const void* x, bool fp8, uint16_t* y, float* chunk_max, int heads,
+                           int rows, int D, int SR, hipStream_t s);
+hipError_t launch_f16_scale(const void* x, bool fp8, uint16_t* y, const float* chunk_max,
                             int32_t* scale, int groups, int hpg, int rows, int D, int SR,
                             hipStream_t s);
 hipError_t launch_split_f32(const float* x, uint16_t* hi, uint16_t* lo, size_t n, hipStream_t s);

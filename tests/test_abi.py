@@ -252,9 +252,13 @@ def test_backward_rejects_before_launch(lib):
 
 
 def test_fp8_workspace(lib):
-    # bf16 copies of q, k, v (and of the indexer tensors)
-    ws = lambda dt: sa.sparse_attn_workspace_bytes(sa.Params(1, 4, 2, 1024, 64, dtype=dt, window=16).cfg())
-    assert ws(sa.SA_FP8) - ws(sa.SA_BF16) == (4 + 2 + 2) * 1024 * 64 * 2
+    # A window-only FP8 prefill keeps q, k, v in fp8 (the attention kernel's
+    # K Q^T on the FP8 matrix cores, V straight to its fp16 copy): the same
+    # workspace as bf16.  With block gating, bf16 copies of q, k, v.
+    ws = lambda dt, **kw: sa.sparse_attn_workspace_bytes(sa.Params(1, 4, 2, 1024, 64, dtype=dt, **kw).cfg())
+    assert ws(sa.SA_FP8, window=16) == ws(sa.SA_BF16, window=16)
+    g = dict(window=16, block_size=64, top_k=3)
+    assert ws(sa.SA_FP8, **g) - ws(sa.SA_BF16, **g) == (4 + 2 + 2) * 1024 * 64 * 2
     p = sa.Params(1, 4, 2, 1024, 64, dtype=sa.SA_FP8, window=16)
     assert sa.load_library().sparse_attn_bwd_workspace_bytes(
         ctypes.byref(p.cfg()), ctypes.byref(ctypes.c_size_t())) == -8     # no fp8 backward

@@ -289,6 +289,15 @@ def test_fp8_inputs(dev, kw):
     run_and_check(inp, dev, label=f"fp8 {kw}")
 
 
+@pytest.mark.parametrize("d", [64, 80, 128])
+@pytest.mark.parametrize("N,window", [(300, 17), (1000, 256)])
+def test_fp8_window_qk8(dev, d, N, window):
+    # FP8 prefill without block gating: K Q^T on the FP8 matrix cores from
+    # the E4M3 inputs, V straight from E4M3 to its fp16 copy.
+    wl = W.Workload("fp8_win", 2, 4, 2, N, d, "fp8", window=window, sink=True)
+    run_and_check(W.make_inputs(wl, 93 + d + N), dev, label=f"fp8_qk8 d={d} N={N}")
+
+
 def test_fp8_decode(dev):
     wl = W.Workload("fp8_dec", 2, 4, 2, 3000, 128, "fp8", window=64, token_top_k=200,
                     index_dim=64, sink=True)
