@@ -125,7 +125,12 @@ def device_inputs(wl, seed, dev):
     return inp, {k: (None if v is None else v.to(dev)) for k, v in t.items()}
 
 
-def timed_calls(fn, steps, warmup, min_warm_ms=80.0):
+# Least wall clock of back-to-back warm-up calls before a timed loop
+# (--warm-ms; 0 under a counter profiler, where the clock is not measured).
+WARM_MS = 80.0
+
+
+def timed_calls(fn, steps, warmup, min_warm_ms=None):
     """`warmup` untimed calls (continued until they have taken at least
     `min_warm_ms` of wall clock), then exactly `steps` calls bracketed by
     torch.cuda.synchronize() on both sides.  Each call is bracketed by HIP
@@ -145,6 +150,8 @@ def timed_calls(fn, steps, warmup, min_warm_ms=80.0):
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
     n = warmup
+    if min_warm_ms is None:
+        min_warm_ms = WARM_MS
     if min_warm_ms > 0:
         torch.cuda.synchronize()
         tw = time.perf_counter()
@@ -322,10 +329,14 @@ def main():
     ap.add_argument("--workload", default=None,
                     help="time only this named forward workload (for profiling runs) and "
                          "print its line")
+    ap.add_argument("--warm-ms", type=float, default=80.0,
+                    help="least wall clock of back-to-back warm-up calls before each timed loop")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 1 GiB device copy, the known-traffic kernel "
                          "that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
     args = ap.parse_args()
+    global WARM_MS
+    WARM_MS = args.warm_ms
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)

@@ -161,6 +161,10 @@ __device__ __forceinline__ void sort_asc(int (&x)[M]) {
 // the 16-byte reads of 32 consecutive rows hit distinct banks); every wave
 // of the workgroup reads them from there as the A operand of
 // S^T = Kbar Q^T.
+// The staging registers are a native vector type: with HIP's uint4 (a struct)
+// the copies become memcpy calls that keep the array in scratch memory.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 template <int D, int NP>
 struct GateTile {
     static constexpr int RS = D + 8;                 // LDS row stride
@@ -225,14 +229,14 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
     const uint16_t* kb = a.kb3 + (size_t)(b * a.Hkv + g) * a.n * D;
 
     // Staging of candidate tile mt: chunk x = (plane, row, 16-byte column).
-    uint4 st[GT::CPT];
+    u32x4 st[GT::CPT];
     auto load = [&](int mt) {
 #pragma unroll
         for (int c = 0; c < GT::CPT; ++c) {
             const int x = min(tid + 256 * c, GT::CHUNKS - 1);
             const int pl = x / (32 * D / 8), r = (x / (D / 8)) % 32, cc = x % (D / 8);
             const int cblk = min(mt * 32 + r, a.n - 1);
-            st[c] = *(const uint4*)(kb + pl * a.plane + (size_t)cblk * D + cc * 8);
+            st[c] = *(const u32x4*)(kb + pl * a.plane + (size_t)cblk * D + cc * 8);
         }
     };
     auto store = [&](uint16_t* dst) {
@@ -240,7 +244,7 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
         for (int c = 0; c < GT::CPT; ++c) {
             const int x = min(tid + 256 * c, GT::CHUNKS - 1);
             const int pl = x / (32 * D / 8), r = (x / (D / 8)) % 32, cc = x % (D / 8);
-            *(uint4*)(dst + pl * GT::PLANE + r * GT::RS + cc * 8) = st[c];
+            *(u32x4*)(dst + pl * GT::PLANE + r * GT::RS + cc * 8) = st[c];
         }
     };
 
