@@ -18,6 +18,8 @@
 // ties toward the lower block id (the low idx_bits of the mantissa are
 // replaced by (mask - c), costing 2^-(23-idx_bits) of relative precision),
 // and keeps a sorted top-M list in registers with a max/min insertion chain.
+#include <type_traits>
+
 #include "sa_device.hpp"
 #include "sa_internal.hpp"
 
@@ -122,20 +124,30 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
 // ---------------------------------------------------------------------------
 // Gate: one wave per 32 query rows of one head, 4 waves per workgroup.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t order_key(float s, int cblk, uint32_t mask) {
+// lo = mask - cblk, the block's index field.
+__device__ __forceinline__ uint32_t order_key_lo(float s, uint32_t lo, uint32_t mask) {
     const uint32_t u = __float_as_uint(s);
-    const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-    return (ord & ~mask) | (mask - (uint32_t)cblk);
+    const uint32_t ord = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);   // ~u if negative
+    return (ord & ~mask) | lo;
 }
 
+// Median of three: one v_med3_u32 (written out as min/max, the compiler's
+// combiner runs for a very long time on these kernels).
+__device__ __forceinline__ uint32_t med3u(uint32_t a, uint32_t b, uint32_t c) {
+    uint32_t r;
+    asm("v_med3_u32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
+// Insert x into the descending list L (top M kept).  Slot t of the new list
+// is the median of the old L[t-1], L[t] and x: x itself where it lands, the
+// shifted L[t-1] below that, L[t] above.  Slots are independent (one median
+// each); a key below L[M-1] changes nothing.
 template <int M>
 __device__ __forceinline__ void insert_desc(uint32_t (&L)[M], uint32_t x) {
 #pragma unroll
-    for (int t = 0; t < M; ++t) {
-        const uint32_t hi = max(L[t], x);
-        x = min(L[t], x);
-        L[t] = hi;
-    }
+    for (int t = M - 1; t >= 1; --t) L[t] = med3u(L[t - 1], L[t], x);
+    L[0] = max(L[0], x);
 }
 
 template <int M>
@@ -302,13 +314,25 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
             // Insert the 16 scores of this lane; a score that does not beat
             // the lane's current M-th key cannot enter its list, and a wave
             // in which no lane has such a score skips the insertion.
+            // Every candidate of the tile is valid for every row of the
+            // wave when the tile ends before the wave's first row block and
+            // holds no forced block 0 (wave-uniform).
+            const bool all_ok = mt * 32 + 31 < q0 / a.B && (mt > 0 || !a.first);
+            const uint32_t kbase = mask - (uint32_t)(mt * 32 + 4 * hh);
+            auto insert_tile = [&](auto check) __attribute__((always_inline)) {
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int cblk = mt * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
-                const uint32_t key = cblk < row_blk && cblk >= c0 ? order_key(acc[v], cblk, mask) : 0u;
-                const bool in = key > L[M - 1];
-                if (__any(in)) insert_desc<M>(L, in ? key : 0u);   // inserting 0 changes nothing
-            }
+                for (int v = 0; v < 16; ++v) {
+                    const int vo = 8 * (v >> 2) + (v & 3);
+                    uint32_t key = order_key_lo(acc[v], kbase - (uint32_t)vo, mask);
+                    if constexpr (decltype(check)::value) {
+                        const int cblk = mt * 32 + vo + 4 * hh;
+                        key = cblk < row_blk && cblk >= c0 ? key : 0u;
+                    }
+                    if (__any(key > L[M - 1])) insert_desc<M>(L, key);
+                }
+            };
+            if (all_ok) insert_tile(std::false_type{});
+            else insert_tile(std::true_type{});
         }
         if (mt + 1 < ntc) store(lds[(mt + 1) & 1]);
         __syncthreads();
