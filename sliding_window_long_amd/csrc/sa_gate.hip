@@ -122,8 +122,13 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Gate: one wave per 32 query rows of one head, 4 waves per workgroup.
+// Gate: one wave per 32 query rows of one head; the waves of a workgroup
+// share each staged candidate tile.  Eight waves when q is one bf16 term
+// (at most 128 registers: four waves per SIMD), four otherwise (the split
+// queries need more registers).
 // ---------------------------------------------------------------------------
+__host__ __device__ constexpr int gate_waves(int qsplit) { return qsplit == 1 ? 8 : 4; }
+
 // lo = mask - cblk, the block's index field.
 __device__ __forceinline__ uint32_t order_key_lo(float s, uint32_t lo, uint32_t mask) {
     const uint32_t u = __float_as_uint(s);
@@ -177,12 +182,12 @@ __device__ __forceinline__ void sort_asc(int (&x)[M]) {
 // the copies become memcpy calls that keep the array in scratch memory.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-template <int D, int NP>
+template <int D, int NP, int NT>
 struct GateTile {
     static constexpr int RS = D + 8;                 // LDS row stride
     static constexpr int PLANE = 32 * RS;            // one plane of 32 rows
     static constexpr int CHUNKS = NP * 32 * D / 8;   // 16-byte pieces per tile
-    static constexpr int CPT = (CHUNKS + 255) / 256;
+    static constexpr int CPT = (CHUNKS + NT - 1) / NT;
 };
 
 // Positive and negative parts of eight bf16 values, selected by the signs of
@@ -203,18 +208,19 @@ __device__ __forceinline__ void sign_split(const bf16x8& x, const bf16x8& sgn, b
 // cores.  QSPLIT: bf16 terms of q (1 or 2); 4 = the parts come split
 // already (q+ hi, lo, q- hi, lo: group sums of a shared min/max gate).
 template <int D, int M, int QSPLIT, int NP, bool MM>
-__global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
-    using GT = GateTile<D, NP>;
+__global__ __launch_bounds__(64 * gate_waves(QSPLIT)) void gate_kernel(GateArgs a) {
+    constexpr int kGateThreads = 64 * gate_waves(QSPLIT), kGateRows = 32 * gate_waves(QSPLIT);
+    using GT = GateTile<D, NP, kGateThreads>;
     constexpr int DK = D / 16;
     __shared__ __align__(16) uint16_t lds[2][NP * GT::PLANE];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int col = lane & 31, hh = lane >> 5;
     const int BH = a.Bt * a.Hq;
-    const int ntiles = (a.N + 127) / 128;
+    const int ntiles = (a.N + kGateRows - 1) / kGateRows;
     const int bh = blockIdx.x % BH;
     const int tile = ntiles - 1 - (int)(blockIdx.x / BH);
     const int b = bh / a.Hq, h = bh % a.Hq, g = h / (a.Hq / a.Hkv);
-    const int q0 = tile * 128 + __builtin_amdgcn_readfirstlane(wave) * 32;
+    const int q0 = tile * kGateRows + __builtin_amdgcn_readfirstlane(wave) * 32;
     const int row = q0 + col;
     const bool row_ok = row < a.N;
     const size_t prow = (size_t)bh * a.N + row;
@@ -230,7 +236,7 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
         }
 
     const int row_blk = (row_ok ? row : a.N - 1) / a.B;
-    const int last = min(tile * 128 + 127, a.N - 1);
+    const int last = min(tile * kGateRows + kGateRows - 1, a.N - 1);
     const int ncand_wg = last / a.B;                           // candidates: blocks < own block
     const int ncand_wave = q0 < a.N ? min(q0 + 31, a.N - 1) / a.B : 0;
     const int ntc = (ncand_wg + 31) / 32;
@@ -245,7 +251,7 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
     auto load = [&](int mt) {
 #pragma unroll
         for (int c = 0; c < GT::CPT; ++c) {
-            const int x = min(tid + 256 * c, GT::CHUNKS - 1);
+            const int x = min(tid + kGateThreads * c, GT::CHUNKS - 1);
             const int pl = x / (32 * D / 8), r = (x / (D / 8)) % 32, cc = x % (D / 8);
             const int cblk = min(mt * 32 + r, a.n - 1);
             st[c] = *(const u32x4*)(kb + pl * a.plane + (size_t)cblk * D + cc * 8);
@@ -254,7 +260,7 @@ __global__ __launch_bounds__(256) void gate_kernel(GateArgs a) {
     auto store = [&](uint16_t* dst) {
 #pragma unroll
         for (int c = 0; c < GT::CPT; ++c) {
-            const int x = min(tid + 256 * c, GT::CHUNKS - 1);
+            const int x = min(tid + kGateThreads * c, GT::CHUNKS - 1);
             const int pl = x / (32 * D / 8), r = (x / (D / 8)) % 32, cc = x % (D / 8);
             *(u32x4*)(dst + pl * GT::PLANE + r * GT::RS + cc * 8) = st[c];
         }
@@ -405,8 +411,9 @@ hipError_t launch_pool(const PoolArgs& a, int head_dim, bool f32_in, int lists, 
 
 template <int D, int M, int QS, int NP, bool MM>
 static hipError_t gate_dm(const GateArgs& a, hipStream_t s) {
-    const int ntiles = (a.N + 127) / 128;
-    hipLaunchKernelGGL((gate_kernel<D, M, QS, NP, MM>), dim3(ntiles * a.Bt * a.Hq), dim3(256), 0, s,
+    const int rows = 32 * gate_waves(QS);
+    const int ntiles = (a.N + rows - 1) / rows;
+    hipLaunchKernelGGL((gate_kernel<D, M, QS, NP, MM>), dim3(ntiles * a.Bt * a.Hq), dim3(2 * rows), 0, s,
                        a);
     return hipGetLastError();
 }
