@@ -48,7 +48,8 @@ struct Plan {
     int Nk, dec_cmax;
     float scale;
     // workspace regions (byte offsets)
-    size_t o_split, o_kb3, o_sel, o_count, o_cursor, o_listoff, o_listch, o_nchunks, o_chunk_list,
+    size_t o_sinkterm;
+    size_t o_split, o_kb3, o_sel, o_count, o_cursor, o_tilebase, o_listoff, o_listch, o_nchunks, o_chunk_list,
         o_chunk_start, o_entries, o_part_o, o_part_lse, o_tok_split, o_tok_state, o_tok_mask,
         o_tok_qn, o_tok_win, o_tok_kpart, o_tok_scr, o_tok_nslow, o_dec_scores, o_dec_list,
         o_dec_nfar, o_dec_plist, o_dec_pcnt, o_dec_redo, o_dec_part, o_qsum, o_cmp_k, o_cmp_v,
@@ -198,6 +199,7 @@ int make_plan(const sparse_attn_cfg* c, Plan* p, bool bwd = false) {
         P.o_q16 = take(nq * 2);
         P.o_do16 = take(nq * 2);
         P.o_delta = take((size_t)rows * 4);
+        P.o_sinkterm = take(c->sink ? (size_t)rows * 4 : 0);   // per-row dsink terms
         P.o_near = take(P.gate ? (size_t)rows * 4 : 0);
     } else {
         P.o_split = take(P.f32 ? 2 * (nq + 2 * nkv) * 2 : 0);
@@ -214,7 +216,8 @@ int make_plan(const sparse_attn_cfg* c, Plan* p, bool bwd = false) {
         P.o_sel = take((size_t)rows * P.top_k * 4);
         if (P.far) {
             P.o_count = take((size_t)P.lists * 4);
-            P.o_cursor = take((size_t)P.lists * 4);
+            P.o_cursor = take(bwd ? 0 : (size_t)P.lists * 4);
+            P.o_tilebase = take(bwd ? (size_t)P.lists * ((P.N + 255) / 256) * 4 : 0);
             P.o_listoff = take((size_t)(P.lists + 1) * 4);
             P.o_listch = take((size_t)(P.lists + 1) * 4);
             P.o_nchunks = take(4);
@@ -333,13 +336,16 @@ int select_blocks(const Plan& P, const void* q, const void* k, const uint16_t* c
 
 // Per-(batch, kv head, block) lists of the rows that keep that block as a
 // far block, and their chunking.
-int compact_far(const Plan& P, const int32_t* sel, char* ws, hipStream_t s, sa::CompactArgs* out) {
+int compact_far(const Plan& P, const int32_t* sel, char* ws, bool ordered, hipStream_t s,
+                sa::CompactArgs* out) {
     sa::CompactArgs& ca = *out;
     ca = sa::CompactArgs{};
     ca.sel = sel; ca.Bt = P.Bt; ca.Hq = P.Hq; ca.Hkv = P.Hkv; ca.N = P.N; ca.B = P.B;
     ca.n = P.n; ca.top_k = P.top_k; ca.span = P.span; ca.kslots = P.kslots;
     ca.count = (int32_t*)(ws + P.o_count);
-    ca.cursor = (int32_t*)(ws + P.o_cursor);
+    ca.cursor = ordered ? nullptr : (int32_t*)(ws + P.o_cursor);
+    ca.tile_base = ordered ? (int32_t*)(ws + P.o_tilebase) : nullptr;
+    ca.ordered = ordered;
     ca.list_off = (int32_t*)(ws + P.o_listoff);
     ca.list_ch = (int32_t*)(ws + P.o_listch);
     ca.entries = (int32_t*)(ws + P.o_entries);
@@ -590,7 +596,7 @@ int sparse_attn_fwd(const void* q, const void* k, const void* v, const sparse_at
             part_o = (uint16_t*)(ws + P.o_part_o);
             part_lse = (float*)(ws + P.o_part_lse);
             sa::CompactArgs ca{};
-            const int rc_comp = compact_far(P, sel, ws, s, &ca);
+            const int rc_comp = compact_far(P, sel, ws, false, s, &ca);
             if (rc_comp != SA_OK) return rc_comp;
             sa::BlocksArgs ba{};
             for (int i = 0; i < 2; ++i) { ba.q[i] = qp[i]; ba.k[i] = kp[i]; ba.v[i] = vp[i]; }
@@ -723,7 +729,7 @@ int sparse_attn_bwd(const void* q, const void* k, const void* v, const void* out
         rc = select_blocks(P, q, k, qp, 1, ws, sel, s);
         if (rc != SA_OK) return rc;
         if (P.far) {
-            rc = compact_far(P, sel, ws, s, &ca);
+            rc = compact_far(P, sel, ws, true, s, &ca);
             if (rc != SA_OK) return rc;
         }
     }
@@ -744,6 +750,7 @@ int sparse_attn_bwd(const void* q, const void* k, const void* v, const void* out
     ba.q16 = q16; ba.k16 = k16; ba.do16 = do16;
     ba.lse = lse; ba.delta = (float*)(ws + P.o_delta);
     ba.sink = cfg->sink; ba.dsink = dsink;
+    ba.sink_term = dsink ? (float*)(ws + P.o_sinkterm) : nullptr;
     ba.dq = (uint16_t*)dq; ba.dk = (uint16_t*)dk; ba.dv = (uint16_t*)dv;
     ba.sel = sel; ba.top_k = P.top_k; ba.B = P.B; ba.n = P.n; ba.span = P.span;
     ba.near_mask = P.gate ? (uint32_t*)(ws + P.o_near) : nullptr;

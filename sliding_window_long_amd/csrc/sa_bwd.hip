@@ -61,22 +61,28 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
             a.near_mask[r] = nm;
         }
     }
-    if (!a.dsink) return;
-    float term = (r < rows && a.sink) ? -__expf(a.sink[h] - a.lse[r]) * dsum : 0.f;
-    // Lanes of one head add once per wave; mixed waves add per lane.
-    const int h0 = __builtin_amdgcn_readfirstlane(h);
-    if (__ballot(h != h0 && h >= 0) == 0) {
-#pragma unroll
-        for (int d = 32; d >= 1; d >>= 1) term += __shfl_xor(term, d);
-        if ((threadIdx.x & 63) == 0 && h0 >= 0) atomicAdd(&a.dsink[h0], term);
-    } else if (h >= 0) {
-        atomicAdd(&a.dsink[h], term);
-    }
+    // The row's term of its head's sink gradient, summed in a fixed order
+    // by bwd_dsink_kernel.
+    if (a.dsink && r < rows) a.sink_term[r] = -__expf(a.sink[h] - a.lse[r]) * dsum;
 }
 
-__global__ __launch_bounds__(256) void bwd_zero_kernel(float* x, int n) {
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i < n) x[i] = 0.f;
+// dsink_h: one workgroup per head sums the head's row terms, each thread a
+// fixed strided set and then a fixed tree, so every call gives the same bits.
+__global__ __launch_bounds__(256) void bwd_dsink_kernel(BwdArgs a) {
+    const int h = blockIdx.x, t = threadIdx.x;
+    float acc = 0.f;
+    for (int b = 0; b < a.Bt; ++b) {
+        const float* tr = a.sink_term + ((size_t)b * a.Hq + h) * a.N;
+        for (int i = t; i < a.N; i += 256) acc += tr[i];
+    }
+    __shared__ float red[256];
+    red[t] = acc;
+    __syncthreads();
+    for (int w = 128; w >= 1; w >>= 1) {
+        if (t < w) red[t] += red[t + w];
+        __syncthreads();
+    }
+    if (t == 0) a.dsink[h] = red[0];
 }
 
 // Probabilities and score gradients of one tile in the S^T register layout:
@@ -666,12 +672,10 @@ static hipError_t bwd_d(const BwdArgs& a, hipStream_t s) {
 
 hipError_t launch_bwd_delta(const BwdArgs& a, hipStream_t s) {
     const size_t rows = (size_t)a.Bt * a.Hq * a.N;
-    if (a.dsink) {
-        hipLaunchKernelGGL(bwd_zero_kernel, dim3((a.Hq + 255) / 256), dim3(256), 0, s, a.dsink, a.Hq);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
     hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)((rows + 255) / 256)), dim3(256), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !a.dsink) return e;
+    hipLaunchKernelGGL(bwd_dsink_kernel, dim3((unsigned)a.Hq), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

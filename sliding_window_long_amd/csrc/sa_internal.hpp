@@ -143,6 +143,7 @@ struct BwdArgs {
     float* delta;           // D_i [Bt*Hq*N]
     const float* sink;      // [Hq] or nullptr
     float* dsink;           // [Hq] or nullptr
+    float* sink_term;       // [Bt*Hq*N] per-row terms of dsink (with dsink)
     uint16_t* dq;
     uint16_t* dk;
     uint16_t* dv;
@@ -177,7 +178,10 @@ struct CompactArgs {
     const int32_t* sel;
     int Bt, Hq, Hkv, N, B, n, top_k, span, kslots;
     int32_t* count;         // [lists] zeroed before the count pass
-    int32_t* cursor;        // [lists]
+    int32_t* cursor;        // [lists] (fast scatter)
+    int32_t* tile_base;     // [Bt*Hkv][ceil(N / 256)][n] per row tile: count, then first
+                            // position (ordered scatter)
+    bool ordered;           // lists in a fixed order (the backward's)
     int32_t* list_off;      // [lists + 1]
     int32_t* list_ch;       // [lists + 1] first chunk of each list (prefix of chunk counts)
     int32_t* entries;
