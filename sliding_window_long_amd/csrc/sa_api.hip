@@ -98,9 +98,12 @@ int make_plan(const sparse_attn_cfg* c, Plan* p, bool bwd = false) {
         return SA_E_UNSUPPORTED;
     if (c->token_top_k > 0) {
         if (c->index_dim != 64) return SA_E_UNSUPPORTED_HEAD_DIM;
-        // 16 index bits in the selection key; block and token gates are
-        // separate methods and are not combined in one call.
-        if (Nk > 65536 || c->top_k > 0) return SA_E_UNSUPPORTED;
+        // Block and token gates are separate methods and are not combined
+        // in one call.  Prefill: token ids below 2^24 (the selection packs
+        // 24 index bits with a row number in its staging area).  Decode
+        // steps: caches of at most 65536 tokens (16 index bits in the decode
+        // selection's keys).
+        if (c->top_k > 0 || Nk > (1 << 24) || (dec && Nk > 65536)) return SA_E_UNSUPPORTED;
     }
 
     Plan& P = *p;

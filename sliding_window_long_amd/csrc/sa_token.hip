@@ -7,8 +7,8 @@
 // candidates j < i, keep the min(top_t, i) best, a tie going to the lower j;
 // the selection is shared by every query head.
 //
-// The selection is exact: "the k best" is the set of the k largest 48-bit keys
-//   key = ord(score) << 16 | (0xFFFF - j)
+// The selection is exact: "the k best" is the set of the k largest 64-bit keys
+//   key = ord(score) << 32 | (0xFFFFFFFF - j)
 // where ord maps fp32 to a uint32 with the same order, so the key order is
 // (score descending, then j ascending).  Scores are recomputed on the matrix
 // core in every pass (same instruction sequence, so bitwise the same values);
@@ -31,11 +31,11 @@
 //   5. bin: the bin b* holding the k-th best candidate, the count above it
 //      and the rank r still to take inside it.
 //   6. mask: keys in bins above b* are kept (mask written whole); the
-//      candidates of bin b* are collected as 48-bit keys.
+//      candidates of bin b* are collected as 64-bit keys.
 //   7. resolve: radix select of the r best collected keys, whose mask bits
 //      are then set.
 // Rows whose bin b* holds more than kTokCap candidates, or whose k-th
-// candidate lies below the window, are left to the radix fallback: radix select over the 48-bit key one byte per pass (per-row
+// candidate lies below the window, are left to the radix fallback: radix select over the 64-bit key one byte per pass (per-row
 // 256-bin histograms in LDS), then the mask of those rows.
 //
 // Output: a keep mask in the layout of the attention kernel's registers.
@@ -501,13 +501,14 @@ __global__ __launch_bounds__(TOK_THREADS) void tok_bin_kernel(TokArgs a) {
 }
 
 // Mask pass: the keep mask of every binned row: keys in bins above b* kept,
-// candidates of b* collected (48-bit key) for the resolve step.  Rows left
+// candidates of b* collected (64-bit key) for the resolve step.  Rows left
 // to the radix fallback are not written.
 constexpr int kTokStage = 2048;   // candidates one mask unit can hold in LDS
 template <int SPLIT>
 __global__ __launch_bounds__(TOK_THREADS) void tok_mask_kernel(TokArgs a) {
     __shared__ __attribute__((aligned(16))) TokLds<SPLIT> lds;
-    // Candidates of this unit: 48-bit key, local row in bits 48..54.
+    // Candidates of this unit: ord(score), and the low 24 bits of
+    // 0xFFFFFFFF - j (j < 2^24: the top 8 bits are ones) under the local row.
     __shared__ uint2 stage[kTokStage];
     __shared__ int s_cnt;
     const int tid = threadIdx.x, wave = wave_id(), lane = tid & 63;
@@ -562,7 +563,7 @@ __global__ __launch_bounds__(TOK_THREADS) void tok_mask_kernel(TokArgs a) {
                 const uint32_t o = ord32(acc[v]);
                 const uint32_t j = (uint32_t)(t * 32 + 8 * (v >> 2) + (v & 3) + 4 * hh);
                 if (pos < kTokStage) {
-                    stage[pos] = make_uint2((o << 16) | (0xffffu - j), (o >> 16) | (lr << 16));
+                    stage[pos] = make_uint2(o, (0xffffffu - j) | (lr << 24));
                 } else {   // no room: the radix fallback takes the row
                     atomicOr(&a.state[gr].w, (int)kTokSlow);
                     atomicAdd(a.nslow, 1);
@@ -576,14 +577,15 @@ __global__ __launch_bounds__(TOK_THREADS) void tok_mask_kernel(TokArgs a) {
     const int n = min(s_cnt, kTokStage);
     for (int e = tid; e < n; e += TOK_THREADS) {
         const uint2 h = stage[e];
-        const size_t g = (size_t)bt * a.N + b * kTokRows + (h.y >> 16);
+        const size_t g = (size_t)bt * a.N + b * kTokRows + (h.y >> 24);
         const int pos = atomicAdd(&a.state[g].y, 1);
-        if (pos < kTokCap) a.hits[g * kTokCap + pos] = make_uint2(h.x, h.y & 0xffffu);
+        // hits: (low word 0xFFFFFFFF - j, high word ord(score)) of the key
+        if (pos < kTokCap) a.hits[g * kTokCap + pos] = make_uint2(0xff000000u | (h.y & 0xffffffu), h.x);
     }
 }
 
 // Resolve step: one wave per binned row: radix select (one byte per step, from
-// the top of the 48-bit key) of the r best collected candidates, then
+// the top of the 64-bit key) of the r best collected candidates, then
 // their mask bits.
 __global__ __launch_bounds__(TOK_THREADS) void tok_resolve_kernel(TokArgs a) {
     __shared__ uint32_t hs[TOK_WAVES][256];
@@ -609,7 +611,7 @@ __global__ __launch_bounds__(TOK_THREADS) void tok_resolve_kernel(TokArgs a) {
     uint64_t prefix = 0, pmask = 0;
     uint32_t rem = (uint32_t)st.z;
     bool ok = true;
-    for (int d = 5; d >= 0; --d) {
+    for (int d = 7; d >= 0; --d) {
         const int sh = 8 * d;
 #pragma unroll
         for (int i = 0; i < 4; ++i) hw[4 * lane + i] = 0;
@@ -639,7 +641,7 @@ __global__ __launch_bounds__(TOK_THREADS) void tok_resolve_kernel(TokArgs a) {
 #pragma unroll
     for (int m = 0; m < PER; ++m) {
         if (!val[m] || key[m] < prefix) continue;
-        const int j = 0xffff - (int)(key[m] & 0xffffu);
+        const int j = (int)(0xffffffffu - (uint32_t)key[m]);
         if (j >= row) continue;   // never taken: collected keys are earlier tokens
         const int kc = j >> 5, jl = j & 31;
         const int ln = (row & 31) + 32 * ((jl >> 2) & 1), v = 4 * (jl >> 3) + (jl & 3);
@@ -650,8 +652,9 @@ __global__ __launch_bounds__(TOK_THREADS) void tok_resolve_kernel(TokArgs a) {
 
 // ---------------------------------------------------------------------------
 // Radix fallback for the rows flagged kTokSlow: one pass over the
-// candidates of a 32-row tile (4 waves split the key tiles).  pass 0..5:
-// radix histogram step; pass 6: write the keep mask of those rows.
+// candidates of a 32-row tile (4 waves split the key tiles).  pass 0..7:
+// radix histogram step (score bytes, then bytes of 0xFFFFFFFF - j); pass 8:
+// write the keep mask of those rows.
 template <int SPLIT>
 __global__ __launch_bounds__(TOK_THREADS) void token_select_kernel(TokArgs a, int pass) {
     if (*a.nslow == 0) return;
@@ -682,8 +685,8 @@ __global__ __launch_bounds__(TOK_THREADS) void token_select_kernel(TokArgs a, in
 
     if (tid == 0) s_skip = 1;
     __syncthreads();
-    if (!(flags & (pass < 6 ? kTokDone : kTokFast))) s_skip = 0;   // benign race: every writer stores 0
-    if (pass < 6)
+    if (!(flags & (pass < 8 ? kTokDone : kTokFast))) s_skip = 0;   // benign race: every writer stores 0
+    if (pass < 8)
         for (int x = tid; x < 32 * HSTRIDE; x += TOK_THREADS) hist[x] = 0;
     __syncthreads();
     if (s_skip) {
@@ -696,11 +699,11 @@ __global__ __launch_bounds__(TOK_THREADS) void token_select_kernel(TokArgs a, in
 
     const bool active = !(flags & kTokDone);
     // Byte of the key examined in this pass and the prefix that must match.
-    const int shift = pass < 4 ? 24 - 8 * pass : 8 - 8 * (pass - 4);
+    const int shift = pass < 4 ? 24 - 8 * pass : 24 - 8 * (pass - 4);
     for (int kc = wave; kc <= rt; kc += TOK_WAVES) {
         const f32x16 acc = index_scores<SPLIT>(a, bt, kc, qf, lane);
         const int rj = row - kc * 32 - 4 * hh;   // row - key = rj - cv
-        if (pass < 6) {
+        if (pass < 8) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int cv = 8 * (v >> 2) + (v & 3);
@@ -711,9 +714,9 @@ __global__ __launch_bounds__(TOK_THREADS) void token_select_kernel(TokArgs a, in
                     if (pass > 0) take = take && ((o ^ pre32) >> (shift + 8)) == 0;
                     digit = (o >> shift) & 0xffu;
                 } else {
-                    const uint32_t ik = 0xffffu - (uint32_t)(kc * 32 + 4 * hh + cv);
+                    const uint32_t ik = 0xffffffffu - (uint32_t)(kc * 32 + 4 * hh + cv);
                     take = take && o == pre32;
-                    if (pass == 5) take = take && ((ik ^ preidx) >> 8) == 0;
+                    if (pass > 4) take = take && ((ik ^ preidx) >> (shift + 8)) == 0;
                     digit = (ik >> shift) & 0xffu;
                 }
                 if (take) atomicAdd(&hist[col * HSTRIDE + digit], 1u);
@@ -725,14 +728,14 @@ __global__ __launch_bounds__(TOK_THREADS) void token_select_kernel(TokArgs a, in
             for (int v = 0; v < 16; ++v) {
                 const int cv = 8 * (v >> 2) + (v & 3);
                 const uint32_t o = ord32(acc[v]);
-                const uint32_t ik = 0xffffu - (uint32_t)(kc * 32 + 4 * hh + cv);
+                const uint32_t ik = 0xffffffffu - (uint32_t)(kc * 32 + 4 * hh + cv);
                 const bool keep = rj > cv && (o > pre32 || (o == pre32 && ik >= preidx));
                 bits |= (keep ? 1u : 0u) << v;
             }
             a.mask[mask_half(bt, nt, (a.N + 63) / 64, rt, kc, lane)] = (uint16_t)bits;
         }
     }
-    if (pass == 6) return;
+    if (pass == 8) return;
     __syncthreads();
     if (tid < 32 && row_ok) {
         if (active) {
@@ -757,7 +760,7 @@ __global__ __launch_bounds__(TOK_THREADS) void token_select_kernel(TokArgs a, in
                 }
             } else {
                 stt.y = (int)(preidx | ((uint32_t)b << shift));
-                if (pass == 5) fl |= kTokDone;
+                if (pass == 7) fl |= kTokDone;
             }
             stt.z = (int)k;
             stt.w = (int)fl;
@@ -820,7 +823,7 @@ hipError_t launch_token_select(const TokArgs& a, int split, hipStream_t s) {
     }
     const int nt = (a.N + 31) / 32;
     const dim3 grid((unsigned)(nt * a.Bt));
-    for (int pass = 0; pass <= 6; ++pass) {
+    for (int pass = 0; pass <= 8; ++pass) {
         if (split == 2)
             hipLaunchKernelGGL(token_select_kernel<2>, grid, dim3(TOK_THREADS), 0, s, a, pass);
         else

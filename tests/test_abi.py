@@ -77,7 +77,7 @@ def code_of(params, **cfg_fields):
     (sa.Params(1, 4, 4, 64 * 40, 64, block_size=64, top_k=34), -8),   # top_k > 33
     (sa.Params(1, 4, 4, 256, 64, window=8, softmax_scale=-1.0), -1),
     (sa.Params(1, 4, 1, 256, 128, window=8, token_top_k=16, index_dim=32), -3),
-    (sa.Params(1, 4, 1, 65536 + 64, 128, window=8, token_top_k=16, index_dim=64), -8),
+    (sa.Params(1, 4, 1, (1 << 24) + 64, 128, window=8, token_top_k=16, index_dim=64), -8),   # ids past 2^24
     (sa.Params(1, 4, 1, 256, 128, window=8, block_size=64, top_k=2, token_top_k=16,
                index_dim=64), -8),
     (sa.Params(1, 1, 1, 1 << 23, 128, window=8), -8),                # one head's K past 2 GiB
@@ -86,7 +86,7 @@ def code_of(params, **cfg_fields):
     (sa.Params(1, 4, 4, 4, 64, block_size=64, top_k=2, kv_len=256), -8),  # decode with block gate
     (sa.Params(1, 4, 4, 65, 64, window=8, kv_len=256), -8),           # decode past 64 queries
     (sa.Params(1, 4, 1, 1, 128, window=8, token_top_k=16, index_dim=64,
-               kv_len=65536 + 1), -8),                               # 16-bit token ids
+               kv_len=65536 + 1), -8),                               # decode: 16-bit token ids
     (sa.Params(1, 4, 4, 1, 64, kv_len=256), -4),                      # decode, no window
     (sa.Params(1, 4, 4, 256, 64, block_size=64, top_k=2, gate_repr=2), -1),   # unknown summary
     (sa.Params(1, 4, 4, 256, 64, block_size=64, top_k=2, gate_shared=2), -1),

@@ -455,6 +455,43 @@ def test_swa_token_full_sampled(dev):
     assert srep.mismatched == 0 and srep.invalid == 0, str(srep)
 
 
+def test_token_history_past_16_bits(dev):
+    # Token ids past 2^16: N = 131072 with 2 q heads on 1 kv head.  4096 equal
+    # indexer keys straddle id 65536 and score above every other key for the
+    # rows from 67584 on (their indexer queries equal that key: score 256
+    # against at most ~80 for the N(0,1) keys), so those rows must keep
+    # exactly the 2048 lowest of the tied ids, 63488 .. 65535 -- a 16-bit id
+    # field would rank 65536 .. 67583 (as 0 .. 2047) above them.  Other rows:
+    # the usual sampled selection and output checks.
+    from parity import check_token_selection
+    wl = W.Workload("swa_token_n131072", 1, 2, 1, 131072, 64, "bf16", window=128,
+                    token_top_k=2048, index_dim=64, sink=True)
+    inp = W.make_inputs(wl, 131)
+    lo, hi = 63488, 67584
+    inp.idx_k[0, lo:hi] = 2.0
+    inp.idx_q[0, hi:] = 2.0
+    log(f"[gpu] token_past_16_bits {wl}")
+    out, lse, bsel, tsel = run_device(inp, dev)
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    rng = np.random.default_rng(9)
+    tied_rows = np.concatenate([[hi, hi + 1, 98304, wl.seq_len - 1],
+                                rng.integers(hi, wl.seq_len, size=60)])
+    want = np.arange(lo, lo + 2048)
+    for r in tied_rows:
+        np.testing.assert_array_equal(tsel[0, r], want, err_msg=f"row {r}")
+    pos = np.unique(np.concatenate([rng.choice(lo, size=400, replace=False),
+                                    np.arange(lo - 2, lo + 40), np.arange(65530, 65542),
+                                    np.arange(hi - 3, hi + 3), rng.integers(hi, wl.seq_len, 60)]))
+    srep = check_token_selection(inp, tsel, pos)
+    log(f"[gpu] token_past_16_bits selection on {len(pos)} positions: {srep}")
+    assert srep.mismatched == 0 and srep.invalid == 0, str(srep)
+    rows = np.unique(np.concatenate([W.sample_rows(wl, 40, 3),
+                                     [h * wl.seq_len + i for h in range(2) for i in (65535, 65536, hi, 100000)]]))
+    rep = check(inp, out, lse, rows, bsel, tsel)
+    log(f"[gpu] token_past_16_bits outputs {rep}")
+    assert rep.ok(), str(rep)
+
+
 # --- decode/append step (queries continuing a cached history) ---------------
 def decode_inputs(wl, nq, seed):
     """The last nq positions of a seeded full-length input as the queries;
