@@ -212,9 +212,13 @@ int sparse_attn_block_pool(const void* k, const sparse_attn_cfg* cfg, float* kba
  * Supported: bf16 prefills with a window and/or block gating (any gate
  * variant); a token gate, the compressed branch, fp32 or a decode step
  * return SA_E_UNSUPPORTED.  The gradient products run on fp16 matrix cores
- * with fp16 copies of q, k and dout and fp16 score gradients dS_ij: their
- * magnitudes must stay below 65504 (no scaling is applied here).  Workspace from sparse_attn_bwd_workspace_bytes;
- * enqueued on cfg->stream, no host sync, nothing allocated. */
+ * with fp16 copies of q, k and dout and fp16 score gradients dS_ij, each at
+ * a power-of-two scale per (batch, kv head) chosen from the data (the rule
+ * of the forward's V copy; for dS from the largest |dout| and |v|), undone
+ * exactly in fp32: every finite bf16 input stays inside the fp16 range.
+ * Results are the same bits on every call (fixed summation orders).
+ * Workspace from sparse_attn_bwd_workspace_bytes; enqueued on cfg->stream,
+ * no host sync, nothing allocated. */
 int sparse_attn_bwd_workspace_bytes(const sparse_attn_cfg* cfg, size_t* bytes);
 int sparse_attn_bwd(const void* q, const void* k, const void* v, const void* out,
                     const float* lse, const void* dout, const sparse_attn_cfg* cfg,

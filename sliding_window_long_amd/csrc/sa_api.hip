@@ -48,7 +48,7 @@ struct Plan {
     int Nk, dec_cmax;
     float scale;
     // workspace regions (byte offsets)
-    size_t o_sinkterm;
+    size_t o_sinkterm, o_bmax_q, o_bmax_do, o_bmax_k, o_bmax_v, o_bgmax, o_bexp;
     size_t o_split, o_kb3, o_sel, o_count, o_cursor, o_tilebase, o_listoff, o_listch, o_nchunks, o_chunk_list,
         o_chunk_start, o_entries, o_part_o, o_part_lse, o_tok_split, o_tok_state, o_tok_mask,
         o_tok_qn, o_tok_win, o_tok_kpart, o_tok_scr, o_tok_nslow, o_dec_scores, o_dec_list,
@@ -203,6 +203,16 @@ int make_plan(const sparse_attn_cfg* c, Plan* p, bool bwd = false) {
         P.o_do16 = take(nq * 2);
         P.o_delta = take((size_t)rows * 4);
         P.o_sinkterm = take(c->sink ? (size_t)rows * 4 : 0);   // per-row dsink terms
+        // Range of the fp16 copies: per-128-row maxima of q, dO (per q head)
+        // and k, v (per kv head), then per (batch, kv head) the largest |dO|,
+        // |v| and the exponents of q, k, dO and the score gradients.
+        const size_t ch = (size_t)sa::f16_chunks(P.N);
+        P.o_bmax_q = take((size_t)P.Bt * P.Hq * ch * 4);
+        P.o_bmax_do = take((size_t)P.Bt * P.Hq * ch * 4);
+        P.o_bmax_k = take((size_t)P.Bt * P.Hkv * ch * 4);
+        P.o_bmax_v = take((size_t)P.Bt * P.Hkv * ch * 4);
+        P.o_bgmax = take((size_t)P.Bt * P.Hkv * 2 * 4);
+        P.o_bexp = take((size_t)P.Bt * P.Hkv * 5 * 4);
         P.o_near = take(P.gate ? (size_t)rows * 4 : 0);
     } else {
         P.o_split = take(P.f32 ? 2 * (nq + 2 * nkv) * 2 : 0);
@@ -736,21 +746,42 @@ int sparse_attn_bwd(const void* q, const void* k, const void* v, const void* out
             if (rc != SA_OK) return rc;
         }
     }
-    const size_t nq = (size_t)P.Bt * P.Hq * P.N * P.D, nkv = (size_t)P.Bt * P.Hkv * P.N * P.D;
     uint16_t* k16 = (uint16_t*)(ws + P.o_k16);
     uint16_t* q16 = (uint16_t*)(ws + P.o_q16);
     uint16_t* do16 = (uint16_t*)(ws + P.o_do16);
+    // fp16 copies of k, q, dO at a power-of-two scale per (batch, kv head)
+    // (the rule of the forward's V copy), and the exponent of the score
+    // gradients from the largest |dO| and |v|.
+    const int groups = P.Bt * P.Hkv;
+    int32_t* bexp = (int32_t*)(ws + P.o_bexp);
+    int32_t *sq = bexp, *sk = bexp + groups, *sd = bexp + 2 * groups, *es = bexp + 3 * groups,
+            *sv = bexp + 4 * groups;
+    float* gmax = (float*)(ws + P.o_bgmax);
     {
         StageScope t("bwd_to_f16", s);
-        if (!ok(sa::launch_bf16_to_f16((const uint16_t*)k, k16, nkv, s)) ||
-            !ok(sa::launch_bf16_to_f16((const uint16_t*)q, q16, nq, s)) ||
-            !ok(sa::launch_bf16_to_f16((const uint16_t*)dout, do16, nq, s)))
+        float* mq = (float*)(ws + P.o_bmax_q);
+        float* mdo = (float*)(ws + P.o_bmax_do);
+        float* mk = (float*)(ws + P.o_bmax_k);
+        float* mv = (float*)(ws + P.o_bmax_v);
+        const int hq = P.Bt * P.Hq, hkv = P.Bt * P.Hkv;
+        if (!ok(sa::launch_f16_copy(k, false, k16, mk, hkv, P.N, P.D, P.D, s)) ||
+            !ok(sa::launch_f16_scale(k, false, k16, mk, sk, groups, 1, P.N, P.D, P.D, s)) ||
+            !ok(sa::launch_f16_copy(q, false, q16, mq, hq, P.N, P.D, P.D, s)) ||
+            !ok(sa::launch_f16_scale(q, false, q16, mq, sq, groups, P.G, P.N, P.D, P.D, s)) ||
+            !ok(sa::launch_f16_copy(dout, false, do16, mdo, hq, P.N, P.D, P.D, s)) ||
+            !ok(sa::launch_f16_scale(dout, false, do16, mdo, sd, groups, P.G, P.N, P.D, P.D, s,
+                                     gmax)) ||
+            !ok(sa::launch_f16_copy(v, false, nullptr, mv, hkv, P.N, P.D, P.D, s)) ||
+            !ok(sa::launch_f16_scale(v, false, nullptr, mv, sv, groups, 1, P.N, P.D, P.D, s,
+                                     gmax + groups)) ||
+            !ok(sa::launch_ds_exponent(gmax, gmax + groups, es, groups, P.D, s)))
             return SA_E_HIP;
     }
     sa::BwdArgs ba{};
     ba.q = (const uint16_t*)q; ba.k = (const uint16_t*)k; ba.v = (const uint16_t*)v;
     ba.out = (const uint16_t*)out; ba.dout = (const uint16_t*)dout;
     ba.q16 = q16; ba.k16 = k16; ba.do16 = do16;
+    ba.sq = sq; ba.sk = sk; ba.sd = sd; ba.es = es;
     ba.lse = lse; ba.delta = (float*)(ws + P.o_delta);
     ba.sink = cfg->sink; ba.dsink = dsink;
     ba.sink_term = dsink ? (float*)(ws + P.o_sinkterm) : nullptr;

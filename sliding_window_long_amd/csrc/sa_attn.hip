@@ -346,22 +346,6 @@ __global__ __launch_bounds__(NTHREADS, D <= 80 && SPLIT == 1 ? 3 : 2) void attn_
 }
 
 
-// bf16 -> fp16, exact for |x| in the fp16 normal range [2^-14, 65504].
-__global__ void bf16_to_f16_kernel(const uint4* __restrict__ x, uint4* __restrict__ y, size_t n8) {
-    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n8) return;
-    const uint4 u = x[i];
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-    uint32_t r[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const _Float16 lo = (_Float16)bf16_to_f32(w[t] & 0xffffu);
-        const _Float16 hi = (_Float16)bf16_to_f32(w[t] >> 16);
-        r[t] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-    }
-    y[i] = make_uint4(r[0], r[1], r[2], r[3]);
-}
-
 // Largest |x| of 8 bf16 values (sign bits cleared; NaN-free compares).
 __device__ __forceinline__ float absmax8(const uint4& u, float m) {
     const uint32_t w[4] = {u.x, u.y, u.z, u.w};
@@ -468,8 +452,8 @@ template <bool FP8>
 __global__ __launch_bounds__(256) void f16_scale_kernel(const void* __restrict__ x,
                                                         uint4* __restrict__ y,
                                                         const float* __restrict__ chunk_max,
-                                                        int32_t* scale, int hpg, int rows, int D,
-                                                        int SR) {
+                                                        int32_t* scale, float* group_max, int hpg,
+                                                        int rows, int D, int SR) {
     const int grp = blockIdx.x, nch = f16_chunks(rows);
     const float* cm = chunk_max + (size_t)grp * hpg * nch;
     float m = 0.f;
@@ -490,6 +474,7 @@ __global__ __launch_bounds__(256) void f16_scale_kernel(const void* __restrict__
         }
         s_sh = sc;
         scale[grp] = sc;
+        if (group_max) group_max[grp] = mx;
     }
     __syncthreads();
     const int sc = s_sh;
@@ -520,24 +505,17 @@ hipError_t launch_f16_copy(const void* x, bool fp8, uint16_t* y, float* chunk_ma
 
 hipError_t launch_f16_scale(const void* x, bool fp8, uint16_t* y, const float* chunk_max,
                             int32_t* scale, int groups, int hpg, int rows, int D, int SR,
-                            hipStream_t s) {
+                            hipStream_t s, float* group_max) {
     if (groups == 0 || rows == 0) return hipSuccess;
     if (fp8)
         hipLaunchKernelGGL(f16_scale_kernel<true>, dim3((unsigned)groups), dim3(256), 0, s, x,
-                           (uint4*)y, chunk_max, scale, hpg, rows, D, SR);
+                           (uint4*)y, chunk_max, scale, group_max, hpg, rows, D, SR);
     else
         hipLaunchKernelGGL(f16_scale_kernel<false>, dim3((unsigned)groups), dim3(256), 0, s, x,
-                           (uint4*)y, chunk_max, scale, hpg, rows, D, SR);
+                           (uint4*)y, chunk_max, scale, group_max, hpg, rows, D, SR);
     return hipGetLastError();
 }
 
-hipError_t launch_bf16_to_f16(const uint16_t* x, uint16_t* y, size_t n, hipStream_t s) {
-    const size_t n8 = n / 8;   // n is a multiple of the head dim, hence of 8
-    if (n8 == 0) return hipSuccess;
-    hipLaunchKernelGGL(bf16_to_f16_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s,
-                       (const uint4*)x, (uint4*)y, n8);
-    return hipGetLastError();
-}
 
 // fp32 -> (hi, lo) bf16 planes: x = hi + lo + O(2^-16 |x|).
 __global__ void split_f32_kernel(const float* __restrict__ x, uint16_t* __restrict__ hi,

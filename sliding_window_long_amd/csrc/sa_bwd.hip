@@ -8,6 +8,14 @@
 //   dq_i = scale sum_j dS_ij k_j,  dk_j = scale sum_i dS_ij q_i,
 //   dv_j = sum_i P_ij dO_i,        dsink_h = -sum_i e^(sink_h - lse_i) D_i.
 //
+// The fp16 operands of the P V-style products are exact power-of-two
+// rescalings, one exponent per (batch, kv head): q 2^-sq, k 2^-sk, dO 2^-sd
+// (the rule of the forward's V copy) and dS 2^-es with es from the largest
+// |dO| and |v| (|dS| <= 2 d max|dO| max|v|); the products are scaled back
+// in fp32 before the bf16 results are written.  Every finite bf16 input then
+// stays inside the fp16 range, and for inputs already inside it the fp16
+// values round exactly as without the scaling.
+//
 // bwd_delta  : D_i per row, and the sink gradient.
 // bwd_far_dq : far blocks' share of dQ, key-block-centric over the forward's
 //              compaction lists (gathered rows), as fp16 partials per slot.
@@ -86,17 +94,17 @@ __global__ __launch_bounds__(256) void bwd_dsink_kernel(BwdArgs a) {
 }
 
 // Probabilities and score gradients of one tile in the S^T register layout:
-// p = 2^(s c - lse2) (0 where s = -inf), ds = p (dp - D).  lse2 and D are
-// given per register (per row of the tile) or per lane.
+// p = 2^(s c - lse2) (0 where s = -inf), ds = p (dp - D), taken as fp16 of
+// p and ds f with f = 2^-es (drf = D f).  lse2 and D are given per lane.
 __device__ __forceinline__ void p_ds(f32x16 (&s)[2], const f32x16 (&dp)[2], float c, float lse2,
-                                     float dr, uint4 (&pb)[4], uint4 (&db)[4]) {
+                                     float f, float drf, uint4 (&pb)[4], uint4 (&db)[4]) {
     float p[2][16], g[2][16];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             p[sub][v] = fast_exp2(fmaf(s[sub][v], c, -lse2));
-            g[sub][v] = p[sub][v] * (dp[sub][v] - dr);
+            g[sub][v] = p[sub][v] * fmaf(dp[sub][v], f, -drf);   // (dp - D) f, one rounding
         }
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
@@ -105,19 +113,20 @@ __device__ __forceinline__ void p_ds(f32x16 (&s)[2], const f32x16 (&dp)[2], floa
     }
 }
 
-// Write 32 rows' O^T registers (times f) as bf16 rows of dst (row stride D):
-// lane (col, hh) holds dims mb*32 + 8j + 4hh .. +3 of row col.
+// Write 32 rows' O^T registers (times f 2^e) as bf16 rows of dst (row
+// stride D): lane (col, hh) holds dims mb*32 + 8j + 4hh .. +3 of row col.
 template <int D>
 __device__ __forceinline__ void write_rows_bf16(uint16_t* dst, const f32x16 (&o)[Tile<D>::DM],
-                                                float f, int hh) {
+                                                float f, int e, int hh) {
 #pragma unroll
     for (int mb = 0; mb < Tile<D>::DM; ++mb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int d0 = mb * 32 + 8 * j + 4 * hh;
             if (d0 < D) {
-                __bf16 r[4] = {(__bf16)(o[mb][4 * j] * f), (__bf16)(o[mb][4 * j + 1] * f),
-                               (__bf16)(o[mb][4 * j + 2] * f), (__bf16)(o[mb][4 * j + 3] * f)};
+                __bf16 r[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) r[t] = (__bf16)ldexpf(o[mb][4 * j + t] * f, e);
                 *(uint2*)(dst + d0) = *(const uint2*)r;
             }
         }
@@ -160,14 +169,14 @@ template <int D>
 __device__ __forceinline__ void dq_tile(const uint16_t* lk, const uint16_t* lv, const uint16_t* lk16,
                                         const bf16x8 (&qf)[1][Tile<D>::DK], const bf16x8 (&df)[1][Tile<D>::DK],
                                         f32x16 (&o)[Tile<D>::DM], const int (&voff)[Tile<D>::DM],
-                                        float c, float lse2, float dr, bool masked, int rk, uint32_t wl,
-                                        int lane) {
+                                        float c, float lse2, float f, float drf, bool masked, int rk,
+                                        uint32_t wl, int lane) {
     f32x16 s[2], dp[2];
     qk_tile<D, 1>(lk, qf, s, lane);
     qk_tile<D, 1>(lv, df, dp, lane);
     if (masked) mask_tile(s, rk, wl);
     uint4 pb[4], db[4];
-    p_ds(s, dp, c, lse2, dr, pb, db);
+    p_ds(s, dp, c, lse2, f, drf, pb, db);
     const uint4 zero4[4] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0),
                             make_uint4(0, 0, 0, 0)};
     pv_tile<D, 1, DqTiles<D>::VS>(lk16, db, zero4, o, voff);
@@ -214,6 +223,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dq_kernel(BwdArgs a) {
     const float c = a.scale * kLog2e;
     const float lse2 = ok ? a.lse[prow] * kLog2e : 0.f;
     const float dr = ok ? a.delta[prow] : 0.f;
+    const int es = a.es[b * a.Hkv + g], sk = a.sk[b * a.Hkv + g];
+    const float f = ldexpf(1.f, -es), drf = dr * f;
 
     // Kept blocks: own and near ones (the near mask of the delta pass) are
     // attended here; far ones come as partials from bwd_far_dq.  nfar = the
@@ -248,7 +259,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dq_kernel(BwdArgs a) {
             const int dlt = row_blk - kt0 / a.B;
             if (dlt == 0 || (dlt >= 1 && dlt <= 32 && ((near_bits >> (dlt - 1)) & 1u))) wl = 0x80000000u;
         }
-        dq_tile<D>(lk, lv, lk16, qf, df, o, voff, c, lse2, dr, true, row - kt0 - 4 * hh, wl, lane);
+        dq_tile<D>(lk, lv, lk16, qf, df, o, voff, c, lse2, f, drf, true, row - kt0 - 4 * hh, wl, lane);
     };
     auto step = [&](auto par, int it) __attribute__((always_inline)) {
         constexpr int PAR = decltype(par)::value;
@@ -267,11 +278,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dq_kernel(BwdArgs a) {
     }
     if (it < n_t) step(Par<0>{}, it);
     if (!ok) return;
-    // dq = scale * near part + the far blocks' partials (already scaled).
+    // dq = scale 2^(es + sk) * near part + the far blocks' partials (bf16,
+    // already in the units of dq).
 #pragma unroll
     for (int mb = 0; mb < T::DM; ++mb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) o[mb][v] *= a.scale;
+        for (int v = 0; v < 16; ++v) o[mb][v] = ldexpf(o[mb][v] * a.scale, es + sk);
     for (int s_ = 0; s_ < nfar; ++s_) {
         const uint16_t* po = a.part_dq + (prow * (size_t)a.kslots + s_) * D;
 #pragma unroll
@@ -281,13 +293,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dq_kernel(BwdArgs a) {
                 const int d0 = mb * 32 + 8 * j + 4 * hh;
                 if (d0 < D) {
                     const uint2 raw = *(const uint2*)(po + d0);
-                    const _Float16* hv = (const _Float16*)&raw;
+                    const uint32_t w[2] = {raw.x, raw.y};
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) o[mb][4 * j + e] += (float)hv[e];
+                    for (int e = 0; e < 4; ++e)
+                        o[mb][4 * j + e] += bf16_to_f32((w[e >> 1] >> (16 * (e & 1))) & 0xffffu);
                 }
             }
     }
-    write_rows_bf16<D>(a.dq + prow * D, o, 1.f, hh);
+    write_rows_bf16<D>(a.dq + prow * D, o, 1.f, 0, hh);
 }
 
 // ---------------------------------------------------------------------------
@@ -295,7 +308,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dq_kernel(BwdArgs a) {
 // the list of rows that kept one block as a far block (the forward's
 // compaction), gathers those rows and walks the block's keys; every key of a
 // far block is attended.  Writes scale * sum_j dS_ij k_j per (row, slot),
-// fp16.
+// bf16 (the range of dq itself).
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(NTHREADS, 1) void bwd_far_dq_kernel(BwdArgs a) {
@@ -342,6 +355,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_far_dq_kernel(BwdArgs a) {
     const float c = a.scale * kLog2e;
     const float lse2 = ok ? a.lse[prow] * kLog2e : INFINITY;
     const float dr = ok ? a.delta[prow] : 0.f;
+    const int es = a.es[bg], sk = a.sk[bg];
+    const float f = ldexpf(1.f, -es), drf = dr * f;
 
     f32x16 o[T::DM];
 #pragma unroll
@@ -357,8 +372,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_far_dq_kernel(BwdArgs a) {
             if (PAR) dt.load(cblk * a.B + (t + 1) * KT, lk0, lv0, lk16_0, wu);
             else dt.load(cblk * a.B + (t + 1) * KT, lk1, lv1, lk16_1, wu);
         }
-        if (PAR) dq_tile<D>(lk1, lv1, lk16_1, qf, df, o, voff, c, lse2, dr, false, 0, 0u, lane);
-        else dq_tile<D>(lk0, lv0, lk16_0, qf, df, o, voff, c, lse2, dr, false, 0, 0u, lane);
+        if (PAR) dq_tile<D>(lk1, lv1, lk16_1, qf, df, o, voff, c, lse2, f, drf, false, 0, 0u, lane);
+        else dq_tile<D>(lk0, lv0, lk16_0, qf, df, o, voff, c, lse2, f, drf, false, 0, 0u, lane);
         __syncthreads();
     };
     int t = 0;
@@ -368,18 +383,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_far_dq_kernel(BwdArgs a) {
     }
     if (t < ntile) step(Par<0>{}, t);
     if (!ok) return;
-    _Float16* dst = (_Float16*)a.part_dq + (prow * (size_t)a.kslots + slot) * D;
-#pragma unroll
-    for (int mb = 0; mb < T::DM; ++mb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int d0 = mb * 32 + 8 * j + 4 * hh;
-            if (d0 < D) {
-                _Float16 r[4] = {(_Float16)(o[mb][4 * j] * a.scale), (_Float16)(o[mb][4 * j + 1] * a.scale),
-                                 (_Float16)(o[mb][4 * j + 2] * a.scale), (_Float16)(o[mb][4 * j + 3] * a.scale)};
-                *(uint2*)(dst + d0) = *(const uint2*)r;
-            }
-        }
+    write_rows_bf16<D>(a.part_dq + (prow * (size_t)a.kslots + slot) * D, o, a.scale, es + sk, hh);
 }
 
 // Mask of an S tile in the key-centric layout (lane = key j, registers =
@@ -475,6 +479,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkv_kernel(BwdArgs a) {
     load_q<D, 1>(vf, &a.v, pkey * D, ok, hh);
     const float c = a.scale * kLog2e;
     const uint32_t wl = a.window > 0 ? (uint32_t)a.window : 0u;
+    const int es = a.es[bg];
+    const float f = ldexpf(1.f, -es);   // dS is taken as fp16(dS f)
     const int blk0 = a.B > 0 ? k0 / a.B : 0;
     const int kb = a.B > 0 ? min(key, N - 1) / a.B - blk0 : 0;   // 0 or 1 (B >= 64)
 
@@ -559,7 +565,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkv_kernel(BwdArgs a) {
         }
         s_ids[sl][lane] = rd.id;
         s_lse[sl][lane] = rd.id >= 0 ? rd.lse * kLog2e : INFINITY;
-        s_d[sl][lane] = rd.id >= 0 ? rd.d : 0.f;
+        s_d[sl][lane] = rd.id >= 0 ? rd.d * f : 0.f;   // D f
         s_info[sl][lane] = info;
     };
     auto gather = [&](int sl, uint16_t* q_, uint16_t* do_, uint16_t* q16_, uint16_t* do16_) __attribute__((always_inline)) {
@@ -595,7 +601,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkv_kernel(BwdArgs a) {
             for (int v = 0; v < 16; ++v) {
                 const int rr = sub * 32 + 8 * (v >> 2) + (v & 3) + 4 * hh;
                 p[sub][v] = fast_exp2(fmaf(s[sub][v], c, -s_lse[sl][rr]));
-                gds[sub][v] = p[sub][v] * (dp[sub][v] - s_d[sl][rr]);
+                gds[sub][v] = p[sub][v] * fmaf(dp[sub][v], f, -s_d[sl][rr]);
             }
         uint4 pb[4], db[4];
 #pragma unroll
@@ -650,8 +656,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkv_kernel(BwdArgs a) {
         if (i < n_tiles) step(Par<0>{}, i);
     }
     if (ok) {
-        write_rows_bf16<D>(a.dk + pkey * D, dk, a.scale, hh);
-        write_rows_bf16<D>(a.dv + pkey * D, dv, 1.f, hh);
+        write_rows_bf16<D>(a.dk + pkey * D, dk, a.scale, es + a.sq[bg], hh);
+        write_rows_bf16<D>(a.dv + pkey * D, dv, 1.f, a.sd[bg], hh);
     }
 }
 
@@ -667,6 +673,33 @@ static hipError_t bwd_d(const BwdArgs& a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dkv_kernel<D>), dim3(nt * a.Bt * a.Hkv), dim3(NTHREADS), 0, s, a);
+    return hipGetLastError();
+}
+
+// es per group from the largest |dO| and |v| (frexp: m < 2^e).
+__global__ void ds_exponent_kernel(const float* __restrict__ do_max, const float* __restrict__ v_max,
+                                   int32_t* es, int groups, int lg2d) {
+    const int g = blockIdx.x * blockDim.x + threadIdx.x;
+    if (g >= groups) return;
+    const float a = do_max[g], b = v_max[g];
+    int e = 0;
+    if (a > 0.f && b > 0.f && a < INFINITY && b < INFINITY) {
+        int ea, eb;
+        frexpf(a, &ea);
+        frexpf(b, &eb);
+        e = ea + eb + lg2d - 15;
+        e = max(-100, min(100, e));   // 2^-e stays a normal float
+    }
+    es[g] = e;
+}
+
+hipError_t launch_ds_exponent(const float* do_max, const float* v_max, int32_t* es, int groups,
+                              int D, hipStream_t s) {
+    if (groups == 0) return hipSuccess;
+    int lg2d = 0;
+    while ((1 << lg2d) < 2 * D) ++lg2d;   // ceil(log2(2 D))
+    hipLaunchKernelGGL(ds_exponent_kernel, dim3((unsigned)((groups + 255) / 256)), dim3(256), 0, s,
+                       do_max, v_max, es, groups, lg2d);
     return hipGetLastError();
 }
 

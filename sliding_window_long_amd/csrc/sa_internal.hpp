@@ -144,6 +144,12 @@ struct BwdArgs {
     const float* sink;      // [Hq] or nullptr
     float* dsink;           // [Hq] or nullptr
     float* sink_term;       // [Bt*Hq*N] per-row terms of dsink (with dsink)
+    // Power-of-two exponents per (batch, kv head): the fp16 copies hold
+    // q 2^-sq, k 2^-sk, dO 2^-sd; the fp16 score gradients dS 2^-es.
+    const int32_t* sq;
+    const int32_t* sk;
+    const int32_t* sd;
+    const int32_t* es;
     uint16_t* dq;
     uint16_t* dk;
     uint16_t* dv;
@@ -157,7 +163,7 @@ struct BwdArgs {
     const int32_t* chunk_start;
     const int32_t* n_chunks;
     int max_chunks;
-    uint16_t* part_dq;      // fp16 [Bt*Hq*N, kslots, D] far-block dq partials
+    uint16_t* part_dq;      // bf16 [Bt*Hq*N, kslots, D] far-block dq partials
     int top_k, B, n, span, kslots;
     int Bt, Hq, Hkv, N, D, window;
     float scale;
@@ -298,7 +304,6 @@ hipError_t launch_fill_i32(int32_t* p, int32_t value, size_t n, hipStream_t s);
 
 hipError_t launch_rows(const RowsArgs& a, int head_dim, int split, hipStream_t s);
 hipError_t launch_blocks(const BlocksArgs& a, int head_dim, int split, int grid, hipStream_t s);
-hipError_t launch_bf16_to_f16(const uint16_t* x, uint16_t* y, size_t n, hipStream_t s);
 // Row stride of the fp16 V copy that the forward's bf16 path reads: at d 80
 // rows of 96 whose columns 80..95 hold fp16 ones (the padding rows of O^T
 // then read ones and accumulate the row sums); otherwise D.
@@ -323,9 +328,17 @@ __host__ __device__ inline int f16_chunks(int rows) { return (rows + kF16ChunkRo
 // (fp8: the source holds OCP E4M3 values, decoded exactly.)
 hipError_t launch_f16_copy(const void* x, bool fp8, uint16_t* y, float* chunk_max, int heads,
                            int rows, int D, int SR, hipStream_t s);
+// group_max (optional): each group's largest |x|.  y may be null (maxima
+// and exponents only).
 hipError_t launch_f16_scale(const void* x, bool fp8, uint16_t* y, const float* chunk_max,
                             int32_t* scale, int groups, int hpg, int rows, int D, int SR,
-                            hipStream_t s);
+                            hipStream_t s, float* group_max = nullptr);
+// Exponent of the backward's fp16 score gradients per group:
+// es[g] = e(max|dO|) + e(max|V|) + ceil(log2(2 D)) - 15 with e(m) the
+// exponent for which m < 2^e (0 when either maximum is 0), so that
+// |dS| 2^-es < 2^15 (|dS| <= 2 D max|dO| max|V| for P <= 1).
+hipError_t launch_ds_exponent(const float* do_max, const float* v_max, int32_t* es, int groups,
+                              int D, hipStream_t s);
 hipError_t launch_split_f32(const float* x, uint16_t* hi, uint16_t* lo, size_t n, hipStream_t s);
 
 }  // namespace sa

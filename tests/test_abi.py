@@ -231,11 +231,16 @@ def test_backward_configs(lib):
     assert ws(sa.Params(1, 4, 1, 256, 128, window=8, token_top_k=16, index_dim=64)) == -8
     assert ws(sa.Params(1, 4, 4, 256, 64, window=8, cmp_block=8)) == -8
     assert ws(sa.Params(1, 4, 4, 1, 64, window=8, kv_len=256)) == -8                 # decode
-    # fp16 copies of q, k and dO plus the row deltas; no far partials
+    # fp16 copies of q, k and dO plus the row deltas; no far partials; then
+    # the copies' range data: per-128-row maxima of q, dO (4 heads) and k, v
+    # (2 kv heads), the largest |dO| and |v| and five exponents per kv head
+    # (each region rounded up to 256 bytes)
     p = sa.Params(1, 4, 2, 512, 64, window=16)
     n = ctypes.c_size_t()
     sa.load_library().sparse_attn_bwd_workspace_bytes(ctypes.byref(p.cfg()), ctypes.byref(n))
-    assert n.value == (2 * 512 * 64 * 2) + 2 * (4 * 512 * 64 * 2) + 4 * 512 * 4
+    a256 = lambda x: (x + 255) // 256 * 256
+    ranges = 2 * a256(4 * 4 * 4) + 2 * a256(2 * 4 * 4) + a256(2 * 2 * 4) + a256(2 * 5 * 4)
+    assert n.value == (2 * 512 * 64 * 2) + 2 * (4 * 512 * 64 * 2) + 4 * 512 * 4 + ranges
 
 
 def test_backward_rejects_before_launch(lib):

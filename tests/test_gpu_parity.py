@@ -310,7 +310,7 @@ def test_fp8_bitaxon_full_sampled(dev):
 
 
 # --- backward (window and block gating, bf16) -------------------------------
-def run_backward(inp, dev, seed):
+def run_backward(inp, dev, seed, do_scale=1.0):
     import torch
     import sliding_window_long_amd as sa
     wl = inp.wl
@@ -319,8 +319,8 @@ def run_backward(inp, dev, seed):
     kw = dict(block_size=wl.block_size, top_k=wl.top_k, window=wl.window, sink=g["sink"],
               gate_repr=wl.gate_repr, gate_shared=wl.gate_shared, gate_first=wl.gate_first)
     out, lse, bsel, _ = sa.forward(g["q"], g["k"], g["v"], return_selection=True, **kw)
-    dout = W._round(np.random.default_rng(seed).standard_normal(inp.q.shape, dtype=np.float32),
-                    "bf16")
+    dout = W._round(np.random.default_rng(seed).standard_normal(inp.q.shape, dtype=np.float32)
+                    * np.float32(do_scale), "bf16")
     dq, dk, dv, ds = sa.backward(g["q"], g["k"], g["v"], out, lse,
                                  torch.from_numpy(dout).to(torch.bfloat16).to(dev), **kw)
     torch.cuda.synchronize()
@@ -366,6 +366,35 @@ def test_backward_ragged(dev):
 
 def test_backward_bora_all_rows(dev):
     bwd_and_check(W.make_inputs(W.BORA_HYBRID, 102), dev, 83, label="bwd_bora")
+
+
+# Value ranges past fp16 for the backward's fp16 operands (q, k, dO and the
+# score gradients): (name, workload options, q scale, k scale, v scale, dO scale).
+BWD_RANGE_CASES = [
+    ("v_big", dict(window=64), 1.0, 1.0, 1e5, 1.0),
+    ("do_big_v_big", dict(block_size=64, top_k=3, window=40), 1.0, 1.0, 300.0, 1e3),
+    ("do_tiny", dict(window=64), 1.0, 1.0, 1.0, 1e-6),
+    ("v_tiny_do_tiny", dict(block_size=64, top_k=4), 1.0, 1.0, 1e-4, 1e-4),
+    ("q_big_k_tiny", dict(block_size=64, top_k=3, window=50), 1e5, 1e-5, 1.0, 1.0),
+]
+
+
+@pytest.mark.parametrize("case", range(len(BWD_RANGE_CASES)), ids=[c[0] for c in BWD_RANGE_CASES])
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_value_range(dev, case, d):
+    name, kw, qs, ks, vs, dos = BWD_RANGE_CASES[case]
+    wl = W.Workload("bwd_range_" + name, 1, 4, 2, 512, d, "bf16", sink=True,
+                    block_offsets="block_size" in kw, **kw)
+    inp = W.make_inputs(wl, 300 + case)
+    rb = lambda a, c: W._round(a * np.float32(c), "bf16")
+    inp = W.Inputs(wl, rb(inp.q, qs), rb(inp.k, ks), rb(inp.v, vs), inp.sink, None, None)
+    log(f"[gpu] bwd range {name} d={d}")
+    dout, bsel, grads = run_backward(inp, dev, 85 + case, do_scale=dos)
+    for x in grads:
+        assert x is None or np.isfinite(x).all()
+    res = check_grads(inp, dout, bsel, grads, sink=inp.sink, joint_floor=False)
+    log(f"[gpu] bwd range {name} d={d} " + " ".join(f"{k}: max {m:.2e} mean {a:.2e}" for k, (m, a) in res.items()))
+    assert grads_ok(res), str(res)
 
 
 def test_backward_deterministic(dev):

@@ -376,6 +376,32 @@ def test_grad_faults_fail(grad_case, name, kind):
     assert not grads_ok(res), (name, kind, res)
 
 
+def test_grad_per_tensor_floor(grad_case):
+    # A tensor 1e4 times smaller than the others: under the joint floor its
+    # 30% error hides below 1e-2 of the largest gradient; with its own floor
+    # the same error fails, and the clean gradients still pass.
+    inp, dout, sel, ref = grad_case
+    g = [x.astype(np.float64).copy() for x in ref]
+    r = [x.astype(np.float64).copy() for x in ref]
+    for t in (0,):
+        g[t] *= 1e-4
+        r[t] *= 1e-4
+    import parity
+
+    def check_scaled(grads, joint):
+        orig = parity.oracle.attend_bwd
+        parity.oracle.attend_bwd = lambda *a, **k: tuple(r)
+        try:
+            return check_grads(inp, dout, sel, grads, sink=inp.sink, joint_floor=joint)
+        finally:
+            parity.oracle.attend_bwd = orig
+    assert grads_ok(check_scaled(g, False))
+    bad = [x.copy() for x in g]
+    bad[0] *= 1.3
+    assert grads_ok(check_scaled(bad, True))
+    assert not grads_ok(check_scaled(bad, False))
+
+
 def test_token_selection_only_checker(tok_case, tok_tie_case):
     from parity import check_token_selection
     inp, (res, out, lse, _, tsel) = tok_case
