@@ -174,7 +174,7 @@ int make_plan(const sparse_attn_cfg* c, Plan* p, bool bwd = false) {
         long long span = 0;
         if (c->window > 0) span = ((long long)c->window - 1 + P.B - 1) / P.B;
         if (span > P.n) span = P.n;
-        if (span > 32 && c->window < P.N) return SA_E_UNSUPPORTED;
+        if (span > 64 && c->window < P.N) return SA_E_UNSUPPORTED;   // near-block masks of 64
         P.span = (int)span;
         P.kslots = P.top_k > 1 ? P.top_k - 1 : 1;
         P.lists = P.Bt * P.Hkv * P.n;
@@ -213,7 +213,7 @@ int make_plan(const sparse_attn_cfg* c, Plan* p, bool bwd = false) {
         P.o_bmax_v = take((size_t)P.Bt * P.Hkv * ch * 4);
         P.o_bgmax = take((size_t)P.Bt * P.Hkv * 2 * 4);
         P.o_bexp = take((size_t)P.Bt * P.Hkv * 5 * 4);
-        P.o_near = take(P.gate ? (size_t)rows * 4 : 0);
+        P.o_near = take(P.gate ? (size_t)rows * 8 : 0);
     } else {
         P.o_split = take(P.f32 ? 2 * (nq + 2 * nkv) * 2 : 0);
         // fp16 copy of V for the P V products (rows padded with ones at d 80)
@@ -787,7 +787,7 @@ int sparse_attn_bwd(const void* q, const void* k, const void* v, const void* out
     ba.sink_term = dsink ? (float*)(ws + P.o_sinkterm) : nullptr;
     ba.dq = (uint16_t*)dq; ba.dk = (uint16_t*)dk; ba.dv = (uint16_t*)dv;
     ba.sel = sel; ba.top_k = P.top_k; ba.B = P.B; ba.n = P.n; ba.span = P.span;
-    ba.near_mask = P.gate ? (uint32_t*)(ws + P.o_near) : nullptr;
+    ba.near_mask = P.gate ? (uint64_t*)(ws + P.o_near) : nullptr;
     ba.kslots = P.kslots;
     ba.list_off = P.far ? ca.list_off : nullptr; ba.entries = P.far ? ca.entries : nullptr;
     ba.entries_cap = P.far ? (int)P.max_entries : 0;

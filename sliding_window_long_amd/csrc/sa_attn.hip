@@ -16,6 +16,8 @@
 // ("슬라이딩 윈도우 마스크") joins the causal own-block pass.
 #include "sa_attn_common.hpp"
 
+#include <type_traits>
+
 namespace sa {
 
 // Epilogue of the query-centric kernels: combine the near part (o, row sum
@@ -134,7 +136,9 @@ __device__ __forceinline__ void finish_rows(const RowsArgs& a, f32x16 (&o)[Tile<
 // unit scales; the 16 dims past a multiple of 64 on the 32x32x16 FP8 op);
 // every E4M3 product is exact in the fp32 accumulator, as the bf16 products
 // of the decoded values would be.  K tiles hold fp8 rows of K8S<D>() bytes.
-template <int D, int SPLIT, bool TOK, bool QK8>
+// WIDE: the near-block mask holds 64 blocks (a window of 33..64 blocks
+// under block gating), else 32.
+template <int D, int SPLIT, bool TOK, bool QK8, bool WIDE = false>
 __global__ __launch_bounds__(NTHREADS, D <= 80 && SPLIT == 1 ? 3 : 2) void attn_rows_kernel(RowsArgs a) {
     using T = Tile<D>;
     constexpr bool ONES = T::DPAD > D;
@@ -178,8 +182,10 @@ __global__ __launch_bounds__(NTHREADS, D <= 80 && SPLIT == 1 ? 3 : 2) void attn_
 
     // Block-gate state of the row: its block, the kept near blocks as a bit
     // mask over (own block - 1 - bit), and the count of far blocks.
+    using NearT = typename std::conditional<WIDE, uint64_t, uint32_t>::type;
+    constexpr int kNear = WIDE ? 64 : 32;
     int row_blk = 0, nfar = 0;
-    uint32_t near_bits = 0;
+    NearT near_bits = 0;
     if (a.gate) {
         row_blk = (row_ok ? row : N - 1) / a.B;
         if (row_ok) {
@@ -189,7 +195,7 @@ __global__ __launch_bounds__(NTHREADS, D <= 80 && SPLIT == 1 ? 3 : 2) void attn_
                 if (cblk < 0) break;
                 const int dlt = row_blk - cblk;
                 if (dlt > a.span) ++nfar;
-                else if (dlt >= 1 && dlt <= 32) near_bits |= 1u << (dlt - 1);
+                else if (dlt >= 1 && dlt <= kNear) near_bits |= NearT(1) << (dlt - 1);
             }
         }
     }
@@ -257,7 +263,7 @@ __global__ __launch_bounds__(NTHREADS, D <= 80 && SPLIT == 1 ? 3 : 2) void attn_
                 uint32_t wl = wl_window;
                 if (a.gate) {
                     const int dlt = row_blk - kt0 / a.B;
-                    const bool blk_ok = dlt == 0 || (dlt >= 1 && dlt <= a.span && dlt <= 32 &&
+                    const bool blk_ok = dlt == 0 || (dlt >= 1 && dlt <= a.span && dlt <= kNear &&
                                                      ((near_bits >> (dlt - 1)) & 1u));
                     if (blk_ok) wl = 0x80000000u;
                 }
@@ -547,6 +553,8 @@ static hipError_t rows_d(const RowsArgs& a, hipStream_t s) {
     }
     if (a.tokmask)
         hipLaunchKernelGGL((attn_rows_kernel<D, SPLIT, true, false>), dim3(grid), dim3(NTHREADS), 0, s, a);
+    else if (a.gate && a.span > 32)
+        hipLaunchKernelGGL((attn_rows_kernel<D, SPLIT, false, false, true>), dim3(grid), dim3(NTHREADS), 0, s, a);
     else
         hipLaunchKernelGGL((attn_rows_kernel<D, SPLIT, false, false>), dim3(grid), dim3(NTHREADS), 0, s, a);
     return hipGetLastError();

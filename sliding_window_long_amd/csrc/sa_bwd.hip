@@ -59,12 +59,12 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdArgs a) {
         if (a.near_mask) {   // the row's kept near blocks, as the forward attends them
             const int rb = (int)(r % a.N) / a.B;
             const int32_t* sr = a.sel + r * a.top_k;
-            uint32_t nm = 0;
+            uint64_t nm = 0;
             for (int x = 0; x < a.top_k; ++x) {
                 const int cb = sr[x];
                 if (cb < 0) break;
                 const int dlt = rb - cb;
-                if (dlt >= 1 && dlt <= a.span && dlt <= 32) nm |= 1u << (dlt - 1);
+                if (dlt >= 1 && dlt <= a.span && dlt <= 64) nm |= 1ull << (dlt - 1);
             }
             a.near_mask[r] = nm;
         }
@@ -230,7 +230,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dq_kernel(BwdArgs a) {
     // attended here; far ones come as partials from bwd_far_dq.  nfar = the
     // row's far blocks (slots 0 .. nfar-1 of its partials).
     const int row_blk = a.sel ? min(row, N - 1) / a.B : 0;
-    const uint32_t near_bits = a.near_mask && ok ? a.near_mask[prow] : 0u;
+    const uint64_t near_bits = a.near_mask && ok ? a.near_mask[prow] : 0ull;
     int nfar = 0;
     if (a.sel && ok) {
         const int32_t* sr = a.sel + prow * a.top_k;
@@ -257,7 +257,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dq_kernel(BwdArgs a) {
         uint32_t wl = wl_window;
         if (a.sel) {
             const int dlt = row_blk - kt0 / a.B;
-            if (dlt == 0 || (dlt >= 1 && dlt <= 32 && ((near_bits >> (dlt - 1)) & 1u))) wl = 0x80000000u;
+            if (dlt == 0 || (dlt >= 1 && dlt <= 64 && ((near_bits >> (dlt - 1)) & 1u))) wl = 0x80000000u;
         }
         dq_tile<D>(lk, lv, lk16, qf, df, o, voff, c, lse2, f, drf, true, row - kt0 - 4 * hh, wl, lane);
     };
@@ -533,10 +533,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkv_kernel(BwdArgs a) {
     struct RowData {
         int id, rr;
         float lse, d;
-        uint32_t nm;
+        uint64_t nm;
     };
     auto fetch = [&](int i, int r, int ent) __attribute__((always_inline)) -> RowData {
-        RowData rd{-1, 0, 0.f, 0.f, 0u};
+        RowData rd{-1, 0, 0.f, 0.f, 0ull};
         if (i < n1) {
             const int hl = i / n_rt, rr = k0 + (i % n_rt) * KT + r;
             rd.rr = rr;
@@ -560,7 +560,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkv_kernel(BwdArgs a) {
 #pragma unroll
             for (int dl = 0; dl < 2; ++dl) {
                 const int dlt = rb - (blk0 + dl);
-                if (dlt == 0 || (dlt >= 1 && dlt <= 32 && ((rd.nm >> (dlt - 1)) & 1u))) info |= 1 << dl;
+                if (dlt == 0 || (dlt >= 1 && dlt <= 64 && ((rd.nm >> (dlt - 1)) & 1u))) info |= 1 << dl;
             }
         }
         s_ids[sl][lane] = rd.id;
@@ -628,7 +628,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkv_kernel(BwdArgs a) {
         auto step = [&](auto par, int i) __attribute__((always_inline)) {
             constexpr int PAR = decltype(par)::value;
             const bool ahead = wu == 0 && i + 2 < n_tiles;
-            RowData rd{-1, 0, 0.f, 0.f, 0u};
+            RowData rd{-1, 0, 0.f, 0.f, 0ull};
             int ent3 = -1;
             if (ahead) {   // loads first: their data is not needed before the barrier
                 rd = fetch(i + 2, lane, ent2);

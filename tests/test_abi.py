@@ -81,6 +81,7 @@ def code_of(params, **cfg_fields):
     (sa.Params(1, 4, 1, 256, 128, window=8, block_size=64, top_k=2, token_top_k=16,
                index_dim=64), -8),
     (sa.Params(1, 1, 1, 1 << 23, 128, window=8), -8),                # one head's K past 2 GiB
+    (sa.Params(1, 4, 4, 64 * 80, 64, block_size=64, top_k=3, window=64 * 65 + 1), -8),  # 65 near blocks
     (sa.Params(1, 4, 4, 256, 64, window=8, kv_len=255), -1),          # fewer keys than queries
     (sa.Params(1, 4, 4, 256, 64, window=8, kv_len=-1), -1),
     (sa.Params(1, 4, 4, 4, 64, block_size=64, top_k=2, kv_len=256), -8),  # decode with block gate

@@ -122,6 +122,20 @@ def test_gate_edges(dev, kw, d):
     run_and_check(W.make_inputs(wl, 11 + d), dev, label=f"gate_edge {kw}")
 
 
+@pytest.mark.parametrize("wl", [
+    # window of 41 blocks of 64 under the block gate (near blocks past 32)
+    W.Workload("gate_span41_d64", 1, 4, 2, 64 * 72, 64, "bf16", block_size=64, top_k=6,
+               window=64 * 40 + 10, block_offsets=True),
+    W.Workload("gate_span41_d128", 1, 4, 2, 64 * 72, 128, "bf16", block_size=64, top_k=6,
+               window=64 * 40 + 10, block_offsets=True, sink=True),
+    # the Bit-Axon window (4096) with blocks of 64: 64 near blocks
+    W.Workload("gate_span64", 1, 2, 2, 8192, 80, "bf16", block_size=64, top_k=8, window=4096,
+               block_offsets=True),
+], ids=lambda w: w.name)
+def test_gate_long_window(dev, wl):
+    run_and_check(W.make_inputs(wl, 14), dev, W.sample_rows(wl, 1024, 6), label=wl.name)
+
+
 def test_gate_wide_group(dev):
     wl = W.Workload("gqa16", 1, 16, 1, 1024, 80, "bf16", block_size=128, top_k=4, window=64,
                     block_offsets=True)
@@ -357,6 +371,13 @@ def test_backward_small(dev, case, d):
     kw = dict(BWD_SHAPES[case])
     wl = W.Workload("bwd_small", 2, 4, 2, 512, d, "bf16", block_offsets="block_size" in kw, **kw)
     bwd_and_check(W.make_inputs(wl, 71 + case + d), dev, 81 + case, label=f"bwd {kw}")
+
+
+def test_backward_long_window(dev):
+    # window of 36 blocks of 64 under the block gate (near blocks past 32)
+    wl = W.Workload("bwd_span36", 1, 4, 2, 64 * 48, 64, "bf16", block_size=64, top_k=5,
+                    window=64 * 36, block_offsets=True, sink=True)
+    bwd_and_check(W.make_inputs(wl, 74), dev, 86, label="bwd_span36")
 
 
 def test_backward_ragged(dev):
