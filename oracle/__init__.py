@@ -84,6 +84,7 @@ def _load(path=None):
     lib.orc_attend_at.restype = ctypes.c_int
     lib.orc_attend_bwd.argtypes = [_f32p, _f32p, _f32p, _f32p, _i64, _i64, _i64, _i64, _i64,
                                    ctypes.c_double, _i64, _i64, ctypes.c_void_p, _i64,
+                                   ctypes.c_void_p, _i64,
                                    ctypes.c_void_p, _f64p, _f64p, _f64p, _f64p]
     lib.orc_attend_bwd.restype = ctypes.c_int
     _lib = lib
@@ -316,9 +317,11 @@ def forward(q, k, v, *, block_size=0, top_k=0, window=0, idx_q=None, idx_k=None,
     return res
 
 
-def attend_bwd(q, k, v, dout, *, scale=None, window=0, block_size=0, sel=None, sink=None):
-    """Gradients of sum(dout * out) for a fixed selection: window and kept
-    blocks (sel [Bt*Hq*N, w] per row, or None), sink.  Returns dq
+def attend_bwd(q, k, v, dout, *, scale=None, window=0, block_size=0, sel=None, tsel=None,
+               sink=None):
+    """Gradients of sum(dout * out) for a fixed selection: window, kept
+    blocks (sel [Bt*Hq*N, w] per row, or None), kept tokens (tsel [Bt*N, w']
+    per position, shared by the heads, or None), sink.  Returns dq
     [Bt,Hq,N,d], dk, dv [Bt,Hkv,N,d] and dsink [Hq] (None without a sink),
     all fp64."""
     q, k, v, dout = _f32(q), _f32(k), _f32(v), _f32(dout)
@@ -332,6 +335,9 @@ def attend_bwd(q, k, v, dout, *, scale=None, window=0, block_size=0, sel=None, s
     sel_a = None if sel is None else np.ascontiguousarray(sel, dtype=np.int32)
     if sel_a is not None and sel_a.shape[0] != Bt * Hq * N:
         raise ValueError("sel holds one row per query row")
+    tsel_a = None if tsel is None else np.ascontiguousarray(tsel, dtype=np.int32)
+    if tsel_a is not None and tsel_a.shape[0] != Bt * N:
+        raise ValueError("tsel holds one row per position")
     sink_a = None if sink is None else _f32(sink)
     dq = np.empty((Bt, Hq, N, d), dtype=np.float64)
     dk = np.empty((Bt, Hkv, N, d), dtype=np.float64)
@@ -340,6 +346,7 @@ def attend_bwd(q, k, v, dout, *, scale=None, window=0, block_size=0, sel=None, s
     rc = _load().orc_attend_bwd(
         q, k, v, dout, Bt, Hq, Hkv, N, d, scale, int(window), int(block_size),
         None if sel_a is None else sel_a.ctypes.data, 0 if sel_a is None else sel_a.shape[1],
+        None if tsel_a is None else tsel_a.ctypes.data, 0 if tsel_a is None else tsel_a.shape[1],
         None if sink_a is None else sink_a.ctypes.data, dq, dk, dv, dsink)
     if rc != 0:
         raise ValueError("selection id out of range")
@@ -347,16 +354,20 @@ def attend_bwd(q, k, v, dout, *, scale=None, window=0, block_size=0, sel=None, s
 
 
 def backward(q, k, v, dout, *, block_size=0, top_k=0, window=0, sink=None, scale=None,
-             gate_repr="mean", gate_shared=False, gate_first=False):
-    """Gradients of sum(dout * out) of the prefill with block gating and a
-    window (the selection the forward makes, held fixed).  Returns (dq, dk,
-    dv, dsink, sel)."""
+             gate_repr="mean", gate_shared=False, gate_first=False, idx_q=None, idx_k=None,
+             token_top_k=0):
+    """Gradients of sum(dout * out) of the prefill with block gating or the
+    token gate and a window (the selection the forward makes, held fixed).
+    Returns (dq, dk, dv, dsink, sel), sel the block selection, or the token
+    selection [Bt*N, token_top_k] under the token gate."""
     Bt, Hq, N, d = np.shape(q)
-    sel = None
+    sel = tsel = None
     if top_k > 0:
         kb = block_pool(k, block_size, gate_repr)
         sel, _, _ = block_select(q, kb, block_size, top_k, None, gate_repr, gate_shared,
                                  gate_first)
+    if token_top_k > 0:
+        tsel, _, _ = token_select(idx_q, idx_k, token_top_k)
     dq, dk, dv, dsink = attend_bwd(q, k, v, dout, scale=scale, window=window,
-                                   block_size=block_size, sel=sel, sink=sink)
-    return dq, dk, dv, dsink, sel
+                                   block_size=block_size, sel=sel, tsel=tsel, sink=sink)
+    return dq, dk, dv, dsink, (tsel if token_top_k > 0 else sel)

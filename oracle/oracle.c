@@ -432,21 +432,26 @@ int orc_attend(const float* q, const float* k, const float* v,
 /*
  * Backward of the attention for a fixed selection (the gates' top-k choices
  * are not differentiated; MoBA trains through the attention of the chosen
- * blocks).  For every row i of A(i) (window and blocks, as orc_attend; no
- * token or compressed columns) with P_ij = e^(x_ij - lse_i), the sink
+ * blocks, and the DSA hybrid of the Naive-N0.5-Flash page through the
+ * attention of its window and selected tokens).  For every row i of A(i)
+ * (window, blocks and tokens, as orc_attend; no compressed columns) with
+ * P_ij = e^(x_ij - lse_i), the sink
  * column P_i0 = e^(z_h - lse_i), loss gradient dO_i:
  *   D_i   = sum_e dO_ie out_ie
  *   dS_ij = P_ij (<dO_i, v_j> - D_i)
  *   dq_i  = scale sum_j dS_ij k_j,   dk_j += scale dS_ij q_i,
  *   dv_j += P_ij dO_i,               dsink_h += -P_i0 D_i
  * (the softmax Jacobian; the sink's value vector is zero).  All rows of q
- * [Bt, Hq, N, d]; sel is [Bt*Hq*N, sel_w] or NULL; dk, dv [Bt, Hkv, N, d]
- * sum over the kv group's heads.  Returns 0, or -1 if an id is out of range.
+ * [Bt, Hq, N, d]; sel is [Bt*Hq*N, sel_w] or NULL; tsel is [Bt*N, tsel_w]
+ * token ids per position, shared by every head, or NULL; dk, dv [Bt, Hkv,
+ * N, d] sum over the kv group's heads.  Returns 0, or -1 if an id is out of
+ * range.
  */
 int orc_attend_bwd(const float* q, const float* k, const float* v, const float* dout,
                    int64_t Bt, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
                    double scale, int64_t window, int64_t B,
-                   const int32_t* sel, int64_t sel_w, const float* sink,
+                   const int32_t* sel, int64_t sel_w,
+                   const int32_t* tsel, int64_t tsel_w, const float* sink,
                    double* dq, double* dk, double* dv, double* dsink) {
     const int64_t G = Hq / Hkv;
     int bad = 0;
@@ -480,6 +485,13 @@ int orc_attend_bwd(const float* q, const float* k, const float* v, const float* 
                             if (c < 0) continue;
                             if (B <= 0 || c >= N / B) { bad = 1; continue; }
                             for (int64_t j = c * B; j < (c + 1) * B && j <= i; ++j) mark[j] = 1;
+                        }
+                    if (tsel)
+                        for (int64_t s = 0; s < tsel_w; ++s) {
+                            const int64_t j = tsel[(b * N + i) * tsel_w + s];
+                            if (j < 0) continue;
+                            if (j >= N) { bad = 1; continue; }
+                            if (j <= i) mark[j] = 1;
                         }
                     const float* qrow = q + r * d;
                     const float* dorow = dout + r * d;

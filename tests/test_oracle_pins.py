@@ -635,10 +635,11 @@ def test_p27_compressed_brute_force(case, ties):
 # Backward for a fixed selection (MoBA trains through the attention of the
 # chosen blocks; the top-k choice itself has no gradient).
 # ---------------------------------------------------------------------------
-def torch_dense_grads(q, k, v, dout, sel, B, window, sink):
+def torch_dense_grads(q, k, v, dout, sel, B, window, sink, tsel=None):
     """Autograd (fp64, CPU) of sum(dout * out) for the dense attention with
-    the boolean mask of window | kept blocks and the sink as an extra column
-    of zero value."""
+    the boolean mask of window | kept blocks | kept tokens (tsel per
+    position, shared by the heads) and the sink as an extra column of zero
+    value."""
     Bt, Hq, N, d = q.shape
     Hkv = k.shape[1]
     pos = np.arange(N)
@@ -654,6 +655,13 @@ def torch_dense_grads(q, k, v, dout, sel, B, window, sink):
                 for i in range(N):
                     kept = set(int(c) for c in s3[b, h, i] if c >= 0)
                     mask[b, h, i] |= np.isin(blk, list(kept)) & (pos <= i)
+    if tsel is not None:
+        t3 = tsel.reshape(Bt, N, -1)
+        for b in range(Bt):
+            for i in range(N):
+                for j in t3[b, i]:
+                    if 0 <= j <= i:
+                        mask[b, :, i, j] = True
     qt, kt, vt = (torch.tensor(a.astype(np.float64), requires_grad=True) for a in (q, k, v))
     zt = torch.tensor(sink.astype(np.float64), requires_grad=True) if sink is not None else None
     G = Hq // Hkv
@@ -723,6 +731,52 @@ def test_p29_backward_matches_finite_differences():
             args_p[key], args_m[key] = a_p, a_m
             fd = (loss(args_p["q"], args_p["k"], args_p["v"], args_p["z"]) -
                   loss(args_m["q"], args_m["k"], args_m["v"], args_m["z"])) / \
+                 (float(a_p[idx]) - float(a_m[idx]))
+            assert abs(fd - grad[idx]) <= 1e-5 * max(1.0, abs(grad[idx])), (name, idx, fd, grad[idx])
+
+
+# P28 with the token gate: the backward under a token selection (window 3,
+# top 5 of an indexer over 8 dims, sink) equals autograd of the dense
+# attention masked to window | kept tokens.
+def test_p28_token_backward_is_autograd():
+    Bt, Hq, Hkv, N, d = 2, 4, 2, 24, 8
+    q, k, v = rnd((Bt, Hq, N, d), 430), rnd((Bt, Hkv, N, d), 431), rnd((Bt, Hkv, N, d), 432)
+    dout, sink = rnd((Bt, Hq, N, d), 433), rnd((Hq,), 434)
+    iq, ik = rnd((Bt, N, 8), 435), rnd((Bt, N, 8), 436)
+    dq, dk, dv, dsink, tsel = oracle.backward(q, k, v, dout, window=3, sink=sink, idx_q=iq,
+                                              idx_k=ik, token_top_k=5)
+    assert tsel.shape == (Bt * N, 5)
+    tq, tk, tv, tz = torch_dense_grads(q, k, v, dout, None, 0, 3, sink, tsel=tsel)
+    for a, b_ in ((dq, tq), (dk, tk), (dv, tv), (dsink, tz)):
+        np.testing.assert_allclose(a, b_, atol=1e-12)
+
+
+# P29 with the token gate: finite differences of the forward under the
+# selection (held fixed) agree with the backward.
+def test_p29_token_backward_matches_finite_differences():
+    Bt, Hq, Hkv, N, d = 1, 2, 1, 14, 3
+    q, k, v = rnd((Bt, Hq, N, d), 440), rnd((Bt, Hkv, N, d), 441), rnd((Bt, Hkv, N, d), 442)
+    dout = rnd((Bt, Hq, N, d), 443)
+    iq, ik = rnd((Bt, N, 4), 444), rnd((Bt, N, 4), 445)
+    dq, dk, dv, _, tsel = oracle.backward(q, k, v, dout, window=2, idx_q=iq, idx_k=ik,
+                                          token_top_k=3)
+    rows_t = np.repeat(tsel.reshape(Bt, 1, N, -1), Hq, axis=1).reshape(Bt * Hq * N, -1)
+
+    def loss(q, k, v):
+        o, _, _ = oracle.attend(q, k, v, window=2, tsel=rows_t)
+        return float((o.reshape(dout.shape) * dout.astype(np.float64)).sum())
+
+    rng = np.random.default_rng(446)
+    for name, arr, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for _ in range(6):
+            idx = tuple(rng.integers(0, s_) for s_ in arr.shape)
+            a_p, a_m = arr.copy(), arr.copy()
+            a_p[idx] += np.float32(1e-3)
+            a_m[idx] -= np.float32(1e-3)
+            args_p = dict(q=q, k=k, v=v); args_m = dict(args_p)
+            args_p[name], args_m[name] = a_p, a_m
+            fd = (loss(**{kk: args_p[kk] for kk in ("q", "k", "v")}) -
+                  loss(**{kk: args_m[kk] for kk in ("q", "k", "v")})) / \
                  (float(a_p[idx]) - float(a_m[idx]))
             assert abs(fd - grad[idx]) <= 1e-5 * max(1.0, abs(grad[idx])), (name, idx, fd, grad[idx])
 
