@@ -221,7 +221,7 @@ GATE_VARIANTS = [W.LONG_MOBA.replace(name="long_moba_minmax_n131072", gate_repr=
 
 # Backward calls (gradients for the forward's selection) on the window and
 # block-gated shapes.
-BACKWARD = [W.BORA_HYBRID, W.BITAXON_SWA, W.LONG_MOBA]
+BACKWARD = [W.BORA_HYBRID, W.BITAXON_SWA, W.LONG_MOBA, W.SWA_TOKEN_TOPK]
 
 
 def time_backward(wl, seed, dev, steps, warmup):
@@ -231,8 +231,9 @@ def time_backward(wl, seed, dev, steps, warmup):
     import sliding_window_long_amd as sa
     inp, g = device_inputs(wl, seed, dev)
     kw = dict(block_size=wl.block_size, top_k=wl.top_k, window=wl.window, sink=g["sink"],
-              gate_repr=wl.gate_repr, gate_shared=wl.gate_shared, gate_first=wl.gate_first)
-    out, lse, bsel, _ = sa.forward(g["q"], g["k"], g["v"], return_selection=True, **kw)
+              gate_repr=wl.gate_repr, gate_shared=wl.gate_shared, gate_first=wl.gate_first,
+              idx_q=g["idx_q"], idx_k=g["idx_k"], token_top_k=wl.token_top_k)
+    out, lse, bsel, tsel = sa.forward(g["q"], g["k"], g["v"], return_selection=True, **kw)
     dout = torch.randn(g["q"].shape, dtype=torch.float32, device=dev,
                        generator=torch.Generator(device=dev).manual_seed(seed)).to(torch.bfloat16)
     ws = sa.Workspace()
@@ -240,7 +241,8 @@ def time_backward(wl, seed, dev, steps, warmup):
     def call():
         sa.backward(g["q"], g["k"], g["v"], out, lse, dout, workspace=ws, **kw)
     _, med, _, stage_ms = timed_calls(call, steps, warmup)
-    pairs = attended_pairs(wl, None if bsel is None else bsel.cpu().numpy())
+    pairs = attended_pairs(wl, None if bsel is None else bsel.cpu().numpy(),
+                           None if tsel is None else tsel.cpu().numpy())
     return med, stage_ms, pairs
 
 

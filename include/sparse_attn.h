@@ -210,8 +210,9 @@ int sparse_attn_block_pool(const void* k, const sparse_attn_cfg* cfg, float* kba
  * n_kv_heads, seq_len, head_dim]: bf16, device, 16-byte aligned; lse the
  * forward's fp32 lse; dsink [n_q_heads] fp32 or NULL (needs cfg->sink).
  * Supported: bf16 prefills with a window and/or block gating (any gate
- * variant); a token gate, the compressed branch, fp32 or a decode step
- * return SA_E_UNSUPPORTED.  The gradient products run on fp16 matrix cores
+ * variant) or the token gate (cfg->idx_q, cfg->idx_k as for the forward;
+ * the selection is recomputed and held fixed); the compressed branch, fp32
+ * or a decode step return SA_E_UNSUPPORTED.  The gradient products run on fp16 matrix cores
  * with fp16 copies of q, k and dout and fp16 score gradients dS_ij, each at
  * a power-of-two scale per (batch, kv head) chosen from the data (the rule
  * of the forward's V copy; for dS from the largest |dout| and |v|), undone

@@ -354,9 +354,9 @@ def block_pool(k, block_size: int, gate_repr: str = "mean"):
     return kbar
 
 
-def backward(q, k, v, out, lse, dout, *, block_size=0, top_k=0, window=0, sink=None, scale=None,
-             gate_repr="mean", gate_shared=False, gate_first=False,
-             workspace: Workspace | None = None):
+def backward(q, k, v, out, lse, dout, *, block_size=0, top_k=0, window=0, idx_q=None,
+             idx_k=None, token_top_k=0, sink=None, scale=None, gate_repr="mean",
+             gate_shared=False, gate_first=False, workspace: Workspace | None = None):
     """Gradients of the prefill for the selection the forward makes (same
     arguments as forward; out and lse are its results, dout the gradient of
     out).  bf16 tensors on one device; returns (dq, dk, dv, dsink), dsink
@@ -367,14 +367,18 @@ def backward(q, k, v, out, lse, dout, *, block_size=0, top_k=0, window=0, sink=N
           "the backward is a prefill: k, v over q's positions")
     _need(tuple(dout.shape) == tuple(q.shape) and dout.dtype == q.dtype and dout.is_contiguous(),
           "dout must be a contiguous tensor of q's shape and dtype")
-    _check_fwd_tensors(q, k, v, None, None, sink, out, lse, 0)
+    _check_fwd_tensors(q, k, v, idx_q, idx_k, sink, out, lse, token_top_k)
     _need(dout.is_cuda and dout.device == q.device, "dout must be on q's device")
-    p = params_for(q, k, block_size=block_size, top_k=top_k, window=window, scale=scale,
+    index_dim = idx_q.shape[-1] if idx_q is not None else 0
+    p = params_for(q, k, block_size=block_size, top_k=top_k, window=window,
+                   token_top_k=token_top_k, index_dim=index_dim, scale=scale,
                    gate_repr=gate_repr, gate_shared=gate_shared, gate_first=gate_first)
     cfg = p.cfg()
     dev = q.device
     if sink is not None:
         cfg.sink = sink.data_ptr()
+    if idx_q is not None:
+        cfg.idx_q, cfg.idx_k = idx_q.data_ptr(), idx_k.data_ptr()
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     dsink = None if sink is None else torch.empty_like(sink)
     nbytes = sparse_attn_bwd_workspace_bytes(cfg)

@@ -51,7 +51,7 @@ struct Plan {
     size_t o_sinkterm, o_bmax_q, o_bmax_do, o_bmax_k, o_bmax_v, o_bgmax, o_bexp;
     size_t o_split, o_kb3, o_sel, o_count, o_cursor, o_tilebase, o_listoff, o_listch, o_nchunks, o_chunk_list,
         o_chunk_start, o_entries, o_part_o, o_part_lse, o_tok_split, o_tok_state, o_tok_mask,
-        o_tok_qn, o_tok_win, o_tok_kpart, o_tok_scr, o_tok_nslow, o_dec_scores, o_dec_list,
+        o_tok_qn, o_tok_win, o_tok_kpart, o_tok_scr, o_tok_nslow, o_tok_maskT, o_dec_scores, o_dec_list,
         o_dec_nfar, o_dec_plist, o_dec_pcnt, o_dec_redo, o_dec_part, o_qsum, o_cmp_k, o_cmp_v,
         o_cmp_out, o_k16, o_q16, o_do16, o_delta, o_near, o_f8q, o_f8k, o_f8v, o_f8iq, o_f8ik,
         o_v16, o_vmax, o_vscale, total;
@@ -94,8 +94,7 @@ int make_plan(const sparse_attn_cfg* c, Plan* p, bool bwd = false) {
     // the token gate.
     if (c->cmp_block > 0 && c->token_top_k > 0) return SA_E_UNSUPPORTED;
     // The backward covers window and block gating on bf16 prefills.
-    if (bwd && (dec || c->dtype != SA_BF16 || c->token_top_k > 0 || c->cmp_block > 0))
-        return SA_E_UNSUPPORTED;
+    if (bwd && (dec || c->dtype != SA_BF16 || c->cmp_block > 0)) return SA_E_UNSUPPORTED;
     if (c->token_top_k > 0) {
         if (c->index_dim != 64) return SA_E_UNSUPPORTED_HEAD_DIM;
         // Block and token gates are separate methods and are not combined
@@ -269,6 +268,7 @@ int make_plan(const sparse_attn_cfg* c, Plan* p, bool bwd = false) {
         const size_t cands = (size_t)P.Bt * P.N * sa::kTokCap * 8;
         P.o_tok_scr = take(counts > cands ? counts : cands);
         P.o_tok_nslow = take(4);
+        P.o_tok_maskT = take(bwd ? (size_t)P.Bt * P.nt32 * ((P.N + 63) / 64) * 64 * 4 : 0);
     }
     P.qk8 = P.fp8 && !P.gate && !P.cmp;
     if (P.fp8) {
@@ -345,6 +345,47 @@ int select_blocks(const Plan& P, const void* q, const void* k, const uint16_t* c
     }
     StageScope t("block_gate", s);
     return ok(sa::launch_gate(ga, P.D, gate_split, P.gate_planes, P.gate_mm, s)) ? SA_OK : SA_E_HIP;
+}
+
+// Token gate: the per-query top-t token selection as the keep mask
+// (ta->mask), and the selected ids into cfg->token_sel_out when set.
+int select_tokens(const Plan& P, const sparse_attn_cfg* cfg, char* ws, int split, hipStream_t s,
+                  sa::TokArgs* out) {
+    auto ok = [](hipError_t e) { return e == hipSuccess; };
+    sa::TokArgs& ta = *out;
+    ta = sa::TokArgs{};
+    ta.iq[0] = (const uint16_t*)cfg->idx_q;
+    ta.ik[0] = (const uint16_t*)cfg->idx_k;
+    if (P.f32) {
+        const size_t nidx = (size_t)P.Bt * P.N * 64;
+        uint16_t* base = (uint16_t*)(ws + P.o_tok_split);
+        StageScope t("split_f32_indexer", s);
+        if (!ok(sa::launch_split_f32((const float*)cfg->idx_q, base, base + nidx, nidx, s)) ||
+            !ok(sa::launch_split_f32((const float*)cfg->idx_k, base + 2 * nidx, base + 3 * nidx,
+                                     nidx, s)))
+            return SA_E_HIP;
+        ta.iq[0] = base; ta.iq[1] = base + nidx;
+        ta.ik[0] = base + 2 * nidx; ta.ik[1] = base + 3 * nidx;
+    }
+    ta.Bt = P.Bt; ta.N = P.N; ta.top_t = P.top_t;
+    ta.state = (int4*)(ws + P.o_tok_state);
+    ta.mask = (uint16_t*)(ws + P.o_tok_mask);
+    ta.qn = (float*)(ws + P.o_tok_qn);
+    ta.win = (float2*)(ws + P.o_tok_win);
+    ta.kpart = (float*)(ws + P.o_tok_kpart);
+    ta.part = (uint32_t*)(ws + P.o_tok_scr);
+    ta.hits = (uint2*)(ws + P.o_tok_scr);
+    ta.nslow = (int*)(ws + P.o_tok_nslow);
+    ta.units = P.tok_units; ta.nkp = P.tok_nkp;
+    {
+        StageScope t("token_select", s);
+        if (!ok(sa::launch_token_select(ta, split, s))) return SA_E_HIP;
+    }
+    if (cfg->token_sel_out) {
+        StageScope t("token_list", s);
+        if (!ok(sa::launch_token_list(ta, cfg->token_sel_out, s))) return SA_E_HIP;
+    }
+    return SA_OK;
 }
 
 // Per-(batch, kv head, block) lists of the rows that keep that block as a
@@ -627,37 +668,8 @@ int sparse_attn_fwd(const void* q, const void* k, const void* v, const sparse_at
     const uint32_t* tokmask = nullptr;
     if (P.tok) {
         sa::TokArgs ta{};
-        ta.iq[0] = (const uint16_t*)cfg->idx_q;
-        ta.ik[0] = (const uint16_t*)cfg->idx_k;
-        if (P.f32) {
-            const size_t nidx = (size_t)P.Bt * P.N * 64;
-            uint16_t* base = (uint16_t*)(ws + P.o_tok_split);
-            StageScope t("split_f32_indexer", s);
-            if (!ok(sa::launch_split_f32((const float*)cfg->idx_q, base, base + nidx, nidx, s)) ||
-                !ok(sa::launch_split_f32((const float*)cfg->idx_k, base + 2 * nidx, base + 3 * nidx,
-                                         nidx, s)))
-                return SA_E_HIP;
-            ta.iq[0] = base; ta.iq[1] = base + nidx;
-            ta.ik[0] = base + 2 * nidx; ta.ik[1] = base + 3 * nidx;
-        }
-        ta.Bt = P.Bt; ta.N = P.N; ta.top_t = P.top_t;
-        ta.state = (int4*)(ws + P.o_tok_state);
-        ta.mask = (uint16_t*)(ws + P.o_tok_mask);
-        ta.qn = (float*)(ws + P.o_tok_qn);
-        ta.win = (float2*)(ws + P.o_tok_win);
-        ta.kpart = (float*)(ws + P.o_tok_kpart);
-        ta.part = (uint32_t*)(ws + P.o_tok_scr);
-        ta.hits = (uint2*)(ws + P.o_tok_scr);
-        ta.nslow = (int*)(ws + P.o_tok_nslow);
-        ta.units = P.tok_units; ta.nkp = P.tok_nkp;
-        {
-            StageScope t("token_select", s);
-            if (!ok(sa::launch_token_select(ta, split, s))) return SA_E_HIP;
-        }
-        if (cfg->token_sel_out) {
-            StageScope t("token_list", s);
-            if (!ok(sa::launch_token_list(ta, cfg->token_sel_out, s))) return SA_E_HIP;
-        }
+        const int rc_tok = select_tokens(P, cfg, ws, split, s, &ta);
+        if (rc_tok != SA_OK) return rc_tok;
         tokmask = (const uint32_t*)ta.mask;
     }
 
@@ -726,6 +738,12 @@ int sparse_attn_bwd(const void* q, const void* k, const void* v, const void* out
         misaligned(cfg->workspace, 16) || misaligned(lse, 4) || misaligned(dsink, 4) ||
         misaligned(cfg->sink, 4) || misaligned(cfg->block_sel_out, 4))
         return SA_E_ALIGNMENT;
+    if (P.tok) {
+        if (!cfg->idx_q || !cfg->idx_k) return SA_E_INVALID_ARG;
+        if (misaligned(cfg->idx_q, 16) || misaligned(cfg->idx_k, 16) ||
+            misaligned(cfg->token_sel_out, 4))
+            return SA_E_ALIGNMENT;
+    }
     if ((long long)P.Bt * P.Hq * P.N >= (1LL << 31)) return SA_E_UNSUPPORTED;   // 32-bit row ids
     if (P.total > 0 && (!cfg->workspace || cfg->workspace_bytes < P.total))
         return SA_E_WORKSPACE_TOO_SMALL;
@@ -745,6 +763,18 @@ int sparse_attn_bwd(const void* q, const void* k, const void* v, const void* out
             rc = compact_far(P, sel, ws, true, s, &ca);
             if (rc != SA_OK) return rc;
         }
+    }
+    // The forward's token selection (bit-identical), and its key-major copy.
+    const uint32_t *tokmask = nullptr, *tokmaskT = nullptr;
+    if (P.tok) {
+        sa::TokArgs ta{};
+        rc = select_tokens(P, cfg, ws, 1, s, &ta);
+        if (rc != SA_OK) return rc;
+        uint32_t* mt = (uint32_t*)(ws + P.o_tok_maskT);
+        StageScope t("bwd_token_mask", s);
+        if (!ok(sa::launch_token_mask_transpose(ta, mt, s))) return SA_E_HIP;
+        tokmask = (const uint32_t*)ta.mask;
+        tokmaskT = mt;
     }
     uint16_t* k16 = (uint16_t*)(ws + P.o_k16);
     uint16_t* q16 = (uint16_t*)(ws + P.o_q16);
@@ -782,6 +812,7 @@ int sparse_attn_bwd(const void* q, const void* k, const void* v, const void* out
     ba.out = (const uint16_t*)out; ba.dout = (const uint16_t*)dout;
     ba.q16 = q16; ba.k16 = k16; ba.do16 = do16;
     ba.sq = sq; ba.sk = sk; ba.sd = sd; ba.es = es;
+    ba.tokmask = tokmask; ba.tokmaskT = tokmaskT;
     ba.lse = lse; ba.delta = (float*)(ws + P.o_delta);
     ba.sink = cfg->sink; ba.dsink = dsink;
     ba.sink_term = dsink ? (float*)(ws + P.o_sinkterm) : nullptr;

@@ -19,6 +19,9 @@
 // bwd_delta  : D_i per row, and the sink gradient.
 // bwd_far_dq : far blocks' share of dQ, key-block-centric over the forward's
 //              compaction lists (gathered rows), as fp16 partials per slot.
+// Token gate: both passes walk every key or row that can be kept (all
+// earlier keys / all later rows), masked by the forward's keep mask (bwd_dq
+// reads it as the forward does, bwd_dkv a key-major copy) or the window.
 // bwd_dq     : query-centric (lane = query row): per 64-key tile S^T = K Q^T
 //              and dP^T = V dO^T on the matrix cores, P^T from the saved lse,
 //              dS^T, and dQ^T += K^T dS^T (K in fp16, P V-style product) over
@@ -170,11 +173,12 @@ __device__ __forceinline__ void dq_tile(const uint16_t* lk, const uint16_t* lv, 
                                         const bf16x8 (&qf)[1][Tile<D>::DK], const bf16x8 (&df)[1][Tile<D>::DK],
                                         f32x16 (&o)[Tile<D>::DM], const int (&voff)[Tile<D>::DM],
                                         float c, float lse2, float f, float drf, bool masked, int rk,
-                                        uint32_t wl, int lane) {
+                                        uint32_t wl, int lane, bool tok = false, uint32_t tword = 0u) {
     f32x16 s[2], dp[2];
     qk_tile<D, 1>(lk, qf, s, lane);
     qk_tile<D, 1>(lv, df, dp, lane);
-    if (masked) mask_tile(s, rk, wl);
+    if (tok) mask_tile_tok(s, rk, wl, wl != 0u, tword);
+    else if (masked) mask_tile(s, rk, wl);
     uint4 pb[4], db[4];
     p_ds(s, dp, c, lse2, f, drf, pb, db);
     const uint4 zero4[4] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0),
@@ -197,7 +201,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dq_kernel(BwdArgs a) {
     const int wu = __builtin_amdgcn_readfirstlane(wave);
     const int N = a.N;
     const int ntiles = (N + RT - 1) / RT;
-    const int bh = blockIdx.x / ntiles, rtile = blockIdx.x % ntiles;
+    const bool tok = a.tokmask != nullptr;
+    const int bh = blockIdx.x / ntiles;
+    // token gate: the longest row tiles (every earlier key) first
+    const int rtile = tok ? ntiles - 1 - (int)(blockIdx.x % ntiles) : (int)(blockIdx.x % ntiles);
     const int b = bh / a.Hq, h = bh % a.Hq, g = h / (a.Hq / a.Hkv);
     const int r0 = rtile * RT;
     const int r_hi = min(r0 + RT - 1, N - 1);
@@ -211,6 +218,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dq_kernel(BwdArgs a) {
     int lo = r0;
     if (a.window > 0) lo = min(lo, r0 - a.window + 1);
     if (a.sel) lo = min(lo, (r0 / a.B - a.span) * a.B);
+    if (tok) lo = 0;   // kept tokens can be anywhere before the row
     const int t_begin = max(lo, 0) / KT, t_end = r_hi / KT;
     const int n_t = t_end - t_begin + 1;
     DT dt;
@@ -250,10 +258,23 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dq_kernel(BwdArgs a) {
     for (int mb = 0; mb < T::DM; ++mb) voff[mb] = v_lane_offset<D, DT::VS>(lane, mb);
     __syncthreads();
 
-    // Mask of tile t: window keys, and every causal key of a kept block.
+    // Mask of tile t: window keys, and every causal key of a kept block or
+    // every kept token.
+    const int nt32 = (N + 31) / 32, nt64 = (N + KT - 1) / KT, rt32 = q0 / 32;
     auto compute = [&](int t, const uint16_t* lk, const uint16_t* lv, const uint16_t* lk16)
                        __attribute__((always_inline)) {
         const int kt0 = t * KT;
+        if (tok) {
+            // this lane's keep word of key tile t (none past the wave's rows;
+            // the half past the row tile is not written)
+            uint32_t tw = t <= rt32 / 2 && q0 < N
+                              ? a.tokmask[(((size_t)b * nt32 + rt32) * nt64 + t) * 64 + lane]
+                              : 0u;
+            if (2 * t + 1 > rt32) tw &= 0xffffu;
+            dq_tile<D>(lk, lv, lk16, qf, df, o, voff, c, lse2, f, drf, true, row - kt0 - 4 * hh,
+                       wl_window, lane, true, tw);
+            return;
+        }
         uint32_t wl = wl_window;
         if (a.sel) {
             const int dlt = row_blk - kt0 / a.B;
@@ -402,6 +423,19 @@ __device__ __forceinline__ void mask_rows(f32x16 (&s)[2], int rj, uint32_t w, co
         }
 }
 
+// Token-gate mask of an S tile in the key-centric layout: keep iff the
+// keep-mask word has bit 16*sub + v, or (unsigned)(i - j) < w (the window).
+__device__ __forceinline__ void mask_rows_tok(f32x16 (&s)[2], int rj, uint32_t w, uint32_t word) {
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int cv = sub * 32 + 8 * (v >> 2) + (v & 3);
+            const bool keep = ((word >> (16 * sub + v)) & 1u) || (uint32_t)(rj + cv) < w;
+            if (!keep) s[sub][v] = -INFINITY;
+        }
+}
+
 // Lane offsets of a gathered 64-row tile in an LDS image of row stride S
 // (the layout of TileDma): instruction j of this wave writes chunk p = 64 i +
 // lane, i = min(wave + NWAVES j, S/8 - 1), of row p / (S/8); chunks past the
@@ -499,9 +533,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkv_kernel(BwdArgs a) {
 
     // The row tiles: n_rt contiguous tiles per head of the group, then the
     // far lists of the keys' (at most two) blocks.
+    const bool tok = a.tokmaskT != nullptr;
     int r_end = a.window > 0 ? min(N - 1, k_hi + a.window - 1) : -1;
     if (a.sel) r_end = max(r_end, min(N - 1, (k_hi / a.B + a.span + 1) * a.B - 1));
+    if (tok) r_end = N - 1;   // every later row can keep these keys
     const int n_rt = r_end >= k0 ? (r_end - k0) / KT + 1 : 0;
+    const int nt32k = (N + 31) / 32, nt64k = (N + KT - 1) / KT;   // key-major mask tiles
     const int n1 = G * n_rt;
     // (Scalars, not arrays: a runtime-indexed array would live in scratch,
     // whose loads wait for every tile load in flight.)
@@ -590,6 +627,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkv_kernel(BwdArgs a) {
 #pragma unroll
                     for (int v = 0; v < 16; ++v) s[sub][v] = -INFINITY;
             }
+        } else if (tok) {
+            // keep word of (this wave's 32 keys, the tile's 64 rows, lane)
+            const int rt0 = k0 + (i % n_rt) * KT;
+            const uint32_t tw = j0 < N   // a wave past the last key keeps nothing
+                                    ? a.tokmaskT[(((size_t)b * nt32k + j0 / 32) * nt64k + rt0 / KT) * 64 + lane]
+                                    : 0u;
+            mask_rows_tok(s, rt0 + 4 * hh - key, wl, tw);
         } else {
             const int rt0 = k0 + (i % n_rt) * KT;
             mask_rows(s, rt0 + 4 * hh - key, wl, s_info[sl], kb, hh);

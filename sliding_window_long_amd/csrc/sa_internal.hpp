@@ -154,6 +154,10 @@ struct BwdArgs {
     uint16_t* dk;
     uint16_t* dv;
     const int32_t* sel;     // [Bt*Hq*N, top_k] or nullptr (no block gate)
+    // Token gate (else nullptr): the forward's keep mask (query-major, the
+    // layout the forward reads) and its key-major copy.
+    const uint32_t* tokmask;
+    const uint32_t* tokmaskT;
     uint64_t* near_mask;    // [Bt*Hq*N]: bit dlt-1 = block (own - dlt) kept as a near
                             // block (1 <= dlt <= min(span, 64)); nullptr without gate
     const int32_t* list_off;  // far-row lists of the compaction, or nullptr
@@ -294,6 +298,9 @@ hipError_t launch_decode_attn(const DecArgs& a, hipStream_t s);
 
 hipError_t launch_token_select(const TokArgs& a, int split, hipStream_t s);
 hipError_t launch_token_list(const TokArgs& a, int32_t* out, hipStream_t s);
+// Key-major copy of the keep mask (the backward's key-centric pass):
+// [Bt][N/32 key groups][N/64 row tiles][64 lanes] words.
+hipError_t launch_token_mask_transpose(const TokArgs& a, uint32_t* maskT, hipStream_t s);
 
 hipError_t launch_pool(const PoolArgs& a, int head_dim, bool f32_in, int lists, hipStream_t s);
 hipError_t launch_gate(const GateArgs& a, int head_dim, int qsplit, int planes, bool minmax,

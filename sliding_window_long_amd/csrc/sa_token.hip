@@ -833,6 +833,75 @@ hipError_t launch_token_select(const TokArgs& a, int split, hipStream_t s) {
     return hipSuccess;
 }
 
+// Key-major copy of the keep mask for the backward's key-centric pass: for
+// the 32 keys kc*32 .. kc*32+31, the 64 rows rt*64 .. rt*64+63 and lane L,
+// word maskT[((bt*NT32 + kc)*NT64 + rt)*64 + L] has bit 16*sub + v set iff
+// row rt*64 + 32*sub + 8*(v/4) + 4*(L/32) + v%4 keeps key kc*32 + L%32 (the
+// register layout of S = Q K^T with lane = key).  One workgroup (128
+// threads) per (batch, 64-row tile, run of up to 16 64-key tiles): each
+// 64 x 64 block goes through LDS as row bitmaps.  Blocks wholly above the
+// diagonal are zero; the mask halves the forward layout leaves unwritten
+// are read as zero.
+constexpr int kTransRun = 16;
+__global__ __launch_bounds__(128) void tok_mask_transpose_kernel(TokArgs a, uint32_t* maskT) {
+    __shared__ uint32_t rowbits[64][2];
+    const int tid = threadIdx.x;
+    const int rt = blockIdx.y, bt = blockIdx.z;
+    const int nt32 = (a.N + 31) / 32, nt64 = (a.N + 63) / 64;
+    const uint32_t* mask32 = (const uint32_t*)a.mask;
+    const int kt_begin = blockIdx.x * kTransRun;
+    for (int kt = kt_begin; kt < min(kt_begin + kTransRun, nt64); ++kt) {
+        // Read: thread t takes forward word (row tile 2 rt + t / 64, key tile
+        // kt, lane t % 64): row 32 (t / 64) + t % 32 of the block, the keys
+        // 32 sub + 8 (v / 4) + 4 hh + v % 4 with hh = (t / 32) % 2.
+        const int r32 = 2 * rt + tid / 64, L = tid & 63, hh = L >> 5;
+        uint32_t w = 0;
+        if (kt <= r32 / 2 && r32 < nt32) {
+            w = mask32[(((size_t)bt * nt32 + r32) * nt64 + kt) * 64 + L];
+            if (2 * kt + 1 > r32) w &= 0xffffu;   // the half past the row tile
+        }
+        uint32_t lo = 0, hi = 0;   // keys 0..31, 32..63 of the block
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int kl = 8 * (v >> 2) + 4 * hh + (v & 3);
+            lo |= ((w >> v) & 1u) << kl;
+            hi |= ((w >> (16 + v)) & 1u) << kl;
+        }
+        // Lanes L and L ^ 32 hold the two key halves of the same row.
+        lo |= (uint32_t)__shfl_xor((int)lo, 32);
+        hi |= (uint32_t)__shfl_xor((int)hi, 32);
+        __syncthreads();   // the previous block's reads of rowbits are done
+        if (hh == 0) {
+            const int row = 32 * (tid / 64) + (L & 31);
+            rowbits[row][0] = lo;
+            rowbits[row][1] = hi;
+        }
+        __syncthreads();
+        // Write: thread t makes word (key group 2 kt + t / 64, row tile rt,
+        // lane t % 64).
+        const int kc = 2 * kt + tid / 64, col = L & 31;
+        if (kc < nt32) {
+            uint32_t o = 0;
+#pragma unroll
+            for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int row = 32 * sub + 8 * (v >> 2) + (v & 3) + 4 * hh;
+                    o |= ((rowbits[row][tid / 64] >> col) & 1u) << (16 * sub + v);
+                }
+            maskT[(((size_t)bt * nt32 + kc) * nt64 + rt) * 64 + L] = o;
+        }
+    }
+}
+
+hipError_t launch_token_mask_transpose(const TokArgs& a, uint32_t* maskT, hipStream_t s) {
+    const int nt64 = (a.N + 63) / 64;
+    if (a.Bt == 0 || nt64 == 0) return hipSuccess;
+    const dim3 grid((unsigned)((nt64 + kTransRun - 1) / kTransRun), (unsigned)nt64, (unsigned)a.Bt);
+    hipLaunchKernelGGL(tok_mask_transpose_kernel, grid, dim3(128), 0, s, a, maskT);
+    return hipGetLastError();
+}
+
 hipError_t launch_token_list(const TokArgs& a, int32_t* out, hipStream_t s) {
     const int total = a.Bt * a.N;
     hipLaunchKernelGGL(token_list_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a,

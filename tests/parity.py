@@ -192,16 +192,19 @@ def check_token_selection(inp, dev_tsel, trows) -> Report:
 GRAD_MAX, GRAD_MEAN = 2e-2, 1e-2
 
 
-def check_grads(inp, dout, dev_sel, dev_grads, *, sink=None, joint_floor=True):
+def check_grads(inp, dout, dev_sel, dev_grads, *, sink=None, joint_floor=True, dev_tsel=None):
     """Compare device (dq, dk, dv, dsink) with the oracle's backward under the
     device's own block selection.  Returns {name: (max_rel, mean_rel)}.
     joint_floor=False floors each tensor at 1e-2 of its own largest |g*|
     instead (inputs whose gradients differ by orders of magnitude between
-    tensors, where the joint floor would leave the small ones unchecked)."""
+    tensors, where the joint floor would leave the small ones unchecked).
+    dev_tsel: the device's token selection ([Bt, N, top_t]) under the token
+    gate, held fixed like the block selection."""
     wl = inp.wl
     sel = None if dev_sel is None else dev_sel.reshape(-1, wl.top_k)
+    tsel = None if dev_tsel is None else dev_tsel.reshape(-1, wl.token_top_k)
     ref = oracle.attend_bwd(inp.q, inp.k, inp.v, dout, window=wl.window,
-                            block_size=wl.block_size, sel=sel, sink=sink)
+                            block_size=wl.block_size, sel=sel, tsel=tsel, sink=sink)
     joint_max = max(float(np.abs(r).max()) for r in ref[:3])
     joint_mean = max(float(np.abs(r).mean()) for r in ref[:3])
     res = {}

@@ -229,7 +229,7 @@ def test_backward_configs(lib):
     assert ws(sa.Params(2, 8, 4, 4096, 128, block_size=128, top_k=16, window=512)) == 0
     assert ws(sa.Params(1, 32, 32, 16384, 80, window=4096)) == 0
     assert ws(sa.Params(1, 2, 2, 512, 64, dtype=sa.SA_F32, window=8)) == -8           # fp32
-    assert ws(sa.Params(1, 4, 1, 256, 128, window=8, token_top_k=16, index_dim=64)) == -8
+    assert ws(sa.Params(1, 4, 1, 256, 128, window=8, token_top_k=16, index_dim=64)) == 0
     assert ws(sa.Params(1, 4, 4, 256, 64, window=8, cmp_block=8)) == -8
     assert ws(sa.Params(1, 4, 4, 1, 64, window=8, kv_len=256)) == -8                 # decode
     # fp16 copies of q, k and dO plus the row deltas; no far partials; then
@@ -255,6 +255,17 @@ def test_backward_rejects_before_launch(lib):
     assert f(dsink=0x9000) == -1               # a sink gradient without a sink
     assert f(q=0x1008) == -5                   # misaligned
     assert f() == -6                           # no workspace
+    # the token gate: the indexer tensors are required and checked too
+    p = sa.Params(1, 4, 1, 256, 64, window=8, token_top_k=16, index_dim=64)
+    assert f() == -1                           # no idx_q / idx_k
+    cfg = p.cfg()
+    cfg.idx_q, cfg.idx_k = 0x20000, 0x30008
+    g = lambda c: sa.load_library().sparse_attn_bwd(
+        *[ctypes.c_void_p(0x1000 * (i + 1)) for i in range(6)], ctypes.byref(c),
+        *[ctypes.c_void_p(0x8000 * (i + 1)) for i in range(3)], ctypes.c_void_p(0))
+    assert g(cfg) == -5                        # misaligned idx_k
+    cfg.idx_k = 0x30000
+    assert g(cfg) == -6                        # no workspace
 
 
 def test_fp8_workspace(lib):

@@ -331,23 +331,28 @@ def run_backward(inp, dev, seed, do_scale=1.0):
     t = inp.tensors()
     g = {k_: (None if v_ is None else v_.to(dev)) for k_, v_ in t.items()}
     kw = dict(block_size=wl.block_size, top_k=wl.top_k, window=wl.window, sink=g["sink"],
-              gate_repr=wl.gate_repr, gate_shared=wl.gate_shared, gate_first=wl.gate_first)
-    out, lse, bsel, _ = sa.forward(g["q"], g["k"], g["v"], return_selection=True, **kw)
+              gate_repr=wl.gate_repr, gate_shared=wl.gate_shared, gate_first=wl.gate_first,
+              idx_q=g["idx_q"], idx_k=g["idx_k"], token_top_k=wl.token_top_k)
+    out, lse, bsel, tsel = sa.forward(g["q"], g["k"], g["v"], return_selection=True, **kw)
     dout = W._round(np.random.default_rng(seed).standard_normal(inp.q.shape, dtype=np.float32)
                     * np.float32(do_scale), "bf16")
     dq, dk, dv, ds = sa.backward(g["q"], g["k"], g["v"], out, lse,
                                  torch.from_numpy(dout).to(torch.bfloat16).to(dev), **kw)
     torch.cuda.synchronize()
     grads = tuple(None if x is None else x.float().cpu().numpy() for x in (dq, dk, dv, ds))
-    return dout, (None if bsel is None else bsel.cpu().numpy()), grads
+    sel = tsel if wl.token_top_k else bsel
+    return dout, (None if sel is None else sel.cpu().numpy()), grads
 
 
 def bwd_and_check(inp, dev, seed, label):
     log(f"[gpu] {label} {inp.wl}")
-    dout, bsel, grads = run_backward(inp, dev, seed)
+    dout, sel, grads = run_backward(inp, dev, seed)
     for x in grads:
         assert x is None or np.isfinite(x).all()
-    res = check_grads(inp, dout, bsel, grads, sink=inp.sink)
+    if inp.wl.token_top_k:
+        res = check_grads(inp, dout, None, grads, sink=inp.sink, dev_tsel=sel)
+    else:
+        res = check_grads(inp, dout, sel, grads, sink=inp.sink)
     log(f"[gpu] {label} " + " ".join(f"{k}: max {m:.2e} mean {a:.2e}" for k, (m, a) in res.items()))
     assert grads_ok(res), str(res)
     return grads
@@ -378,6 +383,24 @@ def test_backward_long_window(dev):
     wl = W.Workload("bwd_span36", 1, 4, 2, 64 * 48, 64, "bf16", block_size=64, top_k=5,
                     window=64 * 36, block_offsets=True, sink=True)
     bwd_and_check(W.make_inputs(wl, 74), dev, 86, label="bwd_span36")
+
+
+@pytest.mark.parametrize("N,top_t,window,sink", [
+    (1, 4, 1, False), (300, 16, 8, True), (1000, 100, 128, True), (1500, 40, 1, False),
+    (2048, 300, 64, True)])
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_token_gate(dev, N, top_t, window, sink, d):
+    # the token gate's selection (shared by the heads, GQA 4/1), held fixed
+    wl = W.Workload("bwd_tok", 1, 4, 1, N, d, "bf16", window=window, token_top_k=top_t,
+                    index_dim=64, sink=sink)
+    bwd_and_check(W.make_inputs(wl, 91 + N + d), dev, 92 + N, label=f"bwd_tok N={N} k={top_t}")
+
+
+def test_backward_token_reduced(dev):
+    # the Naive SWA + DSA shape at N = 4096 (16 q heads on 4 kv heads, window
+    # 128, top 2048 tokens, sink)
+    wl = W.SWA_TOKEN_TOPK.replace(name="bwd_tok_n4096", seq_len=4096)
+    bwd_and_check(W.make_inputs(wl, 93), dev, 94, label="bwd_tok_n4096")
 
 
 def test_backward_ragged(dev):
