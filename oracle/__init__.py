@@ -85,7 +85,8 @@ def _load(path=None):
     lib.orc_attend_bwd.argtypes = [_f32p, _f32p, _f32p, _f32p, _i64, _i64, _i64, _i64, _i64,
                                    ctypes.c_double, _i64, _i64, ctypes.c_void_p, _i64,
                                    ctypes.c_void_p, _i64,
-                                   ctypes.c_void_p, _f64p, _f64p, _f64p, _f64p]
+                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, _i64,
+                                   _f64p, _f64p, _f64p, _f64p]
     lib.orc_attend_bwd.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -318,12 +319,13 @@ def forward(q, k, v, *, block_size=0, top_k=0, window=0, idx_q=None, idx_k=None,
 
 
 def attend_bwd(q, k, v, dout, *, scale=None, window=0, block_size=0, sel=None, tsel=None,
-               sink=None):
+               sink=None, cmp_block=0):
     """Gradients of sum(dout * out) for a fixed selection: window, kept
     blocks (sel [Bt*Hq*N, w] per row, or None), kept tokens (tsel [Bt*N, w']
-    per position, shared by the heads, or None), sink.  Returns dq
-    [Bt,Hq,N,d], dk, dv [Bt,Hkv,N,d] and dsink [Hq] (None without a sink),
-    all fp64."""
+    per position, shared by the heads, or None), sink, and with cmp_block > 0
+    the compressed columns (see compress; their gradient reaches k and v
+    through the group means).  Returns dq [Bt,Hq,N,d], dk, dv [Bt,Hkv,N,d]
+    and dsink [Hq] (None without a sink), all fp64."""
     q, k, v, dout = _f32(q), _f32(k), _f32(v), _f32(dout)
     Bt, Hq, N, d = q.shape
     Hkv = k.shape[1]
@@ -339,6 +341,9 @@ def attend_bwd(q, k, v, dout, *, scale=None, window=0, block_size=0, sel=None, t
     if tsel_a is not None and tsel_a.shape[0] != Bt * N:
         raise ValueError("tsel holds one row per position")
     sink_a = None if sink is None else _f32(sink)
+    kc = vc = None
+    if cmp_block:
+        kc, vc = compress(k, cmp_block), compress(v, cmp_block)
     dq = np.empty((Bt, Hq, N, d), dtype=np.float64)
     dk = np.empty((Bt, Hkv, N, d), dtype=np.float64)
     dv = np.empty((Bt, Hkv, N, d), dtype=np.float64)
@@ -347,7 +352,9 @@ def attend_bwd(q, k, v, dout, *, scale=None, window=0, block_size=0, sel=None, t
         q, k, v, dout, Bt, Hq, Hkv, N, d, scale, int(window), int(block_size),
         None if sel_a is None else sel_a.ctypes.data, 0 if sel_a is None else sel_a.shape[1],
         None if tsel_a is None else tsel_a.ctypes.data, 0 if tsel_a is None else tsel_a.shape[1],
-        None if sink_a is None else sink_a.ctypes.data, dq, dk, dv, dsink)
+        None if sink_a is None else sink_a.ctypes.data,
+        None if kc is None else kc.ctypes.data, None if vc is None else vc.ctypes.data,
+        int(cmp_block), dq, dk, dv, dsink)
     if rc != 0:
         raise ValueError("selection id out of range")
     return dq, dk, dv, (dsink if sink is not None else None)
@@ -355,11 +362,12 @@ def attend_bwd(q, k, v, dout, *, scale=None, window=0, block_size=0, sel=None, t
 
 def backward(q, k, v, dout, *, block_size=0, top_k=0, window=0, sink=None, scale=None,
              gate_repr="mean", gate_shared=False, gate_first=False, idx_q=None, idx_k=None,
-             token_top_k=0):
+             token_top_k=0, cmp_block=0):
     """Gradients of sum(dout * out) of the prefill with block gating or the
-    token gate and a window (the selection the forward makes, held fixed).
-    Returns (dq, dk, dv, dsink, sel), sel the block selection, or the token
-    selection [Bt*N, token_top_k] under the token gate."""
+    token gate and a window, and the compressed columns when cmp_block > 0
+    (the selection the forward makes, held fixed).  Returns (dq, dk, dv,
+    dsink, sel), sel the block selection, or the token selection
+    [Bt*N, token_top_k] under the token gate."""
     Bt, Hq, N, d = np.shape(q)
     sel = tsel = None
     if top_k > 0:
@@ -369,5 +377,6 @@ def backward(q, k, v, dout, *, block_size=0, top_k=0, window=0, sink=None, scale
     if token_top_k > 0:
         tsel, _, _ = token_select(idx_q, idx_k, token_top_k)
     dq, dk, dv, dsink = attend_bwd(q, k, v, dout, scale=scale, window=window,
-                                   block_size=block_size, sel=sel, tsel=tsel, sink=sink)
+                                   block_size=block_size, sel=sel, tsel=tsel, sink=sink,
+                                   cmp_block=cmp_block)
     return dq, dk, dv, dsink, (tsel if token_top_k > 0 else sel)

@@ -434,7 +434,7 @@ int orc_attend(const float* q, const float* k, const float* v,
  * are not differentiated; MoBA trains through the attention of the chosen
  * blocks, and the DSA hybrid of the Naive-N0.5-Flash page through the
  * attention of its window and selected tokens).  For every row i of A(i)
- * (window, blocks and tokens, as orc_attend; no compressed columns) with
+ * (window, blocks and tokens, as orc_attend) with
  * P_ij = e^(x_ij - lse_i), the sink
  * column P_i0 = e^(z_h - lse_i), loss gradient dO_i:
  *   D_i   = sum_e dO_ie out_ie
@@ -446,14 +446,25 @@ int orc_attend(const float* q, const float* k, const float* v,
  * token ids per position, shared by every head, or NULL; dk, dv [Bt, Hkv,
  * N, d] sum over the kv group's heads.  Returns 0, or -1 if an id is out of
  * range.
+ *
+ * Compressed columns (C > 0; kc, vc the group means, as orc_attend_at): each
+ * visible group c of row i is one more column of the same softmax, so with
+ * P_ic = e^(scale <q_i, kc_c> - lse_i) it adds
+ *   dS_ic = P_ic (<dO_i, vc_c> - D_i),  dq_i += scale dS_ic kc_c,
+ *   dkc_c += scale dS_ic q_i,           dvc_c += P_ic dO_i,
+ * and, kc_c and vc_c being means of C tokens, every token j of group c
+ * receives dkc_c / C in dk_j and dvc_c / C in dv_j (the chain rule through
+ * the mean; tokens past the last complete group receive nothing).
  */
 int orc_attend_bwd(const float* q, const float* k, const float* v, const float* dout,
                    int64_t Bt, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
                    double scale, int64_t window, int64_t B,
                    const int32_t* sel, int64_t sel_w,
                    const int32_t* tsel, int64_t tsel_w, const float* sink,
+                   const double* kc, const double* vc, int64_t C,
                    double* dq, double* dk, double* dv, double* dsink) {
     const int64_t G = Hq / Hkv;
+    const int64_t Nc = C > 0 ? N / C : 0;
     int bad = 0;
     for (int64_t h = 0; h < Hq; ++h) dsink[h] = 0.0;
     memset(dk, 0, sizeof(double) * (size_t)(Bt * Hkv * N * d));
@@ -465,13 +476,19 @@ int orc_attend_bwd(const float* q, const float* k, const float* v, const float* 
         double* x = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
         double* o = (double*)malloc(sizeof(double) * (size_t)(d > 0 ? d : 1));
         double* ds_h = (double*)calloc((size_t)Hq, sizeof(double));
+        double* xc = (double*)malloc(sizeof(double) * (size_t)(Nc > 0 ? Nc : 1));
+        double* dkc = (double*)malloc(sizeof(double) * (size_t)(Nc > 0 ? Nc * d : 1));
+        double* dvc = (double*)malloc(sizeof(double) * (size_t)(Nc > 0 ? Nc * d : 1));
 #pragma omp for schedule(dynamic, 1)
         for (int64_t bg = 0; bg < Bt * Hkv; ++bg) {
             const int64_t b = bg / Hkv, g = bg % Hkv;
             const float* kb = k + bg * N * d;
             const float* vb = v + bg * N * d;
+            const double* kcb = Nc > 0 ? kc + bg * Nc * d : NULL;
+            const double* vcb = Nc > 0 ? vc + bg * Nc * d : NULL;
             double* dkb = dk + bg * N * d;
             double* dvb = dv + bg * N * d;
+            for (int64_t e = 0; e < Nc * d; ++e) dkc[e] = dvc[e] = 0.0;
             for (int64_t h = g * G; h < (g + 1) * G; ++h)
                 for (int64_t i = 0; i < N; ++i) {
                     const int64_t r = (b * Hq + h) * N + i;
@@ -504,6 +521,14 @@ int orc_attend_bwd(const float* q, const float* k, const float* v, const float* 
                         x[j] = scale * acc;
                         if (x[j] > M) M = x[j];
                     }
+                    /* compressed groups c with (c+1)C - 1 <= i */
+                    const int64_t nvis = C > 0 ? (i + 1) / C : 0;
+                    for (int64_t c = 0; c < nvis; ++c) {
+                        double acc = 0.0;
+                        for (int64_t e = 0; e < d; ++e) acc += (double)qrow[e] * kcb[c * d + e];
+                        xc[c] = scale * acc;
+                        if (xc[c] > M) M = xc[c];
+                    }
                     const double z = sink ? (double)sink[h] : -INFINITY;
                     if (z > M) M = z;
                     double L = 0.0;
@@ -513,6 +538,11 @@ int orc_attend_bwd(const float* q, const float* k, const float* v, const float* 
                         const double p = exp(x[j] - M);
                         L += p;
                         for (int64_t e = 0; e < d; ++e) o[e] += p * (double)vb[j * d + e];
+                    }
+                    for (int64_t c = 0; c < nvis; ++c) {
+                        const double p = exp(xc[c] - M);
+                        L += p;
+                        for (int64_t e = 0; e < d; ++e) o[e] += p * vcb[c * d + e];
                     }
                     if (sink) L += exp(z - M);
                     const double lse = M + log(L);
@@ -533,7 +563,24 @@ int orc_attend_bwd(const float* q, const float* k, const float* v, const float* 
                             dvb[j * d + e] += p * (double)dorow[e];
                         }
                     }
+                    for (int64_t c = 0; c < nvis; ++c) {
+                        const double p = exp(xc[c] - lse);
+                        double dp = 0.0;
+                        for (int64_t e = 0; e < d; ++e) dp += (double)dorow[e] * vcb[c * d + e];
+                        const double dsic = p * (dp - Di);
+                        for (int64_t e = 0; e < d; ++e) {
+                            dqr[e] += scale * dsic * kcb[c * d + e];
+                            dkc[c * d + e] += scale * dsic * (double)qrow[e];
+                            dvc[c * d + e] += p * (double)dorow[e];
+                        }
+                    }
                     if (sink) ds_h[h] += -exp(z - lse) * Di;
+                }
+            /* through the means: token j of group c gets 1/C of its gradient */
+            for (int64_t j = 0; j < Nc * C; ++j)
+                for (int64_t e = 0; e < d; ++e) {
+                    dkb[j * d + e] += dkc[(j / C) * d + e] / (double)C;
+                    dvb[j * d + e] += dvc[(j / C) * d + e] / (double)C;
                 }
         }
 #pragma omp critical
@@ -542,6 +589,9 @@ int orc_attend_bwd(const float* q, const float* k, const float* v, const float* 
         free(x);
         free(o);
         free(ds_h);
+        free(xc);
+        free(dkc);
+        free(dvc);
     }
     return bad ? -1 : 0;
 }

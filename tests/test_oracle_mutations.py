@@ -37,10 +37,31 @@ MUTATIONS = [
                                     "const int64_t c0 = 0;\n        for (int64_t c = 0; c < n; ++c)"),
                                    ("const int64_t c0 = (first && own > 0 && top_k >= 2) ? 1 : 0;",
                                     "const int64_t c0 = 0;\n            if (first && own > 0) sel[t * top_k] = 0;")]),
-    ("compressed group seen one token early", [("const int64_t nvis = C > 0 ? (i + 1) / C : 0;",
-                                                "const int64_t nvis = C > 0 ? (i + 2) / C : 0;")]),
-    ("compressed value is its key", [("o[e] += p * vcb[c * d + e];", "o[e] += p * kcb[c * d + e];")]),
-    ("compressed logit unscaled", [("xc[c] = scale * acc;", "xc[c] = acc;")]),
+    ("compressed group seen one token early", [("\n            const int64_t nvis = C > 0 ? (i + 1) / C : 0;",
+                                                "\n            const int64_t nvis = C > 0 ? (i + 2) / C : 0;")]),
+    ("compressed value is its key", [("\n                for (int64_t e = 0; e < d; ++e) o[e] += p * vcb[c * d + e];",
+                                      "\n                for (int64_t e = 0; e < d; ++e) o[e] += p * kcb[c * d + e];")]),
+    ("compressed logit unscaled", [("\n                xc[c] = scale * acc;", "\n                xc[c] = acc;")]),
+    ("backward compressed group seen one token late", [
+        ("\n                    const int64_t nvis = C > 0 ? (i + 1) / C : 0;",
+         "\n                    const int64_t nvis = C > 0 ? i / C : 0;")]),
+    ("backward compressed logit unscaled", [("\n                        xc[c] = scale * acc;",
+                                             "\n                        xc[c] = acc;")]),
+    ("backward compressed columns left out of the forward", [
+        ("const double p = exp(xc[c] - M);\n                        L += p;",
+         "const double p = 0.0 * exp(xc[c] - M);\n                        L += p;")]),
+    ("backward compressed score gradient drops D", [("const double dsic = p * (dp - Di);",
+                                                     "const double dsic = p * dp;")]),
+    ("backward compressed dv from the query", [("dvc[c * d + e] += p * (double)dorow[e];",
+                                                "dvc[c * d + e] += p * (double)qrow[e];")]),
+    ("backward compressed dq from the group's value", [("dqr[e] += scale * dsic * kcb[c * d + e];",
+                                                        "dqr[e] += scale * dsic * vcb[c * d + e];")]),
+    ("backward group gradient not shared over its tokens", [
+        ("dkb[j * d + e] += dkc[(j / C) * d + e] / (double)C;",
+         "dkb[j * d + e] += dkc[(j / C) * d + e];")]),
+    ("backward group value gradient to the next group", [
+        ("dvb[j * d + e] += dvc[(j / C) * d + e] / (double)C;",
+         "dvb[j * d + e] += dvc[((j / C + 1) % Nc) * d + e] / (double)C;")]),
     ("compressed columns not counted", [("if (xc[c] > M) M = xc[c];\n                ++cnt;",
                                          "if (xc[c] > M) M = xc[c];")]),
     ("backward drops the D term", [("const double dsij = p * (dp - Di);", "const double dsij = p * dp;")]),
@@ -109,7 +130,13 @@ PIN_CALLS = [
     (lambda c=c: pins.test_p28_backward_is_autograd(c)) for c in range(len(pins.BWD_CASES))
 ] + [
     lambda: pins.test_p29_backward_matches_finite_differences(),
-    lambda: pins.test_p30_key_gradients_sum_to_sink_term(True),
+    lambda: pins.test_p30_key_gradients_sum_to_sink_term(True, 0),
+] + [
+    (lambda c=c: pins.test_p28_compressed_backward_is_autograd(c))
+    for c in range(len(pins.CMP_BWD_CASES))
+] + [
+    lambda: pins.test_p29_compressed_backward_matches_finite_differences(),
+    lambda: pins.test_p30_key_gradients_sum_to_sink_term(True, 8),
 ] + [
     (lambda c=c, n=n: pins.test_p15_decode_is_last_prefill_rows(c, n))
     for c in range(len(pins.DECODE_CASES)) for n in (1, 5)

@@ -635,11 +635,14 @@ def test_p27_compressed_brute_force(case, ties):
 # Backward for a fixed selection (MoBA trains through the attention of the
 # chosen blocks; the top-k choice itself has no gradient).
 # ---------------------------------------------------------------------------
-def torch_dense_grads(q, k, v, dout, sel, B, window, sink, tsel=None):
+def torch_dense_grads(q, k, v, dout, sel, B, window, sink, tsel=None, cmp_block=0):
     """Autograd (fp64, CPU) of sum(dout * out) for the dense attention with
     the boolean mask of window | kept blocks | kept tokens (tsel per
     position, shared by the heads) and the sink as an extra column of zero
-    value."""
+    value.  cmp_block = C > 0 adds the compressed columns: torch means of
+    each complete group of C keys and values (taken from the leaf tensors,
+    so autograd carries their gradient back through the mean), group c
+    visible to row i iff (c+1)C - 1 <= i."""
     Bt, Hq, N, d = q.shape
     Hkv = k.shape[1]
     pos = np.arange(N)
@@ -668,12 +671,23 @@ def torch_dense_grads(q, k, v, dout, sel, B, window, sink, tsel=None):
     kr, vr = kt.repeat_interleave(G, dim=1), vt.repeat_interleave(G, dim=1)
     logits = torch.matmul(qt, kr.transpose(-1, -2)) / math.sqrt(d)
     logits = logits.masked_fill(~torch.from_numpy(mask), -math.inf)
+    cols, vals = [logits], [vr]
+    if cmp_block:
+        C = cmp_block
+        Nc = N // C
+        kc = kt[:, :, :Nc * C].reshape(Bt, Hkv, Nc, C, d).mean(dim=3)
+        vc = vt[:, :, :Nc * C].reshape(Bt, Hkv, Nc, C, d).mean(dim=3)
+        lc = torch.matmul(qt, kc.repeat_interleave(G, dim=1).transpose(-1, -2)) / math.sqrt(d)
+        vis = (np.arange(Nc)[None, :] + 1) * C - 1 <= pos[:, None]
+        cols.append(lc.masked_fill(~torch.from_numpy(vis), -math.inf))
+        vals.append(vc.repeat_interleave(G, dim=1))
     if zt is not None:
-        col = zt.view(1, Hq, 1, 1).expand(Bt, Hq, N, 1)
-        p = torch.softmax(torch.cat([logits, col], dim=-1), dim=-1)[..., :N]
-    else:
-        p = torch.softmax(logits, dim=-1)
-    out = torch.matmul(p, vr)
+        cols.append(zt.view(1, Hq, 1, 1).expand(Bt, Hq, N, 1))
+    p = torch.softmax(torch.cat(cols, dim=-1), dim=-1)
+    out, at = 0, 0
+    for val in vals:
+        out = out + torch.matmul(p[..., at:at + val.shape[2]], val)
+        at += val.shape[2]
     (out * torch.from_numpy(dout.astype(np.float64))).sum().backward()
     return (qt.grad.numpy(), kt.grad.numpy(), vt.grad.numpy(),
             None if zt is None else zt.grad.numpy())
@@ -781,21 +795,84 @@ def test_p29_token_backward_matches_finite_differences():
             assert abs(fd - grad[idx]) <= 1e-5 * max(1.0, abs(grad[idx])), (name, idx, fd, grad[idx])
 
 
+# P28 with the compressed columns: the backward with groups of C tokens
+# (C = 1: every token is also its own group; C = 5 and 4 leave a ragged
+# tail that no group covers) next to a window, block gating and a sink
+# equals autograd through torch's group means.
+CMP_BWD_CASES = [
+    dict(window=3, cmp_block=4, sink=True),
+    dict(window=1, cmp_block=1),
+    dict(window=2, block_size=4, top_k=2, cmp_block=5, sink=True),
+    dict(window=4, block_size=4, top_k=3, cmp_block=4, gate_shared=True),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CMP_BWD_CASES)))
+def test_p28_compressed_backward_is_autograd(case):
+    kw = dict(CMP_BWD_CASES[case])
+    use_sink = kw.pop("sink", False)
+    Bt, Hq, Hkv, N, d = 2, 4, 2, 24, 8
+    if case == 0:
+        N = 26   # two tokens past the last group of 4
+    q, k, v = rnd((Bt, Hq, N, d), 450 + case), rnd((Bt, Hkv, N, d), 455 + case), rnd((Bt, Hkv, N, d), 460)
+    dout = rnd((Bt, Hq, N, d), 465 + case)
+    sink = rnd((Hq,), 470) if use_sink else None
+    dq, dk, dv, dsink, sel = oracle.backward(q, k, v, dout, sink=sink, **kw)
+    tq, tk, tv, tz = torch_dense_grads(q, k, v, dout, sel, kw.get("block_size", 0),
+                                       kw.get("window", 0), sink, cmp_block=kw["cmp_block"])
+    for a, b_ in ((dq, tq), (dk, tk), (dv, tv)):
+        np.testing.assert_allclose(a, b_, atol=1e-12)
+    if use_sink:
+        np.testing.assert_allclose(dsink, tz, atol=1e-12)
+
+
+# P29 with the compressed columns: finite differences of the oracle's
+# forward (groups of 5 over 12 tokens, window 2, kept blocks held fixed).
+def test_p29_compressed_backward_matches_finite_differences():
+    Bt, Hq, Hkv, N, d, B, C = 1, 2, 1, 12, 3, 3, 5
+    q, k, v = rnd((Bt, Hq, N, d), 475), rnd((Bt, Hkv, N, d), 476), rnd((Bt, Hkv, N, d), 477)
+    dout, sink = rnd((Bt, Hq, N, d), 478), rnd((Hq,), 479)
+    dq, dk, dv, dsink, sel = oracle.backward(q, k, v, dout, block_size=B, top_k=2, window=2,
+                                             sink=sink, cmp_block=C)
+
+    def loss(q_, k_, v_, z_):
+        o, _, _ = oracle.attend(q_, k_, v_, window=2, block_size=B, sel=sel, sink=z_, cmp_block=C)
+        return float((o.reshape(dout.shape) * dout.astype(np.float64)).sum())
+
+    rng = np.random.default_rng(480)
+    for name, arr, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv), ("sink", sink, dsink)):
+        for _ in range(8):
+            idx = tuple(rng.integers(0, s_) for s_ in arr.shape)
+            a_p, a_m = arr.copy(), arr.copy()
+            a_p[idx] += np.float32(1e-3)
+            a_m[idx] -= np.float32(1e-3)
+            args_p = dict(q=q, k=k, v=v, z=sink); args_m = dict(args_p)
+            key = {"q": "q", "k": "k", "v": "v", "sink": "z"}[name]
+            args_p[key], args_m[key] = a_p, a_m
+            fd = (loss(args_p["q"], args_p["k"], args_p["v"], args_p["z"]) -
+                  loss(args_m["q"], args_m["k"], args_m["v"], args_m["z"])) / \
+                 (float(a_p[idx]) - float(a_m[idx]))
+            assert abs(fd - grad[idx]) <= 1e-5 * max(1.0, abs(grad[idx])), (name, idx, fd, grad[idx])
+
+
 # P30: shifting all logits of a row leaves its output unchanged, so the
 # score gradients of a row sum to minus that of its sink column: summed over
 # the keys of a kv group, dk = scale * sum_i q_i P_i,sink D_i (zero without a
 # sink).
-@pytest.mark.parametrize("use_sink", [False, True])
-def test_p30_key_gradients_sum_to_sink_term(use_sink):
+# With the compressed columns (C = 8) the identity holds unchanged: a
+# group's key gradient reaches its C tokens in equal parts.
+@pytest.mark.parametrize("use_sink,cmp_block", [(False, 0), (True, 0), (True, 8)])
+def test_p30_key_gradients_sum_to_sink_term(use_sink, cmp_block):
     Bt, Hq, Hkv, N, d = 2, 4, 2, 32, 8
     q, k, v = rnd((Bt, Hq, N, d), 390), rnd((Bt, Hkv, N, d), 391), rnd((Bt, Hkv, N, d), 392)
     dout = rnd((Bt, Hq, N, d), 393)
     sink = rnd((Hq,), 394) if use_sink else None
     dq, dk, dv, dsink, sel = oracle.backward(q, k, v, dout, block_size=4, top_k=3, window=4,
-                                             sink=sink)
+                                             sink=sink, cmp_block=cmp_block)
     want = np.zeros((Bt, Hkv, d))
     if use_sink:
-        o, lse, _ = oracle.attend(q, k, v, window=4, block_size=4, sel=sel, sink=sink)
+        o, lse, _ = oracle.attend(q, k, v, window=4, block_size=4, sel=sel, sink=sink,
+                                  cmp_block=cmp_block)
         o, lse = o.reshape(Bt, Hq, N, d), lse.reshape(Bt, Hq, N)
         D = (o * dout).sum(-1)
         p0 = np.exp(sink[None, :, None] - lse)
