@@ -219,9 +219,10 @@ GATE_VARIANTS = [W.LONG_MOBA.replace(name="long_moba_minmax_n131072", gate_repr=
                  W.BITAXON_SWA.replace(name="bitaxon_swa_n16384_fp8", dtype="fp8")]
 
 
-# Backward calls (gradients for the forward's selection) on the window and
-# block-gated shapes.
-BACKWARD = [W.BORA_HYBRID, W.BITAXON_SWA, W.LONG_MOBA, W.SWA_TOKEN_TOPK]
+# Backward calls (gradients for the forward's selection) on the window,
+# block-gated, token-gated and compressed-branch shapes.
+BACKWARD = [W.BORA_HYBRID, W.BITAXON_SWA, W.LONG_MOBA, W.SWA_TOKEN_TOPK,
+            W.BORA_HYBRID.replace(name="bora_nsa_n4096", cmp_block=8, gate_shared=True)]
 
 
 def time_backward(wl, seed, dev, steps, warmup):
@@ -232,7 +233,8 @@ def time_backward(wl, seed, dev, steps, warmup):
     inp, g = device_inputs(wl, seed, dev)
     kw = dict(block_size=wl.block_size, top_k=wl.top_k, window=wl.window, sink=g["sink"],
               gate_repr=wl.gate_repr, gate_shared=wl.gate_shared, gate_first=wl.gate_first,
-              idx_q=g["idx_q"], idx_k=g["idx_k"], token_top_k=wl.token_top_k)
+              idx_q=g["idx_q"], idx_k=g["idx_k"], token_top_k=wl.token_top_k,
+              cmp_block=wl.cmp_block)
     out, lse, bsel, tsel = sa.forward(g["q"], g["k"], g["v"], return_selection=True, **kw)
     dout = torch.randn(g["q"].shape, dtype=torch.float32, device=dev,
                        generator=torch.Generator(device=dev).manual_seed(seed)).to(torch.bfloat16)

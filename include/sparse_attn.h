@@ -157,7 +157,8 @@ typedef struct {
     int32_t gate_shared;    /* 0 or 1: one block selection per kv group; 0 unless top_k > 0 */
     int32_t gate_first;     /* 0 or 1: block 0 always kept (top_k >= 2); 0 unless top_k > 0 */
     int32_t cmp_block;      /* tokens per compressed key/value (the BORA card's 8); 0 = no
-                               compressed branch.  Prefill only, not with token_top_k */
+                               compressed branch.  Prefill (and its backward) only, not
+                               with token_top_k */
 } sparse_attn_cfg;
 
 /* Bytes of device workspace sparse_attn_fwd needs for this configuration
@@ -211,8 +212,12 @@ int sparse_attn_block_pool(const void* k, const sparse_attn_cfg* cfg, float* kba
  * forward's fp32 lse; dsink [n_q_heads] fp32 or NULL (needs cfg->sink).
  * Supported: bf16 prefills with a window and/or block gating (any gate
  * variant) or the token gate (cfg->idx_q, cfg->idx_k as for the forward;
- * the selection is recomputed and held fixed); the compressed branch, fp32
- * or a decode step return SA_E_UNSUPPORTED.  The gradient products run on fp16 matrix cores
+ * the selection is recomputed and held fixed), and the compressed branch
+ * (cmp_block = C: each visible group c adds the column of its K and V means,
+ * and its gradients dkc_c = scale sum_i dS_ic q_i, dvc_c = sum_i P_ic dout_i
+ * reach each of its C tokens as dkc_c / C and dvc_c / C, the chain rule
+ * through the mean); fp32 or a decode step return SA_E_UNSUPPORTED.  The
+ * gradient products run on fp16 matrix cores
  * with fp16 copies of q, k and dout and fp16 score gradients dS_ij, each at
  * a power-of-two scale per (batch, kv head) chosen from the data (the rule
  * of the forward's V copy; for dS from the largest |dout| and |v|), undone

@@ -356,11 +356,12 @@ def block_pool(k, block_size: int, gate_repr: str = "mean"):
 
 def backward(q, k, v, out, lse, dout, *, block_size=0, top_k=0, window=0, idx_q=None,
              idx_k=None, token_top_k=0, sink=None, scale=None, gate_repr="mean",
-             gate_shared=False, gate_first=False, workspace: Workspace | None = None):
+             gate_shared=False, gate_first=False, cmp_block=0,
+             workspace: Workspace | None = None):
     """Gradients of the prefill for the selection the forward makes (same
-    arguments as forward; out and lse are its results, dout the gradient of
-    out).  bf16 tensors on one device; returns (dq, dk, dv, dsink), dsink
-    None without a sink."""
+    arguments as forward, the compressed branch included; out and lse are
+    its results, dout the gradient of out).  bf16 tensors on one device;
+    returns (dq, dk, dv, dsink), dsink None without a sink."""
     import torch
     _need(q.dtype == torch.bfloat16, "the backward takes bfloat16 tensors", TypeError)
     _need(q.dim() == 4 and k.dim() == 4 and k.shape[2] == q.shape[2],
@@ -372,7 +373,8 @@ def backward(q, k, v, out, lse, dout, *, block_size=0, top_k=0, window=0, idx_q=
     index_dim = idx_q.shape[-1] if idx_q is not None else 0
     p = params_for(q, k, block_size=block_size, top_k=top_k, window=window,
                    token_top_k=token_top_k, index_dim=index_dim, scale=scale,
-                   gate_repr=gate_repr, gate_shared=gate_shared, gate_first=gate_first)
+                   gate_repr=gate_repr, gate_shared=gate_shared, gate_first=gate_first,
+                   cmp_block=cmp_block)
     cfg = p.cfg()
     dev = q.device
     if sink is not None:

@@ -48,7 +48,7 @@ struct Plan {
     int Nk, dec_cmax;
     float scale;
     // workspace regions (byte offsets)
-    size_t o_sinkterm, o_bmax_q, o_bmax_do, o_bmax_k, o_bmax_v, o_bgmax, o_bexp;
+    size_t o_sinkterm, o_bmax_q, o_bmax_do, o_bmax_k, o_bmax_v, o_bgmax, o_bexp, o_cmp_grad;
     size_t o_split, o_kb3, o_sel, o_count, o_cursor, o_tilebase, o_listoff, o_listch, o_nchunks, o_chunk_list,
         o_chunk_start, o_entries, o_part_o, o_part_lse, o_tok_split, o_tok_state, o_tok_mask,
         o_tok_qn, o_tok_win, o_tok_kpart, o_tok_scr, o_tok_nslow, o_tok_maskT, o_dec_scores, o_dec_list,
@@ -93,8 +93,8 @@ int make_plan(const sparse_attn_cfg* c, Plan* p, bool bwd = false) {
     // The compressed branch joins window / block gating (the NSA layout), not
     // the token gate.
     if (c->cmp_block > 0 && c->token_top_k > 0) return SA_E_UNSUPPORTED;
-    // The backward covers window and block gating on bf16 prefills.
-    if (bwd && (dec || c->dtype != SA_BF16 || c->cmp_block > 0)) return SA_E_UNSUPPORTED;
+    // The backward covers bf16 prefills (every branch).
+    if (bwd && (dec || c->dtype != SA_BF16)) return SA_E_UNSUPPORTED;
     if (c->token_top_k > 0) {
         if (c->index_dim != 64) return SA_E_UNSUPPORTED_HEAD_DIM;
         // Block and token gates are separate methods and are not combined
@@ -246,9 +246,15 @@ int make_plan(const sparse_attn_cfg* c, Plan* p, bool bwd = false) {
         P.Nc = P.N / P.C;
         const size_t ncmp = (size_t)P.Bt * P.Hkv * P.Nc * P.D;
         const int planes = P.f32 ? 2 : 1;
-        P.o_cmp_k = take(planes * ncmp * 2);
-        P.o_cmp_v = take(planes * ncmp * 2);
-        P.o_cmp_out = take((size_t)rows * P.D * 4);
+        if (bwd) {   // bf16 K means and their scaled fp16 copy; bf16 V means; fp32 dK, dV per group
+            P.o_cmp_k = take(2 * ncmp * 2);
+            P.o_cmp_v = take(ncmp * 2);
+            P.o_cmp_grad = take(2 * ncmp * 4);
+        } else {
+            P.o_cmp_k = take(planes * ncmp * 2);
+            P.o_cmp_v = take(planes * ncmp * 2);
+            P.o_cmp_out = take((size_t)rows * P.D * 4);
+        }
     }
     P.tok = c->token_top_k > 0;
     if (P.tok) {
@@ -827,6 +833,21 @@ int sparse_attn_bwd(const void* q, const void* k, const void* v, const void* out
     ba.part_dq = P.far ? (uint16_t*)(ws + P.o_part_o) : nullptr;
     ba.Bt = P.Bt; ba.Hq = P.Hq; ba.Hkv = P.Hkv; ba.N = P.N; ba.D = P.D; ba.window = cfg->window;
     ba.scale = P.scale;
+    if (P.cmp && P.Nc > 0) {
+        // The compressed columns' operands: the forward's bf16 K means (the
+        // same kernel and rounding), bf16 V means, and the K means as fp16 in
+        // the units of the K copy.
+        StageScope t("bwd_cmp_pool", s);
+        const size_t ncmp = (size_t)P.Bt * P.Hkv * P.Nc * P.D;
+        uint16_t* kcp = (uint16_t*)(ws + P.o_cmp_k);
+        uint16_t* vcp = (uint16_t*)(ws + P.o_cmp_v);
+        sa::CmpPoolArgs cp{k, v, {kcp, kcp + ncmp}, {vcp, nullptr}, P.Bt * P.Hkv, P.N, P.C, P.Nc, P.D,
+                           nullptr, sk, 1};
+        if (!ok(sa::launch_cmp_pool(cp, false, s))) return SA_E_HIP;
+        ba.kc = kcp; ba.kc16 = kcp + ncmp; ba.vc = vcp;
+        ba.cmp_dk = (float*)(ws + P.o_cmp_grad); ba.cmp_dv = ba.cmp_dk + ncmp;
+        ba.C = P.C; ba.Nc = P.Nc;
+    }
     {
         StageScope t("bwd_delta", s);
         if (!ok(sa::launch_bwd_delta(ba, s))) return SA_E_HIP;

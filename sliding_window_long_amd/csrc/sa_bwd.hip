@@ -150,13 +150,15 @@ struct DqTiles {
     TileDma<D, VS> vd;
     uint64_t kb[1], vb[1], k16b[1];
     int N;
-    __device__ __forceinline__ void init(const BwdArgs& a, size_t kvoff, int wave, int lane) {
+    // Planes k, v (bf16) and k16 (fp16) of n keys.
+    __device__ __forceinline__ void init(const uint16_t* k, const uint16_t* v, const uint16_t* k16,
+                                         int n, int wave, int lane) {
         kd.init(wave, lane);
         vd.init(wave, lane);
-        kb[0] = uniform_u64((uint64_t)(a.k + kvoff));
-        vb[0] = uniform_u64((uint64_t)(a.v + kvoff));
-        k16b[0] = uniform_u64((uint64_t)(a.k16 + kvoff));
-        N = a.N;
+        kb[0] = uniform_u64((uint64_t)k);
+        vb[0] = uniform_u64((uint64_t)v);
+        k16b[0] = uniform_u64((uint64_t)k16);
+        N = n;
     }
     // Issue the loads of the tile at key kt0 (0 <= kt0 < N).
     __device__ __forceinline__ void load(int kt0, uint16_t* lk, uint16_t* lv, uint16_t* lk16, int wave) const {
@@ -189,7 +191,7 @@ __device__ __forceinline__ void dq_tile(const uint16_t* lk, const uint16_t* lv, 
 // ---------------------------------------------------------------------------
 // dQ: a workgroup owns 128 query rows of one (batch, head).
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool CMP>
 __global__ __launch_bounds__(NTHREADS, 1) void bwd_dq_kernel(BwdArgs a) {
     using T = Tile<D>;
     using DT = DqTiles<D>;
@@ -222,7 +224,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dq_kernel(BwdArgs a) {
     const int t_begin = max(lo, 0) / KT, t_end = r_hi / KT;
     const int n_t = t_end - t_begin + 1;
     DT dt;
-    dt.init(a, (size_t)(b * a.Hkv + g) * N * D, wu, lane);
+    const size_t kvoff = (size_t)(b * a.Hkv + g) * N * D;
+    dt.init(a.k + kvoff, a.v + kvoff, a.k16 + kvoff, N, wu, lane);
     dt.load(t_begin * KT, lk0, lv0, lk16_0, wu);
 
     bf16x8 qf[1][T::DK], df[1][T::DK];
@@ -298,6 +301,38 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dq_kernel(BwdArgs a) {
         step(Par<1>{}, it + 1);
     }
     if (it < n_t) step(Par<0>{}, it);
+    if constexpr (CMP) {
+        // The compressed columns: row i sees groups 0 .. (i+1)/C - 1, a
+        // causal mask in group coordinates; the K means come in the units of
+        // the fp16 K copy, so they add to the same accumulator.
+        const int g_hi = (r_hi + 1) / a.C - 1;   // the workgroup's last visible group
+        if (g_hi >= 0) {
+            const int n_c = g_hi / KT + 1;
+            const int ip = (min(row, N - 1) + 1) / a.C - 1;
+            const size_t coff = (size_t)(b * a.Hkv + g) * a.Nc * D;
+            DT dc;
+            dc.init(a.kc + coff, a.vc + coff, a.kc16 + coff, a.Nc, wu, lane);
+            dc.load(0, lk0, lv0, lk16_0, wu);   // the loop above left both buffers free
+            __syncthreads();
+            auto cstep = [&](auto par, int t) __attribute__((always_inline)) {
+                constexpr int PAR = decltype(par)::value;
+                if (t + 1 < n_c) {
+                    if (PAR) dc.load((t + 1) * KT, lk0, lv0, lk16_0, wu);
+                    else dc.load((t + 1) * KT, lk1, lv1, lk16_1, wu);
+                }
+                const int rk = ip - t * KT - 4 * hh;
+                if (PAR) dq_tile<D>(lk1, lv1, lk16_1, qf, df, o, voff, c, lse2, f, drf, true, rk, 0x80000000u, lane);
+                else dq_tile<D>(lk0, lv0, lk16_0, qf, df, o, voff, c, lse2, f, drf, true, rk, 0x80000000u, lane);
+                __syncthreads();
+            };
+            int t = 0;
+            for (; t + 1 < n_c; t += 2) {
+                cstep(Par<0>{}, t);
+                cstep(Par<1>{}, t + 1);
+            }
+            if (t < n_c) cstep(Par<0>{}, t);
+        }
+    }
     if (!ok) return;
     // dq = scale 2^(es + sk) * near part + the far blocks' partials (bf16,
     // already in the units of dq).
@@ -359,7 +394,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_far_dq_kernel(BwdArgs a) {
     const int b = bg / a.Hkv, g = bg % a.Hkv;
     const int ntile = a.B / KT;
     DT dt;
-    dt.init(a, (size_t)bg * N * D, wu, lane);
+    const size_t kvoff = (size_t)bg * N * D;
+    dt.init(a.k + kvoff, a.v + kvoff, a.k16 + kvoff, N, wu, lane);
     dt.load(cblk * a.B, lk0, lv0, lk16_0, wu);
 
     const bool ok = e < e_end;
@@ -436,6 +472,60 @@ __device__ __forceinline__ void mask_rows_tok(f32x16 (&s)[2], int rj, uint32_t w
         }
 }
 
+// Compressed-column mask of an S tile in the key-centric layout (lane =
+// group c, registers = rows i = rt0 + cv + 4hh): row i sees group c iff
+// (i+1)/C - 1 >= c, i.e. i >= (c+1)C - 1.  rc = rt0 + 4hh - ((c+1)C - 1).
+__device__ __forceinline__ void mask_rows_cmp(f32x16 (&s)[2], int rc) {
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int cv = sub * 32 + 8 * (v >> 2) + (v & 3);
+            if (rc + cv < 0) s[sub][v] = -INFINITY;
+        }
+}
+
+// Write 32 keys' accumulators as bf16 rows: o f 2^e, plus (extra != nullptr)
+// the fp32 row extra[0 .. D-1] of the key's compressed group.
+template <int D>
+__device__ __forceinline__ void write_rows_bf16_add(uint16_t* dst, const f32x16 (&o)[Tile<D>::DM],
+                                                    float f, int e, int hh, const float* extra) {
+#pragma unroll
+    for (int mb = 0; mb < Tile<D>::DM; ++mb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int d0 = mb * 32 + 8 * j + 4 * hh;
+            if (d0 < D) {
+                float x[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) x[t] = ldexpf(o[mb][4 * j + t] * f, e);
+                if (extra) {
+                    const float4 ex = *(const float4*)(extra + d0);
+                    x[0] += ex.x; x[1] += ex.y; x[2] += ex.z; x[3] += ex.w;
+                }
+                __bf16 r[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) r[t] = (__bf16)x[t];
+                *(uint2*)(dst + d0) = *(const uint2*)r;
+            }
+        }
+}
+
+// The same as fp32 rows, times f 2^e.
+template <int D>
+__device__ __forceinline__ void write_rows_f32(float* dst, const f32x16 (&o)[Tile<D>::DM], float f,
+                                               int e, int hh) {
+#pragma unroll
+    for (int mb = 0; mb < Tile<D>::DM; ++mb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int d0 = mb * 32 + 8 * j + 4 * hh;
+            if (d0 < D)
+                *(float4*)(dst + d0) = make_float4(ldexpf(o[mb][4 * j] * f, e), ldexpf(o[mb][4 * j + 1] * f, e),
+                                                   ldexpf(o[mb][4 * j + 2] * f, e), ldexpf(o[mb][4 * j + 3] * f, e));
+        }
+}
+
 // Lane offsets of a gathered 64-row tile in an LDS image of row stride S
 // (the layout of TileDma): instruction j of this wave writes chunk p = 64 i +
 // lane, i = min(wave + NWAVES j, S/8 - 1), of row p / (S/8); chunks past the
@@ -483,8 +573,12 @@ __device__ __forceinline__ void gather_dma(const GatherDma<D, S>& gd, const uint
 // other LDS buffer while the current one is computed, and wave 0 fetches the
 // per-row data (id, lse, D, kept-block bits) two tiles ahead into a ring of
 // three slots.
+// CMP: the keys are the compressed groups (K, V means); the rows are every
+// row from the first one that sees the workgroup's first group; the result
+// goes to fp32 per group, divided by C, and the plain pass adds it to each
+// token of the group (the chain rule through the mean).
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, bool CMP>
 __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkv_kernel(BwdArgs a) {
     using T = Tile<D>;
     constexpr int VS = dma_vs<D>();
@@ -498,19 +592,22 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkv_kernel(BwdArgs a) {
     const int col = lane & 31, hh = lane >> 5;
     const int wu = __builtin_amdgcn_readfirstlane(wave);
     const int N = a.N, G = a.Hq / a.Hkv;
-    const int ntiles = (N + RT - 1) / RT;
+    const int Nk = CMP ? a.Nc : N;   // keys: tokens, or compressed groups
+    const int ntiles = (Nk + RT - 1) / RT;
     const int bg = blockIdx.x / ntiles, ktile = blockIdx.x % ntiles;
     const int b = bg / a.Hkv, g = bg % a.Hkv;
     const int k0 = ktile * RT;
-    const int k_hi = min(k0 + RT - 1, N - 1);
+    const int k_hi = min(k0 + RT - 1, Nk - 1);
     const int j0 = k0 + wu * 32;
     const int key = j0 + col;
-    const bool ok = key < N;
-    const size_t pkey = (size_t)bg * N + (ok ? key : 0);
+    const bool ok = key < Nk;
+    const size_t pkey = (size_t)bg * Nk + (ok ? key : 0);
 
     bf16x8 kf[1][T::DK], vf[1][T::DK];
-    load_q<D, 1>(kf, &a.k, pkey * D, ok, hh);
-    load_q<D, 1>(vf, &a.v, pkey * D, ok, hh);
+    const uint16_t* kp = CMP ? a.kc : a.k;
+    const uint16_t* vp = CMP ? a.vc : a.v;
+    load_q<D, 1>(kf, &kp, pkey * D, ok, hh);
+    load_q<D, 1>(vf, &vp, pkey * D, ok, hh);
     const float c = a.scale * kLog2e;
     const uint32_t wl = a.window > 0 ? (uint32_t)a.window : 0u;
     const int es = a.es[bg];
@@ -533,17 +630,22 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkv_kernel(BwdArgs a) {
 
     // The row tiles: n_rt contiguous tiles per head of the group, then the
     // far lists of the keys' (at most two) blocks.
-    const bool tok = a.tokmaskT != nullptr;
+    const bool tok = !CMP && a.tokmaskT != nullptr;
+    int r_beg = k0;
     int r_end = a.window > 0 ? min(N - 1, k_hi + a.window - 1) : -1;
     if (a.sel) r_end = max(r_end, min(N - 1, (k_hi / a.B + a.span + 1) * a.B - 1));
     if (tok) r_end = N - 1;   // every later row can keep these keys
-    const int n_rt = r_end >= k0 ? (r_end - k0) / KT + 1 : 0;
+    if constexpr (CMP) {      // rows from the first that sees group k0
+        r_beg = min((k0 + 1) * a.C - 1, N);
+        r_end = N - 1;
+    }
+    const int n_rt = r_end >= r_beg ? (r_end - r_beg) / KT + 1 : 0;
     const int nt32k = (N + 31) / 32, nt64k = (N + KT - 1) / KT;   // key-major mask tiles
     const int n1 = G * n_rt;
     // (Scalars, not arrays: a runtime-indexed array would live in scratch,
     // whose loads wait for every tile load in flight.)
     int fa0 = 0, fa1 = 0, fb0 = 0, fb1 = 0;   // entry ranges of blocks blk0, blk0 + 1
-    if (a.sel && a.list_off) {
+    if (!CMP && a.sel && a.list_off) {
         const int list = bg * a.n + blk0;
         if (blk0 * a.B <= k_hi && blk0 < a.n) {
             fa0 = a.list_off[list];
@@ -575,7 +677,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkv_kernel(BwdArgs a) {
     auto fetch = [&](int i, int r, int ent) __attribute__((always_inline)) -> RowData {
         RowData rd{-1, 0, 0.f, 0.f, 0ull};
         if (i < n1) {
-            const int hl = i / n_rt, rr = k0 + (i % n_rt) * KT + r;
+            const int hl = i / n_rt, rr = r_beg + (i % n_rt) * KT + r;
             rd.rr = rr;
             if (rr < N) rd.id = (int)((size_t)(b * a.Hq + g * G + hl) * N + rr);
         } else if (ent >= 0) {   // entry = (i*G + head in group)*kslots + slot
@@ -585,12 +687,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkv_kernel(BwdArgs a) {
         const int idc = max(rd.id, 0);
         rd.lse = a.lse[idc];
         rd.d = a.delta[idc];
-        if (a.near_mask && i < n1) rd.nm = a.near_mask[idc];
+        if (!CMP && a.near_mask && i < n1) rd.nm = a.near_mask[idc];
         return rd;
     };
     auto put = [&](const RowData& rd, int i, int sl) __attribute__((always_inline)) {
         int info = 0;
-        if (a.near_mask && i < n1 && rd.id >= 0) {
+        if (!CMP && a.near_mask && i < n1 && rd.id >= 0) {
             // Blocks blk0 and blk0 + 1 kept for this row by the forward: its
             // own block, or a near block it selected.
             const int rb = rd.rr / a.B;
@@ -618,7 +720,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkv_kernel(BwdArgs a) {
         f32x16 s[2], dp[2];
         qk_tile<D, 1>(q_, kf, s, lane);
         qk_tile<D, 1>(do_, vf, dp, lane);
-        if (i >= n1) {
+        if (CMP) {
+            mask_rows_cmp(s, r_beg + (i % n_rt) * KT + 4 * hh - ((key + 1) * a.C - 1));
+        } else if (i >= n1) {
             // every key of the far block, none of the other block
             const int far_kb = i - n1 < fn0 ? 0 : 1;
             if (kb != far_kb) {
@@ -629,13 +733,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkv_kernel(BwdArgs a) {
             }
         } else if (tok) {
             // keep word of (this wave's 32 keys, the tile's 64 rows, lane)
-            const int rt0 = k0 + (i % n_rt) * KT;
+            const int rt0 = r_beg + (i % n_rt) * KT;
             const uint32_t tw = j0 < N   // a wave past the last key keeps nothing
                                     ? a.tokmaskT[(((size_t)b * nt32k + j0 / 32) * nt64k + rt0 / KT) * 64 + lane]
                                     : 0u;
             mask_rows_tok(s, rt0 + 4 * hh - key, wl, tw);
         } else {
-            const int rt0 = k0 + (i % n_rt) * KT;
+            const int rt0 = r_beg + (i % n_rt) * KT;
             mask_rows(s, rt0 + 4 * hh - key, wl, s_info[sl], kb, hh);
         }
         float p[2][16], gds[2][16];
@@ -699,9 +803,20 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkv_kernel(BwdArgs a) {
         }
         if (i < n_tiles) step(Par<0>{}, i);
     }
-    if (ok) {
-        write_rows_bf16<D>(a.dk + pkey * D, dk, a.scale, es + a.sq[bg], hh);
-        write_rows_bf16<D>(a.dv + pkey * D, dv, 1.f, a.sd[bg], hh);
+    if (!ok) return;
+    if constexpr (CMP) {
+        const float invc = 1.f / (float)a.C;
+        write_rows_f32<D>(a.cmp_dk + pkey * D, dk, a.scale * invc, es + a.sq[bg], hh);
+        write_rows_f32<D>(a.cmp_dv + pkey * D, dv, invc, a.sd[bg], hh);
+    } else {
+        // the share of the key's compressed group (tokens past the last
+        // complete group have none)
+        const bool grp = a.kc != nullptr && key < a.Nc * a.C;
+        const size_t prow_c = ((size_t)bg * a.Nc + (grp ? key / a.C : 0)) * D;
+        write_rows_bf16_add<D>(a.dk + pkey * D, dk, a.scale, es + a.sq[bg], hh,
+                               grp ? a.cmp_dk + prow_c : nullptr);
+        write_rows_bf16_add<D>(a.dv + pkey * D, dv, 1.f, a.sd[bg], hh,
+                               grp ? a.cmp_dv + prow_c : nullptr);
     }
 }
 
@@ -713,10 +828,20 @@ static hipError_t bwd_d(const BwdArgs& a, hipStream_t s) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((bwd_dq_kernel<D>), dim3(nt * a.Bt * a.Hq), dim3(NTHREADS), 0, s, a);
+    const bool cmp = a.kc != nullptr;
+    if (cmp)
+        hipLaunchKernelGGL((bwd_dq_kernel<D, true>), dim3(nt * a.Bt * a.Hq), dim3(NTHREADS), 0, s, a);
+    else
+        hipLaunchKernelGGL((bwd_dq_kernel<D, false>), dim3(nt * a.Bt * a.Hq), dim3(NTHREADS), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_dkv_kernel<D>), dim3(nt * a.Bt * a.Hkv), dim3(NTHREADS), 0, s, a);
+    if (cmp) {   // the groups' dK, dV first: the token pass adds them
+        const int ntc = (a.Nc + RT - 1) / RT;
+        hipLaunchKernelGGL((bwd_dkv_kernel<D, true>), dim3(ntc * a.Bt * a.Hkv), dim3(NTHREADS), 0, s, a);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((bwd_dkv_kernel<D, false>), dim3(nt * a.Bt * a.Hkv), dim3(NTHREADS), 0, s, a);
     return hipGetLastError();
 }
 

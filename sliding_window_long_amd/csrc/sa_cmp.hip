@@ -93,6 +93,15 @@ __global__ __launch_bounds__(256) void cmp_pool_kernel(CmpPoolArgs a) {
     }
     const size_t o = row * a.D + e0;
     *(uint4*)(a.kc[0] + o) = pack_bf16(sk, false);
+    if (!F32IN && a.bwd) {   // backward operands: bf16 V, and the bf16 K means as scaled fp16
+        *(uint4*)(a.vc[0] + o) = pack_bf16(sv, false);
+        const int e = a.kscale[bg];
+        float kr[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) kr[t] = ldexpf((float)(__bf16)sk[t], -e);
+        *(uint4*)(a.kc[1] + o) = pack_f16(kr);
+        return;
+    }
     if constexpr (F32IN) {   // split operands: hi and lo bf16 terms of K and V
         *(uint4*)(a.kc[1] + o) = pack_bf16(sk, true);
         *(uint4*)(a.vc[0] + o) = pack_bf16(sv, false);

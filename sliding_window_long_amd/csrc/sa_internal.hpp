@@ -111,6 +111,10 @@ struct CmpPoolArgs {
     uint16_t* vc[2];
     int lists, N, C, Nc, D;
     const int32_t* vscale;  // [lists] fp16 V means are stored times 2^-s, or nullptr
+    // Backward (bwd != 0, bf16 inputs): kc[0] bf16 K means, kc[1] the same
+    // values as fp16 times 2^-kscale[list], vc[0] bf16 V means.
+    const int32_t* kscale;
+    int bwd;
 };
 
 // Attention over the compressed columns, merged with the other branches'
@@ -168,6 +172,16 @@ struct BwdArgs {
     const int32_t* n_chunks;
     int max_chunks;
     uint16_t* part_dq;      // bf16 [Bt*Hq*N, kslots, D] far-block dq partials
+    // Compressed columns (kc == nullptr: none): group means [Bt*Hkv, Nc, D]
+    // of K (bf16, and fp16 times 2^-sk) and V (bf16); the pass over them
+    // leaves each group's fp32 dK, dV, already divided by C, for the key
+    // pass to add to every token of the group.
+    const uint16_t* kc;
+    const uint16_t* kc16;
+    const uint16_t* vc;
+    float* cmp_dk;
+    float* cmp_dv;
+    int C, Nc;
     int top_k, B, n, span, kslots;
     int Bt, Hq, Hkv, N, D, window;
     float scale;

@@ -204,7 +204,8 @@ def check_grads(inp, dout, dev_sel, dev_grads, *, sink=None, joint_floor=True, d
     sel = None if dev_sel is None else dev_sel.reshape(-1, wl.top_k)
     tsel = None if dev_tsel is None else dev_tsel.reshape(-1, wl.token_top_k)
     ref = oracle.attend_bwd(inp.q, inp.k, inp.v, dout, window=wl.window,
-                            block_size=wl.block_size, sel=sel, tsel=tsel, sink=sink)
+                            block_size=wl.block_size, sel=sel, tsel=tsel, sink=sink,
+                            cmp_block=wl.cmp_block)
     joint_max = max(float(np.abs(r).max()) for r in ref[:3])
     joint_mean = max(float(np.abs(r).mean()) for r in ref[:3])
     res = {}

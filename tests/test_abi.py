@@ -230,7 +230,7 @@ def test_backward_configs(lib):
     assert ws(sa.Params(1, 32, 32, 16384, 80, window=4096)) == 0
     assert ws(sa.Params(1, 2, 2, 512, 64, dtype=sa.SA_F32, window=8)) == -8           # fp32
     assert ws(sa.Params(1, 4, 1, 256, 128, window=8, token_top_k=16, index_dim=64)) == 0
-    assert ws(sa.Params(1, 4, 4, 256, 64, window=8, cmp_block=8)) == -8
+    assert ws(sa.Params(1, 4, 4, 256, 64, window=8, cmp_block=8)) == 0
     assert ws(sa.Params(1, 4, 4, 1, 64, window=8, kv_len=256)) == -8                 # decode
     # fp16 copies of q, k and dO plus the row deltas; no far partials; then
     # the copies' range data: per-128-row maxima of q, dO (4 heads) and k, v
@@ -241,7 +241,14 @@ def test_backward_configs(lib):
     sa.load_library().sparse_attn_bwd_workspace_bytes(ctypes.byref(p.cfg()), ctypes.byref(n))
     a256 = lambda x: (x + 255) // 256 * 256
     ranges = 2 * a256(4 * 4 * 4) + 2 * a256(2 * 4 * 4) + a256(2 * 2 * 4) + a256(2 * 5 * 4)
-    assert n.value == (2 * 512 * 64 * 2) + 2 * (4 * 512 * 64 * 2) + 4 * 512 * 4 + ranges
+    base = (2 * 512 * 64 * 2) + 2 * (4 * 512 * 64 * 2) + 4 * 512 * 4 + ranges
+    assert n.value == base
+    # the compressed branch (groups of 8): bf16 K means and their scaled fp16
+    # copy, bf16 V means, and fp32 dK, dV per group
+    p = sa.Params(1, 4, 2, 512, 64, window=16, cmp_block=8)
+    sa.load_library().sparse_attn_bwd_workspace_bytes(ctypes.byref(p.cfg()), ctypes.byref(n))
+    ncmp = 2 * 64 * 64
+    assert n.value == base + 3 * ncmp * 2 + 2 * ncmp * 4
 
 
 def test_backward_rejects_before_launch(lib):

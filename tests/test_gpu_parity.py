@@ -332,7 +332,8 @@ def run_backward(inp, dev, seed, do_scale=1.0):
     g = {k_: (None if v_ is None else v_.to(dev)) for k_, v_ in t.items()}
     kw = dict(block_size=wl.block_size, top_k=wl.top_k, window=wl.window, sink=g["sink"],
               gate_repr=wl.gate_repr, gate_shared=wl.gate_shared, gate_first=wl.gate_first,
-              idx_q=g["idx_q"], idx_k=g["idx_k"], token_top_k=wl.token_top_k)
+              idx_q=g["idx_q"], idx_k=g["idx_k"], token_top_k=wl.token_top_k,
+              cmp_block=wl.cmp_block)
     out, lse, bsel, tsel = sa.forward(g["q"], g["k"], g["v"], return_selection=True, **kw)
     dout = W._round(np.random.default_rng(seed).standard_normal(inp.q.shape, dtype=np.float32)
                     * np.float32(do_scale), "bf16")
@@ -410,6 +411,35 @@ def test_backward_ragged(dev):
 
 def test_backward_bora_all_rows(dev):
     bwd_and_check(W.make_inputs(W.BORA_HYBRID, 102), dev, 83, label="bwd_bora")
+
+
+# The compressed branch's gradients (groups of C tokens; GQA 4/2, two
+# batches): ragged N and tails past the last group, with a window, block
+# gating and its shared variant, a sink; C = 1 (every token also its own
+# group), C = 64 (groups as large as the blocks), C = 300 (one group).
+CMP_BWD_SHAPES = [
+    dict(N=300, window=16, cmp_block=8),
+    dict(N=1000, window=64, cmp_block=8, sink=True),
+    dict(N=512, block_size=64, top_k=3, window=70, cmp_block=8, gate_shared=True),
+    dict(N=257, window=1, cmp_block=1),
+    dict(N=512, block_size=64, top_k=4, cmp_block=64, sink=True),
+    dict(N=513, window=32, cmp_block=300),
+]
+
+
+@pytest.mark.parametrize("case", range(len(CMP_BWD_SHAPES)))
+@pytest.mark.parametrize("d", [64, 80, 128])
+def test_backward_compressed(dev, case, d):
+    kw = dict(CMP_BWD_SHAPES[case])
+    N = kw.pop("N")
+    wl = W.Workload("bwd_cmp", 2, 4, 2, N, d, "bf16", block_offsets="block_size" in kw, **kw)
+    bwd_and_check(W.make_inputs(wl, 121 + case + d), dev, 131 + case, label=f"bwd_cmp N={N} {kw}")
+
+
+def test_backward_bora_nsa_all_rows(dev):
+    # the BORA NSA layout: 8:1 compression, one selection per kv group
+    wl = W.BORA_HYBRID.replace(name="bwd_bora_nsa", cmp_block=8, gate_shared=True)
+    bwd_and_check(W.make_inputs(wl, 103), dev, 84, label="bwd_bora_nsa")
 
 
 # Value ranges past fp16 for the backward's fp16 operands (q, k, dO and the
