@@ -135,7 +135,8 @@ typedef struct {
     int32_t seq_len;        /* N >= 1 */
     int32_t head_dim;       /* d in {64, 80, 128} */
     int32_t dtype;          /* sa_dtype */
-    int32_t block_size;     /* B: a multiple of 64 dividing N; ignored if top_k == 0 */
+    int32_t block_size;     /* B: 8, 16, 32 or a multiple of 64, dividing N (else
+                               SA_E_SHAPE); ignored if top_k == 0 */
     int32_t top_k;          /* blocks kept per query, own block included; 0 = no
                                block gate; 1 <= top_k <= min(33, N/B) */
     int32_t window;         /* w >= 0: attend iff 0 <= i-j < w; 0 = no window */

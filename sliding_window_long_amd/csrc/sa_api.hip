@@ -157,7 +157,10 @@ int make_plan(const sparse_attn_cfg* c, Plan* p, bool bwd = false) {
     P.gate = c->top_k > 0;
     if (P.gate) {
         P.B = c->block_size;
-        if (P.B < 64 || P.B % 64 || P.N % P.B) return SA_E_SHAPE;
+        // 64-key tiles: blocks of 8, 16 or 32 keys share a tile; larger
+        // blocks are whole tiles.
+        if (!(P.B == 8 || P.B == 16 || P.B == 32 || (P.B >= 64 && P.B % 64 == 0)) || P.N % P.B)
+            return SA_E_SHAPE;
         P.n = P.N / P.B;
         P.top_k = c->top_k;
         if (P.top_k > P.n) return SA_E_SHAPE;

@@ -136,9 +136,10 @@ __device__ __forceinline__ void finish_rows(const RowsArgs& a, f32x16 (&o)[Tile<
 // unit scales; the 16 dims past a multiple of 64 on the 32x32x16 FP8 op);
 // every E4M3 product is exact in the fp32 accumulator, as the bf16 products
 // of the decoded values would be.  K tiles hold fp8 rows of K8S<D>() bytes.
-// WIDE: the near-block mask holds 64 blocks (a window of 33..64 blocks
-// under block gating), else 32.
-template <int D, int SPLIT, bool TOK, bool QK8, bool WIDE = false>
+// NEAR: the near-block mask holds 32 blocks (0) or 64 (1: a window of
+// 33..64 blocks under block gating); 2: 64, with blocks smaller than the
+// 64-key tile (B = 8, 16, 32), whose tiles get per-key block bits.
+template <int D, int SPLIT, bool TOK, bool QK8, int NEAR = 0>
 __global__ __launch_bounds__(NTHREADS, D <= 80 && SPLIT == 1 ? 3 : 2) void attn_rows_kernel(RowsArgs a) {
     using T = Tile<D>;
     constexpr bool ONES = T::DPAD > D;
@@ -182,6 +183,7 @@ __global__ __launch_bounds__(NTHREADS, D <= 80 && SPLIT == 1 ? 3 : 2) void attn_
 
     // Block-gate state of the row: its block, the kept near blocks as a bit
     // mask over (own block - 1 - bit), and the count of far blocks.
+    constexpr bool WIDE = NEAR > 0, SMALLB = NEAR == 2;
     using NearT = typename std::conditional<WIDE, uint64_t, uint32_t>::type;
     constexpr int kNear = WIDE ? 64 : 32;
     int row_blk = 0, nfar = 0;
@@ -255,6 +257,17 @@ __global__ __launch_bounds__(NTHREADS, D <= 80 && SPLIT == 1 ? 3 : 2) void attn_
         if constexpr (TOK) {
             const bool near = kt0 + KT - 1 >= q0 - a.window + 1;   // tile meets a window
             mask_tile_tok(sv, rk, wl_window, near, tword);
+        } else if (SMALLB) {
+            // blocks smaller than the tile: per-block key bits of the own
+            // block and the kept near blocks
+            uint32_t word = 0;
+            for (int bo = 0; bo < KT / a.B; ++bo) {
+                const int dlt = row_blk - (kt0 / a.B + bo);
+                if (dlt == 0 || (dlt >= 1 && dlt <= a.span && dlt <= kNear &&
+                                 ((near_bits >> (dlt - 1)) & 1u)))
+                    word |= block_bits(a.B, bo);
+            }
+            mask_tile_blocks(sv, rk, wl_window, word);
         } else {
             const bool full = kt0 + KT - 1 <= q0 &&
                               ((a.window > 0 && q1 - kt0 < a.window) ||
@@ -553,8 +566,10 @@ static hipError_t rows_d(const RowsArgs& a, hipStream_t s) {
     }
     if (a.tokmask)
         hipLaunchKernelGGL((attn_rows_kernel<D, SPLIT, true, false>), dim3(grid), dim3(NTHREADS), 0, s, a);
+    else if (a.gate && a.B < KT)
+        hipLaunchKernelGGL((attn_rows_kernel<D, SPLIT, false, false, 2>), dim3(grid), dim3(NTHREADS), 0, s, a);
     else if (a.gate && a.span > 32)
-        hipLaunchKernelGGL((attn_rows_kernel<D, SPLIT, false, false, true>), dim3(grid), dim3(NTHREADS), 0, s, a);
+        hipLaunchKernelGGL((attn_rows_kernel<D, SPLIT, false, false, 1>), dim3(grid), dim3(NTHREADS), 0, s, a);
     else
         hipLaunchKernelGGL((attn_rows_kernel<D, SPLIT, false, false>), dim3(grid), dim3(NTHREADS), 0, s, a);
     return hipGetLastError();

@@ -22,6 +22,7 @@ constexpr int KT = 64;                 // keys per tile
 constexpr int NWAVES = 4;              // waves per workgroup
 constexpr int NTHREADS = 64 * NWAVES;
 constexpr int RT = 32 * NWAVES;        // query rows per workgroup
+constexpr int kMaxKeyBlocks = RT / 8;  // blocks met by RT consecutive keys (smallest block: 8)
 
 template <int D>
 struct Tile {
@@ -310,6 +311,31 @@ __device__ __forceinline__ void mask_tile_tok(f32x16 (&s)[2], int rk, uint32_t w
             }
             if (!keep) s[sub][v] = -INFINITY;
         }
+}
+
+// Block-gate mask of an S^T tile with blocks smaller than the tile: key j
+// stays iff it is causal (j <= i) and either its bit is set in this lane's
+// word (bit 16*sub + v for register v of half sub: the key's block is the
+// row's own block or a kept near block) or it passes the window test.
+__device__ __forceinline__ void mask_tile_blocks(f32x16 (&s)[2], int rk, uint32_t wl, uint32_t word) {
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int cv = sub * 32 + 8 * (v >> 2) + (v & 3);
+            const int dif = rk - cv;   // i - j
+            const bool keep = dif >= 0 && (((word >> (16 * sub + v)) & 1u) || (uint32_t)dif < wl);
+            if (!keep) s[sub][v] = -INFINITY;
+        }
+}
+
+// This lane's key bits of one block of a tile when blocks are smaller than
+// the tile: for block size B in {8, 16, 32}, the lane's keys of block bo
+// (key offsets 32 sub + 8 (v/4) + v%4 + 4 (lane/32)) are bits
+// B/2 * bo .. B/2 * (bo + 1) - 1 of the word.
+__device__ __forceinline__ uint32_t block_bits(int B, int bo) {
+    const int w = B / 2;
+    return (w >= 32 ? 0xffffffffu : ((1u << w) - 1u)) << (w * bo);
 }
 
 // Row max of an S^T tile (both lanes of a row get it).

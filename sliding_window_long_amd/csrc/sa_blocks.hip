@@ -93,7 +93,7 @@ __global__ __launch_bounds__(NTHREADS, D <= 80 && SPLIT == 1 ? 3 : 2) void attn_
     const int cblk = list % a.n, bg = list / a.n;   // bg = b*Hkv + g
     const int b = bg / a.Hkv, g = bg % a.Hkv, G = a.Hq / a.Hkv;
     const int N = a.N;
-    const int ntile = a.B / KT;
+    const int ntile = a.B >= KT ? a.B / KT : 1;   // a block smaller than a tile: one masked tile
     const int k_begin = cblk * a.B;
 
     // V rows: the fp16 copy's stride (bf16 path; ones past D at d 80) or D.
@@ -142,6 +142,7 @@ __global__ __launch_bounds__(NTHREADS, D <= 80 && SPLIT == 1 ? 3 : 2) void attn_
     load_k(min(1, ntile - 1), lds_k1);
     f32x16 s0[2];
     qk_tile<D, SPLIT>(lds_k0, qf, s0, lane);
+    if (a.B < KT) mask_tile(s0, a.B - 1 - 4 * hh, (uint32_t)a.B);   // keys past the block
     max_tile(s0, rs, c);
     exp_tile<SPLIT, !ONES>(s0, rs, c, pb, pl);
     __syncthreads();

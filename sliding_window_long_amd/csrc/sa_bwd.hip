@@ -175,11 +175,13 @@ __device__ __forceinline__ void dq_tile(const uint16_t* lk, const uint16_t* lv, 
                                         const bf16x8 (&qf)[1][Tile<D>::DK], const bf16x8 (&df)[1][Tile<D>::DK],
                                         f32x16 (&o)[Tile<D>::DM], const int (&voff)[Tile<D>::DM],
                                         float c, float lse2, float f, float drf, bool masked, int rk,
-                                        uint32_t wl, int lane, bool tok = false, uint32_t tword = 0u) {
+                                        uint32_t wl, int lane, bool tok = false, uint32_t tword = 0u,
+                                        bool blocks = false) {
     f32x16 s[2], dp[2];
     qk_tile<D, 1>(lk, qf, s, lane);
     qk_tile<D, 1>(lv, df, dp, lane);
     if (tok) mask_tile_tok(s, rk, wl, wl != 0u, tword);
+    else if (blocks) mask_tile_blocks(s, rk, wl, tword);
     else if (masked) mask_tile(s, rk, wl);
     uint4 pb[4], db[4];
     p_ds(s, dp, c, lse2, f, drf, pb, db);
@@ -279,6 +281,18 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dq_kernel(BwdArgs a) {
             return;
         }
         uint32_t wl = wl_window;
+        if (a.sel && a.B < KT) {
+            // blocks smaller than the tile: key bits of the own and kept near blocks
+            uint32_t word = 0;
+            for (int bo = 0; bo < KT / a.B; ++bo) {
+                const int dlt = row_blk - (kt0 / a.B + bo);
+                if (dlt == 0 || (dlt >= 1 && dlt <= 64 && ((near_bits >> (dlt - 1)) & 1u)))
+                    word |= block_bits(a.B, bo);
+            }
+            dq_tile<D>(lk, lv, lk16, qf, df, o, voff, c, lse2, f, drf, true, row - kt0 - 4 * hh, wl, lane,
+                       false, word, true);
+            return;
+        }
         if (a.sel) {
             const int dlt = row_blk - kt0 / a.B;
             if (dlt == 0 || (dlt >= 1 && dlt <= 64 && ((near_bits >> (dlt - 1)) & 1u))) wl = 0x80000000u;
@@ -392,7 +406,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_far_dq_kernel(BwdArgs a) {
     const int e_end = min(e0 + RT, a.list_off[list + 1]);
     const int cblk = list % a.n, bg = list / a.n;
     const int b = bg / a.Hkv, g = bg % a.Hkv;
-    const int ntile = a.B / KT;
+    const int ntile = a.B >= KT ? a.B / KT : 1;   // a block smaller than a tile: one masked tile
+    const bool small = a.B < KT;
     DT dt;
     const size_t kvoff = (size_t)bg * N * D;
     dt.init(a.k + kvoff, a.v + kvoff, a.k16 + kvoff, N, wu, lane);
@@ -429,8 +444,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_far_dq_kernel(BwdArgs a) {
             if (PAR) dt.load(cblk * a.B + (t + 1) * KT, lk0, lv0, lk16_0, wu);
             else dt.load(cblk * a.B + (t + 1) * KT, lk1, lv1, lk16_1, wu);
         }
-        if (PAR) dq_tile<D>(lk1, lv1, lk16_1, qf, df, o, voff, c, lse2, f, drf, false, 0, 0u, lane);
-        else dq_tile<D>(lk0, lv0, lk16_0, qf, df, o, voff, c, lse2, f, drf, false, 0, 0u, lane);
+        // every key of the block (keys past a block smaller than the tile masked)
+        const int rk = a.B - 1 - 4 * hh;
+        if (PAR) dq_tile<D>(lk1, lv1, lk16_1, qf, df, o, voff, c, lse2, f, drf, small, rk, (uint32_t)a.B, lane);
+        else dq_tile<D>(lk0, lv0, lk16_0, qf, df, o, voff, c, lse2, f, drf, small, rk, (uint32_t)a.B, lane);
         __syncthreads();
     };
     int t = 0;
@@ -587,6 +604,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkv_kernel(BwdArgs a) {
     __shared__ __align__(16) uint16_t lq16_0[VEL], lq16_1[VEL], ldo16_0[VEL], ldo16_1[VEL];
     __shared__ float s_lse[3][KT], s_d[3][KT];
     __shared__ int s_info[3][KT], s_ids[3][KT];
+    // Far-row lists of the workgroup's key blocks (128 keys: at most 16
+    // blocks of 8): first and end entry, and the prefix of their tile counts.
+    __shared__ int s_fl_e0[kMaxKeyBlocks], s_fl_e1[kMaxKeyBlocks], s_fl_tp[kMaxKeyBlocks + 1];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int col = lane & 31, hh = lane >> 5;
@@ -613,7 +633,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkv_kernel(BwdArgs a) {
     const int es = a.es[bg];
     const float f = ldexpf(1.f, -es);   // dS is taken as fp16(dS f)
     const int blk0 = a.B > 0 ? k0 / a.B : 0;
-    const int kb = a.B > 0 ? min(key, N - 1) / a.B - blk0 : 0;   // 0 or 1 (B >= 64)
+    const int kb = a.B > 0 ? min(key, N - 1) / a.B - blk0 : 0;   // the key's block, from blk0
+    const int nbw = a.B > 0 ? k_hi / a.B - blk0 + 1 : 0;         // blocks of the workgroup's keys
 
     f32x16 dv[T::DM], dk[T::DM];
 #pragma unroll
@@ -642,22 +663,32 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkv_kernel(BwdArgs a) {
     const int n_rt = r_end >= r_beg ? (r_end - r_beg) / KT + 1 : 0;
     const int nt32k = (N + 31) / 32, nt64k = (N + KT - 1) / KT;   // key-major mask tiles
     const int n1 = G * n_rt;
-    // (Scalars, not arrays: a runtime-indexed array would live in scratch,
-    // whose loads wait for every tile load in flight.)
-    int fa0 = 0, fa1 = 0, fb0 = 0, fb1 = 0;   // entry ranges of blocks blk0, blk0 + 1
-    if (!CMP && a.sel && a.list_off) {
-        const int list = bg * a.n + blk0;
-        if (blk0 * a.B <= k_hi && blk0 < a.n) {
-            fa0 = a.list_off[list];
-            fa1 = a.list_off[list + 1];
-        }
-        if ((blk0 + 1) * a.B <= k_hi && blk0 + 1 < a.n) {
-            fb0 = a.list_off[list + 1];
-            fb1 = a.list_off[list + 2];
+    // The table lives in LDS (a runtime-indexed register array would live
+    // in scratch, whose loads wait for every tile load in flight).
+    const bool has_far = !CMP && a.sel && a.list_off;
+    if (wu == 0 && lane <= kMaxKeyBlocks) {
+        int tp = 0;   // tiles of the lists before this lane's
+        if (has_far)
+            for (int m = 0; m < min(lane, nbw); ++m) {
+                const int l = bg * a.n + blk0 + m;
+                tp += (a.list_off[l + 1] - a.list_off[l] + KT - 1) / KT;
+            }
+        s_fl_tp[lane] = tp;
+        if (lane < kMaxKeyBlocks) {
+            const bool in = has_far && lane < nbw;
+            s_fl_e0[lane] = in ? a.list_off[bg * a.n + blk0 + lane] : 0;
+            s_fl_e1[lane] = in ? a.list_off[bg * a.n + blk0 + lane + 1] : 0;
         }
     }
-    const int fn0 = (fa1 - fa0 + KT - 1) / KT, fn1 = (fb1 - fb0 + KT - 1) / KT;
-    const int n_tiles = n1 + fn0 + fn1;
+    __syncthreads();
+    const int n_far = has_far ? s_fl_tp[nbw] : 0;
+    const int n_tiles = n1 + n_far;
+    // The list (block offset from blk0) of far tile fi = i - n1.
+    auto far_list = [&](int fi) __attribute__((always_inline)) -> int {
+        int li = 0;
+        while (li + 1 < nbw && s_fl_tp[li + 1] <= fi) ++li;
+        return li;
+    };
 
     // Per-row data of row r of tile i, fetched by wave 0 (r = lane) in three
     // parts so that no load is waited for before the step's closing barrier:
@@ -665,9 +696,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkv_kernel(BwdArgs a) {
     // unconditional at a clamped id) and the values into their slot (put).
     auto ent_of = [&](int i, int r) __attribute__((always_inline)) -> int {
         if (i < n1 || i >= n_tiles) return -1;
-        const bool second = i - n1 >= fn0;
-        const int ee = (second ? fb0 + (i - n1 - fn0) * KT : fa0 + (i - n1) * KT) + r;
-        return ee < (second ? fb1 : fa1) ? a.entries[min(ee, a.entries_cap - 1)] : -1;
+        const int li = far_list(i - n1);
+        const int ee = s_fl_e0[li] + (i - n1 - s_fl_tp[li]) * KT + r;
+        return ee < s_fl_e1[li] ? a.entries[min(ee, a.entries_cap - 1)] : -1;
     };
     struct RowData {
         int id, rr;
@@ -693,11 +724,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkv_kernel(BwdArgs a) {
     auto put = [&](const RowData& rd, int i, int sl) __attribute__((always_inline)) {
         int info = 0;
         if (!CMP && a.near_mask && i < n1 && rd.id >= 0) {
-            // Blocks blk0 and blk0 + 1 kept for this row by the forward: its
-            // own block, or a near block it selected.
+            // Blocks blk0 .. blk0 + nbw - 1 kept for this row by the
+            // forward: its own block, or a near block it selected.
             const int rb = rd.rr / a.B;
-#pragma unroll
-            for (int dl = 0; dl < 2; ++dl) {
+            for (int dl = 0; dl < nbw; ++dl) {
                 const int dlt = rb - (blk0 + dl);
                 if (dlt == 0 || (dlt >= 1 && dlt <= 64 && ((rd.nm >> (dlt - 1)) & 1u))) info |= 1 << dl;
             }
@@ -723,8 +753,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkv_kernel(BwdArgs a) {
         if (CMP) {
             mask_rows_cmp(s, r_beg + (i % n_rt) * KT + 4 * hh - ((key + 1) * a.C - 1));
         } else if (i >= n1) {
-            // every key of the far block, none of the other block
-            const int far_kb = i - n1 < fn0 ? 0 : 1;
+            // every key of the far block, none of the other blocks
+            const int far_kb = far_list(i - n1);
             if (kb != far_kb) {
 #pragma unroll
                 for (int sub = 0; sub < 2; ++sub)

@@ -71,7 +71,8 @@ def code_of(params, **cfg_fields):
     (sa.Params(1, 6, 4, 256, 64, window=8), -2),                      # Hq % Hkv
     (sa.Params(1, 4, 4, 256, 64), -4),                                # no window, no gate
     (sa.Params(1, 4, 4, 250, 64, block_size=64, top_k=2), -2),        # N % B
-    (sa.Params(1, 4, 4, 256, 64, block_size=32, top_k=2), -2),        # B % 64
+    (sa.Params(1, 4, 4, 256, 64, block_size=48, top_k=2), -2),        # B neither 8, 16, 32 nor a multiple of 64
+    (sa.Params(1, 4, 4, 256, 64, block_size=4, top_k=2), -2),         # B below 8
     (sa.Params(1, 4, 4, 256, 64, block_size=64, top_k=5), -2),        # top_k > n
     (sa.Params(1, 34, 1, 256, 64, window=8), -8),                     # group > 16
     (sa.Params(1, 4, 4, 64 * 40, 64, block_size=64, top_k=34), -8),   # top_k > 33

@@ -188,6 +188,41 @@ def test_gate_variants_small(dev, var, d):
     run_and_check(W.make_inputs(wl, 31 + d), dev, label=f"gate_var {var}")
 
 
+# Blocks smaller than the 64-key tile (Quest-style pages of 8, 16 or 32
+# keys): a tile holds several blocks, near tiles get per-key block bits and
+# a far block attends one masked tile.  N = 992 leaves a ragged 64-key tile.
+SMALL_BLOCK_CASES = [
+    dict(block_size=32, top_k=4),                                  # own + far blocks
+    dict(block_size=16, top_k=6, window=40),                       # near and far blocks
+    dict(block_size=8, top_k=8, window=100, sink=True),            # 13 near blocks
+    dict(block_size=16, top_k=5, gate_repr="minmax", sink=True),   # Quest's min/max pages
+    dict(block_size=32, top_k=3, window=70, gate_shared=True, gate_first=True),
+    dict(block_size=16, top_k=4, window=700),                      # window of 44 blocks
+]
+
+
+@pytest.mark.parametrize("case", range(len(SMALL_BLOCK_CASES)))
+@pytest.mark.parametrize("d", [64, 80, 128])
+def test_small_blocks(dev, case, d):
+    kw = SMALL_BLOCK_CASES[case]
+    wl = W.Workload("small_blk", 2, 8, 2, 992, d, "bf16", block_offsets=True, **kw)
+    run_and_check(W.make_inputs(wl, 141 + case + d), dev, label=f"small_blk {kw}")
+
+
+@pytest.mark.parametrize("B", [8, 16, 32])
+def test_small_blocks_dense(dev, B):
+    # k = n: every earlier block kept, dense causal attention
+    wl = W.Workload("small_blk_dense", 1, 4, 2, 32 * B, 64, "bf16", block_size=B, top_k=32,
+                    block_offsets=True)
+    run_and_check(W.make_inputs(wl, 150 + B), dev, label=f"small_blk_dense B={B}")
+
+
+def test_small_blocks_fp32(dev):
+    wl = W.Workload("small_blk_f32", 1, 4, 2, 384, 64, "f32", block_size=16, top_k=5, window=24,
+                    block_offsets=True, sink=True)
+    run_and_check(W.make_inputs(wl, 155), dev, label="small_blk_f32")
+
+
 @pytest.mark.parametrize("var", VARIANTS, ids=VARIANT_IDS)
 def test_gate_variants_fp32(dev, var):
     wl = W.Workload("gate_var_f32", 1, 4, 2, 384, 64, "f32", block_size=64, top_k=3, window=40,
@@ -411,6 +446,16 @@ def test_backward_ragged(dev):
 
 def test_backward_bora_all_rows(dev):
     bwd_and_check(W.make_inputs(W.BORA_HYBRID, 102), dev, 83, label="bwd_bora")
+
+
+@pytest.mark.parametrize("case", [0, 1, 2, 4, 5])
+@pytest.mark.parametrize("d", [64, 128])
+def test_backward_small_blocks(dev, case, d):
+    # blocks of 8, 16 and 32 keys (several per 64-key tile; 128-key dK/dV
+    # workgroups meet up to 16 blocks and their far lists)
+    kw = dict(SMALL_BLOCK_CASES[case])
+    wl = W.Workload("bwd_small_blk", 2, 4, 2, 992, d, "bf16", block_offsets=True, **kw)
+    bwd_and_check(W.make_inputs(wl, 161 + case + d), dev, 171 + case, label=f"bwd_small_blk {kw}")
 
 
 # The compressed branch's gradients (groups of C tokens; GQA 4/2, two
