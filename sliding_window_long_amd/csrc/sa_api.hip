@@ -38,7 +38,7 @@ struct Plan {
     bool gate_mm, gate_shared, gate_first;   // gate variants
     int gate_planes;
     bool cmp;               // compressed branch
-    int C, Nc;
+    int C, Nc, cmp_splits;
     bool far;
     long long max_entries;
     int max_chunks;
@@ -249,10 +249,16 @@ int make_plan(const sparse_attn_cfg* c, Plan* p, bool bwd = false) {
         P.Nc = P.N / P.C;
         const size_t ncmp = (size_t)P.Bt * P.Hkv * P.Nc * P.D;
         const int planes = P.f32 ? 2 : 1;
-        if (bwd) {   // bf16 K means and their scaled fp16 copy; bf16 V means; fp32 dK, dV per group
+        if (bwd) {
+            // bf16 K means and their scaled fp16 copy; bf16 V means; fp32
+            // dK, dV per group from cmp_splits row ranges (enough
+            // workgroups to fill the GPU: about 1024, at most 16 ranges)
             P.o_cmp_k = take(2 * ncmp * 2);
             P.o_cmp_v = take(ncmp * 2);
-            P.o_cmp_grad = take(2 * ncmp * 4);
+            const long long wgs = (long long)((P.Nc + 127) / 128) * P.Bt * P.Hkv;
+            long long sp = wgs > 0 ? (1024 + wgs - 1) / wgs : 1;
+            P.cmp_splits = (int)(sp < 1 ? 1 : sp > 16 ? 16 : sp);
+            P.o_cmp_grad = take((size_t)P.cmp_splits * 2 * ncmp * 4);
         } else {
             P.o_cmp_k = take(planes * ncmp * 2);
             P.o_cmp_v = take(planes * ncmp * 2);
@@ -848,8 +854,8 @@ int sparse_attn_bwd(const void* q, const void* k, const void* v, const void* out
                            nullptr, sk, 1};
         if (!ok(sa::launch_cmp_pool(cp, false, s))) return SA_E_HIP;
         ba.kc = kcp; ba.kc16 = kcp + ncmp; ba.vc = vcp;
-        ba.cmp_dk = (float*)(ws + P.o_cmp_grad); ba.cmp_dv = ba.cmp_dk + ncmp;
-        ba.C = P.C; ba.Nc = P.Nc;
+        ba.cmp_dk = (float*)(ws + P.o_cmp_grad); ba.cmp_dv = ba.cmp_dk + (size_t)P.cmp_splits * ncmp;
+        ba.C = P.C; ba.Nc = P.Nc; ba.cmp_splits = P.cmp_splits;
     }
     {
         StageScope t("bwd_delta", s);

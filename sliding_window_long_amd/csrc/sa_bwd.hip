@@ -614,7 +614,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkv_kernel(BwdArgs a) {
     const int N = a.N, G = a.Hq / a.Hkv;
     const int Nk = CMP ? a.Nc : N;   // keys: tokens, or compressed groups
     const int ntiles = (Nk + RT - 1) / RT;
-    const int bg = blockIdx.x / ntiles, ktile = blockIdx.x % ntiles;
+    // CMP: cmp_splits workgroups share one 128-group key tile, each a
+    // contiguous range of its row tiles.
+    const int nsp = CMP ? a.cmp_splits : 1;
+    const int sp = CMP ? (int)(blockIdx.x % nsp) : 0;
+    const int wg = CMP ? (int)(blockIdx.x / nsp) : (int)blockIdx.x;
+    const int bg = wg / ntiles, ktile = wg % ntiles;
     const int b = bg / a.Hkv, g = bg % a.Hkv;
     const int k0 = ktile * RT;
     const int k_hi = min(k0 + RT - 1, Nk - 1);
@@ -662,7 +667,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkv_kernel(BwdArgs a) {
     }
     const int n_rt = r_end >= r_beg ? (r_end - r_beg) / KT + 1 : 0;
     const int nt32k = (N + 31) / 32, nt64k = (N + KT - 1) / KT;   // key-major mask tiles
-    const int n1 = G * n_rt;
+    // Row tiles ib .. ib + n1 - 1 of the G * n_rt (all of them but under CMP).
+    const int ib = CMP ? (int)((long long)G * n_rt * sp / nsp) : 0;
+    const int n1 = CMP ? (int)((long long)G * n_rt * (sp + 1) / nsp) - ib : G * n_rt;
     // The table lives in LDS (a runtime-indexed register array would live
     // in scratch, whose loads wait for every tile load in flight).
     const bool has_far = !CMP && a.sel && a.list_off;
@@ -708,7 +715,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkv_kernel(BwdArgs a) {
     auto fetch = [&](int i, int r, int ent) __attribute__((always_inline)) -> RowData {
         RowData rd{-1, 0, 0.f, 0.f, 0ull};
         if (i < n1) {
-            const int hl = i / n_rt, rr = r_beg + (i % n_rt) * KT + r;
+            const int hl = (ib + i) / n_rt, rr = r_beg + ((ib + i) % n_rt) * KT + r;
             rd.rr = rr;
             if (rr < N) rd.id = (int)((size_t)(b * a.Hq + g * G + hl) * N + rr);
         } else if (ent >= 0) {   // entry = (i*G + head in group)*kslots + slot
@@ -751,7 +758,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkv_kernel(BwdArgs a) {
         qk_tile<D, 1>(q_, kf, s, lane);
         qk_tile<D, 1>(do_, vf, dp, lane);
         if (CMP) {
-            mask_rows_cmp(s, r_beg + (i % n_rt) * KT + 4 * hh - ((key + 1) * a.C - 1));
+            mask_rows_cmp(s, r_beg + ((ib + i) % n_rt) * KT + 4 * hh - ((key + 1) * a.C - 1));
         } else if (i >= n1) {
             // every key of the far block, none of the other blocks
             const int far_kb = far_list(i - n1);
@@ -836,8 +843,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkv_kernel(BwdArgs a) {
     if (!ok) return;
     if constexpr (CMP) {
         const float invc = 1.f / (float)a.C;
-        write_rows_f32<D>(a.cmp_dk + pkey * D, dk, a.scale * invc, es + a.sq[bg], hh);
-        write_rows_f32<D>(a.cmp_dv + pkey * D, dv, invc, a.sd[bg], hh);
+        const size_t part = (size_t)sp * a.Bt * a.Hkv * a.Nc + pkey;   // this split's row
+        write_rows_f32<D>(a.cmp_dk + part * D, dk, a.scale * invc, es + a.sq[bg], hh);
+        write_rows_f32<D>(a.cmp_dv + part * D, dv, invc, a.sd[bg], hh);
     } else {
         // the share of the key's compressed group (tokens past the last
         // complete group have none)
@@ -848,6 +856,21 @@ __global__ __launch_bounds__(NTHREADS, 1) void bwd_dkv_kernel(BwdArgs a) {
         write_rows_bf16_add<D>(a.dv + pkey * D, dv, 1.f, a.sd[bg], hh,
                                grp ? a.cmp_dv + prow_c : nullptr);
     }
+}
+
+// The compressed groups' dK, dV: split 0 += splits 1 .. cmp_splits - 1, in
+// order (one thread per 4 floats of dK, then of dV).
+__global__ __launch_bounds__(256) void cmp_split_sum_kernel(BwdArgs a, size_t n4) {
+    const size_t x = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (x >= 2 * n4) return;
+    float4* base = (float4*)(x < n4 ? a.cmp_dk : a.cmp_dv);
+    const size_t i = x < n4 ? x : x - n4;
+    float4 acc = base[i];
+    for (int sp = 1; sp < a.cmp_splits; ++sp) {
+        const float4 p = base[(size_t)sp * n4 + i];
+        acc.x += p.x; acc.y += p.y; acc.z += p.z; acc.w += p.w;
+    }
+    base[i] = acc;
 }
 
 template <int D>
@@ -867,9 +890,16 @@ static hipError_t bwd_d(const BwdArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     if (cmp) {   // the groups' dK, dV first: the token pass adds them
         const int ntc = (a.Nc + RT - 1) / RT;
-        hipLaunchKernelGGL((bwd_dkv_kernel<D, true>), dim3(ntc * a.Bt * a.Hkv), dim3(NTHREADS), 0, s, a);
+        hipLaunchKernelGGL((bwd_dkv_kernel<D, true>), dim3(ntc * a.Bt * a.Hkv * a.cmp_splits), dim3(NTHREADS),
+                           0, s, a);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
+        if (a.cmp_splits > 1) {
+            const size_t n4 = (size_t)a.Bt * a.Hkv * a.Nc * D / 4;
+            hipLaunchKernelGGL(cmp_split_sum_kernel, dim3((unsigned)((2 * n4 + 255) / 256)), dim3(256), 0, s, a, n4);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
     }
     hipLaunchKernelGGL((bwd_dkv_kernel<D, false>), dim3(nt * a.Bt * a.Hkv), dim3(NTHREADS), 0, s, a);
     return hipGetLastError();

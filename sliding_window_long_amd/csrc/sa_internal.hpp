@@ -179,9 +179,9 @@ struct BwdArgs {
     const uint16_t* kc;
     const uint16_t* kc16;
     const uint16_t* vc;
-    float* cmp_dk;
-    float* cmp_dv;
-    int C, Nc;
+    float* cmp_dk;          // [cmp_splits][Bt*Hkv*Nc, D] partials over row ranges;
+    float* cmp_dv;          // summed in order into split 0
+    int C, Nc, cmp_splits;
     int top_k, B, n, span, kslots;
     int Bt, Hq, Hkv, N, D, window;
     float scale;

@@ -245,11 +245,12 @@ def test_backward_configs(lib):
     base = (2 * 512 * 64 * 2) + 2 * (4 * 512 * 64 * 2) + 4 * 512 * 4 + ranges
     assert n.value == base
     # the compressed branch (groups of 8): bf16 K means and their scaled fp16
-    # copy, bf16 V means, and fp32 dK, dV per group
+    # copy, bf16 V means, and fp32 dK, dV per group from 16 row ranges (two
+    # key tiles of 128 groups are far fewer workgroups than the GPU holds)
     p = sa.Params(1, 4, 2, 512, 64, window=16, cmp_block=8)
     sa.load_library().sparse_attn_bwd_workspace_bytes(ctypes.byref(p.cfg()), ctypes.byref(n))
     ncmp = 2 * 64 * 64
-    assert n.value == base + 3 * ncmp * 2 + 2 * ncmp * 4
+    assert n.value == base + 3 * ncmp * 2 + 16 * 2 * ncmp * 4
 
 
 def test_backward_rejects_before_launch(lib):
