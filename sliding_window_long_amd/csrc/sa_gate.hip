@@ -6,12 +6,14 @@
 // own block plus the min(top_k-1, b) best earlier ones (ties toward the
 // lower block id), and never sees a later block.
 //
-// Accuracy: the pooled keys are split into three bf16 terms
-// (mean = hi + mid + lo to about 24 bits) so the score GEMM runs on bf16
-// matrix cores with fp32 accumulation and still carries fp32-level
-// accuracy -- a single bf16 rounding of the mean (2^-9 relative) would flip
-// selections whose top-k margin is far larger than the accepted tolerance.
-// This is the bf16x3 splitting of Henry, Tang and Heinecke (ARITH 2019).
+// Accuracy: the pooled keys are split into bf16 terms so the score GEMM runs
+// on bf16 matrix cores with fp32 accumulation -- a single bf16 rounding of
+// the mean (2^-9 relative) would flip selections whose top-k margin is far
+// larger than the accepted tolerance.  For bf16 queries two terms (mean = hi
+// + lo to about 17 bits) match what the order key keeps of a score (its
+// low idx_bits carry the block index: 23 - idx_bits mantissa bits); fp32
+// queries take three (hi + mid + lo, about 24 bits).  This is the bf16x3
+// splitting of Henry, Tang and Heinecke (ARITH 2019).
 //
 // Top-k: each lane owns one query row (lane pair l, l^32 split the blocks),
 // packs every score into a 32-bit key that orders like the float and breaks
@@ -30,6 +32,13 @@ namespace sa {
 // the block's keys; MM = true: their per-dimension min and max [MoBA summary
 // page, the remark on Quest's min/max-pooled block representation].
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ void split2(float x, uint16_t* dst, size_t plane, size_t o) {
+    const __bf16 hi = (__bf16)x;
+    const __bf16 lo = (__bf16)(x - (float)hi);
+    dst[o] = __builtin_bit_cast(uint16_t, hi);
+    dst[plane + o] = __builtin_bit_cast(uint16_t, lo);
+}
+
 __device__ __forceinline__ void split3(float x, uint16_t* dst, size_t plane, size_t o) {
     const __bf16 hi = (__bf16)x;
     const float r1 = x - (float)hi;
@@ -116,7 +125,10 @@ __global__ __launch_bounds__(256) void pool_kernel(PoolArgs a) {
             for (int r = 0; r < NG; ++r) sum += red[0][r * D + tid];
             const float mean = sum / (float)a.B;
             if (a.kbar) a.kbar[o] = mean;
-            if (a.kb3) split3(mean, a.kb3, a.plane, o);
+            if (a.kb3) {
+                if constexpr (F32IN) split3(mean, a.kb3, a.plane, o);
+                else split2(mean, a.kb3, a.plane, o);
+            }
         }
     }
 }
@@ -201,7 +213,7 @@ __device__ __forceinline__ void sign_split(const bf16x8& x, const bf16x8& sgn, b
     pos = as_bf16x8(make_uint4(u.x & ~m0, u.y & ~m1, u.z & ~m2, u.w & ~m3));
 }
 
-// MM = false: NP = 3 planes of the mean.  MM = true: the min/max summary,
+// MM = false: NP planes of the mean (2 for bf16 keys, 3 for fp32).  MM = true: the min/max summary,
 // NP / 2 planes of the max then of the min; the score
 // sum_e max(q_e min_e, q_e max_e) is <q+, max> + <q-, min> with q+ and q-
 // the positive and negative parts of q, two exact products on the matrix
@@ -283,12 +295,14 @@ __global__ __launch_bounds__(64 * gate_waves(QSPLIT)) void gate_kernel(GateArgs 
 #pragma unroll
             for (int ks = 0; ks < DK; ++ks) {
                 if constexpr (!MM) {
+                    // NP terms of the mean against q (and q's lo term against
+                    // all but the last)
 #pragma unroll
-                    for (int p = 0; p < 3; ++p) {
+                    for (int p = 0; p < NP; ++p) {
                         const bf16x8 av = *(const bf16x8*)(src + p * GT::PLANE + ks * 16);
                         acc = mfma32(av, qf[0][ks], acc);
                         if constexpr (QSPLIT >= 2) {
-                            if (p < 2) acc = mfma32(av, qf[1][ks], acc);
+                            if (p < NP - 1) acc = mfma32(av, qf[1][ks], acc);
                         }
                     }
                 } else {
@@ -442,8 +456,11 @@ static hipError_t gate_v(const GateArgs& a, int head_dim, hipStream_t s) {
 // planes come with fp32 (split) queries only.
 hipError_t launch_gate(const GateArgs& a, int head_dim, int qsplit, int planes, bool minmax,
                        hipStream_t s) {
-    if (!minmax && planes == 3) {
-        if (qsplit == 1) return gate_v<1, 3, false>(a, head_dim, s);
+    if (!minmax && planes == 2) {   // bf16 keys
+        if (qsplit == 1) return gate_v<1, 2, false>(a, head_dim, s);
+        if (qsplit == 2) return gate_v<2, 2, false>(a, head_dim, s);
+    }
+    if (!minmax && planes == 3) {   // fp32 keys
         if (qsplit == 2) return gate_v<2, 3, false>(a, head_dim, s);
     }
     if (minmax && planes == 2) {

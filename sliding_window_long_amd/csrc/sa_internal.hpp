@@ -66,10 +66,10 @@ struct PoolArgs {
     int minmax;             // 0: mean; 1: per-dimension min and max
 };
 
-// bf16 planes of the pooled keys the gate reads: the mean split into three
-// terms; min/max as the max terms then the min terms, one term each for
-// bf16 keys (exact) and three for fp32 keys.
-inline int gate_planes(bool minmax, bool f32) { return minmax ? (f32 ? 6 : 2) : 3; }
+// bf16 planes of the pooled keys the gate reads: the mean split into two
+// terms for bf16 keys, three for fp32 keys; min/max as the max terms then
+// the min terms, one term each for bf16 keys (exact) and three for fp32.
+inline int gate_planes(bool minmax, bool f32) { return minmax ? (f32 ? 6 : 2) : (f32 ? 3 : 2); }
 
 // Block gate: scores against the pooled keys and top-(k-1) earlier blocks.
 // Rows are (batch, head, position) over Hq heads of q; each row's selection
