@@ -88,6 +88,11 @@ def _load(path=None):
                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, _i64,
                                    _f64p, _f64p, _f64p, _f64p]
     lib.orc_attend_bwd.restype = ctypes.c_int
+    lib.orc_attend_bwd_at.argtypes = [_f32p, _f32p, _f32p, _f32p, _i64, _i64, _i64, _i64, _i64,
+                                      ctypes.c_double, _i64, _i64, ctypes.c_void_p, _i64,
+                                      ctypes.c_void_p, _i64, ctypes.c_void_p,
+                                      _i64p, _i64, _i64p, _i64, _f64p, _f64p, _f64p]
+    lib.orc_attend_bwd_at.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -358,6 +363,44 @@ def attend_bwd(q, k, v, dout, *, scale=None, window=0, block_size=0, sel=None, t
     if rc != 0:
         raise ValueError("selection id out of range")
     return dq, dk, dv, (dsink if sink is not None else None)
+
+
+def attend_bwd_at(q, k, v, dout, *, rows, keys, scale=None, window=0, block_size=0, sel=None,
+                  tsel=None, sink=None):
+    """attend_bwd at listed outputs (no compressed columns): dq of the q
+    rows `rows` (flat ids (b*Hq + h)*N + i) and dk, dv of the keys `keys`
+    (flat ids (b*Hkv + g)*N + j), for a fixed selection of every row (sel
+    [Bt*Hq*N, w] or None, tsel [Bt*N, w'] or None).  Returns (dq
+    [len(rows), d], dk [len(keys), d], dv [len(keys), d]) fp64."""
+    q, k, v, dout = _f32(q), _f32(k), _f32(v), _f32(dout)
+    Bt, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape[2] != N or dout.shape != q.shape:
+        raise ValueError("the backward is a prefill: q, k, v, dout over the same positions")
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    scale = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    sel_a = None if sel is None else np.ascontiguousarray(sel, dtype=np.int32)
+    if sel_a is not None and sel_a.shape[0] != Bt * Hq * N:
+        raise ValueError("sel holds one row per query row")
+    tsel_a = None if tsel is None else np.ascontiguousarray(tsel, dtype=np.int32)
+    if tsel_a is not None and tsel_a.shape[0] != Bt * N:
+        raise ValueError("tsel holds one row per position")
+    sink_a = None if sink is None else _f32(sink)
+    rows_a = np.ascontiguousarray(rows, dtype=np.int64)
+    keys_a = np.ascontiguousarray(keys, dtype=np.int64)
+    dq = np.empty((len(rows_a), d), dtype=np.float64)
+    dk = np.empty((len(keys_a), d), dtype=np.float64)
+    dv = np.empty((len(keys_a), d), dtype=np.float64)
+    rc = _load().orc_attend_bwd_at(
+        q, k, v, dout, Bt, Hq, Hkv, N, d, scale, int(window), int(block_size),
+        None if sel_a is None else sel_a.ctypes.data, 0 if sel_a is None else sel_a.shape[1],
+        None if tsel_a is None else tsel_a.ctypes.data, 0 if tsel_a is None else tsel_a.shape[1],
+        None if sink_a is None else sink_a.ctypes.data, rows_a, len(rows_a), keys_a, len(keys_a),
+        dq, dk, dv)
+    if rc != 0:
+        raise ValueError("row, key or selection id out of range")
+    return dq, dk, dv
 
 
 def backward(q, k, v, dout, *, block_size=0, top_k=0, window=0, sink=None, scale=None,

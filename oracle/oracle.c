@@ -595,3 +595,164 @@ int orc_attend_bwd(const float* q, const float* k, const float* v, const float* 
     }
     return bad ? -1 : 0;
 }
+
+/*
+ * The same gradients as orc_attend_bwd (no compressed columns) at listed
+ * outputs only, for shapes where the full backward is out of reach: dq of
+ * the listed q rows (rows: flat ids (b*Hq + h)*N + i) and dk, dv of the
+ * listed keys (keys: flat ids (b*Hkv + g)*N + j).  dq_i needs row i's
+ * attention alone; dk_j and dv_j sum over every row of the kv group's heads
+ * whose attended set A(i) holds j (the window, a kept block or a kept
+ * token), each with its own lse_i and D_i.  sel [Bt*Hq*N, sel_w] and tsel
+ * [Bt*N, tsel_w] are the selections of every row.  Returns 0, or -1 if an id
+ * is out of range.
+ */
+static void row_mark(unsigned char* mark, int64_t r, int64_t i, int64_t b, int64_t N,
+                     int64_t window, int64_t B, const int32_t* sel, int64_t sel_w,
+                     const int32_t* tsel, int64_t tsel_w, int* bad) {
+    memset(mark, 0, (size_t)(i + 1));
+    if (window > 0)
+        for (int64_t j = (i - window + 1 > 0 ? i - window + 1 : 0); j <= i; ++j) mark[j] = 1;
+    if (sel)
+        for (int64_t s = 0; s < sel_w; ++s) {
+            const int64_t c = sel[r * sel_w + s];
+            if (c < 0) continue;
+            if (B <= 0 || c >= N / B) { *bad = 1; continue; }
+            for (int64_t j = c * B; j < (c + 1) * B && j <= i; ++j) mark[j] = 1;
+        }
+    if (tsel)
+        for (int64_t s = 0; s < tsel_w; ++s) {
+            const int64_t j = tsel[(b * N + i) * tsel_w + s];
+            if (j < 0) continue;
+            if (j >= N) { *bad = 1; continue; }
+            if (j <= i) mark[j] = 1;
+        }
+}
+
+/* Whether row r (position i, batch b) attends key j <= i: the window, a
+ * kept block holding j, or j kept as a token (row_mark's rule for one key). */
+static int row_attends(int64_t r, int64_t i, int64_t b, int64_t j, int64_t N, int64_t window,
+                       int64_t B, const int32_t* sel, int64_t sel_w, const int32_t* tsel,
+                       int64_t tsel_w) {
+    if (j > i) return 0;
+    if (window > 0 && i - j < window) return 1;
+    if (sel && B > 0)
+        for (int64_t s = 0; s < sel_w; ++s)
+            if (sel[r * sel_w + s] == j / B) return 1;
+    if (tsel)
+        for (int64_t s = 0; s < tsel_w; ++s)
+            if (tsel[(b * N + i) * tsel_w + s] == j) return 1;
+    return 0;
+}
+
+/* Row i of head h over its marked keys: logits x, lse, and D = <dO_i, out_i>. */
+static void row_stats(const unsigned char* mark, const float* qrow, const float* dorow,
+                      const float* kb, const float* vb, int64_t i, int64_t d, double scale,
+                      double z, double* x, double* o, double* lse, double* Di) {
+    double M = -INFINITY;
+    for (int64_t j = 0; j <= i; ++j) {
+        if (!mark[j]) continue;
+        double acc = 0.0;
+        for (int64_t e = 0; e < d; ++e) acc += (double)qrow[e] * (double)kb[j * d + e];
+        x[j] = scale * acc;
+        if (x[j] > M) M = x[j];
+    }
+    if (z > M) M = z;
+    double L = 0.0;
+    for (int64_t e = 0; e < d; ++e) o[e] = 0.0;
+    for (int64_t j = 0; j <= i; ++j) {
+        if (!mark[j]) continue;
+        const double p = exp(x[j] - M);
+        L += p;
+        for (int64_t e = 0; e < d; ++e) o[e] += p * (double)vb[j * d + e];
+    }
+    if (z > -INFINITY) L += exp(z - M);
+    *lse = M + log(L);
+    double s = 0.0;
+    for (int64_t e = 0; e < d; ++e) s += (double)dorow[e] * (o[e] / L);
+    *Di = s;
+}
+
+int orc_attend_bwd_at(const float* q, const float* k, const float* v, const float* dout,
+                      int64_t Bt, int64_t Hq, int64_t Hkv, int64_t N, int64_t d,
+                      double scale, int64_t window, int64_t B,
+                      const int32_t* sel, int64_t sel_w,
+                      const int32_t* tsel, int64_t tsel_w, const float* sink,
+                      const int64_t* rows, int64_t nrows, const int64_t* keys, int64_t nkeys,
+                      double* dq, double* dk, double* dv) {
+    const int64_t G = Hq / Hkv;
+    int bad = 0;
+    for (int64_t t = 0; t < nrows; ++t)
+        if (rows[t] < 0 || rows[t] >= Bt * Hq * N) return -1;
+    for (int64_t t = 0; t < nkeys; ++t)
+        if (keys[t] < 0 || keys[t] >= Bt * Hkv * N) return -1;
+    memset(dk, 0, sizeof(double) * (size_t)(nkeys * d));
+    memset(dv, 0, sizeof(double) * (size_t)(nkeys * d));
+#pragma omp parallel
+    {
+        unsigned char* mark = (unsigned char*)malloc((size_t)(N > 0 ? N : 1));
+        double* x = (double*)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+        double* o = (double*)malloc(sizeof(double) * (size_t)(d > 0 ? d : 1));
+        double* acc_k = (double*)malloc(sizeof(double) * (size_t)(d > 0 ? d : 1));
+        double* acc_v = (double*)malloc(sizeof(double) * (size_t)(d > 0 ? d : 1));
+        /* dq of the listed rows */
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t t = 0; t < nrows; ++t) {
+            const int64_t r = rows[t], i = r % N, bh = r / N, b = bh / Hq, h = bh % Hq, g = h / G;
+            const float* kb = k + (b * Hkv + g) * N * d;
+            const float* vb = v + (b * Hkv + g) * N * d;
+            row_mark(mark, r, i, b, N, window, B, sel, sel_w, tsel, tsel_w, &bad);
+            double lse, Di;
+            const double z = sink ? (double)sink[h] : -INFINITY;
+            row_stats(mark, q + r * d, dout + r * d, kb, vb, i, d, scale, z, x, o, &lse, &Di);
+            double* dqr = dq + t * d;
+            for (int64_t e = 0; e < d; ++e) dqr[e] = 0.0;
+            for (int64_t j = 0; j <= i; ++j) {
+                if (!mark[j]) continue;
+                const double p = exp(x[j] - lse);
+                double dp = 0.0;
+                for (int64_t e = 0; e < d; ++e) dp += (double)dout[r * d + e] * (double)vb[j * d + e];
+                const double ds = p * (dp - Di);
+                for (int64_t e = 0; e < d; ++e) dqr[e] += scale * ds * (double)kb[j * d + e];
+            }
+        }
+        /* dk, dv of the listed keys: every row of the group's heads attending j */
+        for (int64_t t = 0; t < nkeys; ++t) {
+            const int64_t bg = keys[t] / N, j = keys[t] % N, b = bg / Hkv, g = bg % Hkv;
+            const float* kb = k + bg * N * d;
+            const float* vb = v + bg * N * d;
+            for (int64_t e = 0; e < d; ++e) acc_k[e] = acc_v[e] = 0.0;
+#pragma omp for schedule(dynamic, 16)
+            for (int64_t u = 0; u < G * (N - j); ++u) {
+                const int64_t h = g * G + u / (N - j), i = j + u % (N - j);
+                const int64_t r = (b * Hq + h) * N + i;
+                if (!row_attends(r, i, b, j, N, window, B, sel, sel_w, tsel, tsel_w)) continue;
+                row_mark(mark, r, i, b, N, window, B, sel, sel_w, tsel, tsel_w, &bad);
+                if (!mark[j]) continue;
+                double lse, Di;
+                const double z = sink ? (double)sink[h] : -INFINITY;
+                row_stats(mark, q + r * d, dout + r * d, kb, vb, i, d, scale, z, x, o, &lse, &Di);
+                const double p = exp(x[j] - lse);
+                double dp = 0.0;
+                for (int64_t e = 0; e < d; ++e) dp += (double)dout[r * d + e] * (double)vb[j * d + e];
+                const double ds = p * (dp - Di);
+                for (int64_t e = 0; e < d; ++e) {
+                    acc_k[e] += scale * ds * (double)q[r * d + e];
+                    acc_v[e] += p * (double)dout[r * d + e];
+                }
+            }
+#pragma omp critical
+            for (int64_t e = 0; e < d; ++e) {
+                dk[t * d + e] += acc_k[e];
+                dv[t * d + e] += acc_v[e];
+            }
+#pragma omp barrier
+        }
+        free(mark);
+        free(x);
+        free(o);
+        free(acc_k);
+        free(acc_v);
+    }
+    return bad ? -1 : 0;
+}

@@ -222,5 +222,21 @@ def check_grads(inp, dout, dev_sel, dev_grads, *, sink=None, joint_floor=True, d
     return res
 
 
+def check_grads_at(dev, ref):
+    """check_grads at listed outputs: dev and ref are (dq of listed rows, dk
+    and dv of listed keys) as [n, d] arrays; the same relative measures, with
+    the floor at 1e-2 of the largest |g*| (and of the largest mean |g*|) over
+    the three.  Returns {name: (max_rel, mean_rel)}."""
+    ref = [np.asarray(r, dtype=np.float64) for r in ref]
+    joint_max = max(float(np.abs(r).max()) for r in ref)
+    joint_mean = max(float(np.abs(r).mean()) for r in ref)
+    res = {}
+    for name, g, r in zip(("dq", "dk", "dv"), dev, ref):
+        err = np.abs(np.asarray(g, dtype=np.float64) - r)
+        res[name] = (float(err.max() / max(np.abs(r).max(), 1e-2 * joint_max)),
+                     float(err.mean() / max(np.abs(r).mean(), 1e-2 * joint_mean)))
+    return res
+
+
 def grads_ok(res) -> bool:
     return all(m <= GRAD_MAX and a <= GRAD_MEAN for m, a in res.values())

@@ -458,6 +458,61 @@ def test_backward_small_blocks(dev, case, d):
     bwd_and_check(W.make_inputs(wl, 161 + case + d), dev, 171 + case, label=f"bwd_small_blk {kw}")
 
 
+# Full-size backward in the benchmark's configuration, checked at listed
+# outputs: dq of sampled rows (first/last rows of each head, block and
+# window edges, random rows) and dk, dv of keys at window and block edges,
+# each against every row that attends it (the device's selection held
+# fixed).
+def bwd_at_and_check(inp, dev, seed, rows, keys, label):
+    from parity import check_grads_at
+    wl = inp.wl
+    d = wl.head_dim
+    log(f"[gpu] {label} {wl} rows={len(rows)} keys={len(keys)}")
+    dout, sel, grads = run_backward(inp, dev, seed)
+    dq, dk, dv, _ = grads
+    tok = wl.token_top_k > 0
+    ref = oracle.attend_bwd_at(
+        inp.q, inp.k, inp.v, dout, rows=rows, keys=keys, window=wl.window,
+        block_size=wl.block_size, sink=inp.sink,
+        sel=None if (tok or sel is None) else sel.reshape(-1, wl.top_k),
+        tsel=sel.reshape(-1, wl.token_top_k) if tok else None)
+    got = (dq.reshape(-1, d)[rows], dk.reshape(-1, d)[keys], dv.reshape(-1, d)[keys])
+    for x in got:
+        assert np.isfinite(x).all()
+    res = check_grads_at(got, ref)
+    log(f"[gpu] {label} " + " ".join(f"{k}: max {m:.2e} mean {a:.2e}" for k, (m, a) in res.items()))
+    assert grads_ok(res), str(res)
+
+
+def _keys(wl, pairs):
+    return np.array([g * wl.seq_len + j for g, j in pairs], dtype=np.int64)
+
+
+def test_backward_bitaxon_full_sampled(dev):
+    wl = W.BITAXON_SWA   # 32 heads, N 16384, d 80, window 4096
+    N = wl.seq_len
+    keys = _keys(wl, [(0, 0), (3, 1), (7, 4095), (12, 4096), (20, 8191), (17, 12345), (31, N - 1)])
+    bwd_at_and_check(W.make_inputs(wl, 103), dev, 87, W.sample_rows(wl, 96, 5), keys,
+                     "bwd_bitaxon_full")
+
+
+def test_backward_long_moba_full_sampled(dev):
+    wl = W.LONG_MOBA     # 32/8 heads, N 131072, d 128, blocks of 512, top 8
+    B, N = wl.block_size, wl.seq_len
+    keys = _keys(wl, [(0, N - 1), (3, 255 * B + 5), (5, 250 * B + 100), (7, 200 * B + B - 1),
+                      (2, 160 * B), (6, 128 * B + 300)])
+    bwd_at_and_check(W.make_inputs(wl, 104), dev, 88, W.sample_rows(wl, 96, 6), keys,
+                     "bwd_long_moba_full")
+
+
+def test_backward_token_full_sampled(dev):
+    wl = W.SWA_TOKEN_TOPK   # 16/4 heads, N 65536, d 128, window 128, top 2048 tokens, sink
+    N = wl.seq_len
+    keys = _keys(wl, [(0, N - 1), (1, N - 130), (2, 60000), (3, 40000), (0, 32768)])
+    bwd_at_and_check(W.make_inputs(wl, 105), dev, 89, W.sample_rows(wl, 96, 7), keys,
+                     "bwd_token_full")
+
+
 # The compressed branch's gradients (groups of C tokens; GQA 4/2, two
 # batches): ragged N and tails past the last group, with a window, block
 # gating and its shared variant, a sink; C = 1 (every token also its own

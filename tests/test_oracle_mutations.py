@@ -59,6 +59,16 @@ MUTATIONS = [
     ("backward group gradient not shared over its tokens", [
         ("dkb[j * d + e] += dkc[(j / C) * d + e] / (double)C;",
          "dkb[j * d + e] += dkc[(j / C) * d + e];")]),
+    ("listed-output backward skips the last row", [("for (int64_t u = 0; u < G * (N - j); ++u) {",
+                                                    "for (int64_t u = 0; u < G * (N - j) - 1; ++u) {")]),
+    ("listed-output backward reads another head", [("const int64_t h = g * G + u / (N - j), i = j + u % (N - j);",
+                                                    "const int64_t h = g + u / (N - j), i = j + u % (N - j);")]),
+    ("listed-output dv from the query", [("acc_v[e] += p * (double)dout[r * d + e];",
+                                          "acc_v[e] += p * (double)q[r * d + e];")]),
+    ("listed-output dq without the D term", [
+        ("const double ds = p * (dp - Di);\n                for (int64_t e = 0; e < d; ++e) dqr[e]",
+         "const double ds = p * dp;\n                for (int64_t e = 0; e < d; ++e) dqr[e]")]),
+    ("listed-output sink left out of the row", [("if (z > -INFINITY) L += exp(z - M);", "")]),
     ("backward group value gradient to the next group", [
         ("dvb[j * d + e] += dvc[(j / C) * d + e] / (double)C;",
          "dvb[j * d + e] += dvc[((j / C + 1) % Nc) * d + e] / (double)C;")]),
@@ -131,6 +141,10 @@ PIN_CALLS = [
 ] + [
     lambda: pins.test_p29_backward_matches_finite_differences(),
     lambda: pins.test_p30_key_gradients_sum_to_sink_term(True, 0),
+] + [
+    (lambda kw=kw: pins.test_p31_backward_at_listed_outputs(kw))
+    for kw in (dict(window=5, sink=True), dict(block_size=4, top_k=3, window=3),
+               dict(window=2, token_top_k=5, sink=True))
 ] + [
     (lambda c=c: pins.test_p28_compressed_backward_is_autograd(c))
     for c in range(len(pins.CMP_BWD_CASES))

@@ -855,6 +855,38 @@ def test_p29_compressed_backward_matches_finite_differences():
             assert abs(fd - grad[idx]) <= 1e-5 * max(1.0, abs(grad[idx])), (name, idx, fd, grad[idx])
 
 
+# P31: the backward at listed outputs (dq of some rows, dk and dv of some
+# keys) equals the full backward there (window, kept blocks or kept tokens,
+# sink, GQA 4/2; every key of one kv group and rows of every head).
+@pytest.mark.parametrize("kw", [
+    dict(window=5, sink=True),
+    dict(block_size=4, top_k=3, window=3),
+    dict(window=2, token_top_k=5, sink=True),
+])
+def test_p31_backward_at_listed_outputs(kw):
+    kw = dict(kw)
+    use_sink = kw.pop("sink", False)
+    Bt, Hq, Hkv, N, d = 2, 4, 2, 24, 8
+    q, k, v = rnd((Bt, Hq, N, d), 490), rnd((Bt, Hkv, N, d), 491), rnd((Bt, Hkv, N, d), 492)
+    dout, sink = rnd((Bt, Hq, N, d), 493), (rnd((Hq,), 494) if use_sink else None)
+    iq = ik = None
+    if kw.get("token_top_k"):
+        iq, ik = rnd((Bt, N, 8), 495), rnd((Bt, N, 8), 496)
+    dq, dk, dv, _, sel = oracle.backward(q, k, v, dout, sink=sink, idx_q=iq, idx_k=ik, **kw)
+    tok = kw.get("token_top_k", 0) > 0
+    rows = np.array([0, 5, 23, 24 * 3 + 11, 24 * 6 + 23, 24 * 7 + 1])
+    keys = np.arange(Bt * Hkv * N)[N: 2 * N]          # every key of (b 0, g 1)
+    keys = np.concatenate([keys, [2 * N + 3, 3 * N + 23]])
+    gq, gk, gv = oracle.attend_bwd_at(q, k, v, dout, rows=rows, keys=keys,
+                                      window=kw.get("window", 0),
+                                      block_size=kw.get("block_size", 0),
+                                      sel=None if tok else sel, tsel=sel if tok else None,
+                                      sink=sink)
+    np.testing.assert_allclose(gq, dq.reshape(-1, d)[rows], atol=1e-12)
+    np.testing.assert_allclose(gk, dk.reshape(-1, d)[keys], atol=1e-12)
+    np.testing.assert_allclose(gv, dv.reshape(-1, d)[keys], atol=1e-12)
+
+
 # P30: shifting all logits of a row leaves its output unchanged, so the
 # score gradients of a row sum to minus that of its sink column: summed over
 # the keys of a kv group, dk = scale * sum_i q_i P_i,sink D_i (zero without a

@@ -21,7 +21,7 @@ import pytest
 
 import oracle
 import workloads as W
-from parity import GAP_REL, check, check_grads, grads_ok
+from parity import GAP_REL, check, check_grads, check_grads_at, grads_ok
 
 GATE_WL = W.Workload("pc_gate", 1, 2, 1, 768, 64, "bf16", block_size=64, top_k=4, window=0,
                      block_offsets=True)
@@ -374,6 +374,28 @@ def test_grad_faults_fail(grad_case, name, kind):
         x *= 1 + 1.1e-2
     res = check_grads(inp, dout, sel, g, sink=inp.sink)
     assert not grads_ok(res), (name, kind, res)
+
+
+@pytest.mark.parametrize("name,kind", [(None, None), ("dq", "max"), ("dk", "max"), ("dv", "max"),
+                                       ("dk", "mean"), ("dv", "mean")])
+def test_grad_at_listed_outputs(grad_case, name, kind):
+    # the checker of sampled gradients: the oracle's own values pass, a 3e-2
+    # error at the largest entry or a 1.1e-2 mean shift of one tensor fails
+    inp, dout, sel, ref = grad_case
+    d = inp.q.shape[-1]
+    rows, keys = np.array([0, 40, 191, 250, 383]), np.array([3, 64, 100, 191])
+    want = [ref[0].reshape(-1, d)[rows], ref[1].reshape(-1, d)[keys], ref[2].reshape(-1, d)[keys]]
+    got = [w.astype(np.float32).astype(np.float64) for w in want]
+    if name is None:
+        assert grads_ok(check_grads_at(got, want))
+        return
+    x = got[("dq", "dk", "dv").index(name)].reshape(-1)
+    if kind == "max":
+        j = int(np.argmax(np.abs(x)))
+        x[j] += 3e-2 * np.abs(x).max()
+    else:
+        x *= 1 + 1.1e-2
+    assert not grads_ok(check_grads_at(got, want)), (name, kind)
 
 
 def test_grad_per_tensor_floor(grad_case):
