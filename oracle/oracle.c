@@ -703,8 +703,8 @@ int orc_attend_bwd_at(const float* q, const float* k, const float* v, const floa
             const float* vb = v + (b * Hkv + g) * N * d;
             row_mark(mark, r, i, b, N, window, B, sel, sel_w, tsel, tsel_w, &bad);
             double lse, Di;
-            const double z = sink ? (double)sink[h] : -INFINITY;
-            row_stats(mark, q + r * d, dout + r * d, kb, vb, i, d, scale, z, x, o, &lse, &Di);
+            const double zh = sink ? (double)sink[h] : -INFINITY;
+            row_stats(mark, q + r * d, dout + r * d, kb, vb, i, d, scale, zh, x, o, &lse, &Di);
             double* dqr = dq + t * d;
             for (int64_t e = 0; e < d; ++e) dqr[e] = 0.0;
             for (int64_t j = 0; j <= i; ++j) {
@@ -730,8 +730,8 @@ int orc_attend_bwd_at(const float* q, const float* k, const float* v, const floa
                 row_mark(mark, r, i, b, N, window, B, sel, sel_w, tsel, tsel_w, &bad);
                 if (!mark[j]) continue;
                 double lse, Di;
-                const double z = sink ? (double)sink[h] : -INFINITY;
-                row_stats(mark, q + r * d, dout + r * d, kb, vb, i, d, scale, z, x, o, &lse, &Di);
+                const double zh = sink ? (double)sink[h] : -INFINITY;
+                row_stats(mark, q + r * d, dout + r * d, kb, vb, i, d, scale, zh, x, o, &lse, &Di);
                 const double p = exp(x[j] - lse);
                 double dp = 0.0;
                 for (int64_t e = 0; e < d; ++e) dp += (double)dout[r * d + e] * (double)vb[j * d + e];
