@@ -105,6 +105,125 @@ __device__ __forceinline__ void finish_rows(const RowsArgs& a, f32x16 (&o)[Tile<
     if (hh == 0) a.lse[prow] = M + kLn2 * fast_log2(total);
 }
 
+// Pieces of the staged epilogue below (finish_rows_lds).  rows_begin: the common exponent base M of the row's parts (near lse, far
+// partials' lse, sink), the near part's weight applied to o; returns the
+// running weight sum.  rows_end: the sink's weight, then out and lse.
+template <int D>
+__device__ __forceinline__ float rows_begin(const RowsArgs& a, f32x16 (&o)[Tile<D>::DM], float lt,
+                                            float m, size_t pbase, int h, int nfar, float& M, float& z) {
+    using T = Tile<D>;
+    const float lse_near = m * a.scale + kLn2 * fast_log2(lt);
+    M = lse_near;
+    for (int s_ = 0; s_ < nfar; ++s_) M = fmaxf(M, a.part_lse[pbase + s_]);
+    z = a.sink ? a.sink[h] : -INFINITY;
+    M = fmaxf(M, z);
+    const float total = __expf(lse_near - M);
+    const float wn = total / lt;
+#pragma unroll
+    for (int mb = 0; mb < T::DM; ++mb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[mb][v] *= wn;
+    return total;
+}
+
+template <int D>
+__device__ __forceinline__ void rows_end(const RowsArgs& a, f32x16 (&o)[Tile<D>::DM], float M,
+                                         float total, float z, size_t prow, int hh) {
+    using T = Tile<D>;
+    if (a.sink) total += __expf(z - M);
+    const float inv = 1.f / total;
+    // V (and the far partials) were taken in units of 2^s.
+    const int vs = a.vscale ? a.vscale[prow / a.N / (a.Hq / a.Hkv)] : 0;
+#pragma unroll
+    for (int mb = 0; mb < T::DM; ++mb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int d0 = mb * 32 + 8 * j + 4 * hh;
+            if (d0 < D) {
+                const float v0 = ldexpf(o[mb][4 * j] * inv, vs), v1 = ldexpf(o[mb][4 * j + 1] * inv, vs);
+                const float v2 = ldexpf(o[mb][4 * j + 2] * inv, vs), v3 = ldexpf(o[mb][4 * j + 3] * inv, vs);
+                if (a.out_f32) {
+                    *(float4*)((float*)a.out + prow * D + d0) = make_float4(v0, v1, v2, v3);
+                } else {
+                    __bf16 r[4] = {(__bf16)v0, (__bf16)v1, (__bf16)v2, (__bf16)v3};
+                    *(uint2*)((uint16_t*)a.out + prow * D + d0) = *(const uint2*)r;
+                }
+            }
+        }
+    if (hh == 0) a.lse[prow] = M + kLn2 * fast_log2(total);
+}
+
+// Add the fp16 partial raw (this lane's dims of one row) with weight w.
+template <int D>
+__device__ __forceinline__ void add_part(f32x16 (&o)[Tile<D>::DM], float w, const uint2 (&raw)[Tile<D>::DM][4],
+                                         int hh) {
+#pragma unroll
+    for (int mb = 0; mb < Tile<D>::DM; ++mb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (mb * 32 + 8 * j + 4 * hh < D) {
+                const _Float16* hv = (const _Float16*)&raw[mb][j];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[mb][4 * j + e] += w * (float)hv[e];
+            }
+        }
+}
+
+// The far partials staged through LDS (block gate, after the key loop): a
+// wave's 32 rows hold their partials in one contiguous run of memory (kslots
+// slots per row), so two slots of every row are loaded straight into the
+// wave's own LDS buffer with coalesced 16-byte loads (global_load_lds), then
+// read back one row per lane.  In LDS each row takes 2 (D / 8) + 1 chunks of
+// 16 bytes (one chunk of padding: an odd stride, so the 32 rows' reads of a
+// chunk spread over the banks).  Called by every lane of the workgroup (the
+// batch loop holds barriers); ok: the lane's row exists.
+template <int D>
+__device__ __forceinline__ void finish_rows_lds(const RowsArgs& a, f32x16 (&o)[Tile<D>::DM], float lt,
+                                                float m, size_t prow, int h, int nfar, int hh, bool ok,
+                                                int col, int lane, uint16_t* buf) {
+    using T = Tile<D>;
+    constexpr int CH = D / 8, CPR = 2 * CH + 1, NI = (32 * CPR + 63) / 64;
+    const size_t pbase = prow * (size_t)a.kslots;
+    float M = 0.f, z = 0.f, total = 0.f;
+    if (ok) total = rows_begin<D>(a, o, lt, m, pbase, h, nfar, M, z);
+    const size_t wrow0 = (size_t)__builtin_amdgcn_readfirstlane((int)(prow - col));   // the wave's first row
+    const size_t last_el = (size_t)a.Bt * a.Hq * a.N * a.kslots * D - 8;
+    for (int s0 = 0; __syncthreads_or(ok && nfar > s0); s0 += 2) {
+        // (the barrier above: every wave is done with the buffers it reads)
+#if defined(__HIP_DEVICE_COMPILE__)   // the host pass rejects the LDS-pointer builtin
+#pragma unroll 2
+        for (int j = 0; j < NI; ++j) {
+            const int qc = 64 * j + lane, r = qc / CPR, c = qc % CPR;
+            size_t el = wrow0 * a.kslots * D;   // padding and past the rows: any chunk in bounds
+            if (r < 32 && c < 2 * CH) el = ((wrow0 + r) * a.kslots + s0 + c / CH) * D + (c % CH) * 8;
+            el = el < last_el ? el : last_el;
+            __builtin_amdgcn_global_load_lds((const void*)(a.part_o + el), (lds_ptr_t)(buf + j * 512), 16, 0,
+                                             0);
+        }
+#endif
+        const bool in0 = ok && s0 < nfar, in1 = ok && s0 + 1 < nfar;
+        const float l0 = in0 ? a.part_lse[pbase + s0] : 0.f, l1 = in1 ? a.part_lse[pbase + s0 + 1] : 0.f;
+        __syncthreads();   // the loads above have landed
+#pragma unroll 1
+        for (int sb = 0; sb < 2; ++sb) {
+            if (sb == 0 ? in0 : in1) {
+                uint2 raw[T::DM][4];
+#pragma unroll
+                for (int mb = 0; mb < T::DM; ++mb)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        raw[mb][j] = mb * 32 + 8 * j + 4 * hh < D
+                                         ? *(const uint2*)(buf + (col * CPR + sb * CH + 4 * mb + j) * 8 + 4 * hh)
+                                         : make_uint2(0, 0);
+                const float w = __expf((sb == 0 ? l0 : l1) - M);
+                total += w;
+                add_part<D>(o, w, raw, hh);
+            }
+        }
+    }
+    if (ok) rows_end<D>(a, o, M, total, z, prow, hh);
+}
+
 // ---------------------------------------------------------------------------
 // Query-centric kernel.
 // ---------------------------------------------------------------------------
@@ -136,9 +255,10 @@ __device__ __forceinline__ void finish_rows(const RowsArgs& a, f32x16 (&o)[Tile<
 // unit scales; the 16 dims past a multiple of 64 on the 32x32x16 FP8 op);
 // every E4M3 product is exact in the fp32 accumulator, as the bf16 products
 // of the decoded values would be.  K tiles hold fp8 rows of K8S<D>() bytes.
-// NEAR: the near-block mask holds 32 blocks (0) or 64 (1: a window of
-// 33..64 blocks under block gating); 2: 64, with blocks smaller than the
-// 64-key tile (B = 8, 16, 32), whose tiles get per-key block bits.
+// NEAR: 0 no block gate; 3 block gate, the near-block mask holding 32
+// blocks; 1 the mask holding 64 (a window of 33..64 blocks); 2 as 1, with
+// blocks smaller than the 64-key tile (B = 8, 16, 32), whose tiles get
+// per-key block bits.
 template <int D, int SPLIT, bool TOK, bool QK8, int NEAR = 0>
 __global__ __launch_bounds__(NTHREADS, D <= 80 && SPLIT == 1 ? 3 : 2) void attn_rows_kernel(RowsArgs a) {
     using T = Tile<D>;
@@ -183,7 +303,7 @@ __global__ __launch_bounds__(NTHREADS, D <= 80 && SPLIT == 1 ? 3 : 2) void attn_
 
     // Block-gate state of the row: its block, the kept near blocks as a bit
     // mask over (own block - 1 - bit), and the count of far blocks.
-    constexpr bool WIDE = NEAR > 0, SMALLB = NEAR == 2;
+    constexpr bool WIDE = NEAR == 1 || NEAR == 2, SMALLB = NEAR == 2, GATED = NEAR != 0;
     using NearT = typename std::conditional<WIDE, uint64_t, uint32_t>::type;
     constexpr int kNear = WIDE ? 64 : 32;
     int row_blk = 0, nfar = 0;
@@ -356,6 +476,19 @@ __global__ __launch_bounds__(NTHREADS, D <= 80 && SPLIT == 1 ? 3 : 2) void attn_
         last(Par<0>{});
     }
 
+    if constexpr (GATED && !TOK && !QK8) {
+        if (a.part_o) {   // far partials exist (workgroup-uniform)
+            float lt = 0.f;
+            if (row_ok) {
+                if constexpr (ONES) lt = o[T::DM - 1][8];
+                else lt = pair_sum(rs.l);
+            }
+            uint16_t* const buf = wu == 0 ? lds_k0 : wu == 1 ? lds_k1 : wu == 2 ? lds_v0 : lds_v1;
+            static_assert((32 * (2 * (D / 8) + 1) + 63) / 64 * 512 <= KE, "a K buffer holds two slots");
+            finish_rows_lds<D>(a, o, lt, rs.m, prow, h, nfar, hh, row_ok, col, lane, buf);
+            return;
+        }
+    }
     if (row_ok) {
         float lt;
         if constexpr (ONES) lt = o[T::DM - 1][8];   // O^T row D (hh 0) or D + 4 (hh 1)
@@ -570,6 +703,8 @@ static hipError_t rows_d(const RowsArgs& a, hipStream_t s) {
         hipLaunchKernelGGL((attn_rows_kernel<D, SPLIT, false, false, 2>), dim3(grid), dim3(NTHREADS), 0, s, a);
     else if (a.gate && a.span > 32)
         hipLaunchKernelGGL((attn_rows_kernel<D, SPLIT, false, false, 1>), dim3(grid), dim3(NTHREADS), 0, s, a);
+    else if (a.gate)
+        hipLaunchKernelGGL((attn_rows_kernel<D, SPLIT, false, false, 3>), dim3(grid), dim3(NTHREADS), 0, s, a);
     else
         hipLaunchKernelGGL((attn_rows_kernel<D, SPLIT, false, false>), dim3(grid), dim3(NTHREADS), 0, s, a);
     return hipGetLastError();
