@@ -458,6 +458,50 @@ def test_backward_small_blocks(dev, case, d):
     bwd_and_check(W.make_inputs(wl, 161 + case + d), dev, 171 + case, label=f"bwd_small_blk {kw}")
 
 
+# Seeded random configurations: head dim, GQA ratio, batch, dtype, and the
+# branches and their options drawn together (block sizes 8 to 128 with
+# windows, every gate variant, the compressed branch, the token gate,
+# sinks), at ragged lengths; every row checked.
+def random_workload(seed, backward=False):
+    rng = np.random.default_rng(seed)
+    d = int(rng.choice([64, 80, 128]))
+    Hkv, G, Bt = int(rng.choice([1, 2, 4])), int(rng.choice([1, 2, 4, 8])), int(rng.choice([1, 2]))
+    dtype = "bf16" if backward else str(rng.choice(["bf16", "bf16", "f32", "fp8"]))
+    kw = dict(sink=bool(rng.random() < 0.4))
+    mode = str(rng.choice(["window", "gate", "gate", "token"]))
+    if mode == "gate":
+        B = int(rng.choice([8, 16, 32, 64, 128]))
+        n = int(rng.integers(2, max(3, min(40, 2048 // B))))
+        N = B * n
+        top_k = int(rng.integers(1, min(n, 33) + 1))
+        kw.update(block_size=B, top_k=top_k, block_offsets=True,
+                  gate_repr=str(rng.choice(["mean", "minmax"])), gate_shared=bool(rng.random() < 0.4),
+                  gate_first=bool(top_k >= 2 and rng.random() < 0.3))
+        if rng.random() < 0.6:
+            kw["window"] = int(rng.integers(1, min(N, 64 * B) + 1))
+    elif mode == "token":
+        N = int(rng.integers(1, 1500))
+        kw.update(window=int(rng.integers(1, 300)), token_top_k=int(rng.integers(1, 600)), index_dim=64)
+    else:
+        N = int(rng.integers(1, 1500))
+        kw["window"] = int(rng.integers(1, 2000))
+    if mode != "token" and rng.random() < 0.35:
+        kw["cmp_block"] = int(rng.choice([1, 4, 8, 16, 64]))
+    return W.Workload(f"rand{seed}", Bt, Hkv * G, Hkv, N, d, dtype, **kw)
+
+
+@pytest.mark.parametrize("seed", range(1000, 1064))
+def test_random_configs(dev, seed):
+    wl = random_workload(seed)
+    run_and_check(W.make_inputs(wl, seed), dev, label=f"random {seed}")
+
+
+@pytest.mark.parametrize("seed", range(2000, 2024))
+def test_backward_random_configs(dev, seed):
+    wl = random_workload(seed, backward=True)
+    bwd_and_check(W.make_inputs(wl, seed), dev, seed + 1, label=f"bwd random {seed}")
+
+
 # Full-size backward in the benchmark's configuration, checked at listed
 # outputs: dq of sampled rows (first/last rows of each head, block and
 # window edges, random rows) and dk, dv of keys at window and block edges,
