@@ -369,10 +369,11 @@ __global__ __launch_bounds__(64 * gate_waves(QSPLIT)) void gate_kernel(GateArgs 
     // cover its 32 rows' selections contiguously.
     if (!row_ok) return;
     const int m = max(0, min(a.top_k - 1 - c0, row_blk - c0));
-    int ids[M];
+    constexpr int MP = M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : M <= 16 ? 16 : 32;   // sorting width
+    int ids[MP];
 #pragma unroll
-    for (int t = 0; t < M; ++t) ids[t] = t < m ? (int)(mask - (L[t] & mask)) : 0x7fffffff;
-    sort_asc<M>(ids);
+    for (int t = 0; t < MP; ++t) ids[t] = t < m && t < M ? (int)(mask - (L[t] & mask)) : 0x7fffffff;
+    sort_asc<MP>(ids);
     // Ascending: block 0 when forced, the m kept candidates, the own block.
     auto val_at = [&](int t) {
         int val = -1;
@@ -380,7 +381,7 @@ __global__ __launch_bounds__(64 * gate_waves(QSPLIT)) void gate_kernel(GateArgs 
             val = 0;
         } else if (t < c0 + m) {
 #pragma unroll
-            for (int u = 0; u < M; ++u)
+            for (int u = 0; u < MP; ++u)
                 if (u == t - c0) val = ids[u];
         } else if (t == c0 + m) {
             val = row_blk;
@@ -437,7 +438,9 @@ static hipError_t gate_d(const GateArgs& a, hipStream_t s) {
     const int need = a.top_k - 1;
     if (need <= 2) return gate_dm<D, 2, QS, NP, MM>(a, s);
     if (need <= 4) return gate_dm<D, 4, QS, NP, MM>(a, s);
+    if (need == 7) return gate_dm<D, 7, QS, NP, MM>(a, s);   // top 8 blocks: seven slots
     if (need <= 8) return gate_dm<D, 8, QS, NP, MM>(a, s);
+    if (need == 15) return gate_dm<D, 15, QS, NP, MM>(a, s);  // top 16
     if (need <= 16) return gate_dm<D, 16, QS, NP, MM>(a, s);
     if (need <= 32) return gate_dm<D, 32, QS, NP, MM>(a, s);
     return hipErrorInvalidValue;
