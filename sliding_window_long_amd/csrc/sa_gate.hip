@@ -331,9 +331,10 @@ __global__ __launch_bounds__(64 * gate_waves(QSPLIT)) void gate_kernel(GateArgs 
                     }
                 }
             }
-            // Insert the 16 scores of this lane; a score that does not beat
-            // the lane's current M-th key cannot enter its list, and a wave
-            // in which no lane has such a score skips the insertion.
+            // Insert the 16 scores of this lane, four at a time; a score
+            // that does not beat the lane's current M-th key cannot enter its
+            // list (inserting it changes nothing), and a wave in which no
+            // lane has such a score among the four skips their insertion.
             // Every candidate of the tile is valid for every row of the
             // wave when the tile ends before the wave's first row block and
             // holds no forced block 0 (wave-uniform).
@@ -341,14 +342,24 @@ __global__ __launch_bounds__(64 * gate_waves(QSPLIT)) void gate_kernel(GateArgs 
             const uint32_t kbase = mask - (uint32_t)(mt * 32 + 4 * hh);
             auto insert_tile = [&](auto check) __attribute__((always_inline)) {
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int vo = 8 * (v >> 2) + (v & 3);
-                    uint32_t key = order_key_lo(acc[v], kbase - (uint32_t)vo, mask);
-                    if constexpr (decltype(check)::value) {
-                        const int cblk = mt * 32 + vo + 4 * hh;
-                        key = cblk < row_blk && cblk >= c0 ? key : 0u;
+                for (int v4 = 0; v4 < 4; ++v4) {
+                    uint32_t keys[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int v = 4 * v4 + u;
+                        const int vo = 8 * (v >> 2) + (v & 3);
+                        uint32_t key = order_key_lo(acc[v], kbase - (uint32_t)vo, mask);
+                        if constexpr (decltype(check)::value) {
+                            const int cblk = mt * 32 + vo + 4 * hh;
+                            key = cblk < row_blk && cblk >= c0 ? key : 0u;
+                        }
+                        keys[u] = key;
                     }
-                    if (__any(key > L[M - 1])) insert_desc<M>(L, key);
+                    const uint32_t top = max(max(keys[0], keys[1]), max(keys[2], keys[3]));
+                    if (__any(top > L[M - 1])) {
+#pragma unroll
+                        for (int u = 0; u < 4; ++u) insert_desc<M>(L, keys[u]);
+                    }
                 }
             };
             if (all_ok) insert_tile(std::false_type{});
