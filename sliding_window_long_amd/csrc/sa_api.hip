@@ -322,10 +322,10 @@ struct StageScope {
         if (!g_timing.on || g_timing.n >= kMaxStages) return;
         idx = g_timing.n++;
         g_timing.names[idx] = name;
-        hipEventRecord(g_timing.ev[idx][0], s);
+        (void)hipEventRecord(g_timing.ev[idx][0], s);   // a failed record only loses the stage's time
     }
     ~StageScope() {
-        if (idx >= 0) hipEventRecord(g_timing.ev[idx][1], s);
+        if (idx >= 0) (void)hipEventRecord(g_timing.ev[idx][1], s);
     }
 };
 
@@ -714,7 +714,7 @@ int sparse_attn_fwd(const void* q, const void* k, const void* v, const sparse_at
         uint16_t* kc = (uint16_t*)(ws + P.o_cmp_k);
         uint16_t* vc = (uint16_t*)(ws + P.o_cmp_v);
         sa::CmpPoolArgs cp{k, v, {kc, P.f32 ? kc + ncmp : nullptr}, {vc, P.f32 ? vc + ncmp : nullptr},
-                           P.Bt * P.Hkv, P.N, P.C, P.Nc, P.D, vscale};
+                           P.Bt * P.Hkv, P.N, P.C, P.Nc, P.D, vscale, nullptr, 0};
         {
             StageScope t("cmp_pool", s);
             if (!ok(sa::launch_cmp_pool(cp, P.f32, s))) return SA_E_HIP;

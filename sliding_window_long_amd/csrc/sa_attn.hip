@@ -182,15 +182,16 @@ __device__ __forceinline__ void finish_rows_lds(const RowsArgs& a, f32x16 (&o)[T
                                                 float m, size_t prow, int h, int nfar, int hh, bool ok,
                                                 int col, int lane, uint16_t* buf) {
     using T = Tile<D>;
-    constexpr int CH = D / 8, CPR = 2 * CH + 1, NI = (32 * CPR + 63) / 64;
+    constexpr int CH = D / 8, CPR = 2 * CH + 1;
     const size_t pbase = prow * (size_t)a.kslots;
     float M = 0.f, z = 0.f, total = 0.f;
     if (ok) total = rows_begin<D>(a, o, lt, m, pbase, h, nfar, M, z);
-    const size_t wrow0 = (size_t)__builtin_amdgcn_readfirstlane((int)(prow - col));   // the wave's first row
-    const size_t last_el = (size_t)a.Bt * a.Hq * a.N * a.kslots * D - 8;
     for (int s0 = 0; __syncthreads_or(ok && nfar > s0); s0 += 2) {
         // (the barrier above: every wave is done with the buffers it reads)
 #if defined(__HIP_DEVICE_COMPILE__)   // the host pass rejects the LDS-pointer builtin
+        constexpr int NI = (32 * CPR + 63) / 64;
+        const size_t wrow0 = (size_t)__builtin_amdgcn_readfirstlane((int)(prow - col));   // the wave's first row
+        const size_t last_el = (size_t)a.Bt * a.Hq * a.N * a.kslots * D - 8;
 #pragma unroll 2
         for (int j = 0; j < NI; ++j) {
             const int qc = 64 * j + lane, r = qc / CPR, c = qc % CPR;
@@ -200,6 +201,8 @@ __device__ __forceinline__ void finish_rows_lds(const RowsArgs& a, f32x16 (&o)[T
             __builtin_amdgcn_global_load_lds((const void*)(a.part_o + el), (lds_ptr_t)(buf + j * 512), 16, 0,
                                              0);
         }
+#else
+        (void)lane;
 #endif
         const bool in0 = ok && s0 < nfar, in1 = ok && s0 + 1 < nfar;
         const float l0 = in0 ? a.part_lse[pbase + s0] : 0.f, l1 = in1 ? a.part_lse[pbase + s0 + 1] : 0.f;
@@ -260,7 +263,7 @@ __device__ __forceinline__ void finish_rows_lds(const RowsArgs& a, f32x16 (&o)[T
 // blocks smaller than the 64-key tile (B = 8, 16, 32), whose tiles get
 // per-key block bits.
 template <int D, int SPLIT, bool TOK, bool QK8, int NEAR = 0>
-__global__ __launch_bounds__(NTHREADS, D <= 80 && SPLIT == 1 ? 3 : 2) void attn_rows_kernel(RowsArgs a) {
+__global__ __launch_bounds__(NTHREADS, rows_waves(D, SPLIT)) void attn_rows_kernel(RowsArgs a) {
     using T = Tile<D>;
     constexpr bool ONES = T::DPAD > D;
     constexpr int VS = dma_vs<D>();

@@ -24,6 +24,13 @@ constexpr int NTHREADS = 64 * NWAVES;
 constexpr int RT = 32 * NWAVES;        // query rows per workgroup
 constexpr int kMaxKeyBlocks = RT / 8;  // blocks met by RT consecutive keys (smallest block: 8)
 
+// Waves per SIMD the attention kernels ask for: three for one bf16 plane at
+// head dims up to 80 (168 registers), one for split fp32 operands past 64
+// (more than 256 registers), else two.
+__host__ __device__ constexpr int rows_waves(int D, int SPLIT) {
+    return SPLIT == 1 ? (D <= 80 ? 3 : 2) : (D >= 80 ? 1 : 2);
+}
+
 template <int D>
 struct Tile {
     static constexpr int DK = D / 16;              // contraction steps of K Q^T
@@ -481,6 +488,8 @@ __device__ __forceinline__ void dma_tile(const TD& td, const uint64_t* base, int
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 r, (lds_ptr_t)(lds + p * PLANE + TD::inst(wave, j) * 512), 16, td.voff[j], 0, 0, 0);
     }
+#else
+    (void)td; (void)base; (void)N; (void)kt0; (void)lds; (void)wave;
 #endif
 }
 

@@ -58,7 +58,7 @@ __device__ __forceinline__ void stage_fence() {
 // chunk table is issued before the ones that need the list end.
 // ---------------------------------------------------------------------------
 template <int D, int SPLIT>
-__global__ __launch_bounds__(NTHREADS, D <= 80 && SPLIT == 1 ? 3 : 2) void attn_blocks_kernel(BlocksArgs a) {
+__global__ __launch_bounds__(NTHREADS, rows_waves(D, SPLIT)) void attn_blocks_kernel(BlocksArgs a) {
     using T = Tile<D>;
     constexpr bool ONES = T::DPAD > D;
     constexpr int VS = dma_vs<D>();

@@ -139,7 +139,7 @@ struct CmpSmem {
 };
 
 template <int D, int SPLIT>
-__global__ __launch_bounds__(NTHREADS, 2) void attn_cmp_kernel(CmpArgs a) {
+__global__ __launch_bounds__(NTHREADS, SPLIT == 2 && D >= 80 ? 1 : 2) void attn_cmp_kernel(CmpArgs a) {
     using T = Tile<D>;
     __shared__ __align__(16) uint8_t smem[CmpSmem<D, SPLIT>::BYTES];
     uint16_t* const lds_k = (uint16_t*)smem;                  // [2][SPLIT * KELEMS]
