@@ -85,7 +85,7 @@
 extern "C" {
 #endif
 
-#define SPARSE_ATTN_ABI_VERSION 4
+#define SPARSE_ATTN_ABI_VERSION 5
 
 typedef enum {
     SA_BF16 = 0, /* bfloat16 inputs and out; fp32 accumulation.  Q K^T runs on
@@ -102,10 +102,14 @@ typedef enum {
     SA_FP8 = 2   /* FP8 inputs (OCP E4M3: bias 7, 3 mantissa bits, max 448, no
                     infinities, 0x7F/0xFF = NaN) for q, k, v, idx_q, idx_k; out
                     is bf16.  [Naive-N0.5-Flash page: FP8 mixed-precision
-                    inference.]  Every E4M3 value is a bf16 value: the inputs
-                    are decoded exactly into bf16 in the workspace and computed
-                    as SA_BF16.  Not for sparse_attn_block_pool or the backward
-                    (SA_E_UNSUPPORTED). */
+                    inference.]  Prefills without a block or token gate read
+                    q and k as E4M3 straight into the FP8 matrix cores for
+                    Q K^T (every E4M3 product is exact in the fp32
+                    accumulator) and copy V to fp16 with the hardware
+                    conversion (exact).  Every other call decodes the inputs
+                    exactly into bf16 in the workspace (every E4M3 value is a
+                    bf16 value) and computes as SA_BF16.  Not for
+                    sparse_attn_block_pool or the backward (SA_E_UNSUPPORTED). */
 } sa_dtype;
 
 typedef enum {
@@ -123,8 +127,10 @@ enum {
     SA_E_WORKSPACE_TOO_SMALL = -6,
     SA_E_HIP = -7,              /* a kernel launch failed (hipGetLastError) */
     SA_E_UNSUPPORTED = -8,      /* a combination outside the documented limits */
-    SA_E_SCRATCH_LIMIT = -9     /* sparse_attn_fwd_noalloc: the configuration needs
+    SA_E_SCRATCH_LIMIT = -9,    /* sparse_attn_fwd_noalloc: the configuration needs
                                    more workspace than its static scratch holds */
+    SA_E_CHECK = -10            /* a list invariant failed (sparse_attn_check_far_lists,
+                                   or a call made with sparse_attn_set_checks(1)) */
 };
 
 typedef struct {
@@ -247,6 +253,67 @@ const char* sparse_attn_strerror(int status);
 int sparse_attn_set_timing(int enable);
 int sparse_attn_stage_times(int32_t* n_stages, const char** names, float* ms,
                             int32_t capacity);
+
+/* Checks of the far-block lists (a debugging aid; off by default).
+ *
+ * Block gating regroups query rows by kept far block (MoBA summary page,
+ * "MoBA의 구현: MoE와 FlashAttention의 결합", steps 1-2: route each query to
+ * its blocks, then reorder the queries by block).  The lists live in the
+ * workspace:
+ *   list l = (batch b, kv head g, block c), l = (b n_kv_heads + g) n_blocks + c;
+ *   list_off[lists + 1]  first entry of each list (exclusive prefix sum);
+ *   list_ch[lists + 1]   first chunk of each list: a list of m entries is cut
+ *                        into ceil(m / rows_per_chunk) chunks;
+ *   chunk_list[n_chunks], chunk_start[n_chunks]  each chunk's list and first
+ *                        entry;
+ *   entries[list_off[lists]]  one entry per (query row, head, selection slot)
+ *                        whose kept block is a far block: (i G + h_local)
+ *                        kslots + x for position i, head g G + h_local of the
+ *                        kv group (G = n_q_heads / n_kv_heads) and slot x of
+ *                        the row's ascending selection sel[b, h, i, x].
+ * A slot holds a far block when it and every slot before it hold a block c
+ * >= 0 with floor(i / block_size) - c > span (blocks within `span` of the
+ * row's own block are attended with the window, not through the lists).
+ *
+ * sparse_attn_check_far_lists verifies host copies of such lists against
+ * the selection: offsets non-decreasing from 0 and at most max_entries; chunk
+ * counts, the chunk table and n_chunks (at most max_chunks) consistent with
+ * the offsets; every entry decodes to a position, head and slot in range
+ * whose selected block is its list's block and is a far block; every far
+ * slot of every row listed exactly once; with `ordered`, the entries of each
+ * list in increasing (floor(i / 64), h_local, x, i mod 64), the fixed order
+ * the backward sums in.  It reads only the arrays it is given (their sizes
+ * follow from the fields and from list_off, list_ch and n_chunks, which are
+ * range-checked before use) and returns SA_OK or SA_E_CHECK, writing the
+ * first violation as a NUL-terminated message into detail (if not NULL).
+ *
+ * sparse_attn_set_checks(1): from then on, every sparse_attn_fwd and
+ * sparse_attn_bwd call on the calling host thread that builds far-block
+ * lists waits for them on cfg->stream, copies the selection and the lists
+ * to the host and runs sparse_attn_check_far_lists, returning SA_E_CHECK on
+ * a violation.  While on, those calls synchronise the stream (the one
+ * exception to the no-sync rule above). */
+typedef struct {
+    int32_t batch, n_q_heads, n_kv_heads, seq_len, block_size, n_blocks, top_k;
+    int32_t span;             /* near blocks below the own block (see above) */
+    int32_t kslots;           /* slot multiplier of an entry (>= top_k - 1, >= 1) */
+    int32_t rows_per_chunk;   /* > 0 */
+    int32_t ordered;          /* 1: require the fixed order */
+    int32_t n_chunks;
+    int64_t max_entries;
+    int32_t max_chunks;
+    const int32_t* sel;          /* [batch, n_q_heads, seq_len, top_k] */
+    const int32_t* list_off;     /* [lists + 1] */
+    const int32_t* list_ch;      /* [lists + 1] */
+    const int32_t* chunk_list;   /* [n_chunks] */
+    const int32_t* chunk_start;  /* [n_chunks] */
+    const int32_t* entries;      /* [list_off[lists]] */
+    char* detail;                /* out: first violation, or NULL */
+    size_t detail_bytes;
+} sparse_attn_far_lists;
+
+int sparse_attn_check_far_lists(const sparse_attn_far_lists* f);
+int sparse_attn_set_checks(int enable);
 
 #ifdef __cplusplus
 }

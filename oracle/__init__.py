@@ -48,6 +48,8 @@ def _load(path=None):
     global _lib
     if _lib is not None and path is None:
         return _lib
+    # SA_ORACLE_LIB: another build of oracle.c (the sanitizer run uses one)
+    path = path or os.environ.get("SA_ORACLE_LIB") or None
     if path is None and not os.path.exists(_LIB):
         build()
     lib = ctypes.CDLL(path or _LIB)

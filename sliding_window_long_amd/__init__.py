@@ -9,6 +9,7 @@ from .binding import (  # noqa: F401
     block_pool, forward, load_library, params_for, sparse_attn_block_pool, sparse_attn_fwd,
     sparse_attn_fwd_noalloc,
     sparse_attn_bwd_workspace_bytes,
+    sparse_attn_check_far_lists, sparse_attn_set_checks,
     sparse_attn_set_timing, sparse_attn_stage_times, sparse_attn_strerror,
     sparse_attn_workspace_bytes,
 )

@@ -16,7 +16,8 @@ import os
 from dataclasses import dataclass
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libsparse_attn.so")
+# SPARSE_ATTN_LIB: load another build of the library (e.g. a sanitizer build)
+LIB_PATH = os.environ.get("SPARSE_ATTN_LIB") or os.path.join(HERE, "libsparse_attn.so")
 
 SA_BF16, SA_F32, SA_FP8 = 0, 1, 2
 SA_GATE_MEAN, SA_GATE_MINMAX = 0, 1
@@ -24,12 +25,13 @@ SA_OK = 0
 ERROR_CODES = {
     -1: "SA_E_INVALID_ARG", -2: "SA_E_SHAPE", -3: "SA_E_UNSUPPORTED_HEAD_DIM",
     -4: "SA_E_NO_SELF", -5: "SA_E_ALIGNMENT", -6: "SA_E_WORKSPACE_TOO_SMALL",
-    -7: "SA_E_HIP", -8: "SA_E_UNSUPPORTED", -9: "SA_E_SCRATCH_LIMIT",
+    -7: "SA_E_HIP", -8: "SA_E_UNSUPPORTED", -9: "SA_E_SCRATCH_LIMIT", -10: "SA_E_CHECK",
 }
 # Every symbol the C header declares.
 EXPORTS = ("sparse_attn_workspace_bytes", "sparse_attn_fwd", "sparse_attn_block_pool",
            "sparse_attn_strerror", "sparse_attn_set_timing", "sparse_attn_stage_times",
-           "sparse_attn_bwd_workspace_bytes", "sparse_attn_bwd", "sparse_attn_fwd_noalloc")
+           "sparse_attn_bwd_workspace_bytes", "sparse_attn_bwd", "sparse_attn_fwd_noalloc",
+           "sparse_attn_check_far_lists", "sparse_attn_set_checks")
 
 
 class SparseAttnCfg(ctypes.Structure):
@@ -50,6 +52,22 @@ class SparseAttnCfg(ctypes.Structure):
         ("kv_len", ctypes.c_int32),
         ("gate_repr", ctypes.c_int32), ("gate_shared", ctypes.c_int32),
         ("gate_first", ctypes.c_int32), ("cmp_block", ctypes.c_int32),
+    ]
+
+
+class SparseAttnFarLists(ctypes.Structure):
+    """Mirror of ``sparse_attn_far_lists``."""
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32), ("seq_len", ctypes.c_int32),
+        ("block_size", ctypes.c_int32), ("n_blocks", ctypes.c_int32), ("top_k", ctypes.c_int32),
+        ("span", ctypes.c_int32), ("kslots", ctypes.c_int32), ("rows_per_chunk", ctypes.c_int32),
+        ("ordered", ctypes.c_int32), ("n_chunks", ctypes.c_int32),
+        ("max_entries", ctypes.c_int64), ("max_chunks", ctypes.c_int32),
+        ("sel", ctypes.c_void_p), ("list_off", ctypes.c_void_p), ("list_ch", ctypes.c_void_p),
+        ("chunk_list", ctypes.c_void_p), ("chunk_start", ctypes.c_void_p),
+        ("entries", ctypes.c_void_p),
+        ("detail", ctypes.c_char_p), ("detail_bytes", ctypes.c_size_t),
     ]
 
 
@@ -92,6 +110,10 @@ def load_library():
     lib.sparse_attn_bwd_workspace_bytes.restype = ctypes.c_int
     lib.sparse_attn_bwd.argtypes = [ctypes.c_void_p] * 6 + [P(SparseAttnCfg)] + [ctypes.c_void_p] * 4
     lib.sparse_attn_bwd.restype = ctypes.c_int
+    lib.sparse_attn_check_far_lists.argtypes = [P(SparseAttnFarLists)]
+    lib.sparse_attn_check_far_lists.restype = ctypes.c_int
+    lib.sparse_attn_set_checks.argtypes = [ctypes.c_int]
+    lib.sparse_attn_set_checks.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -135,6 +157,36 @@ def sparse_attn_strerror(code: int) -> str:
 def _check(rc: int, where: str):
     if rc != SA_OK:
         raise SparseAttnError(rc, where)
+
+
+def sparse_attn_set_checks(enable: bool) -> None:
+    """Far-list checks on every later call of this host thread (see the C
+    header): the calls then synchronise their stream."""
+    _check(load_library().sparse_attn_set_checks(int(bool(enable))), "sparse_attn_set_checks")
+
+
+def sparse_attn_check_far_lists(*, batch, n_q_heads, n_kv_heads, seq_len, block_size, top_k,
+                                span, kslots, rows_per_chunk, ordered, sel, list_off, list_ch,
+                                chunk_list, chunk_start, entries, max_entries, max_chunks):
+    """Check host copies of far-block lists against a selection (int32 numpy
+    arrays); returns (status, message)."""
+    import numpy as np
+    arrs = [np.ascontiguousarray(a, dtype=np.int32) for a in
+            (sel, list_off, list_ch, chunk_list, chunk_start, entries)]
+    n_blocks = seq_len // block_size
+    lists = batch * n_kv_heads * n_blocks
+    _need(arrs[0].size == batch * n_q_heads * seq_len * top_k, "sel size")
+    _need(arrs[1].size == lists + 1 and arrs[2].size == lists + 1, "list_off / list_ch size")
+    _need(arrs[3].size == arrs[4].size, "chunk_list / chunk_start size")
+    _need(int(arrs[1][-1]) <= arrs[5].size or int(arrs[1][-1]) < 0, "entries shorter than list_off says")
+    msg = ctypes.create_string_buffer(400)
+    f = SparseAttnFarLists(batch, n_q_heads, n_kv_heads, seq_len, block_size, n_blocks, top_k,
+                           span, kslots, rows_per_chunk, int(bool(ordered)), arrs[3].size,
+                           int(max_entries), int(max_chunks),
+                           *[a.ctypes.data if a.size else None for a in arrs],
+                           ctypes.cast(msg, ctypes.c_char_p), 400)
+    rc = load_library().sparse_attn_check_far_lists(ctypes.byref(f))
+    return rc, msg.value.decode()
 
 
 def sparse_attn_workspace_bytes(cfg: SparseAttnCfg) -> int:

@@ -14,9 +14,12 @@
 #include "sa_internal.hpp"
 
 #include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
 #include <string.h>
 
 #include <mutex>
+#include <vector>
 
 namespace {
 
@@ -403,6 +406,149 @@ int select_tokens(const Plan& P, const sparse_attn_cfg* cfg, char* ws, int split
     return SA_OK;
 }
 
+// ----------------------------------------------------------------------------
+// Invariants of the far-block lists (debugging aid, sparse_attn_set_checks).
+// ----------------------------------------------------------------------------
+thread_local bool g_checks = false;
+
+int check_fail(const sparse_attn_far_lists* f, const char* fmt, ...) {
+    if (f->detail && f->detail_bytes > 0) {
+        va_list ap;
+        va_start(ap, fmt);
+        vsnprintf(f->detail, f->detail_bytes, fmt, ap);
+        va_end(ap);
+    }
+    return SA_E_CHECK;
+}
+
+int check_far_lists_impl(const sparse_attn_far_lists* f) {
+    if (!f) return SA_E_INVALID_ARG;
+    if (f->detail && f->detail_bytes > 0) f->detail[0] = 0;
+    const long long Bt = f->batch, Hq = f->n_q_heads, Hkv = f->n_kv_heads, N = f->seq_len;
+    const long long B = f->block_size, n = f->n_blocks, K = f->top_k, ks = f->kslots;
+    const long long R = f->rows_per_chunk, span = f->span, nch = f->n_chunks;
+    if (Bt <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv || N <= 0 || B <= 0 || n <= 0 || K <= 0 ||
+        ks < 1 || R <= 0 || span < 0 || nch < 0 || f->max_chunks < 0 || f->max_entries < 0)
+        return SA_E_INVALID_ARG;
+    if (!f->sel || !f->list_off || !f->list_ch || (nch > 0 && (!f->chunk_list || !f->chunk_start)))
+        return SA_E_INVALID_ARG;
+    const long long G = Hq / Hkv, lists = Bt * Hkv * n;
+    const int32_t* off = f->list_off;
+    const int32_t* ch = f->list_ch;
+    // Offsets and chunking.
+    if (off[0] != 0) return check_fail(f, "list_off[0] is %d, not 0", off[0]);
+    for (long long l = 0; l < lists; ++l)
+        if (off[l + 1] < off[l])
+            return check_fail(f, "list_off decreases after list %lld (%d then %d)", l, off[l], off[l + 1]);
+    const long long total = off[lists];
+    if (total > f->max_entries)
+        return check_fail(f, "%lld entries, more than the %lld the workspace holds", total,
+                          (long long)f->max_entries);
+    if (total > 0 && !f->entries) return SA_E_INVALID_ARG;
+    if (ch[0] != 0) return check_fail(f, "list_ch[0] is %d, not 0", ch[0]);
+    for (long long l = 0; l < lists; ++l) {
+        const long long m = off[l + 1] - off[l];
+        if ((long long)ch[l + 1] - ch[l] != (m + R - 1) / R)
+            return check_fail(f, "list %lld: %lld entries but %lld chunks", l, m, (long long)ch[l + 1] - ch[l]);
+    }
+    if (ch[lists] > f->max_chunks)
+        return check_fail(f, "%d chunks, more than the chunk table's %d", ch[lists], f->max_chunks);
+    if (nch != ch[lists]) return check_fail(f, "n_chunks is %lld, the lists make %d", nch, ch[lists]);
+    for (long long q = 0; q < nch; ++q) {
+        const long long l = f->chunk_list[q];
+        if (l < 0 || l >= lists || q < ch[l] || q >= ch[l + 1])
+            return check_fail(f, "chunk %lld names list %lld, which does not own it", q, l);
+        if (f->chunk_start[q] != off[l] + (q - ch[l]) * R)
+            return check_fail(f, "chunk %lld of list %lld starts at entry %d, not %lld", q, l,
+                              f->chunk_start[q], off[l] + (q - ch[l]) * R);
+    }
+    // Entries: each one a far slot of a row, listed under that slot's block,
+    // once; with `ordered`, in the fixed order.
+    std::vector<uint8_t> seen((size_t)(Bt * Hq * N * K), 0);
+    for (long long l = 0; l < lists; ++l) {
+        const long long bg = l / n, c = l % n, b = bg / Hkv, g = bg % Hkv;
+        long long prev = -1;
+        for (long long e = off[l]; e < off[l + 1]; ++e) {
+            const long long ent = f->entries[e];
+            if (ent < 0) return check_fail(f, "entry %lld of list %lld is negative (%lld)", e, l, ent);
+            const long long x = ent % ks, t2 = ent / ks, hl = t2 % G, i = t2 / G;
+            if (i >= N || x >= K)
+                return check_fail(f, "entry %lld of list %lld (%lld) decodes to position %lld, slot %lld: "
+                                  "out of range", e, l, ent, i, x);
+            const long long h = g * G + hl, prow = (b * Hq + h) * N + i, bi = i / B;
+            const int32_t* sr = f->sel + prow * K;
+            if (sr[x] != c)
+                return check_fail(f, "entry %lld of list %lld (block %lld) names slot %lld of row (b %lld, h "
+                                  "%lld, i %lld), which holds block %d", e, l, c, x, b, h, i, sr[x]);
+            for (long long xx = 0; xx <= x; ++xx)
+                if (sr[xx] < 0 || bi - sr[xx] <= span)
+                    return check_fail(f, "entry %lld of list %lld: slot %lld of row (b %lld, h %lld, i %lld) "
+                                      "is listed but slot %lld (block %d, own block %lld, span %lld) is not far",
+                                      e, l, x, b, h, i, xx, sr[xx], bi, span);
+            if (seen[prow * K + x]++)
+                return check_fail(f, "slot %lld of row (b %lld, h %lld, i %lld) is listed twice", x, b, h, i);
+            if (f->ordered) {
+                const long long key = (((i / 64) * G + hl) * K + x) * 64 + i % 64;
+                if (key <= prev)
+                    return check_fail(f, "list %lld: entry %lld (row %lld, head %lld, slot %lld) is out of order",
+                                      l, e, i, h, x);
+                prev = key;
+            }
+        }
+    }
+    for (long long prow = 0; prow < Bt * Hq * N; ++prow) {
+        const long long i = prow % N, bi = i / B;
+        const int32_t* sr = f->sel + prow * K;
+        for (long long x = 0; x < K; ++x) {
+            if (sr[x] < 0 || bi - sr[x] <= span) break;
+            if (!seen[prow * K + x])
+                return check_fail(f, "far slot %lld (block %d) of row (b %lld, h %lld, i %lld) is in no list", x,
+                                  sr[x], prow / (Hq * N), (prow / N) % Hq, i);
+        }
+    }
+    return SA_OK;
+}
+
+// With checks on: wait for the lists, copy them and the selection to the
+// host and check them.
+int run_far_checks(const Plan& P, const int32_t* sel, const sa::CompactArgs& ca, bool ordered,
+                   hipStream_t s) {
+    auto d2h = [](void* dst, const void* src, size_t bytes) {
+        return bytes == 0 || hipMemcpy(dst, src, bytes, hipMemcpyDeviceToHost) == hipSuccess;
+    };
+    StageScope t("far_list_check", s);   // shows in the stage record that the check ran
+    if (hipStreamSynchronize(s) != hipSuccess) return SA_E_HIP;
+    const size_t lists = (size_t)P.lists;
+    std::vector<int32_t> off(lists + 1), ch(lists + 1);
+    int32_t nch = 0;
+    if (!d2h(&nch, ca.n_chunks, 4) || !d2h(off.data(), ca.list_off, off.size() * 4) ||
+        !d2h(ch.data(), ca.list_ch, ch.size() * 4))
+        return SA_E_HIP;
+    char msg[400] = {0};
+    const long long total = off[lists];
+    if (total < 0 || total > P.max_entries || nch < 0 || nch > P.max_chunks) {
+        fprintf(stderr, "sparse_attn: far-list check: %lld entries, %d chunks (limits %lld, %d)\n", total,
+                nch, (long long)P.max_entries, P.max_chunks);
+        return SA_E_CHECK;
+    }
+    std::vector<int32_t> cl((size_t)nch), cs((size_t)nch), ent((size_t)total);
+    std::vector<int32_t> selh((size_t)P.Bt * P.Hq * P.N * P.top_k);
+    if (!d2h(cl.data(), ca.chunk_list, cl.size() * 4) || !d2h(cs.data(), ca.chunk_start, cs.size() * 4) ||
+        !d2h(ent.data(), ca.entries, ent.size() * 4) || !d2h(selh.data(), sel, selh.size() * 4))
+        return SA_E_HIP;
+    sparse_attn_far_lists f{};
+    f.batch = P.Bt; f.n_q_heads = P.Hq; f.n_kv_heads = P.Hkv; f.seq_len = P.N;
+    f.block_size = P.B; f.n_blocks = P.n; f.top_k = P.top_k; f.span = P.span; f.kslots = P.kslots;
+    f.rows_per_chunk = ca.rows_per_chunk; f.ordered = ordered ? 1 : 0; f.n_chunks = nch;
+    f.max_entries = P.max_entries; f.max_chunks = P.max_chunks;
+    f.sel = selh.data(); f.list_off = off.data(); f.list_ch = ch.data();
+    f.chunk_list = cl.data(); f.chunk_start = cs.data(); f.entries = ent.data();
+    f.detail = msg; f.detail_bytes = sizeof msg;
+    const int rc = check_far_lists_impl(&f);
+    if (rc != SA_OK) fprintf(stderr, "sparse_attn: far-list check failed: %s\n", msg);
+    return rc;
+}
+
 // Per-(batch, kv head, block) lists of the rows that keep that block as a
 // far block, and their chunking.
 int compact_far(const Plan& P, const int32_t* sel, char* ws, bool ordered, hipStream_t s,
@@ -424,7 +570,8 @@ int compact_far(const Plan& P, const int32_t* sel, char* ws, bool ordered, hipSt
     ca.max_chunks = P.max_chunks;
     ca.rows_per_chunk = kRowsPerChunk;
     StageScope t("compact", s);
-    return sa::launch_compact(ca, s) == hipSuccess ? SA_OK : SA_E_HIP;
+    if (sa::launch_compact(ca, s) != hipSuccess) return SA_E_HIP;
+    return g_checks ? run_far_checks(P, sel, ca, ordered, s) : SA_OK;
 }
 
 // ----------------------------------------------------------------------------
@@ -464,7 +611,7 @@ const char* sparse_attn_strerror(int status) {
     switch (status) {
         case SA_OK: return "success";
         case SA_E_INVALID_ARG: return "invalid argument (null pointer, struct_size, negative size or scale)";
-        case SA_E_SHAPE: return "shape mismatch (block_size must be a multiple of 64 dividing seq_len; n_q_heads a multiple of n_kv_heads; top_k <= seq_len/block_size)";
+        case SA_E_SHAPE: return "shape mismatch (block_size must be 8, 16, 32 or a multiple of 64, dividing seq_len; n_q_heads a multiple of n_kv_heads; top_k <= seq_len/block_size)";
         case SA_E_UNSUPPORTED_HEAD_DIM: return "unsupported head_dim (64, 80 or 128) or index_dim (64)";
         case SA_E_NO_SELF: return "window == 0 and top_k == 0: a query would have no guaranteed key";
         case SA_E_ALIGNMENT: return "tensor pointer not aligned (16 bytes for q/k/v/out/idx/workspace, 4 for lse/sink/selections)";
@@ -472,6 +619,7 @@ const char* sparse_attn_strerror(int status) {
         case SA_E_HIP: return "HIP kernel launch failed";
         case SA_E_UNSUPPORTED: return "configuration outside the supported limits";
         case SA_E_SCRATCH_LIMIT: return "the configuration needs more workspace than the allocation-free entry point's static scratch (128 MiB)";
+        case SA_E_CHECK: return "a far-block list invariant failed (sparse_attn_check_far_lists or a checked call)";
         default: return "unknown status";
     }
 }
@@ -499,6 +647,13 @@ int sparse_attn_workspace_bytes(const sparse_attn_cfg* cfg, size_t* bytes) {
     const int rc = make_plan(cfg, &P);
     if (rc != SA_OK) return rc;
     *bytes = P.total;
+    return SA_OK;
+}
+
+int sparse_attn_check_far_lists(const sparse_attn_far_lists* f) { return check_far_lists_impl(f); }
+
+int sparse_attn_set_checks(int enable) {
+    g_checks = enable != 0;
     return SA_OK;
 }
 
