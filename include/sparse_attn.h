@@ -74,6 +74,14 @@
  * All argument checks happen before anything is enqueued, so every code but
  * SA_E_HIP is returned without touching the GPU.  On error, out, lse and
  * the selection outputs are unspecified.
+ *
+ * Non-finite inputs: a NaN or an infinity in q, k or v is an ordinary value.
+ * The call returns SA_OK and every row whose attended set meets it comes out
+ * non-finite; rows that cannot see it are unchanged, except that a
+ * non-finite value in v also reaches, in its own head dimension, the earlier
+ * rows of its 64-key tile (they weight it 0, and 0 * inf is NaN).  Block
+ * selections stay within each row's candidate blocks whatever the scores.
+ * The indexer inputs idx_q, idx_k must be finite.
  */
 #ifndef SPARSE_ATTN_H
 #define SPARSE_ATTN_H

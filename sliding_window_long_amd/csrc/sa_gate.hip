@@ -383,7 +383,11 @@ __global__ __launch_bounds__(64 * gate_waves(QSPLIT)) void gate_kernel(GateArgs 
     constexpr int MP = M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : M <= 16 ? 16 : 32;   // sorting width
     int ids[MP];
 #pragma unroll
-    for (int t = 0; t < MP; ++t) ids[t] = t < m && t < M ? (int)(mask - (L[t] & mask)) : 0x7fffffff;
+    // Clamped to the candidate range: with finite inputs every kept key is
+    // a candidate's and the clamp changes nothing; NaN scores can leave keys
+    // that decode past the last block, and a selection must stay in range.
+    for (int t = 0; t < MP; ++t)
+        ids[t] = t < m && t < M ? min(max((int)(mask - (L[t] & mask)), c0), row_blk - 1) : 0x7fffffff;
     sort_asc<MP>(ids);
     // Ascending: block 0 when forced, the m kept candidates, the own block.
     auto val_at = [&](int t) {

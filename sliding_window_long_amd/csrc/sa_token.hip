@@ -642,7 +642,7 @@ __global__ __launch_bounds__(TOK_THREADS) void tok_resolve_kernel(TokArgs a) {
     for (int m = 0; m < PER; ++m) {
         if (!val[m] || key[m] < prefix) continue;
         const int j = (int)(0xffffffffu - (uint32_t)key[m]);
-        if (j >= row) continue;   // never taken: collected keys are earlier tokens
+        if (j < 0 || j >= row) continue;   // never taken: collected keys are earlier tokens
         const int kc = j >> 5, jl = j & 31;
         const int ln = (row & 31) + 32 * ((jl >> 2) & 1), v = 4 * (jl >> 3) + (jl & 3);
         const size_t hf = mask_half(bt, nt32, nt64, rt, kc, ln);
