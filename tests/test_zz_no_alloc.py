@@ -68,3 +68,49 @@ def test_noalloc_rejects_oversized(dev):
     k = torch.zeros((1, 1, wl.seq_len, 128), dtype=torch.bfloat16, device=dev)
     with pytest.raises(sa.SparseAttnError, match="SCRATCH_LIMIT"):
         sa.forward(q, k, k, block_size=512, top_k=8, noalloc=True)
+
+
+def test_noalloc_under_graph_capture(dev):
+    """The callers this entry point is for include HIP graph capture: one
+    call captured into a graph (inputs, out and lse in fixed buffers), then
+    replayed three times with new inputs copied into those buffers, eager
+    calls and synchronisations between the replays; every replay must equal
+    an eager call on the same inputs bit for bit."""
+    import torch
+    import sliding_window_long_amd as sa
+    for wl in (W.BORA_HYBRID.replace(name="bora_n2048", seq_len=2048, top_k=6, sink=True),
+               W.BITAXON_SWA.replace(name="swa_n2048", seq_len=2048, n_q_heads=4, n_kv_heads=4,
+                                     window=512)):
+        seeds = (31, 32, 33, 34)
+        inps = [W.make_inputs(wl, s) for s in seeds]
+        dv = [{k_: (None if v_ is None else v_.to(dev)) for k_, v_ in i.tensors().items()} for i in inps]
+        kw = dict(block_size=wl.block_size, top_k=wl.top_k, window=wl.window)
+        # fixed buffers the graph reads and writes
+        q, k, v = (dv[0][n].clone() for n in ("q", "k", "v"))
+        sink = None if dv[0]["sink"] is None else dv[0]["sink"].clone()
+        out = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        sa.forward(q, k, v, sink=sink, noalloc=True, out=out, lse=lse, **kw)   # warm-up, eager
+        torch.cuda.synchronize()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                sa.forward(q, k, v, sink=sink, noalloc=True, out=out, lse=lse, **kw)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        for rep, d_in in enumerate(dv[1:]):
+            q.copy_(d_in["q"]); k.copy_(d_in["k"]); v.copy_(d_in["v"])
+            if sink is not None:
+                sink.copy_(d_in["sink"])
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            got_o, got_l = out.clone(), lse.clone()
+            # eager call on the same inputs (its own buffers; same static scratch)
+            ro, rl = sa.forward(d_in["q"], d_in["k"], d_in["v"], sink=d_in["sink"], noalloc=True, **kw)
+            torch.cuda.synchronize()
+            print(f"[gpu] graph replay {rep} {wl.name}", flush=True)
+            assert torch.equal(got_o.view(torch.int16), ro.view(torch.int16)), f"{wl.name} replay {rep}: out"
+            assert torch.equal(got_l.view(torch.int32), rl.view(torch.int32)), f"{wl.name} replay {rep}: lse"
