@@ -63,6 +63,9 @@ def _load(path=None):
     lib.orc_block_select.argtypes = [_f32p, _f64p, _i64, _i64, _i64, _i64, _i64, _i64,
                                      _i64, _i64, _i64, _i64p, _i64, _i32p, _f64p, _f64p]
     lib.orc_block_select.restype = None
+    lib.orc_block_select_at.argtypes = [_f32p, _f64p, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+                                        _i64, _i64, _i64, _i64, _i64p, _i64, _i32p, _f64p, _f64p]
+    lib.orc_block_select_at.restype = None
     lib.orc_token_scores.argtypes = [_f32p, _f32p, _i64, _i64, _i64p, _i64, _f64p]
     lib.orc_token_scores.restype = None
     lib.orc_token_select.argtypes = [_f32p, _f32p, _i64, _i64, _i64, _i64p, _i64,
@@ -193,23 +196,32 @@ def block_scores(q, kb, B, rows, gate_repr="mean", shared=False, first=False):
     return out
 
 
-def block_select(q, kb, B, top_k, rows=None, gate_repr="mean", shared=False, first=False):
+def block_select(q, kb, B, top_k, rows=None, gate_repr="mean", shared=False, first=False,
+                 nk=None):
     """Selected blocks per row [len(rows), top_k] (ascending, -1 padded) and the
     scores of the last kept / first dropped candidate (NaN when absent).
     shared: one selection per kv group (scores summed over its heads);
-    first: block 0 always kept, taking a slot (needs top_k >= 2)."""
+    first: block 0 always kept, taking a slot (needs top_k >= 2).
+    nk: length of the history when the queries continue it (a decode step:
+    row rq at position rq + nk - Nq; kb then holds its nk // B complete
+    blocks); None for a prefill."""
     q = _f32(q)
-    Bt, Hq, N, d = q.shape
+    Bt, Hq, Nq, d = q.shape
     Hkv = kb.shape[1]
     rep = _gate_args(kb, gate_repr, d)
     if first and top_k < 2:
         raise ValueError("keeping the first block needs top_k >= 2")
-    rows = _rows(rows, Bt * Hq * N)
+    nk = Nq if nk is None else nk
+    off = _offset(Nq, nk)
+    if kb.shape[2] != nk // B:
+        raise ValueError("kb must hold the history's complete blocks")
+    rows = _rows(rows, Bt * Hq * Nq)
     sel = np.empty((len(rows), top_k), dtype=np.int32)
     s_last = np.empty(len(rows), dtype=np.float64)
     s_next = np.empty(len(rows), dtype=np.float64)
-    _load().orc_block_select(q, np.ascontiguousarray(kb), Hq, Hkv, N, d, B, top_k, rep,
-                             int(shared), int(first), rows, len(rows), sel, s_last, s_next)
+    _load().orc_block_select_at(q, np.ascontiguousarray(kb), Hq, Hkv, Nq, nk, d, off, B, top_k,
+                                rep, int(shared), int(first), rows, len(rows), sel, s_last,
+                                s_next)
     return sel, s_last, s_next
 
 
@@ -299,20 +311,22 @@ def forward(q, k, v, *, block_size=0, top_k=0, window=0, idx_q=None, idx_k=None,
 
     q [Bt, Hq, Nq, d] may be shorter than k, v [Bt, Hkv, Nk, d] (and idx_q
     than idx_k): the queries then continue the cached history, row rq at
-    position rq + Nk - Nq.  Block gating is a prefill method here (the MoBA
-    summary switches to full attention for generation) and needs Nq = Nk.
+    position rq + Nk - Nq.  Under block gating such a query is gated as the
+    same position of a prefill over the history: its candidates are the
+    complete blocks before its own, pooled from the cache (Nk need not be a
+    multiple of the block size; the own block may be incomplete).
     gate_repr / gate_shared / gate_first pick the block gate's variant
     (see block_pool and block_select); cmp_block > 0 adds the compressed
     branch (see attend)."""
     Bt, Hq, N, d = np.shape(q)
+    Nk = np.shape(k)[2]
     rows = _rows(rows, Bt * Hq * N)
     res = dict(sel=None, s_last=None, s_next=None, tsel=None, t_last=None, t_next=None)
-    if top_k > 0 and np.shape(k)[2] != N:
-        raise ValueError("block gating needs as many queries as keys")
     if top_k > 0:
-        kb = block_pool(k, block_size, gate_repr)
+        nfull = Nk // block_size * block_size
+        kb = block_pool(np.asarray(k)[:, :, :nfull], block_size, gate_repr)
         res["sel"], res["s_last"], res["s_next"] = block_select(
-            q, kb, block_size, top_k, rows, gate_repr, gate_shared, gate_first)
+            q, kb, block_size, top_k, rows, gate_repr, gate_shared, gate_first, nk=Nk)
     if token_top_k > 0:
         trow = (rows // (Hq * N)) * N + rows % N
         uniq, inv = np.unique(trow, return_inverse=True)

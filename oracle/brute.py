@@ -69,12 +69,13 @@ def forward(q, k, v, *, block_size=0, top_k=0, window=0, idx_q=None, idx_k=None,
 
     q may hold fewer rows (Nq) than k, v (Nk): query row iq is then the token
     at position iq + Nk - Nq of the history (the causal offset of the
-    Bit-Axon page).  Block gating needs Nq = Nk."""
+    Bit-Axon page); under block gating it is gated as that position of a
+    prefill (candidates: the complete blocks before its own)."""
     q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
     Bt, Hq, Nq, d = q.shape
     Hkv, N = k.shape[1], k.shape[2]
     off = N - Nq
-    assert off >= 0 and (not top_k or off == 0)
+    assert off >= 0
     G = Hq // Hkv
     scale = 1.0 / math.sqrt(d) if scale is None else scale
     out = np.zeros((Bt, Hq, Nq, d))

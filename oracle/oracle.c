@@ -132,15 +132,16 @@ static double gate_score(const float* qrow, const double* kb, int64_t d, int rep
  * 16 blocks) but no rule for sharing it; summing the heads' scores is the
  * plainest one.
  */
-static double row_score(const float* q, const double* kb, int64_t Hq, int64_t Hkv, int64_t N,
+static double row_score(const float* q, const double* kb, int64_t Hq, int64_t Hkv, int64_t Nq,
                         int64_t d, int64_t n, int rep, int shared, int64_t b, int64_t h,
-                        int64_t i, int64_t c) {
+                        int64_t rq, int64_t c) {
+    /* q [Bt, Hq, Nq, d], query row rq */
     const int64_t G = Hq / Hkv, g = h / G;
     const double* kbc = kb + ((b * Hkv + g) * n + c) * d * (rep ? 2 : 1);
-    if (!shared) return gate_score(q + ((b * Hq + h) * N + i) * d, kbc, d, rep);
+    if (!shared) return gate_score(q + ((b * Hq + h) * Nq + rq) * d, kbc, d, rep);
     double acc = 0.0;
     for (int64_t hh = g * G; hh < (g + 1) * G; ++hh)
-        acc += gate_score(q + ((b * Hq + hh) * N + i) * d, kbc, d, rep);
+        acc += gate_score(q + ((b * Hq + hh) * Nq + rq) * d, kbc, d, rep);
     return acc;
 }
 
@@ -182,26 +183,39 @@ void orc_block_scores(const float* q, const double* kb, int64_t Hq, int64_t Hkv,
  * s_last[t] = score of the m-th kept candidate (NaN if m == 0);
  * s_next[t] = score of the best candidate not kept (NaN if none).
  */
-void orc_block_select(const float* q, const double* kb, int64_t Hq, int64_t Hkv,
-                      int64_t N, int64_t d, int64_t B, int64_t top_k, int64_t rep,
-                      int64_t shared, int64_t first, const int64_t* rows, int64_t nrows,
-                      int32_t* sel, double* s_last, double* s_next) {
+/*
+ * The same for queries q [Bt, Hq, Nq, d] continuing a history of N keys:
+ * row r = (b*Hq + h)*Nq + rq sits at position i = rq + off [Bit-Axon page,
+ * "슬라이딩 윈도우 마스크": the causal offset during decoding].  kb holds the
+ * n = N / B complete blocks of the history; the candidates c < i / B are all
+ * complete.  Reading for a decode step: a new query is gated exactly as the
+ * same position of a prefill over the same history.  orc_block_select is the
+ * case Nq = N, off = 0.
+ */
+void orc_block_select_at(const float* q, const double* kb, int64_t Hq, int64_t Hkv,
+                         int64_t Nq, int64_t N, int64_t d, int64_t off, int64_t B,
+                         int64_t top_k, int64_t rep, int64_t shared, int64_t first,
+                         const int64_t* rows, int64_t nrows, int32_t* sel, double* s_last,
+                         double* s_next) {
     const int64_t n = N / B;
 #pragma omp parallel
     {
-        cand_t* cand = (cand_t*)malloc(sizeof(cand_t) * (size_t)(n > 0 ? n : 1));
+        /* one spare entry; with the loop bound c < n and the bounded writes
+         * below, no selection rule can make this function touch memory
+         * outside its arrays */
+        cand_t* cand = (cand_t*)malloc(sizeof(cand_t) * (size_t)(n + 1));
 #pragma omp for schedule(dynamic, 16)
         for (int64_t t = 0; t < nrows; ++t) {
             const int64_t r = rows[t];
-            const int64_t i = r % N, bh = r / N, b = bh / Hq, h = bh % Hq;
+            const int64_t rq = r % Nq, i = rq + off, bh = r / Nq, b = bh / Hq, h = bh % Hq;
             const int64_t own = i / B;
             /* block 0 forced (top_k >= 2 is the caller's contract; the
              * guard only keeps the row's writes in bounds) */
             const int64_t c0 = (first && own > 0 && top_k >= 2) ? 1 : 0;
             const int64_t nc = own - c0;
-            for (int64_t c = c0; c < own; ++c) {
-                cand[c - c0].s = row_score(q, kb, Hq, Hkv, N, d, n, (int)rep, (int)shared,
-                                           b, h, i, c);
+            for (int64_t c = c0; c < own && c < n; ++c) {
+                cand[c - c0].s = row_score(q, kb, Hq, Hkv, Nq, d, n, (int)rep, (int)shared,
+                                           b, h, rq, c);
                 cand[c - c0].idx = c;
             }
             qsort(cand, (size_t)nc, sizeof(cand_t), cand_cmp);
@@ -210,15 +224,24 @@ void orc_block_select(const float* q, const double* kb, int64_t Hq, int64_t Hkv,
             if (m < 0) m = 0;
             int32_t* out = sel + t * top_k;
             for (int64_t x = 0; x < top_k; ++x) out[x] = -1;
-            for (int64_t x = 0; x < m; ++x) out[x] = (int32_t)cand[x].idx;
-            out[m] = (int32_t)own;
-            if (c0) out[m + 1] = 0;
-            qsort(out, (size_t)(m + 1 + c0), sizeof(int32_t), int32_cmp);
+            for (int64_t x = 0; x < m && x < top_k; ++x) out[x] = (int32_t)cand[x].idx;
+            if (m < top_k) out[m] = (int32_t)own;
+            if (c0 && m + 1 < top_k) out[m + 1] = 0;
+            const int64_t kept = m + 1 + c0 < top_k ? m + 1 + c0 : top_k;
+            qsort(out, (size_t)kept, sizeof(int32_t), int32_cmp);
             s_last[t] = m > 0 ? cand[m - 1].s : NAN;
             s_next[t] = m < nc ? cand[m].s : NAN;
         }
         free(cand);
     }
+}
+
+void orc_block_select(const float* q, const double* kb, int64_t Hq, int64_t Hkv,
+                      int64_t N, int64_t d, int64_t B, int64_t top_k, int64_t rep,
+                      int64_t shared, int64_t first, const int64_t* rows, int64_t nrows,
+                      int32_t* sel, double* s_last, double* s_next) {
+    orc_block_select_at(q, kb, Hq, Hkv, N, N, d, 0, B, top_k, rep, shared, first, rows, nrows,
+                        sel, s_last, s_next);
 }
 
 /*
@@ -351,7 +374,8 @@ int orc_attend_at(const float* q, const float* k, const float* v,
                 for (int64_t s = 0; s < sel_w; ++s) {
                     const int64_t c = sel[t * sel_w + s];
                     if (c < 0) continue;
-                    if (B <= 0 || c >= N / B) { bad = 1; continue; }
+                    /* blocks of the history; a decode step's last one may be incomplete */
+                    if (B <= 0 || c >= (N + B - 1) / B) { bad = 1; continue; }
                     for (int64_t j = c * B; j < (c + 1) * B && j <= i; ++j) mark[j] = 1;
                 }
             if (tsel)

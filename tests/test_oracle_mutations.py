@@ -17,11 +17,12 @@ MUTATIONS = [
     ("own block not counted in k", [("int64_t m = top_k - 1 - c0;", "int64_t m = top_k - c0;")]),
     ("own block competes instead of being forced", [
         ("const int64_t nc = own - c0;", "const int64_t nc = own + 1 - c0;"),
-        ("for (int64_t c = c0; c < own; ++c) {\n                cand[c - c0].s",
-         "for (int64_t c = c0; c <= own; ++c) {\n                cand[c - c0].s"),
+        ("for (int64_t c = c0; c < own && c < n; ++c) {\n                cand[c - c0].s",
+         "for (int64_t c = c0; c <= own && c < n; ++c) {\n                cand[c - c0].s"),
         ("int64_t m = top_k - 1 - c0;", "int64_t m = top_k - c0;"),
-        ("out[m] = (int32_t)own;\n            if (c0) out[m + 1] = 0;\n            qsort(out, (size_t)(m + 1 + c0)",
-         "if (c0) out[m] = 0;\n            qsort(out, (size_t)(m + c0)")]),
+        ("if (m < top_k) out[m] = (int32_t)own;\n            if (c0 && m + 1 < top_k) out[m + 1] = 0;\n"
+         "            const int64_t kept = m + 1 + c0 < top_k ? m + 1 + c0 : top_k;",
+         "if (c0 && m < top_k) out[m] = 0;\n            const int64_t kept = m + c0 < top_k ? m + c0 : top_k;")]),
     ("min/max score keeps only the max corner", [("acc += a > b ? a : b;", "acc += b;")]),
     ("min/max pool swaps min and max", [("lo[e] = mn;\n            hi[e] = mx;",
                                          "lo[e] = mx;\n            hi[e] = mn;")]),
@@ -32,7 +33,8 @@ MUTATIONS = [
     ("gate reads the wrong kv group", [("const int64_t G = Hq / Hkv, g = h / G;\n    const double* kbc",
                                         "const int64_t G = Hq / Hkv, g = h % Hkv;\n    const double* kbc")]),
     ("first block not counted in k", [("int64_t m = top_k - 1 - c0;", "int64_t m = top_k - 1;")]),
-    ("first block forced as block 1", [("if (c0) out[m + 1] = 0;", "if (c0) out[m + 1] = 1;")]),
+    ("first block forced as block 1", [("if (c0 && m + 1 < top_k) out[m + 1] = 0;",
+                                       "if (c0 && m + 1 < top_k) out[m + 1] = 1;")]),
     ("first block also competes", [("const int64_t c0 = (first && own > 0) ? 1 : 0;\n        for (int64_t c = 0; c < n; ++c)",
                                     "const int64_t c0 = 0;\n        for (int64_t c = 0; c < n; ++c)"),
                                    ("const int64_t c0 = (first && own > 0 && top_k >= 2) ? 1 : 0;",
@@ -97,6 +99,9 @@ MUTATIONS = [
     ("pool divides by B - 1", [("dst[e] = acc / (double)B;", "dst[e] = acc / (double)(B - 1);")]),
     ("decode attention ignores the offset", [("const int64_t i = r % Nq + off, bh = r / Nq,",
                                               "const int64_t i = r % Nq, bh = r / Nq,")]),
+    ("decode block select ignores the offset", [
+        ("const int64_t rq = r % Nq, i = rq + off, bh = r / Nq,",
+         "const int64_t rq = r % Nq, i = rq, bh = r / Nq,")]),
     ("decode token select ignores the offset", [
         ("i = r % Nq + off, b = r / Nq;\n            for (int64_t j = 0; j < i; ++j) {",
          "i = r % Nq, b = r / Nq;\n            for (int64_t j = 0; j < i; ++j) {")]),
@@ -156,6 +161,8 @@ PIN_CALLS = [
     for c in range(len(pins.DECODE_CASES)) for n in (1, 5)
 ] + [
     (lambda c=c: pins.test_p16_decode_brute_force(c, False)) for c in range(len(pins.DECODE_CASES))
+] + [
+    (lambda n=n: pins.test_p15_block_decode_over_incomplete_last_block(n)) for n in (1, 3)
 ]
 
 

@@ -321,6 +321,11 @@ DECODE_CASES = [
     dict(window=1000),
     dict(window=5, token_top_k=6, sink=True),
     dict(window=1, token_top_k=40),
+    # block gating during decode: each new query gated as that position of
+    # a prefill over the same history
+    dict(block_size=4, top_k=3, window=3, sink=True),
+    dict(block_size=4, top_k=2),
+    dict(block_size=4, top_k=4, window=1),
 ]
 
 
@@ -346,6 +351,8 @@ def test_p15_decode_is_last_prefill_rows(case, nq):
     np.testing.assert_array_equal(dec["count"], full["count"][last])
     if kw.get("token_top_k"):
         np.testing.assert_array_equal(dec["tsel"], full["tsel"][last])
+    if kw.get("top_k"):
+        np.testing.assert_array_equal(dec["sel"], full["sel"][last])
 
 
 # P16: the decode step against the exact brute force, which places the
@@ -356,7 +363,7 @@ def test_p16_decode_brute_force(case, ties):
     kw = dict(DECODE_CASES[case])
     use_sink = kw.pop("sink", False)
     Bt, Hq, Hkv, Nq, Nk, d, dI = 1, 2, 1, 3, 16, 4, 3
-    kw["window"] = min(kw["window"], 20)
+    kw["window"] = min(kw.get("window", 0), 20)
     kw["token_top_k"] = min(kw.get("token_top_k", 0), 9)
     rng = np.random.default_rng(200 + case + 50 * ties)
     draw = (lambda s: rng.integers(-1, 2, size=s).astype(np.float32)) if ties else \
@@ -923,10 +930,25 @@ def test_gate_variant_arguments_checked():
         oracle.block_select(q, oracle.block_pool(k, 4), 4, 1, None, "mean", False, True)
 
 
-def test_decode_rejects_block_gating():
-    q, k = rnd((1, 1, 4, 8), 70), rnd((1, 1, 16, 8), 71)
-    with pytest.raises(ValueError):
-        oracle.forward(q, k, k, block_size=4, top_k=2)
+# A block-gated decode step over a history whose length is not a multiple of
+# the block size (the own block of the newest queries is incomplete) equals
+# a prefill over that history padded with arbitrary keys to whole blocks, at
+# the same positions: the padding sits after every query, so it is never
+# attended, and its block is never a candidate for them.
+@pytest.mark.parametrize("nq", [1, 3])
+def test_p15_block_decode_over_incomplete_last_block(nq):
+    Bt, Hq, Hkv, Nk, B, d = 1, 4, 2, 61, 8, 8
+    q = rnd((Bt, Hq, 64, d), 72)
+    k, v = rnd((Bt, Hkv, 64, d), 73), rnd((Bt, Hkv, 64, d), 74)
+    kw = dict(block_size=B, top_k=3, window=5)
+    full = oracle.forward(q, k, v, **kw)
+    off = Nk - nq
+    dec = oracle.forward(np.ascontiguousarray(q[:, :, off:Nk]), np.ascontiguousarray(k[:, :, :Nk]),
+                         np.ascontiguousarray(v[:, :, :Nk]), **kw)
+    last = np.array([(bh * 64 + off + r) for bh in range(Bt * Hq) for r in range(nq)])
+    np.testing.assert_array_equal(dec["sel"], full["sel"][last])
+    np.testing.assert_array_equal(dec["out"], full["out"][last])
+    np.testing.assert_array_equal(dec["lse"], full["lse"][last])
 
 
 # The pooled keys are block means (checked with numpy's mean, a different
