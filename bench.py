@@ -8,7 +8,7 @@ synthetic workloads, each a full forward (pool, gate, compaction, far-block
 and near attention) timed the same way, the block-gate variants (min/max
 block summary, selection shared per kv group, first block kept) on the
 block-gated shapes, backward calls (gradients for the forward's selection) on
-the BORA, Bit-Axon SWA and long MoBA shapes, and two decode/append steps (new
+the BORA, Bit-Axon SWA and long MoBA shapes, and three decode/append steps (new
 tokens after a resident KV cache) reported as step time and algorithmic HBM
 bytes per step against the 8 TB/s peak.
 
@@ -251,7 +251,8 @@ def time_backward(wl, seed, dev, steps, warmup):
 # Decode/append steps: nq new tokens per sequence after a cache of
 # wl.seq_len tokens (the queries are the cache's last nq positions).
 DECODE = [(W.BITAXON_SWA.replace(name="bitaxon_swa_decode_kv16384", batch=4), 1),
-          (W.SWA_TOKEN_TOPK.replace(name="swa_tokentopk_decode_kv65536"), 4)]
+          (W.SWA_TOKEN_TOPK.replace(name="swa_tokentopk_decode_kv65536"), 4),
+          (W.LONG_MOBA.replace(name="long_moba_decode_kv131072"), 4)]
 
 
 def time_decode(wl, nq, seed, dev, steps, warmup):
@@ -266,28 +267,40 @@ def time_decode(wl, nq, seed, dev, steps, warmup):
     iq = None if g["idx_q"] is None else g["idx_q"][:, off:].contiguous()
     ws = sa.Workspace()
     kw = dict(window=wl.window, idx_q=iq, idx_k=g["idx_k"], token_top_k=wl.token_top_k,
-              sink=g["sink"], workspace=ws)
+              sink=g["sink"], workspace=ws, block_size=wl.block_size, top_k=wl.top_k)
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
-    _, _, _, tsel = sa.forward(q, g["k"], g["v"], return_selection=True, **kw)
+    _, _, bsel, tsel = sa.forward(q, g["k"], g["v"], return_selection=True, **kw)
     torch.cuda.synchronize()
-    # Keys each query reads: the window plus the kept tokens before it.
+    # Keys each (batch, kv head, query) reads: its contiguous range (the
+    # window; under the block gate joined by the own block), then the kept
+    # tokens, or the keys of the kept blocks of any head of the group, below it.
     keys = 0
     tsel = None if tsel is None else tsel.cpu().numpy()
+    bsel = None if bsel is None else bsel.cpu().numpy()
+    B, G = wl.block_size, wl.n_q_heads // wl.n_kv_heads
     for b in range(wl.batch):
         for r in range(nq):
             p = off + r
-            lo = max(0, p - wl.window + 1)
-            keys += p - lo + 1
-            if tsel is not None:
-                keys += int(((tsel[b, r] >= 0) & (tsel[b, r] < lo)).sum())
-    kv_bytes = keys * wl.n_kv_heads * wl.head_dim * 2 * 2
+            lo = max(0, p - wl.window + 1) if wl.window > 0 else p
+            if bsel is not None:
+                lo = min(lo, p // B * B)
+            for g_ in range(wl.n_kv_heads):
+                keys += p - lo + 1
+                if tsel is not None:
+                    keys += int(((tsel[b, r] >= 0) & (tsel[b, r] < lo)).sum())
+                if bsel is not None:
+                    blocks = {int(c) for h in range(g_ * G, (g_ + 1) * G) for c in bsel[b, h, r] if c >= 0}
+                    keys += sum(max(0, min(B, lo - c * B)) for c in blocks)
+    kv_bytes = keys * wl.head_dim * 2 * 2
     qo_bytes = wl.batch * wl.n_q_heads * nq * (wl.head_dim * 2 * 2 + 4)
     idx_bytes = wl.batch * (wl.seq_len + nq) * wl.index_dim * 2 if wl.token_top_k else 0
+    # the block gate pools the cache's complete blocks on every step
+    pool_bytes = wl.batch * wl.n_kv_heads * (wl.seq_len // B) * B * wl.head_dim * 2 if bsel is not None else 0
     def call():
         sa.forward(q, g["k"], g["v"], out=out, lse=lse, **kw)
     _, med, _, stage_ms = timed_calls(call, steps, warmup)
-    return med, stage_ms, kv_bytes + qo_bytes + idx_bytes
+    return med, stage_ms, kv_bytes + qo_bytes + idx_bytes + pool_bytes
 
 
 def cpu_baseline(inp, budget_s=15.0):

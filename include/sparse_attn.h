@@ -46,9 +46,14 @@
  * autoregressive decoding with a KV cache]: the seq_len queries are the
  * newest positions of a history of kv_len keys; query row r is position
  * i = kv_len - seq_len + r and the three steps above apply to it over keys
- * 0 .. kv_len-1 (the token gate scans the whole cached history).  Block
- * gating is not offered here: the MoBA summary page runs generation with
- * full attention (window >= kv_len).  Limits: seq_len <= 64.
+ * 0 .. kv_len-1 (the token gate scans the whole cached history).  Under
+ * block gating a new query is gated as that position of a prefill over the
+ * history: its own block (the last one may be incomplete) and the best
+ * top_k - 1 complete earlier blocks by the dot product with their mean keys
+ * (pooled from the cache on every call), per query head; mean summaries
+ * only (no min/max, shared or first-block variant), at most 4096 complete
+ * blocks and top_k <= 64.  Full attention (what the MoBA summary page runs
+ * for generation) is a window >= kv_len.  Limits: seq_len <= 64.
  *
  * Layouts (row-major, contiguous, device memory; kv_len = seq_len unless a
  * decode step):
@@ -166,8 +171,8 @@ typedef struct {
     int32_t* token_sel_out; /* optional copy-out of the token selection, or NULL */
     void* stream;           /* hipStream_t, NULL = default stream */
     int32_t kv_len;         /* keys of the history: 0 or seq_len for a prefill;
-                               > seq_len for a decode/append step (seq_len <= 64,
-                               top_k == 0; kv_len <= 65536 with a token gate) */
+                               > seq_len for a decode/append step (seq_len <= 64;
+                               kv_len <= 65536 with a token gate) */
     int32_t gate_repr;      /* sa_gate_repr; SA_GATE_MEAN unless top_k > 0 */
     int32_t gate_shared;    /* 0 or 1: one block selection per kv group; 0 unless top_k > 0 */
     int32_t gate_first;     /* 0 or 1: block 0 always kept (top_k >= 2); 0 unless top_k > 0 */

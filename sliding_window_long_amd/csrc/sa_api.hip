@@ -49,6 +49,9 @@ struct Plan {
     int top_t, nt32, tok_units, tok_nkp;
     bool dec;               // decode/append step: Nk > N
     int Nk, dec_cmax;
+    bool dgate;             // decode step with a block gate
+    int nb;                 // its complete blocks (Nk / B)
+    size_t o_dec_kbar;
     float scale;
     // workspace regions (byte offsets)
     size_t o_sinkterm, o_bmax_q, o_bmax_do, o_bmax_k, o_bmax_v, o_bgmax, o_bexp, o_cmp_grad;
@@ -91,7 +94,10 @@ int make_plan(const sparse_attn_cfg* c, Plan* p, bool bwd = false) {
     const int Nk = c->kv_len > 0 ? c->kv_len : c->seq_len;
     if (Nk < c->seq_len) return SA_E_INVALID_ARG;
     const bool dec = Nk > c->seq_len;
-    if (dec && (c->top_k > 0 || c->seq_len > sa::kDecMaxQ || c->cmp_block > 0))
+    if (dec && (c->seq_len > sa::kDecMaxQ || c->cmp_block > 0)) return SA_E_UNSUPPORTED;
+    // A decode step's block gate: mean block summaries, one selection per
+    // query head (the variants are prefill-only).
+    if (dec && c->top_k > 0 && (c->gate_repr != SA_GATE_MEAN || c->gate_shared || c->gate_first))
         return SA_E_UNSUPPORTED;
     // The compressed branch joins window / block gating (the NSA layout), not
     // the token gate.
@@ -130,6 +136,23 @@ int make_plan(const sparse_attn_cfg* c, Plan* p, bool bwd = false) {
         auto take = [&](size_t bytes) { const size_t o = off; off = align_up(off + bytes); return o; };
         P.tok = c->token_top_k > 0;
         P.top_t = P.tok ? c->token_top_k : 0;
+        P.dgate = c->top_k > 0;
+        if (P.dgate) {
+            // Blocks of the history; the last may be incomplete (it is then
+            // the own block of the newest queries, never a candidate).
+            P.B = c->block_size;
+            if (!(P.B == 8 || P.B == 16 || P.B == 32 || (P.B >= 64 && P.B % 64 == 0))) return SA_E_SHAPE;
+            P.top_k = c->top_k;
+            if (P.top_k > ((long long)P.Nk + P.B - 1) / P.B) return SA_E_SHAPE;
+            P.nb = P.Nk / P.B;
+            if (P.nb > sa::kDecMaxBlocks || P.top_k > sa::kDecMaxTopK) return SA_E_UNSUPPORTED;
+            P.top_t = (P.top_k - 1) * P.B;   // keys listed per query, at most
+            if ((long long)P.Bt * P.Hq * P.N * (P.top_t > 0 ? P.top_t : 1) >= (1LL << 31))
+                return SA_E_UNSUPPORTED;
+            P.o_dec_kbar = take((size_t)P.Bt * P.Hkv * (P.nb > 0 ? P.nb : 1) * P.D * 4);
+            P.o_dec_list = take((size_t)P.Bt * P.Hq * P.N * (P.top_t > 0 ? P.top_t : 1) * 4);
+            P.o_dec_nfar = take((size_t)P.Bt * P.Hq * P.N * 4);
+        }
         if (P.tok) {
             P.o_dec_scores = take((size_t)P.Bt * P.N * P.Nk * 4);
             P.o_dec_list = take((size_t)P.Bt * P.N * P.top_t * 4);
@@ -140,7 +163,11 @@ int make_plan(const sparse_attn_cfg* c, Plan* p, bool bwd = false) {
                 P.o_dec_redo = take((size_t)P.Bt * P.N * 4);
             }
         }
-        const long long span = (c->window < P.Nk ? c->window : P.Nk) + (long long)P.top_t;
+        // keys one query attends: its contiguous range (the window, under a
+        // block gate joined by the own block) and its list
+        long long near = c->window < P.Nk ? c->window : P.Nk;
+        if (P.dgate && (P.B < P.Nk ? P.B : P.Nk) > near) near = P.B < P.Nk ? P.B : P.Nk;
+        const long long span = near + (long long)P.top_t;
         const int chunk = sa::dec_chunk(P.f32);
         P.dec_cmax = (int)((span + chunk - 1) / chunk);
         P.o_dec_part = take((size_t)P.Bt * P.Hq * P.N * P.dec_cmax * (P.D + 2) * 4);
@@ -771,6 +798,20 @@ int sparse_attn_fwd(const void* q, const void* k, const void* v, const sparse_at
             }
             StageScope t("decode_token_select", s);
             if (!ok(sa::launch_decode_select(da, s))) return SA_E_HIP;
+        }
+        if (P.dgate) {
+            da.B = P.B; da.top_k = P.top_k; da.nb = P.nb; da.per_head = 1;
+            da.kbar = (const float*)(ws + P.o_dec_kbar);
+            da.list = (int32_t*)(ws + P.o_dec_list);
+            da.nfar = (int32_t*)(ws + P.o_dec_nfar);
+            da.bsel = cfg->block_sel_out;
+            if (P.nb > 0) {
+                sa::PoolArgs pa{k, P.Nk, P.B, P.nb, (float*)(ws + P.o_dec_kbar), nullptr, 0, 0};
+                StageScope t("decode_block_pool", s);
+                if (!ok(sa::launch_pool(pa, P.D, P.f32, P.Bt * P.Hkv * P.nb, s))) return SA_E_HIP;
+            }
+            StageScope t("decode_block_select", s);
+            if (!ok(sa::launch_decode_block_select(da, s))) return SA_E_HIP;
         }
         StageScope t("decode_attn", s);
         return ok(sa::launch_decode_attn(da, s)) ? SA_OK : SA_E_HIP;

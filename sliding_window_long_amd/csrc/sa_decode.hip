@@ -470,12 +470,18 @@ __global__ __launch_bounds__(SEL_THREADS) void dec_select_kernel(DecArgs a) {
 
 // Attended keys of query r: the window [lo, p] (nw keys) then the nt kept
 // tokens before lo.
-__device__ __forceinline__ void dec_span(const DecArgs& a, int bt, int r, int& p, int& lo, int& nw,
-                                         int& nt) {
+// Query r of batch bt (query head h for per-head lists) at position p
+// attends the contiguous keys lo .. p (nw of them: the window, joined under
+// a block gate by the own block from its first key) and nt listed keys
+// before lo.
+__device__ __forceinline__ void dec_span(const DecArgs& a, int bt, int h, int r, int& p, int& lo,
+                                         int& nw, int& nt) {
     p = a.Nk - a.Nq + r;
     lo = a.window > 0 ? max(0, p - a.window + 1) : p;
-    nw = a.window > 0 ? p - lo + 1 : 0;
-    nt = a.list ? a.nfar[(size_t)bt * a.Nq + r] : 0;
+    if (a.B > 0) lo = min(lo, (p / a.B) * a.B);
+    nw = (a.window > 0 || a.B > 0) ? p - lo + 1 : 0;
+    const size_t lrow = a.per_head ? ((size_t)bt * a.Hq + h) * a.Nq + r : (size_t)bt * a.Nq + r;
+    nt = a.list ? a.nfar[lrow] : 0;
 }
 
 // Eight consecutive elements of a row staged in LDS, from byte offset b.
@@ -521,28 +527,33 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_attn_kernel(DecArgs a) {
     extern __shared__ float dyn[];   // q [G][D], logits [G][CH]: sized per launch
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c = blockIdx.x, bt = blockIdx.z;
-    const int g = blockIdx.y / a.Nq, r = blockIdx.y % a.Nq;
-    const int G = a.Hq / a.Hkv;
+    // The workgroup's query heads h0 .. h0 + G - 1 share its keys: a kv
+    // group, or under per-head lists one query head.
+    const int grp = blockIdx.y / a.Nq, r = blockIdx.y % a.Nq;
+    const int Gr = a.Hq / a.Hkv;
+    const int G = a.per_head ? 1 : Gr;
+    const int kvh = a.per_head ? grp / Gr : grp, h0 = a.per_head ? grp : grp * Gr;
     float* const qs = dyn;
     float* const ps = dyn + G * D;
     int p, lo, nw, nt;
-    dec_span(a, bt, r, p, lo, nw, nt);
+    dec_span(a, bt, h0, r, p, lo, nw, nt);
     const int L = nw + nt, key0 = c * CH;
     if (key0 >= L) return;   // whole block: nothing past the attended keys
     const int nk = min(CH, L - key0);
 
     for (int x = tid; x < G * D; x += DEC_THREADS) {
         const int hl = x / D, e = x % D;
-        qs[x] = dec_load(a.q, (((size_t)bt * a.Hq + g * G + hl) * a.Nq + r) * D + e, a.f32);
+        qs[x] = dec_load(a.q, (((size_t)bt * a.Hq + h0 + hl) * a.Nq + r) * D + e, a.f32);
     }
     if (tid < CH) {
         const int idx = key0 + min(tid, nk - 1);   // rows past nk repeat the last key
-        js[tid] = idx < nw ? lo + idx : a.list[((size_t)bt * a.Nq + r) * a.top_t + (idx - nw)];
+        const size_t lrow = a.per_head ? ((size_t)bt * a.Hq + h0) * a.Nq + r : (size_t)bt * a.Nq + r;
+        js[tid] = idx < nw ? lo + idx : a.list[lrow * a.top_t + (idx - nw)];
     }
     __syncthreads();
 
     // Stage K and V rows: piece x = row * PIECES + col.
-    const size_t kvb = ((size_t)bt * a.Hkv + g) * a.Nk;
+    const size_t kvb = ((size_t)bt * a.Hkv + kvh) * a.Nk;
     const uint8_t* kg = (const uint8_t*)a.k;
     const uint8_t* vg = (const uint8_t*)a.v;
     uint4 kr[PER], vr[PER];
@@ -625,7 +636,7 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_attn_kernel(DecArgs a) {
         const int h2 = x / D, ee = x % D, pr2 = h2 * DG + ee / 8;
         float sum = 0.f;
         for (int q_ = 0; q_ < parts; ++q_) sum += acc[(q_ * pairs + pr2) * 8 + (ee & 7)];
-        const size_t row = ((size_t)bt * a.Hq + g * G + h2) * a.Nq + r;
+        const size_t row = ((size_t)bt * a.Hq + h0 + h2) * a.Nq + r;
         float* dst = a.part + (row * a.cmax + c) * (D + 2);
         dst[ee] = sum;
         if (ee == 0) {
@@ -647,7 +658,7 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_combine_kernel(DecArgs a) {
     const int r = (int)(row % a.Nq), bt = (int)(row / ((size_t)a.Hq * a.Nq));
     const int h = (int)((row / a.Nq) % a.Hq);
     int p, lo, nw, nt;
-    dec_span(a, bt, r, p, lo, nw, nt);
+    dec_span(a, bt, h, r, p, lo, nw, nt);
     const int chunk = dec_chunk(a.f32 != 0);
     const int nc = (nw + nt + chunk - 1) / chunk;
     const float* src = a.part + row * a.cmax * (D + 2);
@@ -694,8 +705,9 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_combine_kernel(DecArgs a) {
 
 template <int D>
 static hipError_t dec_d(const DecArgs& a, hipStream_t s) {
-    const dim3 ag((unsigned)a.cmax, (unsigned)(a.Hkv * a.Nq), (unsigned)a.Bt);
-    const int G = a.Hq / a.Hkv;
+    const int groups = a.per_head ? a.Hq : a.Hkv;
+    const dim3 ag((unsigned)a.cmax, (unsigned)(groups * a.Nq), (unsigned)a.Bt);
+    const int G = a.per_head ? 1 : a.Hq / a.Hkv;
     const size_t dyn = (size_t)G * (D + dec_chunk(a.f32 != 0)) * sizeof(float);   // q, logits
     if (a.f32)
         hipLaunchKernelGGL((dec_attn_kernel<D, true>), ag, dim3(DEC_THREADS), dyn, s, a);
@@ -739,6 +751,97 @@ hipError_t launch_decode_select(const DecArgs& a, hipStream_t s) {
     // queries whose merge may be inexact, selected again whole
     hipLaunchKernelGGL((dec_select_kernel<65536 / SEL_THREADS, kSelWhole>),
                        dim3((unsigned)a.Nq, (unsigned)a.Bt), dim3(SEL_THREADS), 0, s, a);
+    return hipGetLastError();
+}
+
+// Block gate of a decode step [MoBA summary page, "블록 분할과 top-k 게이팅"
+// and "인과성 보존": score every earlier block by the query's dot product
+// with its mean key, keep the top k with the own block always among them;
+// read for a decode step as the same position of a prefill over the
+// history].  One 64-lane workgroup per (batch, query head, query): the query
+// at position p scores the complete blocks c < p / B against their fp32
+// means, keeps the best min(top_k - 1, p / B) by (score desc, index asc) --
+// an order key ord(score) << 32 | (2^32 - 1 - c), whose wave-wide maximum is
+// taken top_k - 1 times -- and lists the kept blocks' keys below lo (the
+// first key of its contiguous range [lo, p]: the own block, joined with the
+// window), ascending.  Writes list, nfar and, when asked, bsel.
+__global__ __launch_bounds__(64) void dec_block_select_kernel(DecArgs a) {
+    __shared__ float qs[128];
+    __shared__ uint64_t keys[kDecMaxBlocks];
+    __shared__ int kept[kDecMaxTopK];
+    const int lane = threadIdx.x;
+    const size_t row = blockIdx.x;   // (bt * Hq + h) * Nq + r
+    const int r = (int)(row % a.Nq), h = (int)((row / a.Nq) % a.Hq);
+    const int bt = (int)(row / ((size_t)a.Nq * a.Hq)), g = h / (a.Hq / a.Hkv);
+    const int p = a.Nk - a.Nq + r, own = p / a.B;
+    const int ncand = min(own, min(a.nb, kDecMaxBlocks));   // own <= nb, nb <= kDecMaxBlocks (plan)
+    for (int e = lane; e < a.D; e += 64) qs[e] = dec_load(a.q, row * a.D + e, a.f32);
+    __syncthreads();
+    const float* kb = a.kbar + (size_t)(bt * a.Hkv + g) * a.nb * a.D;
+    for (int c = lane; c < ncand; c += 64) {
+        const float* kr = kb + (size_t)c * a.D;
+        float sc = 0.f;
+        for (int e = 0; e < a.D; e += 4) {
+            const float4 k4 = *(const float4*)(kr + e);
+            sc = fmaf(qs[e], k4.x, sc);
+            sc = fmaf(qs[e + 1], k4.y, sc);
+            sc = fmaf(qs[e + 2], k4.z, sc);
+            sc = fmaf(qs[e + 3], k4.w, sc);
+        }
+        keys[c] = (uint64_t)dec_ord32(sc) << 32 | (uint64_t)(0xffffffffu - (uint32_t)c);
+    }
+    __syncthreads();
+    const int m = min(min(a.top_k - 1, kDecMaxTopK), ncand);
+    for (int t = 0; t < m; ++t) {
+        uint64_t best = 0;
+        for (int c = lane; c < ncand; c += 64) best = keys[c] > best ? keys[c] : best;
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) {
+            const uint32_t lo32 = (uint32_t)__shfl_xor((int)(uint32_t)best, d);
+            const uint32_t hi32 = (uint32_t)__shfl_xor((int)(uint32_t)(best >> 32), d);
+            const uint64_t o = (uint64_t)hi32 << 32 | lo32;
+            best = o > best ? o : best;
+        }
+        // every key not yet taken is nonzero, so best names a candidate
+        const int c = min(max((int)(0xffffffffu - (uint32_t)best), 0), ncand - 1);
+        if (lane == 0) kept[t] = c;
+        if (lane == (c & 63)) keys[c] = 0;   // the lane that scans c
+        __syncthreads();
+    }
+    if (lane == 0)   // ascending
+        for (int t = 1; t < m; ++t) {
+            const int x = kept[t];
+            int u = t - 1;
+            while (u >= 0 && kept[u] > x) {
+                kept[u + 1] = kept[u];
+                --u;
+            }
+            kept[u + 1] = x;
+        }
+    __syncthreads();
+    if (a.bsel) {
+        int32_t* o = a.bsel + row * a.top_k;
+        for (int t = lane; t < a.top_k; t += 64) o[t] = t < m ? kept[t] : (t == m ? own : -1);
+    }
+    int lo = own * a.B;
+    if (a.window > 0) lo = min(lo, max(0, p - a.window + 1));
+    int32_t* L = a.list + row * a.top_t;
+    int pos = 0;
+    for (int t = 0; t < m; ++t) {
+        const int c0 = kept[t] * a.B;
+        const int cnt = max(0, min(a.B, lo - c0));   // <= B: the list holds (top_k - 1) B keys
+        for (int j = lane; j < cnt; j += 64) L[pos + j] = c0 + j;
+        pos += cnt;
+    }
+    if (lane == 0) a.nfar[row] = pos;
+}
+
+hipError_t launch_decode_block_select(const DecArgs& a, hipStream_t s) {
+    if (a.B <= 0 || a.D > 128 || a.nb > kDecMaxBlocks || a.top_k > kDecMaxTopK + 1 ||
+        a.top_t < (a.top_k - 1) * a.B)
+        return hipErrorInvalidValue;
+    const unsigned rows = (unsigned)((size_t)a.Bt * a.Hq * a.Nq);
+    hipLaunchKernelGGL(dec_block_select_kernel, dim3(rows), dim3(64), 0, s, a);
     return hipGetLastError();
 }
 

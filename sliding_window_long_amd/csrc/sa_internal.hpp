@@ -284,7 +284,20 @@ struct DecArgs {
     int cmax;               // tiles of dec_chunk(f32) attended keys per query, upper bound
     void* out;              // [Bt, Hq, Nq, D], the input dtype
     float* lse;             // [Bt, Hq, Nq]
+    // Block gate of a decode step (B > 0): every query head keeps its own
+    // list (per_head), the keys of its kept blocks below its range [lo, p].
+    int B;                  // block size, 0: no block gate
+    int top_k;              // blocks kept per query, the own block included
+    int nb;                 // complete blocks of the history (Nk / B)
+    const float* kbar;      // [Bt, Hkv, nb, D] fp32 block means
+    int32_t* bsel;          // [Bt, Hq, Nq, top_k] kept blocks (ascending, own last, -1), or nullptr
+    int per_head;           // list and nfar indexed by (batch, q head, query)
 };
+
+// A decode step's block gate scores at most this many complete blocks per
+// query (their keys sit in the selecting workgroup's LDS).
+constexpr int kDecMaxBlocks = 4096;
+constexpr int kDecMaxTopK = 64;
 
 // The decode token selection takes one workgroup per query.  When few
 // queries (rows = Bt * Nq <= kDecSplitRows) would leave most of the chip
@@ -309,6 +322,7 @@ inline bool dec_split_select(long long rows, int Nk, int top_t) {
 }
 hipError_t launch_decode_select(const DecArgs& a, hipStream_t s);
 hipError_t launch_decode_attn(const DecArgs& a, hipStream_t s);
+hipError_t launch_decode_block_select(const DecArgs& a, hipStream_t s);
 
 hipError_t launch_token_select(const TokArgs& a, int split, hipStream_t s);
 hipError_t launch_token_list(const TokArgs& a, int32_t* out, hipStream_t s);

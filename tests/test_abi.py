@@ -85,7 +85,15 @@ def code_of(params, **cfg_fields):
     (sa.Params(1, 4, 4, 64 * 80, 64, block_size=64, top_k=3, window=64 * 65 + 1), -8),  # 65 near blocks
     (sa.Params(1, 4, 4, 256, 64, window=8, kv_len=255), -1),          # fewer keys than queries
     (sa.Params(1, 4, 4, 256, 64, window=8, kv_len=-1), -1),
-    (sa.Params(1, 4, 4, 4, 64, block_size=64, top_k=2, kv_len=256), -8),  # decode with block gate
+    # decode with a block gate: mean summaries, per-head selection only; at
+    # most 4096 complete blocks and top 64
+    (sa.Params(1, 4, 4, 4, 64, block_size=64, top_k=2, kv_len=256, gate_repr=1), -8),
+    (sa.Params(1, 4, 2, 4, 64, block_size=64, top_k=2, kv_len=256, gate_shared=1), -8),
+    (sa.Params(1, 4, 4, 4, 64, block_size=64, top_k=2, kv_len=256, gate_first=1), -8),
+    (sa.Params(1, 4, 4, 4, 64, block_size=48, top_k=2, kv_len=256), -2),
+    (sa.Params(1, 4, 4, 4, 64, block_size=64, top_k=5, kv_len=250), -2),     # 4 blocks
+    (sa.Params(1, 1, 1, 1, 64, block_size=8, top_k=2, kv_len=8 * 4097), -8),
+    (sa.Params(1, 1, 1, 1, 64, block_size=8, top_k=65, kv_len=8 * 100), -8),
     (sa.Params(1, 4, 4, 65, 64, window=8, kv_len=256), -8),           # decode past 64 queries
     (sa.Params(1, 4, 1, 1, 128, window=8, token_top_k=16, index_dim=64,
                kv_len=65536 + 1), -8),                               # decode: 16-bit token ids

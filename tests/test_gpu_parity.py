@@ -794,6 +794,35 @@ def test_decode_token_long_history_batch(dev):
     run_and_check(decode_inputs(wl, 3, 77), dev, label="decode_long batch 2")
 
 
+# --- decode step under the block gate: every new query is gated as that
+# position of a prefill over the cache (own block, the best k - 1 complete
+# earlier blocks by their mean keys, the window); the cache need not end on a
+# block boundary ---
+@pytest.mark.parametrize("d", [64, 80, 128])
+@pytest.mark.parametrize("Nk,nq,B,top_k,window,offs", [(1024, 1, 64, 4, 0, True),
+                                                      (1000, 5, 64, 3, 100, False),
+                                                      (704, 64, 16, 6, 20, True),
+                                                      (4096, 3, 128, 16, 512, True),
+                                                      (513, 2, 8, 40, 0, False)])
+def test_decode_blocks(dev, d, Nk, nq, B, top_k, window, offs):
+    wl = W.Workload("dec_blk", 2, 4, 2, Nk, d, "bf16", block_size=B, top_k=top_k, window=window,
+                    sink=True, block_offsets=offs)
+    run_and_check(decode_inputs(wl, nq, 41 + d + Nk + nq), dev, label=f"decode_blocks nq={nq} B={B}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "fp8"])
+def test_decode_blocks_dtypes(dev, dtype):
+    wl = W.Workload("dec_blk_dt", 1, 8, 2, 2048, 128, dtype, block_size=64, top_k=5, window=64,
+                    block_offsets=dtype == "f32")
+    run_and_check(decode_inputs(wl, 7, 5), dev, label=f"decode_blocks {dtype}")
+
+
+def test_decode_blocks_long_moba_cache(dev):
+    # The long-MoBA layout (32 query / 8 kv heads, d 128, blocks of 512, top
+    # 8) after a full 131072-token cache: 4 new tokens, every row checked.
+    run_and_check(decode_inputs(W.LONG_MOBA, 4, 8), dev, label="decode_blocks long_moba")
+
+
 @pytest.mark.parametrize("Nk,top_t", [(1500, 37), (20000, 37), (20000, 300)])
 def test_decode_token_ties(dev, Nk, top_t):
     # Equal indexer keys: the lowest token ids win in the decode step too.
