@@ -300,7 +300,17 @@ def time_decode(wl, nq, seed, dev, steps, warmup):
     def call():
         sa.forward(q, g["k"], g["v"], out=out, lse=lse, **kw)
     _, med, _, stage_ms = timed_calls(call, steps, warmup)
-    return med, stage_ms, kv_bytes + qo_bytes + idx_bytes + pool_bytes
+    extra = {}
+    if bsel is not None:
+        # the same step with the block means kept by the caller
+        nb = wl.seq_len // B
+        means = sa.block_pool(g["k"][:, :, :nb * B].contiguous(), B)
+        def call_means():
+            sa.forward(q, g["k"], g["v"], out=out, lse=lse, block_means=means, **kw)
+        _, med_m, _, _ = timed_calls(call_means, steps, warmup)
+        extra = {"ms_per_step_caller_means": med_m,
+                 "algorithmic_bytes_caller_means": kv_bytes + qo_bytes + means.numel() * 4}
+    return med, stage_ms, kv_bytes + qo_bytes + idx_bytes + pool_bytes, extra
 
 
 def cpu_baseline(inp, budget_s=15.0):
@@ -454,13 +464,13 @@ def main():
                                         "stage_ms": bst}
         for dwl, nq in DECODE:
             print(f"[bench] decode {dwl.name}", file=sys.stderr, flush=True)
-            dms, dst, dbytes = time_decode(dwl, nq, 7, dev, 50, 5)
+            dms, dst, dbytes, dextra = time_decode(dwl, nq, 7, dev, 50, 5)
             extra[dwl.name] = {"new_tokens_per_seq": nq, "ms_per_step": dms,
                                "tokens_per_s": dwl.batch * nq / (dms * 1e-3),
                                "algorithmic_bytes": dbytes,
                                "hbm_gbs": dbytes / (dms * 1e-3) / 1e9,
                                "hbm_frac": dbytes / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                               "stage_ms": dst}
+                               "stage_ms": dst, **dextra}
         result["workloads"] = extra
     if not args.no_cpu:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)

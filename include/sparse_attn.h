@@ -179,6 +179,14 @@ typedef struct {
     int32_t cmp_block;      /* tokens per compressed key/value (the BORA card's 8); 0 = no
                                compressed branch.  Prefill (and its backward) only, not
                                with token_top_k */
+    const float* block_means; /* decode step under the block gate: fp32 means of the
+                               history's complete blocks [batch, n_kv_heads,
+                               kv_len / block_size, head_dim] (block c = keys
+                               cB .. cB+B-1), kept by the caller as the cache grows
+                               (sparse_attn_block_pool gives them); the step then reads
+                               them instead of pooling the cache.  NULL: pooled on every
+                               call.  Must be NULL in every other call
+                               (SA_E_INVALID_ARG) */
 } sparse_attn_cfg;
 
 /* Bytes of device workspace sparse_attn_fwd needs for this configuration

@@ -52,6 +52,7 @@ class SparseAttnCfg(ctypes.Structure):
         ("kv_len", ctypes.c_int32),
         ("gate_repr", ctypes.c_int32), ("gate_shared", ctypes.c_int32),
         ("gate_first", ctypes.c_int32), ("cmp_block", ctypes.c_int32),
+        ("block_means", ctypes.c_void_p),
     ]
 
 
@@ -341,7 +342,7 @@ def _check_fwd_tensors(q, k, v, idx_q, idx_k, sink, out, lse, token_top_k):
 def forward(q, k, v, *, block_size=0, top_k=0, window=0, idx_q=None, idx_k=None,
             token_top_k=0, sink=None, scale=None, return_selection=False,
             workspace: Workspace | None = None, out=None, lse=None, gate_repr="mean",
-            gate_shared=False, gate_first=False, cmp_block=0, noalloc=False):
+            gate_shared=False, gate_first=False, cmp_block=0, noalloc=False, block_means=None):
     """Causal sparse-attention prefill on q's device and torch's current
     stream.  Returns (out, lse) or, with return_selection,
     (out, lse, block_sel, token_sel).  When k, v (and idx_k) hold more
@@ -350,7 +351,10 @@ def forward(q, k, v, *, block_size=0, top_k=0, window=0, idx_q=None, idx_k=None,
     "minmax"), gate_shared and gate_first select the block gate's variant;
     cmp_block > 0 adds the compressed branch (see the C header).  noalloc:
     call sparse_attn_fwd_noalloc (the library's static scratch instead of a
-    workspace; out and lse are still allocated here unless given)."""
+    workspace; out and lse are still allocated here unless given).
+    block_means: for a decode step under the block gate, the fp32 means of the
+    history's complete blocks [batch, n_kv_heads, kv_len // block_size, d]
+    (see block_pool), used instead of pooling the cache."""
     import torch
     _check_fwd_tensors(q, k, v, idx_q, idx_k, sink, out, lse, token_top_k)
     index_dim = idx_q.shape[-1] if idx_q is not None else 0
@@ -376,6 +380,15 @@ def forward(q, k, v, *, block_size=0, top_k=0, window=0, idx_q=None, idx_k=None,
         cfg.idx_q, cfg.idx_k = idx_q.data_ptr(), idx_k.data_ptr()
     if sink is not None:
         cfg.sink = sink.data_ptr()
+    if block_means is not None:
+        Nk = k.shape[2]
+        _need(q.shape[2] < Nk and top_k > 0, "block_means serve a decode step under the block gate")
+        _need(tuple(block_means.shape) == (q.shape[0], k.shape[1], Nk // block_size, q.shape[3]),
+              "block_means must be [batch, n_kv_heads, kv_len // block_size, head_dim]")
+        _need(block_means.dtype == torch.float32, "block_means must be float32", TypeError)
+        _need(block_means.is_contiguous() and block_means.device == q.device,
+              "block_means must be contiguous on q's device")
+        cfg.block_means = block_means.data_ptr()
     cfg.stream = torch.cuda.current_stream(dev).cuda_stream
     if noalloc:
         sparse_attn_fwd_noalloc(q, k, v, cfg, out, lse)

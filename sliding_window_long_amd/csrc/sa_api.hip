@@ -95,6 +95,8 @@ int make_plan(const sparse_attn_cfg* c, Plan* p, bool bwd = false) {
     if (Nk < c->seq_len) return SA_E_INVALID_ARG;
     const bool dec = Nk > c->seq_len;
     if (dec && (c->seq_len > sa::kDecMaxQ || c->cmp_block > 0)) return SA_E_UNSUPPORTED;
+    // Caller-kept block means serve a decode step's block gate only.
+    if (c->block_means && !(dec && c->top_k > 0)) return SA_E_INVALID_ARG;
     // A decode step's block gate: mean block summaries, one selection per
     // query head (the variants are prefill-only).
     if (dec && c->top_k > 0 && (c->gate_repr != SA_GATE_MEAN || c->gate_shared || c->gate_first))
@@ -732,7 +734,8 @@ int sparse_attn_fwd(const void* q, const void* k, const void* v, const sparse_at
     if (!q || !k || !v || !out || !lse) return SA_E_INVALID_ARG;
     if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(out, 16) ||
         misaligned(cfg->workspace, 16) || misaligned(lse, 4) || misaligned(cfg->sink, 4) ||
-        misaligned(cfg->block_sel_out, 4) || misaligned(cfg->token_sel_out, 4))
+        misaligned(cfg->block_sel_out, 4) || misaligned(cfg->token_sel_out, 4) ||
+        misaligned(cfg->block_means, 16))
         return SA_E_ALIGNMENT;
     if (P.tok) {
         if (!cfg->idx_q || !cfg->idx_k) return SA_E_INVALID_ARG;
@@ -805,7 +808,9 @@ int sparse_attn_fwd(const void* q, const void* k, const void* v, const sparse_at
             da.list = (int32_t*)(ws + P.o_dec_list);
             da.nfar = (int32_t*)(ws + P.o_dec_nfar);
             da.bsel = cfg->block_sel_out;
-            if (P.nb > 0) {
+            if (cfg->block_means) {
+                da.kbar = cfg->block_means;   // kept by the caller
+            } else if (P.nb > 0) {
                 sa::PoolArgs pa{k, P.Nk, P.B, P.nb, (float*)(ws + P.o_dec_kbar), nullptr, 0, 0};
                 StageScope t("decode_block_pool", s);
                 if (!ok(sa::launch_pool(pa, P.D, P.f32, P.Bt * P.Hkv * P.nb, s))) return SA_E_HIP;

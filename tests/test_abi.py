@@ -313,3 +313,17 @@ def test_noalloc_rejects_before_launch(lib):
     # Argument checks as sparse_attn_fwd's.
     bad = sa.Params(1, 4, 3, 256, 64, window=8).cfg()
     assert lib.sparse_attn_fwd_noalloc(None, None, None, ctypes.byref(bad), None, None) == -2
+
+
+def test_block_means_only_for_block_gated_decode(lib):
+    # caller-kept block means serve a decode step under the block gate; any
+    # other call with them set is an invalid argument (checked on the host)
+    n = ctypes.c_size_t(0)
+    for p in (sa.Params(1, 4, 4, 256, 64, block_size=64, top_k=2),         # prefill
+              sa.Params(1, 4, 4, 4, 64, window=8, kv_len=256)):             # decode, no block gate
+        cfg = p.cfg()
+        cfg.block_means = 4096
+        assert lib.sparse_attn_workspace_bytes(ctypes.byref(cfg), ctypes.byref(n)) == -1
+    cfg = sa.Params(1, 4, 4, 4, 64, block_size=64, top_k=2, kv_len=256).cfg()
+    cfg.block_means = 4096
+    assert lib.sparse_attn_workspace_bytes(ctypes.byref(cfg), ctypes.byref(n)) == 0

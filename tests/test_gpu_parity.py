@@ -823,6 +823,28 @@ def test_decode_blocks_long_moba_cache(dev):
     run_and_check(decode_inputs(W.LONG_MOBA, 4, 8), dev, label="decode_blocks long_moba")
 
 
+@pytest.mark.parametrize("Nk", [1024, 1000])
+def test_decode_blocks_caller_means(dev, Nk):
+    # Block means kept by the caller (here from the pooling entry point over
+    # the complete blocks) give the same step, bit for bit, as pooling the
+    # cache inside the call.
+    import torch
+    import sliding_window_long_amd as sa
+    wl = W.Workload("dec_blk_means", 2, 4, 2, Nk, 128, "bf16", block_size=64, top_k=4, window=32,
+                    sink=True)
+    inp = decode_inputs(wl, 3, 9)
+    g = {k_: (None if v_ is None else v_.to(dev)) for k_, v_ in inp.tensors().items()}
+    kw = dict(block_size=64, top_k=4, window=32, sink=g["sink"])
+    ro, rl = sa.forward(g["q"], g["k"], g["v"], **kw)
+    nb = Nk // 64
+    means = sa.block_pool(g["k"][:, :, :nb * 64].contiguous(), 64)
+    o, l = sa.forward(g["q"], g["k"], g["v"], block_means=means, **kw)
+    torch.cuda.synchronize()
+    log(f"[gpu] decode_blocks caller means Nk={Nk}")
+    assert torch.equal(o.view(torch.int16), ro.view(torch.int16))
+    assert torch.equal(l.view(torch.int32), rl.view(torch.int32))
+
+
 @pytest.mark.parametrize("Nk,top_t", [(1500, 37), (20000, 37), (20000, 300)])
 def test_decode_token_ties(dev, Nk, top_t):
     # Equal indexer keys: the lowest token ids win in the decode step too.
