@@ -50,10 +50,12 @@
  * block gating a new query is gated as that position of a prefill over the
  * history: its own block (the last one may be incomplete) and the best
  * top_k - 1 complete earlier blocks by the dot product with their mean keys
- * (pooled from the cache on every call), per query head; mean summaries
- * only (no min/max, shared or first-block variant), at most 4096 complete
- * blocks and top_k <= 64.  Full attention (what the MoBA summary page runs
- * for generation) is a window >= kv_len.  Limits: seq_len <= 64.
+ * (pooled from the cache on every call, or kept by the caller: block_means),
+ * per query head, or per kv group with gate_shared (at most 16 heads a
+ * group); min/max summaries and block 0 kept work as in the prefill; at most
+ * 4096 complete blocks and top_k <= 64.  Full attention (what the MoBA
+ * summary page runs for generation) is a window >= kv_len.  Limits:
+ * seq_len <= 64.
  *
  * Layouts (row-major, contiguous, device memory; kv_len = seq_len unless a
  * decode step):

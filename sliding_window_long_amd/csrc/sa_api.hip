@@ -95,11 +95,12 @@ int make_plan(const sparse_attn_cfg* c, Plan* p, bool bwd = false) {
     if (Nk < c->seq_len) return SA_E_INVALID_ARG;
     const bool dec = Nk > c->seq_len;
     if (dec && (c->seq_len > sa::kDecMaxQ || c->cmp_block > 0)) return SA_E_UNSUPPORTED;
-    // Caller-kept block means serve a decode step's block gate only.
-    if (c->block_means && !(dec && c->top_k > 0)) return SA_E_INVALID_ARG;
-    // A decode step's block gate: mean block summaries, one selection per
-    // query head (the variants are prefill-only).
-    if (dec && c->top_k > 0 && (c->gate_repr != SA_GATE_MEAN || c->gate_shared || c->gate_first))
+    // Caller-kept block means serve a decode step's mean block gate only.
+    if (c->block_means && !(dec && c->top_k > 0 && c->gate_repr == SA_GATE_MEAN))
+        return SA_E_INVALID_ARG;
+    // A decode step's selection shared by a kv group: at most 16 heads a group.
+    if (dec && c->top_k > 0 && c->gate_shared && c->n_kv_heads > 0 &&
+        c->n_q_heads / c->n_kv_heads > 16)
         return SA_E_UNSUPPORTED;
     // The compressed branch joins window / block gating (the NSA layout), not
     // the token gate.
@@ -151,7 +152,10 @@ int make_plan(const sparse_attn_cfg* c, Plan* p, bool bwd = false) {
             P.top_t = (P.top_k - 1) * P.B;   // keys listed per query, at most
             if ((long long)P.Bt * P.Hq * P.N * (P.top_t > 0 ? P.top_t : 1) >= (1LL << 31))
                 return SA_E_UNSUPPORTED;
-            P.o_dec_kbar = take((size_t)P.Bt * P.Hkv * (P.nb > 0 ? P.nb : 1) * P.D * 4);
+            P.gate_mm = c->gate_repr == SA_GATE_MINMAX;
+            P.gate_shared = c->gate_shared != 0;
+            P.gate_first = c->gate_first != 0;
+            P.o_dec_kbar = take((size_t)P.Bt * P.Hkv * (P.nb > 0 ? P.nb : 1) * P.D * 4 * (P.gate_mm ? 2 : 1));
             P.o_dec_list = take((size_t)P.Bt * P.Hq * P.N * (P.top_t > 0 ? P.top_t : 1) * 4);
             P.o_dec_nfar = take((size_t)P.Bt * P.Hq * P.N * 4);
         }
@@ -803,7 +807,9 @@ int sparse_attn_fwd(const void* q, const void* k, const void* v, const sparse_at
             if (!ok(sa::launch_decode_select(da, s))) return SA_E_HIP;
         }
         if (P.dgate) {
-            da.B = P.B; da.top_k = P.top_k; da.nb = P.nb; da.per_head = 1;
+            da.B = P.B; da.top_k = P.top_k; da.nb = P.nb;
+            da.gate_mm = P.gate_mm; da.gate_shared = P.gate_shared; da.gate_first = P.gate_first;
+            da.list_mode = P.gate_shared ? 2 : 1;
             da.kbar = (const float*)(ws + P.o_dec_kbar);
             da.list = (int32_t*)(ws + P.o_dec_list);
             da.nfar = (int32_t*)(ws + P.o_dec_nfar);
@@ -811,7 +817,7 @@ int sparse_attn_fwd(const void* q, const void* k, const void* v, const sparse_at
             if (cfg->block_means) {
                 da.kbar = cfg->block_means;   // kept by the caller
             } else if (P.nb > 0) {
-                sa::PoolArgs pa{k, P.Nk, P.B, P.nb, (float*)(ws + P.o_dec_kbar), nullptr, 0, 0};
+                sa::PoolArgs pa{k, P.Nk, P.B, P.nb, (float*)(ws + P.o_dec_kbar), nullptr, 0, P.gate_mm ? 1 : 0};
                 StageScope t("decode_block_pool", s);
                 if (!ok(sa::launch_pool(pa, P.D, P.f32, P.Bt * P.Hkv * P.nb, s))) return SA_E_HIP;
             }

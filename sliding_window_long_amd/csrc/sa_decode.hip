@@ -470,18 +470,23 @@ __global__ __launch_bounds__(SEL_THREADS) void dec_select_kernel(DecArgs a) {
 
 // Attended keys of query r: the window [lo, p] (nw keys) then the nt kept
 // tokens before lo.
-// Query r of batch bt (query head h for per-head lists) at position p
-// attends the contiguous keys lo .. p (nw of them: the window, joined under
-// a block gate by the own block from its first key) and nt listed keys
-// before lo.
+// Row of query r's key list for query head h (see list_mode).
+__device__ __forceinline__ size_t dec_list_row(const DecArgs& a, int bt, int h, int r) {
+    if (a.list_mode == 1) return ((size_t)bt * a.Hq + h) * a.Nq + r;
+    if (a.list_mode == 2) return ((size_t)bt * a.Hkv + h / (a.Hq / a.Hkv)) * a.Nq + r;
+    return (size_t)bt * a.Nq + r;
+}
+
+// Query r of batch bt (query head h) at position p attends the contiguous
+// keys lo .. p (nw of them: the window, joined under a block gate by the own
+// block from its first key) and nt listed keys before lo.
 __device__ __forceinline__ void dec_span(const DecArgs& a, int bt, int h, int r, int& p, int& lo,
                                          int& nw, int& nt) {
     p = a.Nk - a.Nq + r;
     lo = a.window > 0 ? max(0, p - a.window + 1) : p;
     if (a.B > 0) lo = min(lo, (p / a.B) * a.B);
     nw = (a.window > 0 || a.B > 0) ? p - lo + 1 : 0;
-    const size_t lrow = a.per_head ? ((size_t)bt * a.Hq + h) * a.Nq + r : (size_t)bt * a.Nq + r;
-    nt = a.list ? a.nfar[lrow] : 0;
+    nt = a.list ? a.nfar[dec_list_row(a, bt, h, r)] : 0;
 }
 
 // Eight consecutive elements of a row staged in LDS, from byte offset b.
@@ -531,8 +536,8 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_attn_kernel(DecArgs a) {
     // group, or under per-head lists one query head.
     const int grp = blockIdx.y / a.Nq, r = blockIdx.y % a.Nq;
     const int Gr = a.Hq / a.Hkv;
-    const int G = a.per_head ? 1 : Gr;
-    const int kvh = a.per_head ? grp / Gr : grp, h0 = a.per_head ? grp : grp * Gr;
+    const int G = a.list_mode == 1 ? 1 : Gr;
+    const int kvh = a.list_mode == 1 ? grp / Gr : grp, h0 = a.list_mode == 1 ? grp : grp * Gr;
     float* const qs = dyn;
     float* const ps = dyn + G * D;
     int p, lo, nw, nt;
@@ -547,8 +552,7 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_attn_kernel(DecArgs a) {
     }
     if (tid < CH) {
         const int idx = key0 + min(tid, nk - 1);   // rows past nk repeat the last key
-        const size_t lrow = a.per_head ? ((size_t)bt * a.Hq + h0) * a.Nq + r : (size_t)bt * a.Nq + r;
-        js[tid] = idx < nw ? lo + idx : a.list[lrow * a.top_t + (idx - nw)];
+        js[tid] = idx < nw ? lo + idx : a.list[dec_list_row(a, bt, h0, r) * a.top_t + (idx - nw)];
     }
     __syncthreads();
 
@@ -705,9 +709,9 @@ __global__ __launch_bounds__(DEC_THREADS) void dec_combine_kernel(DecArgs a) {
 
 template <int D>
 static hipError_t dec_d(const DecArgs& a, hipStream_t s) {
-    const int groups = a.per_head ? a.Hq : a.Hkv;
+    const int groups = a.list_mode == 1 ? a.Hq : a.Hkv;
     const dim3 ag((unsigned)a.cmax, (unsigned)(groups * a.Nq), (unsigned)a.Bt);
-    const int G = a.per_head ? 1 : a.Hq / a.Hkv;
+    const int G = a.list_mode == 1 ? 1 : a.Hq / a.Hkv;
     const size_t dyn = (size_t)G * (D + dec_chunk(a.f32 != 0)) * sizeof(float);   // q, logits
     if (a.f32)
         hipLaunchKernelGGL((dec_attn_kernel<D, true>), ag, dim3(DEC_THREADS), dyn, s, a);
@@ -758,43 +762,68 @@ hipError_t launch_decode_select(const DecArgs& a, hipStream_t s) {
 // and "인과성 보존": score every earlier block by the query's dot product
 // with its mean key, keep the top k with the own block always among them;
 // read for a decode step as the same position of a prefill over the
-// history].  One 64-lane workgroup per (batch, query head, query): the query
-// at position p scores the complete blocks c < p / B against their fp32
-// means, keeps the best min(top_k - 1, p / B) by (score desc, index asc) --
-// an order key ord(score) << 32 | (2^32 - 1 - c), whose wave-wide maximum is
-// taken top_k - 1 times -- and lists the kept blocks' keys below lo (the
-// first key of its contiguous range [lo, p]: the own block, joined with the
-// window), ascending.  Writes list, nfar and, when asked, bsel.
+// history; the related-work remark for the min/max summary (Quest) and
+// block 0 always kept (an attention sink); one selection per kv group from
+// the summed scores of its heads].  One 64-lane workgroup per (batch, query
+// head, query), or per (batch, kv head, query) for a shared selection: the
+// query at position p scores the complete candidate blocks c0 <= c < p / B
+// (c0 = 1 when block 0 is forced) against their fp32 summaries, keeps the
+// best min(top_k - 1 - c0, p / B - c0) by (score desc, index asc) -- an
+// order key ord(score) << 32 | (2^32 - 1 - c), whose wave-wide maximum is
+// taken once per kept block -- and lists the keys of the forced and kept
+// blocks below lo (the first key of its contiguous range [lo, p]: the own
+// block, joined with the window), ascending.  Writes list, nfar and, when
+// asked, bsel (for every head of a sharing group).
 __global__ __launch_bounds__(64) void dec_block_select_kernel(DecArgs a) {
-    __shared__ float qs[128];
+    __shared__ float qs[16 * 128];
     __shared__ uint64_t keys[kDecMaxBlocks];
     __shared__ int kept[kDecMaxTopK];
     const int lane = threadIdx.x;
-    const size_t row = blockIdx.x;   // (bt * Hq + h) * Nq + r
-    const int r = (int)(row % a.Nq), h = (int)((row / a.Nq) % a.Hq);
-    const int bt = (int)(row / ((size_t)a.Nq * a.Hq)), g = h / (a.Hq / a.Hkv);
+    const int Gr = a.Hq / a.Hkv;
+    const size_t row = blockIdx.x;   // (bt * heads + head) * Nq + r, heads = Hkv if shared else Hq
+    const int heads = a.gate_shared ? a.Hkv : a.Hq;
+    const int r = (int)(row % a.Nq), hx = (int)((row / a.Nq) % heads);
+    const int bt = (int)(row / ((size_t)a.Nq * heads));
+    const int g = a.gate_shared ? hx : hx / Gr;
+    const int h_first = a.gate_shared ? g * Gr : hx, nh = a.gate_shared ? min(Gr, 16) : 1;
     const int p = a.Nk - a.Nq + r, own = p / a.B;
+    const int c0 = (a.gate_first && own > 0) ? 1 : 0;
     const int ncand = min(own, min(a.nb, kDecMaxBlocks));   // own <= nb, nb <= kDecMaxBlocks (plan)
-    for (int e = lane; e < a.D; e += 64) qs[e] = dec_load(a.q, row * a.D + e, a.f32);
+    for (int x = lane; x < nh * a.D; x += 64)
+        qs[x] = dec_load(a.q, (((size_t)bt * a.Hq + h_first + x / a.D) * a.Nq + r) * a.D + x % a.D, a.f32);
     __syncthreads();
-    const float* kb = a.kbar + (size_t)(bt * a.Hkv + g) * a.nb * a.D;
-    for (int c = lane; c < ncand; c += 64) {
-        const float* kr = kb + (size_t)c * a.D;
+    const int R = a.gate_mm ? 2 : 1;   // summary rows per block
+    const float* kb = a.kbar + (size_t)(bt * a.Hkv + g) * a.nb * R * a.D;
+    for (int c = c0 + lane; c < ncand; c += 64) {
+        const float* kr = kb + (size_t)c * R * a.D;
         float sc = 0.f;
-        for (int e = 0; e < a.D; e += 4) {
-            const float4 k4 = *(const float4*)(kr + e);
-            sc = fmaf(qs[e], k4.x, sc);
-            sc = fmaf(qs[e + 1], k4.y, sc);
-            sc = fmaf(qs[e + 2], k4.z, sc);
-            sc = fmaf(qs[e + 3], k4.w, sc);
+        for (int hl = 0; hl < nh; ++hl) {
+            const float* qh = qs + hl * a.D;
+            for (int e = 0; e < a.D; e += 4) {
+                const float4 k4 = *(const float4*)(kr + e);
+                if (a.gate_mm) {   // sum_e max(q_e min_e, q_e max_e)
+                    const float4 x4 = *(const float4*)(kr + a.D + e);
+                    sc += fmaxf(qh[e] * k4.x, qh[e] * x4.x);
+                    sc += fmaxf(qh[e + 1] * k4.y, qh[e + 1] * x4.y);
+                    sc += fmaxf(qh[e + 2] * k4.z, qh[e + 2] * x4.z);
+                    sc += fmaxf(qh[e + 3] * k4.w, qh[e + 3] * x4.w);
+                } else {
+                    sc = fmaf(qh[e], k4.x, sc);
+                    sc = fmaf(qh[e + 1], k4.y, sc);
+                    sc = fmaf(qh[e + 2], k4.z, sc);
+                    sc = fmaf(qh[e + 3], k4.w, sc);
+                }
+            }
         }
         keys[c] = (uint64_t)dec_ord32(sc) << 32 | (uint64_t)(0xffffffffu - (uint32_t)c);
     }
     __syncthreads();
-    const int m = min(min(a.top_k - 1, kDecMaxTopK), ncand);
+    // kept[0] = 0 when block 0 is forced, then the chosen candidates
+    const int m = max(0, min(min(a.top_k - 1 - c0, kDecMaxTopK - c0), ncand - c0));
+    if (lane == 0 && c0) kept[0] = 0;
     for (int t = 0; t < m; ++t) {
         uint64_t best = 0;
-        for (int c = lane; c < ncand; c += 64) best = keys[c] > best ? keys[c] : best;
+        for (int c = c0 + lane; c < ncand; c += 64) best = keys[c] > best ? keys[c] : best;
 #pragma unroll
         for (int d = 32; d >= 1; d >>= 1) {
             const uint32_t lo32 = (uint32_t)__shfl_xor((int)(uint32_t)best, d);
@@ -803,13 +832,14 @@ __global__ __launch_bounds__(64) void dec_block_select_kernel(DecArgs a) {
             best = o > best ? o : best;
         }
         // every key not yet taken is nonzero, so best names a candidate
-        const int c = min(max((int)(0xffffffffu - (uint32_t)best), 0), ncand - 1);
-        if (lane == 0) kept[t] = c;
-        if (lane == (c & 63)) keys[c] = 0;   // the lane that scans c
+        const int c = min(max((int)(0xffffffffu - (uint32_t)best), c0), ncand - 1);
+        if (lane == 0) kept[c0 + t] = c;
+        if (lane == ((c - c0) & 63)) keys[c] = 0;   // the lane that scans c
         __syncthreads();
     }
+    const int nk = c0 + m;   // forced and kept blocks before the own one
     if (lane == 0)   // ascending
-        for (int t = 1; t < m; ++t) {
+        for (int t = 1; t < nk; ++t) {
             const int x = kept[t];
             int u = t - 1;
             while (u >= 0 && kept[u] > x) {
@@ -819,28 +849,30 @@ __global__ __launch_bounds__(64) void dec_block_select_kernel(DecArgs a) {
             kept[u + 1] = x;
         }
     __syncthreads();
-    if (a.bsel) {
-        int32_t* o = a.bsel + row * a.top_k;
-        for (int t = lane; t < a.top_k; t += 64) o[t] = t < m ? kept[t] : (t == m ? own : -1);
-    }
+    if (a.bsel)
+        for (int hl = 0; hl < nh; ++hl) {
+            int32_t* o = a.bsel + (((size_t)bt * a.Hq + h_first + hl) * a.Nq + r) * a.top_k;
+            for (int t = lane; t < a.top_k; t += 64) o[t] = t < nk ? kept[t] : (t == nk ? own : -1);
+        }
     int lo = own * a.B;
     if (a.window > 0) lo = min(lo, max(0, p - a.window + 1));
     int32_t* L = a.list + row * a.top_t;
     int pos = 0;
-    for (int t = 0; t < m; ++t) {
-        const int c0 = kept[t] * a.B;
-        const int cnt = max(0, min(a.B, lo - c0));   // <= B: the list holds (top_k - 1) B keys
-        for (int j = lane; j < cnt; j += 64) L[pos + j] = c0 + j;
+    for (int t = 0; t < nk; ++t) {
+        const int kb0 = kept[t] * a.B;
+        const int cnt = max(0, min(a.B, lo - kb0));   // <= B: the list holds (top_k - 1) B keys
+        for (int j = lane; j < cnt; j += 64) L[pos + j] = kb0 + j;
         pos += cnt;
     }
     if (lane == 0) a.nfar[row] = pos;
 }
 
 hipError_t launch_decode_block_select(const DecArgs& a, hipStream_t s) {
-    if (a.B <= 0 || a.D > 128 || a.nb > kDecMaxBlocks || a.top_k > kDecMaxTopK + 1 ||
-        a.top_t < (a.top_k - 1) * a.B)
+    if (a.B <= 0 || a.D > 128 || a.nb > kDecMaxBlocks || a.top_k > kDecMaxTopK ||
+        a.top_t < (a.top_k - 1) * a.B || (a.gate_shared && a.Hq / a.Hkv > 16) ||
+        a.list_mode != (a.gate_shared ? 2 : 1))
         return hipErrorInvalidValue;
-    const unsigned rows = (unsigned)((size_t)a.Bt * a.Hq * a.Nq);
+    const unsigned rows = (unsigned)((size_t)a.Bt * (a.gate_shared ? a.Hkv : a.Hq) * a.Nq);
     hipLaunchKernelGGL(dec_block_select_kernel, dim3(rows), dim3(64), 0, s, a);
     return hipGetLastError();
 }

@@ -284,14 +284,17 @@ struct DecArgs {
     int cmax;               // tiles of dec_chunk(f32) attended keys per query, upper bound
     void* out;              // [Bt, Hq, Nq, D], the input dtype
     float* lse;             // [Bt, Hq, Nq]
-    // Block gate of a decode step (B > 0): every query head keeps its own
-    // list (per_head), the keys of its kept blocks below its range [lo, p].
+    // Block gate of a decode step (B > 0): the keys of the kept blocks below
+    // the query's range [lo, p] are listed per query head, or per kv group
+    // when the group shares its selection.
     int B;                  // block size, 0: no block gate
-    int top_k;              // blocks kept per query, the own block included
+    int top_k;              // blocks kept per query, the own block (and block 0 with first) included
     int nb;                 // complete blocks of the history (Nk / B)
-    const float* kbar;      // [Bt, Hkv, nb, D] fp32 block means
-    int32_t* bsel;          // [Bt, Hq, Nq, top_k] kept blocks (ascending, own last, -1), or nullptr
-    int per_head;           // list and nfar indexed by (batch, q head, query)
+    const float* kbar;      // [Bt, Hkv, nb, D] fp32 block means, or [.., nb, 2, D] min then max
+    int32_t* bsel;          // [Bt, Hq, Nq, top_k] kept blocks (ascending), -1 padded; or nullptr
+    int gate_mm, gate_shared, gate_first;   // gate variants
+    int list_mode;          // list and nfar rows: 0 (batch, query) -- the token gate;
+                            // 1 (batch, q head, query); 2 (batch, kv head, query)
 };
 
 // A decode step's block gate scores at most this many complete blocks per

@@ -85,11 +85,10 @@ def code_of(params, **cfg_fields):
     (sa.Params(1, 4, 4, 64 * 80, 64, block_size=64, top_k=3, window=64 * 65 + 1), -8),  # 65 near blocks
     (sa.Params(1, 4, 4, 256, 64, window=8, kv_len=255), -1),          # fewer keys than queries
     (sa.Params(1, 4, 4, 256, 64, window=8, kv_len=-1), -1),
-    # decode with a block gate: mean summaries, per-head selection only; at
-    # most 4096 complete blocks and top 64
-    (sa.Params(1, 4, 4, 4, 64, block_size=64, top_k=2, kv_len=256, gate_repr=1), -8),
-    (sa.Params(1, 4, 2, 4, 64, block_size=64, top_k=2, kv_len=256, gate_shared=1), -8),
-    (sa.Params(1, 4, 4, 4, 64, block_size=64, top_k=2, kv_len=256, gate_first=1), -8),
+    # decode with a block gate: at most 4096 complete blocks, top 64, and a
+    # shared selection over at most 16 heads a group
+    (sa.Params(1, 34, 2, 4, 64, block_size=64, top_k=2, kv_len=256, gate_shared=1), -8),
+    (sa.Params(1, 4, 4, 4, 64, block_size=64, top_k=1, kv_len=256, gate_first=1), -1),
     (sa.Params(1, 4, 4, 4, 64, block_size=48, top_k=2, kv_len=256), -2),
     (sa.Params(1, 4, 4, 4, 64, block_size=64, top_k=5, kv_len=250), -2),     # 4 blocks
     (sa.Params(1, 1, 1, 1, 64, block_size=8, top_k=2, kv_len=8 * 4097), -8),
@@ -324,6 +323,9 @@ def test_block_means_only_for_block_gated_decode(lib):
         cfg = p.cfg()
         cfg.block_means = 4096
         assert lib.sparse_attn_workspace_bytes(ctypes.byref(cfg), ctypes.byref(n)) == -1
+    cfg = sa.Params(1, 4, 4, 4, 64, block_size=64, top_k=2, kv_len=256, gate_repr=1).cfg()
+    cfg.block_means = 4096   # min/max summaries: not means
+    assert lib.sparse_attn_workspace_bytes(ctypes.byref(cfg), ctypes.byref(n)) == -1
     cfg = sa.Params(1, 4, 4, 4, 64, block_size=64, top_k=2, kv_len=256).cfg()
     cfg.block_means = 4096
     assert lib.sparse_attn_workspace_bytes(ctypes.byref(cfg), ctypes.byref(n)) == 0

@@ -810,6 +810,17 @@ def test_decode_blocks(dev, d, Nk, nq, B, top_k, window, offs):
     run_and_check(decode_inputs(wl, nq, 41 + d + Nk + nq), dev, label=f"decode_blocks nq={nq} B={B}")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("repr_,shared,first", [("minmax", False, False), ("mean", True, False),
+                                                ("mean", False, True), ("minmax", True, True)])
+def test_decode_blocks_variants(dev, d, repr_, shared, first):
+    # the gate variants during decode: min/max summaries, one selection per
+    # kv group (GQA 8/2), block 0 always kept
+    wl = W.Workload("dec_blk_var", 1, 8, 2, 2000, d, "bf16", block_size=64, top_k=5, window=40,
+                    sink=True, gate_repr=repr_, gate_shared=shared, gate_first=first)
+    run_and_check(decode_inputs(wl, 3, 13 + d), dev, label=f"decode_blocks {repr_} shared={shared} first={first}")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "fp8"])
 def test_decode_blocks_dtypes(dev, dtype):
     wl = W.Workload("dec_blk_dt", 1, 8, 2, 2048, 128, dtype, block_size=64, top_k=5, window=64,

@@ -326,6 +326,9 @@ DECODE_CASES = [
     dict(block_size=4, top_k=3, window=3, sink=True),
     dict(block_size=4, top_k=2),
     dict(block_size=4, top_k=4, window=1),
+    # the gate variants during decode
+    dict(block_size=4, top_k=3, window=2, gate_repr="minmax"),
+    dict(block_size=4, top_k=3, gate_shared=True, gate_first=True, sink=True),
 ]
 
 
